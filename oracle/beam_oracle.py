@@ -1,0 +1,229 @@
+"""Oracle for the BEAM masked-MoE layer forward pass.
+
+TEST INFRASTRUCTURE.  Only the tests, the smoke check and the CPU-baseline leg
+of the benchmark may import this module.  It is a plain, slow, float64 numpy
+implementation of what the layer computes, written from the method's
+description and sharing nothing with the HIP library: no kernels, headers,
+helpers or tables.
+
+Sources (cited below by the short names on the left):
+
+  [P3]  "BEAM: Dynamic MoE 라우팅을 위한 Binary Expert Activation Masking"
+        (aitrends.kr).  Its method paragraph gives the four steps: Step 1
+        Standard Top-K Routing, Step 2 Raw Mask Generation, Step 3 Binary
+        Masking, Step 4 Masked Aggregation; its architecture paragraph restates
+        them and adds the zero-initialised mask router; its limitations list,
+        item C, mentions shared experts.
+  [P1]  "BEAM: 用于 MoE 动态路由的二进制专家激活掩码" (ai-feeds.com), section
+        方法 / 输出与推理加速: at inference only experts whose mask is 1 run.
+  [P2]  "BEAM: Binäre Expertenaktivierungsmaskierung für dynamisches Routing in
+        MoE" (chatpaper.ai), the English abstract: MoE-layer FLOPs fall with
+        the number of active experts.
+
+Readings where the pages leave a step open (each is also listed with the
+design notes of the repository):
+
+  * Router R(x) is linear, r = x.Wr^T (+ optional per-expert bias b_r).
+  * The mask router has one logit per expert, z = x.Wm^T (+ optional bias b_m),
+    gathered at the top-K experts; m_hat = sigmoid(z).
+  * "m = 1 if m_hat >= 0.5" is decided as z >= 0, which is the same set in
+    exact arithmetic and avoids a rounded sigmoid landing on 0.5.
+  * Softmax runs over the K kept logits only; masked gates are NOT
+    renormalised (g_hat = g * m, so sum(g_hat) <= 1).
+  * Top-K order: descending logit, equal logits ordered by lower expert index.
+  * Experts are SwiGLU FFNs: E(x) = Wd (silu(Wg x) * (Wu x)), silu(a) = a/(1+e^-a).
+  * Shared experts are always on, with gate 1, and are added to y.
+  * Router and mask decisions (which experts, which bits) are taken on
+    float32 logits, the precision the GPU kernels decide in: the logits are
+    computed in float64 and rounded once to float32.  Everything else is
+    float64.
+
+Parity status: every function here is pinned by tests in tests/test_oracle.py
+(closed forms, a hand-derived worked example under tests/golden/, library
+special cases and brute-force sums); none is "parity unpinned".
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import numpy as np
+
+__all__ = [
+    "widen", "router_logits", "select_experts", "Routing", "route", "silu",
+    "expert_ffn", "forward", "expert_counts", "layer_stats",
+]
+
+
+def widen(a: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact float64 value of stored inputs: bf16 bit patterns (uint16) are
+    moved to the top half of a float32 word; float32 is widened directly."""
+    a = np.asarray(a)
+    if dtype == "bf16":
+        if a.dtype != np.uint16:
+            raise TypeError("bf16 inputs are stored as uint16 bit patterns")
+        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    if dtype == "f32":
+        if a.dtype != np.float32:
+            raise TypeError("f32 inputs are stored as float32")
+        return a.astype(np.float64)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def router_logits(layer, x: np.ndarray):
+    """Router logits r and mask-router logits z, float64, shape [T][E].
+
+    [P3] Step 1: r = R(x); Step 2: the raw mask is sigmoid(x Wm), so z = x Wm
+    is its argument.  Optional biases are added when the layer has them.
+    """
+    dt = layer.cfg.dtype
+    X = widen(x, dt)
+    r = X @ widen(layer.w_router, dt).T
+    z = X @ widen(layer.w_mask, dt).T
+    if layer.b_router is not None:
+        r = r + np.asarray(layer.b_router, dtype=np.float64)
+    if layer.b_mask is not None:
+        z = z + np.asarray(layer.b_mask, dtype=np.float64)
+    return r, z
+
+
+@dataclass
+class Routing:
+    idx: np.ndarray        # [T][K] int32, top-K experts by descending logit
+    g: np.ndarray          # [T][K] float64, softmax over the K kept logits
+    keep: np.ndarray       # [T][K] bool, binary mask m on the top-K candidates
+    ghat: np.ndarray       # [T][K] float64, g * m
+    mask_bits: np.ndarray  # [T] uint32, bit k = keep[t][k]
+
+
+def select_experts(r: np.ndarray, z: np.ndarray, K: int) -> Routing:
+    """Top-K, softmax, binary mask and masked gates for each token.
+
+    [P3] Step 1: keep the K largest router logits and apply a softmax to them
+    (g).  Step 2/3: m_i = 1 when sigmoid(z_i) >= 0.5, for i in the top-K set.
+    Step 4: g_hat = g * m.  Decisions are taken on float32-rounded logits.
+    """
+    r32 = np.asarray(r, dtype=np.float64).astype(np.float32)
+    z32 = np.asarray(z, dtype=np.float64).astype(np.float32)
+    T, E = r32.shape
+    if not (1 <= K <= E):
+        raise ValueError("need 1 <= K <= E")
+    idx = np.empty((T, K), dtype=np.int32)
+    g = np.empty((T, K), dtype=np.float64)
+    keep = np.empty((T, K), dtype=bool)
+    for t in range(T):
+        # Stable sort of the negated logits: equal logits keep index order,
+        # so the lower expert index comes first.
+        order = np.argsort(-r32[t], kind="stable")[:K]
+        idx[t] = order
+        v = r32[t, order].astype(np.float64)
+        w = np.exp(v - v.max())
+        g[t] = w / w.sum()
+        keep[t] = z32[t, order] >= np.float32(0.0)
+    ghat = np.where(keep, g, 0.0)
+    weights = (np.uint64(1) << np.arange(K, dtype=np.uint64))
+    mask_bits = (keep.astype(np.uint64) * weights).sum(axis=1).astype(np.uint32)
+    return Routing(idx, g, keep, ghat, mask_bits)
+
+
+def route(layer, x: np.ndarray) -> Routing:
+    """[P3] Steps 1-3 (and the gate product of Step 4) for every token of x."""
+    r, z = router_logits(layer, x)
+    return select_experts(r, z, layer.cfg.K)
+
+
+def silu(a: np.ndarray) -> np.ndarray:
+    """silu(a) = a * sigmoid(a) = a / (1 + exp(-a))."""
+    with np.errstate(over="ignore"):
+        return a / (1.0 + np.exp(-a))
+
+
+def expert_ffn(wg: np.ndarray, wu: np.ndarray, wd: np.ndarray, X: np.ndarray) -> np.ndarray:
+    """SwiGLU expert applied to rows of X (float64): Wd (silu(Wg x) * (Wu x)).
+
+    wg, wu: [I][D]; wd: [D][I]; X: [n][D]  ->  [n][D].
+    """
+    h = silu(X @ wg.T) * (X @ wu.T)
+    return h @ wd.T
+
+
+def _expert_weights(layer, e: int):
+    dt = layer.cfg.dtype
+    return (widen(layer.w_gate[e], dt), widen(layer.w_up[e], dt), widen(layer.w_down[e], dt))
+
+
+def _shared_weights(layer, s: int):
+    dt = layer.cfg.dtype
+    return (widen(layer.ws_gate[s], dt), widen(layer.ws_up[s], dt), widen(layer.ws_down[s], dt))
+
+
+def forward(layer, x: np.ndarray, tokens: Optional[Sequence[int]] = None,
+            routing: Optional[Routing] = None):
+    """Layer output y (float64) for the given tokens (all by default).
+
+    [P3] Step 4: y = sum_i g_hat_i E_i(x) over the top-K candidates; [P1]
+    only candidates with m = 1 are evaluated (g_hat = 0 for the others, so
+    skipping them leaves y unchanged).  Shared experts ([P3] limitations C)
+    are added with gate 1.  Terms are added token by token in slot order
+    k = 0..K-1, then shared expert 0..S-1; tokens that use the same expert in
+    the same slot are evaluated together.
+
+    Returns (routing of the selected tokens, y [n][D]).
+    """
+    cfg = layer.cfg
+    tok = np.arange(x.shape[0]) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    xs = x[tok]
+    rt = route(layer, xs) if routing is None else routing
+    X = widen(xs, cfg.dtype)
+    y = np.zeros((len(tok), cfg.D), dtype=np.float64)
+    cache = {}
+    for k in range(cfg.K):
+        for e in np.unique(rt.idx[:, k]):
+            rows = np.nonzero((rt.idx[:, k] == e) & rt.keep[:, k])[0]
+            if rows.size == 0:
+                continue
+            if e not in cache:
+                cache[e] = _expert_weights(layer, int(e))
+            out = expert_ffn(*cache[e], X[rows])
+            y[rows] += rt.ghat[rows, k][:, None] * out
+    for s in range(cfg.S):
+        y += expert_ffn(*_shared_weights(layer, s), X)
+    return rt, y
+
+
+def expert_counts(rt: Routing, E: int) -> np.ndarray:
+    """Surviving (token, expert) pairs per expert: c_e = #{(t,k): idx=e, m=1}."""
+    return np.bincount(rt.idx[rt.keep].astype(np.int64), minlength=E).astype(np.int64)
+
+
+def layer_stats(cfg, counts: np.ndarray, T: int) -> dict:
+    """Work accounting from the per-expert counts.
+
+    Avg-K = surviving pairs / T ([P3] results: average active experts per
+    token).  MoE-layer FLOPs scale with the surviving pairs ([P2] abstract):
+    a SwiGLU expert costs 6*D*I flops per token (three D x I products, two
+    flops per multiply-add); the router costs 4*E*D per token (two E x D
+    products).  Active-expert bytes: every expert with at least one pair is
+    read once, plus the shared experts.
+    """
+    counts = np.asarray(counts, dtype=np.int64)
+    P = int(counts.sum())
+    active = int((counts > 0).sum())
+    elt = 4 if cfg.dtype == "f32" else 2
+    D, I = cfg.D, cfg.I
+    out = {
+        "T": T, "E": cfg.E, "K": cfg.K,
+        "active_pairs": P,
+        "active_experts": active,
+        "avg_k": (P / T) if T > 0 else 0.0,
+        "flops_routed": 6.0 * D * I * P,
+        "flops_topk_routed": 6.0 * D * I * T * cfg.K,
+        "flops_shared": 6.0 * D * cfg.I_s * cfg.S * T,
+        "flops_router": 4.0 * cfg.E * D * T,
+        "bytes_active_expert_weights": float(3 * D * I * elt * active + 3 * D * cfg.I_s * elt * cfg.S),
+    }
+    out["flops_reduction"] = (1.0 - out["flops_routed"] / out["flops_topk_routed"]) if T > 0 else 0.0
+    out["bytes_total_min"] = (out["bytes_active_expert_weights"]
+                              + 2.0 * cfg.E * D * elt          # router + mask-router weights
+                              + 2.0 * T * D * elt)             # x in, y out
+    return out

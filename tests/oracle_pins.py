@@ -1,0 +1,329 @@
+"""Pins for the oracle: checks against facts fixed by the method's definition,
+not by the oracle's own code.
+
+Each pin takes the oracle module as an argument so that the same checks can be
+run against deliberately broken copies of it (tests/test_oracle_mutants.py):
+every plausible mistake must make at least one pin fail.
+
+Independent computations used here are written with torch (float64, CPU):
+torch.topk + torch.softmax + torch.sigmoid + torch.nn.functional.silu, i.e.
+library routines, never the oracle's functions.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+from common import (eval_closed_form, layer_from_json, small_config, with_mask)
+import synth
+
+
+# --------------------------------------------------------------------------
+# Independent torch computations (library special cases)
+# --------------------------------------------------------------------------
+
+def _t(a, dtype):
+    """float64 torch tensor of stored inputs (bf16 bits or float32)."""
+    a = np.asarray(a)
+    if dtype == "bf16":
+        return torch.from_numpy(a.astype(np.int16)).view(torch.bfloat16).to(torch.float64)
+    return torch.from_numpy(a.astype(np.float32)).to(torch.float64)
+
+
+def torch_logits(layer, x):
+    dt = layer.cfg.dtype
+    X = _t(x, dt)
+    r = torch.matmul(X, _t(layer.w_router, dt).t())
+    z = torch.matmul(X, _t(layer.w_mask, dt).t())
+    if layer.b_router is not None:
+        r = r + torch.from_numpy(np.asarray(layer.b_router, np.float64))
+    if layer.b_mask is not None:
+        z = z + torch.from_numpy(np.asarray(layer.b_mask, np.float64))
+    # decisions on float32 logits
+    return r.to(torch.float32).to(torch.float64), z.to(torch.float32).to(torch.float64)
+
+
+def torch_dense_gates(layer, x, use_mask=True):
+    """G[t][e]: masked top-K softmax gate of expert e for token t (0 elsewhere)."""
+    r, z = torch_logits(layer, x)
+    K = layer.cfg.K
+    vals, idx = torch.topk(r, K, dim=1)
+    g = torch.softmax(vals, dim=1)
+    if use_mask:
+        m = (torch.sigmoid(torch.gather(z, 1, idx)) >= 0.5).to(torch.float64)
+        g = g * m
+    G = torch.zeros_like(r)
+    G.scatter_(1, idx, g)
+    return G, idx
+
+
+def torch_expert(layer, e, X, shared=False):
+    dt = layer.cfg.dtype
+    if shared:
+        wg, wu, wd = layer.ws_gate[e], layer.ws_up[e], layer.ws_down[e]
+    else:
+        wg, wu, wd = layer.w_gate[e], layer.w_up[e], layer.w_down[e]
+    h = F.silu(X @ _t(wg, dt).t()) * (X @ _t(wu, dt).t())
+    return h @ _t(wd, dt).t()
+
+
+def torch_dense_forward(layer, x, use_mask=True):
+    """Brute force: y = sum over ALL experts of G[:, e] * E_e(x) + shared."""
+    X = _t(x, layer.cfg.dtype)
+    G, _ = torch_dense_gates(layer, x, use_mask)
+    y = torch.zeros(X.shape[0], layer.cfg.D, dtype=torch.float64)
+    for e in range(layer.cfg.E):
+        y += G[:, e:e + 1] * torch_expert(layer, e, X)
+    for s in range(layer.cfg.S):
+        y += torch_expert(layer, s, X, shared=True)
+    return y.numpy()
+
+
+def _rel(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    den = max(np.abs(b).max(), 1e-300)
+    return np.abs(a - b).max() / den
+
+
+# --------------------------------------------------------------------------
+# Small random layers (drawn with the shared seeded generator)
+# --------------------------------------------------------------------------
+
+def small_layer(tag, dtype="bf16", D=96, E=10, K=3, I=40, S=0, I_s=0, keep=0.5, router_bias=False):
+    cfg = small_config("pin:" + tag, dtype, D, E, K, I, S, I_s, keep, router_bias)
+    return synth.make_layer(cfg)
+
+
+def small_x(layer, T, tag="x"):
+    from common import enforce_margins
+    return enforce_margins(layer, synth.make_x(layer.cfg, T, tag), T, tag)
+
+
+# --------------------------------------------------------------------------
+# Pins
+# --------------------------------------------------------------------------
+
+def pin_golden_routed(O):
+    """Hand-derived worked example: idx, mask bits, g, g_hat, counts, Avg-K, y."""
+    j, layer, x = layer_from_json("worked_example_routed.json")
+    rt, y = O.forward(layer, x)
+    ex = j["expect"]
+    assert np.array_equal(rt.idx, np.array(ex["idx"])), rt.idx
+    assert np.array_equal(rt.mask_bits, np.array(ex["mask_bits"], np.uint32)), rt.mask_bits
+    g = np.vectorize(eval_closed_form)(np.array(ex["g"], dtype=object)).astype(float)
+    gh = np.vectorize(eval_closed_form)(np.array(ex["ghat"], dtype=object)).astype(float)
+    assert np.allclose(rt.g, g, rtol=0, atol=1e-7), rt.g
+    assert np.allclose(rt.ghat, gh, rtol=0, atol=1e-7), rt.ghat
+    assert np.array_equal(O.expert_counts(rt, layer.cfg.E), np.array(ex["counts"]))
+    st = O.layer_stats(layer.cfg, O.expert_counts(rt, layer.cfg.E), x.shape[0])
+    assert abs(st["avg_k"] - eval_closed_form(ex["avg_k"])) < 1e-15
+    yy = np.vectorize(eval_closed_form)(np.array(ex["y"], dtype=object)).astype(float)
+    assert np.allclose(y, yy, rtol=0, atol=1e-6), (y, yy)
+    assert np.all(y[2] == 0.0)   # all candidates masked: exact zero
+
+
+def pin_golden_shared(O):
+    """Worked example with an always-on shared expert."""
+    j, layer, x = layer_from_json("worked_example_shared.json")
+    rt, y = O.forward(layer, x)
+    ex = j["expect"]
+    assert np.array_equal(rt.idx, np.array(ex["idx"]))
+    assert np.array_equal(rt.mask_bits, np.array(ex["mask_bits"], np.uint32))
+    assert np.array_equal(O.expert_counts(rt, layer.cfg.E), np.array(ex["counts"]))
+    yy = np.vectorize(eval_closed_form)(np.array(ex["y"], dtype=object)).astype(float)
+    assert np.allclose(y, yy, rtol=0, atol=1e-6), (y, yy)
+
+
+def pin_zero_mask_router_is_topk(O):
+    """Wm = 0 (zero-initialised mask router): m_hat = 0.5 everywhere, every
+    top-K expert is kept, and the layer equals plain top-K MoE (torch)."""
+    for tag, kw in (("zm_bf16", dict(dtype="bf16", D=64, E=12, K=3, I=48)),
+                    ("zm_f32", dict(dtype="f32", D=40, E=6, K=2, I=24, S=1, I_s=16)),
+                    ("zm_k1", dict(dtype="bf16", D=32, E=5, K=1, I=20))):
+        layer = with_mask(small_layer(tag, **kw), w_mask_zero=True)
+        layer = with_mask(layer, b_mask=0.0)
+        x = small_x(layer, 17)
+        rt, y = O.forward(layer, x)
+        assert rt.keep.all()
+        assert np.all(rt.mask_bits == (1 << layer.cfg.K) - 1)
+        ref = torch_dense_forward(layer, x, use_mask=False)
+        assert _rel(y, ref) < 1e-12, (tag, _rel(y, ref))
+        G, idx = torch_dense_gates(layer, x, use_mask=False)
+        assert np.array_equal(rt.idx, idx.numpy()), tag
+
+
+def pin_dense_bruteforce(O):
+    """Brute-force dense sum over all E experts with masked gates (zeros for
+    non-candidates and masked candidates) equals the oracle's sparse forward."""
+    for tag, kw in (("bf_bf16", dict(dtype="bf16", D=64, E=9, K=4, I=32, S=2, I_s=16, keep=0.4)),
+                    ("bf_f32", dict(dtype="f32", D=48, E=7, K=3, I=24, keep=0.6)),
+                    ("bf_bias", dict(dtype="bf16", D=64, E=16, K=5, I=16, keep=0.2, router_bias=True))):
+        layer = small_layer(tag, **kw)
+        x = small_x(layer, 23)
+        rt, y = O.forward(layer, x)
+        ref = torch_dense_forward(layer, x, use_mask=True)
+        assert _rel(y, ref) < 1e-12, (tag, _rel(y, ref))
+        G, idx = torch_dense_gates(layer, x, use_mask=True)
+        assert np.array_equal(rt.idx, idx.numpy()), tag
+        Gs = np.zeros((x.shape[0], layer.cfg.E))
+        np.put_along_axis(Gs, rt.idx.astype(np.int64), rt.ghat, axis=1)
+        assert np.abs(Gs - G.numpy()).max() < 1e-12, tag
+
+
+def pin_avgk_popcount(O):
+    """Avg-K = popcount(mask)/T = sum_e c_e / T (exact integers)."""
+    layer = small_layer("avgk", D=64, E=20, K=6, I=8, keep=0.3)
+    x = small_x(layer, 50)
+    rt = O.route(layer, x)
+    pop = sum(bin(int(b)).count("1") for b in rt.mask_bits)
+    c = O.expert_counts(rt, layer.cfg.E)
+    assert int(c.sum()) == pop == int(rt.keep.sum())
+    st = O.layer_stats(layer.cfg, c, 50)
+    assert st["avg_k"] == pop / 50
+    assert st["active_pairs"] == pop
+    # FLOPs(BEAM) / FLOPs(top-K) = Avg-K / K, compared as exact integer products
+    assert st["flops_routed"] * 50 * layer.cfg.K == st["flops_topk_routed"] * pop
+
+
+def pin_mask_bias_extremes(O):
+    """b_m = -1e4: every candidate masked, y = shared part only (0 without shared).
+    b_m = +1e4: every candidate kept, y equals the Wm = 0 layer."""
+    for tag, kw in (("ext_noshared", dict(D=64, E=8, K=2, I=32)),
+                    ("ext_shared", dict(D=64, E=8, K=3, I=32, S=2, I_s=24))):
+        base = small_layer(tag, **kw)
+        x = small_x(base, 11)
+        lo = with_mask(base, b_mask=-1e4)
+        rt, y = O.forward(lo, x)
+        assert not rt.keep.any() and np.all(rt.mask_bits == 0)
+        if base.cfg.S == 0:
+            assert np.all(y == 0.0)
+        else:
+            X = _t(x, "bf16")
+            sh = sum(torch_expert(base, s, X, shared=True) for s in range(base.cfg.S)).numpy()
+            assert _rel(y, sh) < 1e-12
+        hi = with_mask(base, b_mask=1e4)
+        zero = with_mask(with_mask(base, w_mask_zero=True), b_mask=0.0)
+        _, y_hi = O.forward(hi, x)
+        _, y_zero = O.forward(zero, x)
+        assert _rel(y_hi, y_zero) < 1e-15
+
+
+def pin_k1(O):
+    """K = 1: the softmax of one logit is exactly 1, so y = m * E_argmax(x)."""
+    layer = small_layer("k1", D=64, E=7, K=1, I=24, keep=0.5)
+    x = small_x(layer, 19)
+    rt, y = O.forward(layer, x)
+    assert np.all(rt.g == 1.0)
+    r, _ = torch_logits(layer, x)
+    am = torch.argmax(r, dim=1).numpy()
+    assert np.array_equal(rt.idx[:, 0], am)
+    X = _t(x, "bf16")
+    for t in range(x.shape[0]):
+        ref = torch_expert(layer, int(am[t]), X[t:t + 1]).numpy()[0] * float(rt.keep[t, 0])
+        assert np.abs(y[t] - ref).max() <= 1e-12 * max(1.0, np.abs(ref).max())
+
+
+def pin_k_equals_e(O):
+    """K = E: the top-K is a full descending sort of the logits."""
+    layer = small_layer("kfull", dtype="f32", D=32, E=8, K=8, I=8)
+    x = small_x(layer, 13)
+    rt = O.route(layer, x)
+    r, _ = torch_logits(layer, x)
+    srt = torch.sort(r, dim=1, descending=True, stable=True).indices.numpy()
+    assert np.array_equal(rt.idx, srt)
+
+
+def pin_gate_properties(O):
+    """sum_k g_k = 1 and g is non-increasing in k; g_hat = g on kept slots, 0 elsewhere."""
+    layer = small_layer("gates", D=64, E=30, K=8, I=8, keep=0.5, router_bias=True)
+    x = small_x(layer, 40)
+    rt = O.route(layer, x)
+    assert np.abs(rt.g.sum(axis=1) - 1.0).max() < 1e-12
+    assert np.all(np.diff(rt.g, axis=1) <= 0.0)
+    assert np.array_equal(rt.ghat, np.where(rt.keep, rt.g, 0.0))
+    assert np.all(rt.ghat.sum(axis=1) <= 1.0 + 1e-12)
+
+
+def pin_threshold_is_sigmoid_half(O):
+    """m = [sigmoid(z) >= 0.5] on the candidates, checked with torch.sigmoid."""
+    layer = small_layer("thr", D=64, E=16, K=6, I=8, keep=0.35)
+    x = small_x(layer, 64)
+    rt = O.route(layer, x)
+    _, z = torch_logits(layer, x)
+    zc = torch.gather(z, 1, torch.from_numpy(rt.idx.astype(np.int64)))
+    assert np.array_equal(rt.keep, (torch.sigmoid(zc) >= 0.5).numpy())
+
+
+def pin_batch_invariance(O):
+    """Routing and output of each token computed alone equal the batched ones."""
+    layer = small_layer("batch", D=48, E=9, K=3, I=16, S=1, I_s=8, keep=0.5)
+    x = small_x(layer, 9)
+    rt, y = O.forward(layer, x)
+    for t in range(9):
+        rt1, y1 = O.forward(layer, x[t:t + 1])
+        assert np.array_equal(rt1.idx[0], rt.idx[t])
+        assert rt1.mask_bits[0] == rt.mask_bits[t]
+        assert np.abs(y1[0] - y[t]).max() <= 1e-12 * max(1.0, np.abs(y[t]).max())
+
+
+def pin_expert_permutation(O):
+    """Permuting every per-expert tensor consistently permutes the indices and
+    leaves g, m and y unchanged."""
+    layer = small_layer("perm", D=48, E=11, K=4, I=16, keep=0.5, router_bias=True)
+    x = small_x(layer, 15)
+    rt, y = O.forward(layer, x)
+    p = np.random.default_rng(7).permutation(layer.cfg.E)   # new expert j = old p[j]
+    inv = np.argsort(p)
+    from dataclasses import replace
+    lp = replace(layer, w_router=layer.w_router[p], w_mask=layer.w_mask[p],
+                 b_router=layer.b_router[p], b_mask=None if layer.b_mask is None else layer.b_mask[p],
+                 w_gate=layer.w_gate[p], w_up=layer.w_up[p], w_down=layer.w_down[p])
+    rtp, yp = O.forward(lp, x)
+    assert np.array_equal(p[rtp.idx], rt.idx)
+    assert np.array_equal(inv[rt.idx], rtp.idx)
+    assert np.array_equal(rtp.mask_bits, rt.mask_bits)
+    assert np.abs(rtp.g - rt.g).max() == 0.0
+    assert _rel(yp, y) < 1e-13
+
+
+def pin_silu_closed_forms(O):
+    """silu(0) = 0; silu(a) - silu(-a) = a; silu(1) = e/(1+e); large-|a| limits."""
+    a = np.linspace(-30, 30, 601)
+    s = O.silu(a)
+    assert O.silu(np.array([0.0]))[0] == 0.0
+    assert np.abs((s - O.silu(-a)) - a).max() < 1e-12
+    assert abs(O.silu(np.array([1.0]))[0] - np.e / (1 + np.e)) < 1e-15
+    assert abs(O.silu(np.array([-800.0]))[0]) == 0.0
+    assert O.silu(np.array([800.0]))[0] == 800.0
+
+
+def pin_widen_bf16(O):
+    """bf16 bit patterns widen exactly: 0x3F80 = 1, 0xC000 = -2, 0x3EAB = 0.333984375."""
+    bits = np.array([0x3F80, 0xC000, 0x3EAB, 0x0000, 0x8000, 0x7F7F], dtype=np.uint16)
+    v = O.widen(bits, "bf16")
+    assert v[0] == 1.0 and v[1] == -2.0 and v[2] == 0.333984375 and v[3] == 0.0
+    assert v[5] == float.fromhex("0x1.fep+127")
+
+
+def pin_stats_formulas(O):
+    """FLOPs and bytes: FLOPs(BEAM)/FLOPs(top-K) = AvgK/K; per-expert SwiGLU
+    cost 6*D*I per pair; bytes count each active expert once."""
+    cfg = small_config("stats", "bf16", D=10, E=4, K=2, I=3, S=1, I_s=5)
+    st = O.layer_stats(cfg, np.array([3, 0, 1, 0]), 4)
+    assert st["active_pairs"] == 4 and st["active_experts"] == 2 and st["avg_k"] == 1.0
+    assert st["flops_routed"] == 6 * 10 * 3 * 4
+    assert st["flops_topk_routed"] == 6 * 10 * 3 * 4 * 2
+    assert st["flops_reduction"] == 0.5
+    assert st["flops_shared"] == 6 * 10 * 5 * 1 * 4
+    assert st["flops_router"] == 4 * 4 * 10 * 4
+    assert st["bytes_active_expert_weights"] == 3 * 10 * 3 * 2 * 2 + 3 * 10 * 5 * 2
+
+
+ALL_PINS = [
+    pin_golden_routed, pin_golden_shared, pin_zero_mask_router_is_topk, pin_dense_bruteforce,
+    pin_avgk_popcount, pin_mask_bias_extremes, pin_k1, pin_k_equals_e, pin_gate_properties,
+    pin_threshold_is_sigmoid_half, pin_batch_invariance, pin_expert_permutation,
+    pin_silu_closed_forms, pin_widen_bf16, pin_stats_formulas,
+]

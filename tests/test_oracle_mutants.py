@@ -1,0 +1,92 @@
+"""Every plausible mistake planted in a copy of the oracle fails some pin.
+
+Mistakes are planted only in fresh copies of the oracle module, on the CPU.
+"""
+import os
+import types
+
+import numpy as np
+import pytest
+
+import oracle.beam_oracle as real
+from oracle_pins import ALL_PINS
+
+SRC = open(real.__file__).read()
+
+
+def _copy():
+    mod = types.ModuleType("oracle_mutant")
+    mod.__file__ = real.__file__
+    exec(compile(SRC, real.__file__, "exec"), mod.__dict__)
+    return mod
+
+
+def _src_mutant(*edits):
+    src = SRC
+    for old, new in edits:
+        assert src.count(old) == 1, old
+        src = src.replace(old, new)
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src, real.__file__, "exec"), mod.__dict__)
+    return mod
+
+
+MUTANTS = {
+    # gates renormalised after masking
+    "renormalise": ("ghat = np.where(keep, g, 0.0)",
+                    "ghat = np.where(keep, g, 0.0); ghat = ghat / np.maximum(ghat.sum(1, keepdims=True), 1e-300)"),
+    # softmax over all experts, then top-K
+    "softmax_all_E": ("w = np.exp(v - v.max())\n        g[t] = w / w.sum()",
+                      "w = np.exp(v - r32[t].max())\n        g[t] = w / np.exp(r32[t].astype(np.float64) - r32[t].max()).sum()"),
+    # strict threshold
+    "strict_threshold": ("keep[t] = z32[t, order] >= np.float32(0.0)", "keep[t] = z32[t, order] > np.float32(0.0)"),
+    # mask read by slot instead of by expert
+    "mask_by_slot": ("keep[t] = z32[t, order] >= np.float32(0.0)", "keep[t] = z32[t, :K] >= np.float32(0.0)"),
+    # mask ignored: masked candidates evaluated with their unmasked gate
+    "mask_ignored": [("rows = np.nonzero((rt.idx[:, k] == e) & rt.keep[:, k])[0]",
+                      "rows = np.nonzero(rt.idx[:, k] == e)[0]"),
+                     ("y[rows] += rt.ghat[rows, k][:, None] * out", "y[rows] += rt.g[rows, k][:, None] * out")],
+    # ties broken toward the higher index
+    "ties_high": ('order = np.argsort(-r32[t], kind="stable")[:K]',
+                  'order = (E - 1 - np.argsort(-r32[t][::-1], kind="stable"))[:K]'),
+    # ascending instead of descending
+    "ascending": ('order = np.argsort(-r32[t], kind="stable")[:K]', 'order = np.argsort(r32[t], kind="stable")[:K]'),
+    # silu replaced by sigmoid
+    "sigmoid_not_silu": ("return a / (1.0 + np.exp(-a))", "return 1.0 / (1.0 + np.exp(-a))"),
+    # gate and up swapped inside silu
+    "gate_up_swapped": ("h = silu(X @ wg.T) * (X @ wu.T)", "h = silu(X @ wu.T) * (X @ wg.T)"),
+    # shared experts dropped
+    "no_shared": ("for s in range(cfg.S):\n        y +=", "for s in range(0):\n        y +="),
+    # router bias dropped
+    "no_router_bias": ("r = r + np.asarray(layer.b_router, dtype=np.float64)", "r = r"),
+    # mask bias sign flipped
+    "mask_bias_sign": ("z = z + np.asarray(layer.b_mask, dtype=np.float64)", "z = z - np.asarray(layer.b_mask, dtype=np.float64)"),
+    # down projection not transposed (wrong operand orientation)
+    "down_no_transpose": ("return h @ wd.T", "return (h @ wd.reshape(wd.shape[1], wd.shape[0]))"),
+    # mask applied to the router logit instead of the mask logit
+    "mask_from_router": ("keep[t] = z32[t, order] >= np.float32(0.0)", "keep[t] = r32[t, order] >= np.float32(0.0)"),
+    # bf16 widening drops the shift
+    "widen_wrong": ("(a.astype(np.uint32) << np.uint32(16))", "(a.astype(np.uint32) << np.uint32(15))"),
+    # Avg-K counts all top-K slots
+    "avgk_topk": ('"avg_k": (P / T) if T > 0 else 0.0', '"avg_k": (cfg.K if T > 0 else 0.0)'),
+}
+
+
+def test_real_copy_passes_all_pins():
+    mod = _copy()
+    for pin in ALL_PINS[:2]:
+        pin(mod)
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    edits = MUTANTS[name]
+    mod = _src_mutant(*(edits if isinstance(edits, list) else [edits]))
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(mod)
+        except Exception as exc:  # noqa: BLE001 - any failure counts as caught
+            caught.append((pin.__name__, type(exc).__name__))
+    assert caught, f"mutant {name} passed every pin"
