@@ -1,0 +1,337 @@
+// C ABI of the BEAM masked-MoE layer: argument validation, workspace
+// carving, launch sequence, work accounting and the launch profiler.
+#include <string.h>
+
+#include <map>
+#include <string>
+#include <vector>
+
+#include "beam_internal.h"
+
+namespace beam {
+
+static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int expert_tile_rows(const beam_moe_layer& L, int32_t T) {
+  if (L.dtype == BEAM_F32) return 16;
+  // Expected tokens per routed expert if every top-K candidate were kept.
+  const long per_expert = (long(T) * L.K + L.E - 1) / L.E;
+  if (per_expert <= 16) return 16;
+  if (per_expert <= 32) return 32;
+  if (per_expert <= 96) return 64;
+  return 128;
+}
+
+WsLayout workspace_layout(const beam_moe_layer& L, int32_t T) {
+  WsLayout w;
+  const size_t TK = size_t(T) * L.K;
+  const size_t elt = L.dtype == BEAM_F32 ? 4 : 2;
+  const size_t nblk = (size_t(T) + kSelBlock - 1) / kSelBlock;
+  const size_t IS = size_t(L.n_shared) * L.I_shared;
+  // Smallest tile height is 16 rows: bound on the tile count.
+  w.max_tiles = int32_t((TK + 15) / 16 + std::min<size_t>(L.E, TK) + (size_t(T) + 15) / 16 + 1);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  };
+  w.plan = take(sizeof(Plan));
+  w.logits = take(size_t(T) * 2 * L.E * 4);
+  w.idx = take(TK * 4);
+  w.gates = take(TK * 4);
+  w.mask = take(size_t(T) * 4);
+  w.counts = take(size_t(L.E) * 4);
+  w.rank = take(TK * 4);
+  w.block_counts = take(nblk * L.E * 4);
+  w.expert_off = take(size_t(L.E + 1) * 4);
+  w.tiles = take(size_t(w.max_tiles) * sizeof(Tile));
+  w.perm_token = take(TK * 4);
+  w.slot_pos = take(TK * 4);
+  w.h = take(TK * L.I * elt);
+  w.h_shared = take(size_t(T) * IS * elt);
+  w.o = take(TK * L.D * 4);
+  w.o_shared = take(IS ? size_t(T) * L.D * 4 : 0);
+  w.total = off;
+  return w;
+}
+
+// ---------------------------------------------------------------------------
+// Profiler
+// ---------------------------------------------------------------------------
+
+namespace {
+struct ProfState {
+  bool on = false;
+  int max = 0;
+  int n = 0;
+  bool pending = false;
+  std::vector<hipEvent_t> ev0, ev1;
+  std::vector<const char*> names;
+};
+ProfState g_prof;
+}  // namespace
+
+void prof_before(const char* name, hipStream_t s) {
+  g_prof.pending = false;
+  if (!g_prof.on || g_prof.n >= g_prof.max) return;
+  if (hipEventRecord(g_prof.ev0[g_prof.n], s) != hipSuccess) return;
+  g_prof.names[g_prof.n] = name;
+  g_prof.pending = true;
+}
+
+void prof_after(hipStream_t s) {
+  if (!g_prof.pending) return;
+  g_prof.pending = false;
+  if (hipEventRecord(g_prof.ev1[g_prof.n], s) == hipSuccess) ++g_prof.n;
+}
+
+}  // namespace beam
+
+using namespace beam;
+
+// ---------------------------------------------------------------------------
+// Validation
+// ---------------------------------------------------------------------------
+
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+static int check_layer(const beam_moe_layer* L) {
+  if (!L) return BEAM_ERR_INVALID_ARG;
+  if (L->dtype != BEAM_F32 && L->dtype != BEAM_BF16) return BEAM_ERR_INVALID_ARG;
+  if (L->D <= 0 || L->E <= 0 || L->K <= 0 || L->I <= 0 || L->n_shared < 0)
+    return BEAM_ERR_INVALID_ARG;
+  if (L->K > L->E) return BEAM_ERR_INVALID_ARG;
+  if (L->n_shared > 0 && L->I_shared <= 0) return BEAM_ERR_INVALID_ARG;
+  const void* req[] = {L->w_router, L->w_mask, L->w_gate, L->w_up, L->w_down};
+  for (const void* p : req)
+    if (!p || !aligned16(p)) return BEAM_ERR_INVALID_ARG;
+  if (L->n_shared > 0) {
+    const void* sh[] = {L->ws_gate, L->ws_up, L->ws_down};
+    for (const void* p : sh)
+      if (!p || !aligned16(p)) return BEAM_ERR_INVALID_ARG;
+  }
+  if ((L->b_router && (reinterpret_cast<uintptr_t>(L->b_router) & 3u)) ||
+      (L->b_mask && (reinterpret_cast<uintptr_t>(L->b_mask) & 3u)))
+    return BEAM_ERR_INVALID_ARG;
+  if (L->K > 32 || L->E > kMaxExperts) return BEAM_ERR_UNSUPPORTED;
+  if (L->D % 64 || L->I % 64 || L->D > 16384 || L->I > (1 << 20)) return BEAM_ERR_UNSUPPORTED;
+  if (L->n_shared > 0 && (L->I_shared % 64 || long(L->n_shared) * L->I_shared > (1 << 20)))
+    return BEAM_ERR_UNSUPPORTED;
+  return BEAM_OK;
+}
+
+static int check_call(const beam_moe_layer* L, const void* x, int32_t T, void* ws, size_t ws_bytes,
+                      WsLayout* lay) {
+  int st = check_layer(L);
+  if (st != BEAM_OK) return st;
+  if (T < 0) return BEAM_ERR_INVALID_ARG;
+  if (long(T) * L->K > (1L << 30)) return BEAM_ERR_UNSUPPORTED;
+  if (T == 0) return BEAM_OK;
+  if (!x || !aligned16(x)) return BEAM_ERR_INVALID_ARG;
+  *lay = workspace_layout(*L, T);
+  if (!ws || !aligned16(ws) || ws_bytes < lay->total) return BEAM_ERR_WORKSPACE;
+  return BEAM_OK;
+}
+
+static int check_route_out(const beam_route_out* out) {
+  if (!out || !out->topk_idx || !out->gates || !out->mask || !out->expert_count)
+    return BEAM_ERR_INVALID_ARG;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(out->topk_idx) |
+                      reinterpret_cast<uintptr_t>(out->gates) |
+                      reinterpret_cast<uintptr_t>(out->mask) |
+                      reinterpret_cast<uintptr_t>(out->expert_count);
+  return (a & 3u) ? BEAM_ERR_INVALID_ARG : BEAM_OK;
+}
+
+static Ptrs carve(const WsLayout& w, void* ws, const beam_route_out* out) {
+  char* b = static_cast<char*>(ws);
+  Ptrs p;
+  p.logits = reinterpret_cast<float*>(b + w.logits);
+  p.idx = out ? out->topk_idx : reinterpret_cast<int32_t*>(b + w.idx);
+  p.gates = out ? out->gates : reinterpret_cast<float*>(b + w.gates);
+  p.mask = out ? out->mask : reinterpret_cast<uint32_t*>(b + w.mask);
+  p.counts = out ? out->expert_count : reinterpret_cast<int32_t*>(b + w.counts);
+  p.rank = reinterpret_cast<int32_t*>(b + w.rank);
+  p.block_counts = reinterpret_cast<int32_t*>(b + w.block_counts);
+  p.expert_off = reinterpret_cast<int32_t*>(b + w.expert_off);
+  p.plan = reinterpret_cast<Plan*>(b + w.plan);
+  p.tiles = reinterpret_cast<Tile*>(b + w.tiles);
+  p.perm_token = reinterpret_cast<int32_t*>(b + w.perm_token);
+  p.slot_pos = reinterpret_cast<int32_t*>(b + w.slot_pos);
+  p.h = b + w.h;
+  p.h_shared = b + w.h_shared;
+  p.o = reinterpret_cast<float*>(b + w.o);
+  p.o_shared = reinterpret_cast<float*>(b + w.o_shared);
+  return p;
+}
+
+#define BEAM_TRY(expr)                         \
+  do {                                         \
+    if ((expr) != hipSuccess) return BEAM_ERR_HIP; \
+  } while (0)
+
+static int run_routing(const beam_moe_layer& L, const void* x, int32_t T, int tile_rows,
+                       const Ptrs& p, hipStream_t s) {
+  BEAM_TRY(launch_router_logits(L, x, T, p.logits, s));
+  BEAM_TRY(launch_select(L, T, p, s));
+  BEAM_TRY(launch_scan(L, T, tile_rows, p, s));
+  return BEAM_OK;
+}
+
+extern "C" {
+
+size_t beam_moe_workspace_size(const beam_moe_layer* layer, int32_t T_max) {
+  if (check_layer(layer) != BEAM_OK || T_max < 0) return 0;
+  if (long(T_max) * layer->K > (1L << 30)) return 0;
+  return workspace_layout(*layer, T_max).total;
+}
+
+int beam_moe_route(const beam_moe_layer* layer, const void* x, int32_t T,
+                   const beam_route_out* out, void* ws, size_t ws_bytes, void* stream) {
+  WsLayout lay;
+  int st = check_call(layer, x, T, ws, ws_bytes, &lay);
+  if (st != BEAM_OK) return st;
+  if ((st = check_route_out(out)) != BEAM_OK) return st;
+  if (T == 0) return BEAM_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Ptrs p = carve(lay, ws, out);
+  return run_routing(*layer, x, T, expert_tile_rows(*layer, T), p, s);
+}
+
+int beam_moe_forward(const beam_moe_layer* layer, const void* x, int32_t T, void* y,
+                     const beam_route_out* out, void* ws, size_t ws_bytes, void* stream) {
+  WsLayout lay;
+  int st = check_call(layer, x, T, ws, ws_bytes, &lay);
+  if (st != BEAM_OK) return st;
+  if (out && (st = check_route_out(out)) != BEAM_OK) return st;
+  if (T == 0) return BEAM_OK;
+  if (!y || !aligned16(y) || y == x) return BEAM_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const Ptrs p = carve(lay, ws, out);
+  const int tile_rows = expert_tile_rows(*layer, T);
+  if ((st = run_routing(*layer, x, T, tile_rows, p, s)) != BEAM_OK) return st;
+  BEAM_TRY(launch_scatter(*layer, T, p, s));
+  BEAM_TRY(launch_gate_up(*layer, x, T, tile_rows, lay, p, s));
+  BEAM_TRY(launch_down(*layer, T, tile_rows, lay, p, s));
+  BEAM_TRY(launch_combine(*layer, T, p, y, s));
+  return BEAM_OK;
+}
+
+int beam_moe_stats_host(const beam_moe_layer* layer, const int32_t* counts, int32_t T,
+                        beam_stats* out) {
+  int st = check_layer(layer);
+  if (st != BEAM_OK) return st;
+  if (!out || T < 0 || (!counts && T > 0)) return BEAM_ERR_INVALID_ARG;
+  const beam_moe_layer& L = *layer;
+  beam_stats s;
+  memset(&s, 0, sizeof(s));
+  s.T = T;
+  s.E = L.E;
+  s.K = L.K;
+  int64_t P = 0;
+  int act = 0;
+  for (int e = 0; e < L.E && T > 0; ++e) {
+    if (counts[e] < 0) return BEAM_ERR_INVALID_ARG;
+    P += counts[e];
+    act += counts[e] > 0;
+  }
+  const double elt = L.dtype == BEAM_F32 ? 4.0 : 2.0;
+  const double D = L.D, I = L.I, Is = L.I_shared, S = L.n_shared;
+  s.active_pairs = P;
+  s.active_experts = act;
+  s.avg_k = T > 0 ? double(P) / T : 0.0;
+  s.flops_routed = 6.0 * D * I * double(P);
+  s.flops_topk_routed = 6.0 * D * I * double(T) * L.K;
+  s.flops_shared = 6.0 * D * Is * S * T;
+  s.flops_router = 4.0 * double(L.E) * D * T;
+  s.flops_reduction = T > 0 ? 1.0 - s.flops_routed / s.flops_topk_routed : 0.0;
+  s.bytes_active_expert_weights = 3.0 * D * I * elt * act + 3.0 * D * Is * elt * S;
+  s.bytes_total_min = s.bytes_active_expert_weights + 2.0 * L.E * D * elt + 2.0 * double(T) * D * elt;
+  *out = s;
+  return BEAM_OK;
+}
+
+int beam_moe_stats(const beam_moe_layer* layer, const int32_t* expert_count, int32_t T,
+                   beam_stats* host_out, void* stream) {
+  int st = check_layer(layer);
+  if (st != BEAM_OK) return st;
+  if (!host_out || T < 0 || (!expert_count && T > 0)) return BEAM_ERR_INVALID_ARG;
+  std::vector<int32_t> h(layer->E, 0);
+  if (T > 0) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (hipMemcpyAsync(h.data(), expert_count, sizeof(int32_t) * layer->E, hipMemcpyDeviceToHost,
+                       s) != hipSuccess)
+      return BEAM_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return BEAM_ERR_HIP;
+  }
+  return beam_moe_stats_host(layer, h.data(), T, host_out);
+}
+
+const char* beam_status_str(int status) {
+  switch (status) {
+    case BEAM_OK: return "BEAM_OK";
+    case BEAM_ERR_INVALID_ARG: return "BEAM_ERR_INVALID_ARG: invalid argument";
+    case BEAM_ERR_UNSUPPORTED: return "BEAM_ERR_UNSUPPORTED: shape or option not supported";
+    case BEAM_ERR_WORKSPACE: return "BEAM_ERR_WORKSPACE: workspace missing or too small";
+    case BEAM_ERR_HIP: return "BEAM_ERR_HIP: HIP runtime or launch failure";
+    default: return "unknown beam_status";
+  }
+}
+
+int beam_profile_begin(int32_t max_launches) {
+  if (max_launches <= 0 || g_prof.on) return BEAM_ERR_INVALID_ARG;
+  if (int(g_prof.ev0.size()) < max_launches) {
+    while (int(g_prof.ev0.size()) < max_launches) {
+      hipEvent_t a, b;
+      if (hipEventCreate(&a) != hipSuccess) return BEAM_ERR_HIP;
+      if (hipEventCreate(&b) != hipSuccess) return BEAM_ERR_HIP;
+      g_prof.ev0.push_back(a);
+      g_prof.ev1.push_back(b);
+    }
+  }
+  g_prof.names.assign(max_launches, nullptr);
+  g_prof.max = max_launches;
+  g_prof.n = 0;
+  g_prof.pending = false;
+  g_prof.on = true;
+  return BEAM_OK;
+}
+
+int beam_profile_end(const char** names, int32_t* launches, double* total_ms, int32_t max_out) {
+  if (!g_prof.on) return BEAM_ERR_INVALID_ARG;
+  g_prof.on = false;
+  std::vector<std::string> order;
+  std::map<std::string, std::pair<int, double>> agg;
+  std::map<std::string, const char*> keep;
+  for (int i = 0; i < g_prof.n; ++i) {
+    if (hipEventSynchronize(g_prof.ev1[i]) != hipSuccess) return BEAM_ERR_HIP;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, g_prof.ev0[i], g_prof.ev1[i]) != hipSuccess) return BEAM_ERR_HIP;
+    const std::string k(g_prof.names[i]);
+    if (!agg.count(k)) {
+      order.push_back(k);
+      keep[k] = g_prof.names[i];
+    }
+    agg[k].first += 1;
+    agg[k].second += ms;
+  }
+  int n = 0;
+  for (const auto& k : order) {
+    if (n >= max_out) break;
+    if (names) names[n] = keep[k];
+    if (launches) launches[n] = agg[k].first;
+    if (total_ms) total_ms[n] = agg[k].second;
+    ++n;
+  }
+  return n;
+}
+
+int beam_copy_kernel(void* dst, const void* src, size_t bytes, void* stream) {
+  if (!dst || !src || bytes % 16 || !aligned16(dst) || !aligned16(src)) return BEAM_ERR_INVALID_ARG;
+  if (bytes == 0) return BEAM_OK;
+  return launch_copy(dst, src, bytes, static_cast<hipStream_t>(stream)) == hipSuccess ? BEAM_OK
+                                                                                      : BEAM_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,87 @@
+// Host-side internal interfaces of the BEAM library: workspace layout, the
+// device plan record, and the kernel launchers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "../../include/beam_moe.h"
+
+namespace beam {
+
+// Tokens per routing block (selection, block-local ranks, per-block counts).
+constexpr int kSelBlock = 64;
+// Largest E the selection and scan kernels handle.
+constexpr int kMaxExperts = 1024;
+
+// Written by the scan kernel, read by the expert kernels.  Tiles are listed
+// routed first (expert-major, ascending expert id), then the shared tiles.
+struct Plan {
+  int32_t pairs;            // P = surviving (token, expert) pairs
+  int32_t n_tiles_routed;   // tiles of routed experts
+  int32_t n_tiles_shared;   // tiles of the fused shared expert
+  int32_t active_experts;
+};
+
+// One tile of rows of a (virtual) expert: rows [row0, row0 + rows) of the
+// compacted pair order (routed) or of the token order (shared, expert == E).
+struct Tile {
+  int32_t expert;
+  int32_t row0;
+  int32_t rows;
+  int32_t pad;
+};
+
+struct WsLayout {
+  size_t plan, logits, idx, gates, mask, counts, rank, block_counts, expert_off, tiles, perm_token,
+      slot_pos, h, h_shared, o, o_shared, total;
+  int32_t max_tiles;
+};
+
+// Row-tile height of the expert kernels (multiple of 16).
+int expert_tile_rows(const beam_moe_layer& L, int32_t T);
+WsLayout workspace_layout(const beam_moe_layer& L, int32_t T);
+
+struct Ptrs {
+  // routing
+  float* logits;
+  int32_t* idx;
+  float* gates;
+  uint32_t* mask;
+  int32_t* counts;
+  int32_t* rank;
+  int32_t* block_counts;
+  int32_t* expert_off;
+  Plan* plan;
+  Tile* tiles;
+  int32_t* perm_token;
+  int32_t* slot_pos;
+  // experts
+  void* h;
+  void* h_shared;
+  float* o;
+  float* o_shared;
+};
+
+// ---- launchers (return hipSuccess or the launch error) ----
+hipError_t launch_router_logits(const beam_moe_layer& L, const void* x, int32_t T, float* logits,
+                                hipStream_t s);
+hipError_t launch_select(const beam_moe_layer& L, int32_t T, const Ptrs& p, hipStream_t s);
+hipError_t launch_scan(const beam_moe_layer& L, int32_t T, int tile_rows, const Ptrs& p,
+                       hipStream_t s);
+hipError_t launch_scatter(const beam_moe_layer& L, int32_t T, const Ptrs& p, hipStream_t s);
+hipError_t launch_gate_up(const beam_moe_layer& L, const void* x, int32_t T, int tile_rows,
+                          const WsLayout& w, const Ptrs& p, hipStream_t s);
+hipError_t launch_down(const beam_moe_layer& L, int32_t T, int tile_rows, const WsLayout& w,
+                       const Ptrs& p, hipStream_t s);
+hipError_t launch_combine(const beam_moe_layer& L, int32_t T, const Ptrs& p, void* y,
+                          hipStream_t s);
+hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t s);
+
+// Profiler hooks around each launch (no-ops unless the profiler is on).
+void prof_before(const char* name, hipStream_t s);
+void prof_after(hipStream_t s);
+
+}  // namespace beam

@@ -1,0 +1,575 @@
+// Expert kernels of the BEAM layer: grouped SwiGLU gate/up products, grouped
+// down products, and the gated combine.
+//
+// Method: BEAM page on aitrends.kr ("BEAM: Dynamic MoE 라우팅을 위한 Binary
+// Expert Activation Masking"), method paragraph Step 4: y = sum_i g_hat_i
+// E_i(x) with g_hat = g * m; only pairs with m = 1 are evaluated (ai-feeds.com
+// summary, section on inference), and shared experts are added with gate 1
+// (aitrends.kr page, limitation C).  Experts are SwiGLU FFNs,
+// E(x) = Wd (silu(Wg x) * (Wu x)).
+//
+// Work is listed as (tile, n-block) items: tiles come from the scan kernel
+// (routed tiles expert-major, then the shared tiles); the fused shared expert
+// is virtual expert E whose intermediate rows are the n_shared experts'
+// rows back to back.  Grids are persistent: workgroup b takes items b,
+// b + gridDim.x, ... up to the device-side item count, so no host readback of
+// the counts is needed.
+#include "beam_internal.h"
+#include "gemm_engines.h"
+
+namespace beam {
+
+struct ExpertArgs {
+  const void* x;
+  const void* wg;
+  const void* wu;
+  const void* wd;
+  const void* sg;
+  const void* su;
+  const void* sd;
+  int T, D, E, I, S, Is;
+  const Plan* plan;
+  const Tile* tiles;
+  const int32_t* perm_token;
+  void* h;         // [P][I]
+  void* h_sh;      // [T][S*Is]
+  float* o;        // [P][D]
+  float* o_sh;     // [T][D]
+};
+
+// Decodes work item w into (tile index, n-block, shared?).
+__device__ __forceinline__ bool work_item(long w, int ntr, int nts, int nbr, int nbs, int& ti,
+                                          int& nb, bool& shared) {
+  const long wr = long(ntr) * nbr;
+  if (w < wr) {
+    ti = int(w / nbr);
+    nb = int(w % nbr);
+    shared = false;
+    return true;
+  }
+  const long w2 = w - wr;
+  if (w2 < long(nts) * nbs) {
+    ti = ntr + int(w2 / nbs);
+    nb = int(w2 % nbs);
+    shared = true;
+    return true;
+  }
+  return false;
+}
+
+// ---------------------------------------------------------------------------
+// gate/up + SwiGLU (bf16)
+// ---------------------------------------------------------------------------
+
+struct GateUpSkinnyProv {
+  const u16* wg;     // expert's [I][D] (or shared [S*Is][D])
+  const u16* wu;
+  const u16* xb;
+  const int32_t* perm;  // nullptr for the shared expert (rows are tokens)
+  int D, n0, row0, rows;
+  __device__ int nseg() const { return 1; }
+  __device__ int seg_chunks() const { return D / 64; }
+  __device__ const u16* w(int mat, int r, int) const {
+    return (mat == 0 ? wg : wu) + size_t(n0 + r) * D;
+  }
+  __device__ const u16* x_row(int r) const {
+    if (r >= rows) return nullptr;
+    const int t = perm ? perm[row0 + r] : row0 + r;
+    return xb + size_t(t) * D;
+  }
+  __device__ const u16* x(int r, int) const { return x_row(r); }
+};
+
+template <int MT>
+__global__ __launch_bounds__(256) void k_gate_up_skinny(ExpertArgs a) {
+  __shared__ f32x4 red[4 * 2 * MT * kWave];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ntr = a.plan->n_tiles_routed, nts = a.plan->n_tiles_shared;
+  const int nbr = a.I / 16, nbs = a.S > 0 ? (a.S * a.Is) / 16 : 1;
+  const long total = long(ntr) * nbr + long(nts) * nbs;
+  for (long w = blockIdx.x; w < total; w += gridDim.x) {
+    int ti, nb;
+    bool shared;
+    work_item(w, ntr, nts, nbr, nbs, ti, nb, shared);
+    const Tile tl = a.tiles[ti];
+    const int Iv = shared ? a.S * a.Is : a.I;
+    GateUpSkinnyProv pv;
+    if (shared) {
+      pv.wg = (const u16*)a.sg;
+      pv.wu = (const u16*)a.su;
+      pv.perm = nullptr;
+    } else {
+      pv.wg = (const u16*)a.wg + size_t(tl.expert) * a.I * a.D;
+      pv.wu = (const u16*)a.wu + size_t(tl.expert) * a.I * a.D;
+      pv.perm = a.perm_token;
+    }
+    pv.xb = (const u16*)a.x;
+    pv.D = a.D;
+    pv.n0 = nb * 16;
+    pv.row0 = tl.row0;
+    pv.rows = tl.rows;
+    f32x4 acc[2][MT];
+    skinny_accumulate<2, MT, (MT >= 4 ? 1 : 4 / MT)>(pv, lane, wave, 4, acc);
+    skinny_reduce<2, MT>(acc, red, lane, wave, 4);
+    u16* hb = shared ? (u16*)a.h_sh : (u16*)a.h;
+    for (int mt = wave; mt < MT; mt += 4) {
+      f32x4 g = acc[0][0], u = acc[1][0];
+#pragma unroll
+      for (int b = 0; b < MT; ++b)
+        if (b == mt) {
+          g = acc[0][b];
+          u = acc[1][b];
+        }
+      const int r = 16 * mt + (lane & 15);
+      if (r < tl.rows) {
+        const int n = nb * 16 + 4 * (lane >> 4);
+        ushort4 hv;
+        hv.x = f32_to_bf16(silu_f32(g[0]) * u[0]);
+        hv.y = f32_to_bf16(silu_f32(g[1]) * u[1]);
+        hv.z = f32_to_bf16(silu_f32(g[2]) * u[2]);
+        hv.w = f32_to_bf16(silu_f32(g[3]) * u[3]);
+        *reinterpret_cast<ushort4*>(hb + size_t(tl.row0 + r) * Iv + n) = hv;
+      }
+    }
+  }
+}
+
+// Tiled: the 128 weight rows of an n-block are 64 intermediate rows of Wg and
+// the same 64 rows of Wu, interleaved in 16-row groups (gate, up, gate, up
+// per wave) so that a lane holds gate and up of the same element.
+template <int BM>
+struct GateUpTiledProv {
+  const u16* wg;
+  const u16* wu;
+  const u16* xb;
+  const int32_t* perm;
+  int D, i0, row0, rows;
+  __device__ int nseg() const { return 1; }
+  __device__ int seg_chunks() const { return D / 64; }
+  __device__ const u16* w(int r, int) const {
+    const int q = r >> 5, sel = (r >> 4) & 1;
+    const int irow = i0 + q * 16 + (r & 15);
+    return (sel ? wu : wg) + size_t(irow) * D;
+  }
+  __device__ const u16* x(int r, int) const {
+    if (r >= rows) return nullptr;
+    const int t = perm ? perm[row0 + r] : row0 + r;
+    return xb + size_t(t) * D;
+  }
+};
+
+template <int BM>
+__global__ __launch_bounds__(256) void k_gate_up_tiled(ExpertArgs a) {
+  __shared__ TiledSmem<BM> sm;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wn = wave & 1, wm = wave >> 1;
+  const int ntr = a.plan->n_tiles_routed, nts = a.plan->n_tiles_shared;
+  const int nbr = a.I / 64, nbs = a.S > 0 ? (a.S * a.Is) / 64 : 1;
+  const long total = long(ntr) * nbr + long(nts) * nbs;
+  for (long w = blockIdx.x; w < total; w += gridDim.x) {
+    int ti, nb;
+    bool shared;
+    work_item(w, ntr, nts, nbr, nbs, ti, nb, shared);
+    const Tile tl = a.tiles[ti];
+    const int Iv = shared ? a.S * a.Is : a.I;
+    GateUpTiledProv<BM> pv;
+    if (shared) {
+      pv.wg = (const u16*)a.sg;
+      pv.wu = (const u16*)a.su;
+      pv.perm = nullptr;
+    } else {
+      pv.wg = (const u16*)a.wg + size_t(tl.expert) * a.I * a.D;
+      pv.wu = (const u16*)a.wu + size_t(tl.expert) * a.I * a.D;
+      pv.perm = a.perm_token;
+    }
+    pv.xb = (const u16*)a.x;
+    pv.D = a.D;
+    pv.i0 = nb * 64;
+    pv.row0 = tl.row0;
+    pv.rows = tl.rows;
+    f32x4 acc[4][BM / 32];
+    tiled_accumulate<BM>(pv, sm, acc);
+    u16* hb = shared ? (u16*)a.h_sh : (u16*)a.h;
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int jm = 0; jm < BM / 32; ++jm) {
+        const int r = wm * (BM / 2) + jm * 16 + (lane & 15);
+        if (r < tl.rows) {
+          const f32x4 g = acc[2 * q][jm], u = acc[2 * q + 1][jm];
+          const int n = nb * 64 + (2 * wn + q) * 16 + 4 * (lane >> 4);
+          ushort4 hv;
+          hv.x = f32_to_bf16(silu_f32(g[0]) * u[0]);
+          hv.y = f32_to_bf16(silu_f32(g[1]) * u[1]);
+          hv.z = f32_to_bf16(silu_f32(g[2]) * u[2]);
+          hv.w = f32_to_bf16(silu_f32(g[3]) * u[3]);
+          *reinterpret_cast<ushort4*>(hb + size_t(tl.row0 + r) * Iv + n) = hv;
+        }
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// down (bf16): O[row][d] = sum_i h[row][i] Wd[d][i]
+// ---------------------------------------------------------------------------
+
+struct DownProvBase {
+  const u16* wd;     // expert's [D][I] or shared [S][D][Is]
+  const u16* h;      // rows of h for this tile, row stride hs
+  int D, Iv, Is, S, hs, d0, rows;
+  bool shared;
+  __device__ int nseg() const { return shared ? S : 1; }
+  __device__ int seg_chunks() const { return (shared ? Is : Iv) / 64; }
+  __device__ const u16* wrow(int d, int seg) const {
+    if (d >= D) return nullptr;
+    return shared ? wd + size_t(seg) * D * Is + size_t(d) * Is : wd + size_t(d) * Iv;
+  }
+  __device__ const u16* hrow(int r, int seg) const {
+    if (r >= rows) return nullptr;
+    return h + size_t(r) * hs + (shared ? seg * Is : 0);
+  }
+};
+
+struct DownSkinnyProv : DownProvBase {
+  __device__ const u16* w(int, int r, int seg) const { return wrow(d0 + r, seg); }
+  __device__ const u16* x(int r, int seg) const { return hrow(r, seg); }
+};
+
+struct DownTiledProv : DownProvBase {
+  __device__ const u16* w(int r, int seg) const { return wrow(d0 + r, seg); }
+  __device__ const u16* x(int r, int seg) const { return hrow(r, seg); }
+};
+
+template <class P>
+__device__ __forceinline__ void down_setup(const ExpertArgs& a, const Tile& tl, bool shared, P& pv) {
+  pv.D = a.D;
+  pv.S = a.S;
+  pv.Is = a.Is;
+  pv.shared = shared;
+  pv.rows = tl.rows;
+  if (shared) {
+    pv.wd = (const u16*)a.sd;
+    pv.Iv = a.S * a.Is;
+    pv.hs = a.S * a.Is;
+    pv.h = (const u16*)a.h_sh + size_t(tl.row0) * pv.hs;
+  } else {
+    pv.wd = (const u16*)a.wd + size_t(tl.expert) * a.D * a.I;
+    pv.Iv = a.I;
+    pv.hs = a.I;
+    pv.h = (const u16*)a.h + size_t(tl.row0) * pv.hs;
+  }
+}
+
+template <int MT>
+__global__ __launch_bounds__(256) void k_down_skinny(ExpertArgs a) {
+  __shared__ f32x4 red[4 * MT * kWave];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ntr = a.plan->n_tiles_routed, nts = a.plan->n_tiles_shared;
+  const int nb_all = (a.D + 15) / 16;
+  const long total = long(ntr + nts) * nb_all;
+  for (long w = blockIdx.x; w < total; w += gridDim.x) {
+    const int ti = int(w / nb_all), nb = int(w % nb_all);
+    const bool shared = ti >= ntr;
+    const Tile tl = a.tiles[ti];
+    DownSkinnyProv pv;
+    down_setup(a, tl, shared, pv);
+    pv.d0 = nb * 16;
+    f32x4 acc[1][MT];
+    skinny_accumulate<1, MT, (MT >= 4 ? 1 : 4 / MT)>(pv, lane, wave, 4, acc);
+    skinny_reduce<1, MT>(acc, red, lane, wave, 4);
+    float* ob = shared ? a.o_sh : a.o;
+    for (int mt = wave; mt < MT; mt += 4) {
+      f32x4 v = acc[0][0];
+#pragma unroll
+      for (int b = 0; b < MT; ++b)
+        if (b == mt) v = acc[0][b];
+      const int r = 16 * mt + (lane & 15);
+      const int d = nb * 16 + 4 * (lane >> 4);
+      if (r < tl.rows && d < a.D)
+        *reinterpret_cast<float4*>(ob + size_t(tl.row0 + r) * a.D + d) =
+            make_float4(v[0], v[1], v[2], v[3]);
+    }
+  }
+}
+
+template <int BM>
+__global__ __launch_bounds__(256) void k_down_tiled(ExpertArgs a) {
+  __shared__ TiledSmem<BM> sm;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wn = wave & 1, wm = wave >> 1;
+  const int ntr = a.plan->n_tiles_routed, nts = a.plan->n_tiles_shared;
+  const int nb_all = (a.D + kTBN - 1) / kTBN;
+  const long total = long(ntr + nts) * nb_all;
+  for (long w = blockIdx.x; w < total; w += gridDim.x) {
+    const int ti = int(w / nb_all), nb = int(w % nb_all);
+    const bool shared = ti >= ntr;
+    const Tile tl = a.tiles[ti];
+    DownTiledProv pv;
+    down_setup(a, tl, shared, pv);
+    pv.d0 = nb * kTBN;
+    f32x4 acc[4][BM / 32];
+    tiled_accumulate<BM>(pv, sm, acc);
+    float* ob = shared ? a.o_sh : a.o;
+#pragma unroll
+    for (int jn = 0; jn < 4; ++jn)
+#pragma unroll
+      for (int jm = 0; jm < BM / 32; ++jm) {
+        const int r = wm * (BM / 2) + jm * 16 + (lane & 15);
+        const int d = nb * kTBN + wn * 64 + jn * 16 + 4 * (lane >> 4);
+        if (r < tl.rows && d < a.D) {
+          const f32x4 v = acc[jn][jm];
+          *reinterpret_cast<float4*>(ob + size_t(tl.row0 + r) * a.D + d) =
+              make_float4(v[0], v[1], v[2], v[3]);
+        }
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 layers: plain SIMT products over the same tiles (16 rows per tile).
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void k_gate_up_f32(ExpertArgs a) {
+  const int ntr = a.plan->n_tiles_routed, nts = a.plan->n_tiles_shared;
+  const int nbr = a.I / 16, nbs = a.S > 0 ? (a.S * a.Is) / 16 : 1;
+  const long total = long(ntr) * nbr + long(nts) * nbs;
+  const int r = threadIdx.x >> 4, c = threadIdx.x & 15;
+  for (long w = blockIdx.x; w < total; w += gridDim.x) {
+    int ti, nb;
+    bool shared;
+    work_item(w, ntr, nts, nbr, nbs, ti, nb, shared);
+    const Tile tl = a.tiles[ti];
+    if (r >= tl.rows) continue;
+    const int Iv = shared ? a.S * a.Is : a.I;
+    const float* wg = shared ? (const float*)a.sg : (const float*)a.wg + size_t(tl.expert) * a.I * a.D;
+    const float* wu = shared ? (const float*)a.su : (const float*)a.wu + size_t(tl.expert) * a.I * a.D;
+    const int t = shared ? tl.row0 + r : a.perm_token[tl.row0 + r];
+    const float* xr = (const float*)a.x + size_t(t) * a.D;
+    const int n = nb * 16 + c;
+    const float* g_row = wg + size_t(n) * a.D;
+    const float* u_row = wu + size_t(n) * a.D;
+    float g = 0.f, u = 0.f;
+    for (int k = 0; k < a.D; ++k) {
+      g = fmaf(xr[k], g_row[k], g);
+      u = fmaf(xr[k], u_row[k], u);
+    }
+    float* hb = shared ? (float*)a.h_sh : (float*)a.h;
+    hb[size_t(tl.row0 + r) * Iv + n] = silu_f32(g) * u;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_down_f32(ExpertArgs a) {
+  const int ntr = a.plan->n_tiles_routed, nts = a.plan->n_tiles_shared;
+  const int nb_all = (a.D + 15) / 16;
+  const long total = long(ntr + nts) * nb_all;
+  const int r = threadIdx.x >> 4, c = threadIdx.x & 15;
+  for (long w = blockIdx.x; w < total; w += gridDim.x) {
+    const int ti = int(w / nb_all), nb = int(w % nb_all);
+    const bool shared = ti >= ntr;
+    const Tile tl = a.tiles[ti];
+    const int d = nb * 16 + c;
+    if (r >= tl.rows || d >= a.D) continue;
+    float s = 0.f;
+    if (shared) {
+      const int hs = a.S * a.Is;
+      const float* hr = (const float*)a.h_sh + size_t(tl.row0 + r) * hs;
+      for (int sx = 0; sx < a.S; ++sx) {
+        const float* wrow = (const float*)a.sd + size_t(sx) * a.D * a.Is + size_t(d) * a.Is;
+        for (int i = 0; i < a.Is; ++i) s = fmaf(hr[sx * a.Is + i], wrow[i], s);
+      }
+      a.o_sh[size_t(tl.row0 + r) * a.D + d] = s;
+    } else {
+      const float* hr = (const float*)a.h + size_t(tl.row0 + r) * a.I;
+      const float* wrow = (const float*)a.wd + size_t(tl.expert) * a.D * a.I + size_t(d) * a.I;
+      for (int i = 0; i < a.I; ++i) s = fmaf(hr[i], wrow[i], s);
+      a.o[size_t(tl.row0 + r) * a.D + d] = s;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Combine: y[t] = sum_{k=0}^{K-1} g_hat[t][k] O[slot_pos[t][k]] + O_shared[t],
+// accumulated in fp32 in slot order, rounded once.  A token with no surviving
+// pair and no shared expert gets exactly 0.
+// ---------------------------------------------------------------------------
+
+template <bool BF16_OUT>
+__global__ __launch_bounds__(256) void k_combine(int T, int D, int K, const float* __restrict__ gates,
+                                                 const int32_t* __restrict__ slot_pos,
+                                                 const float* __restrict__ o,
+                                                 const float* __restrict__ o_sh, void* __restrict__ y) {
+  __shared__ float s_g[32];
+  __shared__ int32_t s_p[32];
+  const int t = blockIdx.x;
+  if (threadIdx.x < K) {
+    s_g[threadIdx.x] = gates[size_t(t) * K + threadIdx.x];
+    s_p[threadIdx.x] = slot_pos[size_t(t) * K + threadIdx.x];
+  }
+  __syncthreads();
+  for (int d = threadIdx.x * 4; d < D; d += blockDim.x * 4) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k = 0; k < K; ++k) {
+      const int p = s_p[k];
+      if (p < 0) continue;
+      const float g = s_g[k];
+      const float4 v = *reinterpret_cast<const float4*>(o + size_t(p) * D + d);
+      acc.x += g * v.x;
+      acc.y += g * v.y;
+      acc.z += g * v.z;
+      acc.w += g * v.w;
+    }
+    if (o_sh) {
+      const float4 v = *reinterpret_cast<const float4*>(o_sh + size_t(t) * D + d);
+      acc.x += v.x;
+      acc.y += v.y;
+      acc.z += v.z;
+      acc.w += v.w;
+    }
+    if (BF16_OUT) {
+      ushort4 out;
+      out.x = f32_to_bf16(acc.x);
+      out.y = f32_to_bf16(acc.y);
+      out.z = f32_to_bf16(acc.z);
+      out.w = f32_to_bf16(acc.w);
+      *reinterpret_cast<ushort4*>((u16*)y + size_t(t) * D + d) = out;
+    } else {
+      *reinterpret_cast<float4*>((float*)y + size_t(t) * D + d) = acc;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+
+static ExpertArgs expert_args(const beam_moe_layer& L, const void* x, int32_t T, const Ptrs& p) {
+  ExpertArgs a;
+  a.x = x;
+  a.wg = L.w_gate;
+  a.wu = L.w_up;
+  a.wd = L.w_down;
+  a.sg = L.ws_gate;
+  a.su = L.ws_up;
+  a.sd = L.ws_down;
+  a.T = T;
+  a.D = L.D;
+  a.E = L.E;
+  a.I = L.I;
+  a.S = L.n_shared;
+  a.Is = L.I_shared;
+  a.plan = p.plan;
+  a.tiles = p.tiles;
+  a.perm_token = p.perm_token;
+  a.h = p.h;
+  a.h_sh = p.h_shared;
+  a.o = p.o;
+  a.o_sh = p.o_shared;
+  return a;
+}
+
+// Upper bound on the number of tiles the scan can produce.
+static long tile_bound(const beam_moe_layer& L, int32_t T, int tile_rows, long* shared_tiles) {
+  const long pairs = long(T) * L.K;
+  const long routed = (pairs + tile_rows - 1) / tile_rows + std::min<long>(L.E, pairs);
+  *shared_tiles = L.n_shared > 0 ? (T + tile_rows - 1) / tile_rows : 0;
+  return routed;
+}
+
+static unsigned persistent_grid(long items, long cap) {
+  long g = std::min(items, cap);
+  return unsigned(std::max<long>(g, 1));
+}
+
+hipError_t launch_gate_up(const beam_moe_layer& L, const void* x, int32_t T, int tile_rows,
+                          const WsLayout&, const Ptrs& p, hipStream_t s) {
+  const ExpertArgs a = expert_args(L, x, T, p);
+  long nts;
+  const long ntr = tile_bound(L, T, tile_rows, &nts);
+  if (L.dtype == BEAM_F32) {
+    const long items = ntr * (L.I / 16) + nts * (L.n_shared ? (L.n_shared * L.I_shared) / 16 : 0);
+    prof_before("gate_up_f32", s);
+    hipLaunchKernelGGL(k_gate_up_f32, dim3(persistent_grid(items, 2048)), dim3(256), 0, s, a);
+    prof_after(s);
+    return hipGetLastError();
+  }
+  if (tile_rows <= 64) {
+    const long items = ntr * (L.I / 16) + nts * (L.n_shared ? (L.n_shared * L.I_shared) / 16 : 0);
+    const dim3 grid(persistent_grid(items, 2048));
+    prof_before("gate_up_swiglu_skinny", s);
+    if (tile_rows == 16) hipLaunchKernelGGL(k_gate_up_skinny<1>, grid, dim3(256), 0, s, a);
+    else if (tile_rows == 32) hipLaunchKernelGGL(k_gate_up_skinny<2>, grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(k_gate_up_skinny<4>, grid, dim3(256), 0, s, a);
+    prof_after(s);
+  } else {
+    const long items = ntr * (L.I / 64) + nts * (L.n_shared ? (L.n_shared * L.I_shared) / 64 : 0);
+    prof_before("gate_up_swiglu_tiled", s);
+    hipLaunchKernelGGL(k_gate_up_tiled<128>, dim3(persistent_grid(items, 512)), dim3(256), 0, s, a);
+    prof_after(s);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_down(const beam_moe_layer& L, int32_t T, int tile_rows, const WsLayout&,
+                       const Ptrs& p, hipStream_t s) {
+  const ExpertArgs a = expert_args(L, nullptr, T, p);
+  long nts;
+  const long ntr = tile_bound(L, T, tile_rows, &nts);
+  if (L.dtype == BEAM_F32) {
+    const long items = (ntr + nts) * ((L.D + 15) / 16);
+    prof_before("down_f32", s);
+    hipLaunchKernelGGL(k_down_f32, dim3(persistent_grid(items, 2048)), dim3(256), 0, s, a);
+    prof_after(s);
+    return hipGetLastError();
+  }
+  if (tile_rows <= 64) {
+    const long items = (ntr + nts) * ((L.D + 15) / 16);
+    const dim3 grid(persistent_grid(items, 2048));
+    prof_before("down_skinny", s);
+    if (tile_rows == 16) hipLaunchKernelGGL(k_down_skinny<1>, grid, dim3(256), 0, s, a);
+    else if (tile_rows == 32) hipLaunchKernelGGL(k_down_skinny<2>, grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(k_down_skinny<4>, grid, dim3(256), 0, s, a);
+    prof_after(s);
+  } else {
+    const long items = (ntr + nts) * ((L.D + kTBN - 1) / kTBN);
+    prof_before("down_tiled", s);
+    hipLaunchKernelGGL(k_down_tiled<128>, dim3(persistent_grid(items, 512)), dim3(256), 0, s, a);
+    prof_after(s);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const beam_moe_layer& L, int32_t T, const Ptrs& p, void* y,
+                          hipStream_t s) {
+  const float* osh = L.n_shared > 0 ? p.o_shared : nullptr;
+  prof_before("combine", s);
+  if (L.dtype == BEAM_F32)
+    hipLaunchKernelGGL(k_combine<false>, dim3(unsigned(T)), dim3(256), 0, s, T, L.D, L.K, p.gates,
+                       p.slot_pos, p.o, osh, y);
+  else
+    hipLaunchKernelGGL(k_combine<true>, dim3(unsigned(T)), dim3(256), 0, s, T, L.D, L.K, p.gates,
+                       p.slot_pos, p.o, osh, y);
+  prof_after(s);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Plain copy (counter calibration)
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void k_copy16(uint4* __restrict__ dst,
+                                                const uint4* __restrict__ src, long n) {
+  for (long i = long(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += long(gridDim.x) * blockDim.x)
+    dst[i] = src[i];
+}
+
+hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t s) {
+  const long n = long(bytes / 16);
+  const long blocks = std::min<long>((n + 255) / 256, 4096);
+  prof_before("copy16", s);
+  hipLaunchKernelGGL(k_copy16, dim3(unsigned(std::max<long>(blocks, 1))), dim3(256), 0, s,
+                     (uint4*)dst, (const uint4*)src, n);
+  prof_after(s);
+  return hipGetLastError();
+}
+
+}  // namespace beam

@@ -1,0 +1,84 @@
+"""Device-memory plumbing for the binding: uploads host parameter arrays to
+torch device tensors, fills the layer descriptor and sizes workspaces.
+
+Host arrays follow one convention: bf16 values are uint16 bit patterns,
+fp32 values are float32.  Nothing here computes any part of the layer.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import BEAM_BF16, BEAM_F32, beam_moe_workspace_size, make_layer, make_route_out
+
+
+def to_device(a: np.ndarray, device="cuda") -> torch.Tensor:
+    """Upload a host array: uint16 -> torch.bfloat16 (same bits), float32 -> float32."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+    if a.dtype == np.float32:
+        return torch.from_numpy(a).to(device)
+    raise TypeError(f"unsupported host dtype {a.dtype}")
+
+
+def to_host_bits(t: torch.Tensor) -> np.ndarray:
+    """Download: bfloat16 -> uint16 bit patterns, float32 -> float32."""
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+class DeviceLayer:
+    """Device copy of a layer's parameters plus its C descriptor.
+
+    `host` is any object with the attributes of the parameter set: cfg (with
+    D, E, K, I, S, I_s, dtype), w_router, w_mask, b_router, b_mask, w_gate,
+    w_up, w_down, ws_gate, ws_up, ws_down.
+    """
+
+    def __init__(self, host, device="cuda"):
+        c = host.cfg
+        self.cfg = c
+        self.device = device
+        up = lambda a: None if a is None else to_device(a, device)  # noqa: E731
+        self.t = {name: up(getattr(host, name)) for name in
+                  ("w_router", "w_mask", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")}
+        self.t["b_router"] = up(host.b_router)
+        self.t["b_mask"] = up(host.b_mask)
+        self.dtype_code = BEAM_F32 if c.dtype == "f32" else BEAM_BF16
+        self.torch_dtype = torch.float32 if c.dtype == "f32" else torch.bfloat16
+        self.desc = self._desc(self.t)
+
+    def _desc(self, t):
+        c = self.cfg
+        return make_layer(c.D, c.E, c.K, c.I, self.dtype_code, t["w_router"], t["w_mask"],
+                          t["w_gate"], t["w_up"], t["w_down"], b_router=t["b_router"],
+                          b_mask=t["b_mask"], n_shared=c.S, I_shared=c.I_s if c.S else 0,
+                          ws_gate=t["ws_gate"], ws_up=t["ws_up"], ws_down=t["ws_down"])
+
+    def replicas(self, n: int):
+        """n extra copies of the expert weights at distinct addresses (same
+        values); returns their descriptors.  Used to keep repeated calls from
+        being served by the last-level cache."""
+        out = []
+        for _ in range(n):
+            t = {k: (None if v is None else v.clone()) for k, v in self.t.items()}
+            out.append((t, self._desc(t)))
+        return out
+
+    def workspace(self, T_max: int) -> torch.Tensor:
+        n = beam_moe_workspace_size(self.desc, T_max)
+        if n == 0 and T_max > 0:
+            raise ValueError("invalid layer for workspace sizing")
+        return torch.empty(max(n, 256), dtype=torch.uint8, device=self.device)
+
+    def route_buffers(self, T: int):
+        c = self.cfg
+        d = self.device
+        bufs = dict(topk_idx=torch.empty(T, c.K, dtype=torch.int32, device=d),
+                    gates=torch.empty(T, c.K, dtype=torch.float32, device=d),
+                    mask=torch.empty(T, dtype=torch.int32, device=d),
+                    expert_count=torch.empty(c.E, dtype=torch.int32, device=d))
+        return bufs, make_route_out(**bufs)

@@ -1,0 +1,149 @@
+/*
+ * beam_moe.h -- C ABI of the BEAM masked-MoE layer forward pass on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * What the layer computes (BEAM page on aitrends.kr, "BEAM: Dynamic MoE
+ * 라우팅을 위한 Binary Expert Activation Masking", method paragraph, Steps
+ * 1-4, restated in its architecture paragraph):
+ *
+ *   Step 1  r = x Wr^T (+ b_r); keep the K largest r; g = softmax over them.
+ *   Step 2  raw mask m_hat = sigmoid(z), z = x Wm^T (+ b_m), one mask logit
+ *           per expert, read at the K candidates.
+ *   Step 3  m = 1 when m_hat >= 0.5 (decided as z >= 0), else 0.
+ *   Step 4  g_hat = g * m (not renormalised); y = sum_k g_hat_k E_k(x).
+ *
+ * Only the (token, expert) pairs with m = 1 run their expert (the ai-feeds.com
+ * summary, section on inference: experts whose mask is 0 skip their FFN).
+ * Experts are SwiGLU FFNs, E(x) = Wd (silu(Wg x) * (Wu x)).  Shared experts,
+ * when the layer has them, are added to y with gate 1 and are never masked
+ * (they are what the aitrends.kr page's limitation C refers to).
+ *
+ * Conventions for every call below:
+ *   - All tensor pointers are DEVICE pointers, owned by the caller, 16-byte
+ *     aligned, row-major and densely packed.  The library allocates nothing
+ *     and keeps no state between calls except the optional profiler.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  route and
+ *     forward only enqueue work: they never synchronise the host.
+ *   - Arguments are validated before anything is launched; on any error
+ *     nothing is written.  A failed kernel launch returns BEAM_ERR_HIP.
+ *   - T = 0 is a no-op returning BEAM_OK.
+ *   - Results are bit-identical from run to run for identical inputs.
+ *   - One workspace per concurrently running call: two calls in flight on the
+ *     same workspace (different streams) race.
+ */
+#ifndef BEAM_MOE_H
+#define BEAM_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BEAM_OK = 0,
+  BEAM_ERR_INVALID_ARG = -1,  /* null/misaligned pointer, bad shape or size  */
+  BEAM_ERR_UNSUPPORTED = -2,  /* valid but outside what the kernels handle   */
+  BEAM_ERR_WORKSPACE = -3,    /* workspace pointer null or too small         */
+  BEAM_ERR_HIP = -4           /* a HIP runtime call or kernel launch failed  */
+} beam_status;
+
+typedef enum { BEAM_F32 = 0, BEAM_BF16 = 1 } beam_dtype;
+
+/* Layer description.  Shapes: D hidden, E routed experts, K top-K, I routed
+ * expert intermediate size, n_shared shared experts of intermediate size
+ * I_shared.  Supported: 1 <= K <= min(E, 32), E <= 1024, D, I and I_shared
+ * multiples of 64, D <= 16384.  Every weight tensor has the layer's dtype.  */
+typedef struct {
+  int32_t D, E, K, I, n_shared, I_shared;
+  int32_t dtype;               /* beam_dtype                                  */
+  const void *w_router;        /* [E][D]  router weights Wr                   */
+  const void *w_mask;          /* [E][D]  mask-router weights Wm              */
+  const float *b_router;       /* [E] fp32 router bias, or NULL (= 0)         */
+  const float *b_mask;         /* [E] fp32 mask-router bias, or NULL (= 0)    */
+  const void *w_gate;          /* [E][I][D]  Wg                               */
+  const void *w_up;            /* [E][I][D]  Wu                               */
+  const void *w_down;          /* [E][D][I]  Wd                               */
+  const void *ws_gate;         /* [n_shared][I_shared][D], NULL if n_shared=0 */
+  const void *ws_up;           /* [n_shared][I_shared][D]                     */
+  const void *ws_down;         /* [n_shared][D][I_shared]                     */
+} beam_moe_layer;
+
+/* Routing results (device pointers, caller-owned). */
+typedef struct {
+  int32_t *topk_idx;      /* [T][K] experts by descending router logit; equal
+                             logits are ordered by lower expert index         */
+  float *gates;           /* [T][K] masked gates g_hat (0 where m = 0)        */
+  uint32_t *mask;         /* [T] bit k = m of slot k                          */
+  int32_t *expert_count;  /* [E] surviving pairs per expert                   */
+} beam_route_out;
+
+/* Host-side work accounting (beam_moe_stats / beam_moe_stats_host). */
+typedef struct {
+  int32_t T, E, K, active_experts;
+  int64_t active_pairs;               /* sum of expert_count                  */
+  double avg_k;                       /* active_pairs / T                     */
+  double flops_routed;                /* 6 D I active_pairs                   */
+  double flops_topk_routed;           /* 6 D I T K (plain top-K MoE)          */
+  double flops_shared;                /* 6 D I_shared n_shared T              */
+  double flops_router;                /* 4 E D T                              */
+  double flops_reduction;             /* 1 - flops_routed / flops_topk_routed */
+  double bytes_active_expert_weights; /* experts with a pair + shared, once   */
+  double bytes_total_min;             /* + router weights + x + y             */
+} beam_stats;
+
+/* Bytes of workspace that route/forward need for batches of up to T_max
+ * tokens.  Returns 0 for an invalid layer or T_max < 0. */
+size_t beam_moe_workspace_size(const beam_moe_layer *layer, int32_t T_max);
+
+/* Steps 1-3 of the method and the per-expert counts: fills every field of
+ * *out (all four pointers required).  x: [T][D] in the layer dtype.
+ * ws: device workspace of at least beam_moe_workspace_size(layer, T) bytes.  */
+int beam_moe_route(const beam_moe_layer *layer, const void *x, int32_t T,
+                   const beam_route_out *out, void *ws, size_t ws_bytes,
+                   void *stream);
+
+/* The whole layer, Steps 1-4: y [T][D] in the layer dtype.  out may be NULL
+ * (routing is then kept in the workspace only); if given, all four of its
+ * pointers are filled as by beam_moe_route.  y must not alias x. */
+int beam_moe_forward(const beam_moe_layer *layer, const void *x, int32_t T,
+                     void *y, const beam_route_out *out, void *ws,
+                     size_t ws_bytes, void *stream);
+
+/* Work accounting from the device expert counts of a route/forward call:
+ * copies expert_count [E] to the host and SYNCHRONISES the stream. */
+int beam_moe_stats(const beam_moe_layer *layer, const int32_t *expert_count,
+                   int32_t T, beam_stats *host_out, void *stream);
+
+/* Same accounting from host-resident counts [E]; touches no GPU. */
+int beam_moe_stats_host(const beam_moe_layer *layer,
+                        const int32_t *expert_count_host, int32_t T,
+                        beam_stats *host_out);
+
+/* Static, human-readable name of a status code. */
+const char *beam_status_str(int status);
+
+/* ---- Measurement helpers (not part of the layer) ------------------------ */
+
+/* Per-kernel timing: while enabled, every kernel that route/forward launch is
+ * bracketed by a pair of hipEvents recorded on the call's stream.  Up to
+ * max_launches launches are recorded; later ones run untimed.  Not thread
+ * safe; meant for a single benchmarking thread.  Host-side setup only. */
+int beam_profile_begin(int32_t max_launches);
+
+/* Waits for the recorded events, then reports per kernel name: number of
+ * timed launches and their summed duration in ms.  names[i] receives a
+ * pointer to a static string.  Returns the number of distinct kernels
+ * (capped at max_out) and disables the profiler. */
+int beam_profile_end(const char **names, int32_t *launches, double *total_ms,
+                     int32_t max_out);
+
+/* Plain device copy kernel (16-byte vector loads and stores) of `bytes`
+ * (multiple of 16) from src to dst; used to calibrate memory counters. */
+int beam_copy_kernel(void *dst, const void *src, size_t bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BEAM_MOE_H */

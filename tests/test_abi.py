@@ -1,0 +1,140 @@
+"""The C-ABI library on the host: it loads, exports every declared symbol,
+sizes workspaces, validates arguments before touching any GPU, and its
+host-side work accounting matches the oracle's."""
+import ctypes
+import glob
+import os
+import re
+
+import numpy as np
+import pytest
+
+import dynamic_expert_masking_amd as dm
+import oracle
+import synth
+from common import small_config
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+pytestmark = pytest.mark.skipif(not os.path.exists(dm.LIB_PATH), reason="library not built")
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        src = open(h).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        for m in re.finditer(r"^[A-Za-z_][\w \*]*?\b(beam_\w+)\s*\(", src, flags=re.M):
+            names.add(m.group(1))
+    return sorted(names)
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert "beam_moe_forward" in names and "beam_moe_route" in names and "beam_moe_stats" in names
+    lib = ctypes.CDLL(dm.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+FAKE = 0x10000   # aligned, never dereferenced: validation fails before any use
+
+
+def fake_layer(**kw):
+    p = dict(D=128, E=8, K=2, I=256, dtype=dm.BEAM_BF16, w_router=FAKE, w_mask=FAKE,
+             w_gate=FAKE, w_up=FAKE, w_down=FAKE)
+    p.update(kw)
+    return dm.make_layer(**p)
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4):
+        assert dm.beam_status_str(s).startswith("BEAM_")
+    assert "unknown" in dm.beam_status_str(7)
+
+
+def test_workspace_size_monotone_and_invalid():
+    L = fake_layer()
+    sizes = [dm.beam_moe_workspace_size(L, T) for T in (0, 1, 64, 65, 4096)]
+    assert all(a <= b for a, b in zip(sizes, sizes[1:])) and sizes[-1] > sizes[1] > 0
+    assert dm.beam_moe_workspace_size(fake_layer(K=9), 16) == 0          # K > E
+    assert dm.beam_moe_workspace_size(fake_layer(D=100), 16) == 0        # D % 64
+    assert dm.beam_moe_workspace_size(L, -1) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=0), dm.BEAM_ERR_INVALID_ARG),
+    (dict(K=9), dm.BEAM_ERR_INVALID_ARG),
+    (dict(E=40, K=33), dm.BEAM_ERR_UNSUPPORTED),
+    (dict(E=2000, K=4), dm.BEAM_ERR_UNSUPPORTED),
+    (dict(D=96), dm.BEAM_ERR_UNSUPPORTED),
+    (dict(I=100), dm.BEAM_ERR_UNSUPPORTED),
+    (dict(dtype=5), dm.BEAM_ERR_INVALID_ARG),
+    (dict(w_gate=None), dm.BEAM_ERR_INVALID_ARG),
+    (dict(w_up=FAKE + 8), dm.BEAM_ERR_INVALID_ARG),
+    (dict(n_shared=2, I_shared=0), dm.BEAM_ERR_INVALID_ARG),
+    (dict(n_shared=1, I_shared=64), dm.BEAM_ERR_INVALID_ARG),       # shared pointers missing
+    (dict(n_shared=1, I_shared=96, ws_gate=FAKE, ws_up=FAKE, ws_down=FAKE), dm.BEAM_ERR_UNSUPPORTED),
+])
+def test_forward_rejects_bad_layers(kw, status):
+    L = fake_layer(**kw)
+    rc = dm.lib().beam_moe_forward(ctypes.byref(L), FAKE, 4, FAKE * 2, None, FAKE * 3, 1 << 40, None)
+    assert rc == status
+
+
+def test_forward_rejects_bad_calls():
+    L = fake_layer()
+    f = dm.lib().beam_moe_forward
+    big = 1 << 40
+    assert f(ctypes.byref(L), FAKE, -1, FAKE, None, FAKE, big, None) == dm.BEAM_ERR_INVALID_ARG
+    assert f(ctypes.byref(L), None, 4, FAKE, None, FAKE, big, None) == dm.BEAM_ERR_INVALID_ARG
+    assert f(ctypes.byref(L), FAKE + 4, 4, FAKE * 2, None, FAKE, big, None) == dm.BEAM_ERR_INVALID_ARG
+    assert f(ctypes.byref(L), FAKE, 4, None, None, FAKE, big, None) == dm.BEAM_ERR_INVALID_ARG
+    assert f(ctypes.byref(L), FAKE, 4, FAKE, None, FAKE * 3, big, None) == dm.BEAM_ERR_INVALID_ARG  # y == x
+    assert f(ctypes.byref(L), FAKE, 4, FAKE * 2, None, None, big, None) == dm.BEAM_ERR_WORKSPACE
+    need = dm.beam_moe_workspace_size(L, 4)
+    assert f(ctypes.byref(L), FAKE, 4, FAKE * 2, None, FAKE * 3, need - 1, None) == dm.BEAM_ERR_WORKSPACE
+    bad_out = dm.beam_route_out(FAKE, None, FAKE, FAKE)
+    assert f(ctypes.byref(L), FAKE, 4, FAKE * 2, ctypes.byref(bad_out), FAKE * 3, big, None) \
+        == dm.BEAM_ERR_INVALID_ARG
+    # T = 0 is a no-op, even with no workspace
+    assert f(ctypes.byref(L), FAKE, 0, FAKE * 2, None, None, 0, None) == dm.BEAM_OK
+
+
+def test_route_requires_all_outputs():
+    L = fake_layer()
+    r = dm.lib().beam_moe_route
+    assert r(ctypes.byref(L), FAKE, 4, None, FAKE, 1 << 40, None) == dm.BEAM_ERR_INVALID_ARG
+    out = dm.beam_route_out(FAKE, FAKE, None, FAKE)
+    assert r(ctypes.byref(L), FAKE, 4, ctypes.byref(out), FAKE, 1 << 40, None) == dm.BEAM_ERR_INVALID_ARG
+
+
+def test_profile_and_copy_argument_checks():
+    assert dm.lib().beam_profile_begin(0) == dm.BEAM_ERR_INVALID_ARG
+    assert dm.lib().beam_profile_end(None, None, None, 0) == dm.BEAM_ERR_INVALID_ARG
+    assert dm.lib().beam_copy_kernel(FAKE, FAKE, 15, None) == dm.BEAM_ERR_INVALID_ARG
+    assert dm.lib().beam_copy_kernel(FAKE, FAKE, 0, None) == dm.BEAM_OK
+
+
+@pytest.mark.parametrize("name", synth.CONFIG_ORDER)
+def test_stats_host_matches_oracle(name):
+    cfg = synth.CONFIGS[name]
+    rng = np.random.default_rng(11)
+    T = cfg.tokens[-1]
+    counts = rng.integers(0, 5, size=cfg.E)
+    counts[rng.random(cfg.E) < 0.3] = 0
+    kw = dict(D=cfg.D, E=cfg.E, K=cfg.K, I=cfg.I,
+              dtype=dm.BEAM_F32 if cfg.dtype == "f32" else dm.BEAM_BF16)
+    if cfg.S:
+        kw.update(n_shared=cfg.S, I_shared=cfg.I_s, ws_gate=FAKE, ws_up=FAKE, ws_down=FAKE)
+    L = fake_layer(**kw)
+    got = dm.beam_moe_stats_host(L, list(counts), T)
+    ref = oracle.layer_stats(cfg, counts, T)
+    for k, v in ref.items():
+        assert got[k] == pytest.approx(v, rel=1e-12, abs=0), k
+
+
+def test_stats_host_rejects_negative_counts():
+    L = fake_layer()
+    with pytest.raises(dm.BeamError):
+        dm.beam_moe_stats_host(L, [1, -1, 0, 0, 0, 0, 0, 0], 4)
