@@ -1,0 +1,265 @@
+#!/usr/bin/env python3
+"""Benchmark of the BEAM masked-MoE layer forward on one MI355X.
+
+Workload (default): the DeepSeek-V2-Lite-shaped decode layer -- D=2048, 64
+routed experts, top-6, expert intermediate 1408, 2 shared experts of 1408,
+bf16, mask bias for Avg-K ~3 -- at a decode batch of T=64 tokens.  One step
+is one beam_moe_forward call (router, top-K/mask, compaction, grouped SwiGLU
+gate/up, grouped down, combine) on a fresh batch x from a pool of seeded
+synthetic batches, with the layer's weights taken round-robin from enough
+copies that more than 1 GB is read between two uses of the same copy (so the
+256 MB last-level cache cannot serve them).
+
+Prints one JSON line.  `value` is layer tokens/s = T / (time per step).  The
+`roofline` object covers the dominant kernel (grouped gate/up): algorithmic
+bytes per launch (the gate and up weights of the experts that received at
+least one pair, plus the shared experts' gate and up weights) divided by its
+mean launch time from hipEvents recorded around each launch on the call's
+stream during a second timed pass.  `cpu_baseline` times the float64 oracle
+on the host on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+DOMINANT = "gate_up_swiglu"    # prefix of the dominant kernel's names
+KERNEL_SOURCES = ("dynamic_expert_masking_amd/csrc/experts.hip",
+                  "dynamic_expert_masking_amd/csrc/gemm_engines.h",
+                  "dynamic_expert_masking_amd/csrc/device_common.h")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--config", default="dsv2lite_decode")
+    p.add_argument("--tokens", type=int, default=None, help="batch size (default: 64 for decode)")
+    p.add_argument("--copies", type=int, default=0, help="weight copies rotated (0 = auto)")
+    p.add_argument("--pool", type=int, default=16, help="distinct input batches")
+    p.add_argument("--no-sweep", action="store_true", help="skip the other batch sizes")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--calibrate-copy", type=int, default=0,
+                   help="only run the plain copy kernel on this many MiB (counter calibration)")
+    return p.parse_args()
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, or None when absent or taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{DOMINANT}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_sources_sha256_16") != kernel_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import dynamic_expert_masking_amd as dm
+    from dynamic_expert_masking_amd.device import DeviceLayer, to_device
+    import synth
+
+    dev = "cuda"
+    torch.cuda.init()
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty(n, dtype=torch.uint8, device=dev)
+        for _ in range(5):
+            dm.beam_copy_kernel(b, a, n, sh)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration_copy_bytes": n, "launches": 5}))
+        return
+
+    cfg = synth.CONFIGS[args.config]
+    T = args.tokens or (64 if args.config == "dsv2lite_decode" else cfg.tokens[-1])
+    t0 = time.time()
+    host = synth.make_layer(cfg)
+    dl = DeviceLayer(host, dev)
+    per_copy = sum(v.numel() * v.element_size() for k, v in dl.t.items() if v is not None)
+    copies = args.copies or max(2, min(16, int(np.ceil(1.5e9 / max(1, per_copy))) + 1))
+    reps = [(dl.t, dl.desc)] + dl.replicas(copies - 1)
+    print(f"[bench] {cfg.name}: layer {per_copy / 1e9:.2f} GB x {copies} copies "
+          f"(setup {time.time() - t0:.1f}s)", file=sys.stderr, flush=True)
+
+    def run_T(Tb: int, steps: int, warmup: int, profile: bool):
+        xs = [to_device(synth.make_x(cfg, Tb, f"bench{i}"), dev) for i in range(args.pool)]
+        y = torch.empty(Tb, cfg.D, dtype=dl.torch_dtype, device=dev)
+        ws = dl.workspace(Tb)
+        counts = torch.empty(cfg.E, dtype=torch.int32, device=dev)
+        # per-batch work accounting (outside any timed region)
+        stats = []
+        for i in range(args.pool):
+            bufs, out = dl.route_buffers(Tb)
+            dm.beam_moe_route(dl.desc, xs[i], Tb, out, ws, ws.numel(), sh)
+            stats.append(dm.beam_moe_stats(dl.desc, bufs["expert_count"], Tb, sh))
+        del counts
+
+        def step(i):
+            _, desc = reps[i % len(reps)]
+            dm.beam_moe_forward(desc, xs[i % args.pool], Tb, y, None, ws, ws.numel(), sh)
+
+        for i in range(warmup):
+            step(i)
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for i in range(steps):
+            step(warmup + i)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t_start
+        res = {"T": Tb, "ms_per_step": elapsed * 1e3 / steps}
+        used = [stats[(warmup + i) % args.pool] for i in range(steps)]
+        res["bytes_per_step"] = float(np.mean([s["bytes_total_min"] for s in used]))
+        res["weight_bytes_per_step"] = float(np.mean([s["bytes_active_expert_weights"] for s in used]))
+        res["flops_per_step"] = float(np.mean([s["flops_routed"] + s["flops_shared"] + s["flops_router"]
+                                               for s in used]))
+        res["avg_k"] = float(np.mean([s["avg_k"] for s in used]))
+        res["active_experts"] = float(np.mean([s["active_experts"] for s in used]))
+        if profile:
+            # second timed pass with a hipEvent pair around every launch
+            dm.beam_profile_begin(steps * 16)
+            torch.cuda.synchronize()
+            for i in range(steps):
+                step(warmup + i)
+            torch.cuda.synchronize()
+            prof = dm.beam_profile_end(64)
+            res["kernels"] = {k: {"launches": n, "mean_us": ms * 1e3 / max(n, 1)}
+                              for k, (n, ms) in prof.items()}
+            # algorithmic bytes of the gate/up launches: gate+up weights of the
+            # active routed experts plus the shared experts
+            D, I = cfg.D, cfg.I
+            elt = 4 if cfg.dtype == "f32" else 2
+            gu = [2 * D * I * elt * s["active_experts"] + 2 * D * cfg.I_s * elt * cfg.S for s in used]
+            res["gate_up_alg_bytes"] = float(np.mean(gu))
+        return res
+
+    main_res = run_T(T, args.steps, args.warmup, profile=True)
+    ms = main_res["ms_per_step"]
+    value = T / (ms / 1e3)
+
+    dom = [k for k in main_res["kernels"] if k.startswith(DOMINANT)]
+    roofline = None
+    if dom:
+        kname = dom[0]
+        mean_us = main_res["kernels"][kname]["mean_us"]
+        achieved = main_res["gate_up_alg_bytes"] / (mean_us * 1e-6) / 1e9
+        workload = f"{cfg.name}_T{T}"
+        traffic = read_traffic(workload)
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": traffic, "kernel": kname, "mean_launch_us": round(mean_us, 2),
+                    "alg_bytes_per_launch": main_res["gate_up_alg_bytes"]}
+
+    sweep = []
+    if not args.no_sweep:
+        for Tb in cfg.tokens:
+            if Tb == T:
+                continue
+            r = run_T(Tb, max(10, args.steps // 2), args.warmup, profile=False)
+            sweep.append({"T": Tb, "tokens_per_s": round(Tb / (r["ms_per_step"] / 1e3), 1),
+                          "ms_per_step": round(r["ms_per_step"], 4),
+                          "layer_hbm_gbs": round(r["bytes_per_step"] / (r["ms_per_step"] / 1e3) / 1e9, 1),
+                          "avg_k": round(r["avg_k"], 3)})
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(cfg, host, T, args)
+
+    layer_gbs = main_res["bytes_per_step"] / (ms / 1e3) / 1e9
+    out = {
+        "metric": "masked-MoE layer tokens/s (decode: HBM GB/s on active-expert bytes)",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded; x~N(0,1), weights~N(0,1/D))",
+        "config": {"workload": f"{cfg.name}: D={cfg.D} E={cfg.E} K={cfg.K} I={cfg.I} "
+                               f"shared={cfg.S}x{cfg.I_s} T={T}",
+                   "tokens": T, "weight_copies": copies, "input_pool": args.pool},
+        "layer": {"avg_k": round(main_res["avg_k"], 3),
+                  "active_experts": round(main_res["active_experts"], 2),
+                  "alg_bytes_per_step": main_res["bytes_per_step"],
+                  "hbm_gbs": round(layer_gbs, 1),
+                  "frac_hbm_peak": round(layer_gbs / HBM_PEAK_GBS, 4),
+                  "mfma_frac_peak": round(main_res["flops_per_step"] / (ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS, 5),
+                  "kernels_mean_us": {k: round(v["mean_us"], 2) for k, v in main_res["kernels"].items()}},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "sweep": sweep,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(cfg, host, T, args):
+    """The oracle, as it stands, on the host: whole-layer forward over
+    successive batches of the same workload until cpu-seconds have passed."""
+    import numpy as np
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    done = 0
+    t0 = time.perf_counter()
+    batches = 0
+    while time.perf_counter() - t0 < args.cpu_seconds and batches < 8:
+        x = synth.make_x(cfg, T, f"bench{batches % args.pool}")
+        oracle.forward(host, x)
+        done += T
+        batches += 1
+    el = time.perf_counter() - t0
+    return {"value": round(done / el, 2), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{batches} whole batches of T={T} ({done} tokens) of the same workload, "
+                      f"float64 numpy, {el:.1f}s"}
+
+
+if __name__ == "__main__":
+    main()

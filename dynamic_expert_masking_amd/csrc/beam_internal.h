@@ -40,6 +40,8 @@ struct WsLayout {
   int32_t max_tiles;
 };
 
+// Number of k slices of the router logits (partial sums added by selection).
+int router_ksplit(const beam_moe_layer& L, int32_t T);
 // Row-tile height of the expert kernels (multiple of 16).
 int expert_tile_rows(const beam_moe_layer& L, int32_t T);
 WsLayout workspace_layout(const beam_moe_layer& L, int32_t T);
@@ -66,9 +68,12 @@ struct Ptrs {
 };
 
 // ---- launchers (return hipSuccess or the launch error) ----
-hipError_t launch_router_logits(const beam_moe_layer& L, const void* x, int32_t T, float* logits,
+hipError_t launch_router_logits(const beam_moe_layer& L, const void* x, int32_t T, float* part,
                                 hipStream_t s);
-hipError_t launch_select(const beam_moe_layer& L, int32_t T, const Ptrs& p, hipStream_t s);
+hipError_t launch_select(const beam_moe_layer& L, int32_t T, int tile_rows, const Ptrs& p,
+                         hipStream_t s);
+// True when the selection kernel also builds the plan and places the pairs.
+bool select_builds_plan(int32_t T);
 hipError_t launch_scan(const beam_moe_layer& L, int32_t T, int tile_rows, const Ptrs& p,
                        hipStream_t s);
 hipError_t launch_scatter(const beam_moe_layer& L, int32_t T, const Ptrs& p, hipStream_t s);

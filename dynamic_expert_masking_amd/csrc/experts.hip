@@ -80,56 +80,59 @@ struct GateUpSkinnyProv {
   __device__ const u16* x(int r, int) const { return x_row(r); }
 };
 
-template <int MT>
-__global__ __launch_bounds__(256) void k_gate_up_skinny(ExpertArgs a) {
-  __shared__ f32x4 red[4 * 2 * MT * kWave];
+// Skinny: one workgroup of NW waves per (tile, 16-row n-block) item; the
+// waves split the k range.  The grid covers an upper bound on the item count;
+// workgroups past the device-side count exit at once.
+template <int MT, int NW>
+__global__ __launch_bounds__(NW * 64) void k_gate_up_skinny(ExpertArgs a) {
+  __shared__ f32x4 red[NW * 2 * MT * kWave];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ntr = a.plan->n_tiles_routed, nts = a.plan->n_tiles_shared;
   const int nbr = a.I / 16, nbs = a.S > 0 ? (a.S * a.Is) / 16 : 1;
   const long total = long(ntr) * nbr + long(nts) * nbs;
-  for (long w = blockIdx.x; w < total; w += gridDim.x) {
-    int ti, nb;
-    bool shared;
-    work_item(w, ntr, nts, nbr, nbs, ti, nb, shared);
-    const Tile tl = a.tiles[ti];
-    const int Iv = shared ? a.S * a.Is : a.I;
-    GateUpSkinnyProv pv;
-    if (shared) {
-      pv.wg = (const u16*)a.sg;
-      pv.wu = (const u16*)a.su;
-      pv.perm = nullptr;
-    } else {
-      pv.wg = (const u16*)a.wg + size_t(tl.expert) * a.I * a.D;
-      pv.wu = (const u16*)a.wu + size_t(tl.expert) * a.I * a.D;
-      pv.perm = a.perm_token;
-    }
-    pv.xb = (const u16*)a.x;
-    pv.D = a.D;
-    pv.n0 = nb * 16;
-    pv.row0 = tl.row0;
-    pv.rows = tl.rows;
-    f32x4 acc[2][MT];
-    skinny_accumulate<2, MT, (MT >= 4 ? 1 : 4 / MT)>(pv, lane, wave, 4, acc);
-    skinny_reduce<2, MT>(acc, red, lane, wave, 4);
-    u16* hb = shared ? (u16*)a.h_sh : (u16*)a.h;
-    for (int mt = wave; mt < MT; mt += 4) {
-      f32x4 g = acc[0][0], u = acc[1][0];
+  const long w = blockIdx.x;
+  if (w >= total) return;
+  int ti, nb;
+  bool shared;
+  work_item(w, ntr, nts, nbr, nbs, ti, nb, shared);
+  const Tile tl = a.tiles[ti];
+  const int Iv = shared ? a.S * a.Is : a.I;
+  GateUpSkinnyProv pv;
+  if (shared) {
+    pv.wg = (const u16*)a.sg;
+    pv.wu = (const u16*)a.su;
+    pv.perm = nullptr;
+  } else {
+    pv.wg = (const u16*)a.wg + size_t(tl.expert) * a.I * a.D;
+    pv.wu = (const u16*)a.wu + size_t(tl.expert) * a.I * a.D;
+    pv.perm = a.perm_token;
+  }
+  pv.xb = (const u16*)a.x;
+  pv.D = a.D;
+  pv.n0 = nb * 16;
+  pv.row0 = tl.row0;
+  pv.rows = tl.rows;
+  f32x4 acc[2][MT];
+  skinny_accumulate<2, MT, (MT >= 4 ? 1 : 4 / MT)>(pv, lane, wave, NW, acc);
+  skinny_reduce<2, MT>(acc, red, lane, wave, NW);
+  u16* hb = shared ? (u16*)a.h_sh : (u16*)a.h;
+  for (int mt = wave; mt < MT; mt += NW) {
+    f32x4 g = acc[0][0], u = acc[1][0];
 #pragma unroll
-      for (int b = 0; b < MT; ++b)
-        if (b == mt) {
-          g = acc[0][b];
-          u = acc[1][b];
-        }
-      const int r = 16 * mt + (lane & 15);
-      if (r < tl.rows) {
-        const int n = nb * 16 + 4 * (lane >> 4);
-        ushort4 hv;
-        hv.x = f32_to_bf16(silu_f32(g[0]) * u[0]);
-        hv.y = f32_to_bf16(silu_f32(g[1]) * u[1]);
-        hv.z = f32_to_bf16(silu_f32(g[2]) * u[2]);
-        hv.w = f32_to_bf16(silu_f32(g[3]) * u[3]);
-        *reinterpret_cast<ushort4*>(hb + size_t(tl.row0 + r) * Iv + n) = hv;
+    for (int b = 0; b < MT; ++b)
+      if (b == mt) {
+        g = acc[0][b];
+        u = acc[1][b];
       }
+    const int r = 16 * mt + (lane & 15);
+    if (r < tl.rows) {
+      const int n = nb * 16 + 4 * (lane >> 4);
+      ushort4 hv;
+      hv.x = f32_to_bf16(silu_f32(g[0]) * u[0]);
+      hv.y = f32_to_bf16(silu_f32(g[1]) * u[1]);
+      hv.z = f32_to_bf16(silu_f32(g[2]) * u[2]);
+      hv.w = f32_to_bf16(silu_f32(g[3]) * u[3]);
+      *reinterpret_cast<ushort4*>(hb + size_t(tl.row0 + r) * Iv + n) = hv;
     }
   }
 }
@@ -260,35 +263,35 @@ __device__ __forceinline__ void down_setup(const ExpertArgs& a, const Tile& tl, 
   }
 }
 
-template <int MT>
-__global__ __launch_bounds__(256) void k_down_skinny(ExpertArgs a) {
-  __shared__ f32x4 red[4 * MT * kWave];
+template <int MT, int NW>
+__global__ __launch_bounds__(NW * 64) void k_down_skinny(ExpertArgs a) {
+  __shared__ f32x4 red[NW * MT * kWave];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ntr = a.plan->n_tiles_routed, nts = a.plan->n_tiles_shared;
   const int nb_all = (a.D + 15) / 16;
   const long total = long(ntr + nts) * nb_all;
-  for (long w = blockIdx.x; w < total; w += gridDim.x) {
-    const int ti = int(w / nb_all), nb = int(w % nb_all);
-    const bool shared = ti >= ntr;
-    const Tile tl = a.tiles[ti];
-    DownSkinnyProv pv;
-    down_setup(a, tl, shared, pv);
-    pv.d0 = nb * 16;
-    f32x4 acc[1][MT];
-    skinny_accumulate<1, MT, (MT >= 4 ? 1 : 4 / MT)>(pv, lane, wave, 4, acc);
-    skinny_reduce<1, MT>(acc, red, lane, wave, 4);
-    float* ob = shared ? a.o_sh : a.o;
-    for (int mt = wave; mt < MT; mt += 4) {
-      f32x4 v = acc[0][0];
+  const long w = blockIdx.x;
+  if (w >= total) return;
+  const int ti = int(w / nb_all), nb = int(w % nb_all);
+  const bool shared = ti >= ntr;
+  const Tile tl = a.tiles[ti];
+  DownSkinnyProv pv;
+  down_setup(a, tl, shared, pv);
+  pv.d0 = nb * 16;
+  f32x4 acc[1][MT];
+  skinny_accumulate<1, MT, (MT >= 4 ? 1 : 4 / MT)>(pv, lane, wave, NW, acc);
+  skinny_reduce<1, MT>(acc, red, lane, wave, NW);
+  float* ob = shared ? a.o_sh : a.o;
+  for (int mt = wave; mt < MT; mt += NW) {
+    f32x4 v = acc[0][0];
 #pragma unroll
-      for (int b = 0; b < MT; ++b)
-        if (b == mt) v = acc[0][b];
-      const int r = 16 * mt + (lane & 15);
-      const int d = nb * 16 + 4 * (lane >> 4);
-      if (r < tl.rows && d < a.D)
-        *reinterpret_cast<float4*>(ob + size_t(tl.row0 + r) * a.D + d) =
-            make_float4(v[0], v[1], v[2], v[3]);
-    }
+    for (int b = 0; b < MT; ++b)
+      if (b == mt) v = acc[0][b];
+    const int r = 16 * mt + (lane & 15);
+    const int d = nb * 16 + 4 * (lane >> 4);
+    if (r < tl.rows && d < a.D)
+      *reinterpret_cast<float4*>(ob + size_t(tl.row0 + r) * a.D + d) =
+          make_float4(v[0], v[1], v[2], v[3]);
   }
 }
 
@@ -467,6 +470,9 @@ static ExpertArgs expert_args(const beam_moe_layer& L, const void* x, int32_t T,
   return a;
 }
 
+// Waves per workgroup of the skinny (decode) expert kernels; they split k.
+constexpr int kSkinnyWaves = 8;
+
 // Upper bound on the number of tiles the scan can produce.
 static long tile_bound(const beam_moe_layer& L, int32_t T, int tile_rows, long* shared_tiles) {
   const long pairs = long(T) * L.K;
@@ -494,11 +500,12 @@ hipError_t launch_gate_up(const beam_moe_layer& L, const void* x, int32_t T, int
   }
   if (tile_rows <= 64) {
     const long items = ntr * (L.I / 16) + nts * (L.n_shared ? (L.n_shared * L.I_shared) / 16 : 0);
-    const dim3 grid(persistent_grid(items, 2048));
+    const dim3 grid(unsigned(std::max<long>(items, 1)));
+    const dim3 blk(kSkinnyWaves * 64);
     prof_before("gate_up_swiglu_skinny", s);
-    if (tile_rows == 16) hipLaunchKernelGGL(k_gate_up_skinny<1>, grid, dim3(256), 0, s, a);
-    else if (tile_rows == 32) hipLaunchKernelGGL(k_gate_up_skinny<2>, grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(k_gate_up_skinny<4>, grid, dim3(256), 0, s, a);
+    if (tile_rows == 16) hipLaunchKernelGGL((k_gate_up_skinny<1, kSkinnyWaves>), grid, blk, 0, s, a);
+    else if (tile_rows == 32) hipLaunchKernelGGL((k_gate_up_skinny<2, kSkinnyWaves>), grid, blk, 0, s, a);
+    else hipLaunchKernelGGL((k_gate_up_skinny<4, kSkinnyWaves>), grid, blk, 0, s, a);
     prof_after(s);
   } else {
     const long items = ntr * (L.I / 64) + nts * (L.n_shared ? (L.n_shared * L.I_shared) / 64 : 0);
@@ -523,11 +530,12 @@ hipError_t launch_down(const beam_moe_layer& L, int32_t T, int tile_rows, const 
   }
   if (tile_rows <= 64) {
     const long items = (ntr + nts) * ((L.D + 15) / 16);
-    const dim3 grid(persistent_grid(items, 2048));
+    const dim3 grid(unsigned(std::max<long>(items, 1)));
+    const dim3 blk(kSkinnyWaves * 64);
     prof_before("down_skinny", s);
-    if (tile_rows == 16) hipLaunchKernelGGL(k_down_skinny<1>, grid, dim3(256), 0, s, a);
-    else if (tile_rows == 32) hipLaunchKernelGGL(k_down_skinny<2>, grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(k_down_skinny<4>, grid, dim3(256), 0, s, a);
+    if (tile_rows == 16) hipLaunchKernelGGL((k_down_skinny<1, kSkinnyWaves>), grid, blk, 0, s, a);
+    else if (tile_rows == 32) hipLaunchKernelGGL((k_down_skinny<2, kSkinnyWaves>), grid, blk, 0, s, a);
+    else hipLaunchKernelGGL((k_down_skinny<4, kSkinnyWaves>), grid, blk, 0, s, a);
     prof_after(s);
   } else {
     const long items = (ntr + nts) * ((L.D + kTBN - 1) / kTBN);

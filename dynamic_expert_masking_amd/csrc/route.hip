@@ -12,18 +12,18 @@
 namespace beam {
 
 // ---------------------------------------------------------------------------
-// Router + mask-router logits: logits[t][j], j < E -> r_j, j >= E -> z_{j-E}
-// (fp32, bias added).  Weight rows 0..2E-1 are Wr's rows then Wm's rows.
+// Router + mask-router logits (no bias): part[ks][t][j], j < E -> Wr row j,
+// j >= E -> Wm row j-E.  For small batches the k range is split over KS
+// workgroups (ks) so that the router's weight rows stream through many CUs;
+// the selection kernel adds the KS partial sums in ks order, then the bias.
 // ---------------------------------------------------------------------------
 
 struct RouterArgs {
   const u16* x;
   const u16* wr;
   const u16* wm;
-  const float* br;
-  const float* bm;
-  float* logits;
-  int T, D, E;
+  float* part;
+  int T, D, E, KS;
 };
 
 __device__ __forceinline__ const u16* router_row(const RouterArgs& a, int j) {
@@ -32,39 +32,39 @@ __device__ __forceinline__ const u16* router_row(const RouterArgs& a, int j) {
   return nullptr;
 }
 
-__device__ __forceinline__ void router_store(const RouterArgs& a, int t, int j, float v) {
+__device__ __forceinline__ void router_store(const RouterArgs& a, int ks, int t, int j, float v) {
   if (t >= a.T || j >= 2 * a.E) return;
-  float b = 0.f;
-  if (j < a.E) {
-    if (a.br) b = a.br[j];
-  } else if (a.bm) {
-    b = a.bm[j - a.E];
-  }
-  a.logits[size_t(t) * 2 * a.E + j] = v + b;
+  a.part[(size_t(ks) * a.T + t) * 2 * a.E + j] = v;
 }
 
 template <int MT>
 struct RouterSkinnyProv {
   const RouterArgs* a;
-  int j0, t0;
+  int j0, t0, k0;   // k0: first element of this k slice
   __device__ int nseg() const { return 1; }
-  __device__ int seg_chunks() const { return a->D / 64; }
-  __device__ const u16* w(int, int r, int) const { return router_row(*a, j0 + r); }
+  __device__ int seg_chunks() const { return a->D / 64 / a->KS; }
+  __device__ const u16* w(int, int r, int) const {
+    const u16* p = router_row(*a, j0 + r);
+    return p ? p + k0 : nullptr;
+  }
   __device__ const u16* x(int r, int) const {
     const int t = t0 + r;
-    return t < a->T ? a->x + size_t(t) * a->D : nullptr;
+    return t < a->T ? a->x + size_t(t) * a->D + k0 : nullptr;
   }
 };
 
-// One workgroup per (16*MT tokens) x (16 router rows); 4 waves split k.
+// One workgroup per (16*MT tokens) x (16 router rows) x (k slice); 4 waves
+// split the slice.
 template <int MT>
 __global__ __launch_bounds__(256) void k_router_skinny(RouterArgs a) {
   __shared__ f32x4 red[4 * MT * kWave];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nrb = (2 * a.E + 15) / 16;
-  const int j0 = (blockIdx.x % nrb) * 16;
-  const int t0 = (blockIdx.x / nrb) * 16 * MT;
-  RouterSkinnyProv<MT> pv{&a, j0, t0};
+  const int ks = blockIdx.x % a.KS;
+  const int rest = blockIdx.x / a.KS;
+  const int j0 = (rest % nrb) * 16;
+  const int t0 = (rest / nrb) * 16 * MT;
+  RouterSkinnyProv<MT> pv{&a, j0, t0, ks * (a.D / a.KS)};
   f32x4 acc[1][MT];
   skinny_accumulate<1, MT, (MT >= 4 ? 1 : 4 / MT)>(pv, lane, wave, 4, acc);
   skinny_reduce<1, MT>(acc, red, lane, wave, 4);
@@ -76,7 +76,7 @@ __global__ __launch_bounds__(256) void k_router_skinny(RouterArgs a) {
       if (b == mt) v = acc[0][b];
     const int t = t0 + 16 * mt + (lane & 15);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) router_store(a, t, j0 + 4 * (lane >> 4) + i, v[i]);
+    for (int i = 0; i < 4; ++i) router_store(a, ks, t, j0 + 4 * (lane >> 4) + i, v[i]);
   }
 }
 
@@ -93,7 +93,7 @@ struct RouterTiledProv {
   }
 };
 
-// One workgroup per (BM tokens) x (128 router rows).
+// One workgroup per (BM tokens) x (128 router rows), whole k range.
 template <int BM>
 __global__ __launch_bounds__(256) void k_router_tiled(RouterArgs a) {
   __shared__ TiledSmem<BM> sm;
@@ -112,7 +112,7 @@ __global__ __launch_bounds__(256) void k_router_tiled(RouterArgs a) {
       const int t = t0 + wm * (BM / 2) + jm * 16 + (lane & 15);
       const int j = j0 + wn * 64 + jn * 16 + 4 * (lane >> 4);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) router_store(a, t, j + i, acc[jn][jm][i]);
+      for (int i = 0; i < 4; ++i) router_store(a, 0, t, j + i, acc[jn][jm][i]);
     }
 }
 
@@ -121,9 +121,7 @@ struct RouterArgsF32 {
   const float* x;
   const float* wr;
   const float* wm;
-  const float* br;
-  const float* bm;
-  float* logits;
+  float* part;
   int T, D, E;
 };
 
@@ -143,33 +141,40 @@ __global__ __launch_bounds__(256) void k_router_f32(RouterArgsF32 a) {
     s = fmaf(xv.z, wv.z, s);
     s = fmaf(xv.w, wv.w, s);
   }
-  float b = 0.f;
-  if (j < a.E) {
-    if (a.br) b = a.br[j];
-  } else if (a.bm) {
-    b = a.bm[j - a.E];
-  }
-  a.logits[size_t(t) * R + j] = s + b;
+  a.part[size_t(t) * R + j] = s;
 }
 
-hipError_t launch_router_logits(const beam_moe_layer& L, const void* x, int32_t T, float* logits,
+int router_ksplit(const beam_moe_layer& L, int32_t T) {
+  if (L.dtype == BEAM_F32 || T > 64) return 1;
+  const int chunks = L.D / 64;
+  const int mt = T <= 16 ? 1 : (T <= 32 ? 2 : 4);
+  const int blocks = ((2 * L.E + 15) / 16) * ((T + 16 * mt - 1) / (16 * mt));
+  int best = 1;
+  // largest divisor of the chunk count that leaves >= 4 chunks per slice and
+  // brings the grid to about 256 workgroups
+  for (int ks = 1; ks <= chunks; ++ks)
+    if (chunks % ks == 0 && chunks / ks >= 4 && blocks * ks <= 320) best = ks;
+  return best;
+}
+
+hipError_t launch_router_logits(const beam_moe_layer& L, const void* x, int32_t T, float* part,
                                 hipStream_t s) {
   if (L.dtype == BEAM_F32) {
-    RouterArgsF32 a{(const float*)x, (const float*)L.w_router, (const float*)L.w_mask, L.b_router,
-                    L.b_mask, logits, T, L.D, L.E};
+    RouterArgsF32 a{(const float*)x, (const float*)L.w_router, (const float*)L.w_mask, part, T,
+                    L.D, L.E};
     const long n = long(T) * 2 * L.E;
     prof_before("router_logits_f32", s);
     hipLaunchKernelGGL(k_router_f32, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, a);
     prof_after(s);
     return hipGetLastError();
   }
-  RouterArgs a{(const u16*)x, (const u16*)L.w_router, (const u16*)L.w_mask, L.b_router, L.b_mask,
-               logits, T, L.D, L.E};
+  const int KS = router_ksplit(L, T);
+  RouterArgs a{(const u16*)x, (const u16*)L.w_router, (const u16*)L.w_mask, part, T, L.D, L.E, KS};
   if (T <= 64) {
     const int nrb = (2 * L.E + 15) / 16;
     const int mt = T <= 16 ? 1 : (T <= 32 ? 2 : 4);
     const int ntb = (T + 16 * mt - 1) / (16 * mt);
-    const dim3 grid(unsigned(nrb * ntb));
+    const dim3 grid(unsigned(nrb * ntb * KS));
     prof_before("router_logits_skinny", s);
     if (mt == 1) hipLaunchKernelGGL(k_router_skinny<1>, grid, dim3(256), 0, s, a);
     else if (mt == 2) hipLaunchKernelGGL(k_router_skinny<2>, grid, dim3(256), 0, s, a);
@@ -186,165 +191,81 @@ hipError_t launch_router_logits(const beam_moe_layer& L, const void* x, int32_t 
 }
 
 // ---------------------------------------------------------------------------
-// Selection: top-K by descending router logit (equal logits: lower expert
-// index first), softmax over the K kept logits, mask bit m_k = [z >= 0] on
-// the candidates, g_hat = g * m.  One workgroup per 64-token block; each wave
-// handles 16 tokens.  Also computes, per block, the block-local rank of every
-// surviving pair among the block's pairs of the same expert (token order) and
-// the per-expert pair count of the block.
+// Plan: from per-expert pair counts (in LDS), the expert offsets of the
+// compacted pair order and the tile list.  Experts with no surviving pair
+// get no tile, so their weights are never read.  Runs in one 1024-thread
+// workgroup.  On return s_off holds the exclusive offsets.
 // ---------------------------------------------------------------------------
 
-constexpr int kKeysPerLane = kMaxExperts / kWave;   // 16
-
-__global__ __launch_bounds__(256) void k_select(const float* __restrict__ logits, int T, int E,
-                                                int K, int32_t* __restrict__ idx,
-                                                float* __restrict__ gates,
-                                                uint32_t* __restrict__ mask,
-                                                int32_t* __restrict__ rank,
-                                                int32_t* __restrict__ block_counts) {
-  __shared__ unsigned long long bits[kMaxExperts];
-  __shared__ int32_t s_idx[kSelBlock * 32];
-  __shared__ uint32_t s_mask[kSelBlock];
+// Exclusive prefix sums of two arrays of n <= 1024 entries at once
+// (blockDim.x == 1024): wave-level scans, then a scan of the 16 wave totals.
+__device__ __forceinline__ void block_exclusive_scan2(int32_t* v1, int32_t* v2, int n,
+                                                      int32_t* tmp /* >= 64 entries */) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int blk = blockIdx.x;
-  const int t0 = blk * kSelBlock;
-  for (int e = tid; e < E; e += blockDim.x) bits[e] = 0ull;
-  __syncthreads();
-
-  const int nper = (E + kWave - 1) / kWave;
-  for (int tl = wave; tl < kSelBlock; tl += 4) {
-    const int t = t0 + tl;
-    if (t >= T) break;
-    const float* row = logits + size_t(t) * 2 * E;
-    unsigned long long key[kKeysPerLane];
-#pragma unroll
-    for (int i = 0; i < kKeysPerLane; ++i) {
-      const int e = lane + kWave * i;
-      key[i] = 0ull;
-      if (i < nper && e < E)
-        key[i] = (static_cast<unsigned long long>(float_key(row[e])) << 32) |
-                 static_cast<unsigned long long>(0xFFFFFFFFu - uint32_t(e));
-    }
-    // K rounds of a wave-wide maximum; round k only considers keys below the
-    // previous winner (keys are distinct because they embed the index).
-    unsigned long long mine = 0ull, prev = ~0ull;
-    for (int k = 0; k < K; ++k) {
-      unsigned long long lm = 0ull;
-#pragma unroll
-      for (int i = 0; i < kKeysPerLane; ++i)
-        if (key[i] < prev && key[i] > lm) lm = key[i];
-      const unsigned long long wmx = wave_max_u64(lm);
-      if (lane == k) mine = wmx;
-      prev = wmx;
-    }
-    const bool slot = lane < K;
-    const int e_k = slot ? int(0xFFFFFFFFu - uint32_t(mine & 0xFFFFFFFFull)) : 0;
-    const float r_k = slot ? row[e_k] : 0.f;
-    const float r_0 = __shfl(r_k, 0, kWave);
-    const float ex = slot ? expf(r_k - r_0) : 0.f;
-    const float sum = wave_sum_f32(ex);
-    const bool keep = slot && row[E + e_k] >= 0.f;
-    const unsigned long long bal = __ballot(keep);
-    if (slot) {
-      idx[size_t(t) * K + lane] = e_k;
-      gates[size_t(t) * K + lane] = keep ? ex / sum : 0.f;
-      s_idx[tl * 32 + lane] = e_k;
-    }
-    if (lane == 0) {
-      mask[t] = uint32_t(bal);
-      s_mask[tl] = uint32_t(bal);
-    }
-    if (keep) atomicOr(&bits[e_k], 1ull << tl);
+  const int32_t a = tid < n ? v1[tid] : 0;
+  const int32_t b = tid < n ? v2[tid] : 0;
+  const int32_t ia = wave_inclusive_scan_i32(a, lane);
+  const int32_t ib = wave_inclusive_scan_i32(b, lane);
+  if (lane == 63) {
+    tmp[wave] = ia;
+    tmp[16 + wave] = ib;
   }
   __syncthreads();
-
-  for (int q = tid; q < kSelBlock * K; q += blockDim.x) {
-    const int tl = q / K, k = q % K;
-    const int t = t0 + tl;
-    if (t >= T) continue;
-    int rk = -1;
-    if ((s_mask[tl] >> k) & 1u) {
-      const int e = s_idx[tl * 32 + k];
-      rk = __popcll(bits[e] & ((1ull << tl) - 1ull));
+  if (wave == 0) {
+    const int32_t xa = lane < 16 ? tmp[lane] : 0;
+    const int32_t xb = lane < 16 ? tmp[16 + lane] : 0;
+    const int32_t sa = wave_inclusive_scan_i32(xa, lane);
+    const int32_t sb = wave_inclusive_scan_i32(xb, lane);
+    if (lane < 16) {
+      tmp[32 + lane] = sa - xa;
+      tmp[48 + lane] = sb - xb;
     }
-    rank[size_t(t) * K + k] = rk;
   }
-  for (int e = tid; e < E; e += blockDim.x)
-    block_counts[size_t(blk) * E + e] = __popcll(bits[e]);
-}
-
-hipError_t launch_select(const beam_moe_layer& L, int32_t T, const Ptrs& p, hipStream_t s) {
-  const int nblk = (T + kSelBlock - 1) / kSelBlock;
-  prof_before("select_topk_mask", s);
-  hipLaunchKernelGGL(k_select, dim3(unsigned(nblk)), dim3(256), 0, s, p.logits, T, L.E, L.K,
-                     p.idx, p.gates, p.mask, p.rank, p.block_counts);
-  prof_after(s);
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
-// Scan (one workgroup): per-expert totals and per-block exclusive offsets,
-// expert offsets in the compacted order, and the tile list.  Experts with no
-// surviving pair get no tile, so their weights are never read.
-// ---------------------------------------------------------------------------
-
-__device__ __forceinline__ void block_exclusive_scan(int32_t* v, int n, int32_t* tmp) {
-  // Hillis-Steele over n <= 1024 entries with blockDim.x == 1024.
-  const int tid = threadIdx.x;
-  int32_t own = tid < n ? v[tid] : 0;
-  tmp[tid] = own;
   __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int32_t add = tid >= off ? tmp[tid - off] : 0;
-    __syncthreads();
-    tmp[tid] += add;
-    __syncthreads();
+  if (tid < n) {
+    v1[tid] = tmp[32 + wave] + ia - a;
+    v2[tid] = tmp[48 + wave] + ib - b;
   }
-  if (tid < n) v[tid] = tmp[tid] - own;
   __syncthreads();
 }
 
-__global__ __launch_bounds__(1024) void k_scan(int T, int E, int nblk, int tile_rows,
-                                               int has_shared, int32_t* __restrict__ block_counts,
-                                               int32_t* __restrict__ counts,
-                                               int32_t* __restrict__ expert_off,
-                                               Plan* __restrict__ plan, Tile* __restrict__ tiles) {
-  __shared__ int32_t s_cnt[kMaxExperts];
-  __shared__ int32_t s_off[kMaxExperts];
-  __shared__ int32_t s_toff[kMaxExperts];
-  __shared__ int32_t s_tmp[1024];
+struct PlanSmem {
+  int32_t cnt[kMaxExperts];
+  int32_t off[kMaxExperts];
+  int32_t toff[kMaxExperts];
+  int32_t tmp[1024];
+};
+
+__device__ void build_plan(PlanSmem& sm, int T, int E, int tile_rows, int has_shared,
+                           int32_t* __restrict__ counts, int32_t* __restrict__ expert_off,
+                           Plan* __restrict__ plan, Tile* __restrict__ tiles) {
   const int tid = threadIdx.x;
   for (int e = tid; e < E; e += 1024) {
-    int32_t run = 0;
-    for (int b = 0; b < nblk; ++b) {
-      const int32_t c = block_counts[size_t(b) * E + e];
-      block_counts[size_t(b) * E + e] = run;
-      run += c;
-    }
-    s_cnt[e] = run;
-    counts[e] = run;
-    s_off[e] = run;
-    s_toff[e] = (run + tile_rows - 1) / tile_rows;
+    const int32_t c = sm.cnt[e];
+    counts[e] = c;
+    sm.off[e] = c;
+    sm.toff[e] = (c + tile_rows - 1) / tile_rows;
   }
   __syncthreads();
-  const int32_t last_cnt = E > 0 ? s_cnt[E - 1] : 0;
-  const int32_t last_tiles = E > 0 ? s_toff[E - 1] : 0;
-  block_exclusive_scan(s_off, E, s_tmp);
-  block_exclusive_scan(s_toff, E, s_tmp);
-  const int32_t P = s_off[E - 1] + last_cnt;
-  const int32_t ntr = s_toff[E - 1] + last_tiles;
+  const int32_t last_cnt = sm.cnt[E - 1];
+  const int32_t last_tiles = sm.toff[E - 1];
+  block_exclusive_scan2(sm.off, sm.toff, E, sm.tmp);
+  const int32_t P = sm.off[E - 1] + last_cnt;
+  const int32_t ntr = sm.toff[E - 1] + last_tiles;
   const int32_t nts = has_shared ? (T + tile_rows - 1) / tile_rows : 0;
+  int act = 0;
   for (int e = tid; e < E; e += 1024) {
-    expert_off[e] = s_off[e];
-    const int c = s_cnt[e];
+    expert_off[e] = sm.off[e];
+    const int c = sm.cnt[e];
+    act += c > 0;
     const int nt = (c + tile_rows - 1) / tile_rows;
     for (int j = 0; j < nt; ++j) {
       Tile tl;
       tl.expert = e;
-      tl.row0 = s_off[e] + j * tile_rows;
+      tl.row0 = sm.off[e] + j * tile_rows;
       tl.rows = min(tile_rows, c - j * tile_rows);
       tl.pad = 0;
-      tiles[s_toff[e] + j] = tl;
+      tiles[sm.toff[e] + j] = tl;
     }
   }
   for (int j = tid; j < nts; j += 1024) {
@@ -355,13 +276,10 @@ __global__ __launch_bounds__(1024) void k_scan(int T, int E, int nblk, int tile_
     tl.pad = 0;
     tiles[ntr + j] = tl;
   }
-  // active experts
-  int act = 0;
-  for (int e = tid; e < E; e += 1024) act += s_cnt[e] > 0;
-  s_tmp[tid] = act;
+  sm.tmp[tid] = act;
   __syncthreads();
-  for (int off = 512; off >= 1; off >>= 1) {
-    if (tid < off) s_tmp[tid] += s_tmp[tid + off];
+  for (int o = 512; o >= 1; o >>= 1) {
+    if (tid < o) sm.tmp[tid] += sm.tmp[tid + o];
     __syncthreads();
   }
   if (tid == 0) {
@@ -370,9 +288,288 @@ __global__ __launch_bounds__(1024) void k_scan(int T, int E, int nblk, int tile_
     pl.pairs = P;
     pl.n_tiles_routed = ntr;
     pl.n_tiles_shared = nts;
-    pl.active_experts = s_tmp[0];
+    pl.active_experts = sm.tmp[0];
     *plan = pl;
   }
+  __syncthreads();
+}
+
+// ---------------------------------------------------------------------------
+// Selection: top-K by descending router logit (equal logits: lower expert
+// index first), softmax over the K kept logits, mask bit m_k = [z >= 0] on
+// the candidates, g_hat = g * m.  One 1024-thread workgroup per 64-token
+// block; each of its 16 waves handles 4 tokens, with all four tokens' logits
+// loaded before any is processed.  Then, per block, the block-local rank of
+// every surviving pair among the block's pairs of the same expert (token
+// order) and the block's per-expert pair counts.  When the batch is a single
+// block, the same workgroup also builds the plan and places every pair, so
+// the scan and scatter kernels are not launched.
+// ---------------------------------------------------------------------------
+
+constexpr int kSelWaves = 16;
+constexpr int kSelTokPerWave = kSelBlock / kSelWaves;   // 4
+
+// Inverse of float_key on the high word of a selection key.
+__device__ __forceinline__ float key_float(unsigned long long key) {
+  uint32_t u = uint32_t(key >> 32);
+  u = (u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u;
+  return __uint_as_float(u);
+}
+
+struct SelectArgs {
+  const float* part;   // [KS][T][2E] router / mask-router partial logits
+  int KS;
+  const float* br;
+  const float* bm;
+  int T, E, K;
+  int32_t* idx;
+  float* gates;
+  uint32_t* mask;
+  int32_t* rank;
+  int32_t* block_counts;
+  // single-block batches
+  int tile_rows, has_shared;
+  int32_t* counts;
+  int32_t* expert_off;
+  Plan* plan;
+  Tile* tiles;
+  int32_t* perm_token;
+  int32_t* slot_pos;
+};
+
+template <int NPER>
+__global__ __launch_bounds__(1024) void k_select(SelectArgs a) {
+  __shared__ unsigned long long bits[kMaxExperts];
+  __shared__ int32_t s_idx[kSelBlock * 32];
+  __shared__ uint32_t s_mask[kSelBlock];
+  __shared__ PlanSmem psm;
+  constexpr int TPW = kSelTokPerWave;
+  constexpr int KB = NPER >= 4 ? 1 : 4 / NPER;   // partial slices loaded per round
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int blk = blockIdx.x;
+  const int t0 = blk * kSelBlock;
+  const int T = a.T, E = a.E, K = a.K;
+  for (int e = tid; e < E; e += blockDim.x) bits[e] = 0ull;
+
+  // r and z of this wave's tokens: partial sums added in ks order, then the
+  // biases.  All loads of a round are issued before any is used.
+  float rv[TPW][NPER], zv[TPW][NPER];
+#pragma unroll
+  for (int j = 0; j < TPW; ++j)
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) rv[j][i] = zv[j][i] = 0.f;
+  for (int ks0 = 0; ks0 < a.KS; ks0 += KB) {
+    float pr[KB][TPW][NPER], pz[KB][TPW][NPER];
+#pragma unroll
+    for (int u = 0; u < KB; ++u)
+#pragma unroll
+      for (int j = 0; j < TPW; ++j) {
+        const int t = t0 + wave * TPW + j;
+#pragma unroll
+        for (int i = 0; i < NPER; ++i) {
+          const int e = lane + kWave * i;
+          pr[u][j][i] = pz[u][j][i] = 0.f;
+          if (ks0 + u < a.KS && t < T && e < E) {
+            const float* row = a.part + (size_t(ks0 + u) * T + t) * 2 * E;
+            pr[u][j][i] = row[e];
+            pz[u][j][i] = row[E + e];
+          }
+        }
+      }
+#pragma unroll
+    for (int u = 0; u < KB; ++u)
+#pragma unroll
+      for (int j = 0; j < TPW; ++j)
+#pragma unroll
+        for (int i = 0; i < NPER; ++i) {
+          rv[j][i] += pr[u][j][i];
+          zv[j][i] += pz[u][j][i];
+        }
+  }
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    const int e = lane + kWave * i;
+    const float b_r = (a.br && e < E) ? a.br[e] : 0.f;
+    const float b_m = (a.bm && e < E) ? a.bm[e] : 0.f;
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+      rv[j][i] += b_r;
+      zv[j][i] += b_m;
+    }
+  }
+  __syncthreads();   // bits[] cleared
+
+  // Top-K of the wave's tokens, IL tokens at a time with their reductions
+  // interleaved.  Round k: the wave-wide maximum M of the remaining logits,
+  // then the lowest expert index holding M (ballot + find-first-set, so equal
+  // logits go to the lower index); that entry is then removed.
+  constexpr int IL = NPER <= 4 ? TPW : 1;
+#pragma unroll
+  for (int j0 = 0; j0 < TPW; j0 += IL) {
+    float vals[IL][NPER];
+#pragma unroll
+    for (int jj = 0; jj < IL; ++jj)
+#pragma unroll
+      for (int i = 0; i < NPER; ++i)
+        vals[jj][i] = (lane + kWave * i < E) ? rv[j0 + jj][i] + 0.0f : -__builtin_inff();
+    int mine_e[IL];
+    float mine_r[IL];
+#pragma unroll
+    for (int jj = 0; jj < IL; ++jj) {
+      mine_e[jj] = 0;
+      mine_r[jj] = 0.f;
+    }
+    for (int k = 0; k < K; ++k) {
+      float m[IL];
+#pragma unroll
+      for (int jj = 0; jj < IL; ++jj) {
+        m[jj] = vals[jj][0];
+#pragma unroll
+        for (int i = 1; i < NPER; ++i) m[jj] = fmaxf(m[jj], vals[jj][i]);
+      }
+      wave_max_f32_n<IL>(m);
+#pragma unroll
+      for (int jj = 0; jj < IL; ++jj) {
+        int win = -1;
+#pragma unroll
+        for (int i = NPER - 1; i >= 0; --i) {
+          const unsigned long long b = __ballot(vals[jj][i] == m[jj]);
+          if (b) win = kWave * i + __builtin_ctzll(b);
+        }
+        // win is wave-uniform: remove it from its owner lane
+#pragma unroll
+        for (int i = 0; i < NPER; ++i)
+          if (win == kWave * i + lane) vals[jj][i] = -__builtin_inff();
+        if (lane == k) {
+          mine_e[jj] = win;
+          mine_r[jj] = m[jj];
+        }
+      }
+    }
+#pragma unroll
+    for (int jj = 0; jj < IL; ++jj) {
+      const int tl = wave * TPW + j0 + jj;
+      const int t = t0 + tl;
+      if (t >= T) break;
+      const bool slot = lane < K;
+      const int e_k = slot ? mine_e[jj] : 0;
+      const float r_k = slot ? mine_r[jj] : 0.f;
+      // mask logit of expert e_k lives in lane e_k % 64, register e_k / 64
+      float z_k = 0.f;
+#pragma unroll
+      for (int i = 0; i < NPER; ++i) {
+        const float c = __shfl(zv[j0 + jj][i], e_k & 63, kWave);
+        if (i == (e_k >> 6)) z_k = c;
+      }
+      const float r_0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r_k), 0));
+      const float ex = slot ? expf(r_k - r_0) : 0.f;
+      const float sum = wave_sum_f32(ex);
+      const bool keep = slot && z_k >= 0.f;
+      const unsigned long long bal = __ballot(keep);
+      if (slot) {
+        a.idx[size_t(t) * K + lane] = e_k;
+        a.gates[size_t(t) * K + lane] = keep ? ex / sum : 0.f;
+        s_idx[tl * 32 + lane] = e_k;
+      }
+      if (lane == 0) {
+        a.mask[t] = uint32_t(bal);
+        s_mask[tl] = uint32_t(bal);
+      }
+      if (keep) atomicOr(&bits[e_k], 1ull << tl);
+    }
+  }
+  __syncthreads();
+
+  const bool single = gridDim.x == 1;
+  if (single) {
+    for (int e = tid; e < E; e += blockDim.x) psm.cnt[e] = __popcll(bits[e]);
+    __syncthreads();
+    build_plan(psm, T, E, a.tile_rows, a.has_shared, a.counts, a.expert_off, a.plan, a.tiles);
+  }
+  for (int q = tid; q < kSelBlock * K; q += blockDim.x) {
+    const int tl = q / K, k = q % K;
+    const int t = t0 + tl;
+    if (t >= T) continue;
+    int rk = -1;
+    if ((s_mask[tl] >> k) & 1u) {
+      const int e = s_idx[tl * 32 + k];
+      rk = __popcll(bits[e] & ((1ull << tl) - 1ull));
+    }
+    if (single) {
+      int pos = -1;
+      if (rk >= 0) {
+        pos = psm.off[s_idx[tl * 32 + k]] + rk;
+        a.perm_token[pos] = t;
+      }
+      a.slot_pos[size_t(t) * K + k] = pos;
+    } else {
+      a.rank[size_t(t) * K + k] = rk;
+    }
+  }
+  if (!single)
+    for (int e = tid; e < E; e += blockDim.x)
+      a.block_counts[size_t(blk) * E + e] = __popcll(bits[e]);
+}
+
+hipError_t launch_select(const beam_moe_layer& L, int32_t T, int tile_rows, const Ptrs& p,
+                         hipStream_t s) {
+  const int nblk = (T + kSelBlock - 1) / kSelBlock;
+  SelectArgs a;
+  a.part = p.logits;
+  a.KS = router_ksplit(L, T);
+  a.br = L.b_router;
+  a.bm = L.b_mask;
+  a.T = T;
+  a.E = L.E;
+  a.K = L.K;
+  a.idx = p.idx;
+  a.gates = p.gates;
+  a.mask = p.mask;
+  a.rank = p.rank;
+  a.block_counts = p.block_counts;
+  a.tile_rows = tile_rows;
+  a.has_shared = L.n_shared > 0 ? 1 : 0;
+  a.counts = p.counts;
+  a.expert_off = p.expert_off;
+  a.plan = p.plan;
+  a.tiles = p.tiles;
+  a.perm_token = p.perm_token;
+  a.slot_pos = p.slot_pos;
+  const dim3 g{unsigned(nblk), 1, 1}, b{1024, 1, 1};
+  prof_before(nblk == 1 ? "select_topk_mask_plan" : "select_topk_mask", s);
+  if (L.E <= 64) hipLaunchKernelGGL(k_select<1>, g, b, 0, s, a);
+  else if (L.E <= 128) hipLaunchKernelGGL(k_select<2>, g, b, 0, s, a);
+  else if (L.E <= 256) hipLaunchKernelGGL(k_select<4>, g, b, 0, s, a);
+  else hipLaunchKernelGGL(k_select<16>, g, b, 0, s, a);
+  prof_after(s);
+  return hipGetLastError();
+}
+
+bool select_builds_plan(int32_t T) { return T <= kSelBlock; }
+
+// ---------------------------------------------------------------------------
+// Scan (one workgroup, multi-block batches): per-expert totals and per-block
+// exclusive offsets, then the plan.
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(1024) void k_scan(int T, int E, int nblk, int tile_rows,
+                                               int has_shared, int32_t* __restrict__ block_counts,
+                                               int32_t* __restrict__ counts,
+                                               int32_t* __restrict__ expert_off,
+                                               Plan* __restrict__ plan, Tile* __restrict__ tiles) {
+  __shared__ PlanSmem psm;
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += 1024) {
+    int32_t run = 0;
+    for (int b = 0; b < nblk; ++b) {
+      const int32_t c = block_counts[size_t(b) * E + e];
+      block_counts[size_t(b) * E + e] = run;
+      run += c;
+    }
+    psm.cnt[e] = run;
+  }
+  __syncthreads();
+  build_plan(psm, T, E, tile_rows, has_shared, counts, expert_off, plan, tiles);
 }
 
 hipError_t launch_scan(const beam_moe_layer& L, int32_t T, int tile_rows, const Ptrs& p,
@@ -387,9 +584,9 @@ hipError_t launch_scan(const beam_moe_layer& L, int32_t T, int tile_rows, const 
 }
 
 // ---------------------------------------------------------------------------
-// Scatter: position of every surviving pair in the expert-major compacted
-// order (ascending expert, then ascending token), its token, and the
-// per-slot position used by the combine (-1 for masked slots).
+// Scatter (multi-block batches): position of every surviving pair in the
+// expert-major compacted order (ascending expert, then ascending token), its
+// token, and the per-slot position used by the combine (-1 for masked slots).
 // ---------------------------------------------------------------------------
 
 __global__ __launch_bounds__(256) void k_scatter(int T, int E, int K, const int32_t* __restrict__ idx,

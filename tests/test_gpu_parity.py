@@ -137,7 +137,7 @@ def test_all_masked(shared):
         assert np.all(y == 0.0)
 
 
-@pytest.mark.parametrize("E,K", [(7, 1), (8, 8), (64, 32)])
+@pytest.mark.parametrize("E,K", [(7, 1), (8, 8), (64, 32), (300, 12), (1024, 3)])
 def test_k_extremes(E, K):
     layer = small_layer(f"gpu_k{E}_{K}", D=128, E=E, K=K, I=64, keep=0.5)
     x = small_x(layer, 33, "kx")
