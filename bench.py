@@ -34,6 +34,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 DOMINANT = "gate_up_swiglu"    # prefix of the dominant kernel's names
 KERNEL_SOURCES = ("dynamic_expert_masking_amd/csrc/experts.hip",
+                  "dynamic_expert_masking_amd/csrc/stream_engine.h",
                   "dynamic_expert_masking_amd/csrc/gemm_engines.h",
                   "dynamic_expert_masking_amd/csrc/device_common.h")
 

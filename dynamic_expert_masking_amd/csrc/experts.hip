@@ -14,8 +14,12 @@
 // rows back to back.  Grids are persistent: workgroup b takes items b,
 // b + gridDim.x, ... up to the device-side item count, so no host readback of
 // the counts is needed.
+#include <map>
+#include <mutex>
+
 #include "beam_internal.h"
 #include "gemm_engines.h"
+#include "stream_engine.h"
 
 namespace beam {
 
@@ -49,92 +53,187 @@ __device__ __forceinline__ bool work_item(long w, int ntr, int nts, int nbr, int
   }
   const long w2 = w - wr;
   if (w2 < long(nts) * nbs) {
-    ti = ntr + int(w2 / nbs);
-    nb = int(w2 % nbs);
+    // shared tiles: n-block-major, so the tiles that reuse one weight block
+    // are consecutive items (same workgroup, cache-warm)
+    ti = ntr + int(w2 % nts);
+    nb = int(w2 / nts);
     shared = true;
     return true;
   }
   return false;
 }
 
+// Down items: routed (tile, d-block) tile-major, then shared d-block-major.
+__device__ __forceinline__ void down_item(long w, int ntr, int nts, int nb_all, int& ti, int& nb) {
+  const long wr = long(ntr) * nb_all;
+  if (w < wr) {
+    ti = int(w / nb_all);
+    nb = int(w % nb_all);
+  } else {
+    const long w2 = w - wr;
+    ti = ntr + int(w2 % nts);
+    nb = int(w2 / nts);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // gate/up + SwiGLU (bf16)
 // ---------------------------------------------------------------------------
 
-struct GateUpSkinnyProv {
-  const u16* wg;     // expert's [I][D] (or shared [S*Is][D])
-  const u16* wu;
-  const u16* xb;
-  const int32_t* perm;  // nullptr for the shared expert (rows are tokens)
-  int D, n0, row0, rows;
-  __device__ int nseg() const { return 1; }
-  __device__ int seg_chunks() const { return D / 64; }
-  __device__ const u16* w(int mat, int r, int) const {
-    return (mat == 0 ? wg : wu) + size_t(n0 + r) * D;
-  }
-  __device__ const u16* x_row(int r) const {
-    if (r >= rows) return nullptr;
-    const int t = perm ? perm[row0 + r] : row0 + r;
-    return xb + size_t(t) * D;
-  }
-  __device__ const u16* x(int r, int) const { return x_row(r); }
-};
-
-// Skinny: one workgroup of NW waves per (tile, 16-row n-block) item; the
-// waves split the k range.  The grid covers an upper bound on the item count;
-// workgroups past the device-side count exit at once.
-template <int MT, int NW>
-__global__ __launch_bounds__(NW * 64) void k_gate_up_skinny(ExpertArgs a) {
-  __shared__ f32x4 red[NW * 2 * MT * kWave];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int ntr = a.plan->n_tiles_routed, nts = a.plan->n_tiles_shared;
-  const int nbr = a.I / 16, nbs = a.S > 0 ? (a.S * a.Is) / 16 : 1;
-  const long total = long(ntr) * nbr + long(nts) * nbs;
-  const long w = blockIdx.x;
-  if (w >= total) return;
-  int ti, nb;
-  bool shared;
-  work_item(w, ntr, nts, nbr, nbs, ti, nb, shared);
-  const Tile tl = a.tiles[ti];
-  const int Iv = shared ? a.S * a.Is : a.I;
-  GateUpSkinnyProv pv;
-  if (shared) {
-    pv.wg = (const u16*)a.sg;
-    pv.wu = (const u16*)a.su;
-    pv.perm = nullptr;
-  } else {
-    pv.wg = (const u16*)a.wg + size_t(tl.expert) * a.I * a.D;
-    pv.wu = (const u16*)a.wu + size_t(tl.expert) * a.I * a.D;
-    pv.perm = a.perm_token;
-  }
-  pv.xb = (const u16*)a.x;
-  pv.D = a.D;
-  pv.n0 = nb * 16;
-  pv.row0 = tl.row0;
-  pv.rows = tl.rows;
-  f32x4 acc[2][MT];
-  skinny_accumulate<2, MT, (MT >= 4 ? 1 : 4 / MT)>(pv, lane, wave, NW, acc);
-  skinny_reduce<2, MT>(acc, red, lane, wave, NW);
-  u16* hb = shared ? (u16*)a.h_sh : (u16*)a.h;
-  for (int mt = wave; mt < MT; mt += NW) {
-    f32x4 g = acc[0][0], u = acc[1][0];
+// Streaming (decode) gate/up: items are (tile, 16-row n-block); see
+// stream_engine.h.
+template <int MT>
+struct GateUpStream {
+  const ExpertArgs* a;
+  int ntr, nts, nbr, nbs;
+  long total;
+  __device__ long total_items() const { return total; }
+  __device__ void decode(long item, int lane, StreamItem<2, MT>& it) const {
+    it.valid = item >= 0;
+    it.nseg = 1;
+    it.w_seg = 0;
+    it.x_seg = 0;
+    it.cps = a->D / 64;
+    it.w_row = a->D;
+    if (!it.valid) {
+      it.cps = 1;
+      it.w_row = 0;
+      it.w[0] = it.w[1] = (const u16*)a->wg;
 #pragma unroll
-    for (int b = 0; b < MT; ++b)
-      if (b == mt) {
-        g = acc[0][b];
-        u = acc[1][b];
-      }
-    const int r = 16 * mt + (lane & 15);
-    if (r < tl.rows) {
-      const int n = nb * 16 + 4 * (lane >> 4);
-      ushort4 hv;
-      hv.x = f32_to_bf16(silu_f32(g[0]) * u[0]);
-      hv.y = f32_to_bf16(silu_f32(g[1]) * u[1]);
-      hv.z = f32_to_bf16(silu_f32(g[2]) * u[2]);
-      hv.w = f32_to_bf16(silu_f32(g[3]) * u[3]);
-      *reinterpret_cast<ushort4*>(hb + size_t(tl.row0 + r) * Iv + n) = hv;
+      for (int b = 0; b < MT; ++b) it.x[b] = (const u16*)a->x;
+      return;
+    }
+    int ti, nb;
+    bool shared;
+    work_item(item, ntr, nts, nbr, nbs, ti, nb, shared);
+    const Tile tl = a->tiles[ti];
+    const u16* wg = shared ? (const u16*)a->sg : (const u16*)a->wg + size_t(tl.expert) * a->I * a->D;
+    const u16* wu = shared ? (const u16*)a->su : (const u16*)a->wu + size_t(tl.expert) * a->I * a->D;
+    it.w[0] = wg + size_t(nb) * 16 * a->D;
+    it.w[1] = wu + size_t(nb) * 16 * a->D;
+#pragma unroll
+    for (int b = 0; b < MT; ++b) {
+      const int r = 16 * b + (lane & 15);
+      int t = 0;   // absent rows read token 0
+      if (r < tl.rows) t = shared ? tl.row0 + r : a->perm_token[tl.row0 + r];
+      it.x[b] = (const u16*)a->x + size_t(t) * a->D;
     }
   }
+  __device__ void epilogue(long item, const f32x4 (&acc)[2][MT], int lane) const {
+    int ti, nb;
+    bool shared;
+    work_item(item, ntr, nts, nbr, nbs, ti, nb, shared);
+    const Tile tl = a->tiles[ti];
+    const int Iv = shared ? a->S * a->Is : a->I;
+    u16* hb = shared ? (u16*)a->h_sh : (u16*)a->h;
+#pragma unroll
+    for (int b = 0; b < MT; ++b) {
+      const int r = 16 * b + (lane & 15);
+      if (r < tl.rows) {
+        const f32x4 g = acc[0][b], u = acc[1][b];
+        const int n = nb * 16 + 4 * (lane >> 4);
+        ushort4 hv;
+        hv.x = f32_to_bf16(silu_f32(g[0]) * u[0]);
+        hv.y = f32_to_bf16(silu_f32(g[1]) * u[1]);
+        hv.z = f32_to_bf16(silu_f32(g[2]) * u[2]);
+        hv.w = f32_to_bf16(silu_f32(g[3]) * u[3]);
+        *reinterpret_cast<ushort4*>(hb + size_t(tl.row0 + r) * Iv + n) = hv;
+      }
+    }
+  }
+};
+
+template <int MT, int U, int KSPLIT>
+__global__ __launch_bounds__(kStreamWaves * 64) void k_gate_up_stream(ExpertArgs a) {
+  __shared__ u16 lds[kStreamWaves * 2 * 2 * 16 * kLdsRow];
+  __shared__ f32x4 red[KSPLIT > 1 ? kStreamWaves * 2 * MT * kWave : 1];
+  GateUpStream<MT> pb;
+  pb.a = &a;
+  pb.ntr = a.plan->n_tiles_routed;
+  pb.nts = a.plan->n_tiles_shared;
+  pb.nbr = a.I / 16;
+  pb.nbs = a.S > 0 ? (a.S * a.Is) / 16 : 1;
+  pb.total = long(pb.ntr) * pb.nbr + long(pb.nts) * pb.nbs;
+  stream_run<2, MT, U, KSPLIT>(pb, lds, red);
+}
+
+// Streaming (decode) down: items are (tile, 16-row d-block); the fused
+// shared expert has one k segment per shared expert.
+template <int MT>
+struct DownStream {
+  const ExpertArgs* a;
+  int ntr, nts, nb_all;
+  long total;
+  __device__ long total_items() const { return total; }
+  __device__ void decode(long item, int lane, StreamItem<1, MT>& it) const {
+    it.valid = item >= 0;
+    if (!it.valid) {
+      it.nseg = 1;
+      it.cps = 1;
+      it.w[0] = (const u16*)a->wd;
+      it.w_row = it.w_seg = it.x_seg = 0;
+#pragma unroll
+      for (int b = 0; b < MT; ++b) it.x[b] = (const u16*)a->h;
+      return;
+    }
+    int ti, nb;
+    down_item(item, ntr, nts, nb_all, ti, nb);
+    const bool shared = ti >= ntr;
+    const Tile tl = a->tiles[ti];
+    const int d0 = nb * 16;
+    if (shared) {
+      it.nseg = a->S;
+      it.cps = a->Is / 64;
+      it.w[0] = (const u16*)a->sd + size_t(d0) * a->Is;
+      it.w_row = a->Is;
+      it.w_seg = long(a->D) * a->Is;
+      it.x_seg = a->Is;
+    } else {
+      it.nseg = 1;
+      it.cps = a->I / 64;
+      it.w[0] = (const u16*)a->wd + size_t(tl.expert) * a->D * a->I + size_t(d0) * a->I;
+      it.w_row = a->I;
+      it.w_seg = 0;
+      it.x_seg = 0;
+    }
+    const long hs = shared ? long(a->S) * a->Is : a->I;
+    const u16* hb = shared ? (const u16*)a->h_sh : (const u16*)a->h;
+#pragma unroll
+    for (int b = 0; b < MT; ++b) {
+      const int r = 16 * b + (lane & 15);
+      // absent rows read the tile's first row
+      it.x[b] = hb + size_t(tl.row0 + (r < tl.rows ? r : 0)) * hs;
+    }
+  }
+  __device__ void epilogue(long item, const f32x4 (&acc)[1][MT], int lane) const {
+    int ti, nb;
+    down_item(item, ntr, nts, nb_all, ti, nb);
+    const bool shared = ti >= ntr;
+    const Tile tl = a->tiles[ti];
+    float* ob = shared ? a->o_sh : a->o;
+#pragma unroll
+    for (int b = 0; b < MT; ++b) {
+      const int r = 16 * b + (lane & 15);
+      const int d = nb * 16 + 4 * (lane >> 4);
+      if (r < tl.rows) {
+        const f32x4 v = acc[0][b];
+        *reinterpret_cast<float4*>(ob + size_t(tl.row0 + r) * a->D + d) = make_float4(v[0], v[1], v[2], v[3]);
+      }
+    }
+  }
+};
+
+template <int MT, int U, int KSPLIT>
+__global__ __launch_bounds__(kStreamWaves * 64) void k_down_stream(ExpertArgs a) {
+  __shared__ u16 lds[kStreamWaves * 2 * 1 * 16 * kLdsRow];
+  __shared__ f32x4 red[KSPLIT > 1 ? kStreamWaves * MT * kWave : 1];
+  DownStream<MT> pb;
+  pb.a = &a;
+  pb.ntr = a.plan->n_tiles_routed;
+  pb.nts = a.plan->n_tiles_shared;
+  pb.nb_all = a.D / 16;
+  pb.total = long(pb.ntr + pb.nts) * pb.nb_all;
+  stream_run<1, MT, U, KSPLIT>(pb, lds, red);
 }
 
 // Tiled: the 128 weight rows of an n-block are 64 intermediate rows of Wg and
@@ -233,11 +332,6 @@ struct DownProvBase {
   }
 };
 
-struct DownSkinnyProv : DownProvBase {
-  __device__ const u16* w(int, int r, int seg) const { return wrow(d0 + r, seg); }
-  __device__ const u16* x(int r, int seg) const { return hrow(r, seg); }
-};
-
 struct DownTiledProv : DownProvBase {
   __device__ const u16* w(int r, int seg) const { return wrow(d0 + r, seg); }
   __device__ const u16* x(int r, int seg) const { return hrow(r, seg); }
@@ -263,38 +357,6 @@ __device__ __forceinline__ void down_setup(const ExpertArgs& a, const Tile& tl, 
   }
 }
 
-template <int MT, int NW>
-__global__ __launch_bounds__(NW * 64) void k_down_skinny(ExpertArgs a) {
-  __shared__ f32x4 red[NW * MT * kWave];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int ntr = a.plan->n_tiles_routed, nts = a.plan->n_tiles_shared;
-  const int nb_all = (a.D + 15) / 16;
-  const long total = long(ntr + nts) * nb_all;
-  const long w = blockIdx.x;
-  if (w >= total) return;
-  const int ti = int(w / nb_all), nb = int(w % nb_all);
-  const bool shared = ti >= ntr;
-  const Tile tl = a.tiles[ti];
-  DownSkinnyProv pv;
-  down_setup(a, tl, shared, pv);
-  pv.d0 = nb * 16;
-  f32x4 acc[1][MT];
-  skinny_accumulate<1, MT, (MT >= 4 ? 1 : 4 / MT)>(pv, lane, wave, NW, acc);
-  skinny_reduce<1, MT>(acc, red, lane, wave, NW);
-  float* ob = shared ? a.o_sh : a.o;
-  for (int mt = wave; mt < MT; mt += NW) {
-    f32x4 v = acc[0][0];
-#pragma unroll
-    for (int b = 0; b < MT; ++b)
-      if (b == mt) v = acc[0][b];
-    const int r = 16 * mt + (lane & 15);
-    const int d = nb * 16 + 4 * (lane >> 4);
-    if (r < tl.rows && d < a.D)
-      *reinterpret_cast<float4*>(ob + size_t(tl.row0 + r) * a.D + d) =
-          make_float4(v[0], v[1], v[2], v[3]);
-  }
-}
-
 template <int BM>
 __global__ __launch_bounds__(256) void k_down_tiled(ExpertArgs a) {
   __shared__ TiledSmem<BM> sm;
@@ -304,7 +366,8 @@ __global__ __launch_bounds__(256) void k_down_tiled(ExpertArgs a) {
   const int nb_all = (a.D + kTBN - 1) / kTBN;
   const long total = long(ntr + nts) * nb_all;
   for (long w = blockIdx.x; w < total; w += gridDim.x) {
-    const int ti = int(w / nb_all), nb = int(w % nb_all);
+    int ti, nb;
+    down_item(w, ntr, nts, nb_all, ti, nb);
     const bool shared = ti >= ntr;
     const Tile tl = a.tiles[ti];
     DownTiledProv pv;
@@ -367,7 +430,8 @@ __global__ __launch_bounds__(256) void k_down_f32(ExpertArgs a) {
   const long total = long(ntr + nts) * nb_all;
   const int r = threadIdx.x >> 4, c = threadIdx.x & 15;
   for (long w = blockIdx.x; w < total; w += gridDim.x) {
-    const int ti = int(w / nb_all), nb = int(w % nb_all);
+    int ti, nb;
+    down_item(w, ntr, nts, nb_all, ti, nb);
     const bool shared = ti >= ntr;
     const Tile tl = a.tiles[ti];
     const int d = nb * 16 + c;
@@ -470,8 +534,43 @@ static ExpertArgs expert_args(const beam_moe_layer& L, const void* x, int32_t T,
   return a;
 }
 
-// Waves per workgroup of the skinny (decode) expert kernels; they split k.
-constexpr int kSkinnyWaves = 8;
+// Persistent grid of the streaming kernels: as many workgroups as can be
+// resident at once (occupancy x CUs, queried once per kernel and device).
+constexpr long kStreamGrid = 512;   // for choosing the k split only
+
+static int resident_blocks(const void* kernel, int block) {
+  static std::mutex mu;
+  static std::map<std::pair<int, const void*>, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  auto key = std::make_pair(dev, kernel);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int per_cu = 1, cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;
+  const int n = per_cu * cus;
+  cache[key] = n;
+  return n;
+}
+
+// Waves per item of the streaming kernels: split k when there are too few
+// items (an upper bound on them) to give every wave of the grid its own.
+static int stream_ksplit(long items_bound) {
+  const long waves = kStreamGrid * kStreamWaves;
+  if (items_bound >= 2 * waves) return 1;
+  if (items_bound >= waves) return 2;
+  return 4;
+}
+
+static unsigned stream_grid(const void* kernel, long items_bound, int ksplit) {
+  const long groups = kStreamWaves / ksplit;
+  const long cap = resident_blocks(kernel, kStreamWaves * 64);
+  return unsigned(std::max<long>(1, std::min<long>(cap, (items_bound + groups - 1) / groups)));
+}
 
 // Upper bound on the number of tiles the scan can produce.
 static long tile_bound(const beam_moe_layer& L, int32_t T, int tile_rows, long* shared_tiles) {
@@ -500,12 +599,21 @@ hipError_t launch_gate_up(const beam_moe_layer& L, const void* x, int32_t T, int
   }
   if (tile_rows <= 64) {
     const long items = ntr * (L.I / 16) + nts * (L.n_shared ? (L.n_shared * L.I_shared) / 16 : 0);
-    const dim3 grid(unsigned(std::max<long>(items, 1)));
-    const dim3 blk(kSkinnyWaves * 64);
-    prof_before("gate_up_swiglu_skinny", s);
-    if (tile_rows == 16) hipLaunchKernelGGL((k_gate_up_skinny<1, kSkinnyWaves>), grid, blk, 0, s, a);
-    else if (tile_rows == 32) hipLaunchKernelGGL((k_gate_up_skinny<2, kSkinnyWaves>), grid, blk, 0, s, a);
-    else hipLaunchKernelGGL((k_gate_up_skinny<4, kSkinnyWaves>), grid, blk, 0, s, a);
+    const int ks = tile_rows == 16 ? 4 : stream_ksplit(items);
+    const dim3 blk(kStreamWaves * 64);
+    prof_before("gate_up_swiglu_stream", s);
+#define BEAM_GU(MT_, U_, KS_)                                                                  \
+  hipLaunchKernelGGL((k_gate_up_stream<MT_, U_, KS_>),                                         \
+                     dim3(stream_grid((const void*)&k_gate_up_stream<MT_, U_, KS_>, items, ks)), \
+                     blk, 0, s, a)
+    if (tile_rows == 16) {
+      BEAM_GU(1, 1, 4);   // single-tile rows: four waves per item, one-chunk stages
+    } else if (tile_rows == 32) {
+      if (ks == 1) BEAM_GU(2, 2, 1); else if (ks == 2) BEAM_GU(2, 2, 2); else BEAM_GU(2, 2, 4);
+    } else {
+      if (ks == 1) BEAM_GU(4, 1, 1); else if (ks == 2) BEAM_GU(4, 1, 2); else BEAM_GU(4, 1, 4);
+    }
+#undef BEAM_GU
     prof_after(s);
   } else {
     const long items = ntr * (L.I / 64) + nts * (L.n_shared ? (L.n_shared * L.I_shared) / 64 : 0);
@@ -530,12 +638,21 @@ hipError_t launch_down(const beam_moe_layer& L, int32_t T, int tile_rows, const 
   }
   if (tile_rows <= 64) {
     const long items = (ntr + nts) * ((L.D + 15) / 16);
-    const dim3 grid(unsigned(std::max<long>(items, 1)));
-    const dim3 blk(kSkinnyWaves * 64);
-    prof_before("down_skinny", s);
-    if (tile_rows == 16) hipLaunchKernelGGL((k_down_skinny<1, kSkinnyWaves>), grid, blk, 0, s, a);
-    else if (tile_rows == 32) hipLaunchKernelGGL((k_down_skinny<2, kSkinnyWaves>), grid, blk, 0, s, a);
-    else hipLaunchKernelGGL((k_down_skinny<4, kSkinnyWaves>), grid, blk, 0, s, a);
+    const int ks = tile_rows == 16 ? 4 : stream_ksplit(items);
+    const dim3 blk(kStreamWaves * 64);
+    prof_before("down_stream", s);
+#define BEAM_DN(MT_, U_, KS_)                                                               \
+  hipLaunchKernelGGL((k_down_stream<MT_, U_, KS_>),                                         \
+                     dim3(stream_grid((const void*)&k_down_stream<MT_, U_, KS_>, items, ks)), \
+                     blk, 0, s, a)
+    if (tile_rows == 16) {
+      BEAM_DN(1, 2, 4);
+    } else if (tile_rows == 32) {
+      if (ks == 1) BEAM_DN(2, 2, 1); else if (ks == 2) BEAM_DN(2, 2, 2); else BEAM_DN(2, 2, 4);
+    } else {
+      if (ks == 1) BEAM_DN(4, 2, 1); else if (ks == 2) BEAM_DN(4, 2, 2); else BEAM_DN(4, 2, 4);
+    }
+#undef BEAM_DN
     prof_after(s);
   } else {
     const long items = (ntr + nts) * ((L.D + kTBN - 1) / kTBN);
