@@ -3,6 +3,7 @@
 #include <string.h>
 
 #include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -19,7 +20,8 @@ int expert_tile_rows(const beam_moe_layer& L, int32_t T) {
   if (per_expert <= 16) return 16;
   if (per_expert <= 32) return 32;
   if (per_expert <= 96) return 64;
-  return 128;
+  if (per_expert < 512) return 128;
+  return 256;
 }
 
 WsLayout workspace_layout(const beam_moe_layer& L, int32_t T) {
@@ -28,7 +30,7 @@ WsLayout workspace_layout(const beam_moe_layer& L, int32_t T) {
   const size_t elt = L.dtype == BEAM_F32 ? 4 : 2;
   const size_t nblk = (size_t(T) + kSelBlock - 1) / kSelBlock;
   const size_t IS = size_t(L.n_shared) * L.I_shared;
-  // Smallest tile height is 16 rows: bound on the tile count.
+  // Smallest tile height is 16 rows: bound on the tile count (any height).
   w.max_tiles = int32_t((TK + 15) / 16 + std::min<size_t>(L.E, TK) + (size_t(T) + 15) / 16 + 1);
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -54,6 +56,25 @@ WsLayout workspace_layout(const beam_moe_layer& L, int32_t T) {
   w.o_shared = take(IS ? size_t(T) * L.D * 4 : 0);
   w.total = off;
   return w;
+}
+
+int resident_blocks(const void* kernel, int block) {
+  static std::mutex mu;
+  static std::map<std::pair<int, const void*>, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  auto key = std::make_pair(dev, kernel);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int per_cu = 1, cus = 256;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;
+  const int n = per_cu * cus;
+  cache[key] = n;
+  return n;
 }
 
 // ---------------------------------------------------------------------------

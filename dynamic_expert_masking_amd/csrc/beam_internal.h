@@ -85,6 +85,10 @@ hipError_t launch_combine(const beam_moe_layer& L, int32_t T, const Ptrs& p, voi
                           hipStream_t s);
 hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t s);
 
+// Workgroups of `block` threads of `kernel` that fit on the device at once
+// (occupancy x CUs), cached per device and kernel.
+int resident_blocks(const void* kernel, int block);
+
 // Profiler hooks around each launch (no-ops unless the profiler is on).
 void prof_before(const char* name, hipStream_t s);
 void prof_after(hipStream_t s);

@@ -236,76 +236,78 @@ __global__ __launch_bounds__(kStreamWaves * 64) void k_down_stream(ExpertArgs a)
   stream_run<1, MT, U, KSPLIT>(pb, lds, red);
 }
 
-// Tiled: the 128 weight rows of an n-block are 64 intermediate rows of Wg and
-// the same 64 rows of Wu, interleaved in 16-row groups (gate, up, gate, up
-// per wave) so that a lane holds gate and up of the same element.
-template <int BM>
+// Tiled (prefill): the BN weight rows of an n-block are BN/2 intermediate
+// rows of Wg and the same rows of Wu, interleaved in 32-row groups (gate, up,
+// gate, up, ...) so that a lane holds gate and up of the same element.
 struct GateUpTiledProv {
   const u16* wg;
   const u16* wu;
   const u16* xb;
   const int32_t* perm;
-  int D, i0, row0, rows;
+  int D, Iv, i0, row0, rows;
   __device__ int nseg() const { return 1; }
   __device__ int seg_chunks() const { return D / 64; }
-  __device__ const u16* w(int r, int) const {
-    const int q = r >> 5, sel = (r >> 4) & 1;
-    const int irow = i0 + q * 16 + (r & 15);
-    return (sel ? wu : wg) + size_t(irow) * D;
+  __device__ const u16* wbase(int g, int) const { return (g & 1) ? wu : wg; }
+  __device__ uint32_t woff(int r) const {
+    int irow = i0 + (r >> 6) * 32 + (r & 31);
+    if (irow >= Iv) irow = 0;
+    return uint32_t(long(irow) * D);
   }
-  __device__ const u16* x(int r, int) const {
-    if (r >= rows) return nullptr;
-    const int t = perm ? perm[row0 + r] : row0 + r;
-    return xb + size_t(t) * D;
+  __device__ const u16* xbase(int) const { return xb; }
+  __device__ uint32_t xoff(int r) const {
+    int t = 0;
+    if (r < rows) t = perm ? perm[row0 + r] : row0 + r;
+    return uint32_t(long(t) * D);
   }
 };
 
-template <int BM>
-__global__ __launch_bounds__(256) void k_gate_up_tiled(ExpertArgs a) {
-  __shared__ TiledSmem<BM> sm;
+template <int BN, int BM>
+__global__ __launch_bounds__(256, 2) void k_gate_up_tiled(ExpertArgs a) {
+  __shared__ TiledSmem<BN, BM> sm;
+  constexpr int JN = BN / 64, JM = BM / 64, IB = BN / 2;   // IB: intermediate rows per tile
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wn = wave & 1, wm = wave >> 1;
   const int ntr = a.plan->n_tiles_routed, nts = a.plan->n_tiles_shared;
-  const int nbr = a.I / 64, nbs = a.S > 0 ? (a.S * a.Is) / 64 : 1;
+  const int nbr = (a.I + IB - 1) / IB, nbs = a.S > 0 ? (a.S * a.Is + IB - 1) / IB : 1;
   const long total = long(ntr) * nbr + long(nts) * nbs;
-  for (long w = blockIdx.x; w < total; w += gridDim.x) {
+  for (XcdRange it = xcd_range(total); it.next < it.end; it.next += it.step) {
     int ti, nb;
     bool shared;
-    work_item(w, ntr, nts, nbr, nbs, ti, nb, shared);
+    work_item(it.next, ntr, nts, nbr, nbs, ti, nb, shared);
     const Tile tl = a.tiles[ti];
     const int Iv = shared ? a.S * a.Is : a.I;
-    GateUpTiledProv<BM> pv;
-    if (shared) {
-      pv.wg = (const u16*)a.sg;
-      pv.wu = (const u16*)a.su;
-      pv.perm = nullptr;
-    } else {
-      pv.wg = (const u16*)a.wg + size_t(tl.expert) * a.I * a.D;
-      pv.wu = (const u16*)a.wu + size_t(tl.expert) * a.I * a.D;
-      pv.perm = a.perm_token;
-    }
+    GateUpTiledProv pv;
+    pv.wg = shared ? (const u16*)a.sg : (const u16*)a.wg + size_t(tl.expert) * a.I * a.D;
+    pv.wu = shared ? (const u16*)a.su : (const u16*)a.wu + size_t(tl.expert) * a.I * a.D;
+    pv.perm = shared ? nullptr : a.perm_token;
     pv.xb = (const u16*)a.x;
     pv.D = a.D;
-    pv.i0 = nb * 64;
+    pv.Iv = Iv;
+    pv.i0 = nb * IB;
     pv.row0 = tl.row0;
     pv.rows = tl.rows;
-    f32x4 acc[4][BM / 32];
-    tiled_accumulate<BM>(pv, sm, acc);
+    f32x16 acc[JN][JM];
+    tiled_accumulate<BN, BM>(pv, sm, acc, tl.rows);
     u16* hb = shared ? (u16*)a.h_sh : (u16*)a.h;
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
+    for (int p = 0; p < JN / 2; ++p)
 #pragma unroll
-      for (int jm = 0; jm < BM / 32; ++jm) {
-        const int r = wm * (BM / 2) + jm * 16 + (lane & 15);
+      for (int jm = 0; jm < JM; ++jm) {
+        const int r = wm * (BM / 2) + jm * 32 + (lane & 31);
         if (r < tl.rows) {
-          const f32x4 g = acc[2 * q][jm], u = acc[2 * q + 1][jm];
-          const int n = nb * 64 + (2 * wn + q) * 16 + 4 * (lane >> 4);
-          ushort4 hv;
-          hv.x = f32_to_bf16(silu_f32(g[0]) * u[0]);
-          hv.y = f32_to_bf16(silu_f32(g[1]) * u[1]);
-          hv.z = f32_to_bf16(silu_f32(g[2]) * u[2]);
-          hv.w = f32_to_bf16(silu_f32(g[3]) * u[3]);
-          *reinterpret_cast<ushort4*>(hb + size_t(tl.row0 + r) * Iv + n) = hv;
+          const f32x16 g = acc[2 * p][jm], u = acc[2 * p + 1][jm];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int n = nb * IB + (wn * (JN / 2) + p) * 32 + 8 * q + 4 * (lane >> 5);
+            if (n < Iv) {
+              ushort4 hv;
+              hv.x = f32_to_bf16(silu_f32(g[4 * q + 0]) * u[4 * q + 0]);
+              hv.y = f32_to_bf16(silu_f32(g[4 * q + 1]) * u[4 * q + 1]);
+              hv.z = f32_to_bf16(silu_f32(g[4 * q + 2]) * u[4 * q + 2]);
+              hv.w = f32_to_bf16(silu_f32(g[4 * q + 3]) * u[4 * q + 3]);
+              *reinterpret_cast<ushort4*>(hb + size_t(tl.row0 + r) * Iv + n) = hv;
+            }
+          }
         }
       }
   }
@@ -322,19 +324,14 @@ struct DownProvBase {
   bool shared;
   __device__ int nseg() const { return shared ? S : 1; }
   __device__ int seg_chunks() const { return (shared ? Is : Iv) / 64; }
-  __device__ const u16* wrow(int d, int seg) const {
-    if (d >= D) return nullptr;
-    return shared ? wd + size_t(seg) * D * Is + size_t(d) * Is : wd + size_t(d) * Iv;
+  __device__ const u16* wbase(int, int seg) const { return shared ? wd + size_t(seg) * D * Is : wd; }
+  __device__ uint32_t woff(int r) const {
+    int d = d0 + r;
+    if (d >= D) d = 0;
+    return uint32_t(long(d) * (shared ? Is : Iv));
   }
-  __device__ const u16* hrow(int r, int seg) const {
-    if (r >= rows) return nullptr;
-    return h + size_t(r) * hs + (shared ? seg * Is : 0);
-  }
-};
-
-struct DownTiledProv : DownProvBase {
-  __device__ const u16* w(int r, int seg) const { return wrow(d0 + r, seg); }
-  __device__ const u16* x(int r, int seg) const { return hrow(r, seg); }
+  __device__ const u16* xbase(int seg) const { return h + (shared ? seg * Is : 0); }
+  __device__ uint32_t xoff(int r) const { return uint32_t(long(r < rows ? r : 0) * hs); }
 };
 
 template <class P>
@@ -357,35 +354,41 @@ __device__ __forceinline__ void down_setup(const ExpertArgs& a, const Tile& tl, 
   }
 }
 
-template <int BM>
-__global__ __launch_bounds__(256) void k_down_tiled(ExpertArgs a) {
-  __shared__ TiledSmem<BM> sm;
+template <int BN, int BM>
+__global__ __launch_bounds__(256, 2) void k_down_tiled(ExpertArgs a) {
+  __shared__ TiledSmem<BN, BM> sm;
+  constexpr int JN = BN / 64, JM = BM / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wn = wave & 1, wm = wave >> 1;
   const int ntr = a.plan->n_tiles_routed, nts = a.plan->n_tiles_shared;
-  const int nb_all = (a.D + kTBN - 1) / kTBN;
+  const int nb_all = (a.D + BN - 1) / BN;
   const long total = long(ntr + nts) * nb_all;
-  for (long w = blockIdx.x; w < total; w += gridDim.x) {
+  for (XcdRange it = xcd_range(total); it.next < it.end; it.next += it.step) {
     int ti, nb;
-    down_item(w, ntr, nts, nb_all, ti, nb);
+    down_item(it.next, ntr, nts, nb_all, ti, nb);
     const bool shared = ti >= ntr;
     const Tile tl = a.tiles[ti];
-    DownTiledProv pv;
+    DownProvBase pv;
     down_setup(a, tl, shared, pv);
-    pv.d0 = nb * kTBN;
-    f32x4 acc[4][BM / 32];
-    tiled_accumulate<BM>(pv, sm, acc);
+    pv.d0 = nb * BN;
+    f32x16 acc[JN][JM];
+    tiled_accumulate<BN, BM>(pv, sm, acc, tl.rows);
     float* ob = shared ? a.o_sh : a.o;
 #pragma unroll
-    for (int jn = 0; jn < 4; ++jn)
+    for (int jn = 0; jn < JN; ++jn)
 #pragma unroll
-      for (int jm = 0; jm < BM / 32; ++jm) {
-        const int r = wm * (BM / 2) + jm * 16 + (lane & 15);
-        const int d = nb * kTBN + wn * 64 + jn * 16 + 4 * (lane >> 4);
-        if (r < tl.rows && d < a.D) {
-          const f32x4 v = acc[jn][jm];
-          *reinterpret_cast<float4*>(ob + size_t(tl.row0 + r) * a.D + d) =
-              make_float4(v[0], v[1], v[2], v[3]);
+      for (int jm = 0; jm < JM; ++jm) {
+        const int r = wm * (BM / 2) + jm * 32 + (lane & 31);
+        if (r < tl.rows) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int d = nb * BN + wn * (BN / 2) + jn * 32 + 8 * q + 4 * (lane >> 5);
+            if (d < a.D) {
+              const f32x16& v = acc[jn][jm];
+              *reinterpret_cast<float4*>(ob + size_t(tl.row0 + r) * a.D + d) =
+                  make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+            }
+          }
         }
       }
   }
@@ -538,25 +541,6 @@ static ExpertArgs expert_args(const beam_moe_layer& L, const void* x, int32_t T,
 // resident at once (occupancy x CUs, queried once per kernel and device).
 constexpr long kStreamGrid = 512;   // for choosing the k split only
 
-static int resident_blocks(const void* kernel, int block) {
-  static std::mutex mu;
-  static std::map<std::pair<int, const void*>, int> cache;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 256;
-  std::lock_guard<std::mutex> lock(mu);
-  auto key = std::make_pair(dev, kernel);
-  auto it = cache.find(key);
-  if (it != cache.end()) return it->second;
-  int per_cu = 1, cus = 256;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess || per_cu < 1)
-    per_cu = 1;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-    cus = 256;
-  const int n = per_cu * cus;
-  cache[key] = n;
-  return n;
-}
-
 // Waves per item of the streaming kernels: split k when there are too few
 // items (an upper bound on them) to give every wave of the grid its own.
 static int stream_ksplit(long items_bound) {
@@ -578,6 +562,13 @@ static long tile_bound(const beam_moe_layer& L, int32_t T, int tile_rows, long* 
   const long routed = (pairs + tile_rows - 1) / tile_rows + std::min<long>(L.E, pairs);
   *shared_tiles = L.n_shared > 0 ? (T + tile_rows - 1) / tile_rows : 0;
   return routed;
+}
+
+// Persistent grid of the tiled kernels: resident workgroups, a multiple of 8.
+static unsigned tiled_grid(const void* kernel, long items) {
+  long cap = resident_blocks(kernel, 256);
+  cap = std::max<long>(8, cap / 8 * 8);
+  return unsigned(std::max<long>(1, std::min<long>(cap, items)));
 }
 
 static unsigned persistent_grid(long items, long cap) {
@@ -616,9 +607,16 @@ hipError_t launch_gate_up(const beam_moe_layer& L, const void* x, int32_t T, int
 #undef BEAM_GU
     prof_after(s);
   } else {
-    const long items = ntr * (L.I / 64) + nts * (L.n_shared ? (L.n_shared * L.I_shared) / 64 : 0);
+    const int ib = tile_rows == 256 ? 64 : 128;   // intermediate rows per tile
+    const long items = ntr * ((L.I + ib - 1) / ib) +
+                       nts * (L.n_shared ? (L.n_shared * L.I_shared + ib - 1) / ib : 0);
     prof_before("gate_up_swiglu_tiled", s);
-    hipLaunchKernelGGL(k_gate_up_tiled<128>, dim3(persistent_grid(items, 512)), dim3(256), 0, s, a);
+    if (tile_rows == 256)
+      hipLaunchKernelGGL((k_gate_up_tiled<128, 256>),
+                         dim3(tiled_grid((const void*)&k_gate_up_tiled<128, 256>, items)), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_gate_up_tiled<256, 128>),
+                         dim3(tiled_grid((const void*)&k_gate_up_tiled<256, 128>, items)), dim3(256), 0, s, a);
     prof_after(s);
   }
   return hipGetLastError();
@@ -655,9 +653,15 @@ hipError_t launch_down(const beam_moe_layer& L, int32_t T, int tile_rows, const 
 #undef BEAM_DN
     prof_after(s);
   } else {
-    const long items = (ntr + nts) * ((L.D + kTBN - 1) / kTBN);
+    const int bn = tile_rows == 256 ? 128 : 256;
+    const long items = (ntr + nts) * ((L.D + bn - 1) / bn);
     prof_before("down_tiled", s);
-    hipLaunchKernelGGL(k_down_tiled<128>, dim3(persistent_grid(items, 512)), dim3(256), 0, s, a);
+    if (tile_rows == 256)
+      hipLaunchKernelGGL((k_down_tiled<128, 256>),
+                         dim3(tiled_grid((const void*)&k_down_tiled<128, 256>, items)), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_down_tiled<256, 128>),
+                         dim3(tiled_grid((const void*)&k_down_tiled<256, 128>, items)), dim3(256), 0, s, a);
     prof_after(s);
   }
   return hipGetLastError();

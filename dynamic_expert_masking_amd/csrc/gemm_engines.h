@@ -133,108 +133,168 @@ __device__ __forceinline__ void skinny_reduce(f32x4 (&acc)[NMAT][MT], f32x4* red
 }
 
 // ---------------------------------------------------------------------------
-// Tiled engine
+// Tiled engine (prefill-shaped tiles)
+//
+// One workgroup of 4 waves computes a tile of BN weight rows x BM token rows
+// (BN x BM = 256 x 128 or 128 x 256); waves sit in a 2 x 2 layout and each
+// owns BN/2 weight rows x BM/2 token rows as blocks of 32 x 32 MFMAs
+// (v_mfma_f32_32x32x16_bf16, fp32 accumulators; 8 blocks per wave, so two
+// workgroups fit on a CU and cover each other's barrier waits).  The k range
+// is walked in 64-wide slices: the next slice of both operands is loaded from
+// global memory into registers (coalesced 16-byte loads, 8 lanes per 128-byte
+// row segment, 32-bit offsets from a uniform base) while the current slice is
+// multiplied out of a padded LDS tile (row stride 144 bytes, so the 16 rows
+// read by 16 consecutive lanes hit distinct banks).  Loads are branch-free:
+// absent rows read row 0 of their operand and the slice past the end reads
+// one fixed address, so the compiler's load counters stay exact; absent rows
+// only feed accumulator rows or columns that the epilogues never store.
 // ---------------------------------------------------------------------------
 
-constexpr int kTBN = 128;           // weight rows per tile
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16 mfma32_bf16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 ld16_at(const u16* base, uint32_t elem_off) {
+  return *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(base) + size_t(elem_off) * 2);
+}
+__device__ __forceinline__ u32x4 ld16_at_stream(const u16* base, uint32_t elem_off) {
+  return __builtin_nontemporal_load(
+      reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(base) + size_t(elem_off) * 2));
+}
+
 constexpr int kTBK = 64;            // k slice
 constexpr int kTLD = kTBK + 8;      // padded LDS row (bf16 elements)
 
-template <int BM>
+template <int BN, int BM>
 struct TiledSmem {
-  u16 w[2][kTBN * kTLD];
-  u16 x[2][BM * kTLD];
+  u16 w[BN * kTLD];
+  u16 x[BM * kTLD];
 };
 
-// acc[jn][jm][i] = C[n = 64*(wave&1) + 16*jn + 4*(lane/16) + i]
-//                   [m = (BM/2)*(wave>>1) + 16*jm + lane%16]
-template <int BM, class Prov>
-__device__ __forceinline__ void tiled_accumulate(const Prov& pv, TiledSmem<BM>& sm,
-                                                 f32x4 (&acc)[4][BM / 32]) {
-  constexpr int JM = BM / 32;
-  constexpr int XL = BM / 32;   // X chunks per thread per slice (BM*8/256)
+// Provider interface (per tile):
+//   int nseg(), seg_chunks()
+//   const u16* wbase(g, seg)    uniform base of weight rows [32g, 32g+32) in segment seg
+//   uint32_t   woff(r)          element offset of weight row r (0..BN-1) from its base
+//   const u16* xbase(seg)       uniform base of the token rows in segment seg
+//   uint32_t   xoff(r)          element offset of token row r (0..BM-1) from xbase
+// acc[jn][jm][i] = C[n = (BN/2)*(wave&1) + 32*jn + 8*(i/4) + 4*(lane/32) + i%4]
+//                   [m = (BM/2)*(wave>>1) + 32*jm + lane%32]
+// MFMAs of 32-row token blocks at or past rows_valid are skipped.
+template <int BN, int BM, class Prov>
+__device__ __forceinline__ void tiled_accumulate(const Prov& pv, TiledSmem<BN, BM>& sm,
+                                                 f32x16 (&acc)[BN / 64][BM / 64], int rows_valid) {
+  constexpr int JN = BN / 64, JM = BM / 64;
+  constexpr int WL = BN / 32;   // weight chunks per thread per slice
+  constexpr int XL = BM / 32;   // token chunks per thread per slice
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wn = wave & 1, wm = wave >> 1;
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
+  for (int a = 0; a < JN; ++a)
 #pragma unroll
-    for (int b = 0; b < JM; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < JM; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
 
   const int nseg = pv.nseg();
   const int cps = pv.seg_chunks();
   const int C = nseg * cps;
   const int lrow = tid >> 3;          // 0..31
   const int lcol = (tid & 7) * 8;     // element offset of this thread's 16 bytes
+  uint32_t wo[WL], xo[XL];
+#pragma unroll
+  for (int i = 0; i < WL; ++i) wo[i] = pv.woff(lrow + 32 * i) + lcol;
+#pragma unroll
+  for (int i = 0; i < XL; ++i) xo[i] = pv.xoff(lrow + 32 * i) + lcol;
+  const u16* const w_dummy = pv.wbase(0, 0);
+  const u16* const x_dummy = pv.xbase(0);
 
-  const u16* wr[4];
-  const u16* xr[XL];
-  auto set_rows = [&](int seg) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const u16* p = pv.w(lrow + 32 * i, seg);
-      wr[i] = p ? p + lcol : nullptr;
-    }
-#pragma unroll
-    for (int i = 0; i < XL; ++i) {
-      const u16* p = pv.x(lrow + 32 * i, seg);
-      xr[i] = p ? p + lcol : nullptr;
-    }
+  struct Stage {
+    u32x4 w[WL];
+    u32x4 x[XL];
   };
-  u32x4 wreg[4], xreg[XL];
-  auto load = [&](int cc) {
-    const int k = cc * kTBK;
+  // The slice past the end is loaded from one fixed address (all lanes the
+  // same, one cache line) so that every call issues the same loads.
+  auto load = [&](Stage& st, int c) {
+    const bool live = c < C;
+    const int cc = min(c, C - 1);
+    const int seg = cc / cps;
+    const uint32_t k = uint32_t(cc - seg * cps) * kTBK;
+    const u16* xb = live ? pv.xbase(seg) : x_dummy;
+    const uint32_t km = live ? k : 0u;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wreg[i] = wr[i] ? ld16_stream(wr[i] + k) : zero16();
+    for (int i = 0; i < WL; ++i)   // this thread's row lrow + 32 i lies in row group i
+      st.w[i] = ld16_at_stream(live ? pv.wbase(i, seg) : w_dummy, live ? wo[i] + km : 0u);
 #pragma unroll
-    for (int i = 0; i < XL; ++i) xreg[i] = xr[i] ? ld16(xr[i] + k) : zero16();
+    for (int i = 0; i < XL; ++i) st.x[i] = ld16_at(xb, live ? xo[i] + km : 0u);
   };
-  auto store = [&](int buf) {
+  auto store = [&](const Stage& st) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<u32x4*>(&sm.w[buf][(lrow + 32 * i) * kTLD + lcol]) = wreg[i];
+    for (int i = 0; i < WL; ++i)
+      *reinterpret_cast<u32x4*>(&sm.w[(lrow + 32 * i) * kTLD + lcol]) = st.w[i];
 #pragma unroll
     for (int i = 0; i < XL; ++i)
-      *reinterpret_cast<u32x4*>(&sm.x[buf][(lrow + 32 * i) * kTLD + lcol]) = xreg[i];
+      *reinterpret_cast<u32x4*>(&sm.x[(lrow + 32 * i) * kTLD + lcol]) = st.x[i];
   };
-
-  int seg = 0, cc = 0;
-  set_rows(0);
-  load(0);
-  store(0);
-  __syncthreads();
-  const int fr = lane & 15;
-  const int fk = (lane >> 4) * 8;
-  for (int c = 0; c < C; ++c) {
-    const int buf = c & 1;
-    const bool more = (c + 1) < C;
-    if (more) {
-      if (++cc == cps) {
-        cc = 0;
-        ++seg;
-        set_rows(seg);
-      }
-      load(cc);
-    }
+  const int fr = lane & 31;
+  const int fk = (lane >> 5) * 8;
+  auto compute = [&]() {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      u32x4 wf[4], xf[JM];
+    for (int ks = 0; ks < kTBK / 16; ++ks) {
+      u32x4 wf[JN], xf[JM];
 #pragma unroll
-      for (int jn = 0; jn < 4; ++jn)
+      for (int jn = 0; jn < JN; ++jn)
         wf[jn] = *reinterpret_cast<const u32x4*>(
-            &sm.w[buf][(wn * 64 + jn * 16 + fr) * kTLD + ks * 32 + fk]);
+            &sm.w[(wn * (BN / 2) + jn * 32 + fr) * kTLD + ks * 16 + fk]);
 #pragma unroll
       for (int jm = 0; jm < JM; ++jm)
         xf[jm] = *reinterpret_cast<const u32x4*>(
-            &sm.x[buf][(wm * (BM / 2) + jm * 16 + fr) * kTLD + ks * 32 + fk]);
+            &sm.x[(wm * (BM / 2) + jm * 32 + fr) * kTLD + ks * 16 + fk]);
 #pragma unroll
-      for (int jn = 0; jn < 4; ++jn)
+      for (int jm = 0; jm < JM; ++jm)
+        if (wm * (BM / 2) + jm * 32 < rows_valid) {
 #pragma unroll
-        for (int jm = 0; jm < JM; ++jm) acc[jn][jm] = mfma_bf16(wf[jn], xf[jm], acc[jn][jm]);
+          for (int jn = 0; jn < JN; ++jn) acc[jn][jm] = mfma32_bf16(wf[jn], xf[jm], acc[jn][jm]);
+        }
     }
-    if (more) store(buf ^ 1);
+  };
+
+  Stage st;
+  load(st, 0);
+  for (int c = 0; c < C; ++c) {
+    store(st);          // slice c
+    __syncthreads();
+    load(st, c + 1);    // in flight while slice c is multiplied
+    compute();
     __syncthreads();
   }
+}
+
+// Persistent, XCD-aware work split: workgroups are dispatched round-robin over
+// the 8 XCDs (b % 8), so the item space is cut into 8 contiguous parts and the
+// workgroups of one XCD stride through its part.  Items that share operands
+// and are adjacent in the item order then meet in the same L2.
+constexpr int kXcds = 8;
+
+struct XcdRange {
+  long next, step, end;
+};
+
+__device__ __forceinline__ XcdRange xcd_range(long total) {
+  const long G = gridDim.x;
+  const long groups = G >= kXcds ? kXcds : 1;
+  const long x = blockIdx.x % groups;
+  const long per = G / groups;                  // workgroups per XCD part
+  const long li = blockIdx.x / groups;
+  XcdRange r;
+  const long p0 = total * x / groups, p1 = total * (x + 1) / groups;
+  r.next = li < per ? p0 + li : p1;             // leftover workgroups idle
+  r.step = per;
+  r.end = p1;
+  return r;
 }
 
 }  // namespace beam

@@ -53,6 +53,18 @@ struct RouterSkinnyProv {
   }
 };
 
+// The skinny router handles small batches and layers with few experts (whose
+// 2E router rows would waste most of a tiled weight block); its token tile is
+// 16*MT rows, chosen so that the grid has enough workgroups.
+constexpr int kRouterSkinnyMaxT = 1024;
+__host__ __device__ inline bool router_use_skinny(int T, int E) { return T <= kRouterSkinnyMaxT || E <= 64; }
+__host__ __device__ inline int router_mt(int T, int E) {
+  const int nrb = (2 * E + 15) / 16;
+  if (T <= 16) return 1;
+  if (T <= 32) return 2;
+  return long(nrb) * ((T + 63) / 64) >= 256 ? 4 : 1;
+}
+
 // One workgroup per (16*MT tokens) x (16 router rows) x (k slice); 4 waves
 // split the slice.
 template <int MT>
@@ -80,40 +92,53 @@ __global__ __launch_bounds__(256) void k_router_skinny(RouterArgs a) {
   }
 }
 
-template <int BM>
+constexpr int kRouterBN = 64, kRouterBM = 256;
+
+// A tile covers rows [jb, jb + 64) of one of the two weight matrices
+// (which = 0: Wr, 1: Wm), so that its rows share one base address.
 struct RouterTiledProv {
   const RouterArgs* a;
-  int j0, t0;
+  int which, jb, t0;
   __device__ int nseg() const { return 1; }
   __device__ int seg_chunks() const { return a->D / 64; }
-  __device__ const u16* w(int r, int) const { return router_row(*a, j0 + r); }
-  __device__ const u16* x(int r, int) const {
+  __device__ const u16* wbase(int, int) const { return which ? a->wm : a->wr; }
+  __device__ uint32_t woff(int r) const {
+    const int j = jb + r;
+    return uint32_t((j < a->E ? j : 0) * a->D);
+  }
+  __device__ const u16* xbase(int) const { return a->x; }
+  __device__ uint32_t xoff(int r) const {
     const int t = t0 + r;
-    return t < a->T ? a->x + size_t(t) * a->D : nullptr;
+    return uint32_t((t < a->T ? t : 0) * a->D);
   }
 };
 
-// One workgroup per (BM tokens) x (128 router rows), whole k range.
-template <int BM>
-__global__ __launch_bounds__(256) void k_router_tiled(RouterArgs a) {
-  __shared__ TiledSmem<BM> sm;
-  const int nrb = (2 * a.E + kTBN - 1) / kTBN;
-  const int j0 = (blockIdx.x % nrb) * kTBN;
-  const int t0 = (blockIdx.x / nrb) * BM;
-  RouterTiledProv<BM> pv{&a, j0, t0};
-  f32x4 acc[4][BM / 32];
-  tiled_accumulate<BM>(pv, sm, acc);
+// Persistent: items are (token tile, matrix, 64-row block).
+__global__ __launch_bounds__(256, 2) void k_router_tiled(RouterArgs a) {
+  __shared__ TiledSmem<kRouterBN, kRouterBM> sm;
+  constexpr int JN = kRouterBN / 64, JM = kRouterBM / 64;
+  const int nrb = (a.E + kRouterBN - 1) / kRouterBN;   // blocks per matrix
+  const long total = long((a.T + kRouterBM - 1) / kRouterBM) * 2 * nrb;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wn = wave & 1, wm = wave >> 1;
+  for (XcdRange it = xcd_range(total); it.next < it.end; it.next += it.step) {
+    const int rb = int(it.next % (2 * nrb));
+    const int t0 = int(it.next / (2 * nrb)) * kRouterBM;
+    RouterTiledProv pv{&a, rb / nrb, (rb % nrb) * kRouterBN, t0};
+    f32x16 acc[JN][JM];
+    tiled_accumulate<kRouterBN, kRouterBM>(pv, sm, acc, a.T - t0);
 #pragma unroll
-  for (int jn = 0; jn < 4; ++jn)
+    for (int jn = 0; jn < JN; ++jn)
 #pragma unroll
-    for (int jm = 0; jm < BM / 32; ++jm) {
-      const int t = t0 + wm * (BM / 2) + jm * 16 + (lane & 15);
-      const int j = j0 + wn * 64 + jn * 16 + 4 * (lane >> 4);
+      for (int jm = 0; jm < JM; ++jm) {
+        const int t = t0 + wm * (kRouterBM / 2) + jm * 32 + (lane & 31);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) router_store(a, 0, t, j + i, acc[jn][jm][i]);
-    }
+        for (int i = 0; i < 16; ++i) {
+          const int jr = pv.jb + wn * (kRouterBN / 2) + jn * 32 + 8 * (i / 4) + 4 * (lane >> 5) + (i % 4);
+          if (jr < a.E) router_store(a, 0, t, pv.which * a.E + jr, acc[jn][jm][i]);
+        }
+      }
+  }
 }
 
 // fp32 layers: one thread per (token, router row), k in float4 steps.
@@ -145,15 +170,15 @@ __global__ __launch_bounds__(256) void k_router_f32(RouterArgsF32 a) {
 }
 
 int router_ksplit(const beam_moe_layer& L, int32_t T) {
-  if (L.dtype == BEAM_F32 || T > 64) return 1;
+  if (L.dtype == BEAM_F32 || !router_use_skinny(T, L.E)) return 1;
+  // Split k (at most 4 ways, so that selection reads at most 4 partial sums
+  // per logit) when the (row block x token block) grid is small.
   const int chunks = L.D / 64;
-  const int mt = T <= 16 ? 1 : (T <= 32 ? 2 : 4);
-  const int blocks = ((2 * L.E + 15) / 16) * ((T + 16 * mt - 1) / (16 * mt));
+  const int mt = router_mt(T, L.E);
+  const long blocks = long((2 * L.E + 15) / 16) * ((T + 16 * mt - 1) / (16 * mt));
   int best = 1;
-  // largest divisor of the chunk count that leaves >= 4 chunks per slice and
-  // brings the grid to about 256 workgroups
-  for (int ks = 1; ks <= chunks; ++ks)
-    if (chunks % ks == 0 && chunks / ks >= 4 && blocks * ks <= 320) best = ks;
+  for (int ks = 2; ks <= 4; ++ks)
+    if (chunks % ks == 0 && chunks / ks >= 4 && blocks * (ks - 1) < 256) best = ks;
   return best;
 }
 
@@ -170,9 +195,9 @@ hipError_t launch_router_logits(const beam_moe_layer& L, const void* x, int32_t 
   }
   const int KS = router_ksplit(L, T);
   RouterArgs a{(const u16*)x, (const u16*)L.w_router, (const u16*)L.w_mask, part, T, L.D, L.E, KS};
-  if (T <= 64) {
+  if (router_use_skinny(T, L.E)) {
     const int nrb = (2 * L.E + 15) / 16;
-    const int mt = T <= 16 ? 1 : (T <= 32 ? 2 : 4);
+    const int mt = router_mt(T, L.E);
     const int ntb = (T + 16 * mt - 1) / (16 * mt);
     const dim3 grid(unsigned(nrb * ntb * KS));
     prof_before("router_logits_skinny", s);
@@ -181,10 +206,13 @@ hipError_t launch_router_logits(const beam_moe_layer& L, const void* x, int32_t 
     else hipLaunchKernelGGL(k_router_skinny<4>, grid, dim3(256), 0, s, a);
     prof_after(s);
   } else {
-    const int nrb = (2 * L.E + kTBN - 1) / kTBN;
-    const int ntb = (T + 63) / 64;
+    const int nrb = (L.E + kRouterBN - 1) / kRouterBN;
+    const long items = long((T + kRouterBM - 1) / kRouterBM) * 2 * nrb;
+    long cap = resident_blocks((const void*)&k_router_tiled, 256);
+    cap = std::max<long>(8, cap / 8 * 8);
+    const unsigned grid = unsigned(std::max<long>(1, std::min<long>(items, cap)));
     prof_before("router_logits_tiled", s);
-    hipLaunchKernelGGL(k_router_tiled<64>, dim3(unsigned(nrb * ntb)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_router_tiled, dim3(grid), dim3(256), 0, s, a);
     prof_after(s);
   }
   return hipGetLastError();
@@ -406,6 +434,7 @@ __global__ __launch_bounds__(1024) void k_select(SelectArgs a) {
   constexpr int IL = NPER <= 4 ? TPW : 1;
 #pragma unroll
   for (int j0 = 0; j0 < TPW; j0 += IL) {
+    if (t0 + wave * TPW + j0 >= T) break;   // no valid token left in this wave
     float vals[IL][NPER];
 #pragma unroll
     for (int jj = 0; jj < IL; ++jj)
@@ -560,11 +589,18 @@ __global__ __launch_bounds__(1024) void k_scan(int T, int E, int nblk, int tile_
   __shared__ PlanSmem psm;
   const int tid = threadIdx.x;
   for (int e = tid; e < E; e += 1024) {
+    // exclusive running sum over blocks, 8 independent loads at a time
     int32_t run = 0;
-    for (int b = 0; b < nblk; ++b) {
-      const int32_t c = block_counts[size_t(b) * E + e];
-      block_counts[size_t(b) * E + e] = run;
-      run += c;
+    for (int b0 = 0; b0 < nblk; b0 += 8) {
+      int32_t c[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) c[u] = b0 + u < nblk ? block_counts[size_t(b0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (b0 + u < nblk) {
+          block_counts[size_t(b0 + u) * E + e] = run;
+          run += c[u];
+        }
     }
     psm.cnt[e] = run;
   }
