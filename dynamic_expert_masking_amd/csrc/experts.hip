@@ -41,7 +41,21 @@ struct ExpertArgs {
   float* o_sh;     // [T][D]
 };
 
-// Decodes work item w into (tile index, n-block, shared?).
+// Order of the shared items.  Every shared tile reads the same weights, so
+// the items are taken in groups of 8 weight blocks x nts tiles, weight block
+// fastest: item w and w + 8 read the same block, and the streaming kernels run
+// item w on XCD w % 8, so the tiles of one block meet in one L2.
+__device__ __forceinline__ void shared_item(long w2, int nts, int nbs, int& t, int& nb) {
+  constexpr int kX = 8;
+  const long g = w2 / (long(kX) * nts);
+  const int q = int(w2 - g * kX * nts);
+  const int r = min(kX, nbs - int(g) * kX);   // blocks in this group
+  t = q / r;
+  nb = int(g) * kX + q % r;
+}
+
+// Decodes work item w into (tile index, n-block, shared?): routed items
+// tile-major, then the shared items.
 __device__ __forceinline__ bool work_item(long w, int ntr, int nts, int nbr, int nbs, int& ti,
                                           int& nb, bool& shared) {
   const long wr = long(ntr) * nbr;
@@ -53,26 +67,25 @@ __device__ __forceinline__ bool work_item(long w, int ntr, int nts, int nbr, int
   }
   const long w2 = w - wr;
   if (w2 < long(nts) * nbs) {
-    // shared tiles: n-block-major, so the tiles that reuse one weight block
-    // are consecutive items (same workgroup, cache-warm)
-    ti = ntr + int(w2 % nts);
-    nb = int(w2 / nts);
+    int t;
+    shared_item(w2, nts, nbs, t, nb);
+    ti = ntr + t;
     shared = true;
     return true;
   }
   return false;
 }
 
-// Down items: routed (tile, d-block) tile-major, then shared d-block-major.
+// Down items: routed (tile, d-block) tile-major, then the shared items.
 __device__ __forceinline__ void down_item(long w, int ntr, int nts, int nb_all, int& ti, int& nb) {
   const long wr = long(ntr) * nb_all;
   if (w < wr) {
     ti = int(w / nb_all);
     nb = int(w % nb_all);
   } else {
-    const long w2 = w - wr;
-    ti = ntr + int(w2 % nts);
-    nb = int(w2 / nts);
+    int t;
+    shared_item(w - wr, nts, nb_all, t, nb);
+    ti = ntr + t;
   }
 }
 
@@ -80,15 +93,17 @@ __device__ __forceinline__ void down_item(long w, int ntr, int nts, int nb_all, 
 // gate/up + SwiGLU (bf16)
 // ---------------------------------------------------------------------------
 
-// Streaming (decode) gate/up: items are (tile, 16-row n-block); see
-// stream_engine.h.
-template <int MT>
+// Streaming (decode) gate/up: items are (tile, n-block of 16*NB intermediate
+// rows); the 2*NB streamed matrices are the gate and up rows of each 16-row
+// group, which share the token operand (see stream_engine.h).
+template <int MT, int NB>
 struct GateUpStream {
+  static constexpr int NMAT = 2 * NB;
   const ExpertArgs* a;
   int ntr, nts, nbr, nbs;
   long total;
   __device__ long total_items() const { return total; }
-  __device__ void decode(long item, int lane, StreamItem<2, MT>& it) const {
+  __device__ void decode(long item, int lane, StreamItem<NMAT, MT>& it) const {
     it.valid = item >= 0;
     it.nseg = 1;
     it.w_seg = 0;
@@ -98,7 +113,8 @@ struct GateUpStream {
     if (!it.valid) {
       it.cps = 1;
       it.w_row = 0;
-      it.w[0] = it.w[1] = (const u16*)a->wg;
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) it.w[m] = (const u16*)a->wg;
 #pragma unroll
       for (int b = 0; b < MT; ++b) it.x[b] = (const u16*)a->x;
       return;
@@ -109,8 +125,12 @@ struct GateUpStream {
     const Tile tl = a->tiles[ti];
     const u16* wg = shared ? (const u16*)a->sg : (const u16*)a->wg + size_t(tl.expert) * a->I * a->D;
     const u16* wu = shared ? (const u16*)a->su : (const u16*)a->wu + size_t(tl.expert) * a->I * a->D;
-    it.w[0] = wg + size_t(nb) * 16 * a->D;
-    it.w[1] = wu + size_t(nb) * 16 * a->D;
+#pragma unroll
+    for (int g = 0; g < NB; ++g) {
+      const size_t off = size_t(nb * NB + g) * 16 * a->D;
+      it.w[2 * g] = wg + off;
+      it.w[2 * g + 1] = wu + off;
+    }
 #pragma unroll
     for (int b = 0; b < MT; ++b) {
       const int r = 16 * b + (lane & 15);
@@ -119,7 +139,7 @@ struct GateUpStream {
       it.x[b] = (const u16*)a->x + size_t(t) * a->D;
     }
   }
-  __device__ void epilogue(long item, const f32x4 (&acc)[2][MT], int lane) const {
+  __device__ void epilogue(long item, const f32x4 (&acc)[NMAT][MT], int lane) const {
     int ti, nb;
     bool shared;
     work_item(item, ntr, nts, nbr, nbs, ti, nb, shared);
@@ -130,47 +150,52 @@ struct GateUpStream {
     for (int b = 0; b < MT; ++b) {
       const int r = 16 * b + (lane & 15);
       if (r < tl.rows) {
-        const f32x4 g = acc[0][b], u = acc[1][b];
-        const int n = nb * 16 + 4 * (lane >> 4);
-        ushort4 hv;
-        hv.x = f32_to_bf16(silu_f32(g[0]) * u[0]);
-        hv.y = f32_to_bf16(silu_f32(g[1]) * u[1]);
-        hv.z = f32_to_bf16(silu_f32(g[2]) * u[2]);
-        hv.w = f32_to_bf16(silu_f32(g[3]) * u[3]);
-        *reinterpret_cast<ushort4*>(hb + size_t(tl.row0 + r) * Iv + n) = hv;
+#pragma unroll
+        for (int g = 0; g < NB; ++g) {
+          const f32x4 gv = acc[2 * g][b], uv = acc[2 * g + 1][b];
+          const int n = (nb * NB + g) * 16 + 4 * (lane >> 4);
+          ushort4 hv;
+          hv.x = f32_to_bf16(silu_f32(gv[0]) * uv[0]);
+          hv.y = f32_to_bf16(silu_f32(gv[1]) * uv[1]);
+          hv.z = f32_to_bf16(silu_f32(gv[2]) * uv[2]);
+          hv.w = f32_to_bf16(silu_f32(gv[3]) * uv[3]);
+          *reinterpret_cast<ushort4*>(hb + size_t(tl.row0 + r) * Iv + n) = hv;
+        }
       }
     }
   }
 };
 
-template <int MT, int U, int KSPLIT>
+template <int MT, int NB, int U, int KSPLIT>
 __global__ __launch_bounds__(kStreamWaves * 64) void k_gate_up_stream(ExpertArgs a) {
-  __shared__ u16 lds[kStreamWaves * 2 * 2 * 16 * kLdsRow];
-  __shared__ f32x4 red[KSPLIT > 1 ? kStreamWaves * 2 * MT * kWave : 1];
-  GateUpStream<MT> pb;
+  constexpr int NMAT = 2 * NB;
+  __shared__ __align__(16) unsigned char lds[StreamLds<NMAT, MT, U, KSPLIT>::kBytes];
+  GateUpStream<MT, NB> pb;
   pb.a = &a;
   pb.ntr = a.plan->n_tiles_routed;
   pb.nts = a.plan->n_tiles_shared;
-  pb.nbr = a.I / 16;
-  pb.nbs = a.S > 0 ? (a.S * a.Is) / 16 : 1;
+  pb.nbr = a.I / (16 * NB);
+  pb.nbs = a.S > 0 ? (a.S * a.Is) / (16 * NB) : 1;
   pb.total = long(pb.ntr) * pb.nbr + long(pb.nts) * pb.nbs;
-  stream_run<2, MT, U, KSPLIT>(pb, lds, red);
+  stream_run<NMAT, MT, U, KSPLIT>(pb, lds);
 }
 
-// Streaming (decode) down: items are (tile, 16-row d-block); the fused
-// shared expert has one k segment per shared expert.
-template <int MT>
+// Streaming (decode) down: items are (tile, d-block of 16*NB output rows),
+// the NB 16-row groups streamed as NB matrices that share the h operand; the
+// fused shared expert has one k segment per shared expert.
+template <int MT, int NB>
 struct DownStream {
   const ExpertArgs* a;
   int ntr, nts, nb_all;
   long total;
   __device__ long total_items() const { return total; }
-  __device__ void decode(long item, int lane, StreamItem<1, MT>& it) const {
+  __device__ void decode(long item, int lane, StreamItem<NB, MT>& it) const {
     it.valid = item >= 0;
     if (!it.valid) {
       it.nseg = 1;
       it.cps = 1;
-      it.w[0] = (const u16*)a->wd;
+#pragma unroll
+      for (int g = 0; g < NB; ++g) it.w[g] = (const u16*)a->wd;
       it.w_row = it.w_seg = it.x_seg = 0;
 #pragma unroll
       for (int b = 0; b < MT; ++b) it.x[b] = (const u16*)a->h;
@@ -180,22 +205,25 @@ struct DownStream {
     down_item(item, ntr, nts, nb_all, ti, nb);
     const bool shared = ti >= ntr;
     const Tile tl = a->tiles[ti];
-    const int d0 = nb * 16;
+    const int d0 = nb * 16 * NB;
+    const u16* w0;
     if (shared) {
       it.nseg = a->S;
       it.cps = a->Is / 64;
-      it.w[0] = (const u16*)a->sd + size_t(d0) * a->Is;
+      w0 = (const u16*)a->sd + size_t(d0) * a->Is;
       it.w_row = a->Is;
       it.w_seg = long(a->D) * a->Is;
       it.x_seg = a->Is;
     } else {
       it.nseg = 1;
       it.cps = a->I / 64;
-      it.w[0] = (const u16*)a->wd + size_t(tl.expert) * a->D * a->I + size_t(d0) * a->I;
+      w0 = (const u16*)a->wd + size_t(tl.expert) * a->D * a->I + size_t(d0) * a->I;
       it.w_row = a->I;
       it.w_seg = 0;
       it.x_seg = 0;
     }
+#pragma unroll
+    for (int g = 0; g < NB; ++g) it.w[g] = w0 + size_t(16 * g) * it.w_row;
     const long hs = shared ? long(a->S) * a->Is : a->I;
     const u16* hb = shared ? (const u16*)a->h_sh : (const u16*)a->h;
 #pragma unroll
@@ -205,7 +233,7 @@ struct DownStream {
       it.x[b] = hb + size_t(tl.row0 + (r < tl.rows ? r : 0)) * hs;
     }
   }
-  __device__ void epilogue(long item, const f32x4 (&acc)[1][MT], int lane) const {
+  __device__ void epilogue(long item, const f32x4 (&acc)[NB][MT], int lane) const {
     int ti, nb;
     down_item(item, ntr, nts, nb_all, ti, nb);
     const bool shared = ti >= ntr;
@@ -214,26 +242,28 @@ struct DownStream {
 #pragma unroll
     for (int b = 0; b < MT; ++b) {
       const int r = 16 * b + (lane & 15);
-      const int d = nb * 16 + 4 * (lane >> 4);
       if (r < tl.rows) {
-        const f32x4 v = acc[0][b];
-        *reinterpret_cast<float4*>(ob + size_t(tl.row0 + r) * a->D + d) = make_float4(v[0], v[1], v[2], v[3]);
+#pragma unroll
+        for (int g = 0; g < NB; ++g) {
+          const int d = (nb * NB + g) * 16 + 4 * (lane >> 4);
+          const f32x4 v = acc[g][b];
+          *reinterpret_cast<float4*>(ob + size_t(tl.row0 + r) * a->D + d) = make_float4(v[0], v[1], v[2], v[3]);
+        }
       }
     }
   }
 };
 
-template <int MT, int U, int KSPLIT>
+template <int MT, int NB, int U, int KSPLIT>
 __global__ __launch_bounds__(kStreamWaves * 64) void k_down_stream(ExpertArgs a) {
-  __shared__ u16 lds[kStreamWaves * 2 * 1 * 16 * kLdsRow];
-  __shared__ f32x4 red[KSPLIT > 1 ? kStreamWaves * MT * kWave : 1];
-  DownStream<MT> pb;
+  __shared__ __align__(16) unsigned char lds[StreamLds<NB, MT, U, KSPLIT>::kBytes];
+  DownStream<MT, NB> pb;
   pb.a = &a;
   pb.ntr = a.plan->n_tiles_routed;
   pb.nts = a.plan->n_tiles_shared;
-  pb.nb_all = a.D / 16;
+  pb.nb_all = a.D / (16 * NB);
   pb.total = long(pb.ntr + pb.nts) * pb.nb_all;
-  stream_run<1, MT, U, KSPLIT>(pb, lds, red);
+  stream_run<NB, MT, U, KSPLIT>(pb, lds);
 }
 
 // Tiled (prefill): the BN weight rows of an n-block are BN/2 intermediate
@@ -550,10 +580,19 @@ static int stream_ksplit(long items_bound) {
   return 4;
 }
 
+// Single-tile (16-row) problems: the k split follows the chunks per item, so
+// that each wave's share still holds several 64-wide chunks, and items carry
+// two 16-row groups when that leaves at least two shares per wave of a full
+// grid (fewer, longer items cost less per byte; too few would idle CUs).
+static int stream_ksplit_chunks(int chunks) { return chunks >= 16 ? 4 : chunks >= 8 ? 2 : 1; }
+constexpr long kWideShares = 2 * kStreamGrid * kStreamWaves;
+
+// A multiple of 8, so that item i of the round-robin deal runs on XCD i % 8.
 static unsigned stream_grid(const void* kernel, long items_bound, int ksplit) {
   const long groups = kStreamWaves / ksplit;
-  const long cap = resident_blocks(kernel, kStreamWaves * 64);
-  return unsigned(std::max<long>(1, std::min<long>(cap, (items_bound + groups - 1) / groups)));
+  const long cap = std::max<long>(8, resident_blocks(kernel, kStreamWaves * 64) / 8 * 8);
+  const long want = ((items_bound + groups - 1) / groups + 7) / 8 * 8;
+  return unsigned(std::max<long>(8, std::min<long>(cap, want)));
 }
 
 // Upper bound on the number of tiles the scan can produce.
@@ -576,6 +615,35 @@ static unsigned persistent_grid(long items, long cap) {
   return unsigned(std::max<long>(g, 1));
 }
 
+// Launches the streaming gate/up variant <MT token blocks, NB row groups,
+// U-chunk stages> with k split ks (0: chosen from the item count).
+template <int MT, int NB, int U>
+static void gate_up_stream(const ExpertArgs& a, long ntr, long nts, int I, int Is_all, int ks,
+                           hipStream_t s) {
+  const long items = ntr * (I / (16 * NB)) + nts * (Is_all / (16 * NB));
+  if (ks == 0) ks = stream_ksplit(items);
+  const dim3 blk(kStreamWaves * 64);
+#define BEAM_GU(KS_)                                                                       \
+  hipLaunchKernelGGL((k_gate_up_stream<MT, NB, U, KS_>),                                   \
+                     dim3(stream_grid((const void*)&k_gate_up_stream<MT, NB, U, KS_>, items, KS_)), \
+                     blk, 0, s, a)
+  if (ks == 1) BEAM_GU(1); else if (ks == 2) BEAM_GU(2); else BEAM_GU(4);
+#undef BEAM_GU
+}
+
+template <int MT, int NB, int U>
+static void down_stream(const ExpertArgs& a, long tiles, int D, int ks, hipStream_t s) {
+  const long items = tiles * (D / (16 * NB));
+  if (ks == 0) ks = stream_ksplit(items);
+  const dim3 blk(kStreamWaves * 64);
+#define BEAM_DN(KS_)                                                                       \
+  hipLaunchKernelGGL((k_down_stream<MT, NB, U, KS_>),                                      \
+                     dim3(stream_grid((const void*)&k_down_stream<MT, NB, U, KS_>, items, KS_)), \
+                     blk, 0, s, a)
+  if (ks == 1) BEAM_DN(1); else if (ks == 2) BEAM_DN(2); else BEAM_DN(4);
+#undef BEAM_DN
+}
+
 hipError_t launch_gate_up(const beam_moe_layer& L, const void* x, int32_t T, int tile_rows,
                           const WsLayout&, const Ptrs& p, hipStream_t s) {
   const ExpertArgs a = expert_args(L, x, T, p);
@@ -589,22 +657,18 @@ hipError_t launch_gate_up(const beam_moe_layer& L, const void* x, int32_t T, int
     return hipGetLastError();
   }
   if (tile_rows <= 64) {
-    const long items = ntr * (L.I / 16) + nts * (L.n_shared ? (L.n_shared * L.I_shared) / 16 : 0);
-    const int ks = tile_rows == 16 ? 4 : stream_ksplit(items);
-    const dim3 blk(kStreamWaves * 64);
+    const int Is_all = L.n_shared ? L.n_shared * L.I_shared : 0;
     prof_before("gate_up_swiglu_stream", s);
-#define BEAM_GU(MT_, U_, KS_)                                                                  \
-  hipLaunchKernelGGL((k_gate_up_stream<MT_, U_, KS_>),                                         \
-                     dim3(stream_grid((const void*)&k_gate_up_stream<MT_, U_, KS_>, items, ks)), \
-                     blk, 0, s, a)
     if (tile_rows == 16) {
-      BEAM_GU(1, 1, 4);   // single-tile rows: four waves per item, one-chunk stages
-    } else if (tile_rows == 32) {
-      if (ks == 1) BEAM_GU(2, 2, 1); else if (ks == 2) BEAM_GU(2, 2, 2); else BEAM_GU(2, 2, 4);
-    } else {
-      if (ks == 1) BEAM_GU(4, 1, 1); else if (ks == 2) BEAM_GU(4, 1, 2); else BEAM_GU(4, 1, 4);
+      const int ks = stream_ksplit_chunks(L.D / 64);
+      const long items2 = ntr * (L.I / 32) + nts * (Is_all / 32);
+      if (items2 * ks >= kWideShares) gate_up_stream<1, 2, 1>(a, ntr, nts, L.I, Is_all, ks, s);
+      else gate_up_stream<1, 1, 1>(a, ntr, nts, L.I, Is_all, ks, s);
     }
-#undef BEAM_GU
+    else if (tile_rows == 32)
+      gate_up_stream<2, 1, 2>(a, ntr, nts, L.I, Is_all, 0, s);
+    else
+      gate_up_stream<4, 1, 1>(a, ntr, nts, L.I, Is_all, 0, s);
     prof_after(s);
   } else {
     const int ib = tile_rows == 256 ? 64 : 128;   // intermediate rows per tile
@@ -635,22 +699,16 @@ hipError_t launch_down(const beam_moe_layer& L, int32_t T, int tile_rows, const 
     return hipGetLastError();
   }
   if (tile_rows <= 64) {
-    const long items = (ntr + nts) * ((L.D + 15) / 16);
-    const int ks = tile_rows == 16 ? 4 : stream_ksplit(items);
-    const dim3 blk(kStreamWaves * 64);
     prof_before("down_stream", s);
-#define BEAM_DN(MT_, U_, KS_)                                                               \
-  hipLaunchKernelGGL((k_down_stream<MT_, U_, KS_>),                                         \
-                     dim3(stream_grid((const void*)&k_down_stream<MT_, U_, KS_>, items, ks)), \
-                     blk, 0, s, a)
     if (tile_rows == 16) {
-      BEAM_DN(1, 2, 4);
-    } else if (tile_rows == 32) {
-      if (ks == 1) BEAM_DN(2, 2, 1); else if (ks == 2) BEAM_DN(2, 2, 2); else BEAM_DN(2, 2, 4);
-    } else {
-      if (ks == 1) BEAM_DN(4, 2, 1); else if (ks == 2) BEAM_DN(4, 2, 2); else BEAM_DN(4, 2, 4);
+      const int ks = stream_ksplit_chunks(L.I / 64);
+      if ((ntr + nts) * (L.D / 32) * ks >= kWideShares) down_stream<1, 2, 1>(a, ntr + nts, L.D, ks, s);
+      else down_stream<1, 1, 2>(a, ntr + nts, L.D, ks, s);
     }
-#undef BEAM_DN
+    else if (tile_rows == 32)
+      down_stream<2, 1, 2>(a, ntr + nts, L.D, 0, s);
+    else
+      down_stream<4, 1, 2>(a, ntr + nts, L.D, 0, s);
     prof_after(s);
   } else {
     const int bn = tile_rows == 256 ? 128 : 256;

@@ -2,9 +2,10 @@
 //
 // Each work item is one 16-row block of NMAT weight matrices (e.g. gate and
 // up) applied to one tile of 16*MT token rows over the whole k range.
-// Persistent workgroups of 4 waves take contiguous, balanced ranges of items;
-// within a workgroup, groups of KSPLIT waves share an item and split its k
-// chunks (KSPLIT = 1: every wave streams whole items on its own).
+// Persistent workgroups of 4 waves take the items round-robin (workgroup b:
+// items b, b + G, b + 2G, ...); within a workgroup, groups of KSPLIT waves
+// share an item and split its k chunks (KSPLIT = 1: every wave streams whole
+// items on its own).
 //
 // Memory access: weights are read with coalesced, non-temporal 16-byte loads
 // in which 8 consecutive lanes cover one 128-byte line of a row, so every load
@@ -76,7 +77,22 @@ __device__ __forceinline__ void stream_issue(StreamStage<NMAT, MT, U>& st,
   }
 }
 
-// lds: this wave's 2 x NMAT tiles of 16 x kLdsRow bf16 (alternating per chunk).
+// LDS of one workgroup.  Each wave owns a region holding its transpose tiles:
+// NMAT tiles of 16 x kLdsRow bf16, twice when a stage has several chunks (so
+// consecutive chunks of a stage use alternate tiles).  With a k split, the
+// partial sums of the wave are exchanged through the same region once the
+// wave has consumed its share (a wave's LDS accesses complete in order).
+template <int NMAT, int MT, int U, int KSPLIT>
+struct StreamLds {
+  static constexpr int kBufs = U > 1 ? 2 : 1;
+  static constexpr int kTileBytes = kBufs * NMAT * 16 * kLdsRow * 2;
+  static constexpr int kRedBytes = KSPLIT > 1 ? NMAT * MT * kWave * 16 : 0;
+  static constexpr int kWaveBytes = kTileBytes > kRedBytes ? kTileBytes : kRedBytes;
+  static constexpr int kBytes = kStreamWaves * kWaveBytes;
+  static_assert(kWaveBytes % 16 == 0, "regions must stay 16-byte aligned");
+};
+
+// lds: this wave's transpose tiles (alternating per chunk when U > 1).
 template <int NMAT, int MT, int U>
 __device__ __forceinline__ void stream_consume(const StreamStage<NMAT, MT, U>& st, bool valid,
                                                int c_begin, int c_end, u16* lds, int lane,
@@ -86,7 +102,7 @@ __device__ __forceinline__ void stream_consume(const StreamStage<NMAT, MT, U>& s
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     if (!valid || c_begin + u >= c_end) continue;
-    u16* buf = lds + (u & 1) * NMAT * 16 * kLdsRow;
+    u16* buf = lds + (U > 1 ? (u & 1) : 0) * NMAT * 16 * kLdsRow;
     u32x4 f[NMAT][2];
 #pragma unroll
     for (int m = 0; m < NMAT; ++m) {
@@ -115,18 +131,27 @@ __device__ __forceinline__ void stream_consume(const StreamStage<NMAT, MT, U>& s
 //   void decode(long item, int lane, StreamItem<NMAT, MT>& it)   (sets it.valid)
 //   void epilogue(long item, const f32x4 (&acc)[NMAT][MT], int lane)
 // acc[m][b][i] = sum_k W_m[row 4*(lane/16)+i][k] * X[row 16*b + lane%16][k].
+// lds_all: StreamLds<NMAT, MT, U, KSPLIT>::kBytes bytes, 16-byte aligned.
 template <int NMAT, int MT, int U, int KSPLIT, class P>
-__device__ __forceinline__ void stream_run(P& prob, u16* lds_all, f32x4* red) {
+__device__ __forceinline__ void stream_run(P& prob, unsigned char* lds_all) {
+  using Lds = StreamLds<NMAT, MT, U, KSPLIT>;
   constexpr int GROUPS = kStreamWaves / KSPLIT;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int group = wave / KSPLIT, kw = wave % KSPLIT;
-  u16* lds = lds_all + wave * 2 * NMAT * 16 * kLdsRow;
+  u16* lds = reinterpret_cast<u16*>(lds_all + wave * Lds::kWaveBytes);
+  auto red = [&](int w) { return reinterpret_cast<f32x4*>(lds_all + w * Lds::kWaveBytes); };
 
+  // Items are dealt round-robin: the k-th item of workgroup b is b + G*k
+  // (G = gridDim.x), taken by group k % GROUPS in round k / GROUPS.  The whole
+  // grid thus sweeps the item list front to back, so the weight blocks in
+  // flight at any time are neighbours and spread evenly over the HBM
+  // channels; with G a multiple of 8, item i always runs on XCD i % 8.
   const long total = prob.total_items();
-  const long ib0 = total * blockIdx.x / gridDim.x;
-  const long ib1 = total * (blockIdx.x + 1) / gridDim.x;
-  const long rounds = (ib1 - ib0 + GROUPS - 1) / GROUPS;
+  const long G = gridDim.x;
+  const long mine_n = total > long(blockIdx.x) ? (total - blockIdx.x + G - 1) / G : 0;
+  const long rounds = (mine_n + GROUPS - 1) / GROUPS;
   if (rounds <= 0) return;   // uniform across the workgroup
+  auto item_of = [&](long k) { return k < mine_n ? long(blockIdx.x) + G * k : -1L; };
 
   // this wave's chunk share [cb, ce) of an item with C chunks
   auto share = [&](const StreamItem<NMAT, MT>& it, int& cb, int& ce) {
@@ -136,16 +161,16 @@ __device__ __forceinline__ void stream_run(P& prob, u16* lds_all, f32x4* red) {
   };
 
   StreamItem<NMAT, MT> cur, nxt;
-  long item = ib0 + group;
-  prob.decode(item < ib1 ? item : -1, lane, cur);
+  long item = item_of(group);
+  prob.decode(item, lane, cur);
   int cb, ce;
   share(cur, cb, ce);
   StreamStage<NMAT, MT, U> A, B;
   stream_issue<NMAT, MT, U>(A, cur, cb, ce, lane);
 
   for (long r = 0; r < rounds; ++r) {
-    const long nitem = item + GROUPS;
-    prob.decode((r + 1 < rounds && nitem < ib1) ? nitem : -1, lane, nxt);
+    const long nitem = item_of((r + 1) * GROUPS + group);
+    prob.decode(nitem, lane, nxt);
     int nb, ne;
     share(nxt, nb, ne);
     f32x4 acc[NMAT][MT];
@@ -178,18 +203,19 @@ __device__ __forceinline__ void stream_run(P& prob, u16* lds_all, f32x4* red) {
     if (ce <= cb) stream_issue<NMAT, MT, U>(A, nxt, nb, ne, lane);   // empty share
     // combine the group's partial sums (fixed wave order) and finish the item
     if (KSPLIT > 1) {
+      f32x4* mine = red(wave);
 #pragma unroll
       for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-        for (int b = 0; b < MT; ++b) red[((wave * NMAT + m) * MT + b) * kWave + lane] = acc[m][b];
+        for (int b = 0; b < MT; ++b) mine[(m * MT + b) * kWave + lane] = acc[m][b];
       __syncthreads();
       if (kw == 0) {
 #pragma unroll
         for (int m = 0; m < NMAT; ++m)
 #pragma unroll
           for (int b = 0; b < MT; ++b) {
-            f32x4 s = red[((wave * NMAT + m) * MT + b) * kWave + lane];
-            for (int w = 1; w < KSPLIT; ++w) s += red[(((wave + w) * NMAT + m) * MT + b) * kWave + lane];
+            f32x4 s = acc[m][b];
+            for (int w = 1; w < KSPLIT; ++w) s += red(wave + w)[(m * MT + b) * kWave + lane];
             acc[m][b] = s;
           }
         if (cur.valid) prob.epilogue(item, acc, lane);
