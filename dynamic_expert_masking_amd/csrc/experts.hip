@@ -569,17 +569,12 @@ static ExpertArgs expert_args(const beam_moe_layer& L, const void* x, int32_t T,
 
 // Persistent grid of the streaming kernels: as many workgroups as can be
 // resident at once (occupancy x CUs, queried once per kernel and device).
-constexpr long kStreamGrid = 512;   // for choosing the k split only
+constexpr long kStreamGrid = 512;   // a typical resident grid, for sizing choices only
 
-// Waves per item of the streaming kernels: split k when there are too few
-// items (an upper bound on them) to give every wave of the grid its own.
-static int stream_ksplit(long items_bound) {
-  const long waves = kStreamGrid * kStreamWaves;
-  if (items_bound >= 2 * waves) return 1;
-  if (items_bound >= waves) return 2;
-  return 4;
-}
-
+// The variants below were chosen by timing on MI355X over the decode batch
+// sizes of three layer shapes (d_model 1536 to 4096, d_ff 256 to 14336).
+// Multi-tile problems stream two 16-row groups per item; k is split four ways
+// only for d_model >= 4096 (gate/up) and two ways for d_ff >= 1024 (down).
 // Single-tile (16-row) problems: the k split follows the chunks per item, so
 // that each wave's share still holds several 64-wide chunks, and items carry
 // two 16-row groups when that leaves at least two shares per wave of a full
@@ -616,12 +611,11 @@ static unsigned persistent_grid(long items, long cap) {
 }
 
 // Launches the streaming gate/up variant <MT token blocks, NB row groups,
-// U-chunk stages> with k split ks (0: chosen from the item count).
+// U-chunk stages> with k split ks.
 template <int MT, int NB, int U>
 static void gate_up_stream(const ExpertArgs& a, long ntr, long nts, int I, int Is_all, int ks,
                            hipStream_t s) {
   const long items = ntr * (I / (16 * NB)) + nts * (Is_all / (16 * NB));
-  if (ks == 0) ks = stream_ksplit(items);
   const dim3 blk(kStreamWaves * 64);
 #define BEAM_GU(KS_)                                                                       \
   hipLaunchKernelGGL((k_gate_up_stream<MT, NB, U, KS_>),                                   \
@@ -634,7 +628,6 @@ static void gate_up_stream(const ExpertArgs& a, long ntr, long nts, int I, int I
 template <int MT, int NB, int U>
 static void down_stream(const ExpertArgs& a, long tiles, int D, int ks, hipStream_t s) {
   const long items = tiles * (D / (16 * NB));
-  if (ks == 0) ks = stream_ksplit(items);
   const dim3 blk(kStreamWaves * 64);
 #define BEAM_DN(KS_)                                                                       \
   hipLaunchKernelGGL((k_down_stream<MT, NB, U, KS_>),                                      \
@@ -666,9 +659,9 @@ hipError_t launch_gate_up(const beam_moe_layer& L, const void* x, int32_t T, int
       else gate_up_stream<1, 1, 1>(a, ntr, nts, L.I, Is_all, ks, s);
     }
     else if (tile_rows == 32)
-      gate_up_stream<2, 1, 2>(a, ntr, nts, L.I, Is_all, 0, s);
+      gate_up_stream<2, 2, 1>(a, ntr, nts, L.I, Is_all, L.D >= 4096 ? 4 : 2, s);
     else
-      gate_up_stream<4, 1, 1>(a, ntr, nts, L.I, Is_all, 0, s);
+      gate_up_stream<4, 2, 1>(a, ntr, nts, L.I, Is_all, L.D >= 4096 ? 4 : 1, s);
     prof_after(s);
   } else {
     const int ib = tile_rows == 256 ? 64 : 128;   // intermediate rows per tile
@@ -706,9 +699,9 @@ hipError_t launch_down(const beam_moe_layer& L, int32_t T, int tile_rows, const 
       else down_stream<1, 1, 2>(a, ntr + nts, L.D, ks, s);
     }
     else if (tile_rows == 32)
-      down_stream<2, 1, 2>(a, ntr + nts, L.D, 0, s);
+      down_stream<2, 2, 1>(a, ntr + nts, L.D, 2, s);
     else
-      down_stream<4, 1, 2>(a, ntr + nts, L.D, 0, s);
+      down_stream<4, 2, 1>(a, ntr + nts, L.D, L.I >= 1024 ? 2 : 1, s);
     prof_after(s);
   } else {
     const int bn = tile_rows == 256 ? 128 : 256;
