@@ -39,6 +39,7 @@ WsLayout workspace_layout(const beam_moe_layer& L, int32_t T) {
     return o;
   };
   w.plan = take(sizeof(Plan));
+  w.arrive = take(sizeof(uint32_t));
   w.logits = take(size_t(router_ksplit(L, T)) * T * 2 * L.E * 4);
   w.idx = take(TK * 4);
   w.gates = take(TK * 4);
@@ -168,6 +169,7 @@ static int check_route_out(const beam_route_out* out) {
 static Ptrs carve(const WsLayout& w, void* ws, const beam_route_out* out) {
   char* b = static_cast<char*>(ws);
   Ptrs p;
+  p.arrive = reinterpret_cast<uint32_t*>(b + w.arrive);
   p.logits = reinterpret_cast<float*>(b + w.logits);
   p.idx = out ? out->topk_idx : reinterpret_cast<int32_t*>(b + w.idx);
   p.gates = out ? out->gates : reinterpret_cast<float*>(b + w.gates);
@@ -194,9 +196,9 @@ static Ptrs carve(const WsLayout& w, void* ws, const beam_route_out* out) {
 
 static int run_routing(const beam_moe_layer& L, const void* x, int32_t T, int tile_rows,
                        const Ptrs& p, hipStream_t s) {
-  BEAM_TRY(launch_router_logits(L, x, T, p.logits, s));
+  BEAM_TRY(launch_router_logits(L, x, T, p, s));
   BEAM_TRY(launch_select(L, T, tile_rows, p, s));
-  if (!select_builds_plan(T)) BEAM_TRY(launch_scan(L, T, tile_rows, p, s));
+  if (!select_builds_plan(L, T)) BEAM_TRY(launch_scan(L, T, tile_rows, p, s));
   return BEAM_OK;
 }
 
@@ -232,7 +234,7 @@ int beam_moe_forward(const beam_moe_layer* layer, const void* x, int32_t T, void
   const Ptrs p = carve(lay, ws, out);
   const int tile_rows = expert_tile_rows(*layer, T);
   if ((st = run_routing(*layer, x, T, tile_rows, p, s)) != BEAM_OK) return st;
-  if (!select_builds_plan(T)) BEAM_TRY(launch_scatter(*layer, T, p, s));
+  if (!select_builds_plan(*layer, T)) BEAM_TRY(launch_scatter(*layer, T, p, s));
   BEAM_TRY(launch_gate_up(*layer, x, T, tile_rows, lay, p, s));
   BEAM_TRY(launch_down(*layer, T, tile_rows, lay, p, s));
   BEAM_TRY(launch_combine(*layer, T, p, y, s));

@@ -35,7 +35,7 @@ struct Tile {
 };
 
 struct WsLayout {
-  size_t plan, logits, idx, gates, mask, counts, rank, block_counts, expert_off, tiles, perm_token,
+  size_t plan, arrive, logits, idx, gates, mask, counts, rank, block_counts, expert_off, tiles, perm_token,
       slot_pos, h, h_shared, o, o_shared, total;
   int32_t max_tiles;
 };
@@ -48,6 +48,7 @@ WsLayout workspace_layout(const beam_moe_layer& L, int32_t T);
 
 struct Ptrs {
   // routing
+  uint32_t* arrive;   // arrival counter of the selection kernel (zeroed by the router kernel)
   float* logits;
   int32_t* idx;
   float* gates;
@@ -68,12 +69,14 @@ struct Ptrs {
 };
 
 // ---- launchers (return hipSuccess or the launch error) ----
-hipError_t launch_router_logits(const beam_moe_layer& L, const void* x, int32_t T, float* part,
+hipError_t launch_router_logits(const beam_moe_layer& L, const void* x, int32_t T, const Ptrs& p,
                                 hipStream_t s);
+// True when the selection kernel also builds the plan and places the pairs
+// (the per-expert token bitmaps of the batch fit in one workgroup's LDS);
+// otherwise the scan and scatter kernels follow it.
+bool select_builds_plan(const beam_moe_layer& L, int32_t T);
 hipError_t launch_select(const beam_moe_layer& L, int32_t T, int tile_rows, const Ptrs& p,
                          hipStream_t s);
-// True when the selection kernel also builds the plan and places the pairs.
-bool select_builds_plan(int32_t T);
 hipError_t launch_scan(const beam_moe_layer& L, int32_t T, int tile_rows, const Ptrs& p,
                        hipStream_t s);
 hipError_t launch_scatter(const beam_moe_layer& L, int32_t T, const Ptrs& p, hipStream_t s);

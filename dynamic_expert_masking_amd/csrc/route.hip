@@ -23,6 +23,7 @@ struct RouterArgs {
   const u16* wr;
   const u16* wm;
   float* part;
+  uint32_t* arrive;   // selection's arrival counter, zeroed here for the next kernel
   int T, D, E, KS;
 };
 
@@ -71,6 +72,7 @@ template <int MT>
 __global__ __launch_bounds__(256) void k_router_skinny(RouterArgs a) {
   __shared__ f32x4 red[4 * MT * kWave];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *a.arrive = 0u;
   const int nrb = (2 * a.E + 15) / 16;
   const int ks = blockIdx.x % a.KS;
   const int rest = blockIdx.x / a.KS;
@@ -121,6 +123,7 @@ __global__ __launch_bounds__(256, 2) void k_router_tiled(RouterArgs a) {
   const long total = long((a.T + kRouterBM - 1) / kRouterBM) * 2 * nrb;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wn = wave & 1, wm = wave >> 1;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *a.arrive = 0u;
   for (XcdRange it = xcd_range(total); it.next < it.end; it.next += it.step) {
     const int rb = int(it.next % (2 * nrb));
     const int t0 = int(it.next / (2 * nrb)) * kRouterBM;
@@ -147,10 +150,12 @@ struct RouterArgsF32 {
   const float* wr;
   const float* wm;
   float* part;
+  uint32_t* arrive;
   int T, D, E;
 };
 
 __global__ __launch_bounds__(256) void k_router_f32(RouterArgsF32 a) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) *a.arrive = 0u;
   const long q = long(blockIdx.x) * blockDim.x + threadIdx.x;
   const int R = 2 * a.E;
   if (q >= long(a.T) * R) return;
@@ -182,11 +187,12 @@ int router_ksplit(const beam_moe_layer& L, int32_t T) {
   return best;
 }
 
-hipError_t launch_router_logits(const beam_moe_layer& L, const void* x, int32_t T, float* part,
+hipError_t launch_router_logits(const beam_moe_layer& L, const void* x, int32_t T, const Ptrs& p,
                                 hipStream_t s) {
+  float* part = p.logits;
   if (L.dtype == BEAM_F32) {
-    RouterArgsF32 a{(const float*)x, (const float*)L.w_router, (const float*)L.w_mask, part, T,
-                    L.D, L.E};
+    RouterArgsF32 a{(const float*)x, (const float*)L.w_router, (const float*)L.w_mask, part,
+                    p.arrive, T, L.D, L.E};
     const long n = long(T) * 2 * L.E;
     prof_before("router_logits_f32", s);
     hipLaunchKernelGGL(k_router_f32, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, a);
@@ -194,7 +200,7 @@ hipError_t launch_router_logits(const beam_moe_layer& L, const void* x, int32_t 
     return hipGetLastError();
   }
   const int KS = router_ksplit(L, T);
-  RouterArgs a{(const u16*)x, (const u16*)L.w_router, (const u16*)L.w_mask, part, T, L.D, L.E, KS};
+  RouterArgs a{(const u16*)x, (const u16*)L.w_router, (const u16*)L.w_mask, part, p.arrive, T, L.D, L.E, KS};
   if (router_use_skinny(T, L.E)) {
     const int nrb = (2 * L.E + 15) / 16;
     const int mt = router_mt(T, L.E);
@@ -221,54 +227,62 @@ hipError_t launch_router_logits(const beam_moe_layer& L, const void* x, int32_t 
 // ---------------------------------------------------------------------------
 // Plan: from per-expert pair counts (in LDS), the expert offsets of the
 // compacted pair order and the tile list.  Experts with no surviving pair
-// get no tile, so their weights are never read.  Runs in one 1024-thread
-// workgroup.  On return s_off holds the exclusive offsets.
+// get no tile, so their weights are never read.  Runs in one workgroup of NT
+// threads.  On return sm.off holds the exclusive offsets.
 // ---------------------------------------------------------------------------
 
-// Exclusive prefix sums of two arrays of n <= 1024 entries at once
-// (blockDim.x == 1024): wave-level scans, then a scan of the 16 wave totals.
-__device__ __forceinline__ void block_exclusive_scan2(int32_t* v1, int32_t* v2, int n,
-                                                      int32_t* tmp /* >= 64 entries */) {
+// In-place exclusive prefix sums of two arrays of n entries at once, in
+// passes of NT entries: wave-level scans, then the wave totals.
+template <int NT>
+__device__ void block_exclusive_scan2(int32_t* v1, int32_t* v2, int n,
+                                      int32_t* tmp /* >= 2 * NT / 64 entries */) {
+  constexpr int NW = NT / kWave;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int32_t a = tid < n ? v1[tid] : 0;
-  const int32_t b = tid < n ? v2[tid] : 0;
-  const int32_t ia = wave_inclusive_scan_i32(a, lane);
-  const int32_t ib = wave_inclusive_scan_i32(b, lane);
-  if (lane == 63) {
-    tmp[wave] = ia;
-    tmp[16 + wave] = ib;
-  }
-  __syncthreads();
-  if (wave == 0) {
-    const int32_t xa = lane < 16 ? tmp[lane] : 0;
-    const int32_t xb = lane < 16 ? tmp[16 + lane] : 0;
-    const int32_t sa = wave_inclusive_scan_i32(xa, lane);
-    const int32_t sb = wave_inclusive_scan_i32(xb, lane);
-    if (lane < 16) {
-      tmp[32 + lane] = sa - xa;
-      tmp[48 + lane] = sb - xb;
+  int32_t c1 = 0, c2 = 0;   // totals of the earlier passes
+  for (int base = 0; base < n; base += NT) {
+    const int i = base + tid;
+    const int32_t a = i < n ? v1[i] : 0;
+    const int32_t b = i < n ? v2[i] : 0;
+    const int32_t ia = wave_inclusive_scan_i32(a, lane);
+    const int32_t ib = wave_inclusive_scan_i32(b, lane);
+    if (lane == 63) {
+      tmp[wave] = ia;
+      tmp[NW + wave] = ib;
     }
+    __syncthreads();
+    int32_t pa = c1, pb = c2;
+    for (int w = 0; w < NW; ++w) {
+      const int32_t ta = tmp[w], tb = tmp[NW + w];
+      if (w < wave) {
+        pa += ta;
+        pb += tb;
+      }
+      c1 += ta;
+      c2 += tb;
+    }
+    if (i < n) {
+      v1[i] = pa + ia - a;
+      v2[i] = pb + ib - b;
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  if (tid < n) {
-    v1[tid] = tmp[32 + wave] + ia - a;
-    v2[tid] = tmp[48 + wave] + ib - b;
-  }
-  __syncthreads();
 }
 
 struct PlanSmem {
   int32_t cnt[kMaxExperts];
   int32_t off[kMaxExperts];
   int32_t toff[kMaxExperts];
-  int32_t tmp[1024];
+  int32_t tmp[32];
+  int32_t act;
 };
 
+template <int NT>
 __device__ void build_plan(PlanSmem& sm, int T, int E, int tile_rows, int has_shared,
                            int32_t* __restrict__ counts, int32_t* __restrict__ expert_off,
                            Plan* __restrict__ plan, Tile* __restrict__ tiles) {
-  const int tid = threadIdx.x;
-  for (int e = tid; e < E; e += 1024) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (tid == 0) sm.act = 0;
+  for (int e = tid; e < E; e += NT) {
     const int32_t c = sm.cnt[e];
     counts[e] = c;
     sm.off[e] = c;
@@ -277,26 +291,29 @@ __device__ void build_plan(PlanSmem& sm, int T, int E, int tile_rows, int has_sh
   __syncthreads();
   const int32_t last_cnt = sm.cnt[E - 1];
   const int32_t last_tiles = sm.toff[E - 1];
-  block_exclusive_scan2(sm.off, sm.toff, E, sm.tmp);
+  block_exclusive_scan2<NT>(sm.off, sm.toff, E, sm.tmp);
   const int32_t P = sm.off[E - 1] + last_cnt;
   const int32_t ntr = sm.toff[E - 1] + last_tiles;
   const int32_t nts = has_shared ? (T + tile_rows - 1) / tile_rows : 0;
-  int act = 0;
-  for (int e = tid; e < E; e += 1024) {
-    expert_off[e] = sm.off[e];
-    const int c = sm.cnt[e];
-    act += c > 0;
-    const int nt = (c + tile_rows - 1) / tile_rows;
-    for (int j = 0; j < nt; ++j) {
-      Tile tl;
-      tl.expert = e;
-      tl.row0 = sm.off[e] + j * tile_rows;
-      tl.rows = min(tile_rows, c - j * tile_rows);
-      tl.pad = 0;
-      tiles[sm.toff[e] + j] = tl;
+  for (int e0 = 0; e0 < E; e0 += NT) {   // whole waves, for the ballot
+    const int e = e0 + tid;
+    const int32_t c = e < E ? sm.cnt[e] : 0;
+    const unsigned long long act = __ballot(c > 0);
+    if (lane == 0 && act) atomicAdd(&sm.act, int32_t(__popcll(act)));
+    if (e < E) {
+      expert_off[e] = sm.off[e];
+      const int nt = (c + tile_rows - 1) / tile_rows;
+      for (int j = 0; j < nt; ++j) {
+        Tile tl;
+        tl.expert = e;
+        tl.row0 = sm.off[e] + j * tile_rows;
+        tl.rows = min(tile_rows, c - j * tile_rows);
+        tl.pad = 0;
+        tiles[sm.toff[e] + j] = tl;
+      }
     }
   }
-  for (int j = tid; j < nts; j += 1024) {
+  for (int j = tid; j < nts; j += NT) {
     Tile tl;
     tl.expert = E;
     tl.row0 = j * tile_rows;
@@ -304,19 +321,14 @@ __device__ void build_plan(PlanSmem& sm, int T, int E, int tile_rows, int has_sh
     tl.pad = 0;
     tiles[ntr + j] = tl;
   }
-  sm.tmp[tid] = act;
   __syncthreads();
-  for (int o = 512; o >= 1; o >>= 1) {
-    if (tid < o) sm.tmp[tid] += sm.tmp[tid + o];
-    __syncthreads();
-  }
   if (tid == 0) {
     expert_off[E] = P;
     Plan pl;
     pl.pairs = P;
     pl.n_tiles_routed = ntr;
     pl.n_tiles_shared = nts;
-    pl.active_experts = sm.tmp[0];
+    pl.active_experts = sm.act;
     *plan = pl;
   }
   __syncthreads();
@@ -325,23 +337,30 @@ __device__ void build_plan(PlanSmem& sm, int T, int E, int tile_rows, int has_sh
 // ---------------------------------------------------------------------------
 // Selection: top-K by descending router logit (equal logits: lower expert
 // index first), softmax over the K kept logits, mask bit m_k = [z >= 0] on
-// the candidates, g_hat = g * m.  One 1024-thread workgroup per 64-token
-// block; each of its 16 waves handles 4 tokens, with all four tokens' logits
-// loaded before any is processed.  Then, per block, the block-local rank of
-// every surviving pair among the block's pairs of the same expert (token
-// order) and the block's per-expert pair counts.  When the batch is a single
-// block, the same workgroup also builds the plan and places every pair, so
-// the scan and scatter kernels are not launched.
+// the candidates, g_hat = g * m.
+//
+// Two forms.  When the batch's per-expert token bitmaps (E x ceil(T/64)
+// words) fit in LDS, one wave selects each token and the workgroup that
+// finishes last builds the plan and places every pair (k_select_plan).
+// Otherwise one 1024-thread workgroup handles each 64-token block and records
+// block-local ranks and counts, and the scan and scatter kernels follow
+// (k_select).
 // ---------------------------------------------------------------------------
 
 constexpr int kSelWaves = 16;
 constexpr int kSelTokPerWave = kSelBlock / kSelWaves;   // 4
+// Limits of the one-launch form: the LDS of the plan-building workgroup, and
+// the batch size beyond which the arrival of many workgroups (each publishing
+// its selections device-wide) costs more than the separate scan and scatter
+// launches (timed on MI355X).
+constexpr int kPlanWords = 4096;   // E * ceil(T / 64) bitmap words
+constexpr int kPlanPairs = 8192;   // T * K selections
+constexpr int kPlanTokens = 512;   // T
+constexpr int kPlanThreads = 256;  // four tokens per workgroup, one wave per SIMD
 
-// Inverse of float_key on the high word of a selection key.
-__device__ __forceinline__ float key_float(unsigned long long key) {
-  uint32_t u = uint32_t(key >> 32);
-  u = (u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u;
-  return __uint_as_float(u);
+bool select_builds_plan(const beam_moe_layer& L, int32_t T) {
+  return long(L.E) * ((T + kSelBlock - 1) / kSelBlock) <= kPlanWords &&
+         long(T) * L.K <= kPlanPairs && T <= kPlanTokens;
 }
 
 struct SelectArgs {
@@ -355,7 +374,8 @@ struct SelectArgs {
   uint32_t* mask;
   int32_t* rank;
   int32_t* block_counts;
-  // single-block batches
+  // plan (k_select_plan)
+  uint32_t* arrive;
   int tile_rows, has_shared;
   int32_t* counts;
   int32_t* expert_off;
@@ -365,12 +385,180 @@ struct SelectArgs {
   int32_t* slot_pos;
 };
 
+// Token t's selection by one wave.  Expert e's logits are held by lane
+// e % 64 in register e / 64; the KS partial sums are added in ks order, then
+// the biases.  Round k of the top-K takes the wave-wide maximum M of the
+// remaining logits and the lowest expert index holding M (ballot and
+// find-first-set), then removes that entry.
+template <int NPER>
+__device__ __forceinline__ void select_token(const SelectArgs& a, int t, int lane) {
+  const int E = a.E, K = a.K;
+  float pr[4][NPER], pz[4][NPER];
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) {
+      const int e = lane + kWave * i;
+      pr[u][i] = pz[u][i] = 0.f;
+      if (u < a.KS && e < E) {
+        const float* row = a.part + (size_t(u) * a.T + t) * 2 * E;
+        pr[u][i] = row[e];
+        pz[u][i] = row[E + e];
+      }
+    }
+  float vals[NPER], zv[NPER];
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    const int e = lane + kWave * i;
+    float r = 0.f, z = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      r += pr[u][i];
+      z += pz[u][i];
+    }
+    r += (a.br && e < E) ? a.br[e] : 0.f;
+    z += (a.bm && e < E) ? a.bm[e] : 0.f;
+    vals[i] = e < E ? r + 0.0f : -__builtin_inff();   // + 0: -0 and +0 compare alike
+    zv[i] = z;
+  }
+  int my_e = 0;
+  float my_r = 0.f;
+  for (int k = 0; k < K; ++k) {
+    float m[1] = {vals[0]};
+#pragma unroll
+    for (int i = 1; i < NPER; ++i) m[0] = fmaxf(m[0], vals[i]);
+    wave_max_f32_n<1>(m);
+    int win = 0;
+#pragma unroll
+    for (int i = NPER - 1; i >= 0; --i) {
+      const unsigned long long b = __ballot(vals[i] == m[0] && lane + kWave * i < E);
+      if (b) win = kWave * i + __builtin_ctzll(b);
+    }
+#pragma unroll
+    for (int i = 0; i < NPER; ++i)
+      if (win == kWave * i + lane) vals[i] = -__builtin_inff();
+    if (lane == k) {
+      my_e = win;
+      my_r = m[0];
+    }
+  }
+  const bool slot = lane < K;
+  const int e_k = slot ? my_e : 0;
+  const float r_k = slot ? my_r : 0.f;
+  float z_k = 0.f;
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    const float c = __shfl(zv[i], e_k & 63, kWave);
+    if (i == (e_k >> 6)) z_k = c;
+  }
+  const float r_0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r_k), 0));
+  const float ex = slot ? expf(r_k - r_0) : 0.f;
+  const float sum = wave_sum_f32(ex);
+  const bool keep = slot && z_k >= 0.f;
+  const unsigned long long bal = __ballot(keep);
+  if (slot) {
+    a.idx[size_t(t) * K + lane] = e_k;
+    a.gates[size_t(t) * K + lane] = keep ? ex / sum : 0.f;
+  }
+  if (lane == 0) a.mask[t] = uint32_t(bal);
+}
+
+struct BitmapPlanSmem {
+  unsigned long long bits[kPlanWords];   // [E][W]: bit t%64 of word t/64: token t keeps e
+  int32_t pre[kPlanWords];               // [E][W]: pairs of expert e in earlier words
+  uint16_t idx[kPlanPairs];              // selections of the batch, [T][K]
+  uint32_t mask[kPlanTokens];            // mask bits of the batch
+  PlanSmem plan;
+  int32_t last;
+};
+
+// Copies n entries of src (global) into dst (LDS), four independent loads in
+// flight per thread.
+template <int NT, class S, class D>
+__device__ __forceinline__ void stage_to_lds(D* dst, const S* __restrict__ src, int n) {
+  const int tid = threadIdx.x;
+  for (int i0 = 0; i0 < n; i0 += 4 * NT) {
+    S v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * NT + tid;
+      v[u] = src[i < n ? i : 0];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * NT + tid;
+      if (i < n) dst[i] = D(v[u]);
+    }
+  }
+}
+
+// One wave per token, NT / 64 tokens per workgroup; the last workgroup to
+// arrive builds the plan.  Positions: expert-major, tokens ascending within
+// an expert, i.e. off[e] + (kept tokens of e before t).
+template <int NPER, int NT>
+__global__ __launch_bounds__(NT) void k_select_plan(SelectArgs a) {
+  __shared__ BitmapPlanSmem sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int T = a.T, E = a.E, K = a.K;
+  const int t = blockIdx.x * (NT / kWave) + wave;
+  if (t < T) select_token<NPER>(a, t, lane);
+
+  // This workgroup's selections are made visible device-wide before it is
+  // counted; the workgroup that arrives last then sees all of them.  The
+  // counter was zeroed by the router kernel of the same call, and is zeroed
+  // again below.
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) sm.last = atomicAdd(a.arrive, 1u) == gridDim.x - 1 ? 1 : 0;
+  __syncthreads();
+  if (!sm.last) return;
+  __threadfence();
+
+  const int W = (T + kSelBlock - 1) / kSelBlock;
+  const int TK = T * K;
+  stage_to_lds<NT>(sm.mask, a.mask, T);
+  stage_to_lds<NT>(sm.idx, a.idx, TK);
+  for (int i = tid; i < E * W; i += NT) sm.bits[i] = 0ull;
+  __syncthreads();
+  for (int q = tid; q < TK; q += NT) {
+    const int tt = q / K, k = q - tt * K;
+    if ((sm.mask[tt] >> k) & 1u) atomicOr(&sm.bits[sm.idx[q] * W + (tt >> 6)], 1ull << (tt & 63));
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += NT) {
+    int32_t run = 0;
+    for (int w = 0; w < W; ++w) {
+      sm.pre[e * W + w] = run;
+      run += __popcll(sm.bits[e * W + w]);
+    }
+    sm.plan.cnt[e] = run;
+  }
+  __syncthreads();
+  build_plan<NT>(sm.plan, T, E, a.tile_rows, a.has_shared, a.counts, a.expert_off, a.plan, a.tiles);
+  for (int q = tid; q < TK; q += NT) {
+    const int tt = q / K, k = q - tt * K;
+    int pos = -1;
+    if ((sm.mask[tt] >> k) & 1u) {
+      const int e = sm.idx[q], w = tt >> 6;
+      const unsigned long long before = sm.bits[e * W + w] & ((1ull << (tt & 63)) - 1ull);
+      pos = sm.plan.off[e] + sm.pre[e * W + w] + __popcll(before);
+      a.perm_token[pos] = tt;
+    }
+    a.slot_pos[q] = pos;
+  }
+  if (tid == 0) *a.arrive = 0u;
+}
+
+// Multi-block form: one 1024-thread workgroup per 64-token block; each of its
+// 16 waves handles 4 tokens, with all four tokens' logits loaded before any
+// is processed.  Then, per block, the block-local rank of every surviving
+// pair among the block's pairs of the same expert (token order) and the
+// block's per-expert pair counts.
 template <int NPER>
 __global__ __launch_bounds__(1024) void k_select(SelectArgs a) {
   __shared__ unsigned long long bits[kMaxExperts];
   __shared__ int32_t s_idx[kSelBlock * 32];
   __shared__ uint32_t s_mask[kSelBlock];
-  __shared__ PlanSmem psm;
   constexpr int TPW = kSelTokPerWave;
   constexpr int KB = NPER >= 4 ? 1 : 4 / NPER;   // partial slices loaded per round
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -378,7 +566,6 @@ __global__ __launch_bounds__(1024) void k_select(SelectArgs a) {
   const int t0 = blk * kSelBlock;
   const int T = a.T, E = a.E, K = a.K;
   for (int e = tid; e < E; e += blockDim.x) bits[e] = 0ull;
-
   // r and z of this wave's tokens: partial sums added in ks order, then the
   // biases.  All loads of a round are issued before any is used.
   float rv[TPW][NPER], zv[TPW][NPER];
@@ -459,10 +646,10 @@ __global__ __launch_bounds__(1024) void k_select(SelectArgs a) {
       wave_max_f32_n<IL>(m);
 #pragma unroll
       for (int jj = 0; jj < IL; ++jj) {
-        int win = -1;
+        int win = 0;
 #pragma unroll
         for (int i = NPER - 1; i >= 0; --i) {
-          const unsigned long long b = __ballot(vals[jj][i] == m[jj]);
+          const unsigned long long b = __ballot(vals[jj][i] == m[jj] && lane + kWave * i < E);
           if (b) win = kWave * i + __builtin_ctzll(b);
         }
         // win is wave-uniform: remove it from its owner lane
@@ -509,12 +696,6 @@ __global__ __launch_bounds__(1024) void k_select(SelectArgs a) {
   }
   __syncthreads();
 
-  const bool single = gridDim.x == 1;
-  if (single) {
-    for (int e = tid; e < E; e += blockDim.x) psm.cnt[e] = __popcll(bits[e]);
-    __syncthreads();
-    build_plan(psm, T, E, a.tile_rows, a.has_shared, a.counts, a.expert_off, a.plan, a.tiles);
-  }
   for (int q = tid; q < kSelBlock * K; q += blockDim.x) {
     const int tl = q / K, k = q % K;
     const int t = t0 + tl;
@@ -524,25 +705,14 @@ __global__ __launch_bounds__(1024) void k_select(SelectArgs a) {
       const int e = s_idx[tl * 32 + k];
       rk = __popcll(bits[e] & ((1ull << tl) - 1ull));
     }
-    if (single) {
-      int pos = -1;
-      if (rk >= 0) {
-        pos = psm.off[s_idx[tl * 32 + k]] + rk;
-        a.perm_token[pos] = t;
-      }
-      a.slot_pos[size_t(t) * K + k] = pos;
-    } else {
-      a.rank[size_t(t) * K + k] = rk;
-    }
+    a.rank[size_t(t) * K + k] = rk;
   }
-  if (!single)
-    for (int e = tid; e < E; e += blockDim.x)
-      a.block_counts[size_t(blk) * E + e] = __popcll(bits[e]);
+  for (int e = tid; e < E; e += blockDim.x)
+    a.block_counts[size_t(blk) * E + e] = __popcll(bits[e]);
 }
 
 hipError_t launch_select(const beam_moe_layer& L, int32_t T, int tile_rows, const Ptrs& p,
                          hipStream_t s) {
-  const int nblk = (T + kSelBlock - 1) / kSelBlock;
   SelectArgs a;
   a.part = p.logits;
   a.KS = router_ksplit(L, T);
@@ -556,6 +726,7 @@ hipError_t launch_select(const beam_moe_layer& L, int32_t T, int tile_rows, cons
   a.mask = p.mask;
   a.rank = p.rank;
   a.block_counts = p.block_counts;
+  a.arrive = p.arrive;
   a.tile_rows = tile_rows;
   a.has_shared = L.n_shared > 0 ? 1 : 0;
   a.counts = p.counts;
@@ -564,8 +735,20 @@ hipError_t launch_select(const beam_moe_layer& L, int32_t T, int tile_rows, cons
   a.tiles = p.tiles;
   a.perm_token = p.perm_token;
   a.slot_pos = p.slot_pos;
+  if (select_builds_plan(L, T)) {
+    constexpr int nt = kPlanThreads;
+    const dim3 g{unsigned((T + nt / kWave - 1) / (nt / kWave)), 1, 1}, b{unsigned(nt), 1, 1};
+    prof_before("select_topk_mask_plan", s);
+    if (L.E <= 64) hipLaunchKernelGGL((k_select_plan<1, nt>), g, b, 0, s, a);
+    else if (L.E <= 128) hipLaunchKernelGGL((k_select_plan<2, nt>), g, b, 0, s, a);
+    else if (L.E <= 256) hipLaunchKernelGGL((k_select_plan<4, nt>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((k_select_plan<16, nt>), g, b, 0, s, a);
+    prof_after(s);
+    return hipGetLastError();
+  }
+  const int nblk = (T + kSelBlock - 1) / kSelBlock;
   const dim3 g{unsigned(nblk), 1, 1}, b{1024, 1, 1};
-  prof_before(nblk == 1 ? "select_topk_mask_plan" : "select_topk_mask", s);
+  prof_before("select_topk_mask", s);
   if (L.E <= 64) hipLaunchKernelGGL(k_select<1>, g, b, 0, s, a);
   else if (L.E <= 128) hipLaunchKernelGGL(k_select<2>, g, b, 0, s, a);
   else if (L.E <= 256) hipLaunchKernelGGL(k_select<4>, g, b, 0, s, a);
@@ -573,8 +756,6 @@ hipError_t launch_select(const beam_moe_layer& L, int32_t T, int tile_rows, cons
   prof_after(s);
   return hipGetLastError();
 }
-
-bool select_builds_plan(int32_t T) { return T <= kSelBlock; }
 
 // ---------------------------------------------------------------------------
 // Scan (one workgroup, multi-block batches): per-expert totals and per-block
@@ -605,7 +786,7 @@ __global__ __launch_bounds__(1024) void k_scan(int T, int E, int nblk, int tile_
     psm.cnt[e] = run;
   }
   __syncthreads();
-  build_plan(psm, T, E, tile_rows, has_shared, counts, expert_off, plan, tiles);
+  build_plan<1024>(psm, T, E, tile_rows, has_shared, counts, expert_off, plan, tiles);
 }
 
 hipError_t launch_scan(const beam_moe_layer& L, int32_t T, int tile_rows, const Ptrs& p,

@@ -84,9 +84,11 @@ def test_golden_examples(fname, dtype):
         assert np.all(y[2] == 0.0)
 
 
-@pytest.mark.parametrize("T", [1, 37, 100, 129])
+@pytest.mark.parametrize("T", [1, 37, 100, 129, 512, 513])
 def test_ragged_batches(T):
-    """Batch sizes that are not multiples of the 16/64-token blocks."""
+    """Batch sizes that are not multiples of the 16/64-token blocks; 512 is the
+    largest batch whose plan is built by the selection kernel itself, 513 the
+    smallest that takes the scan and scatter kernels."""
     layer = small_layer("ragged", D=192, E=24, K=5, I=128, S=1, I_s=64, keep=0.45, router_bias=True)
     x = small_x(layer, T, "ragged")
     note(f"[ragged] T={T}")
