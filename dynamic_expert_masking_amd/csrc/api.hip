@@ -49,7 +49,7 @@ WsLayout workspace_layout(const beam_moe_layer& L, int32_t T) {
   w.block_counts = take(nblk * L.E * 4);
   w.expert_off = take(size_t(L.E + 1) * 4);
   w.tiles = take(size_t(w.max_tiles) * sizeof(Tile));
-  w.perm_token = take(TK * 4);
+  w.perm_token = take((TK + 64) * 4);   // + 64: whole 16-row groups are read
   w.slot_pos = take(TK * 4);
   w.h = take(TK * L.I * elt);
   w.h_shared = take(size_t(T) * IS * elt);

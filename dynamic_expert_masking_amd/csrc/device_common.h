@@ -9,6 +9,17 @@ typedef uint16_t u16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// Load through the constant address space, for data that nothing writes
+// while the kernel runs (e.g. the routing plan, written by an earlier
+// kernel).  A wave-uniform address then becomes a scalar load, which is
+// counted apart from the vector loads in flight, so waiting for it does not
+// drain them.
+template <class T>
+__device__ __forceinline__ T ld_const(const T* p) {
+  return *reinterpret_cast<const __attribute__((address_space(4))) T*>(reinterpret_cast<uintptr_t>(p));
+}
 
 constexpr int kWave = 64;
 

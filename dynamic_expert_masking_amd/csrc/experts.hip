@@ -54,6 +54,17 @@ __device__ __forceinline__ void shared_item(long w2, int nts, int nbs, int& t, i
   nb = int(g) * kX + q % r;
 }
 
+// Tile record via scalar loads (see ld_const).
+__device__ __forceinline__ Tile ld_tile(const Tile* p) {
+  const i32x4 v = ld_const(reinterpret_cast<const i32x4*>(p));
+  Tile t;
+  t.expert = v[0];
+  t.row0 = v[1];
+  t.rows = v[2];
+  t.pad = v[3];
+  return t;
+}
+
 // Decodes work item w into (tile index, n-block, shared?): routed items
 // tile-major, then the shared items.
 __device__ __forceinline__ bool work_item(long w, int ntr, int nts, int nbr, int nbs, int& ti,
@@ -122,7 +133,7 @@ struct GateUpStream {
     int ti, nb;
     bool shared;
     work_item(item, ntr, nts, nbr, nbs, ti, nb, shared);
-    const Tile tl = a->tiles[ti];
+    const Tile tl = ld_tile(a->tiles + ti);
     const u16* wg = shared ? (const u16*)a->sg : (const u16*)a->wg + size_t(tl.expert) * a->I * a->D;
     const u16* wu = shared ? (const u16*)a->su : (const u16*)a->wu + size_t(tl.expert) * a->I * a->D;
 #pragma unroll
@@ -134,8 +145,19 @@ struct GateUpStream {
 #pragma unroll
     for (int b = 0; b < MT; ++b) {
       const int r = 16 * b + (lane & 15);
-      int t = 0;   // absent rows read token 0
-      if (r < tl.rows) t = shared ? tl.row0 + r : a->perm_token[tl.row0 + r];
+      int t = tl.row0 + r;
+      if (!shared) {
+        // the 16 rows' tokens by scalar loads, each lane picking its own (the
+        // perm_token region is padded so that reading 16 past a tile's start
+        // stays inside it)
+        const int32_t* pt = a->perm_token + tl.row0 + 16 * b;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int32_t v = ld_const(pt + j);
+          t = (lane & 15) == j ? v : t;
+        }
+      }
+      if (r >= tl.rows) t = 0;   // absent rows read token 0
       it.x[b] = (const u16*)a->x + size_t(t) * a->D;
     }
   }
@@ -143,7 +165,7 @@ struct GateUpStream {
     int ti, nb;
     bool shared;
     work_item(item, ntr, nts, nbr, nbs, ti, nb, shared);
-    const Tile tl = a->tiles[ti];
+    const Tile tl = ld_tile(a->tiles + ti);
     const int Iv = shared ? a->S * a->Is : a->I;
     u16* hb = shared ? (u16*)a->h_sh : (u16*)a->h;
 #pragma unroll
@@ -172,8 +194,8 @@ __global__ __launch_bounds__(kStreamWaves * 64) void k_gate_up_stream(ExpertArgs
   __shared__ __align__(16) unsigned char lds[StreamLds<NMAT, MT, U, KSPLIT>::kBytes];
   GateUpStream<MT, NB> pb;
   pb.a = &a;
-  pb.ntr = a.plan->n_tiles_routed;
-  pb.nts = a.plan->n_tiles_shared;
+  pb.ntr = ld_const(&a.plan->n_tiles_routed);
+  pb.nts = ld_const(&a.plan->n_tiles_shared);
   pb.nbr = a.I / (16 * NB);
   pb.nbs = a.S > 0 ? (a.S * a.Is) / (16 * NB) : 1;
   pb.total = long(pb.ntr) * pb.nbr + long(pb.nts) * pb.nbs;
@@ -204,7 +226,7 @@ struct DownStream {
     int ti, nb;
     down_item(item, ntr, nts, nb_all, ti, nb);
     const bool shared = ti >= ntr;
-    const Tile tl = a->tiles[ti];
+    const Tile tl = ld_tile(a->tiles + ti);
     const int d0 = nb * 16 * NB;
     const u16* w0;
     if (shared) {
@@ -237,7 +259,7 @@ struct DownStream {
     int ti, nb;
     down_item(item, ntr, nts, nb_all, ti, nb);
     const bool shared = ti >= ntr;
-    const Tile tl = a->tiles[ti];
+    const Tile tl = ld_tile(a->tiles + ti);
     float* ob = shared ? a->o_sh : a->o;
 #pragma unroll
     for (int b = 0; b < MT; ++b) {
@@ -259,8 +281,8 @@ __global__ __launch_bounds__(kStreamWaves * 64) void k_down_stream(ExpertArgs a)
   __shared__ __align__(16) unsigned char lds[StreamLds<NB, MT, U, KSPLIT>::kBytes];
   DownStream<MT, NB> pb;
   pb.a = &a;
-  pb.ntr = a.plan->n_tiles_routed;
-  pb.nts = a.plan->n_tiles_shared;
+  pb.ntr = ld_const(&a.plan->n_tiles_routed);
+  pb.nts = ld_const(&a.plan->n_tiles_shared);
   pb.nb_all = a.D / (16 * NB);
   pb.total = long(pb.ntr + pb.nts) * pb.nb_all;
   stream_run<NB, MT, U, KSPLIT>(pb, lds);

@@ -136,7 +136,9 @@ template <int NMAT, int MT, int U, int KSPLIT, class P>
 __device__ __forceinline__ void stream_run(P& prob, unsigned char* lds_all) {
   using Lds = StreamLds<NMAT, MT, U, KSPLIT>;
   constexpr int GROUPS = kStreamWaves / KSPLIT;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  // wave-uniform, and known to be so: item decoding then stays scalar
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int group = wave / KSPLIT, kw = wave % KSPLIT;
   u16* lds = reinterpret_cast<u16*>(lds_all + wave * Lds::kWaveBytes);
   auto red = [&](int w) { return reinterpret_cast<f32x4*>(lds_all + w * Lds::kWaveBytes); };
