@@ -307,8 +307,8 @@ struct GateUpTiledProv {
   }
   __device__ const u16* xbase(int) const { return xb; }
   __device__ uint32_t xoff(int r) const {
-    int t = 0;
-    if (r < rows) t = perm ? perm[row0 + r] : row0 + r;
+    const int rr = r < rows ? r : 0;   // absent rows read the tile's first token
+    const int t = perm ? perm[row0 + rr] : row0 + rr;
     return uint32_t(long(t) * D);
   }
 };
