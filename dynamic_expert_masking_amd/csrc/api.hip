@@ -124,6 +124,7 @@ static int check_layer(const beam_moe_layer* L) {
   if (L->D <= 0 || L->E <= 0 || L->K <= 0 || L->I <= 0 || L->n_shared < 0)
     return BEAM_ERR_INVALID_ARG;
   if (L->K > L->E) return BEAM_ERR_INVALID_ARG;
+  if (L->gating & ~(BEAM_GATE_SOFTMAX_ALL | BEAM_GATE_RENORM)) return BEAM_ERR_INVALID_ARG;
   if (L->n_shared > 0 && L->I_shared <= 0) return BEAM_ERR_INVALID_ARG;
   const void* req[] = {L->w_router, L->w_mask, L->w_gate, L->w_up, L->w_down};
   for (const void* p : req)

@@ -369,6 +369,7 @@ struct SelectArgs {
   const float* br;
   const float* bm;
   int T, E, K;
+  int gating;   // beam_gate_flag bits
   int32_t* idx;
   float* gates;
   uint32_t* mask;
@@ -384,6 +385,33 @@ struct SelectArgs {
   int32_t* perm_token;
   int32_t* slot_pos;
 };
+
+// Gates of one token from its K selected logits: lane k < K holds slot k's
+// logit r_k and its mask bit; r_0 (the largest) sits in lane 0.  Without
+// options, g = softmax over the K logits; BEAM_GATE_SOFTMAX_ALL divides by the
+// sum over all E experts instead (lane l's NPER logits in r_all, -inf for
+// absent experts); BEAM_GATE_RENORM renormalises g * m over the kept slots.
+template <int NPER>
+__device__ __forceinline__ float token_gate(int gating, bool slot, bool keep, float r_k,
+                                            const float (&r_all)[NPER]) {
+  const float r_0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r_k), 0));
+  const float ex = slot ? expf(r_k - r_0) : 0.f;
+  float den;
+  if (gating & BEAM_GATE_SOFTMAX_ALL) {
+    float part = 0.f;
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) part += expf(r_all[i] - r_0);   // exp(-inf) = 0
+    den = wave_sum_f32(part);
+  } else {
+    den = wave_sum_f32(ex);
+  }
+  float gh = keep ? ex / den : 0.f;
+  if (gating & BEAM_GATE_RENORM) {
+    const float s = wave_sum_f32(gh);
+    gh = s > 0.f ? gh / s : 0.f;
+  }
+  return gh;
+}
 
 // Token t's selection by one wave.  Expert e's logits are held by lane
 // e % 64 in register e / 64; the KS partial sums are added in ks order, then
@@ -421,6 +449,9 @@ __device__ __forceinline__ void select_token(const SelectArgs& a, int t, int lan
     vals[i] = e < E ? r + 0.0f : -__builtin_inff();   // + 0: -0 and +0 compare alike
     zv[i] = z;
   }
+  float r_all[NPER];
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) r_all[i] = vals[i];
   int my_e = 0;
   float my_r = 0.f;
   for (int k = 0; k < K; ++k) {
@@ -451,14 +482,12 @@ __device__ __forceinline__ void select_token(const SelectArgs& a, int t, int lan
     const float c = __shfl(zv[i], e_k & 63, kWave);
     if (i == (e_k >> 6)) z_k = c;
   }
-  const float r_0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r_k), 0));
-  const float ex = slot ? expf(r_k - r_0) : 0.f;
-  const float sum = wave_sum_f32(ex);
   const bool keep = slot && z_k >= 0.f;
   const unsigned long long bal = __ballot(keep);
+  const float gh = token_gate<NPER>(a.gating, slot, keep, r_k, r_all);
   if (slot) {
     a.idx[size_t(t) * K + lane] = e_k;
-    a.gates[size_t(t) * K + lane] = keep ? ex / sum : 0.f;
+    a.gates[size_t(t) * K + lane] = gh;
   }
   if (lane == 0) a.mask[t] = uint32_t(bal);
 }
@@ -677,14 +706,16 @@ __global__ __launch_bounds__(1024) void k_select(SelectArgs a) {
         const float c = __shfl(zv[j0 + jj][i], e_k & 63, kWave);
         if (i == (e_k >> 6)) z_k = c;
       }
-      const float r_0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r_k), 0));
-      const float ex = slot ? expf(r_k - r_0) : 0.f;
-      const float sum = wave_sum_f32(ex);
       const bool keep = slot && z_k >= 0.f;
       const unsigned long long bal = __ballot(keep);
+      float r_all[NPER];
+#pragma unroll
+      for (int i = 0; i < NPER; ++i)
+        r_all[i] = (lane + kWave * i < E) ? rv[j0 + jj][i] : -__builtin_inff();
+      const float gh = token_gate<NPER>(a.gating, slot, keep, r_k, r_all);
       if (slot) {
         a.idx[size_t(t) * K + lane] = e_k;
-        a.gates[size_t(t) * K + lane] = keep ? ex / sum : 0.f;
+        a.gates[size_t(t) * K + lane] = gh;
         s_idx[tl * 32 + lane] = e_k;
       }
       if (lane == 0) {
@@ -721,6 +752,7 @@ hipError_t launch_select(const beam_moe_layer& L, int32_t T, int tile_rows, cons
   a.T = T;
   a.E = L.E;
   a.K = L.K;
+  a.gating = L.gating;
   a.idx = p.idx;
   a.gates = p.gates;
   a.mask = p.mask;

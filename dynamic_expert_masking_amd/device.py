@@ -56,7 +56,8 @@ class DeviceLayer:
         return make_layer(c.D, c.E, c.K, c.I, self.dtype_code, t["w_router"], t["w_mask"],
                           t["w_gate"], t["w_up"], t["w_down"], b_router=t["b_router"],
                           b_mask=t["b_mask"], n_shared=c.S, I_shared=c.I_s if c.S else 0,
-                          ws_gate=t["ws_gate"], ws_up=t["ws_up"], ws_down=t["ws_down"])
+                          ws_gate=t["ws_gate"], ws_up=t["ws_up"], ws_down=t["ws_down"],
+                          gating=getattr(c, "gating", 0))
 
     def replicas(self, n: int):
         """n extra copies of the expert weights at distinct addresses (same

@@ -51,6 +51,17 @@ typedef enum {
 
 typedef enum { BEAM_F32 = 0, BEAM_BF16 = 1 } beam_dtype;
 
+/* Gate options (beam_moe_layer.gating, bits; 0 = the method as described
+ * above).  The ai-feeds.com summary's section on the input and overall flow
+ * applies the mask to the router's expert scores without fixing where the
+ * softmax sits, so two common forms are offered besides Steps 1 and 4:
+ *   BEAM_GATE_SOFTMAX_ALL  g_k = softmax over all E router logits, read at
+ *                          the top-K experts (no renormalisation over K).
+ *   BEAM_GATE_RENORM       after masking, g_hat_k = g_k m_k / sum_j g_j m_j
+ *                          (0 for every slot when no slot survives).
+ * The top-K set, its order and the mask bits do not depend on these bits. */
+typedef enum { BEAM_GATE_SOFTMAX_ALL = 1, BEAM_GATE_RENORM = 2 } beam_gate_flag;
+
 /* Layer description.  Shapes: D hidden, E routed experts, K top-K, I routed
  * expert intermediate size, n_shared shared experts of intermediate size
  * I_shared.  Supported: 1 <= K <= min(E, 32), E <= 1024, D, I and I_shared
@@ -68,6 +79,8 @@ typedef struct {
   const void *ws_gate;         /* [n_shared][I_shared][D], NULL if n_shared=0 */
   const void *ws_up;           /* [n_shared][I_shared][D]                     */
   const void *ws_down;         /* [n_shared][D][I_shared]                     */
+  int32_t gating;              /* beam_gate_flag bits; unknown bits are
+                                  BEAM_ERR_INVALID_ARG                        */
 } beam_moe_layer;
 
 /* Routing results (device pointers, caller-owned). */

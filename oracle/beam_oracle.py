@@ -33,6 +33,12 @@ design notes of the repository):
   * Top-K order: descending logit, equal logits ordered by lower expert index.
   * Experts are SwiGLU FFNs: E(x) = Wd (silu(Wg x) * (Wu x)), silu(a) = a/(1+e^-a).
   * Shared experts are always on, with gate 1, and are added to y.
+  * Gate options (off by default; not part of the method as the pages
+    describe it): [P1]'s section on the input and overall flow applies the
+    mask to the router's scores without fixing where the softmax sits, so
+    select_experts also offers g = softmax over all E logits read at the
+    top-K experts (gating bit 1), and renormalising g_hat over the kept
+    slots after masking (gating bit 2; all zero when no slot is kept).
   * Router and mask decisions (which experts, which bits) are taken on
     float32 logits, the precision the GPU kernels decide in: the logits are
     computed in float64 and rounded once to float32.  Everything else is
@@ -51,6 +57,7 @@ import numpy as np
 
 __all__ = [
     "widen", "router_logits", "select_experts", "Routing", "route", "silu",
+    "GATE_SOFTMAX_ALL", "GATE_RENORM",
     "expert_ffn", "forward", "expert_counts", "layer_stats",
 ]
 
@@ -90,18 +97,25 @@ def router_logits(layer, x: np.ndarray):
 @dataclass
 class Routing:
     idx: np.ndarray        # [T][K] int32, top-K experts by descending logit
-    g: np.ndarray          # [T][K] float64, softmax over the K kept logits
+    g: np.ndarray          # [T][K] float64, softmax over the K kept logits (over all E with GATE_SOFTMAX_ALL)
     keep: np.ndarray       # [T][K] bool, binary mask m on the top-K candidates
     ghat: np.ndarray       # [T][K] float64, g * m
     mask_bits: np.ndarray  # [T] uint32, bit k = keep[t][k]
 
 
-def select_experts(r: np.ndarray, z: np.ndarray, K: int) -> Routing:
+GATE_SOFTMAX_ALL = 1
+GATE_RENORM = 2
+
+
+def select_experts(r: np.ndarray, z: np.ndarray, K: int, gating: int = 0) -> Routing:
     """Top-K, softmax, binary mask and masked gates for each token.
 
     [P3] Step 1: keep the K largest router logits and apply a softmax to them
     (g).  Step 2/3: m_i = 1 when sigmoid(z_i) >= 0.5, for i in the top-K set.
     Step 4: g_hat = g * m.  Decisions are taken on float32-rounded logits.
+    Gate options (see the module notes): GATE_SOFTMAX_ALL takes g from a
+    softmax over all E logits; GATE_RENORM divides g_hat by its sum over the
+    token's slots when that sum is positive.
     """
     r32 = np.asarray(r, dtype=np.float64).astype(np.float32)
     z32 = np.asarray(z, dtype=np.float64).astype(np.float32)
@@ -116,11 +130,19 @@ def select_experts(r: np.ndarray, z: np.ndarray, K: int) -> Routing:
         # so the lower expert index comes first.
         order = np.argsort(-r32[t], kind="stable")[:K]
         idx[t] = order
-        v = r32[t, order].astype(np.float64)
-        w = np.exp(v - v.max())
-        g[t] = w / w.sum()
+        if gating & GATE_SOFTMAX_ALL:
+            v = r32[t].astype(np.float64)
+            w = np.exp(v - v.max())
+            g[t] = w[order] / w.sum()
+        else:
+            v = r32[t, order].astype(np.float64)
+            w = np.exp(v - v.max())
+            g[t] = w / w.sum()
         keep[t] = z32[t, order] >= np.float32(0.0)
     ghat = np.where(keep, g, 0.0)
+    if gating & GATE_RENORM:
+        s = ghat.sum(axis=1, keepdims=True)
+        ghat = np.where(s > 0.0, ghat / np.where(s > 0.0, s, 1.0), 0.0)
     weights = (np.uint64(1) << np.arange(K, dtype=np.uint64))
     mask_bits = (keep.astype(np.uint64) * weights).sum(axis=1).astype(np.uint32)
     return Routing(idx, g, keep, ghat, mask_bits)
@@ -129,7 +151,7 @@ def select_experts(r: np.ndarray, z: np.ndarray, K: int) -> Routing:
 def route(layer, x: np.ndarray) -> Routing:
     """[P3] Steps 1-3 (and the gate product of Step 4) for every token of x."""
     r, z = router_logits(layer, x)
-    return select_experts(r, z, layer.cfg.K)
+    return select_experts(r, z, layer.cfg.K, getattr(layer.cfg, "gating", 0))
 
 
 def silu(a: np.ndarray) -> np.ndarray:

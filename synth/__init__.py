@@ -50,6 +50,7 @@ class LayerConfig:
     tokens: Tuple[int, ...]   # batch sizes this workload is run at
     keep: float         # expected keep probability of a top-K candidate
     router_bias: bool   # per-expert router bias ~ N(0, 1)
+    gating: int = 0     # gate option bits: 1 softmax over all E, 2 renormalise after masking
 
     @property
     def avg_k_target(self) -> float:

@@ -15,7 +15,10 @@ import numpy as np
 import torch
 import torch.nn.functional as F
 
-from common import (eval_closed_form, layer_from_json, small_config, with_mask)
+import json
+import os
+
+from common import (GOLDEN, eval_closed_form, layer_from_json, small_config, with_mask)
 import synth
 
 
@@ -45,17 +48,32 @@ def torch_logits(layer, x):
 
 
 def torch_dense_gates(layer, x, use_mask=True):
-    """G[t][e]: masked top-K softmax gate of expert e for token t (0 elsewhere)."""
+    """G[t][e]: masked top-K softmax gate of expert e for token t (0 elsewhere).
+    Gate options of layer.cfg.gating: bit 1 takes the softmax over all E and
+    reads it at the top-K experts; bit 2 renormalises the masked gates."""
     r, z = torch_logits(layer, x)
     K = layer.cfg.K
+    gating = getattr(layer.cfg, "gating", 0)
     vals, idx = torch.topk(r, K, dim=1)
-    g = torch.softmax(vals, dim=1)
+    if gating & 1:
+        g = torch.gather(torch.softmax(r, dim=1), 1, idx)
+    else:
+        g = torch.softmax(vals, dim=1)
     if use_mask:
         m = (torch.sigmoid(torch.gather(z, 1, idx)) >= 0.5).to(torch.float64)
         g = g * m
+    if gating & 2:
+        s = g.sum(dim=1, keepdim=True)
+        g = torch.where(s > 0, g / torch.where(s > 0, s, torch.ones_like(s)), torch.zeros_like(g))
     G = torch.zeros_like(r)
     G.scatter_(1, idx, g)
     return G, idx
+
+
+def with_gating(layer, gating):
+    """The same layer with other gate options."""
+    from dataclasses import replace
+    return replace(layer, cfg=replace(layer.cfg, gating=gating))
 
 
 def torch_expert(layer, e, X, shared=False):
@@ -134,6 +152,56 @@ def pin_golden_shared(O):
     assert np.array_equal(O.expert_counts(rt, layer.cfg.E), np.array(ex["counts"]))
     yy = np.vectorize(eval_closed_form)(np.array(ex["y"], dtype=object)).astype(float)
     assert np.allclose(y, yy, rtol=0, atol=1e-6), (y, yy)
+
+
+def pin_golden_gating(O):
+    """Hand-derived worked example of the gate options (softmax over all E;
+    renormalised masked gates; both), on the routed example's inputs."""
+    j, layer0, x = layer_from_json("worked_example_routed.json")
+    with open(os.path.join(GOLDEN, "worked_example_gating.json")) as f:
+        jg = json.load(f)
+    ev = lambda a: np.vectorize(eval_closed_form)(np.array(a, dtype=object)).astype(float)  # noqa: E731
+    for flags, ex in jg["expect"].items():
+        layer = with_gating(layer0, int(flags))
+        rt, y = O.forward(layer, x)
+        assert np.array_equal(rt.idx, np.array(j["expect"]["idx"])), (flags, rt.idx)
+        assert np.array_equal(rt.mask_bits, np.array(j["expect"]["mask_bits"], np.uint32))
+        assert np.allclose(rt.g, ev(ex["g"]), rtol=0, atol=1e-7), (flags, rt.g)
+        assert np.allclose(rt.ghat, ev(ex["ghat"]), rtol=0, atol=1e-7), (flags, rt.ghat)
+        assert np.allclose(y, ev(ex["y"]), rtol=0, atol=1e-6), (flags, y)
+        assert np.all(y[2] == 0.0)
+
+
+def pin_gate_options_vs_torch(O):
+    """Gate options against torch (softmax over all E gathered at torch.topk;
+    renormalisation of the masked gates), gates and the dense brute-force y."""
+    base = small_layer("gating", D=64, E=9, K=4, I=24, S=1, I_s=16, keep=0.45, router_bias=True)
+    x = small_x(base, 12, "gating")
+    for flags in (1, 2, 3):
+        layer = with_gating(base, flags)
+        G, idx = torch_dense_gates(layer, x)
+        rt = O.route(layer, x)
+        assert np.array_equal(rt.idx, idx.numpy())
+        assert _rel(rt.ghat, torch.gather(G, 1, idx).numpy()) < 1e-12, flags
+        _, y = O.forward(layer, x)
+        assert _rel(y, torch_dense_forward(layer, x)) < 1e-9, flags
+        if flags & 2:
+            s = rt.ghat.sum(axis=1)
+            kept = rt.keep.any(axis=1)
+            assert np.allclose(s[kept], 1.0, atol=1e-12) and np.all(s[~kept] == 0.0)
+
+
+def pin_gate_options_identity(O):
+    """With every candidate kept (Wm = 0), softmax over all E read at the top K
+    and then renormalised over the K equals the softmax over the K logits."""
+    base = with_mask(small_layer("gate_id", D=48, E=7, K=3, I=16), True, 0.0)
+    x = small_x(base, 10, "gate_id")
+    rt0, y0 = O.forward(base, x)
+    rt3, y3 = O.forward(with_gating(base, 3), x)
+    assert np.array_equal(rt0.idx, rt3.idx)
+    assert _rel(rt3.ghat, rt0.ghat) < 1e-12 and _rel(y3, y0) < 1e-12
+    rt1 = O.route(with_gating(base, 1), x)
+    assert np.all(rt1.g.sum(axis=1) < 1.0)   # K < E: part of the mass is outside the top K
 
 
 def pin_zero_mask_router_is_topk(O):
@@ -322,7 +390,8 @@ def pin_stats_formulas(O):
 
 
 ALL_PINS = [
-    pin_golden_routed, pin_golden_shared, pin_zero_mask_router_is_topk, pin_dense_bruteforce,
+    pin_golden_routed, pin_golden_shared, pin_golden_gating, pin_gate_options_vs_torch,
+    pin_gate_options_identity, pin_zero_mask_router_is_topk, pin_dense_bruteforce,
     pin_avgk_popcount, pin_mask_bias_extremes, pin_k1, pin_k_equals_e, pin_gate_properties,
     pin_threshold_is_sigmoid_half, pin_batch_invariance, pin_expert_permutation,
     pin_silu_closed_forms, pin_widen_bf16, pin_stats_formulas,

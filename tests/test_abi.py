@@ -58,6 +58,8 @@ def test_workspace_size_monotone_and_invalid():
     sizes = [dm.beam_moe_workspace_size(L, T) for T in (0, 1, 64, 65, 4096)]
     assert all(a <= b for a, b in zip(sizes, sizes[1:])) and sizes[-1] > sizes[1] > 0
     assert dm.beam_moe_workspace_size(fake_layer(K=9), 16) == 0          # K > E
+    assert dm.beam_moe_workspace_size(fake_layer(gating=4), 16) == 0     # unknown gate bit
+    assert dm.beam_moe_workspace_size(fake_layer(gating=dm.GATE_SOFTMAX_ALL | dm.GATE_RENORM), 16) > 0
     assert dm.beam_moe_workspace_size(fake_layer(D=100), 16) == 0        # D % 64
     assert dm.beam_moe_workspace_size(L, -1) == 0
 

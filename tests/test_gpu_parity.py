@@ -150,6 +150,38 @@ def test_k_extremes(E, K):
     check_output(y, y_ref, "bf16")
 
 
+@pytest.mark.parametrize("flags", [1, 2, 3])
+@pytest.mark.parametrize("T", [37, 600])
+def test_gate_options(flags, T):
+    """Gate options (softmax over all E; renormalised masked gates), in the
+    one-launch selection (37 tokens) and the multi-block one (600)."""
+    from oracle_pins import with_gating
+    base = small_layer("gates", D=128, E=40, K=6, I=64, S=1, I_s=64, keep=0.4, router_bias=True)
+    layer = with_gating(base, flags)
+    x = small_x(base, T, "gates")
+    note(f"[gate options] flags={flags} T={T}")
+    y, rt, _ = run_forward(device_layer(layer), x)
+    rt_ref, y_ref = oracle.forward(layer, x)
+    check_routing(rt, rt_ref, layer.cfg.E)
+    check_output(y, y_ref, "bf16")
+
+
+def test_gate_options_on_workload():
+    """Both gate options on the DeepSeek-V2-Lite-shaped decode layer, T=64."""
+    from oracle_pins import with_gating
+    name, T = "dsv2lite_decode", 64
+    cfg = synth.CONFIGS[name]
+    layer = with_gating(cached_layer(name), 3)
+    x = inputs(cfg, T, layer)
+    note("[gate options] dsv2lite_decode T=64 flags=3")
+    y, rt, _ = run_forward(device_layer(layer, key=name + ":gating3"), x)
+    rt_ref = oracle.route(layer, x)
+    check_routing(rt, rt_ref, cfg.E)
+    toks = sample_tokens(T)
+    _, y_ref = oracle.forward(layer, x, tokens=toks)
+    check_output(y[toks], y_ref, cfg.dtype)
+
+
 def test_route_entry_matches_forward():
     name, T = "finegrained", 512
     cfg = synth.CONFIGS[name]

@@ -36,8 +36,14 @@ MUTANTS = {
     "renormalise": ("ghat = np.where(keep, g, 0.0)",
                     "ghat = np.where(keep, g, 0.0); ghat = ghat / np.maximum(ghat.sum(1, keepdims=True), 1e-300)"),
     # softmax over all experts, then top-K
-    "softmax_all_E": ("w = np.exp(v - v.max())\n        g[t] = w / w.sum()",
-                      "w = np.exp(v - r32[t].max())\n        g[t] = w / np.exp(r32[t].astype(np.float64) - r32[t].max()).sum()"),
+    "softmax_all_E": ("v = r32[t, order].astype(np.float64)\n            w = np.exp(v - v.max())\n            g[t] = w / w.sum()",
+                      "v = r32[t, order].astype(np.float64)\n            w = np.exp(v - r32[t].max())\n            g[t] = w / np.exp(r32[t].astype(np.float64) - r32[t].max()).sum()"),
+    # gate option 1 taken over the top-K logits only
+    "softmax_all_ignored": ("g[t] = w[order] / w.sum()", "g[t] = w[order] / w[order].sum()"),
+    # gate option 2 ignored
+    "renorm_ignored": ("if gating & GATE_RENORM:", "if False:"),
+    # gate option 2 normalising by the unmasked gates
+    "renorm_unmasked_sum": ("s = ghat.sum(axis=1, keepdims=True)", "s = g.sum(axis=1, keepdims=True)"),
     # strict threshold
     "strict_threshold": ("keep[t] = z32[t, order] >= np.float32(0.0)", "keep[t] = z32[t, order] > np.float32(0.0)"),
     # mask read by slot instead of by expert
