@@ -39,7 +39,6 @@ WsLayout workspace_layout(const beam_moe_layer& L, int32_t T) {
     return o;
   };
   w.plan = take(sizeof(Plan));
-  w.arrive = take(sizeof(uint32_t));
   w.logits = take(size_t(router_ksplit(L, T)) * T * 2 * L.E * 4);
   w.idx = take(TK * 4);
   w.gates = take(TK * 4);
@@ -170,7 +169,6 @@ static int check_route_out(const beam_route_out* out) {
 static Ptrs carve(const WsLayout& w, void* ws, const beam_route_out* out) {
   char* b = static_cast<char*>(ws);
   Ptrs p;
-  p.arrive = reinterpret_cast<uint32_t*>(b + w.arrive);
   p.logits = reinterpret_cast<float*>(b + w.logits);
   p.idx = out ? out->topk_idx : reinterpret_cast<int32_t*>(b + w.idx);
   p.gates = out ? out->gates : reinterpret_cast<float*>(b + w.gates);

@@ -35,7 +35,7 @@ struct Tile {
 };
 
 struct WsLayout {
-  size_t plan, arrive, logits, idx, gates, mask, counts, rank, block_counts, expert_off, tiles, perm_token,
+  size_t plan, logits, idx, gates, mask, counts, rank, block_counts, expert_off, tiles, perm_token,
       slot_pos, h, h_shared, o, o_shared, total;
   int32_t max_tiles;
 };
@@ -48,7 +48,6 @@ WsLayout workspace_layout(const beam_moe_layer& L, int32_t T);
 
 struct Ptrs {
   // routing
-  uint32_t* arrive;   // arrival counter of the selection kernel (zeroed by the router kernel)
   float* logits;
   int32_t* idx;
   float* gates;
@@ -71,9 +70,9 @@ struct Ptrs {
 // ---- launchers (return hipSuccess or the launch error) ----
 hipError_t launch_router_logits(const beam_moe_layer& L, const void* x, int32_t T, const Ptrs& p,
                                 hipStream_t s);
-// True when the selection kernel also builds the plan and places the pairs
-// (the per-expert token bitmaps of the batch fit in one workgroup's LDS);
-// otherwise the scan and scatter kernels follow it.
+// True when the plan comes from per-expert token bitmaps in one workgroup
+// (they and the batch's selections fit in its LDS); otherwise the scan and
+// scatter kernels follow the selection.
 bool select_builds_plan(const beam_moe_layer& L, int32_t T);
 hipError_t launch_select(const beam_moe_layer& L, int32_t T, int tile_rows, const Ptrs& p,
                          hipStream_t s);

@@ -23,7 +23,6 @@ struct RouterArgs {
   const u16* wr;
   const u16* wm;
   float* part;
-  uint32_t* arrive;   // selection's arrival counter, zeroed here for the next kernel
   int T, D, E, KS;
 };
 
@@ -72,7 +71,6 @@ template <int MT>
 __global__ __launch_bounds__(256) void k_router_skinny(RouterArgs a) {
   __shared__ f32x4 red[4 * MT * kWave];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (blockIdx.x == 0 && threadIdx.x == 0) *a.arrive = 0u;
   const int nrb = (2 * a.E + 15) / 16;
   const int ks = blockIdx.x % a.KS;
   const int rest = blockIdx.x / a.KS;
@@ -123,7 +121,6 @@ __global__ __launch_bounds__(256, 2) void k_router_tiled(RouterArgs a) {
   const long total = long((a.T + kRouterBM - 1) / kRouterBM) * 2 * nrb;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wn = wave & 1, wm = wave >> 1;
-  if (blockIdx.x == 0 && threadIdx.x == 0) *a.arrive = 0u;
   for (XcdRange it = xcd_range(total); it.next < it.end; it.next += it.step) {
     const int rb = int(it.next % (2 * nrb));
     const int t0 = int(it.next / (2 * nrb)) * kRouterBM;
@@ -150,12 +147,10 @@ struct RouterArgsF32 {
   const float* wr;
   const float* wm;
   float* part;
-  uint32_t* arrive;
   int T, D, E;
 };
 
 __global__ __launch_bounds__(256) void k_router_f32(RouterArgsF32 a) {
-  if (blockIdx.x == 0 && threadIdx.x == 0) *a.arrive = 0u;
   const long q = long(blockIdx.x) * blockDim.x + threadIdx.x;
   const int R = 2 * a.E;
   if (q >= long(a.T) * R) return;
@@ -192,7 +187,7 @@ hipError_t launch_router_logits(const beam_moe_layer& L, const void* x, int32_t 
   float* part = p.logits;
   if (L.dtype == BEAM_F32) {
     RouterArgsF32 a{(const float*)x, (const float*)L.w_router, (const float*)L.w_mask, part,
-                    p.arrive, T, L.D, L.E};
+                    T, L.D, L.E};
     const long n = long(T) * 2 * L.E;
     prof_before("router_logits_f32", s);
     hipLaunchKernelGGL(k_router_f32, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, a);
@@ -200,7 +195,7 @@ hipError_t launch_router_logits(const beam_moe_layer& L, const void* x, int32_t 
     return hipGetLastError();
   }
   const int KS = router_ksplit(L, T);
-  RouterArgs a{(const u16*)x, (const u16*)L.w_router, (const u16*)L.w_mask, part, p.arrive, T, L.D, L.E, KS};
+  RouterArgs a{(const u16*)x, (const u16*)L.w_router, (const u16*)L.w_mask, part, T, L.D, L.E, KS};
   if (router_use_skinny(T, L.E)) {
     const int nrb = (2 * L.E + 15) / 16;
     const int mt = router_mt(T, L.E);
@@ -340,23 +335,21 @@ __device__ void build_plan(PlanSmem& sm, int T, int E, int tile_rows, int has_sh
 // the candidates, g_hat = g * m.
 //
 // Two forms.  When the batch's per-expert token bitmaps (E x ceil(T/64)
-// words) fit in LDS, one wave selects each token and the workgroup that
-// finishes last builds the plan and places every pair (k_select_plan).
-// Otherwise one 1024-thread workgroup handles each 64-token block and records
-// block-local ranks and counts, and the scan and scatter kernels follow
-// (k_select).
+// words) and its selections fit in one workgroup's LDS, one wave selects each
+// token (k_select_tokens) and a one-workgroup kernel builds the plan and
+// places every pair (k_plan_bitmap).  Otherwise one 1024-thread workgroup
+// handles each 64-token block and records block-local ranks and counts, and
+// the scan and scatter kernels follow (k_select).
 // ---------------------------------------------------------------------------
 
 constexpr int kSelWaves = 16;
 constexpr int kSelTokPerWave = kSelBlock / kSelWaves;   // 4
-// Limits of the one-launch form: the LDS of the plan-building workgroup, and
-// the batch size beyond which the arrival of many workgroups (each publishing
-// its selections device-wide) costs more than the separate scan and scatter
-// launches (timed on MI355X).
-constexpr int kPlanWords = 4096;   // E * ceil(T / 64) bitmap words
-constexpr int kPlanPairs = 8192;   // T * K selections
-constexpr int kPlanTokens = 512;   // T
-constexpr int kPlanThreads = 256;  // four tokens per workgroup, one wave per SIMD
+// Limits of the bitmap plan (LDS of its one workgroup).
+constexpr int kPlanWords = 4096;    // E * ceil(T / 64) bitmap words
+constexpr int kPlanPairs = 8192;    // T * K selections (above, the block-rank kernels are faster)
+constexpr int kPlanTokens = 4096;   // T
+constexpr int kPlanThreads = 1024;  // plan kernel workgroup
+constexpr int kSelThreads = 256;    // selection: four tokens per workgroup, one wave per SIMD
 
 bool select_builds_plan(const beam_moe_layer& L, int32_t T) {
   return long(L.E) * ((T + kSelBlock - 1) / kSelBlock) <= kPlanWords &&
@@ -375,8 +368,7 @@ struct SelectArgs {
   uint32_t* mask;
   int32_t* rank;
   int32_t* block_counts;
-  // plan (k_select_plan)
-  uint32_t* arrive;
+  // plan
   int tile_rows, has_shared;
   int32_t* counts;
   int32_t* expert_off;
@@ -498,7 +490,6 @@ struct BitmapPlanSmem {
   uint16_t idx[kPlanPairs];              // selections of the batch, [T][K]
   uint32_t mask[kPlanTokens];            // mask bits of the batch
   PlanSmem plan;
-  int32_t last;
 };
 
 // Copies n entries of src (global) into dst (LDS), four independent loads in
@@ -521,28 +512,23 @@ __device__ __forceinline__ void stage_to_lds(D* dst, const S* __restrict__ src, 
   }
 }
 
-// One wave per token, NT / 64 tokens per workgroup; the last workgroup to
-// arrive builds the plan.  Positions: expert-major, tokens ascending within
-// an expert, i.e. off[e] + (kept tokens of e before t).
+// One wave per token, NT / 64 tokens per workgroup.
 template <int NPER, int NT>
-__global__ __launch_bounds__(NT) void k_select_plan(SelectArgs a) {
-  __shared__ BitmapPlanSmem sm;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int T = a.T, E = a.E, K = a.K;
+__global__ __launch_bounds__(NT) void k_select_tokens(SelectArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t = blockIdx.x * (NT / kWave) + wave;
-  if (t < T) select_token<NPER>(a, t, lane);
+  if (t < a.T) select_token<NPER>(a, t, lane);
+}
 
-  // This workgroup's selections are made visible device-wide before it is
-  // counted; the workgroup that arrives last then sees all of them.  The
-  // counter was zeroed by the router kernel of the same call, and is zeroed
-  // again below.
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) sm.last = atomicAdd(a.arrive, 1u) == gridDim.x - 1 ? 1 : 0;
-  __syncthreads();
-  if (!sm.last) return;
-  __threadfence();
-
+// The plan from all tokens' selections, in one workgroup: every token's mask
+// and indices are copied into LDS with independent loads, per-expert token
+// bitmaps give the counts, and a pair's position is off[e] + (kept tokens of
+// e before t): expert-major, tokens ascending within an expert.
+template <int NT>
+__global__ __launch_bounds__(NT) void k_plan_bitmap(SelectArgs a) {
+  __shared__ BitmapPlanSmem sm;
+  const int tid = threadIdx.x;
+  const int T = a.T, E = a.E, K = a.K;
   const int W = (T + kSelBlock - 1) / kSelBlock;
   const int TK = T * K;
   stage_to_lds<NT>(sm.mask, a.mask, T);
@@ -575,7 +561,6 @@ __global__ __launch_bounds__(NT) void k_select_plan(SelectArgs a) {
     }
     a.slot_pos[q] = pos;
   }
-  if (tid == 0) *a.arrive = 0u;
 }
 
 // Multi-block form: one 1024-thread workgroup per 64-token block; each of its
@@ -758,7 +743,6 @@ hipError_t launch_select(const beam_moe_layer& L, int32_t T, int tile_rows, cons
   a.mask = p.mask;
   a.rank = p.rank;
   a.block_counts = p.block_counts;
-  a.arrive = p.arrive;
   a.tile_rows = tile_rows;
   a.has_shared = L.n_shared > 0 ? 1 : 0;
   a.counts = p.counts;
@@ -768,13 +752,17 @@ hipError_t launch_select(const beam_moe_layer& L, int32_t T, int tile_rows, cons
   a.perm_token = p.perm_token;
   a.slot_pos = p.slot_pos;
   if (select_builds_plan(L, T)) {
-    constexpr int nt = kPlanThreads;
+    constexpr int nt = kSelThreads;
     const dim3 g{unsigned((T + nt / kWave - 1) / (nt / kWave)), 1, 1}, b{unsigned(nt), 1, 1};
-    prof_before("select_topk_mask_plan", s);
-    if (L.E <= 64) hipLaunchKernelGGL((k_select_plan<1, nt>), g, b, 0, s, a);
-    else if (L.E <= 128) hipLaunchKernelGGL((k_select_plan<2, nt>), g, b, 0, s, a);
-    else if (L.E <= 256) hipLaunchKernelGGL((k_select_plan<4, nt>), g, b, 0, s, a);
-    else hipLaunchKernelGGL((k_select_plan<16, nt>), g, b, 0, s, a);
+    prof_before("select_topk_mask", s);
+    if (L.E <= 64) hipLaunchKernelGGL((k_select_tokens<1, nt>), g, b, 0, s, a);
+    else if (L.E <= 128) hipLaunchKernelGGL((k_select_tokens<2, nt>), g, b, 0, s, a);
+    else if (L.E <= 256) hipLaunchKernelGGL((k_select_tokens<4, nt>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((k_select_tokens<16, nt>), g, b, 0, s, a);
+    prof_after(s);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    prof_before("plan_bitmap", s);
+    hipLaunchKernelGGL((k_plan_bitmap<kPlanThreads>), dim3(1), dim3(kPlanThreads), 0, s, a);
     prof_after(s);
     return hipGetLastError();
   }

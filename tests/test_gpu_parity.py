@@ -84,11 +84,12 @@ def test_golden_examples(fname, dtype):
         assert np.all(y[2] == 0.0)
 
 
-@pytest.mark.parametrize("T", [1, 37, 100, 129, 512, 513])
+@pytest.mark.parametrize("T", [1, 37, 100, 129, 1638, 1639])
 def test_ragged_batches(T):
-    """Batch sizes that are not multiples of the 16/64-token blocks; 512 is the
-    largest batch whose plan is built by the selection kernel itself, 513 the
-    smallest that takes the scan and scatter kernels."""
+    """Batch sizes that are not multiples of the 16/64-token blocks.  With
+    K = 5, 1638 tokens (8190 selections) is the largest batch whose plan comes
+    from per-expert token bitmaps in one workgroup (at most 8192 selections),
+    1639 the smallest that takes the block ranks, scan and scatter kernels."""
     layer = small_layer("ragged", D=192, E=24, K=5, I=128, S=1, I_s=64, keep=0.45, router_bias=True)
     x = small_x(layer, T, "ragged")
     note(f"[ragged] T={T}")
@@ -151,10 +152,10 @@ def test_k_extremes(E, K):
 
 
 @pytest.mark.parametrize("flags", [1, 2, 3])
-@pytest.mark.parametrize("T", [37, 600])
+@pytest.mark.parametrize("T", [37, 4200])
 def test_gate_options(flags, T):
     """Gate options (softmax over all E; renormalised masked gates), in the
-    one-launch selection (37 tokens) and the multi-block one (600)."""
+    one-wave-per-token selection (37 tokens) and the 64-token-block one (4200)."""
     from oracle_pins import with_gating
     base = small_layer("gates", D=128, E=40, K=6, I=64, S=1, I_s=64, keep=0.4, router_bias=True)
     layer = with_gating(base, flags)
