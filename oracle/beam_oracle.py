@@ -44,6 +44,9 @@ design notes of the repository):
     computed in float64 and rounded once to float32.  Everything else is
     float64.
 
+mask_router_backward follows [P3]'s training strategy (L_reg and the
+straight-through estimator); see its docstring.
+
 Parity status: every function here is pinned by tests in tests/test_oracle.py
 (closed forms, a hand-derived worked example under tests/golden/, library
 special cases and brute-force sums); none is "parity unpinned".
@@ -57,7 +60,7 @@ import numpy as np
 
 __all__ = [
     "widen", "router_logits", "select_experts", "Routing", "route", "silu",
-    "GATE_SOFTMAX_ALL", "GATE_RENORM",
+    "GATE_SOFTMAX_ALL", "GATE_RENORM", "mask_router_backward",
     "expert_ffn", "forward", "expert_counts", "layer_stats",
 ]
 
@@ -211,6 +214,58 @@ def forward(layer, x: np.ndarray, tokens: Optional[Sequence[int]] = None,
     for s in range(cfg.S):
         y += expert_ffn(*_shared_weights(layer, s), X)
     return rt, y
+
+
+def mask_router_backward(layer, x: np.ndarray, dy: np.ndarray, beta: float):
+    """Gradient of L = L_task + beta * L_reg with respect to the mask router.
+
+    [P3] training strategy (method paragraph): L = L_lm + alpha L_bal + beta
+    L_reg with L_reg = (1/K) sum_{i in TK} |m_hat_i|, and the straight-through
+    estimator passes m_hat's gradient through the binarisation (dm/dm_hat :=
+    1); [P1] method section, binarisation and STE.  Over a batch, L_reg is the
+    mean over tokens.  dy = dL_task/dy (float64 [T][D]) is given; with
+    y = sum_k g_k m_k E_k(x):
+
+      dL/dm_hat_k = g_k <dy, E_k(x)> + beta / (T K)       (m_hat > 0)
+      dL/dz_k     = dL/dm_hat_k * m_hat_k (1 - m_hat_k)
+      dL/dWm[e]   = sum over (t, k) with TK_k = e of dL/dz_k * x_t
+      dL/db_m[e]  = sum over the same (t, k) of dL/dz_k
+
+    E_k(x) is evaluated for every top-K candidate, masked or not.  m_hat is
+    taken from the float32-rounded mask logit, like the decisions.  Only the
+    method's own gate (gating 0) is covered.
+
+    Returns (L_reg, dWm [E][D], db_m [E], dz [T][K]) in float64.
+    """
+    cfg = layer.cfg
+    if getattr(cfg, "gating", 0):
+        raise ValueError("the mask-router backward covers the method's own gate only")
+    T = x.shape[0]
+    r, z = router_logits(layer, x)
+    rt = select_experts(r, z, cfg.K)
+    z32 = np.asarray(z, dtype=np.float64).astype(np.float32).astype(np.float64)
+    zk = np.take_along_axis(z32, rt.idx.astype(np.int64), axis=1)
+    mhat = 1.0 / (1.0 + np.exp(-zk))
+    X = widen(x, cfg.dtype)
+    DY = np.asarray(dy, dtype=np.float64)
+    dot = np.zeros((T, cfg.K))
+    for e in np.unique(rt.idx):
+        wg, wu, wd = _expert_weights(layer, int(e))
+        for k in range(cfg.K):
+            rows = np.nonzero(rt.idx[:, k] == e)[0]
+            if rows.size:
+                dot[rows, k] = np.sum(DY[rows] * expert_ffn(wg, wu, wd, X[rows]), axis=1)
+    dmhat = rt.g * dot + beta / (T * cfg.K)
+    dz = dmhat * mhat * (1.0 - mhat)
+    dwm = np.zeros((cfg.E, cfg.D))
+    dbm = np.zeros(cfg.E)
+    for t in range(T):
+        for k in range(cfg.K):
+            e = int(rt.idx[t, k])
+            dwm[e] += dz[t, k] * X[t]
+            dbm[e] += dz[t, k]
+    lreg = float(mhat.sum() / (T * cfg.K))
+    return lreg, dwm, dbm, dz
 
 
 def expert_counts(rt: Routing, E: int) -> np.ndarray:

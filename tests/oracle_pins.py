@@ -204,6 +204,59 @@ def pin_gate_options_identity(O):
     assert np.all(rt1.g.sum(axis=1) < 1.0)   # K < E: part of the mass is outside the top K
 
 
+def pin_mask_backward_autograd(O):
+    """Mask-router gradient against torch autograd of the straight-through
+    surrogate (m replaced by m_hat in y, so dm/dm_hat = 1) plus beta * L_reg,
+    L_reg = mean over tokens of (1/K) sum_{i in TK} m_hat_i."""
+    layer = small_layer("mbwd", D=48, E=7, K=3, I=20, S=1, I_s=12, keep=0.5, router_bias=True)
+    T, beta = 9, 0.37
+    x = small_x(layer, T, "mbwd")
+    dy = np.random.default_rng(11).standard_normal((T, layer.cfg.D))
+    lreg, dwm, dbm, _ = O.mask_router_backward(layer, x, dy, beta)
+    dt = layer.cfg.dtype
+    X = _t(x, dt)
+    r, _ = torch_logits(layer, x)
+    _, idx = torch.topk(r, layer.cfg.K, dim=1)
+    g = torch.softmax(torch.gather(r, 1, idx), dim=1)
+    Wm = _t(layer.w_mask, dt).clone().requires_grad_(True)
+    bm0 = np.zeros(layer.cfg.E) if layer.b_mask is None else np.asarray(layer.b_mask, np.float64)
+    bm = torch.from_numpy(bm0).clone().requires_grad_(True)
+    z = X @ Wm.t() + bm
+    mh = torch.sigmoid(torch.gather(z, 1, idx))
+    y = torch.zeros(T, layer.cfg.D, dtype=torch.float64)
+    for t in range(T):
+        for k in range(layer.cfg.K):
+            y[t] += g[t, k] * mh[t, k] * torch_expert(layer, int(idx[t, k]), X[t:t + 1])[0]
+    L_reg = mh.sum() / (T * layer.cfg.K)
+    L = (torch.from_numpy(dy) * y).sum() + beta * L_reg
+    L.backward()
+    assert abs(lreg - float(L_reg)) < 1e-7
+    assert _rel(dwm, Wm.grad.numpy()) < 1e-6, _rel(dwm, Wm.grad.numpy())
+    assert _rel(dbm, bm.grad.numpy()) < 1e-6
+
+
+def pin_mask_backward_zero_router(O):
+    """Zero-initialised mask router (Wm = 0, b_m = 0): m_hat = 1/2 exactly, so
+    L_reg = 1/2, and with dL/dy = 0 every candidate gets dL/dz = beta/(T K) / 4."""
+    layer = with_mask(small_layer("mbwd0", D=32, E=6, K=2, I=16), True, 0.0)
+    T, beta = 5, 0.8
+    x = small_x(layer, T, "mbwd0")
+    lreg, dwm, dbm, dz = O.mask_router_backward(layer, x, np.zeros((T, layer.cfg.D)), beta)
+    assert lreg == 0.5
+    c = beta / (T * layer.cfg.K) * 0.25
+    assert np.all(dz == c)
+    r, _ = torch_logits(layer, x)
+    _, idx = torch.topk(r, layer.cfg.K, dim=1)
+    X = _t(x, layer.cfg.dtype).numpy()
+    ref = np.zeros((layer.cfg.E, layer.cfg.D))
+    cnt = np.zeros(layer.cfg.E)
+    for t in range(T):
+        for e in idx[t].numpy():
+            ref[e] += c * X[t]
+            cnt[e] += 1
+    assert np.allclose(dwm, ref, rtol=0, atol=1e-15) and np.allclose(dbm, c * cnt, rtol=0, atol=1e-15)
+
+
 def pin_zero_mask_router_is_topk(O):
     """Wm = 0 (zero-initialised mask router): m_hat = 0.5 everywhere, every
     top-K expert is kept, and the layer equals plain top-K MoE (torch)."""
@@ -391,7 +444,8 @@ def pin_stats_formulas(O):
 
 ALL_PINS = [
     pin_golden_routed, pin_golden_shared, pin_golden_gating, pin_gate_options_vs_torch,
-    pin_gate_options_identity, pin_zero_mask_router_is_topk, pin_dense_bruteforce,
+    pin_gate_options_identity, pin_mask_backward_autograd, pin_mask_backward_zero_router,
+    pin_zero_mask_router_is_topk, pin_dense_bruteforce,
     pin_avgk_popcount, pin_mask_bias_extremes, pin_k1, pin_k_equals_e, pin_gate_properties,
     pin_threshold_is_sigmoid_half, pin_batch_invariance, pin_expert_permutation,
     pin_silu_closed_forms, pin_widen_bf16, pin_stats_formulas,

@@ -42,6 +42,12 @@ MUTANTS = {
     "softmax_all_ignored": ("g[t] = w[order] / w.sum()", "g[t] = w[order] / w[order].sum()"),
     # gate option 2 ignored
     "renorm_ignored": ("if gating & GATE_RENORM:", "if False:"),
+    # backward: sigmoid derivative dropped
+    "bwd_no_sigmoid_grad": ("dz = dmhat * mhat * (1.0 - mhat)", "dz = dmhat"),
+    # backward: masked gates used (masked candidates get no task gradient)
+    "bwd_masked_gate": ("dmhat = rt.g * dot + beta / (T * cfg.K)", "dmhat = rt.ghat * dot + beta / (T * cfg.K)"),
+    # backward: L_reg summed over tokens instead of averaged
+    "bwd_lreg_sum": ("lreg = float(mhat.sum() / (T * cfg.K))", "lreg = float(mhat.sum() / cfg.K)"),
     # gate option 2 normalising by the unmasked gates
     "renorm_unmasked_sum": ("s = ghat.sum(axis=1, keepdims=True)", "s = g.sum(axis=1, keepdims=True)"),
     # strict threshold
