@@ -83,6 +83,9 @@ def lib() -> ctypes.CDLL:
         L.beam_moe_route.restype = ctypes.c_int
         L.beam_moe_forward.argtypes = [P(beam_moe_layer), VP, I32, VP, P(beam_route_out), VP, SZ, VP]
         L.beam_moe_forward.restype = ctypes.c_int
+        L.beam_moe_mask_backward.argtypes = [P(beam_moe_layer), VP, VP, I32, ctypes.c_float, VP, VP,
+                                             VP, VP, SZ, VP]
+        L.beam_moe_mask_backward.restype = ctypes.c_int
         L.beam_moe_stats.argtypes = [P(beam_moe_layer), VP, I32, P(beam_stats), VP]
         L.beam_moe_stats.restype = ctypes.c_int
         L.beam_moe_stats_host.argtypes = [P(beam_moe_layer), P(ctypes.c_int32), I32, P(beam_stats)]
@@ -135,6 +138,14 @@ def beam_moe_route(layer: beam_moe_layer, x, T: int, out: beam_route_out, ws, ws
                    stream: int = 0) -> None:
     _check(lib().beam_moe_route(ctypes.byref(layer), _ptr(x), int(T), ctypes.byref(out), _ptr(ws),
                                 int(ws_bytes), stream), "beam_moe_route")
+
+
+def beam_moe_mask_backward(layer: beam_moe_layer, x, dy, T: int, beta: float, dwm, dbm, lreg, ws,
+                           ws_bytes: int, stream: int = 0) -> None:
+    """Mask-router loss value and straight-through gradient (see the header)."""
+    _check(lib().beam_moe_mask_backward(ctypes.byref(layer), _ptr(x), _ptr(dy), int(T), float(beta),
+                                        _ptr(dwm), _ptr(dbm), _ptr(lreg), _ptr(ws), int(ws_bytes),
+                                        stream), "beam_moe_mask_backward")
 
 
 def beam_moe_forward(layer: beam_moe_layer, x, T: int, y, out: Optional[beam_route_out], ws,

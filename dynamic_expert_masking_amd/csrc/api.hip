@@ -54,6 +54,9 @@ WsLayout workspace_layout(const beam_moe_layer& L, int32_t T) {
   w.h_shared = take(size_t(T) * IS * elt);
   w.o = take(TK * L.D * 4);
   w.o_shared = take(IS ? size_t(T) * L.D * 4 : 0);
+  w.zsel = take(TK * 4);
+  w.dz = take(TK * 4);
+  w.lreg_tok = take(size_t(T) * 4);
   w.total = off;
   return w;
 }
@@ -185,6 +188,9 @@ static Ptrs carve(const WsLayout& w, void* ws, const beam_route_out* out) {
   p.h_shared = b + w.h_shared;
   p.o = reinterpret_cast<float*>(b + w.o);
   p.o_shared = reinterpret_cast<float*>(b + w.o_shared);
+  p.zsel = reinterpret_cast<float*>(b + w.zsel);
+  p.dz = reinterpret_cast<float*>(b + w.dz);
+  p.lreg_tok = reinterpret_cast<float*>(b + w.lreg_tok);
   return p;
 }
 
@@ -237,6 +243,35 @@ int beam_moe_forward(const beam_moe_layer* layer, const void* x, int32_t T, void
   BEAM_TRY(launch_gate_up(*layer, x, T, tile_rows, lay, p, s));
   BEAM_TRY(launch_down(*layer, T, tile_rows, lay, p, s));
   BEAM_TRY(launch_combine(*layer, T, p, y, s));
+  return BEAM_OK;
+}
+
+int beam_moe_mask_backward(const beam_moe_layer* layer, const void* x, const void* dy, int32_t T,
+                           float beta, float* dwm, float* dbm, float* lreg, void* ws,
+                           size_t ws_bytes, void* stream) {
+  WsLayout lay;
+  int st = check_call(layer, x, T, ws, ws_bytes, &lay);
+  if (st != BEAM_OK) return st;
+  if (layer->gating != 0) return BEAM_ERR_UNSUPPORTED;
+  if (!dwm || !lreg || (reinterpret_cast<uintptr_t>(dwm) & 15u) ||
+      (reinterpret_cast<uintptr_t>(lreg) & 3u) || (dbm && (reinterpret_cast<uintptr_t>(dbm) & 3u)))
+    return BEAM_ERR_INVALID_ARG;
+  if (T == 0) return BEAM_OK;
+  if (!dy || !aligned16(dy)) return BEAM_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const beam_moe_layer& L = *layer;
+  const Ptrs p = carve(lay, ws, nullptr);
+  const int tile_rows = expert_tile_rows(L, T);
+  // routing with every candidate kept, then every candidate's expert output
+  BEAM_TRY(launch_router_logits(L, x, T, p, s));
+  BEAM_TRY(launch_select(L, T, tile_rows, p, s, true));
+  if (!select_builds_plan(L, T)) {
+    BEAM_TRY(launch_scan(L, T, tile_rows, p, s, true));
+    BEAM_TRY(launch_scatter(L, T, p, s));
+  }
+  BEAM_TRY(launch_gate_up(L, x, T, tile_rows, lay, p, s));
+  BEAM_TRY(launch_down(L, T, tile_rows, lay, p, s));
+  BEAM_TRY(launch_mask_grad(L, x, dy, T, beta, dwm, dbm, lreg, p, s));
   return BEAM_OK;
 }
 

@@ -36,7 +36,7 @@ struct Tile {
 
 struct WsLayout {
   size_t plan, logits, idx, gates, mask, counts, rank, block_counts, expert_off, tiles, perm_token,
-      slot_pos, h, h_shared, o, o_shared, total;
+      slot_pos, h, h_shared, o, o_shared, zsel, dz, lreg_tok, total;
   int32_t max_tiles;
 };
 
@@ -65,6 +65,10 @@ struct Ptrs {
   void* h_shared;
   float* o;
   float* o_shared;
+  // mask-router backward
+  float* zsel;       // [T][K] mask logit of each candidate
+  float* dz;         // [P] dL/dz of each pair (pair order)
+  float* lreg_tok;   // [T] sum of m_hat over the token's candidates
 };
 
 // ---- launchers (return hipSuccess or the launch error) ----
@@ -74,10 +78,13 @@ hipError_t launch_router_logits(const beam_moe_layer& L, const void* x, int32_t 
 // (they and the batch's selections fit in its LDS); otherwise the scan and
 // scatter kernels follow the selection.
 bool select_builds_plan(const beam_moe_layer& L, int32_t T);
+// all_pairs: every top-K candidate is kept (masks written as all ones, gates
+// unmasked, no shared tiles in the plan) and each candidate's mask logit is
+// written to p.zsel -- the routing of the mask-router backward.
 hipError_t launch_select(const beam_moe_layer& L, int32_t T, int tile_rows, const Ptrs& p,
-                         hipStream_t s);
+                         hipStream_t s, bool all_pairs = false);
 hipError_t launch_scan(const beam_moe_layer& L, int32_t T, int tile_rows, const Ptrs& p,
-                       hipStream_t s);
+                       hipStream_t s, bool all_pairs = false);
 hipError_t launch_scatter(const beam_moe_layer& L, int32_t T, const Ptrs& p, hipStream_t s);
 hipError_t launch_gate_up(const beam_moe_layer& L, const void* x, int32_t T, int tile_rows,
                           const WsLayout& w, const Ptrs& p, hipStream_t s);
@@ -86,6 +93,11 @@ hipError_t launch_down(const beam_moe_layer& L, int32_t T, int tile_rows, const 
 hipError_t launch_combine(const beam_moe_layer& L, int32_t T, const Ptrs& p, void* y,
                           hipStream_t s);
 hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t s);
+// Mask-router backward from the all-pairs expert outputs O: per-pair dL/dz and
+// per-token sums of m_hat, then dL/dWm, dL/db_m and L_reg.
+hipError_t launch_mask_grad(const beam_moe_layer& L, const void* x, const void* dy, int32_t T,
+                            float beta, float* dwm, float* dbm, float* lreg, const Ptrs& p,
+                            hipStream_t s);
 
 // Workgroups of `block` threads of `kernel` that fit on the device at once
 // (occupancy x CUs), cached per device and kernel.

@@ -368,6 +368,9 @@ struct SelectArgs {
   uint32_t* mask;
   int32_t* rank;
   int32_t* block_counts;
+  // mask-router backward: keep every candidate, record the mask logits
+  int all_pairs;
+  float* zsel;
   // plan
   int tile_rows, has_shared;
   int32_t* counts;
@@ -474,12 +477,13 @@ __device__ __forceinline__ void select_token(const SelectArgs& a, int t, int lan
     const float c = __shfl(zv[i], e_k & 63, kWave);
     if (i == (e_k >> 6)) z_k = c;
   }
-  const bool keep = slot && z_k >= 0.f;
+  const bool keep = slot && (a.all_pairs || z_k >= 0.f);
   const unsigned long long bal = __ballot(keep);
   const float gh = token_gate<NPER>(a.gating, slot, keep, r_k, r_all);
   if (slot) {
     a.idx[size_t(t) * K + lane] = e_k;
     a.gates[size_t(t) * K + lane] = gh;
+    if (a.all_pairs) a.zsel[size_t(t) * K + lane] = z_k;
   }
   if (lane == 0) a.mask[t] = uint32_t(bal);
 }
@@ -691,7 +695,7 @@ __global__ __launch_bounds__(1024) void k_select(SelectArgs a) {
         const float c = __shfl(zv[j0 + jj][i], e_k & 63, kWave);
         if (i == (e_k >> 6)) z_k = c;
       }
-      const bool keep = slot && z_k >= 0.f;
+      const bool keep = slot && (a.all_pairs || z_k >= 0.f);
       const unsigned long long bal = __ballot(keep);
       float r_all[NPER];
 #pragma unroll
@@ -702,6 +706,7 @@ __global__ __launch_bounds__(1024) void k_select(SelectArgs a) {
         a.idx[size_t(t) * K + lane] = e_k;
         a.gates[size_t(t) * K + lane] = gh;
         s_idx[tl * 32 + lane] = e_k;
+        if (a.all_pairs) a.zsel[size_t(t) * K + lane] = z_k;
       }
       if (lane == 0) {
         a.mask[t] = uint32_t(bal);
@@ -728,7 +733,7 @@ __global__ __launch_bounds__(1024) void k_select(SelectArgs a) {
 }
 
 hipError_t launch_select(const beam_moe_layer& L, int32_t T, int tile_rows, const Ptrs& p,
-                         hipStream_t s) {
+                         hipStream_t s, bool all_pairs) {
   SelectArgs a;
   a.part = p.logits;
   a.KS = router_ksplit(L, T);
@@ -744,7 +749,9 @@ hipError_t launch_select(const beam_moe_layer& L, int32_t T, int tile_rows, cons
   a.rank = p.rank;
   a.block_counts = p.block_counts;
   a.tile_rows = tile_rows;
-  a.has_shared = L.n_shared > 0 ? 1 : 0;
+  a.has_shared = (L.n_shared > 0 && !all_pairs) ? 1 : 0;
+  a.all_pairs = all_pairs ? 1 : 0;
+  a.zsel = p.zsel;
   a.counts = p.counts;
   a.expert_off = p.expert_off;
   a.plan = p.plan;
@@ -810,12 +817,12 @@ __global__ __launch_bounds__(1024) void k_scan(int T, int E, int nblk, int tile_
 }
 
 hipError_t launch_scan(const beam_moe_layer& L, int32_t T, int tile_rows, const Ptrs& p,
-                       hipStream_t s) {
+                       hipStream_t s, bool all_pairs) {
   const int nblk = (T + kSelBlock - 1) / kSelBlock;
   prof_before("scan_tiles", s);
   hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, T, L.E, nblk, tile_rows,
-                     L.n_shared > 0 ? 1 : 0, p.block_counts, p.counts, p.expert_off, p.plan,
-                     p.tiles);
+                     (L.n_shared > 0 && !all_pairs) ? 1 : 0, p.block_counts, p.counts,
+                     p.expert_off, p.plan, p.tiles);
   prof_after(s);
   return hipGetLastError();
 }

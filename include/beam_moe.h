@@ -124,6 +124,28 @@ int beam_moe_forward(const beam_moe_layer *layer, const void *x, int32_t T,
                      void *y, const beam_route_out *out, void *ws,
                      size_t ws_bytes, void *stream);
 
+/* Mask-router training step: the loss value and straight-through gradient.
+ * (BEAM page on aitrends.kr, method paragraph, training strategy: L = L_lm +
+ * alpha L_bal + beta L_reg with L_reg = (1/K) sum_{i in TK} |m_hat_i|; the
+ * straight-through estimator passes m_hat's gradient through the
+ * binarisation, dm/dm_hat := 1.)  Over the batch, L_reg is the mean over the
+ * T tokens.  Given dy = dL_lm/dy [T][D] (layer dtype) and beta, writes
+ *   *lreg         L_reg (one fp32, device memory)
+ *   dwm [E][D]    dL/dWm = sum over top-K candidates (t, k) of expert e of
+ *                 dL/dz_k x_t, dL/dz_k = (g_k <dy_t, E_k(x_t)> + beta/(T K))
+ *                 m_hat_k (1 - m_hat_k), with g the unmasked top-K softmax
+ *                 and E_k evaluated for every candidate, masked or not
+ *   dbm [E]       dL/db_m (same sums of dL/dz_k), or NULL to skip
+ * all fp32, overwritten, device pointers (dwm 16-byte aligned).  Runs the
+ * router and every candidate's expert, so it costs a plain top-K MoE forward;
+ * needs the same workspace as beam_moe_forward.  Only the method's own gate
+ * (gating 0) is supported (otherwise BEAM_ERR_UNSUPPORTED).  Results are
+ * deterministic.  */
+int beam_moe_mask_backward(const beam_moe_layer *layer, const void *x,
+                           const void *dy, int32_t T, float beta, float *dwm,
+                           float *dbm, float *lreg, void *ws, size_t ws_bytes,
+                           void *stream);
+
 /* Work accounting from the device expert counts of a route/forward call:
  * copies expert_count [E] to the host and SYNCHRONISES the stream. */
 int beam_moe_stats(const beam_moe_layer *layer, const int32_t *expert_count,

@@ -230,7 +230,7 @@ def pin_mask_backward_autograd(O):
     L_reg = mh.sum() / (T * layer.cfg.K)
     L = (torch.from_numpy(dy) * y).sum() + beta * L_reg
     L.backward()
-    assert abs(lreg - float(L_reg)) < 1e-7
+    assert abs(lreg - float(L_reg.detach())) < 1e-7
     assert _rel(dwm, Wm.grad.numpy()) < 1e-6, _rel(dwm, Wm.grad.numpy())
     assert _rel(dbm, bm.grad.numpy()) < 1e-6
 

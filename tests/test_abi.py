@@ -103,6 +103,23 @@ def test_forward_rejects_bad_calls():
     assert f(ctypes.byref(L), FAKE, 0, FAKE * 2, None, None, 0, None) == dm.BEAM_OK
 
 
+def test_mask_backward_argument_checks():
+    L = fake_layer()
+    ws = 0x20000
+    n = dm.beam_moe_workspace_size(L, 4)
+    lib = dm.lib()
+    def call(layer, dwm=FAKE, lreg=FAKE, dy=FAKE, T=4, ws_bytes=n):
+        return lib.beam_moe_mask_backward(ctypes.byref(layer), FAKE, dy, T, 0.1, dwm, None, lreg,
+                                          ws, ws_bytes, None)
+    assert call(fake_layer(gating=1)) == dm.BEAM_ERR_UNSUPPORTED
+    assert call(L, dwm=None) == dm.BEAM_ERR_INVALID_ARG
+    assert call(L, dwm=FAKE + 4) == dm.BEAM_ERR_INVALID_ARG     # dWm must be 16-byte aligned
+    assert call(L, lreg=None) == dm.BEAM_ERR_INVALID_ARG
+    assert call(L, dy=None) == dm.BEAM_ERR_INVALID_ARG
+    assert call(L, ws_bytes=n - 1) == dm.BEAM_ERR_WORKSPACE
+    assert call(L, T=0) == dm.BEAM_OK
+
+
 def test_route_requires_all_outputs():
     L = fake_layer()
     r = dm.lib().beam_moe_route

@@ -183,6 +183,70 @@ def test_gate_options_on_workload():
     check_output(y[toks], y_ref, cfg.dtype)
 
 
+def _mask_backward_case(layer, x, beta, seed, dev=None):
+    import dynamic_expert_masking_amd as dm
+    from dynamic_expert_masking_amd.device import to_device
+    cfg = layer.cfg
+    T = x.shape[0]
+    dy32 = np.random.default_rng(seed).standard_normal((T, cfg.D)).astype(np.float32)
+    dy_store = synth.f32_to_bf16_bits(dy32) if cfg.dtype == "bf16" else dy32
+    dl = dev or device_layer(layer)
+    ws = dl.workspace(T)
+    dwm = torch.empty(cfg.E, cfg.D, dtype=torch.float32, device="cuda")
+    dbm = torch.empty(cfg.E, dtype=torch.float32, device="cuda")
+    lreg = torch.empty(1, dtype=torch.float32, device="cuda")
+    dm.beam_moe_mask_backward(dl.desc, to_device(x), to_device(dy_store), T, beta, dwm, dbm, lreg,
+                              ws, ws.numel(), torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    dy64 = oracle.widen(dy_store, cfg.dtype)
+    lreg_ref, dwm_ref, dbm_ref, _ = oracle.mask_router_backward(layer, x, dy64, beta)
+    tol = 3e-2 if cfg.dtype == "bf16" else 1e-4
+    assert abs(float(lreg.item()) - lreg_ref) <= 2e-6, (float(lreg.item()), lreg_ref)
+    for got, ref, name in ((dwm.cpu().numpy(), dwm_ref, "dWm"), (dbm.cpu().numpy(), dbm_ref, "db_m")):
+        err = np.abs(got - ref).max()
+        assert err <= tol * np.abs(ref).max(), f"{name}: max|err| {err:.3e} vs max|ref| {np.abs(ref).max():.3e}"
+    return dwm, dbm
+
+
+@pytest.mark.parametrize("T", [37, 4200])
+def test_mask_backward_small(T):
+    """Mask-router loss value and straight-through gradient, one-wave-per-token
+    selection (37 tokens) and the 64-token-block one (4200)."""
+    layer = small_layer("mbwd", D=128, E=40, K=6, I=64, S=1, I_s=64, keep=0.4, router_bias=True)
+    x = small_x(layer, T, "mbwd")
+    note(f"[mask backward] small T={T}")
+    _mask_backward_case(layer, x, 0.25, 3)
+
+
+def test_mask_backward_f32_and_zero():
+    """fp32 layer (tiny workload); with dL/dy = 0 and beta = 0 the gradient is exactly 0."""
+    import dynamic_expert_masking_amd as dm
+    from dynamic_expert_masking_amd.device import to_device
+    name = "tiny_f32"
+    cfg = synth.CONFIGS[name]
+    layer = cached_layer(name)
+    x = inputs(cfg, 64, layer)
+    note("[mask backward] tiny_f32 T=64")
+    dl = device_layer(layer, key=name)
+    _mask_backward_case(layer, x, 0.5, 4, dl)
+    ws = dl.workspace(64)
+    dwm = torch.full((cfg.E, cfg.D), 7.0, device="cuda")
+    lreg = torch.empty(1, device="cuda")
+    dm.beam_moe_mask_backward(dl.desc, to_device(x), torch.zeros(64, cfg.D, device="cuda"), 64, 0.0,
+                              dwm, None, lreg, ws, ws.numel(), torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dwm).item() == 0
+
+
+def test_mask_backward_workload():
+    name, T = "dsv2lite_decode", 64
+    cfg = synth.CONFIGS[name]
+    layer = cached_layer(name)
+    x = inputs(cfg, T, layer)
+    note("[mask backward] dsv2lite_decode T=64")
+    _mask_backward_case(layer, x, 0.1, 5, device_layer(layer, key=name))
+
+
 def test_route_entry_matches_forward():
     name, T = "finegrained", 512
     cfg = synth.CONFIGS[name]
