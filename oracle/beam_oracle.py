@@ -47,6 +47,16 @@ design notes of the repository):
 mask_router_backward follows [P3]'s training strategy (L_reg and the
 straight-through estimator); see its docstring.
 
+FP8 expert weights ([P1], section on interfaces with existing products and
+workflows, item 3: the masking combines with model quantisation): a layer
+whose config has expert_format "fp8" stores every routed and shared expert
+matrix as OCP FP8 E4M3 codes with one float32 scale per output row.  Its
+weights are decode_e4m3(code) * scale[row], exactly, in float64; everything
+after that is the same computation.  decode_e4m3 is written from the format's
+definition (OCP 8-bit floating point specification, E4M3: 1 sign bit,
+4 exponent bits with bias 7, 3 mantissa bits, subnormals at exponent field 0,
+S.1111.111 is NaN, no infinities).
+
 Parity status: every function here is pinned by tests in tests/test_oracle.py
 (closed forms, a hand-derived worked example under tests/golden/, library
 special cases and brute-force sums); none is "parity unpinned".
@@ -61,7 +71,8 @@ import numpy as np
 __all__ = [
     "widen", "router_logits", "select_experts", "Routing", "route", "silu",
     "GATE_SOFTMAX_ALL", "GATE_RENORM", "mask_router_backward",
-    "expert_ffn", "forward", "expert_counts", "layer_stats",
+    "expert_ffn", "forward", "expert_counts", "layer_stats", "decode_e4m3",
+    "expert_matrices",
 ]
 
 
@@ -172,14 +183,48 @@ def expert_ffn(wg: np.ndarray, wu: np.ndarray, wd: np.ndarray, X: np.ndarray) ->
     return h @ wd.T
 
 
+def decode_e4m3(codes: np.ndarray) -> np.ndarray:
+    """Value of OCP FP8 E4M3 codes (uint8) as float64.
+
+    Bit 7 is the sign, bits 6..3 the exponent field e, bits 2..0 the
+    mantissa field m.  e = 0: (-1)^s m 2^-9 (subnormal, 2^(1-7) m/8);
+    0 < e: (-1)^s (1 + m/8) 2^(e-7); e = 15 with m = 7 is NaN (the format
+    has no infinities, so e = 15, m < 7 are ordinary values up to 448).
+    """
+    c = np.asarray(codes)
+    if c.dtype != np.uint8:
+        raise TypeError("E4M3 codes are stored as uint8")
+    c = c.astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    mag = np.where((e == 15) & ((c & 0x7) == 7), np.nan, mag)
+    return sign * mag
+
+
+def _matrix(layer, name: str, i: int) -> np.ndarray:
+    """float64 value of expert matrix `name` ("w_gate", "ws_down", ...) number i."""
+    cfg = layer.cfg
+    a = getattr(layer, name)[i]
+    if getattr(cfg, "expert_format", "") == "fp8":
+        scale = getattr(layer, "s" + name[1:] if name.startswith("ws_") else "s_" + name[2:])[i]
+        return decode_e4m3(a) * np.asarray(scale, dtype=np.float64)[:, None]
+    return widen(a, cfg.dtype)
+
+
+def expert_matrices(layer, i: int, shared: bool = False):
+    """(Wg, Wu, Wd) of routed expert i, or of shared expert i, in float64."""
+    p = "ws_" if shared else "w_"
+    return tuple(_matrix(layer, p + n, i) for n in ("gate", "up", "down"))
+
+
 def _expert_weights(layer, e: int):
-    dt = layer.cfg.dtype
-    return (widen(layer.w_gate[e], dt), widen(layer.w_up[e], dt), widen(layer.w_down[e], dt))
+    return expert_matrices(layer, e)
 
 
 def _shared_weights(layer, s: int):
-    dt = layer.cfg.dtype
-    return (widen(layer.ws_gate[s], dt), widen(layer.ws_up[s], dt), widen(layer.ws_down[s], dt))
+    return expert_matrices(layer, s, shared=True)
 
 
 def forward(layer, x: np.ndarray, tokens: Optional[Sequence[int]] = None,
@@ -288,6 +333,10 @@ def layer_stats(cfg, counts: np.ndarray, T: int) -> dict:
     active = int((counts > 0).sum())
     elt = 4 if cfg.dtype == "f32" else 2
     D, I = cfg.D, cfg.I
+    fp8 = getattr(cfg, "expert_format", "") == "fp8"
+    # bytes of one expert's three matrices (FP8: codes plus a float32 per row)
+    per_routed = 3 * D * I + 4 * (2 * I + D) if fp8 else 3 * D * I * elt
+    per_shared = 3 * D * cfg.I_s + 4 * (2 * cfg.I_s + D) if fp8 else 3 * D * cfg.I_s * elt
     out = {
         "T": T, "E": cfg.E, "K": cfg.K,
         "active_pairs": P,
@@ -297,7 +346,7 @@ def layer_stats(cfg, counts: np.ndarray, T: int) -> dict:
         "flops_topk_routed": 6.0 * D * I * T * cfg.K,
         "flops_shared": 6.0 * D * cfg.I_s * cfg.S * T,
         "flops_router": 4.0 * cfg.E * D * T,
-        "bytes_active_expert_weights": float(3 * D * I * elt * active + 3 * D * cfg.I_s * elt * cfg.S),
+        "bytes_active_expert_weights": float(per_routed * active + per_shared * cfg.S),
     }
     out["flops_reduction"] = (1.0 - out["flops_routed"] / out["flops_topk_routed"]) if T > 0 else 0.0
     out["bytes_total_min"] = (out["bytes_active_expert_weights"]

@@ -18,6 +18,13 @@ weights ~ N(0, 0.5/D) so that a mask logit has standard deviation sqrt(0.5);
 a scalar mask bias sqrt(0.5) * Phi^-1(keep) sets the expected keep rate of a
 top-K candidate; the skewed prefill workload adds a per-expert router bias
 ~ N(0, 1).
+
+FP8 workloads store the routed and shared expert weights as OCP FP8 E4M3
+codes (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; largest finite
+value 448; no infinities) with one float32 scale per output row: the
+float32 draws of a row are divided by max|row| / 448 and rounded to the
+nearest code, ties to the even code.  This is how the inputs are prepared,
+like the bf16 rounding above; the layer only ever reads the codes and scales.
 """
 from __future__ import annotations
 
@@ -34,6 +41,7 @@ BASE_SEED = 20260514
 
 F32 = "f32"
 BF16 = "bf16"
+FP8 = "fp8"     # expert_format: OCP E4M3 expert weights with per-row float32 scales
 
 
 @dataclass(frozen=True)
@@ -51,6 +59,7 @@ class LayerConfig:
     keep: float         # expected keep probability of a top-K candidate
     router_bias: bool   # per-expert router bias ~ N(0, 1)
     gating: int = 0     # gate option bits: 1 softmax over all E, 2 renormalise after masking
+    expert_format: str = ""   # "" = expert weights in dtype; FP8 = E4M3 codes + row scales
 
     @property
     def avg_k_target(self) -> float:
@@ -80,6 +89,10 @@ CONFIGS: Dict[str, LayerConfig] = {
     # Fine-grained layer, extreme sparsity (Avg-K ~0.15 K).
     "finegrained": LayerConfig("finegrained", BF16, D=1536, E=212, K=16, I=256, S=0, I_s=0,
                                tokens=(16, 512, 8192), keep=0.15, router_bias=False),
+    # The DeepSeek-V2-Lite-shaped decode layer with FP8 (E4M3) expert weights.
+    "dsv2lite_decode_fp8": LayerConfig("dsv2lite_decode_fp8", BF16, D=2048, E=64, K=6, I=1408,
+                                       S=2, I_s=1408, tokens=(1, 8, 64, 256), keep=0.5,
+                                       router_bias=False, expert_format=FP8),
 }
 
 CONFIG_ORDER = ("tiny_f32", "dsv2lite_decode", "dsv2lite_prefill", "mixtral", "finegrained")
@@ -133,6 +146,59 @@ def _threads() -> int:
     return max(1, min(16, os.cpu_count() or 1))
 
 
+# Non-negative E4M3 values in code order (codes 0x00 .. 0x7E; 0x7F is NaN):
+# exponent field 0 holds the subnormals m * 2^-9, field e > 0 the values
+# (1 + m/8) * 2^(e-7).  Strictly increasing, so a code is found by bisection.
+_E4M3_POS = np.array([(m * 2.0 ** -9) if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 7)
+                      for e in range(16) for m in range(8)][:127], dtype=np.float64)
+E4M3_MAX = 448.0
+
+
+def e4m3_encode(a: np.ndarray) -> np.ndarray:
+    """Nearest E4M3 code (ties to the even code) of each float32 value in
+    [-448, 448]; returns uint8 codes.  -0.0 keeps its sign bit."""
+    a = np.asarray(a, dtype=np.float32)
+    if not np.all(np.abs(a) <= E4M3_MAX):
+        raise ValueError("values outside the E4M3 range")
+    mag = np.abs(a).astype(np.float64).ravel()
+    hi = np.searchsorted(_E4M3_POS, mag, side="left")      # first value >= mag
+    hi = np.minimum(hi, 126)
+    lo = np.maximum(hi - 1, 0)
+    d_hi = _E4M3_POS[hi] - mag
+    d_lo = mag - _E4M3_POS[lo]
+    pick_lo = (d_lo < d_hi) | ((d_lo == d_hi) & (lo % 2 == 0))
+    code = np.where(d_hi == 0.0, hi, np.where(pick_lo, lo, hi)).astype(np.uint8)
+    code |= (np.signbit(a.ravel()).astype(np.uint8) << np.uint8(7))
+    return code.reshape(a.shape)
+
+
+def quantize_rows_e4m3(w: np.ndarray):
+    """Per-row scaled E4M3 codes of a float32 matrix [R][C]: scale = max|row|
+    / 448 (1 for an all-zero row), code = nearest E4M3 to w / scale."""
+    w = np.asarray(w, dtype=np.float32)
+    amax = np.abs(w).max(axis=-1)
+    scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    q = w / scale[..., None]
+    np.clip(q, -E4M3_MAX, E4M3_MAX, out=q)
+    return e4m3_encode(q), scale
+
+
+def _gen_fp8(cfg: LayerConfig, name: str, shape: Tuple[int, ...], std: float):
+    """E4M3 codes [n][R][C] and row scales [n][R] of N(0, std^2) draws, one
+    stream per leading index (the same streams as an unquantised tensor)."""
+    codes = np.empty(shape, dtype=np.uint8)
+    scales = np.empty(shape[:2], dtype=np.float32)
+    inner = int(np.prod(shape[1:]))
+
+    def fill(i):
+        a = normal_f32(stream_key(cfg.name, name, i), inner, std).reshape(shape[1:])
+        codes[i], scales[i] = quantize_rows_e4m3(a)
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(fill, range(shape[0])))
+    return codes, scales
+
+
 def _gen_tensor(cfg: LayerConfig, name: str, shape: Tuple[int, ...], std: float,
                 split_leading: bool) -> np.ndarray:
     """Tensor of N(0, std^2) values; with split_leading, one stream per leading index."""
@@ -155,7 +221,8 @@ def _gen_tensor(cfg: LayerConfig, name: str, shape: Tuple[int, ...], std: float,
 
 @dataclass
 class Layer:
-    """Host copy of one layer's parameters (bf16 as uint16 bits, f32 as float32)."""
+    """Host copy of one layer's parameters (bf16 as uint16 bits, f32 as float32,
+    FP8 expert weights as uint8 E4M3 codes with float32 row scales)."""
     cfg: LayerConfig
     w_router: np.ndarray              # [E][D]
     w_mask: np.ndarray                # [E][D]
@@ -168,6 +235,13 @@ class Layer:
     ws_up: Optional[np.ndarray] = None     # [S][I_s][D]
     ws_down: Optional[np.ndarray] = None   # [S][D][I_s]
     extra: dict = field(default_factory=dict)
+    # FP8 expert weights only: float32 scale of each output row
+    s_gate: Optional[np.ndarray] = None    # [E][I]
+    s_up: Optional[np.ndarray] = None      # [E][I]
+    s_down: Optional[np.ndarray] = None    # [E][D]
+    ss_gate: Optional[np.ndarray] = None   # [S][I_s]
+    ss_up: Optional[np.ndarray] = None     # [S][I_s]
+    ss_down: Optional[np.ndarray] = None   # [S][D]
 
 
 def make_layer(cfg: LayerConfig, experts: bool = True) -> Layer:
@@ -180,6 +254,10 @@ def make_layer(cfg: LayerConfig, experts: bool = True) -> Layer:
     b_router = normal_f32(stream_key(cfg.name, "b_router"), E, 1.0) if cfg.router_bias else None
     bm = cfg.mask_bias
     b_mask = np.full(E, bm, dtype=np.float32) if bm != 0.0 else None
+    if cfg.expert_format == FP8:
+        if cfg.dtype != BF16:
+            raise ValueError("FP8 expert weights go with bf16 activations")
+        return _make_fp8_experts(cfg, w_router, w_mask, b_router, b_mask, experts)
     if experts:
         w_gate = _gen_tensor(cfg, "w_gate", (E, I, D), sd, True)
         w_up = _gen_tensor(cfg, "w_up", (E, I, D), sd, True)
@@ -194,6 +272,24 @@ def make_layer(cfg: LayerConfig, experts: bool = True) -> Layer:
         ws_down = _gen_tensor(cfg, "ws_down", (cfg.S, D, cfg.I_s), sd, True)
     return Layer(cfg, w_router, w_mask, b_router, b_mask, w_gate, w_up, w_down,
                  ws_gate, ws_up, ws_down)
+
+
+def _make_fp8_experts(cfg, w_router, w_mask, b_router, b_mask, experts):
+    D, E, I = cfg.D, cfg.E, cfg.I
+    sd = 1.0 / math.sqrt(D)
+    if not experts:
+        z = np.empty((E, 0, 0), dtype=np.uint8)
+        return Layer(cfg, w_router, w_mask, b_router, b_mask, z, z, z)
+    w_gate, s_gate = _gen_fp8(cfg, "w_gate", (E, I, D), sd)
+    w_up, s_up = _gen_fp8(cfg, "w_up", (E, I, D), sd)
+    w_down, s_down = _gen_fp8(cfg, "w_down", (E, D, I), sd)
+    sh = {}
+    if cfg.S > 0:
+        sh["ws_gate"], sh["ss_gate"] = _gen_fp8(cfg, "ws_gate", (cfg.S, cfg.I_s, D), sd)
+        sh["ws_up"], sh["ss_up"] = _gen_fp8(cfg, "ws_up", (cfg.S, cfg.I_s, D), sd)
+        sh["ws_down"], sh["ss_down"] = _gen_fp8(cfg, "ws_down", (cfg.S, D, cfg.I_s), sd)
+    return Layer(cfg, w_router, w_mask, b_router, b_mask, w_gate, w_up, w_down,
+                 s_gate=s_gate, s_up=s_up, s_down=s_down, **sh)
 
 
 def make_x(cfg: LayerConfig, T: int, stream: str = "x") -> np.ndarray:

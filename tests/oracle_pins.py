@@ -76,14 +76,31 @@ def with_gating(layer, gating):
     return replace(layer, cfg=replace(layer.cfg, gating=gating))
 
 
-def torch_expert(layer, e, X, shared=False):
+def torch_e4m3(codes):
+    """float64 values of E4M3 codes by torch's own float8_e4m3fn type."""
+    c = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8))
+    return c.view(torch.float8_e4m3fn).to(torch.float64)
+
+
+def torch_weights(layer, e, shared=False):
+    """(Wg, Wu, Wd) in float64: stored values, or E4M3 codes times row scales."""
     dt = layer.cfg.dtype
-    if shared:
-        wg, wu, wd = layer.ws_gate[e], layer.ws_up[e], layer.ws_down[e]
-    else:
-        wg, wu, wd = layer.w_gate[e], layer.w_up[e], layer.w_down[e]
-    h = F.silu(X @ _t(wg, dt).t()) * (X @ _t(wu, dt).t())
-    return h @ _t(wd, dt).t()
+    names = ("ws_gate", "ws_up", "ws_down") if shared else ("w_gate", "w_up", "w_down")
+    out = []
+    for n in names:
+        a = getattr(layer, n)[e]
+        if getattr(layer.cfg, "expert_format", "") == "fp8":
+            sc = getattr(layer, ("ss_" if shared else "s_") + n.split("_")[1])[e]
+            out.append(torch_e4m3(a) * torch.from_numpy(np.asarray(sc, np.float64)).unsqueeze(1))
+        else:
+            out.append(_t(a, dt))
+    return out
+
+
+def torch_expert(layer, e, X, shared=False):
+    wg, wu, wd = torch_weights(layer, e, shared)
+    h = F.silu(X @ wg.t()) * (X @ wu.t())
+    return h @ wd.t()
 
 
 def torch_dense_forward(layer, x, use_mask=True):
@@ -428,6 +445,59 @@ def pin_widen_bf16(O):
     assert v[5] == float.fromhex("0x1.fep+127")
 
 
+def pin_e4m3_known_values(O):
+    """E4M3 values fixed by the format (OCP 8-bit floating point, E4M3):
+    1.0 = 0 0111 000, the largest finite 448 = S 1111 110, the smallest
+    subnormal 2^-9 = 0 0000 001, the smallest normal 2^-6 = 0 0001 000,
+    S 1111 111 is NaN, and exponent field 15 with m < 7 is finite."""
+    codes = np.array([0x38, 0xB8, 0x7E, 0xFE, 0x01, 0x07, 0x08, 0x3C, 0x77, 0x78,
+                      0x00, 0x80, 0x7F, 0xFF, 0x3B, 0x30], dtype=np.uint8)
+    v = O.decode_e4m3(codes)
+    want = [1.0, -1.0, 448.0, -448.0, 2.0 ** -9, 7 * 2.0 ** -9, 2.0 ** -6, 1.5, 240.0, 256.0,
+            0.0, -0.0]
+    assert np.array_equal(v[:12], want)
+    assert np.signbit(v[11]) and not np.signbit(v[10])
+    assert np.isnan(v[12]) and np.isnan(v[13])
+    assert v[14] == 1.375 and v[15] == 0.5
+
+
+def pin_e4m3_vs_torch(O):
+    """All 256 codes against torch's float8_e4m3fn conversion (NaN codes as NaN)."""
+    codes = np.arange(256, dtype=np.uint8)
+    v = O.decode_e4m3(codes)
+    ref = torch_e4m3(codes).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(v), nan)
+    assert np.array_equal(v[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(v[~nan]), np.signbit(ref[~nan]))
+
+
+def fp8_layer(tag, D=64, E=9, K=3, I=32, S=1, I_s=32, keep=0.5, router_bias=False):
+    from dataclasses import replace
+    cfg = replace(small_config("pin:" + tag, "bf16", D, E, K, I, S, I_s, keep, router_bias),
+                  expert_format="fp8")
+    return synth.make_layer(cfg)
+
+
+def pin_fp8_layer_vs_torch(O):
+    """A layer with E4M3 expert weights and row scales (routed and shared):
+    the oracle's forward equals the torch brute-force dense sum whose weights
+    are torch's float8_e4m3fn values times the row scales."""
+    for tag, kw in (("fp8_a", dict(D=64, E=9, K=3, I=32, S=2, I_s=32, keep=0.5)),
+                    ("fp8_b", dict(D=32, E=6, K=2, I=48, S=0, I_s=0, keep=0.7, router_bias=True))):
+        layer = fp8_layer(tag, **kw)
+        assert layer.w_gate.dtype == np.uint8
+        x = small_x(layer, 19)
+        rt, y = O.forward(layer, x)
+        ref = torch_dense_forward(layer, x, use_mask=True)
+        assert _rel(y, ref) < 1e-12, (tag, _rel(y, ref))
+        st = O.layer_stats(layer.cfg, O.expert_counts(rt, layer.cfg.E), x.shape[0])
+        c = layer.cfg
+        act = int((O.expert_counts(rt, c.E) > 0).sum())
+        assert st["bytes_active_expert_weights"] == act * (3 * c.D * c.I + 4 * (2 * c.I + c.D)) + \
+            c.S * (3 * c.D * c.I_s + 4 * (2 * c.I_s + c.D))
+
+
 def pin_stats_formulas(O):
     """FLOPs and bytes: FLOPs(BEAM)/FLOPs(top-K) = AvgK/K; per-expert SwiGLU
     cost 6*D*I per pair; bytes count each active expert once."""
@@ -449,4 +519,5 @@ ALL_PINS = [
     pin_avgk_popcount, pin_mask_bias_extremes, pin_k1, pin_k_equals_e, pin_gate_properties,
     pin_threshold_is_sigmoid_half, pin_batch_invariance, pin_expert_permutation,
     pin_silu_closed_forms, pin_widen_bf16, pin_stats_formulas,
+    pin_e4m3_known_values, pin_e4m3_vs_torch, pin_fp8_layer_vs_torch,
 ]

@@ -79,6 +79,21 @@ MUTANTS = {
     "mask_from_router": ("keep[t] = z32[t, order] >= np.float32(0.0)", "keep[t] = r32[t, order] >= np.float32(0.0)"),
     # bf16 widening drops the shift
     "widen_wrong": ("(a.astype(np.uint32) << np.uint32(16))", "(a.astype(np.uint32) << np.uint32(15))"),
+    # E4M3 exponent bias 8 instead of 7
+    "e4m3_bias8": ("np.exp2(e.astype(np.float64) - 7.0)", "np.exp2(e.astype(np.float64) - 8.0)"),
+    # E4M3 exponent field 0 decoded as a normal number
+    "e4m3_no_subnormals": ("np.where(e == 0, m * 2.0 ** -9,", "np.where(e < 0, m * 2.0 ** -9,"),
+    # every code with exponent field 15 taken as NaN (as in formats with infinities)
+    "e4m3_top_binade_nan": ("np.where((e == 15) & ((c & 0x7) == 7), np.nan, mag)",
+                            "np.where(e == 15, np.nan, mag)"),
+    # FP8 row scales not applied
+    "fp8_no_scale": ("return decode_e4m3(a) * np.asarray(scale, dtype=np.float64)[:, None]",
+                     "return decode_e4m3(a)"),
+    # FP8 scale applied per input column (broadcast over the other axis)
+    "fp8_scale_columns": ("return decode_e4m3(a) * np.asarray(scale, dtype=np.float64)[:, None]",
+                          "return decode_e4m3(a) * np.resize(np.asarray(scale, dtype=np.float64), a.shape[1])[None, :]"),
+    # shared experts read the routed experts' scales
+    "fp8_shared_uses_routed_scales": ('"s" + name[1:] if name.startswith("ws_")', '"s_" + name[3:] if name.startswith("ws_")'),
     # Avg-K counts all top-K slots
     "avgk_topk": ('"avg_k": (P / T) if T > 0 else 0.0', '"avg_k": (cfg.K if T > 0 else 0.0)'),
 }
