@@ -16,7 +16,9 @@ bytes per launch (the gate and up weights of the experts that received at
 least one pair, plus the shared experts' gate and up weights) divided by its
 mean launch time from hipEvents recorded around each launch on the call's
 stream during a second timed pass.  `cpu_baseline` times the float64 oracle
-on the host on a bounded sample of the same workload.
+on the host on a bounded sample of the same workload.  `fp8_weights` reports
+the same decode layer with its expert weights stored as OCP FP8 E4M3 codes
+with fp32 row scales (same batch size, same timing method).
 """
 from __future__ import annotations
 
@@ -50,6 +52,8 @@ def parse():
     p.add_argument("--pool", type=int, default=16, help="distinct input batches")
     p.add_argument("--no-sweep", action="store_true", help="skip the other batch sizes")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--no-fp8", action="store_true",
+                   help="skip the FP8 (E4M3) expert-weight variant of the decode layer")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--calibrate-copy", type=int, default=0,
                    help="only run the plain copy kernel on this many MiB (counter calibration)")
@@ -112,28 +116,37 @@ def main():
         return
 
     cfg = synth.CONFIGS[args.config]
-    T = args.tokens or (64 if args.config == "dsv2lite_decode" else cfg.tokens[-1])
-    t0 = time.time()
-    host = synth.make_layer(cfg)
-    dl = DeviceLayer(host, dev)
-    per_copy = sum(v.numel() * v.element_size() for k, v in dl.t.items() if v is not None)
-    copies = args.copies or max(2, min(16, int(np.ceil(1.5e9 / max(1, per_copy))) + 1))
-    reps = [(dl.t, dl.desc)] + dl.replicas(copies - 1)
-    print(f"[bench] {cfg.name}: layer {per_copy / 1e9:.2f} GB x {copies} copies "
-          f"(setup {time.time() - t0:.1f}s)", file=sys.stderr, flush=True)
+    T = args.tokens or (64 if args.config.startswith("dsv2lite_decode") else cfg.tokens[-1])
 
-    def run_T(Tb: int, steps: int, warmup: int, profile: bool):
-        xs = [to_device(synth.make_x(cfg, Tb, f"bench{i}"), dev) for i in range(args.pool)]
-        y = torch.empty(Tb, cfg.D, dtype=dl.torch_dtype, device=dev)
+    def setup(c):
+        t0 = time.time()
+        host = synth.make_layer(c)
+        dl = DeviceLayer(host, dev)
+        per_copy = sum(v.numel() * v.element_size() for k, v in dl.t.items() if v is not None)
+        copies = args.copies or max(2, min(16, int(np.ceil(1.5e9 / max(1, per_copy))) + 1))
+        reps = [(dl.t, dl.desc)] + dl.replicas(copies - 1)
+        print(f"[bench] {c.name}: layer {per_copy / 1e9:.2f} GB x {copies} copies "
+              f"(setup {time.time() - t0:.1f}s)", file=sys.stderr, flush=True)
+        return host, dl, reps, copies
+
+    def gate_up_bytes(c, active):
+        """Algorithmic bytes of one gate/up launch: gate and up weights (and
+        FP8 row scales) of the active routed experts and of the shared ones."""
+        if c.expert_format == synth.FP8:
+            return (2 * c.D * c.I + 8 * c.I) * active + (2 * c.D * c.I_s + 8 * c.I_s) * c.S
+        elt = 4 if c.dtype == "f32" else 2
+        return 2 * c.D * c.I * elt * active + 2 * c.D * c.I_s * elt * c.S
+
+    def run_T(c, dl, reps, Tb: int, steps: int, warmup: int, profile: bool):
+        xs = [to_device(synth.make_x(c, Tb, f"bench{i}"), dev) for i in range(args.pool)]
+        y = torch.empty(Tb, c.D, dtype=dl.torch_dtype, device=dev)
         ws = dl.workspace(Tb)
-        counts = torch.empty(cfg.E, dtype=torch.int32, device=dev)
         # per-batch work accounting (outside any timed region)
         stats = []
         for i in range(args.pool):
             bufs, out = dl.route_buffers(Tb)
             dm.beam_moe_route(dl.desc, xs[i], Tb, out, ws, ws.numel(), sh)
             stats.append(dm.beam_moe_stats(dl.desc, bufs["expert_count"], Tb, sh))
-        del counts
 
         def step(i):
             _, desc = reps[i % len(reps)]
@@ -165,15 +178,12 @@ def main():
             prof = dm.beam_profile_end(64)
             res["kernels"] = {k: {"launches": n, "mean_us": ms * 1e3 / max(n, 1)}
                               for k, (n, ms) in prof.items()}
-            # algorithmic bytes of the gate/up launches: gate+up weights of the
-            # active routed experts plus the shared experts
-            D, I = cfg.D, cfg.I
-            elt = 4 if cfg.dtype == "f32" else 2
-            gu = [2 * D * I * elt * s["active_experts"] + 2 * D * cfg.I_s * elt * cfg.S for s in used]
-            res["gate_up_alg_bytes"] = float(np.mean(gu))
+            res["gate_up_alg_bytes"] = float(np.mean([gate_up_bytes(c, s["active_experts"])
+                                                      for s in used]))
         return res
 
-    main_res = run_T(T, args.steps, args.warmup, profile=True)
+    host, dl, reps, copies = setup(cfg)
+    main_res = run_T(cfg, dl, reps, T, args.steps, args.warmup, profile=True)
     ms = main_res["ms_per_step"]
     value = T / (ms / 1e3)
 
@@ -195,11 +205,38 @@ def main():
         for Tb in cfg.tokens:
             if Tb == T:
                 continue
-            r = run_T(Tb, max(10, args.steps // 2), args.warmup, profile=False)
+            r = run_T(cfg, dl, reps, Tb, max(10, args.steps // 2), args.warmup, profile=False)
             sweep.append({"T": Tb, "tokens_per_s": round(Tb / (r["ms_per_step"] / 1e3), 1),
                           "ms_per_step": round(r["ms_per_step"], 4),
                           "layer_hbm_gbs": round(r["bytes_per_step"] / (r["ms_per_step"] / 1e3) / 1e9, 1),
                           "avg_k": round(r["avg_k"], 3)})
+
+    # the same decode layer with FP8 (E4M3) expert weights, same batch size
+    fp8 = None
+    if args.config == "dsv2lite_decode" and not args.no_fp8:
+        del reps
+        dl = None
+        torch.cuda.empty_cache()
+        c8 = synth.CONFIGS["dsv2lite_decode_fp8"]
+        _, dl8, reps8, copies8 = setup(c8)
+        r = run_T(c8, dl8, reps8, T, args.steps, args.warmup, profile=True)
+        k8 = [k for k in r["kernels"] if k.startswith(DOMINANT)]
+        fp8 = {"workload": f"{c8.name}: expert weights OCP E4M3 with fp32 row scales, T={T}",
+               "tokens_per_s": round(T / (r["ms_per_step"] / 1e3), 1),
+               "ms_per_step": round(r["ms_per_step"], 4),
+               "speedup_vs_bf16": round(ms / r["ms_per_step"], 3),
+               "avg_k": round(r["avg_k"], 3),
+               "layer_hbm_gbs": round(r["bytes_per_step"] / (r["ms_per_step"] / 1e3) / 1e9, 1),
+               "weight_copies": copies8,
+               "kernels_mean_us": {k: round(v["mean_us"], 2) for k, v in r["kernels"].items()}}
+        if k8:
+            mu = r["kernels"][k8[0]]["mean_us"]
+            a8 = r["gate_up_alg_bytes"] / (mu * 1e-6) / 1e9
+            fp8["gate_up"] = {"kernel": k8[0], "mean_launch_us": round(mu, 2),
+                              "alg_bytes_per_launch": r["gate_up_alg_bytes"],
+                              "achieved_gbs": round(a8, 1), "frac": round(a8 / HBM_PEAK_GBS, 4)}
+        del reps8, dl8
+        torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu:
@@ -220,7 +257,8 @@ def main():
         "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
         "data": "synthetic (seeded; x~N(0,1), weights~N(0,1/D))",
         "config": {"workload": f"{cfg.name}: D={cfg.D} E={cfg.E} K={cfg.K} I={cfg.I} "
-                               f"shared={cfg.S}x{cfg.I_s} T={T}",
+                               f"shared={cfg.S}x{cfg.I_s} T={T}"
+                               + (" expert weights E4M3" if cfg.expert_format == synth.FP8 else ""),
                    "tokens": T, "weight_copies": copies, "input_pool": args.pool},
         "layer": {"avg_k": round(main_res["avg_k"], 3),
                   "active_experts": round(main_res["active_experts"], 2),
@@ -232,6 +270,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "sweep": sweep,
+        "fp8_weights": fp8,
     }
     print(json.dumps(out), flush=True)
 

@@ -19,7 +19,8 @@ int expert_tile_rows(const beam_moe_layer& L, int32_t T) {
   const long per_expert = (long(T) * L.K + L.E - 1) / L.E;
   if (per_expert <= 16) return 16;
   if (per_expert <= 32) return 32;
-  if (per_expert <= 96) return 64;
+  // FP8 weights only have the streaming kernels (tiles of up to 64 rows)
+  if (per_expert <= 96 || L.expert_format == BEAM_WEIGHTS_FP8_E4M3) return 64;
   if (per_expert < 512) return 128;
   return 256;
 }
@@ -143,6 +144,22 @@ static int check_layer(const beam_moe_layer* L) {
   if (L->D % 64 || L->I % 64 || L->D > 16384 || L->I > (1 << 20)) return BEAM_ERR_UNSUPPORTED;
   if (L->n_shared > 0 && (L->I_shared % 64 || long(L->n_shared) * L->I_shared > (1 << 20)))
     return BEAM_ERR_UNSUPPORTED;
+  if (L->expert_format != BEAM_WEIGHTS_DTYPE && L->expert_format != BEAM_WEIGHTS_FP8_E4M3)
+    return BEAM_ERR_INVALID_ARG;
+  if (L->expert_format == BEAM_WEIGHTS_FP8_E4M3) {
+    const float* sc[] = {L->scale_gate, L->scale_up, L->scale_down};
+    for (const float* p : sc)
+      if (!p || !aligned16(p)) return BEAM_ERR_INVALID_ARG;
+    if (L->n_shared > 0) {
+      const float* ss[] = {L->scale_shared_gate, L->scale_shared_up, L->scale_shared_down};
+      for (const float* p : ss)
+        if (!p || !aligned16(p)) return BEAM_ERR_INVALID_ARG;
+    }
+    // E4M3 weights go with bf16 activations; weight rows stream in 128-byte chunks
+    if (L->dtype != BEAM_BF16 || L->D % 128 || L->I % 128 ||
+        (L->n_shared > 0 && L->I_shared % 128))
+      return BEAM_ERR_UNSUPPORTED;
+  }
   return BEAM_OK;
 }
 
@@ -303,7 +320,11 @@ int beam_moe_stats_host(const beam_moe_layer* layer, const int32_t* counts, int3
   s.flops_shared = 6.0 * D * Is * S * T;
   s.flops_router = 4.0 * double(L.E) * D * T;
   s.flops_reduction = T > 0 ? 1.0 - s.flops_routed / s.flops_topk_routed : 0.0;
-  s.bytes_active_expert_weights = 3.0 * D * I * elt * act + 3.0 * D * Is * elt * S;
+  const bool fp8 = L.expert_format == BEAM_WEIGHTS_FP8_E4M3;
+  // bytes of one expert's three matrices (FP8: codes plus one fp32 per row)
+  const double per_routed = fp8 ? 3.0 * D * I + 4.0 * (2.0 * I + D) : 3.0 * D * I * elt;
+  const double per_shared = fp8 ? 3.0 * D * Is + 4.0 * (2.0 * Is + D) : 3.0 * D * Is * elt;
+  s.bytes_active_expert_weights = per_routed * act + per_shared * S;
   s.bytes_total_min = s.bytes_active_expert_weights + 2.0 * L.E * D * elt + 2.0 * double(T) * D * elt;
   *out = s;
   return BEAM_OK;

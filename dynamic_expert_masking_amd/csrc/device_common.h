@@ -10,6 +10,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // Load through the constant address space, for data that nothing writes
 // while the kernel runs (e.g. the routing plan, written by an earlier
@@ -41,6 +42,27 @@ __device__ __forceinline__ u32x4 ld16_stream(const void* p) {
 }
 
 __device__ __forceinline__ u32x4 zero16() { return u32x4{0u, 0u, 0u, 0u}; }
+
+// Eight OCP FP8 E4M3 codes (the bytes of w0 then w1, in memory order) widened
+// to eight bf16 values in the same order.  Every E4M3 value, subnormals
+// included, is exactly representable in bf16, so the conversion is exact
+// (scale operand 1.0: no exponent adjustment).
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
+  return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true))};
+}
+
+// Scales of 16 consecutive rows starting at p (wave-uniform, 16-byte
+// aligned), read with scalar loads; lane l receives those of rows
+// 4*(l/16) .. 4*(l/16)+3, the rows of its MFMA accumulator elements.
+__device__ __forceinline__ f32x4 row_scales16(const float* p, int lane) {
+  const f32x4* q = reinterpret_cast<const f32x4*>(p);
+  const f32x4 s0 = ld_const(q), s1 = ld_const(q + 1), s2 = ld_const(q + 2), s3 = ld_const(q + 3);
+  const int g = lane >> 4;
+  return g == 0 ? s0 : g == 1 ? s1 : g == 2 ? s2 : s3;
+}
 
 // D(16x16, fp32) += A(16x32, bf16) * B(32x16, bf16).
 // Operand lane layout (v_mfma_f32_16x16x32_bf16): lane l supplies row/column

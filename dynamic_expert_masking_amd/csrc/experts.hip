@@ -31,6 +31,13 @@ struct ExpertArgs {
   const void* sg;
   const void* su;
   const void* sd;
+  // FP8 E4M3 expert weights: float32 scale of each output row (else null)
+  const float* qg;    // [E][I]
+  const float* qu;    // [E][I]
+  const float* qd;    // [E][D]
+  const float* qsg;   // [S*Is] (the fused shared expert's intermediate rows)
+  const float* qsu;   // [S*Is]
+  const float* qsd;   // [S][D]
   int T, D, E, I, S, Is;
   const Plan* plan;
   const Tile* tiles;
@@ -106,10 +113,13 @@ __device__ __forceinline__ void down_item(long w, int ntr, int nts, int nb_all, 
 
 // Streaming (decode) gate/up: items are (tile, n-block of 16*NB intermediate
 // rows); the 2*NB streamed matrices are the gate and up rows of each 16-row
-// group, which share the token operand (see stream_engine.h).
-template <int MT, int NB>
+// group, which share the token operand (see stream_engine.h).  F8: the
+// weights are E4M3 codes with row scales.
+template <int MT, int NB, bool F8>
 struct GateUpStream {
   static constexpr int NMAT = 2 * NB;
+  static constexpr bool kMultiSeg = false;
+  static constexpr long EB = F8 ? 1 : 2;   // bytes per weight
   const ExpertArgs* a;
   int ntr, nts, nbr, nbs;
   long total;
@@ -119,13 +129,13 @@ struct GateUpStream {
     it.nseg = 1;
     it.w_seg = 0;
     it.x_seg = 0;
-    it.cps = a->D / 64;
-    it.w_row = a->D;
+    it.cps = a->D / chunk_k<F8>();
+    it.w_row = a->D * EB;
     if (!it.valid) {
       it.cps = 1;
       it.w_row = 0;
 #pragma unroll
-      for (int m = 0; m < NMAT; ++m) it.w[m] = (const u16*)a->wg;
+      for (int m = 0; m < NMAT; ++m) it.w[m] = (const unsigned char*)a->wg;
 #pragma unroll
       for (int b = 0; b < MT; ++b) it.x[b] = (const u16*)a->x;
       return;
@@ -134,11 +144,12 @@ struct GateUpStream {
     bool shared;
     work_item(item, ntr, nts, nbr, nbs, ti, nb, shared);
     const Tile tl = ld_tile(a->tiles + ti);
-    const u16* wg = shared ? (const u16*)a->sg : (const u16*)a->wg + size_t(tl.expert) * a->I * a->D;
-    const u16* wu = shared ? (const u16*)a->su : (const u16*)a->wu + size_t(tl.expert) * a->I * a->D;
+    const size_t eoff = shared ? 0 : size_t(tl.expert) * a->I * a->D * EB;
+    const unsigned char* wg = (const unsigned char*)(shared ? a->sg : a->wg) + eoff;
+    const unsigned char* wu = (const unsigned char*)(shared ? a->su : a->wu) + eoff;
 #pragma unroll
     for (int g = 0; g < NB; ++g) {
-      const size_t off = size_t(nb * NB + g) * 16 * a->D;
+      const size_t off = size_t(nb * NB + g) * 16 * a->D * EB;
       it.w[2 * g] = wg + off;
       it.w[2 * g + 1] = wu + off;
     }
@@ -159,6 +170,19 @@ struct GateUpStream {
       }
       if (r >= tl.rows) t = 0;   // absent rows read token 0
       it.x[b] = (const u16*)a->x + size_t(t) * a->D;
+    }
+  }
+  __device__ void scales(long item, int, int lane, f32x4 (&sc)[NMAT]) const {
+    int ti, nb;
+    bool shared;
+    work_item(item, ntr, nts, nbr, nbs, ti, nb, shared);
+    const Tile tl = ld_tile(a->tiles + ti);
+    const size_t base = shared ? 0 : size_t(tl.expert) * a->I;
+#pragma unroll
+    for (int g = 0; g < NB; ++g) {
+      const size_t n0 = base + size_t(nb * NB + g) * 16;
+      sc[2 * g] = row_scales16((shared ? a->qsg : a->qg) + n0, lane);
+      sc[2 * g + 1] = row_scales16((shared ? a->qsu : a->qu) + n0, lane);
     }
   }
   __device__ void epilogue(long item, const f32x4 (&acc)[NMAT][MT], int lane) const {
@@ -188,25 +212,27 @@ struct GateUpStream {
   }
 };
 
-template <int MT, int NB, int U, int KSPLIT>
+template <int MT, int NB, int U, int KSPLIT, bool F8>
 __global__ __launch_bounds__(kStreamWaves * 64) void k_gate_up_stream(ExpertArgs a) {
   constexpr int NMAT = 2 * NB;
   __shared__ __align__(16) unsigned char lds[StreamLds<NMAT, MT, U, KSPLIT>::kBytes];
-  GateUpStream<MT, NB> pb;
+  GateUpStream<MT, NB, F8> pb;
   pb.a = &a;
   pb.ntr = ld_const(&a.plan->n_tiles_routed);
   pb.nts = ld_const(&a.plan->n_tiles_shared);
   pb.nbr = a.I / (16 * NB);
   pb.nbs = a.S > 0 ? (a.S * a.Is) / (16 * NB) : 1;
   pb.total = long(pb.ntr) * pb.nbr + long(pb.nts) * pb.nbs;
-  stream_run<NMAT, MT, U, KSPLIT>(pb, lds);
+  stream_run<NMAT, MT, U, KSPLIT, F8>(pb, lds);
 }
 
 // Streaming (decode) down: items are (tile, d-block of 16*NB output rows),
 // the NB 16-row groups streamed as NB matrices that share the h operand; the
 // fused shared expert has one k segment per shared expert.
-template <int MT, int NB>
+template <int MT, int NB, bool F8>
 struct DownStream {
+  static constexpr bool kMultiSeg = true;
+  static constexpr long EB = F8 ? 1 : 2;   // bytes per weight
   const ExpertArgs* a;
   int ntr, nts, nb_all;
   long total;
@@ -217,7 +243,7 @@ struct DownStream {
       it.nseg = 1;
       it.cps = 1;
 #pragma unroll
-      for (int g = 0; g < NB; ++g) it.w[g] = (const u16*)a->wd;
+      for (int g = 0; g < NB; ++g) it.w[g] = (const unsigned char*)a->wd;
       it.w_row = it.w_seg = it.x_seg = 0;
 #pragma unroll
       for (int b = 0; b < MT; ++b) it.x[b] = (const u16*)a->h;
@@ -228,19 +254,19 @@ struct DownStream {
     const bool shared = ti >= ntr;
     const Tile tl = ld_tile(a->tiles + ti);
     const int d0 = nb * 16 * NB;
-    const u16* w0;
+    const unsigned char* w0;
     if (shared) {
       it.nseg = a->S;
-      it.cps = a->Is / 64;
-      w0 = (const u16*)a->sd + size_t(d0) * a->Is;
-      it.w_row = a->Is;
-      it.w_seg = long(a->D) * a->Is;
+      it.cps = a->Is / chunk_k<F8>();
+      w0 = (const unsigned char*)a->sd + size_t(d0) * a->Is * EB;
+      it.w_row = a->Is * EB;
+      it.w_seg = long(a->D) * a->Is * EB;
       it.x_seg = a->Is;
     } else {
       it.nseg = 1;
-      it.cps = a->I / 64;
-      w0 = (const u16*)a->wd + size_t(tl.expert) * a->D * a->I + size_t(d0) * a->I;
-      it.w_row = a->I;
+      it.cps = a->I / chunk_k<F8>();
+      w0 = (const unsigned char*)a->wd + (size_t(tl.expert) * a->D + d0) * a->I * EB;
+      it.w_row = a->I * EB;
       it.w_seg = 0;
       it.x_seg = 0;
     }
@@ -254,6 +280,15 @@ struct DownStream {
       // absent rows read the tile's first row
       it.x[b] = hb + size_t(tl.row0 + (r < tl.rows ? r : 0)) * hs;
     }
+  }
+  __device__ void scales(long item, int seg, int lane, f32x4 (&sc)[NB]) const {
+    int ti, nb;
+    down_item(item, ntr, nts, nb_all, ti, nb);
+    const bool shared = ti >= ntr;
+    const float* q = shared ? a->qsd + size_t(seg) * a->D
+                            : a->qd + size_t(ld_tile(a->tiles + ti).expert) * a->D;
+#pragma unroll
+    for (int g = 0; g < NB; ++g) sc[g] = row_scales16(q + (nb * NB + g) * 16, lane);
   }
   __device__ void epilogue(long item, const f32x4 (&acc)[NB][MT], int lane) const {
     int ti, nb;
@@ -276,16 +311,16 @@ struct DownStream {
   }
 };
 
-template <int MT, int NB, int U, int KSPLIT>
+template <int MT, int NB, int U, int KSPLIT, bool F8>
 __global__ __launch_bounds__(kStreamWaves * 64) void k_down_stream(ExpertArgs a) {
   __shared__ __align__(16) unsigned char lds[StreamLds<NB, MT, U, KSPLIT>::kBytes];
-  DownStream<MT, NB> pb;
+  DownStream<MT, NB, F8> pb;
   pb.a = &a;
   pb.ntr = ld_const(&a.plan->n_tiles_routed);
   pb.nts = ld_const(&a.plan->n_tiles_shared);
   pb.nb_all = a.D / (16 * NB);
   pb.total = long(pb.ntr + pb.nts) * pb.nb_all;
-  stream_run<NB, MT, U, KSPLIT>(pb, lds);
+  stream_run<NB, MT, U, KSPLIT, F8>(pb, lds);
 }
 
 // Tiled (prefill): the BN weight rows of an n-block are BN/2 intermediate
@@ -573,6 +608,12 @@ static ExpertArgs expert_args(const beam_moe_layer& L, const void* x, int32_t T,
   a.sg = L.ws_gate;
   a.su = L.ws_up;
   a.sd = L.ws_down;
+  a.qg = L.scale_gate;
+  a.qu = L.scale_up;
+  a.qd = L.scale_down;
+  a.qsg = L.scale_shared_gate;
+  a.qsu = L.scale_shared_up;
+  a.qsd = L.scale_shared_down;
   a.T = T;
   a.D = L.D;
   a.E = L.E;
@@ -633,30 +674,64 @@ static unsigned persistent_grid(long items, long cap) {
 }
 
 // Launches the streaming gate/up variant <MT token blocks, NB row groups,
-// U-chunk stages> with k split ks.
-template <int MT, int NB, int U>
+// U-chunk stages, FP8 weights?> with k split ks.
+template <int MT, int NB, int U, bool F8>
 static void gate_up_stream(const ExpertArgs& a, long ntr, long nts, int I, int Is_all, int ks,
                            hipStream_t s) {
   const long items = ntr * (I / (16 * NB)) + nts * (Is_all / (16 * NB));
   const dim3 blk(kStreamWaves * 64);
 #define BEAM_GU(KS_)                                                                       \
-  hipLaunchKernelGGL((k_gate_up_stream<MT, NB, U, KS_>),                                   \
-                     dim3(stream_grid((const void*)&k_gate_up_stream<MT, NB, U, KS_>, items, KS_)), \
+  hipLaunchKernelGGL((k_gate_up_stream<MT, NB, U, KS_, F8>),                               \
+                     dim3(stream_grid((const void*)&k_gate_up_stream<MT, NB, U, KS_, F8>, items, KS_)), \
                      blk, 0, s, a)
   if (ks == 1) BEAM_GU(1); else if (ks == 2) BEAM_GU(2); else BEAM_GU(4);
 #undef BEAM_GU
 }
 
-template <int MT, int NB, int U>
+template <int MT, int NB, int U, bool F8>
 static void down_stream(const ExpertArgs& a, long tiles, int D, int ks, hipStream_t s) {
   const long items = tiles * (D / (16 * NB));
   const dim3 blk(kStreamWaves * 64);
 #define BEAM_DN(KS_)                                                                       \
-  hipLaunchKernelGGL((k_down_stream<MT, NB, U, KS_>),                                      \
-                     dim3(stream_grid((const void*)&k_down_stream<MT, NB, U, KS_>, items, KS_)), \
+  hipLaunchKernelGGL((k_down_stream<MT, NB, U, KS_, F8>),                                  \
+                     dim3(stream_grid((const void*)&k_down_stream<MT, NB, U, KS_, F8>, items, KS_)), \
                      blk, 0, s, a)
   if (ks == 1) BEAM_DN(1); else if (ks == 2) BEAM_DN(2); else BEAM_DN(4);
 #undef BEAM_DN
+}
+
+// Streaming launches for tiles of 16, 32 or 64 rows.  Weight chunks are 128
+// bytes of a row in both formats, so the k split follows the chunk count.
+template <bool F8>
+static void gate_up_streaming(const beam_moe_layer& L, const ExpertArgs& a, long ntr, long nts,
+                              int tile_rows, hipStream_t s) {
+  const int Is_all = L.n_shared ? L.n_shared * L.I_shared : 0;
+  const int chunks = L.D / chunk_k<F8>();
+  if (tile_rows == 16) {
+    const int ks = stream_ksplit_chunks(chunks);
+    const long items2 = ntr * (L.I / 32) + nts * (Is_all / 32);
+    if (items2 * ks >= kWideShares) gate_up_stream<1, 2, 1, F8>(a, ntr, nts, L.I, Is_all, ks, s);
+    else gate_up_stream<1, 1, 1, F8>(a, ntr, nts, L.I, Is_all, ks, s);
+  } else if (tile_rows == 32) {
+    gate_up_stream<2, 2, 1, F8>(a, ntr, nts, L.I, Is_all, chunks >= 64 ? 4 : 2, s);
+  } else {
+    gate_up_stream<4, 2, 1, F8>(a, ntr, nts, L.I, Is_all, chunks >= 64 ? 4 : 1, s);
+  }
+}
+
+template <bool F8>
+static void down_streaming(const beam_moe_layer& L, const ExpertArgs& a, long tiles,
+                           int tile_rows, hipStream_t s) {
+  const int chunks = L.I / chunk_k<F8>();
+  if (tile_rows == 16) {
+    const int ks = stream_ksplit_chunks(chunks);
+    if (tiles * (L.D / 32) * ks >= kWideShares) down_stream<1, 2, 1, F8>(a, tiles, L.D, ks, s);
+    else down_stream<1, 1, 2, F8>(a, tiles, L.D, ks, s);
+  } else if (tile_rows == 32) {
+    down_stream<2, 2, 1, F8>(a, tiles, L.D, 2, s);
+  } else {
+    down_stream<4, 2, 1, F8>(a, tiles, L.D, chunks >= 16 ? 2 : 1, s);
+  }
 }
 
 hipError_t launch_gate_up(const beam_moe_layer& L, const void* x, int32_t T, int tile_rows,
@@ -671,19 +746,13 @@ hipError_t launch_gate_up(const beam_moe_layer& L, const void* x, int32_t T, int
     prof_after(s);
     return hipGetLastError();
   }
-  if (tile_rows <= 64) {
-    const int Is_all = L.n_shared ? L.n_shared * L.I_shared : 0;
+  if (L.expert_format == BEAM_WEIGHTS_FP8_E4M3) {   // tiles of at most 64 rows
+    prof_before("gate_up_swiglu_stream_fp8", s);
+    gate_up_streaming<true>(L, a, ntr, nts, tile_rows, s);
+    prof_after(s);
+  } else if (tile_rows <= 64) {
     prof_before("gate_up_swiglu_stream", s);
-    if (tile_rows == 16) {
-      const int ks = stream_ksplit_chunks(L.D / 64);
-      const long items2 = ntr * (L.I / 32) + nts * (Is_all / 32);
-      if (items2 * ks >= kWideShares) gate_up_stream<1, 2, 1>(a, ntr, nts, L.I, Is_all, ks, s);
-      else gate_up_stream<1, 1, 1>(a, ntr, nts, L.I, Is_all, ks, s);
-    }
-    else if (tile_rows == 32)
-      gate_up_stream<2, 2, 1>(a, ntr, nts, L.I, Is_all, L.D >= 4096 ? 4 : 2, s);
-    else
-      gate_up_stream<4, 2, 1>(a, ntr, nts, L.I, Is_all, L.D >= 4096 ? 4 : 1, s);
+    gate_up_streaming<false>(L, a, ntr, nts, tile_rows, s);
     prof_after(s);
   } else {
     const int ib = tile_rows == 256 ? 64 : 128;   // intermediate rows per tile
@@ -713,17 +782,13 @@ hipError_t launch_down(const beam_moe_layer& L, int32_t T, int tile_rows, const 
     prof_after(s);
     return hipGetLastError();
   }
-  if (tile_rows <= 64) {
+  if (L.expert_format == BEAM_WEIGHTS_FP8_E4M3) {   // tiles of at most 64 rows
+    prof_before("down_stream_fp8", s);
+    down_streaming<true>(L, a, ntr + nts, tile_rows, s);
+    prof_after(s);
+  } else if (tile_rows <= 64) {
     prof_before("down_stream", s);
-    if (tile_rows == 16) {
-      const int ks = stream_ksplit_chunks(L.I / 64);
-      if ((ntr + nts) * (L.D / 32) * ks >= kWideShares) down_stream<1, 2, 1>(a, ntr + nts, L.D, ks, s);
-      else down_stream<1, 1, 2>(a, ntr + nts, L.D, ks, s);
-    }
-    else if (tile_rows == 32)
-      down_stream<2, 2, 1>(a, ntr + nts, L.D, 2, s);
-    else
-      down_stream<4, 2, 1>(a, ntr + nts, L.D, L.I >= 1024 ? 2 : 1, s);
+    down_streaming<false>(L, a, ntr + nts, tile_rows, s);
     prof_after(s);
   } else {
     const int bn = tile_rows == 256 ? 128 : 256;

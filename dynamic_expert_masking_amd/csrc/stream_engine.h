@@ -7,40 +7,55 @@
 // share an item and split its k chunks (KSPLIT = 1: every wave streams whole
 // items on its own).
 //
-// Memory access: weights are read with coalesced, non-temporal 16-byte loads
-// in which 8 consecutive lanes cover one 128-byte line of a row, so every load
-// instruction touches 8 whole lines (2 instructions per 16 rows x 64 k chunk).
-// A wave-private LDS tile then turns each chunk into the MFMA operand layout
-// (lane l: row l % 16, k = 8*(l/16) .. +7 and 32 + 8*(l/16) .. +7).  Token
-// rows are small and cache-resident and are loaded straight in operand layout.
-// Stages of U chunks are double-buffered in registers, so the next stage's
-// loads are in flight while the current one is multiplied; the next item's
-// first stage is issued before the current item's epilogue.
+// Memory access: weights are read in chunks of 128 bytes of each of the 16
+// rows (64 k values of bf16, or 128 of FP8 E4M3), with coalesced,
+// non-temporal 16-byte loads in which 8 consecutive lanes cover one 128-byte
+// line of a row, so every load instruction touches 8 whole lines (2
+// instructions per chunk).  A wave-private LDS tile then turns each chunk
+// into the MFMA operand layout (lane l: row l % 16 and 8 consecutive k
+// values).  FP8 codes are widened to bf16 in registers first, exactly, and
+// go through the tile in two halves.  Token rows are small and cache-resident
+// and are loaded straight in operand layout.  Stages of U chunks are
+// double-buffered in registers, so the next stage's loads are in flight while
+// the current one is multiplied; the next item's first stage is issued before
+// the current item's epilogue.
+//
+// FP8 weights carry one float32 scale per row: products are accumulated
+// unscaled and multiplied by the row scales at the end of each k segment
+// (segments are separate matrices, e.g. the fused shared experts' down
+// projections, each with its own scales).
 #pragma once
 #include "device_common.h"
 
 namespace beam {
 
 constexpr int kStreamWaves = 4;
-constexpr int kLdsRow = 72;   // 64 k values + 8 pad (bf16) per LDS tile row
+constexpr int kLdsRow = 72;   // 64 bf16 values + 8 pad per LDS tile row
+
+// k values per 128-byte chunk of a weight row.
+template <bool F8>
+constexpr int chunk_k() { return F8 ? 128 : 64; }
 
 // Per-item operand addresses, filled by the problem's decode().
 template <int NMAT, int MT>
 struct StreamItem {
-  const u16* w[NMAT];    // first element (k = 0, segment 0) of row 0 of the block
-  long w_row;            // elements between consecutive weight rows
-  long w_seg;            // elements between segments
+  const unsigned char* w[NMAT];  // first byte (k = 0, segment 0) of row 0 of the block
+  long w_row;            // bytes between consecutive weight rows
+  long w_seg;            // bytes between segments
   const u16* x[MT];      // this lane's token row (row lane%16 of M tile mt) at k = 0;
                          // absent rows point at a safe dummy row
   long x_seg;            // elements between segments of a token row
-  int nseg, cps;         // segments, 64-wide chunks per segment
+  int nseg, cps;         // segments, 128-byte chunks per segment row
   bool valid;            // false: no item; pointers are safe dummies (w_row = w_seg = 0)
 };
 
-template <int NMAT, int MT, int U>
+// Token operands per chunk and M tile: bf16 chunks hold two MFMA k-steps,
+// FP8 chunks four.
+template <int NMAT, int MT, int U, bool F8>
 struct StreamStage {
+  static constexpr int kX = chunk_k<F8>() / 32;
   u32x4 w[U][NMAT][2];
-  u32x4 x[U][MT][2];
+  u32x4 x[U][MT][kX];
 };
 
 // Issues the loads of chunks c_begin .. c_begin+U-1 of an item.  Every call
@@ -49,13 +64,20 @@ struct StreamStage {
 // compiler can count outstanding loads exactly and wait only for the stage it
 // consumes.  consume() skips chunks past c_end and absent items, and an absent
 // token row only feeds MFMA output columns that are never stored.
-template <int NMAT, int MT, int U>
-__device__ __forceinline__ void stream_issue(StreamStage<NMAT, MT, U>& st,
+//
+// k order inside a chunk (applied to weights and tokens alike, which leaves
+// the products unchanged): bf16 k-step q of lane group s = lane/16 covers
+// k = 32q + 8s .. +7; FP8 steps 0..3 cover k = 16s, 64 + 16s, 16s + 8 and
+// 64 + 16s + 8 (.. +7), the order in which the widened halves come out of
+// the LDS tile.
+template <int NMAT, int MT, int U, bool F8>
+__device__ __forceinline__ void stream_issue(StreamStage<NMAT, MT, U, F8>& st,
                                              const StreamItem<NMAT, MT>& it, int c_begin,
                                              int c_end, int lane) {
+  constexpr int KC = chunk_k<F8>();
   const int wr = lane >> 3;            // coalesced: rows wr and wr + 8
-  const int wc = (lane & 7) * 8;       // column (elements) within the chunk
-  const int xk = (lane >> 4) * 8;      // operand layout k offset
+  const int wb = (lane & 7) * 16;      // byte column within the chunk
+  const int xk = (lane >> 4) * (F8 ? 16 : 8);   // operand layout k offset
   const int c_last = max(c_end - 1, 0);
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -64,15 +86,22 @@ __device__ __forceinline__ void stream_issue(StreamStage<NMAT, MT, U>& st,
     const int j = c - seg * it.cps;
 #pragma unroll
     for (int m = 0; m < NMAT; ++m) {
-      const u16* p = it.w[m] + seg * it.w_seg + long(wr) * it.w_row + j * 64 + wc;
+      const unsigned char* p = it.w[m] + seg * it.w_seg + long(wr) * it.w_row + j * 128 + wb;
       st.w[u][m][0] = ld16_stream(p);
       st.w[u][m][1] = ld16_stream(p + 8 * it.w_row);
     }
 #pragma unroll
     for (int b = 0; b < MT; ++b) {
-      const u16* q = it.x[b] + seg * it.x_seg + j * 64 + xk;
-      st.x[u][b][0] = ld16(q);
-      st.x[u][b][1] = ld16(q + 32);
+      const u16* q = it.x[b] + seg * it.x_seg + j * KC + xk;
+      if constexpr (F8) {
+        st.x[u][b][0] = ld16(q);
+        st.x[u][b][1] = ld16(q + 64);
+        st.x[u][b][2] = ld16(q + 8);
+        st.x[u][b][3] = ld16(q + 72);
+      } else {
+        st.x[u][b][0] = ld16(q);
+        st.x[u][b][1] = ld16(q + 32);
+      }
     }
   }
 }
@@ -83,7 +112,7 @@ __device__ __forceinline__ void stream_issue(StreamStage<NMAT, MT, U>& st,
 // partial sums of the wave are exchanged through the same region once the
 // wave has consumed its share (a wave's LDS accesses complete in order).
 template <int NMAT, int MT, int U, int KSPLIT>
-struct StreamLds {
+struct StreamLds {   // (the same for bf16 and FP8 weights)
   static constexpr int kBufs = U > 1 ? 2 : 1;
   static constexpr int kTileBytes = kBufs * NMAT * 16 * kLdsRow * 2;
   static constexpr int kRedBytes = KSPLIT > 1 ? NMAT * MT * kWave * 16 : 0;
@@ -93,36 +122,48 @@ struct StreamLds {
 };
 
 // lds: this wave's transpose tiles (alternating per chunk when U > 1).
-template <int NMAT, int MT, int U>
-__device__ __forceinline__ void stream_consume(const StreamStage<NMAT, MT, U>& st, bool valid,
+// chunk_end(c) runs after the MFMAs of chunk c (FP8 segment scaling).
+template <int NMAT, int MT, int U, bool F8, class CE>
+__device__ __forceinline__ void stream_consume(const StreamStage<NMAT, MT, U, F8>& st, bool valid,
                                                int c_begin, int c_end, u16* lds, int lane,
-                                               f32x4 (&acc)[NMAT][MT]) {
+                                               f32x4 (&acc)[NMAT][MT], CE&& chunk_end) {
   const int wr = lane >> 3, wc = (lane & 7) * 8;
   const int fr = lane & 15, fk = (lane >> 4) * 8;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     if (!valid || c_begin + u >= c_end) continue;
     u16* buf = lds + (U > 1 ? (u & 1) : 0) * NMAT * 16 * kLdsRow;
-    u32x4 f[NMAT][2];
+    constexpr int NH = F8 ? 2 : 1;   // FP8: the low then the high 8 codes of each load
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m) {
-      u16* t = buf + m * 16 * kLdsRow;
-      *reinterpret_cast<u32x4*>(t + wr * kLdsRow + wc) = st.w[u][m][0];
-      *reinterpret_cast<u32x4*>(t + (wr + 8) * kLdsRow + wc) = st.w[u][m][1];
-    }
+    for (int hf = 0; hf < NH; ++hf) {
+      u32x4 f[NMAT][2];
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m) {
-      const u16* t = buf + m * 16 * kLdsRow;
-      f[m][0] = *reinterpret_cast<const u32x4*>(t + fr * kLdsRow + fk);
-      f[m][1] = *reinterpret_cast<const u32x4*>(t + fr * kLdsRow + 32 + fk);
-    }
-#pragma unroll
-    for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-      for (int b = 0; b < MT; ++b) {
-        acc[m][b] = mfma_bf16(f[m][0], st.x[u][b][0], acc[m][b]);
-        acc[m][b] = mfma_bf16(f[m][1], st.x[u][b][1], acc[m][b]);
+      for (int m = 0; m < NMAT; ++m) {
+        u16* t = buf + m * 16 * kLdsRow;
+        u32x4 v0 = st.w[u][m][0], v1 = st.w[u][m][1];
+        if constexpr (F8) {
+          v0 = hf == 0 ? e4m3x8_to_bf16(v0[0], v0[1]) : e4m3x8_to_bf16(v0[2], v0[3]);
+          v1 = hf == 0 ? e4m3x8_to_bf16(v1[0], v1[1]) : e4m3x8_to_bf16(v1[2], v1[3]);
+        }
+        *reinterpret_cast<u32x4*>(t + wr * kLdsRow + wc) = v0;
+        *reinterpret_cast<u32x4*>(t + (wr + 8) * kLdsRow + wc) = v1;
       }
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) {
+        const u16* t = buf + m * 16 * kLdsRow;
+        f[m][0] = *reinterpret_cast<const u32x4*>(t + fr * kLdsRow + fk);
+        f[m][1] = *reinterpret_cast<const u32x4*>(t + fr * kLdsRow + 32 + fk);
+      }
+      // bf16: x steps 0, 1; FP8 half 0: steps 0, 1 (k 16s, 64 + 16s), half 1: 2, 3
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int b = 0; b < MT; ++b) {
+          acc[m][b] = mfma_bf16(f[m][0], st.x[u][b][2 * hf], acc[m][b]);
+          acc[m][b] = mfma_bf16(f[m][1], st.x[u][b][2 * hf + 1], acc[m][b]);
+        }
+    }
+    chunk_end(c_begin + u);
   }
 }
 
@@ -130,11 +171,17 @@ __device__ __forceinline__ void stream_consume(const StreamStage<NMAT, MT, U>& s
 //   long total_items() const
 //   void decode(long item, int lane, StreamItem<NMAT, MT>& it)   (sets it.valid)
 //   void epilogue(long item, const f32x4 (&acc)[NMAT][MT], int lane)
-// acc[m][b][i] = sum_k W_m[row 4*(lane/16)+i][k] * X[row 16*b + lane%16][k].
+// and, for FP8 weights (F8 = true):
+//   void scales(long item, int seg, int lane, f32x4 (&sc)[NMAT])
+//     (scales of this lane's accumulator rows of each matrix in segment seg)
+//   static constexpr bool kMultiSeg   (items may have several segments)
+// acc[m][b][i] = sum_k W_m[row 4*(lane/16)+i][k] * X[row 16*b + lane%16][k],
+// with W_m the scaled weights for FP8.
 // lds_all: StreamLds<NMAT, MT, U, KSPLIT>::kBytes bytes, 16-byte aligned.
-template <int NMAT, int MT, int U, int KSPLIT, class P>
+template <int NMAT, int MT, int U, int KSPLIT, bool F8, class P>
 __device__ __forceinline__ void stream_run(P& prob, unsigned char* lds_all) {
   using Lds = StreamLds<NMAT, MT, U, KSPLIT>;
+  using Stage = StreamStage<NMAT, MT, U, F8>;
   constexpr int GROUPS = kStreamWaves / KSPLIT;
   const int lane = threadIdx.x & 63;
   // wave-uniform, and known to be so: item decoding then stays scalar
@@ -167,19 +214,45 @@ __device__ __forceinline__ void stream_run(P& prob, unsigned char* lds_all) {
   prob.decode(item, lane, cur);
   int cb, ce;
   share(cur, cb, ce);
-  StreamStage<NMAT, MT, U> A, B;
-  stream_issue<NMAT, MT, U>(A, cur, cb, ce, lane);
+  Stage A, B;
+  stream_issue<NMAT, MT, U, F8>(A, cur, cb, ce, lane);
 
   for (long r = 0; r < rounds; ++r) {
     const long nitem = item_of((r + 1) * GROUPS + group);
     prob.decode(nitem, lane, nxt);
     int nb, ne;
     share(nxt, nb, ne);
-    f32x4 acc[NMAT][MT];
+    f32x4 acc[NMAT][MT], tot[NMAT][MT];
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-      for (int b = 0; b < MT; ++b) acc[m][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int b = 0; b < MT; ++b) acc[m][b] = tot[m][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // FP8: at the end of each segment (or of the share), tot += scales * acc;
+    // single-segment items scale acc in place at the end of the share
+    auto chunk_end = [&](int c) {
+      if constexpr (F8) {
+        if constexpr (P::kMultiSeg) {
+          if ((c + 1) % cur.cps == 0 || c + 1 == ce) {
+            f32x4 sc[NMAT];
+            prob.scales(item, c / cur.cps, lane, sc);
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+              for (int b = 0; b < MT; ++b) {
+                tot[m][b] += sc[m] * acc[m][b];
+                acc[m][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+              }
+          }
+        } else if (c + 1 == ce) {
+          f32x4 sc[NMAT];
+          prob.scales(item, 0, lane, sc);
+#pragma unroll
+          for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+            for (int b = 0; b < MT; ++b) acc[m][b] *= sc[m];
+        }
+      }
+    };
     // stages of this round: c = cb, cb + U, ...; A holds the first.  Pairs
     // (A, B) keep buffer roles static.  The next round's first stage is issued
     // as soon as this round's last stage is in flight; it lands in A, or in B
@@ -189,20 +262,26 @@ __device__ __forceinline__ void stream_run(P& prob, unsigned char* lds_all) {
     for (int c = cb; c < ce; c += 2 * U) {
       const int c2 = c + U;
       if (c2 < ce) {
-        stream_issue<NMAT, MT, U>(B, cur, c2, ce, lane);
+        stream_issue<NMAT, MT, U, F8>(B, cur, c2, ce, lane);
       } else {
-        stream_issue<NMAT, MT, U>(B, nxt, nb, ne, lane);
+        stream_issue<NMAT, MT, U, F8>(B, nxt, nb, ne, lane);
         next_in_b = true;
       }
-      stream_consume<NMAT, MT, U>(A, cur.valid, c, ce, lds, lane, acc);
+      stream_consume<NMAT, MT, U, F8>(A, cur.valid, c, ce, lds, lane, acc, chunk_end);
       if (c2 < ce) {
         const int c3 = c2 + U;
-        if (c3 < ce) stream_issue<NMAT, MT, U>(A, cur, c3, ce, lane);
-        else stream_issue<NMAT, MT, U>(A, nxt, nb, ne, lane);
-        stream_consume<NMAT, MT, U>(B, cur.valid, c2, ce, lds, lane, acc);
+        if (c3 < ce) stream_issue<NMAT, MT, U, F8>(A, cur, c3, ce, lane);
+        else stream_issue<NMAT, MT, U, F8>(A, nxt, nb, ne, lane);
+        stream_consume<NMAT, MT, U, F8>(B, cur.valid, c2, ce, lds, lane, acc, chunk_end);
       }
     }
-    if (ce <= cb) stream_issue<NMAT, MT, U>(A, nxt, nb, ne, lane);   // empty share
+    if (ce <= cb) stream_issue<NMAT, MT, U, F8>(A, nxt, nb, ne, lane);   // empty share
+    if constexpr (F8 && P::kMultiSeg) {
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int b = 0; b < MT; ++b) acc[m][b] = tot[m][b];
+    }
     // combine the group's partial sums (fixed wave order) and finish the item
     if (KSPLIT > 1) {
       f32x4* mine = red(wave);

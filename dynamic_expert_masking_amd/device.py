@@ -9,15 +9,21 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import BEAM_BF16, BEAM_F32, beam_moe_workspace_size, make_layer, make_route_out
+from . import (BEAM_BF16, BEAM_F32, WEIGHTS_DTYPE, WEIGHTS_FP8_E4M3, beam_moe_workspace_size,
+               make_layer, make_route_out)
+
+SCALES = ("s_gate", "s_up", "s_down", "ss_gate", "ss_up", "ss_down")
 
 
 def to_device(a: np.ndarray, device="cuda") -> torch.Tensor:
-    """Upload a host array: uint16 -> torch.bfloat16 (same bits), float32 -> float32."""
+    """Upload a host array: uint16 -> torch.bfloat16 (same bits), float32 ->
+    float32, uint8 (E4M3 codes) -> torch.uint8."""
     a = np.ascontiguousarray(a)
     if a.dtype == np.uint16:
         return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
     if a.dtype == np.float32:
+        return torch.from_numpy(a).to(device)
+    if a.dtype == np.uint8:
         return torch.from_numpy(a).to(device)
     raise TypeError(f"unsupported host dtype {a.dtype}")
 
@@ -34,8 +40,10 @@ class DeviceLayer:
     """Device copy of a layer's parameters plus its C descriptor.
 
     `host` is any object with the attributes of the parameter set: cfg (with
-    D, E, K, I, S, I_s, dtype), w_router, w_mask, b_router, b_mask, w_gate,
-    w_up, w_down, ws_gate, ws_up, ws_down.
+    D, E, K, I, S, I_s, dtype and optionally gating, expert_format), w_router,
+    w_mask, b_router, b_mask, w_gate, w_up, w_down, ws_gate, ws_up, ws_down,
+    and for FP8 expert weights the row scales s_gate, s_up, s_down, ss_gate,
+    ss_up, ss_down.
     """
 
     def __init__(self, host, device="cuda"):
@@ -47,6 +55,9 @@ class DeviceLayer:
                   ("w_router", "w_mask", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")}
         self.t["b_router"] = up(host.b_router)
         self.t["b_mask"] = up(host.b_mask)
+        self.fp8 = getattr(c, "expert_format", "") == "fp8"
+        for name in SCALES:
+            self.t[name] = up(getattr(host, name, None)) if self.fp8 else None
         self.dtype_code = BEAM_F32 if c.dtype == "f32" else BEAM_BF16
         self.torch_dtype = torch.float32 if c.dtype == "f32" else torch.bfloat16
         self.desc = self._desc(self.t)
@@ -57,7 +68,11 @@ class DeviceLayer:
                           t["w_gate"], t["w_up"], t["w_down"], b_router=t["b_router"],
                           b_mask=t["b_mask"], n_shared=c.S, I_shared=c.I_s if c.S else 0,
                           ws_gate=t["ws_gate"], ws_up=t["ws_up"], ws_down=t["ws_down"],
-                          gating=getattr(c, "gating", 0))
+                          gating=getattr(c, "gating", 0),
+                          expert_format=WEIGHTS_FP8_E4M3 if self.fp8 else WEIGHTS_DTYPE,
+                          scale_gate=t["s_gate"], scale_up=t["s_up"], scale_down=t["s_down"],
+                          scale_shared_gate=t["ss_gate"], scale_shared_up=t["ss_up"],
+                          scale_shared_down=t["ss_down"])
 
     def replicas(self, n: int):
         """n extra copies of the expert weights at distinct addresses (same

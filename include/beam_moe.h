@@ -62,10 +62,34 @@ typedef enum { BEAM_F32 = 0, BEAM_BF16 = 1 } beam_dtype;
  * The top-K set, its order and the mask bits do not depend on these bits. */
 typedef enum { BEAM_GATE_SOFTMAX_ALL = 1, BEAM_GATE_RENORM = 2 } beam_gate_flag;
 
+/* Storage of the routed and shared expert weights (beam_moe_layer.
+ * expert_format).  The masking combines with weight quantisation (the
+ * ai-feeds.com summary, section on interfaces with existing products and
+ * workflows, item 3):
+ *   BEAM_WEIGHTS_DTYPE      every expert weight has the layer dtype.
+ *   BEAM_WEIGHTS_FP8_E4M3   w_gate, w_up, w_down, ws_gate, ws_up, ws_down
+ *                           hold OCP FP8 E4M3 codes (one byte per weight,
+ *                           same shapes), and the weight in row r of a
+ *                           matrix is e4m3(code) * scale[r], with one fp32
+ *                           scale per output row: [E][I] for w_gate and
+ *                           w_up, [E][D] for w_down, [n_shared][I_shared]
+ *                           and [n_shared][D] for the shared experts.
+ *                           Requires dtype BEAM_BF16 (x, y and the router
+ *                           weights stay bf16) and D, I, I_shared multiples
+ *                           of 128; every scale pointer in use must be
+ *                           non-NULL and 16-byte aligned.  Products run in
+ *                           bf16 MFMA on the exactly widened codes with fp32
+ *                           accumulation; the scales multiply the fp32 sums.
+ *                           Meant for decode: every batch runs the streaming
+ *                           kernels with tiles of at most 64 token rows. */
+typedef enum { BEAM_WEIGHTS_DTYPE = 0, BEAM_WEIGHTS_FP8_E4M3 = 1 } beam_weight_format;
+
 /* Layer description.  Shapes: D hidden, E routed experts, K top-K, I routed
  * expert intermediate size, n_shared shared experts of intermediate size
  * I_shared.  Supported: 1 <= K <= min(E, 32), E <= 1024, D, I and I_shared
- * multiples of 64, D <= 16384.  Every weight tensor has the layer's dtype.  */
+ * multiples of 64, D <= 16384.  Every weight tensor has the layer's dtype,
+ * except the expert weights when expert_format is BEAM_WEIGHTS_FP8_E4M3.
+ * Fields past `gating` may be left zero (= BEAM_WEIGHTS_DTYPE, no scales). */
 typedef struct {
   int32_t D, E, K, I, n_shared, I_shared;
   int32_t dtype;               /* beam_dtype                                  */
@@ -81,6 +105,14 @@ typedef struct {
   const void *ws_down;         /* [n_shared][D][I_shared]                     */
   int32_t gating;              /* beam_gate_flag bits; unknown bits are
                                   BEAM_ERR_INVALID_ARG                        */
+  int32_t expert_format;       /* beam_weight_format; other values are
+                                  BEAM_ERR_INVALID_ARG                        */
+  const float *scale_gate;         /* FP8 only: [E][I] row scales of w_gate   */
+  const float *scale_up;           /* [E][I] row scales of w_up               */
+  const float *scale_down;         /* [E][D] row scales of w_down             */
+  const float *scale_shared_gate;  /* [n_shared][I_shared] (ws_gate)          */
+  const float *scale_shared_up;    /* [n_shared][I_shared] (ws_up)            */
+  const float *scale_shared_down;  /* [n_shared][D] (ws_down)                 */
 } beam_moe_layer;
 
 /* Routing results (device pointers, caller-owned). */
@@ -102,7 +134,8 @@ typedef struct {
   double flops_shared;                /* 6 D I_shared n_shared T              */
   double flops_router;                /* 4 E D T                              */
   double flops_reduction;             /* 1 - flops_routed / flops_topk_routed */
-  double bytes_active_expert_weights; /* experts with a pair + shared, once   */
+  double bytes_active_expert_weights; /* experts with a pair + shared, once
+                                         (FP8: codes plus the row scales)     */
   double bytes_total_min;             /* + router weights + x + y             */
 } beam_stats;
 

@@ -95,7 +95,8 @@ CONFIGS: Dict[str, LayerConfig] = {
                                        router_bias=False, expert_format=FP8),
 }
 
-CONFIG_ORDER = ("tiny_f32", "dsv2lite_decode", "dsv2lite_prefill", "mixtral", "finegrained")
+CONFIG_ORDER = ("tiny_f32", "dsv2lite_decode", "dsv2lite_prefill", "mixtral", "finegrained",
+                "dsv2lite_decode_fp8")
 
 
 def _norm_ppf(p: float) -> float:

@@ -62,6 +62,8 @@ def test_workspace_size_monotone_and_invalid():
     assert dm.beam_moe_workspace_size(fake_layer(gating=dm.GATE_SOFTMAX_ALL | dm.GATE_RENORM), 16) > 0
     assert dm.beam_moe_workspace_size(fake_layer(D=100), 16) == 0        # D % 64
     assert dm.beam_moe_workspace_size(L, -1) == 0
+    f8 = dict(expert_format=dm.WEIGHTS_FP8_E4M3, scale_gate=FAKE, scale_up=FAKE, scale_down=FAKE)
+    assert dm.beam_moe_workspace_size(fake_layer(**f8), 64) == sizes[2]
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -77,6 +79,21 @@ def test_workspace_size_monotone_and_invalid():
     (dict(n_shared=2, I_shared=0), dm.BEAM_ERR_INVALID_ARG),
     (dict(n_shared=1, I_shared=64), dm.BEAM_ERR_INVALID_ARG),       # shared pointers missing
     (dict(n_shared=1, I_shared=96, ws_gate=FAKE, ws_up=FAKE, ws_down=FAKE), dm.BEAM_ERR_UNSUPPORTED),
+    # FP8 (E4M3) expert weights
+    (dict(expert_format=2), dm.BEAM_ERR_INVALID_ARG),
+    (dict(expert_format=1), dm.BEAM_ERR_INVALID_ARG),                  # scales missing
+    (dict(expert_format=1, scale_gate=FAKE, scale_up=FAKE + 4, scale_down=FAKE), dm.BEAM_ERR_INVALID_ARG),
+    (dict(expert_format=1, scale_gate=FAKE, scale_up=FAKE, scale_down=FAKE, dtype=dm.BEAM_F32),
+     dm.BEAM_ERR_UNSUPPORTED),
+    (dict(expert_format=1, scale_gate=FAKE, scale_up=FAKE, scale_down=FAKE, D=192),
+     dm.BEAM_ERR_UNSUPPORTED),                                          # D % 128
+    (dict(expert_format=1, scale_gate=FAKE, scale_up=FAKE, scale_down=FAKE, I=320),
+     dm.BEAM_ERR_UNSUPPORTED),                                          # I % 128
+    (dict(expert_format=1, scale_gate=FAKE, scale_up=FAKE, scale_down=FAKE, n_shared=1,
+          I_shared=128, ws_gate=FAKE, ws_up=FAKE, ws_down=FAKE), dm.BEAM_ERR_INVALID_ARG),  # shared scales
+    (dict(expert_format=1, scale_gate=FAKE, scale_up=FAKE, scale_down=FAKE, n_shared=1,
+          I_shared=192, ws_gate=FAKE, ws_up=FAKE, ws_down=FAKE, scale_shared_gate=FAKE,
+          scale_shared_up=FAKE, scale_shared_down=FAKE), dm.BEAM_ERR_UNSUPPORTED),  # I_shared % 128
 ])
 def test_forward_rejects_bad_layers(kw, status):
     L = fake_layer(**kw)
@@ -146,6 +163,9 @@ def test_stats_host_matches_oracle(name):
               dtype=dm.BEAM_F32 if cfg.dtype == "f32" else dm.BEAM_BF16)
     if cfg.S:
         kw.update(n_shared=cfg.S, I_shared=cfg.I_s, ws_gate=FAKE, ws_up=FAKE, ws_down=FAKE)
+    if cfg.expert_format == synth.FP8:
+        kw.update(expert_format=dm.WEIGHTS_FP8_E4M3, scale_gate=FAKE, scale_up=FAKE, scale_down=FAKE,
+                  scale_shared_gate=FAKE, scale_shared_up=FAKE, scale_shared_down=FAKE)
     L = fake_layer(**kw)
     got = dm.beam_moe_stats_host(L, list(counts), T)
     ref = oracle.layer_stats(cfg, counts, T)

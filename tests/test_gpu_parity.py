@@ -26,7 +26,7 @@ pytestmark = pytest.mark.gpu
 CASES = [(n, T) for n in synth.CONFIG_ORDER for T in synth.CONFIGS[n].tokens]
 # Largest batch for which every token's output is compared with the oracle.
 FULL_Y_MAX = {"tiny_f32": 64, "dsv2lite_decode": 256, "dsv2lite_prefill": 0, "mixtral": 32,
-              "finegrained": 512}
+              "finegrained": 512, "dsv2lite_decode_fp8": 256}
 
 
 @pytest.fixture(autouse=True)
@@ -245,6 +245,65 @@ def test_mask_backward_workload():
     x = inputs(cfg, T, layer)
     note("[mask backward] dsv2lite_decode T=64")
     _mask_backward_case(layer, x, 0.1, 5, device_layer(layer, key=name))
+
+
+def _fp8_scaled(layer, seed):
+    """The same FP8 layer with every row scale multiplied by its own power of
+    two in 2^-6 .. 2^6, so that a scale applied to the wrong row shows."""
+    from dataclasses import replace
+    rng = np.random.default_rng(seed)
+    kw = {}
+    for n in ("s_gate", "s_up", "s_down", "ss_gate", "ss_up", "ss_down"):
+        a = getattr(layer, n)
+        if a is not None:
+            kw[n] = (a * np.exp2(rng.integers(-6, 7, size=a.shape))).astype(np.float32)
+    return replace(layer, **kw)
+
+
+@pytest.mark.parametrize("S", [0, 1, 2])
+@pytest.mark.parametrize("T", [1, 37, 129, 700])
+def test_fp8_small(S, T):
+    """FP8 (E4M3) expert weights with widely varying row scales: 1 to 700
+    tokens (700 x 3 / 12 = 175 pairs per expert, which FP8 still runs in
+    64-row streaming tiles), with 0, 1 or 2 shared experts (2: the fused
+    shared down projection has one scaled k segment per shared expert)."""
+    from oracle_pins import fp8_layer
+    base = fp8_layer(f"gpu_fp8_{S}", D=256, E=12, K=3, I=128, S=S, I_s=128 if S else 0, keep=0.6,
+                     router_bias=True)
+    layer = _fp8_scaled(base, 10 + S)
+    x = small_x(layer, T, "fp8")
+    note(f"[fp8] S={S} T={T}")
+    y, rt, _ = run_forward(device_layer(layer), x)
+    rt_ref, y_ref = oracle.forward(layer, x)
+    check_routing(rt, rt_ref, layer.cfg.E)
+    check_output(y, y_ref, "bf16")
+
+
+def test_fp8_ksplit_and_wide_rows():
+    """FP8 layer with D = 4096 and I = 1024: 3 tokens (16-row tiles, gate/up
+    k split four ways, down two ways), 100 (32-row tiles, both split two
+    ways) and 200 (64-row tiles, no split)."""
+    from oracle_pins import fp8_layer
+    layer = _fp8_scaled(fp8_layer("gpu_fp8_wide", D=4096, E=8, K=2, I=1024, S=1, I_s=256,
+                                  keep=0.7), 21)
+    for T in (3, 100, 200):
+        x = small_x(layer, T, "fp8w")
+        note(f"[fp8 wide] T={T}")
+        y, rt, _ = run_forward(device_layer(layer), x)
+        rt_ref, y_ref = oracle.forward(layer, x)
+        check_routing(rt, rt_ref, layer.cfg.E)
+        check_output(y, y_ref, "bf16")
+
+
+def test_fp8_mask_backward():
+    """Mask-router gradient of an FP8 layer (every candidate's expert runs on
+    the E4M3 weights)."""
+    from oracle_pins import fp8_layer
+    layer = _fp8_scaled(fp8_layer("gpu_fp8_bwd", D=256, E=16, K=4, I=128, S=1, I_s=128, keep=0.5),
+                        31)
+    x = small_x(layer, 45, "fp8bwd")
+    note("[fp8 mask backward] T=45")
+    _mask_backward_case(layer, x, 0.3, 6)
 
 
 def test_route_entry_matches_forward():
