@@ -707,6 +707,23 @@ static void gate_up_streaming(const beam_moe_layer& L, const ExpertArgs& a, long
                               int tile_rows, hipStream_t s) {
   const int Is_all = L.n_shared ? L.n_shared * L.I_shared : 0;
   const int chunks = L.D / chunk_k<F8>();
+  if constexpr (F8) {
+    // FP8 (half the bytes per item): 16-row tiles stream one row group per
+    // item with the smallest k split that still gives about 3/4 of a share
+    // per wave of a full grid; 32-row tiles two row groups, split only for
+    // long rows; 64-row tiles as bf16.
+    if (tile_rows == 16) {
+      const long items1 = ntr * (L.I / 16) + nts * (Is_all / 16);
+      const long want = kStreamGrid * kStreamWaves * 3 / 4;
+      const int ks = items1 >= want ? 1 : 2 * items1 >= want ? 2 : 4;
+      gate_up_stream<1, 1, 1, F8>(a, ntr, nts, L.I, Is_all, ks, s);
+      return;
+    }
+    if (tile_rows == 32) {
+      gate_up_stream<2, 2, 1, F8>(a, ntr, nts, L.I, Is_all, chunks >= 32 ? 2 : 1, s);
+      return;
+    }
+  }
   if (tile_rows == 16) {
     const int ks = stream_ksplit_chunks(chunks);
     const long items2 = ntr * (L.I / 32) + nts * (Is_all / 32);
