@@ -68,10 +68,10 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload: str):
-    """HBM bytes per launch of the dominant kernel from the committed counter
-    summary, or None when absent or taken on different kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{DOMINANT}_{workload}.txt")
+def read_traffic(workload: str, kernel: str = DOMINANT):
+    """HBM bytes per launch of a kernel from the committed counter summary,
+    or None when absent or taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -234,7 +234,8 @@ def main():
             a8 = r["gate_up_alg_bytes"] / (mu * 1e-6) / 1e9
             fp8["gate_up"] = {"kernel": k8[0], "mean_launch_us": round(mu, 2),
                               "alg_bytes_per_launch": r["gate_up_alg_bytes"],
-                              "achieved_gbs": round(a8, 1), "frac": round(a8 / HBM_PEAK_GBS, 4)}
+                              "achieved_gbs": round(a8, 1), "frac": round(a8 / HBM_PEAK_GBS, 4),
+                              "traffic": read_traffic(f"{c8.name}_T{T}", f"{DOMINANT}_stream_fp8")}
         del reps8, dl8
         torch.cuda.empty_cache()
 
