@@ -19,6 +19,12 @@ Sources (cited below by the short names on the left):
   [P2]  "BEAM: Binäre Expertenaktivierungsmaskierung für dynamisches Routing in
         MoE" (chatpaper.ai), the English abstract: MoE-layer FLOPs fall with
         the number of active experts.
+  [P5]  "Stepped MoE: Segment-Level Routing with Configurable Inference
+        Complexity" (paper.rainbus.top), sections 核心方法 (core method) and
+        方法步骤详情 (method steps): the tokens are cut into segments of S
+        tokens, the representation at each segment's first position picks
+        the segment's top-k experts as a {0,1} mask, and the choice is
+        refreshed every S tokens.
 
 Readings where the pages leave a step open (each is also listed with the
 design notes of the repository):
@@ -39,6 +45,11 @@ design notes of the repository):
     select_experts also offers g = softmax over all E logits read at the
     top-K experts (gating bit 1), and renormalising g_hat over the kept
     slots after masking (gating bit 2; all zero when no slot is kept).
+  * Segment routing (off by default; [P5]): with cfg.segment = S > 1, token t
+    uses the routing (top-K set, g, m) computed from token t - t mod S, the
+    first token of its segment of the batch.  Gate bit 4 (GATE_BINARY)
+    gives every top-K slot g = 1, so g_hat = m: [P5]'s {0,1} expert mask
+    with unweighted expert outputs.  It cannot be combined with bit 1.
   * Router and mask decisions (which experts, which bits) are taken on
     float32 logits, the precision the GPU kernels decide in: the logits are
     computed in float64 and rounded once to float32.  Everything else is
@@ -70,7 +81,8 @@ import numpy as np
 
 __all__ = [
     "widen", "router_logits", "select_experts", "Routing", "route", "silu",
-    "GATE_SOFTMAX_ALL", "GATE_RENORM", "mask_router_backward",
+    "GATE_SOFTMAX_ALL", "GATE_RENORM", "GATE_BINARY", "segment_heads",
+    "mask_router_backward",
     "expert_ffn", "forward", "expert_counts", "layer_stats", "decode_e4m3",
     "expert_matrices",
 ]
@@ -119,6 +131,7 @@ class Routing:
 
 GATE_SOFTMAX_ALL = 1
 GATE_RENORM = 2
+GATE_BINARY = 4
 
 
 def select_experts(r: np.ndarray, z: np.ndarray, K: int, gating: int = 0) -> Routing:
@@ -129,13 +142,16 @@ def select_experts(r: np.ndarray, z: np.ndarray, K: int, gating: int = 0) -> Rou
     Step 4: g_hat = g * m.  Decisions are taken on float32-rounded logits.
     Gate options (see the module notes): GATE_SOFTMAX_ALL takes g from a
     softmax over all E logits; GATE_RENORM divides g_hat by its sum over the
-    token's slots when that sum is positive.
+    token's slots when that sum is positive; GATE_BINARY sets g = 1 on every
+    top-K slot ([P5]'s {0,1} mask).
     """
     r32 = np.asarray(r, dtype=np.float64).astype(np.float32)
     z32 = np.asarray(z, dtype=np.float64).astype(np.float32)
     T, E = r32.shape
     if not (1 <= K <= E):
         raise ValueError("need 1 <= K <= E")
+    if (gating & GATE_BINARY) and (gating & GATE_SOFTMAX_ALL):
+        raise ValueError("binary gates exclude the all-expert softmax")
     idx = np.empty((T, K), dtype=np.int32)
     g = np.empty((T, K), dtype=np.float64)
     keep = np.empty((T, K), dtype=bool)
@@ -144,7 +160,9 @@ def select_experts(r: np.ndarray, z: np.ndarray, K: int, gating: int = 0) -> Rou
         # so the lower expert index comes first.
         order = np.argsort(-r32[t], kind="stable")[:K]
         idx[t] = order
-        if gating & GATE_SOFTMAX_ALL:
+        if gating & GATE_BINARY:
+            g[t] = 1.0
+        elif gating & GATE_SOFTMAX_ALL:
             v = r32[t].astype(np.float64)
             w = np.exp(v - v.max())
             g[t] = w[order] / w.sum()
@@ -162,10 +180,22 @@ def select_experts(r: np.ndarray, z: np.ndarray, K: int, gating: int = 0) -> Rou
     return Routing(idx, g, keep, ghat, mask_bits)
 
 
-def route(layer, x: np.ndarray) -> Routing:
-    """[P3] Steps 1-3 (and the gate product of Step 4) for every token of x."""
-    r, z = router_logits(layer, x)
-    return select_experts(r, z, layer.cfg.K, getattr(layer.cfg, "gating", 0))
+def segment_heads(tokens: np.ndarray, S: int) -> np.ndarray:
+    """[P5]: the first token of each token's S-token segment (t - t mod S);
+    S <= 1 leaves every token its own head."""
+    tokens = np.asarray(tokens, dtype=np.int64)
+    return tokens - tokens % S if S > 1 else tokens
+
+
+def route(layer, x: np.ndarray, tokens: Optional[Sequence[int]] = None) -> Routing:
+    """[P3] Steps 1-3 (and the gate product of Step 4) for the given tokens
+    of x (all by default).  With segment routing ([P5]) each token takes the
+    decisions computed on its segment's first token."""
+    cfg = layer.cfg
+    tok = np.arange(x.shape[0]) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    src = segment_heads(tok, getattr(cfg, "segment", 0))
+    r, z = router_logits(layer, x[src])
+    return select_experts(r, z, cfg.K, getattr(cfg, "gating", 0))
 
 
 def silu(a: np.ndarray) -> np.ndarray:
@@ -242,9 +272,8 @@ def forward(layer, x: np.ndarray, tokens: Optional[Sequence[int]] = None,
     """
     cfg = layer.cfg
     tok = np.arange(x.shape[0]) if tokens is None else np.asarray(tokens, dtype=np.int64)
-    xs = x[tok]
-    rt = route(layer, xs) if routing is None else routing
-    X = widen(xs, cfg.dtype)
+    rt = route(layer, x, tok) if routing is None else routing
+    X = widen(x[tok], cfg.dtype)
     y = np.zeros((len(tok), cfg.D), dtype=np.float64)
     cache = {}
     for k in range(cfg.K):
@@ -283,8 +312,8 @@ def mask_router_backward(layer, x: np.ndarray, dy: np.ndarray, beta: float):
     Returns (L_reg, dWm [E][D], db_m [E], dz [T][K]) in float64.
     """
     cfg = layer.cfg
-    if getattr(cfg, "gating", 0):
-        raise ValueError("the mask-router backward covers the method's own gate only")
+    if getattr(cfg, "gating", 0) or getattr(cfg, "segment", 0) > 1:
+        raise ValueError("the mask-router backward covers the method's own per-token gate only")
     T = x.shape[0]
     r, z = router_logits(layer, x)
     rt = select_experts(r, z, cfg.K)

@@ -60,6 +60,7 @@ class LayerConfig:
     router_bias: bool   # per-expert router bias ~ N(0, 1)
     gating: int = 0     # gate option bits: 1 softmax over all E, 2 renormalise after masking
     expert_format: str = ""   # "" = expert weights in dtype; FP8 = E4M3 codes + row scales
+    segment: int = 0    # > 1: every token routes as the first token of its S-token segment
 
     @property
     def avg_k_target(self) -> float:

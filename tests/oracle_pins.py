@@ -50,12 +50,20 @@ def torch_logits(layer, x):
 def torch_dense_gates(layer, x, use_mask=True):
     """G[t][e]: masked top-K softmax gate of expert e for token t (0 elsewhere).
     Gate options of layer.cfg.gating: bit 1 takes the softmax over all E and
-    reads it at the top-K experts; bit 2 renormalises the masked gates."""
+    reads it at the top-K experts; bit 2 renormalises the masked gates; bit 4
+    gives every top-K expert gate 1.  With layer.cfg.segment = S > 1 every
+    token takes the gates and experts of token t - t % S."""
     r, z = torch_logits(layer, x)
+    S = getattr(layer.cfg, "segment", 0)
+    if S > 1:
+        head = torch.arange(r.shape[0]) // S * S
+        r, z = r[head], z[head]
     K = layer.cfg.K
     gating = getattr(layer.cfg, "gating", 0)
     vals, idx = torch.topk(r, K, dim=1)
-    if gating & 1:
+    if gating & 4:
+        g = torch.ones_like(vals)
+    elif gating & 1:
         g = torch.gather(torch.softmax(r, dim=1), 1, idx)
     else:
         g = torch.softmax(vals, dim=1)
@@ -74,6 +82,15 @@ def with_gating(layer, gating):
     """The same layer with other gate options."""
     from dataclasses import replace
     return replace(layer, cfg=replace(layer.cfg, gating=gating))
+
+
+def with_segment(layer, S, gating=None):
+    """The same layer with segment routing of S tokens (and other gate options)."""
+    from dataclasses import replace
+    kw = {"segment": S}
+    if gating is not None:
+        kw["gating"] = gating
+    return replace(layer, cfg=replace(layer.cfg, **kw))
 
 
 def torch_e4m3(codes):
@@ -194,7 +211,7 @@ def pin_gate_options_vs_torch(O):
     renormalisation of the masked gates), gates and the dense brute-force y."""
     base = small_layer("gating", D=64, E=9, K=4, I=24, S=1, I_s=16, keep=0.45, router_bias=True)
     x = small_x(base, 12, "gating")
-    for flags in (1, 2, 3):
+    for flags in (1, 2, 3, 4, 6):
         layer = with_gating(base, flags)
         G, idx = torch_dense_gates(layer, x)
         rt = O.route(layer, x)
@@ -206,6 +223,66 @@ def pin_gate_options_vs_torch(O):
             s = rt.ghat.sum(axis=1)
             kept = rt.keep.any(axis=1)
             assert np.allclose(s[kept], 1.0, atol=1e-12) and np.all(s[~kept] == 0.0)
+
+
+def pin_golden_segment(O):
+    """Hand-derived worked example of segment routing (S = 2), with the
+    method's own gate and with binary gates."""
+    j, layer0, x = layer_from_json("worked_example_routed.json")
+    with open(os.path.join(GOLDEN, "worked_example_segment.json")) as f:
+        js = json.load(f)
+    ev = lambda a: np.vectorize(eval_closed_form)(np.array(a, dtype=object)).astype(float)  # noqa: E731
+    ex = js["expect"]
+    layer = with_segment(layer0, js["segment"])
+    rt, y = O.forward(layer, x)
+    assert np.array_equal(rt.idx, np.array(ex["idx"])), rt.idx
+    assert np.array_equal(rt.mask_bits, np.array(ex["mask_bits"], np.uint32))
+    assert np.allclose(rt.ghat, ev(ex["ghat"]), rtol=0, atol=1e-7)
+    assert np.array_equal(O.expert_counts(rt, 3), np.array(ex["counts"]))
+    assert np.allclose(y, ev(ex["y"]), rtol=0, atol=1e-6), y
+    _, yb = O.forward(with_segment(layer0, js["segment"], 4), x)
+    assert np.allclose(yb, ev(ex["y_binary"]), rtol=0, atol=1e-6), yb
+
+
+def pin_segment_vs_torch(O):
+    """Segment routing (S = 4 and 16 over ragged batches; with the method's
+    gate, binary gates, and binary + renormalised) against torch: top-K,
+    softmax and mask of each segment's first token, dense brute-force y."""
+    base = small_layer("segment", D=64, E=10, K=3, I=24, S=1, I_s=16, keep=0.5, router_bias=True)
+    x = small_x(base, 23, "segment")
+    for S, flags in ((4, 0), (4, 4), (16, 6), (5, 2)):
+        layer = with_segment(base, S, flags)
+        G, idx = torch_dense_gates(layer, x)
+        rt = O.route(layer, x)
+        assert np.array_equal(rt.idx, idx.numpy()), (S, flags)
+        assert _rel(rt.ghat, torch.gather(G, 1, idx).numpy()) < 1e-12, (S, flags)
+        _, y = O.forward(layer, x)
+        assert _rel(y, torch_dense_forward(layer, x)) < 1e-9, (S, flags)
+
+
+def pin_segment_properties(O):
+    """S <= 1 is per-token routing; S >= T gives every token token 0's
+    experts and mask; routing a sample of tokens equals routing them within
+    the whole batch; a batch whose segments repeat one token routes exactly
+    as per-token routing."""
+    base = small_layer("segprop", D=48, E=8, K=2, I=16, keep=0.5)
+    x = small_x(base, 13, "segprop")
+    rt0 = O.route(base, x)
+    for S in (0, 1):
+        rt = O.route(with_segment(base, S), x)
+        assert np.array_equal(rt.idx, rt0.idx) and np.array_equal(rt.ghat, rt0.ghat)
+    rt = O.route(with_segment(base, 64), x)
+    assert np.all(rt.idx == rt0.idx[0]) and np.all(rt.mask_bits == rt0.mask_bits[0])
+    lay3 = with_segment(base, 3)
+    _, yall = O.forward(lay3, x)
+    toks = np.array([12, 4, 7, 1])
+    rts, ys = O.forward(lay3, x, tokens=toks)
+    assert np.array_equal(rts.idx, O.route(lay3, x).idx[toks])
+    assert np.allclose(ys, yall[toks], rtol=0, atol=1e-12)
+    rep = x[np.arange(12) // 3 * 3]           # every segment of 3 repeats its first token
+    rt_seg, y_seg = O.forward(lay3, rep)
+    rt_tok, y_tok = O.forward(base, rep)
+    assert np.array_equal(rt_seg.idx, rt_tok.idx) and np.array_equal(y_seg, y_tok)
 
 
 def pin_gate_options_identity(O):
@@ -520,4 +597,5 @@ ALL_PINS = [
     pin_threshold_is_sigmoid_half, pin_batch_invariance, pin_expert_permutation,
     pin_silu_closed_forms, pin_widen_bf16, pin_stats_formulas,
     pin_e4m3_known_values, pin_e4m3_vs_torch, pin_fp8_layer_vs_torch,
+    pin_golden_segment, pin_segment_vs_torch, pin_segment_properties,
 ]

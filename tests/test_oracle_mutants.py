@@ -94,6 +94,16 @@ MUTANTS = {
                           "return decode_e4m3(a) * np.resize(np.asarray(scale, dtype=np.float64), a.shape[1])[None, :]"),
     # shared experts read the routed experts' scales
     "fp8_shared_uses_routed_scales": ('"s" + name[1:] if name.startswith("ws_")', '"s_" + name[3:] if name.startswith("ws_")'),
+    # segment routing ignored
+    "segment_ignored": ("return tokens - tokens % S if S > 1 else tokens", "return tokens"),
+    # segment decided by its second token
+    "segment_second_token": ("return tokens - tokens % S if S > 1 else tokens",
+                             "return np.minimum(tokens - tokens % S + 1, tokens) if S > 1 else tokens"),
+    # heads computed on positions within a token sample instead of token indices
+    "segment_sample_positions": ("src = segment_heads(tok, getattr(cfg, \"segment\", 0))",
+                                 "src = tok[segment_heads(np.arange(len(tok)), getattr(cfg, \"segment\", 0))]"),
+    # binary gates normalised over K
+    "binary_over_k": ("            g[t] = 1.0\n", "            g[t] = 1.0 / K\n"),
     # Avg-K counts all top-K slots
     "avgk_topk": ('"avg_k": (P / T) if T > 0 else 0.0', '"avg_k": (cfg.K if T > 0 else 0.0)'),
 }
