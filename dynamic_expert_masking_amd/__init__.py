@@ -42,12 +42,14 @@ class beam_moe_layer(ctypes.Structure):
                 ("gating", ctypes.c_int32), ("expert_format", ctypes.c_int32),
                 ("scale_gate", ctypes.c_void_p), ("scale_up", ctypes.c_void_p),
                 ("scale_down", ctypes.c_void_p), ("scale_shared_gate", ctypes.c_void_p),
-                ("scale_shared_up", ctypes.c_void_p), ("scale_shared_down", ctypes.c_void_p)]
+                ("scale_shared_up", ctypes.c_void_p), ("scale_shared_down", ctypes.c_void_p),
+                ("segment_len", ctypes.c_int32)]
 
 
 # beam_gate_flag bits of beam_moe_layer.gating
 GATE_SOFTMAX_ALL = 1
 GATE_RENORM = 2
+GATE_BINARY = 4
 # beam_weight_format values of beam_moe_layer.expert_format
 WEIGHTS_DTYPE = 0
 WEIGHTS_FP8_E4M3 = 1
@@ -126,14 +128,15 @@ def make_layer(D, E, K, I, dtype, w_router, w_mask, w_gate, w_up, w_down, b_rout
                b_mask=None, n_shared=0, I_shared=0, ws_gate=None, ws_up=None,
                ws_down=None, gating=0, expert_format=WEIGHTS_DTYPE, scale_gate=None,
                scale_up=None, scale_down=None, scale_shared_gate=None, scale_shared_up=None,
-               scale_shared_down=None) -> beam_moe_layer:
+               scale_shared_down=None, segment_len=0) -> beam_moe_layer:
     """Fill a beam_moe_layer descriptor from tensors (or raw addresses).  The
     caller keeps the tensors alive while the descriptor is in use."""
     return beam_moe_layer(D, E, K, I, n_shared, I_shared, dtype, _ptr(w_router), _ptr(w_mask),
                           _ptr(b_router), _ptr(b_mask), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
                           _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down), int(gating),
                           int(expert_format), _ptr(scale_gate), _ptr(scale_up), _ptr(scale_down),
-                          _ptr(scale_shared_gate), _ptr(scale_shared_up), _ptr(scale_shared_down))
+                          _ptr(scale_shared_gate), _ptr(scale_shared_up), _ptr(scale_shared_down),
+                          int(segment_len))
 
 
 def make_route_out(topk_idx, gates, mask, expert_count) -> beam_route_out:

@@ -127,7 +127,11 @@ static int check_layer(const beam_moe_layer* L) {
   if (L->D <= 0 || L->E <= 0 || L->K <= 0 || L->I <= 0 || L->n_shared < 0)
     return BEAM_ERR_INVALID_ARG;
   if (L->K > L->E) return BEAM_ERR_INVALID_ARG;
-  if (L->gating & ~(BEAM_GATE_SOFTMAX_ALL | BEAM_GATE_RENORM)) return BEAM_ERR_INVALID_ARG;
+  if (L->gating & ~(BEAM_GATE_SOFTMAX_ALL | BEAM_GATE_RENORM | BEAM_GATE_BINARY))
+    return BEAM_ERR_INVALID_ARG;
+  if ((L->gating & BEAM_GATE_BINARY) && (L->gating & BEAM_GATE_SOFTMAX_ALL))
+    return BEAM_ERR_INVALID_ARG;
+  if (L->segment_len < 0) return BEAM_ERR_INVALID_ARG;
   if (L->n_shared > 0 && L->I_shared <= 0) return BEAM_ERR_INVALID_ARG;
   const void* req[] = {L->w_router, L->w_mask, L->w_gate, L->w_up, L->w_down};
   for (const void* p : req)
@@ -269,7 +273,7 @@ int beam_moe_mask_backward(const beam_moe_layer* layer, const void* x, const voi
   WsLayout lay;
   int st = check_call(layer, x, T, ws, ws_bytes, &lay);
   if (st != BEAM_OK) return st;
-  if (layer->gating != 0) return BEAM_ERR_UNSUPPORTED;
+  if (layer->gating != 0 || layer->segment_len > 1) return BEAM_ERR_UNSUPPORTED;
   if (!dwm || !lreg || (reinterpret_cast<uintptr_t>(dwm) & 15u) ||
       (reinterpret_cast<uintptr_t>(lreg) & 3u) || (dbm && (reinterpret_cast<uintptr_t>(dbm) & 3u)))
     return BEAM_ERR_INVALID_ARG;

@@ -363,6 +363,7 @@ struct SelectArgs {
   const float* bm;
   int T, E, K;
   int gating;   // beam_gate_flag bits
+  int seg;      // segment routing: > 1 = token t routes as token t - t % seg
   int32_t* idx;
   float* gates;
   uint32_t* mask;
@@ -381,18 +382,27 @@ struct SelectArgs {
   int32_t* slot_pos;
 };
 
+// Row of the router logits that token t's routing is decided on: its own,
+// or with segment routing the first token of its segment.
+__device__ __forceinline__ int route_row(const SelectArgs& a, int t) {
+  return a.seg > 1 ? t - t % a.seg : t;
+}
+
 // Gates of one token from its K selected logits: lane k < K holds slot k's
 // logit r_k and its mask bit; r_0 (the largest) sits in lane 0.  Without
 // options, g = softmax over the K logits; BEAM_GATE_SOFTMAX_ALL divides by the
 // sum over all E experts instead (lane l's NPER logits in r_all, -inf for
-// absent experts); BEAM_GATE_RENORM renormalises g * m over the kept slots.
+// absent experts); BEAM_GATE_BINARY sets g = 1 on every slot;
+// BEAM_GATE_RENORM renormalises g * m over the kept slots.
 template <int NPER>
 __device__ __forceinline__ float token_gate(int gating, bool slot, bool keep, float r_k,
                                             const float (&r_all)[NPER]) {
   const float r_0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(r_k), 0));
-  const float ex = slot ? expf(r_k - r_0) : 0.f;
+  const float ex = slot ? ((gating & BEAM_GATE_BINARY) ? 1.f : expf(r_k - r_0)) : 0.f;
   float den;
-  if (gating & BEAM_GATE_SOFTMAX_ALL) {
+  if (gating & BEAM_GATE_BINARY) {
+    den = 1.f;
+  } else if (gating & BEAM_GATE_SOFTMAX_ALL) {
     float part = 0.f;
 #pragma unroll
     for (int i = 0; i < NPER; ++i) part += expf(r_all[i] - r_0);   // exp(-inf) = 0
@@ -424,7 +434,7 @@ __device__ __forceinline__ void select_token(const SelectArgs& a, int t, int lan
       const int e = lane + kWave * i;
       pr[u][i] = pz[u][i] = 0.f;
       if (u < a.KS && e < E) {
-        const float* row = a.part + (size_t(u) * a.T + t) * 2 * E;
+        const float* row = a.part + (size_t(u) * a.T + route_row(a, t)) * 2 * E;
         pr[u][i] = row[e];
         pz[u][i] = row[E + e];
       }
@@ -603,7 +613,7 @@ __global__ __launch_bounds__(1024) void k_select(SelectArgs a) {
           const int e = lane + kWave * i;
           pr[u][j][i] = pz[u][j][i] = 0.f;
           if (ks0 + u < a.KS && t < T && e < E) {
-            const float* row = a.part + (size_t(ks0 + u) * T + t) * 2 * E;
+            const float* row = a.part + (size_t(ks0 + u) * T + route_row(a, t)) * 2 * E;
             pr[u][j][i] = row[e];
             pz[u][j][i] = row[E + e];
           }
@@ -743,6 +753,7 @@ hipError_t launch_select(const beam_moe_layer& L, int32_t T, int tile_rows, cons
   a.E = L.E;
   a.K = L.K;
   a.gating = L.gating;
+  a.seg = L.segment_len;
   a.idx = p.idx;
   a.gates = p.gates;
   a.mask = p.mask;

@@ -40,7 +40,7 @@ class DeviceLayer:
     """Device copy of a layer's parameters plus its C descriptor.
 
     `host` is any object with the attributes of the parameter set: cfg (with
-    D, E, K, I, S, I_s, dtype and optionally gating, expert_format), w_router,
+    D, E, K, I, S, I_s, dtype and optionally gating, expert_format, segment), w_router,
     w_mask, b_router, b_mask, w_gate, w_up, w_down, ws_gate, ws_up, ws_down,
     and for FP8 expert weights the row scales s_gate, s_up, s_down, ss_gate,
     ss_up, ss_down.
@@ -72,7 +72,7 @@ class DeviceLayer:
                           expert_format=WEIGHTS_FP8_E4M3 if self.fp8 else WEIGHTS_DTYPE,
                           scale_gate=t["s_gate"], scale_up=t["s_up"], scale_down=t["s_down"],
                           scale_shared_gate=t["ss_gate"], scale_shared_up=t["ss_up"],
-                          scale_shared_down=t["ss_down"])
+                          scale_shared_down=t["ss_down"], segment_len=getattr(c, "segment", 0))
 
     def replicas(self, n: int):
         """n extra copies of the expert weights at distinct addresses (same

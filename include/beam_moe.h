@@ -59,8 +59,19 @@ typedef enum { BEAM_F32 = 0, BEAM_BF16 = 1 } beam_dtype;
  *                          the top-K experts (no renormalisation over K).
  *   BEAM_GATE_RENORM       after masking, g_hat_k = g_k m_k / sum_j g_j m_j
  *                          (0 for every slot when no slot survives).
+ *   BEAM_GATE_BINARY       g_k = 1 on every top-K slot, so g_hat = m: the
+ *                          {0,1} expert mask of the Stepped MoE page
+ *                          (paper.rainbus.top, "Stepped MoE: Segment-Level
+ *                          Routing with Configurable Inference Complexity",
+ *                          section on the core method).  Combines with
+ *                          BEAM_GATE_RENORM (g_hat = m / sum m), not with
+ *                          BEAM_GATE_SOFTMAX_ALL (BEAM_ERR_INVALID_ARG).
  * The top-K set, its order and the mask bits do not depend on these bits. */
-typedef enum { BEAM_GATE_SOFTMAX_ALL = 1, BEAM_GATE_RENORM = 2 } beam_gate_flag;
+typedef enum {
+  BEAM_GATE_SOFTMAX_ALL = 1,
+  BEAM_GATE_RENORM = 2,
+  BEAM_GATE_BINARY = 4
+} beam_gate_flag;
 
 /* Storage of the routed and shared expert weights (beam_moe_layer.
  * expert_format).  The masking combines with weight quantisation (the
@@ -113,6 +124,14 @@ typedef struct {
   const float *scale_shared_gate;  /* [n_shared][I_shared] (ws_gate)          */
   const float *scale_shared_up;    /* [n_shared][I_shared] (ws_up)            */
   const float *scale_shared_down;  /* [n_shared][D] (ws_down)                 */
+  int32_t segment_len;         /* Segment routing (Stepped MoE page, sections
+                                  on the core method and the method steps):
+                                  0 or 1 = every token routes itself; S > 1 =
+                                  token t takes the routing (top-K set, g, m)
+                                  of token t - t % S, the first token of its
+                                  S-token segment of the batch, and runs those
+                                  experts on its own x.  Negative values are
+                                  BEAM_ERR_INVALID_ARG.                       */
 } beam_moe_layer;
 
 /* Routing results (device pointers, caller-owned). */
@@ -172,8 +191,8 @@ int beam_moe_forward(const beam_moe_layer *layer, const void *x, int32_t T,
  * all fp32, overwritten, device pointers (dwm 16-byte aligned).  Runs the
  * router and every candidate's expert, so it costs a plain top-K MoE forward;
  * needs the same workspace as beam_moe_forward.  Only the method's own gate
- * (gating 0) is supported (otherwise BEAM_ERR_UNSUPPORTED).  Results are
- * deterministic.  */
+ * (gating 0) with per-token routing (segment_len <= 1) is supported
+ * (otherwise BEAM_ERR_UNSUPPORTED).  Results are deterministic.  */
 int beam_moe_mask_backward(const beam_moe_layer *layer, const void *x,
                            const void *dy, int32_t T, float beta, float *dwm,
                            float *dbm, float *lreg, void *ws, size_t ws_bytes,

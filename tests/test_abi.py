@@ -58,9 +58,14 @@ def test_workspace_size_monotone_and_invalid():
     sizes = [dm.beam_moe_workspace_size(L, T) for T in (0, 1, 64, 65, 4096)]
     assert all(a <= b for a, b in zip(sizes, sizes[1:])) and sizes[-1] > sizes[1] > 0
     assert dm.beam_moe_workspace_size(fake_layer(K=9), 16) == 0          # K > E
-    assert dm.beam_moe_workspace_size(fake_layer(gating=4), 16) == 0     # unknown gate bit
+    assert dm.beam_moe_workspace_size(fake_layer(gating=16), 16) == 0    # unknown gate bit
     assert dm.beam_moe_workspace_size(fake_layer(gating=dm.GATE_SOFTMAX_ALL | dm.GATE_RENORM), 16) > 0
     assert dm.beam_moe_workspace_size(fake_layer(D=100), 16) == 0        # D % 64
+    assert dm.beam_moe_workspace_size(fake_layer(gating=dm.GATE_BINARY | dm.GATE_RENORM), 16) > 0
+    assert dm.beam_moe_workspace_size(fake_layer(gating=dm.GATE_BINARY | dm.GATE_SOFTMAX_ALL), 16) == 0
+    assert dm.beam_moe_workspace_size(fake_layer(gating=8), 16) == 0
+    assert dm.beam_moe_workspace_size(fake_layer(segment_len=16), 16) > 0
+    assert dm.beam_moe_workspace_size(fake_layer(segment_len=-1), 16) == 0
     assert dm.beam_moe_workspace_size(L, -1) == 0
     f8 = dict(expert_format=dm.WEIGHTS_FP8_E4M3, scale_gate=FAKE, scale_up=FAKE, scale_down=FAKE)
     assert dm.beam_moe_workspace_size(fake_layer(**f8), 64) == sizes[2]
@@ -129,6 +134,7 @@ def test_mask_backward_argument_checks():
         return lib.beam_moe_mask_backward(ctypes.byref(layer), FAKE, dy, T, 0.1, dwm, None, lreg,
                                           ws, ws_bytes, None)
     assert call(fake_layer(gating=1)) == dm.BEAM_ERR_UNSUPPORTED
+    assert call(fake_layer(segment_len=4)) == dm.BEAM_ERR_UNSUPPORTED
     assert call(L, dwm=None) == dm.BEAM_ERR_INVALID_ARG
     assert call(L, dwm=FAKE + 4) == dm.BEAM_ERR_INVALID_ARG     # dWm must be 16-byte aligned
     assert call(L, lreg=None) == dm.BEAM_ERR_INVALID_ARG

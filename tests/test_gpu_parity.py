@@ -183,6 +183,44 @@ def test_gate_options_on_workload():
     check_output(y[toks], y_ref, cfg.dtype)
 
 
+@pytest.mark.parametrize("seg,flags", [(16, 0), (32, 4), (16, 6), (7, 2)])
+@pytest.mark.parametrize("T", [37, 4200])
+def test_segment_routing(seg, flags, T):
+    """Segment routing (every token routes as its segment's first token), with
+    the method's gate, binary gates, binary + renormalised and renormalised
+    gates; one-wave-per-token selection (37 tokens) and 64-token blocks (4200)."""
+    from oracle_pins import with_segment
+    base = small_layer("segment", D=128, E=40, K=6, I=64, S=1, I_s=64, keep=0.4, router_bias=True)
+    layer = with_segment(base, seg, flags)
+    x = small_x(base, T, "segment")
+    note(f"[segment routing] S={seg} flags={flags} T={T}")
+    y, rt, _ = run_forward(device_layer(layer), x)
+    rt_ref, y_ref = oracle.forward(layer, x)
+    check_routing(rt, rt_ref, layer.cfg.E)
+    check_output(y, y_ref, "bf16")
+
+
+def test_segment_routing_stepped_form():
+    """The Stepped MoE form on the fine-grained layer (212 experts of 256,
+    top-16): 16-token segments, binary gates, zero-initialised mask router
+    (every top-K expert kept), T = 512."""
+    from oracle_pins import with_segment
+    name, T = "finegrained", 512
+    cfg = synth.CONFIGS[name]
+    layer = with_segment(with_mask(cached_layer(name), True, 0.0), 16, 4)
+    x = inputs(cfg, T, cached_layer(name))
+    note("[segment routing] finegrained T=512 S=16 binary")
+    y, rt, _ = run_forward(device_layer(layer), x)
+    rt_ref = oracle.route(layer, x)
+    check_routing(rt, rt_ref, cfg.E)
+    assert np.all(rt["mask"] == (1 << cfg.K) - 1)
+    for s0 in range(0, T, 16):
+        assert np.all(rt["topk_idx"][s0:s0 + 16] == rt["topk_idx"][s0])
+    toks = sample_tokens(T)
+    _, y_ref = oracle.forward(layer, x, tokens=toks)
+    check_output(y[toks], y_ref, cfg.dtype)
+
+
 def _mask_backward_case(layer, x, beta, seed, dev=None):
     import dynamic_expert_masking_amd as dm
     from dynamic_expert_masking_amd.device import to_device
