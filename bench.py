@@ -52,6 +52,11 @@ def parse():
     p.add_argument("--pool", type=int, default=16, help="distinct input batches")
     p.add_argument("--no-sweep", action="store_true", help="skip the other batch sizes")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--segment", type=int, default=0,
+                   help="segment routing: tokens route as their S-token segment's first token")
+    p.add_argument("--gating", type=int, default=None, help="gate option bits (default: the config's)")
+    p.add_argument("--zero-mask", action="store_true",
+                   help="zero mask router (every top-K candidate kept: plain top-K routing)")
     p.add_argument("--no-fp8", action="store_true",
                    help="skip the FP8 (E4M3) expert-weight variant of the decode layer")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -116,11 +121,17 @@ def main():
         return
 
     cfg = synth.CONFIGS[args.config]
+    from dataclasses import replace
+    if args.segment or args.gating is not None:
+        cfg = replace(cfg, segment=args.segment,
+                      gating=cfg.gating if args.gating is None else args.gating)
     T = args.tokens or (64 if args.config.startswith("dsv2lite_decode") else cfg.tokens[-1])
 
     def setup(c):
         t0 = time.time()
         host = synth.make_layer(c)
+        if args.zero_mask:
+            host = replace(host, w_mask=np.zeros_like(host.w_mask), b_mask=None)
         dl = DeviceLayer(host, dev)
         per_copy = sum(v.numel() * v.element_size() for k, v in dl.t.items() if v is not None)
         copies = args.copies or max(2, min(16, int(np.ceil(1.5e9 / max(1, per_copy))) + 1))
@@ -213,7 +224,8 @@ def main():
 
     # the same decode layer with FP8 (E4M3) expert weights, same batch size
     fp8 = None
-    if args.config == "dsv2lite_decode" and not args.no_fp8:
+    if (args.config == "dsv2lite_decode" and not args.no_fp8 and not args.segment
+            and args.gating is None and not args.zero_mask):
         del reps
         dl = None
         torch.cuda.empty_cache()
@@ -259,7 +271,10 @@ def main():
         "data": "synthetic (seeded; x~N(0,1), weights~N(0,1/D))",
         "config": {"workload": f"{cfg.name}: D={cfg.D} E={cfg.E} K={cfg.K} I={cfg.I} "
                                f"shared={cfg.S}x{cfg.I_s} T={T}"
-                               + (" expert weights E4M3" if cfg.expert_format == synth.FP8 else ""),
+                               + (" expert weights E4M3" if cfg.expert_format == synth.FP8 else "")
+                               + (f" segment={cfg.segment}" if cfg.segment > 1 else "")
+                               + (f" gating={cfg.gating}" if cfg.gating else "")
+                               + (" mask router zero" if args.zero_mask else ""),
                    "tokens": T, "weight_copies": copies, "input_pool": args.pool},
         "layer": {"avg_k": round(main_res["avg_k"], 3),
                   "active_experts": round(main_res["active_experts"], 2),
