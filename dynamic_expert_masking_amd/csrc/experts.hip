@@ -111,6 +111,13 @@ __device__ __forceinline__ void down_item(long w, int ntr, int nts, int nb_all, 
 // gate/up + SwiGLU (bf16)
 // ---------------------------------------------------------------------------
 
+// Cooperative shared items (bf16 launches with a 4-way k split) pay off once
+// a shared weight block would otherwise be streamed for this many tiles:
+// with fewer, their per-step barriers cost more than the re-reads they save
+// (timed on MI355X at T = 1 .. 256, DeepSeek-V2-Lite shapes).
+constexpr int kCoopGateUpTiles = 4;
+constexpr int kCoopDownTiles = 8;
+
 // Streaming (decode) gate/up: items are (tile, n-block of 16*NB intermediate
 // rows); the 2*NB streamed matrices are the gate and up rows of each 16-row
 // group, which share the token operand (see stream_engine.h).  F8: the
@@ -172,6 +179,39 @@ struct GateUpStream {
       it.x[b] = (const u16*)a->x + size_t(t) * a->D;
     }
   }
+  // Cooperative items (bf16, k split 4): (block of NB shared row groups, four
+  // consecutive shared tiles), block fastest; the w-th wave takes tile 4g + w.
+  long n_coop = 0;
+  __device__ long coop_items() const { return n_coop; }
+  __device__ bool decode_coop(long item, int w, int lane, StreamItem<NMAT, MT>& it) const {
+    const int nb = int(item % nbs), g = int(item / nbs);
+    const int t = 4 * g + w;
+    const bool mine = t < nts;
+    it.valid = true;
+    it.nseg = 1;
+    it.w_seg = 0;
+    it.x_seg = 0;
+    it.cps = a->D / chunk_k<F8>();
+    it.w_row = a->D * EB;
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      const size_t off = size_t(nb * NB + q) * 16 * a->D * EB;
+      it.w[2 * q] = (const unsigned char*)a->sg + off;
+      it.w[2 * q + 1] = (const unsigned char*)a->su + off;
+    }
+    const Tile tl = ld_tile(a->tiles + ntr + (mine ? t : 0));
+#pragma unroll
+    for (int b = 0; b < MT; ++b) {
+      const int r = 16 * b + (lane & 15);
+      const int tok = mine && r < tl.rows ? tl.row0 + r : 0;   // absent rows read token 0
+      it.x[b] = (const u16*)a->x + size_t(tok) * a->D;
+    }
+    return mine;
+  }
+  __device__ void epilogue_coop(long item, int w, const f32x4 (&acc)[NMAT][MT], int lane) const {
+    const int nb = int(item % nbs), g = int(item / nbs);
+    store_h(ld_tile(a->tiles + ntr + 4 * g + w), nb, true, acc, lane);
+  }
   __device__ void scales(long item, int, int lane, f32x4 (&sc)[NMAT]) const {
     int ti, nb;
     bool shared;
@@ -189,7 +229,10 @@ struct GateUpStream {
     int ti, nb;
     bool shared;
     work_item(item, ntr, nts, nbr, nbs, ti, nb, shared);
-    const Tile tl = ld_tile(a->tiles + ti);
+    store_h(ld_tile(a->tiles + ti), nb, shared, acc, lane);
+  }
+  __device__ void store_h(const Tile tl, int nb, bool shared, const f32x4 (&acc)[NMAT][MT],
+                          int lane) const {
     const int Iv = shared ? a->S * a->Is : a->I;
     u16* hb = shared ? (u16*)a->h_sh : (u16*)a->h;
 #pragma unroll
@@ -223,7 +266,15 @@ __global__ __launch_bounds__(kStreamWaves * 64) void k_gate_up_stream(ExpertArgs
   pb.nbr = a.I / (16 * NB);
   pb.nbs = a.S > 0 ? (a.S * a.Is) / (16 * NB) : 1;
   pb.total = long(pb.ntr) * pb.nbr + long(pb.nts) * pb.nbs;
-  stream_run<NMAT, MT, U, KSPLIT, F8>(pb, lds);
+  if constexpr (KSPLIT == 4 && !F8) {
+    if (pb.nts >= kCoopGateUpTiles) {
+      // shared tiles as cooperative items, ahead of the routed items
+      pb.n_coop = long((pb.nts + 3) / 4) * pb.nbs;
+      pb.total = long(pb.ntr) * pb.nbr;
+      stream_coop_run<NMAT, MT>(pb, lds, StreamLds<NMAT, MT, U, KSPLIT>::kWaveBytes);
+    }
+  }
+  stream_run<NMAT, MT, U, KSPLIT, F8>(pb, lds, pb.n_coop);
 }
 
 // Streaming (decode) down: items are (tile, d-block of 16*NB output rows),
@@ -290,11 +341,44 @@ struct DownStream {
 #pragma unroll
     for (int g = 0; g < NB; ++g) sc[g] = row_scales16(q + (nb * NB + g) * 16, lane);
   }
+  // Cooperative items (bf16, k split 4): (d-block, four consecutive shared
+  // tiles), d-block fastest; the w-th wave takes tile 4g + w.
+  long n_coop = 0;
+  __device__ long coop_items() const { return n_coop; }
+  __device__ bool decode_coop(long item, int w, int lane, StreamItem<NB, MT>& it) const {
+    const int nb = int(item % nb_all), g = int(item / nb_all);
+    const int t = 4 * g + w;
+    const bool mine = t < nts;
+    it.valid = true;
+    it.nseg = a->S;
+    it.cps = a->Is / chunk_k<F8>();
+    it.w_row = a->Is * EB;
+    it.w_seg = long(a->D) * a->Is * EB;
+    it.x_seg = a->Is;
+    const unsigned char* w0 = (const unsigned char*)a->sd + size_t(nb * 16 * NB) * a->Is * EB;
+#pragma unroll
+    for (int q = 0; q < NB; ++q) it.w[q] = w0 + size_t(16 * q) * it.w_row;
+    const Tile tl = ld_tile(a->tiles + ntr + (mine ? t : 0));
+    const long hs = long(a->S) * a->Is;
+#pragma unroll
+    for (int b = 0; b < MT; ++b) {
+      const int r = 16 * b + (lane & 15);
+      it.x[b] = (const u16*)a->h_sh + size_t(tl.row0 + (mine && r < tl.rows ? r : 0)) * hs;
+    }
+    return mine;
+  }
+  __device__ void epilogue_coop(long item, int w, const f32x4 (&acc)[NB][MT], int lane) const {
+    const int nb = int(item % nb_all), g = int(item / nb_all);
+    store_o(ld_tile(a->tiles + ntr + 4 * g + w), nb, true, acc, lane);
+  }
   __device__ void epilogue(long item, const f32x4 (&acc)[NB][MT], int lane) const {
     int ti, nb;
     down_item(item, ntr, nts, nb_all, ti, nb);
     const bool shared = ti >= ntr;
-    const Tile tl = ld_tile(a->tiles + ti);
+    store_o(ld_tile(a->tiles + ti), nb, shared, acc, lane);
+  }
+  __device__ void store_o(const Tile tl, int nb, bool shared, const f32x4 (&acc)[NB][MT],
+                          int lane) const {
     float* ob = shared ? a->o_sh : a->o;
 #pragma unroll
     for (int b = 0; b < MT; ++b) {
@@ -320,7 +404,15 @@ __global__ __launch_bounds__(kStreamWaves * 64) void k_down_stream(ExpertArgs a)
   pb.nts = ld_const(&a.plan->n_tiles_shared);
   pb.nb_all = a.D / (16 * NB);
   pb.total = long(pb.ntr + pb.nts) * pb.nb_all;
-  stream_run<NB, MT, U, KSPLIT, F8>(pb, lds);
+  if constexpr (KSPLIT == 4 && !F8) {
+    if (pb.nts >= kCoopDownTiles) {
+      // shared tiles as cooperative items, ahead of the routed items
+      pb.n_coop = long((pb.nts + 3) / 4) * pb.nb_all;
+      pb.total = long(pb.ntr) * pb.nb_all;
+      stream_coop_run<NB, MT>(pb, lds, StreamLds<NB, MT, U, KSPLIT>::kWaveBytes);
+    }
+  }
+  stream_run<NB, MT, U, KSPLIT, F8>(pb, lds, pb.n_coop);
 }
 
 // Tiled (prefill): the BN weight rows of an n-block are BN/2 intermediate

@@ -179,7 +179,7 @@ __device__ __forceinline__ void stream_consume(const StreamStage<NMAT, MT, U, F8
 // with W_m the scaled weights for FP8.
 // lds_all: StreamLds<NMAT, MT, U, KSPLIT>::kBytes bytes, 16-byte aligned.
 template <int NMAT, int MT, int U, int KSPLIT, bool F8, class P>
-__device__ __forceinline__ void stream_run(P& prob, unsigned char* lds_all) {
+__device__ __forceinline__ void stream_run(P& prob, unsigned char* lds_all, long n0 = 0) {
   using Lds = StreamLds<NMAT, MT, U, KSPLIT>;
   using Stage = StreamStage<NMAT, MT, U, F8>;
   constexpr int GROUPS = kStreamWaves / KSPLIT;
@@ -191,16 +191,21 @@ __device__ __forceinline__ void stream_run(P& prob, unsigned char* lds_all) {
   auto red = [&](int w) { return reinterpret_cast<f32x4*>(lds_all + w * Lds::kWaveBytes); };
 
   // Items are dealt round-robin: the k-th item of workgroup b is b + G*k
-  // (G = gridDim.x), taken by group k % GROUPS in round k / GROUPS.  The whole
+  // (G = gridDim.x; less n0, see below), taken by group k % GROUPS in round
+  // k / GROUPS.  The whole
   // grid thus sweeps the item list front to back, so the weight blocks in
   // flight at any time are neighbours and spread evenly over the HBM
   // channels; with G a multiple of 8, item i always runs on XCD i % 8.
+  // n0 leading slots of the deal belong to cooperative items (run before by
+  // stream_coop_run); this workgroup's k-th slot is blockIdx.x + G*k.
   const long total = prob.total_items();
-  const long G = gridDim.x;
-  const long mine_n = total > long(blockIdx.x) ? (total - blockIdx.x + G - 1) / G : 0;
+  const long G = gridDim.x, b = blockIdx.x;
+  const long k0 = n0 > b ? (n0 - b + G - 1) / G : 0;
+  const long kend = n0 + total > b ? (n0 + total - b + G - 1) / G : 0;
+  const long mine_n = kend - k0;
   const long rounds = (mine_n + GROUPS - 1) / GROUPS;
   if (rounds <= 0) return;   // uniform across the workgroup
-  auto item_of = [&](long k) { return k < mine_n ? long(blockIdx.x) + G * k : -1L; };
+  auto item_of = [&](long k) { return k < mine_n ? b + G * (k0 + k) - n0 : -1L; };
 
   // this wave's chunk share [cb, ce) of an item with C chunks
   auto share = [&](const StreamItem<NMAT, MT>& it, int& cb, int& ce) {
@@ -310,6 +315,155 @@ __device__ __forceinline__ void stream_run(P& prob, unsigned char* lds_all) {
     cb = nb;
     ce = ne;
     item = nitem;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Cooperative items (bf16, 4 waves): several token tiles that read the same
+// weight block -- the shared experts' tiles -- are taken by one workgroup,
+// one tile per wave, so that the block is streamed once instead of once per
+// tile.  Each wave loads a quarter of the k chunks (the k split of
+// stream_run) and turns its chunk into the operand layout in its own LDS
+// region; after a barrier every wave multiplies the four regions' chunks
+// with its own token tile, and a second barrier frees the regions.  Every
+// wave thus accumulates its tile over the whole k range, with no reduction.
+//
+// Problem P provides, besides what stream_run needs:
+//   long coop_items() const
+//   bool decode_coop(long item, int w, int lane, StreamItem<NMAT, MT>& it)
+//        (weights of the item's block; token rows of the item's w-th tile;
+//         returns false when the item has no w-th tile: its rows are dummies)
+//   void epilogue_coop(long item, int w, const f32x4 (&acc)[NMAT][MT], int lane)
+// Cooperative items take the first coop_items() slots of the round-robin deal
+// (workgroup b: slots b, b + G, ...); stream_run then continues the deal.
+// ---------------------------------------------------------------------------
+
+template <int NMAT, int MT>
+struct CoopStage {
+  u32x4 w[NMAT][2];      // this wave's chunk of the block
+  u32x4 x[4][MT][2];     // own tile's token operands for the four waves' chunks
+};
+
+// Chunk range [cb, ce) of wave w's quarter of C chunks.
+__device__ __forceinline__ void coop_share(int C, int w, int& cb, int& ce) {
+  cb = C * w / 4;
+  ce = C * (w + 1) / 4;
+}
+
+// Chunk c of the item (segment-aware), clamped into [0, C).
+template <int NMAT, int MT>
+__device__ __forceinline__ void coop_load_w(CoopStage<NMAT, MT>& st, const StreamItem<NMAT, MT>& it,
+                                            int c, int lane) {
+  const int seg = c / it.cps, j = c - seg * it.cps;
+  const int wr = lane >> 3, wb = (lane & 7) * 16;
+#pragma unroll
+  for (int m = 0; m < NMAT; ++m) {
+    const unsigned char* p = it.w[m] + seg * it.w_seg + long(wr) * it.w_row + j * 128 + wb;
+    st.w[m][0] = ld16_stream(p);
+    st.w[m][1] = ld16_stream(p + 8 * it.w_row);
+  }
+}
+
+// Loads of step s: this wave's chunk cb_w + s, and the token operands of
+// every wave's chunk cb_r + s (clamped to the last chunk of each quarter;
+// quarters that ran out are skipped in consume).
+template <int NMAT, int MT>
+__device__ __forceinline__ void coop_issue(CoopStage<NMAT, MT>& st, const StreamItem<NMAT, MT>& it,
+                                           int C, int kw, int s, int lane) {
+  const int xk = (lane >> 4) * 8;
+  int cb, ce;
+  coop_share(C, kw, cb, ce);
+  coop_load_w(st, it, min(cb + s, max(ce - 1, 0)), lane);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    int rb, re;
+    coop_share(C, r, rb, re);
+    const int c = min(rb + s, max(re - 1, 0));
+    const int seg = c / it.cps, j = c - seg * it.cps;
+#pragma unroll
+    for (int b = 0; b < MT; ++b) {
+      const u16* q = it.x[b] + seg * it.x_seg + j * 64 + xk;
+      st.x[r][b][0] = ld16(q);
+      st.x[r][b][1] = ld16(q + 32);
+    }
+  }
+}
+
+template <int NMAT, int MT>
+__device__ __forceinline__ void coop_consume(const CoopStage<NMAT, MT>& st, int C, int kw, int s,
+                                             bool mine, unsigned char* lds_all, int wave_bytes,
+                                             int lane, f32x4 (&acc)[NMAT][MT]) {
+  const int wr = lane >> 3, wc = (lane & 7) * 8;
+  const int fr = lane & 15, fk = (lane >> 4) * 8;
+  int cb, ce;
+  coop_share(C, kw, cb, ce);
+  if (cb + s < ce) {
+    u16* own = reinterpret_cast<u16*>(lds_all + kw * wave_bytes);
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) {
+      u16* t = own + m * 16 * kLdsRow;
+      *reinterpret_cast<u32x4*>(t + wr * kLdsRow + wc) = st.w[m][0];
+      *reinterpret_cast<u32x4*>(t + (wr + 8) * kLdsRow + wc) = st.w[m][1];
+    }
+  }
+  __syncthreads();
+  if (mine) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      int rb, re;
+      coop_share(C, r, rb, re);
+      if (rb + s >= re) continue;
+      const u16* reg = reinterpret_cast<const u16*>(lds_all + r * wave_bytes);
+      u32x4 f[NMAT][2];
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) {
+        const u16* t = reg + m * 16 * kLdsRow;
+        f[m][0] = *reinterpret_cast<const u32x4*>(t + fr * kLdsRow + fk);
+        f[m][1] = *reinterpret_cast<const u32x4*>(t + fr * kLdsRow + 32 + fk);
+      }
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int b = 0; b < MT; ++b) {
+          acc[m][b] = mfma_bf16(f[m][0], st.x[r][b][0], acc[m][b]);
+          acc[m][b] = mfma_bf16(f[m][1], st.x[r][b][1], acc[m][b]);
+        }
+    }
+  }
+  __syncthreads();
+}
+
+// Runs this workgroup's cooperative items (KSPLIT = 4 launches, bf16).
+// lds_all: StreamLds<NMAT, MT, U, 4>::kBytes; wave_bytes: its kWaveBytes.
+template <int NMAT, int MT, class P>
+__device__ __forceinline__ void stream_coop_run(P& prob, unsigned char* lds_all, int wave_bytes) {
+  const int lane = threadIdx.x & 63;
+  const int kw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const long n = prob.coop_items();
+  const long G = gridDim.x;
+  for (long item = blockIdx.x; item < n; item += G) {
+    StreamItem<NMAT, MT> it;
+    const bool mine = prob.decode_coop(item, kw, lane, it);
+    const int C = it.nseg * it.cps;
+    int steps, e0;
+    coop_share(C, 3, e0, steps);
+    steps -= e0;   // the last quarter is the longest
+    f32x4 acc[NMAT][MT];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int b = 0; b < MT; ++b) acc[m][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    CoopStage<NMAT, MT> A, B;
+    coop_issue(A, it, C, kw, 0, lane);
+    for (int s = 0; s < steps; s += 2) {
+      coop_issue(B, it, C, kw, s + 1, lane);
+      coop_consume(A, C, kw, s, mine, lds_all, wave_bytes, lane, acc);
+      if (s + 1 < steps) {
+        coop_issue(A, it, C, kw, s + 2, lane);
+        coop_consume(B, C, kw, s + 1, mine, lds_all, wave_bytes, lane, acc);
+      }
+    }
+    if (mine) prob.epilogue_coop(item, kw, acc, lane);
   }
 }
 

@@ -99,6 +99,22 @@ def test_ragged_batches(T):
     check_output(y, y_ref, "bf16")
 
 
+@pytest.mark.parametrize("T", [60, 150])
+def test_shared_cooperative_tiles(T):
+    """Shared experts taken as cooperative items (one shared tile per wave of
+    a workgroup, the weight block streamed once): D = I = 1024 gives a 4-way
+    k split in both expert kernels; 60 tokens are 4 shared tiles (gate/up
+    cooperative, the last tile partial), 150 tokens 10 tiles (gate/up and
+    down cooperative; the last group has two tiles, so two waves hold none)."""
+    layer = small_layer("coop", D=1024, E=32, K=2, I=1024, S=2, I_s=256, keep=0.5)
+    x = small_x(layer, T, "coop")
+    note(f"[cooperative shared tiles] T={T}")
+    y, rt, _ = run_forward(device_layer(layer), x)
+    rt_ref, y_ref = oracle.forward(layer, x)
+    check_routing(rt, rt_ref, layer.cfg.E)
+    check_output(y, y_ref, "bf16")
+
+
 def test_empty_batch_is_noop():
     layer = small_layer("empty", D=64, E=8, K=2, I=64)
     dl = device_layer(layer)
