@@ -344,6 +344,7 @@ __device__ void build_plan(PlanSmem& sm, int T, int E, int tile_rows, int has_sh
 
 constexpr int kSelWaves = 16;
 constexpr int kSelTokPerWave = kSelBlock / kSelWaves;   // 4
+constexpr int kSelMergedMax = 16;   // largest batch whose selection builds the plan itself
 // Limits of the bitmap plan (LDS of its one workgroup).
 constexpr int kPlanWords = 4096;    // E * ceil(T / 64) bitmap words
 constexpr int kPlanPairs = 8192;    // T * K selections (above, the block-rank kernels are faster)
@@ -578,15 +579,21 @@ __global__ __launch_bounds__(NT) void k_plan_bitmap(SelectArgs a) {
 }
 
 // Multi-block form: one 1024-thread workgroup per 64-token block; each of its
-// 16 waves handles 4 tokens, with all four tokens' logits loaded before any
-// is processed.  Then, per block, the block-local rank of every surviving
+// 16 waves handles 4 tokens (wave w: tokens w, w + 16, w + 32, w + 48 of the
+// block, so that short batches use every wave), with all four tokens' logits
+// loaded before any is processed.  Then, per block, the block-local rank of every surviving
 // pair among the block's pairs of the same expert (token order) and the
 // block's per-expert pair counts.
-template <int NPER>
+//
+// PLAN (batches of at most 64 tokens, one workgroup): the block's token
+// bitmaps are the whole batch's, so the same workgroup then builds the plan
+// from them, as k_plan_bitmap does, instead of recording block ranks.
+template <int NPER, bool PLAN>
 __global__ __launch_bounds__(1024) void k_select(SelectArgs a) {
   __shared__ unsigned long long bits[kMaxExperts];
   __shared__ int32_t s_idx[kSelBlock * 32];
   __shared__ uint32_t s_mask[kSelBlock];
+  __shared__ PlanSmem s_plan[1];   // used by the PLAN form only
   constexpr int TPW = kSelTokPerWave;
   constexpr int KB = NPER >= 4 ? 1 : 4 / NPER;   // partial slices loaded per round
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -607,7 +614,7 @@ __global__ __launch_bounds__(1024) void k_select(SelectArgs a) {
     for (int u = 0; u < KB; ++u)
 #pragma unroll
       for (int j = 0; j < TPW; ++j) {
-        const int t = t0 + wave * TPW + j;
+        const int t = t0 + j * kSelWaves + wave;
 #pragma unroll
         for (int i = 0; i < NPER; ++i) {
           const int e = lane + kWave * i;
@@ -649,7 +656,7 @@ __global__ __launch_bounds__(1024) void k_select(SelectArgs a) {
   constexpr int IL = NPER <= 4 ? TPW : 1;
 #pragma unroll
   for (int j0 = 0; j0 < TPW; j0 += IL) {
-    if (t0 + wave * TPW + j0 >= T) break;   // no valid token left in this wave
+    if (t0 + j0 * kSelWaves + wave >= T) break;   // no valid token left in this wave
     float vals[IL][NPER];
 #pragma unroll
     for (int jj = 0; jj < IL; ++jj)
@@ -692,7 +699,7 @@ __global__ __launch_bounds__(1024) void k_select(SelectArgs a) {
     }
 #pragma unroll
     for (int jj = 0; jj < IL; ++jj) {
-      const int tl = wave * TPW + j0 + jj;
+      const int tl = (j0 + jj) * kSelWaves + wave;
       const int t = t0 + tl;
       if (t >= T) break;
       const bool slot = lane < K;
@@ -727,19 +734,36 @@ __global__ __launch_bounds__(1024) void k_select(SelectArgs a) {
   }
   __syncthreads();
 
-  for (int q = tid; q < kSelBlock * K; q += blockDim.x) {
-    const int tl = q / K, k = q % K;
-    const int t = t0 + tl;
-    if (t >= T) continue;
-    int rk = -1;
-    if ((s_mask[tl] >> k) & 1u) {
-      const int e = s_idx[tl * 32 + k];
-      rk = __popcll(bits[e] & ((1ull << tl) - 1ull));
+  if constexpr (PLAN) {
+    PlanSmem& pl = s_plan[0];
+    for (int e = tid; e < E; e += blockDim.x) pl.cnt[e] = __popcll(bits[e]);
+    __syncthreads();
+    build_plan<1024>(pl, T, E, a.tile_rows, a.has_shared, a.counts, a.expert_off, a.plan, a.tiles);
+    for (int q = tid; q < T * K; q += blockDim.x) {
+      const int tl = q / K, k = q - tl * K;
+      int pos = -1;
+      if ((s_mask[tl] >> k) & 1u) {
+        const int e = s_idx[tl * 32 + k];
+        pos = pl.off[e] + __popcll(bits[e] & ((1ull << tl) - 1ull));
+        a.perm_token[pos] = tl;
+      }
+      a.slot_pos[q] = pos;
     }
-    a.rank[size_t(t) * K + k] = rk;
+  } else {
+    for (int q = tid; q < kSelBlock * K; q += blockDim.x) {
+      const int tl = q / K, k = q % K;
+      const int t = t0 + tl;
+      if (t >= T) continue;
+      int rk = -1;
+      if ((s_mask[tl] >> k) & 1u) {
+        const int e = s_idx[tl * 32 + k];
+        rk = __popcll(bits[e] & ((1ull << tl) - 1ull));
+      }
+      a.rank[size_t(t) * K + k] = rk;
+    }
+    for (int e = tid; e < E; e += blockDim.x)
+      a.block_counts[size_t(blk) * E + e] = __popcll(bits[e]);
   }
-  for (int e = tid; e < E; e += blockDim.x)
-    a.block_counts[size_t(blk) * E + e] = __popcll(bits[e]);
 }
 
 hipError_t launch_select(const beam_moe_layer& L, int32_t T, int tile_rows, const Ptrs& p,
@@ -769,6 +793,18 @@ hipError_t launch_select(const beam_moe_layer& L, int32_t T, int tile_rows, cons
   a.tiles = p.tiles;
   a.perm_token = p.perm_token;
   a.slot_pos = p.slot_pos;
+  // Up to 16 tokens one workgroup selects and plans: one launch fewer (T = 1:
+  // 13.4 -> 9.6 us for both steps on MI355X).  From 32 tokens on, selecting
+  // in one workgroup costs more than the second launch saves.
+  if (T <= kSelMergedMax) {
+    prof_before("select_plan", s);
+    if (L.E <= 64) hipLaunchKernelGGL((k_select<1, true>), dim3(1), dim3(1024), 0, s, a);
+    else if (L.E <= 128) hipLaunchKernelGGL((k_select<2, true>), dim3(1), dim3(1024), 0, s, a);
+    else if (L.E <= 256) hipLaunchKernelGGL((k_select<4, true>), dim3(1), dim3(1024), 0, s, a);
+    else hipLaunchKernelGGL((k_select<16, true>), dim3(1), dim3(1024), 0, s, a);
+    prof_after(s);
+    return hipGetLastError();
+  }
   if (select_builds_plan(L, T)) {
     constexpr int nt = kSelThreads;
     const dim3 g{unsigned((T + nt / kWave - 1) / (nt / kWave)), 1, 1}, b{unsigned(nt), 1, 1};
@@ -787,10 +823,10 @@ hipError_t launch_select(const beam_moe_layer& L, int32_t T, int tile_rows, cons
   const int nblk = (T + kSelBlock - 1) / kSelBlock;
   const dim3 g{unsigned(nblk), 1, 1}, b{1024, 1, 1};
   prof_before("select_topk_mask", s);
-  if (L.E <= 64) hipLaunchKernelGGL(k_select<1>, g, b, 0, s, a);
-  else if (L.E <= 128) hipLaunchKernelGGL(k_select<2>, g, b, 0, s, a);
-  else if (L.E <= 256) hipLaunchKernelGGL(k_select<4>, g, b, 0, s, a);
-  else hipLaunchKernelGGL(k_select<16>, g, b, 0, s, a);
+  if (L.E <= 64) hipLaunchKernelGGL((k_select<1, false>), g, b, 0, s, a);
+  else if (L.E <= 128) hipLaunchKernelGGL((k_select<2, false>), g, b, 0, s, a);
+  else if (L.E <= 256) hipLaunchKernelGGL((k_select<4, false>), g, b, 0, s, a);
+  else hipLaunchKernelGGL((k_select<16, false>), g, b, 0, s, a);
   prof_after(s);
   return hipGetLastError();
 }

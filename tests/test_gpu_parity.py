@@ -200,11 +200,12 @@ def test_gate_options_on_workload():
 
 
 @pytest.mark.parametrize("seg,flags", [(16, 0), (32, 4), (16, 6), (7, 2)])
-@pytest.mark.parametrize("T", [37, 4200])
+@pytest.mark.parametrize("T", [13, 37, 4200])
 def test_segment_routing(seg, flags, T):
     """Segment routing (every token routes as its segment's first token), with
     the method's gate, binary gates, binary + renormalised and renormalised
-    gates; one-wave-per-token selection (37 tokens) and 64-token blocks (4200)."""
+    gates; selection and plan in one workgroup (13 tokens), one-wave-per-token
+    selection (37) and 64-token blocks (4200)."""
     from oracle_pins import with_segment
     base = small_layer("segment", D=128, E=40, K=6, I=64, S=1, I_s=64, keep=0.4, router_bias=True)
     layer = with_segment(base, seg, flags)
@@ -262,10 +263,11 @@ def _mask_backward_case(layer, x, beta, seed, dev=None):
     return dwm, dbm
 
 
-@pytest.mark.parametrize("T", [37, 4200])
+@pytest.mark.parametrize("T", [5, 37, 4200])
 def test_mask_backward_small(T):
-    """Mask-router loss value and straight-through gradient, one-wave-per-token
-    selection (37 tokens) and the 64-token-block one (4200)."""
+    """Mask-router loss value and straight-through gradient: selection and
+    plan in one workgroup (5 tokens), one-wave-per-token selection (37) and
+    the 64-token-block one (4200)."""
     layer = small_layer("mbwd", D=128, E=40, K=6, I=64, S=1, I_s=64, keep=0.4, router_bias=True)
     x = small_x(layer, T, "mbwd")
     note(f"[mask backward] small T={T}")
