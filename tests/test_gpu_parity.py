@@ -115,6 +115,22 @@ def test_shared_cooperative_tiles(T):
     check_output(y, y_ref, "bf16")
 
 
+@pytest.mark.parametrize("D", [128, 192])
+def test_wide_tiles(D):
+    """256-row tiles (the prefill kernels' tallest): 2100 tokens, 8 experts, top-2
+    (525 candidates per expert); D = 128 and 192 give an even and an odd number
+    of 64-wide k slices; I = 192 leaves the second 128-row block of
+    intermediate rows half empty; the shared expert's last token tile is
+    partial."""
+    layer = small_layer(f"wide{D}", D=D, E=8, K=2, I=192, S=1, I_s=128, keep=0.8)
+    x = small_x(layer, 2100, "wide")
+    note(f"[wide tiles] D={D}")
+    y, rt, _ = run_forward(device_layer(layer), x)
+    rt_ref, y_ref = oracle.forward(layer, x)
+    check_routing(rt, rt_ref, layer.cfg.E)
+    check_output(y, y_ref, "bf16")
+
+
 def test_empty_batch_is_noop():
     layer = small_layer("empty", D=64, E=8, K=2, I=64)
     dl = device_layer(layer)
