@@ -131,6 +131,21 @@ def test_wide_tiles(D):
     check_output(y, y_ref, "bf16")
 
 
+@pytest.mark.parametrize("fp8", [False, True])
+def test_max_hidden_size(fp8):
+    """The largest supported hidden size, D = 16384 (router k split, 256-chunk
+    weight rows, shared expert), bf16 and FP8 expert weights."""
+    from oracle_pins import fp8_layer
+    kw = dict(D=16384, E=6, K=2, I=128, S=1, I_s=128, keep=0.6)
+    layer = fp8_layer("maxd", **kw) if fp8 else small_layer("maxd", **kw)
+    x = small_x(layer, 40, "maxd")
+    note(f"[max D] fp8={fp8}")
+    y, rt, _ = run_forward(device_layer(layer), x)
+    rt_ref, y_ref = oracle.forward(layer, x)
+    check_routing(rt, rt_ref, layer.cfg.E)
+    check_output(y, y_ref, "bf16")
+
+
 def test_empty_batch_is_noop():
     layer = small_layer("empty", D=64, E=8, K=2, I=64)
     dl = device_layer(layer)
