@@ -37,14 +37,15 @@ __device__ __forceinline__ void router_store(const RouterArgs& a, int ks, int t,
   a.part[(size_t(ks) * a.T + t) * 2 * a.E + j] = v;
 }
 
-template <int MT>
+// NM groups of 16 router rows (rows j0 .. j0 + 16 NM) x 16*MT token rows.
+template <int NM, int MT>
 struct RouterSkinnyProv {
   const RouterArgs* a;
   int j0, t0, k0;   // k0: first element of this k slice
   __device__ int nseg() const { return 1; }
   __device__ int seg_chunks() const { return a->D / 64 / a->KS; }
-  __device__ const u16* w(int, int r, int) const {
-    const u16* p = router_row(*a, j0 + r);
+  __device__ const u16* w(int g, int r, int) const {
+    const u16* p = router_row(*a, j0 + 16 * g + r);
     return p ? p + k0 : nullptr;
   }
   __device__ const u16* x(int r, int) const {
@@ -54,42 +55,57 @@ struct RouterSkinnyProv {
 };
 
 // The skinny router handles small batches and layers with few experts (whose
-// 2E router rows would waste most of a tiled weight block); its token tile is
-// 16*MT rows, chosen so that the grid has enough workgroups.
+// 2E router rows would waste most of a tiled weight block).  A workgroup
+// takes NM groups of 16 router rows x 16*MT tokens x one k slice.  Small
+// batches use one row group and split k so that the router's weight rows
+// stream through many CUs; from 2048 tokens on, four row groups share each
+// token-row load (the token rows, not the weights, are then the traffic:
+// T = 4096, E = 64: 26.8 -> 21.8 us on MI355X; at 256 tokens the smaller grid
+// costs more than the re-reads).
 constexpr int kRouterSkinnyMaxT = 1024;
 __host__ __device__ inline bool router_use_skinny(int T, int E) { return T <= kRouterSkinnyMaxT || E <= 64; }
+__host__ __device__ inline int router_nm(int T, int E) { return T >= 2048 && 2 * E >= 64 ? 4 : 1; }
 __host__ __device__ inline int router_mt(int T, int E) {
-  const int nrb = (2 * E + 15) / 16;
+  const int nrb = (2 * E + 16 * router_nm(T, E) - 1) / (16 * router_nm(T, E));
   if (T <= 16) return 1;
   if (T <= 32) return 2;
-  return long(nrb) * ((T + 63) / 64) >= 256 ? 4 : 1;
+  if (long(nrb) * ((T + 63) / 64) >= 256) return 4;
+  if (long(nrb) * ((T + 31) / 32) >= 256) return 2;
+  return 1;
 }
 
-// One workgroup per (16*MT tokens) x (16 router rows) x (k slice); 4 waves
-// split the slice.
-template <int MT>
-__global__ __launch_bounds__(256) void k_router_skinny(RouterArgs a) {
-  __shared__ f32x4 red[4 * MT * kWave];
+// red: 4 * NM * MT * 64 f32x4 of LDS.
+template <int NM, int MT>
+__device__ __forceinline__ void router_skinny_block(const RouterArgs& a, int blk, f32x4* red) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nrb = (2 * a.E + 15) / 16;
-  const int ks = blockIdx.x % a.KS;
-  const int rest = blockIdx.x / a.KS;
-  const int j0 = (rest % nrb) * 16;
+  const int nrb = (2 * a.E + 16 * NM - 1) / (16 * NM);
+  const int ks = blk % a.KS;
+  const int rest = blk / a.KS;
+  const int j0 = (rest % nrb) * 16 * NM;
   const int t0 = (rest / nrb) * 16 * MT;
-  RouterSkinnyProv<MT> pv{&a, j0, t0, ks * (a.D / a.KS)};
-  f32x4 acc[1][MT];
-  skinny_accumulate<1, MT, (MT >= 4 ? 1 : 4 / MT)>(pv, lane, wave, 4, acc);
-  skinny_reduce<1, MT>(acc, red, lane, wave, 4);
-  // wave w stores the M tiles mt with mt % 4 == w
-  for (int mt = wave; mt < MT; mt += 4) {
+  RouterSkinnyProv<NM, MT> pv{&a, j0, t0, ks * (a.D / a.KS)};
+  f32x4 acc[NM][MT];
+  skinny_accumulate<NM, MT, (NM * MT >= 4 ? 1 : 4 / (NM * MT))>(pv, lane, wave, 4, acc);
+  skinny_reduce<NM, MT>(acc, red, lane, wave, 4);
+  // wave w stores the (row group, token block) pairs q with q % 4 == w
+  for (int q = wave; q < NM * MT; q += 4) {
     f32x4 v = acc[0][0];
 #pragma unroll
-    for (int b = 0; b < MT; ++b)
-      if (b == mt) v = acc[0][b];
-    const int t = t0 + 16 * mt + (lane & 15);
+    for (int g = 0; g < NM; ++g)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) router_store(a, ks, t, j0 + 4 * (lane >> 4) + i, v[i]);
+      for (int b = 0; b < MT; ++b)
+        if (g * MT + b == q) v = acc[g][b];
+    const int t = t0 + 16 * (q % MT) + (lane & 15);
+    const int j = j0 + 16 * (q / MT) + 4 * (lane >> 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) router_store(a, ks, t, j + i, v[i]);
   }
+}
+
+template <int NM, int MT>
+__global__ __launch_bounds__(256) void k_router_skinny(RouterArgs a) {
+  __shared__ f32x4 red[4 * NM * MT * kWave];
+  router_skinny_block<NM, MT>(a, blockIdx.x, red);
 }
 
 constexpr int kRouterBN = 64, kRouterBM = 256;
@@ -174,8 +190,8 @@ int router_ksplit(const beam_moe_layer& L, int32_t T) {
   // Split k (at most 4 ways, so that selection reads at most 4 partial sums
   // per logit) when the (row block x token block) grid is small.
   const int chunks = L.D / 64;
-  const int mt = router_mt(T, L.E);
-  const long blocks = long((2 * L.E + 15) / 16) * ((T + 16 * mt - 1) / (16 * mt));
+  const int nm = router_nm(T, L.E), mt = router_mt(T, L.E);
+  const long blocks = long((2 * L.E + 16 * nm - 1) / (16 * nm)) * ((T + 16 * mt - 1) / (16 * mt));
   int best = 1;
   for (int ks = 2; ks <= 4; ++ks)
     if (chunks % ks == 0 && chunks / ks >= 4 && blocks * (ks - 1) < 256) best = ks;
@@ -197,14 +213,20 @@ hipError_t launch_router_logits(const beam_moe_layer& L, const void* x, int32_t 
   const int KS = router_ksplit(L, T);
   RouterArgs a{(const u16*)x, (const u16*)L.w_router, (const u16*)L.w_mask, part, T, L.D, L.E, KS};
   if (router_use_skinny(T, L.E)) {
-    const int nrb = (2 * L.E + 15) / 16;
-    const int mt = router_mt(T, L.E);
+    const int nm = router_nm(T, L.E), mt = router_mt(T, L.E);
+    const int nrb = (2 * L.E + 16 * nm - 1) / (16 * nm);
     const int ntb = (T + 16 * mt - 1) / (16 * mt);
     const dim3 grid(unsigned(nrb * ntb * KS));
     prof_before("router_logits_skinny", s);
-    if (mt == 1) hipLaunchKernelGGL(k_router_skinny<1>, grid, dim3(256), 0, s, a);
-    else if (mt == 2) hipLaunchKernelGGL(k_router_skinny<2>, grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(k_router_skinny<4>, grid, dim3(256), 0, s, a);
+    if (nm == 4) {
+      if (mt == 1) hipLaunchKernelGGL((k_router_skinny<4, 1>), grid, dim3(256), 0, s, a);
+      else if (mt == 2) hipLaunchKernelGGL((k_router_skinny<4, 2>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((k_router_skinny<4, 4>), grid, dim3(256), 0, s, a);
+    } else {
+      if (mt == 1) hipLaunchKernelGGL((k_router_skinny<1, 1>), grid, dim3(256), 0, s, a);
+      else if (mt == 2) hipLaunchKernelGGL((k_router_skinny<1, 2>), grid, dim3(256), 0, s, a);
+      else hipLaunchKernelGGL((k_router_skinny<1, 4>), grid, dim3(256), 0, s, a);
+    }
     prof_after(s);
   } else {
     const int nrb = (L.E + kRouterBN - 1) / kRouterBN;
