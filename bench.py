@@ -18,7 +18,8 @@ mean launch time from hipEvents recorded around each launch on the call's
 stream during a second timed pass.  `cpu_baseline` times the float64 oracle
 on the host on a bounded sample of the same workload.  `fp8_weights` reports
 the same decode layer with its expert weights stored as OCP FP8 E4M3 codes
-with fp32 row scales (same batch size, same timing method).
+with fp32 row scales (same batch size, same timing method); `prefill` the
+same layer shapes at T=4096 with its MFMA fraction of the bf16 peak.
 """
 from __future__ import annotations
 
@@ -57,6 +58,8 @@ def parse():
     p.add_argument("--gating", type=int, default=None, help="gate option bits (default: the config's)")
     p.add_argument("--zero-mask", action="store_true",
                    help="zero mask router (every top-K candidate kept: plain top-K routing)")
+    p.add_argument("--no-prefill", action="store_true",
+                   help="skip the prefill figure (DeepSeek-V2-Lite-shaped layer, T=4096)")
     p.add_argument("--no-fp8", action="store_true",
                    help="skip the FP8 (E4M3) expert-weight variant of the decode layer")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -251,13 +254,34 @@ def main():
         del reps8, dl8
         torch.cuda.empty_cache()
 
+    # prefill: the same layer shapes at T=4096 (high sparsity, router-bias skew)
+    prefill = None
+    if (args.config == "dsv2lite_decode" and not args.no_prefill and not args.segment
+            and args.gating is None and not args.zero_mask):
+        reps = dl = None
+        torch.cuda.empty_cache()
+        cp = synth.CONFIGS["dsv2lite_prefill"]
+        Tp = cp.tokens[-1]
+        _, dlp, repsp, _ = setup(cp)
+        r = run_T(cp, dlp, repsp, Tp, max(5, args.steps // 5), 2, profile=False)
+        sec = r["ms_per_step"] / 1e3
+        prefill = {"workload": f"{cp.name}: D={cp.D} E={cp.E} K={cp.K} I={cp.I} shared={cp.S}x{cp.I_s} "
+                               f"T={Tp}, router bias N(0,1)",
+                   "tokens_per_s": round(Tp / sec, 1), "ms_per_step": round(r["ms_per_step"], 4),
+                   "avg_k": round(r["avg_k"], 3),
+                   "mfma_frac_peak": round(r["flops_per_step"] / sec / 1e12 / BF16_PEAK_TFLOPS, 4),
+                   "hbm_gbs": round(r["bytes_per_step"] / sec / 1e9, 1),
+                   "flops_per_step": r["flops_per_step"]}
+        del repsp, dlp
+        torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(cfg, host, T, args)
 
     layer_gbs = main_res["bytes_per_step"] / (ms / 1e3) / 1e9
     out = {
-        "metric": "masked-MoE layer tokens/s (decode: HBM GB/s on active-expert bytes)",
+        "metric": "masked-MoE layer tokens/s; decode HBM GB/s, prefill MFMA % of peak",
         "value": round(value, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -287,6 +311,7 @@ def main():
         "cpu_baseline": cpu,
         "sweep": sweep,
         "fp8_weights": fp8,
+        "prefill": prefill,
     }
     print(json.dumps(out), flush=True)
 
