@@ -98,7 +98,7 @@ def read_traffic(workload: str, kernel: str = DOMINANT):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
 
     import numpy as np
