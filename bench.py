@@ -58,6 +58,10 @@ def parse():
     p.add_argument("--gating", type=int, default=None, help="gate option bits (default: the config's)")
     p.add_argument("--zero-mask", action="store_true",
                    help="zero mask router (every top-K candidate kept: plain top-K routing)")
+    p.add_argument("--mask-backward", action="store_true",
+                   help="time the mask-router training step (beam_moe_mask_backward) instead of the forward")
+    p.add_argument("--no-next", action="store_true",
+                   help="skip the gate-option and mask-backward timings of the decode layer")
     p.add_argument("--no-prefill", action="store_true",
                    help="skip the prefill figure (DeepSeek-V2-Lite-shaped layer, T=4096)")
     p.add_argument("--no-fp8", action="store_true",
@@ -151,20 +155,32 @@ def main():
         elt = 4 if c.dtype == "f32" else 2
         return 2 * c.D * c.I * elt * active + 2 * c.D * c.I_s * elt * c.S
 
-    def run_T(c, dl, reps, Tb: int, steps: int, warmup: int, profile: bool):
+    def run_T(c, dl, reps, Tb: int, steps: int, warmup: int, profile: bool, backward: bool = False):
         xs = [to_device(synth.make_x(c, Tb, f"bench{i}"), dev) for i in range(args.pool)]
         y = torch.empty(Tb, c.D, dtype=dl.torch_dtype, device=dev)
         ws = dl.workspace(Tb)
         # per-batch work accounting (outside any timed region)
-        stats = []
+        stats, cand = [], []
         for i in range(args.pool):
             bufs, out = dl.route_buffers(Tb)
             dm.beam_moe_route(dl.desc, xs[i], Tb, out, ws, ws.numel(), sh)
             stats.append(dm.beam_moe_stats(dl.desc, bufs["expert_count"], Tb, sh))
+            cand.append(int(torch.unique(bufs["topk_idx"]).numel()))   # experts with a candidate
+
+        if backward:
+            # dL/dy of the task loss: a seeded batch of the same shape as y
+            dys = [to_device(synth.make_x(c, Tb, f"dy{i}"), dev) for i in range(args.pool)]
+            dwm = torch.empty(c.E, c.D, dtype=torch.float32, device=dev)
+            dbm = torch.empty(c.E, dtype=torch.float32, device=dev)
+            lreg = torch.empty(1, dtype=torch.float32, device=dev)
 
         def step(i):
             _, desc = reps[i % len(reps)]
-            dm.beam_moe_forward(desc, xs[i % args.pool], Tb, y, None, ws, ws.numel(), sh)
+            if backward:
+                dm.beam_moe_mask_backward(desc, xs[i % args.pool], dys[i % args.pool], Tb, 0.1, dwm,
+                                          dbm, lreg, ws, ws.numel(), sh)
+            else:
+                dm.beam_moe_forward(desc, xs[i % args.pool], Tb, y, None, ws, ws.numel(), sh)
 
         for i in range(warmup):
             step(i)
@@ -182,6 +198,14 @@ def main():
                                                for s in used]))
         res["avg_k"] = float(np.mean([s["avg_k"] for s in used]))
         res["active_experts"] = float(np.mean([s["active_experts"] for s in used]))
+        if backward:
+            # every top-K candidate runs its expert (the shared experts do not enter)
+            elt = 4 if c.dtype == "f32" else 2
+            ce = [cand[(warmup + i) % args.pool] for i in range(steps)]
+            res["candidate_experts"] = float(np.mean(ce))
+            res["bytes_per_step"] = float(np.mean([3 * c.D * c.I * elt * n for n in ce])
+                                          + 2 * c.E * c.D * elt + 2 * Tb * c.D * elt)
+            res["flops_per_step"] = 6.0 * c.D * c.I * Tb * c.K + 4.0 * c.E * c.D * Tb
         if profile:
             # second timed pass with a hipEvent pair around every launch
             dm.beam_profile_begin(steps * 16)
@@ -192,12 +216,18 @@ def main():
             prof = dm.beam_profile_end(64)
             res["kernels"] = {k: {"launches": n, "mean_us": ms * 1e3 / max(n, 1)}
                               for k, (n, ms) in prof.items()}
-            res["gate_up_alg_bytes"] = float(np.mean([gate_up_bytes(c, s["active_experts"])
-                                                      for s in used]))
+            if backward:
+                elt = 4 if c.dtype == "f32" else 2
+                res["gate_up_alg_bytes"] = float(np.mean(
+                    [2 * c.D * c.I * elt * cand[(warmup + i) % args.pool] for i in range(steps)]))
+            else:
+                res["gate_up_alg_bytes"] = float(np.mean([gate_up_bytes(c, s["active_experts"])
+                                                          for s in used]))
         return res
 
     host, dl, reps, copies = setup(cfg)
-    main_res = run_T(cfg, dl, reps, T, args.steps, args.warmup, profile=True)
+    main_res = run_T(cfg, dl, reps, T, args.steps, args.warmup, profile=True,
+                     backward=args.mask_backward)
     ms = main_res["ms_per_step"]
     value = T / (ms / 1e3)
 
@@ -207,7 +237,7 @@ def main():
         kname = dom[0]
         mean_us = main_res["kernels"][kname]["mean_us"]
         achieved = main_res["gate_up_alg_bytes"] / (mean_us * 1e-6) / 1e9
-        workload = f"{cfg.name}_T{T}"
+        workload = f"{cfg.name}_T{T}" + ("_mask_backward" if args.mask_backward else "")
         traffic = read_traffic(workload)
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -225,10 +255,32 @@ def main():
                           "layer_hbm_gbs": round(r["bytes_per_step"] / (r["ms_per_step"] / 1e3) / 1e9, 1),
                           "avg_k": round(r["avg_k"], 3)})
 
+    # the gate options and the mask-router training step on the same layer and batch
+    nxt = None
+    plain = not (args.segment or args.gating is not None or args.zero_mask or args.mask_backward)
+    if args.config == "dsv2lite_decode" and plain and not args.no_next:
+        nsteps = max(10, args.steps // 2)
+        nxt = {"gate_options_ms_per_step": {}}
+        for g in (dm.GATE_SOFTMAX_ALL, dm.GATE_RENORM, dm.GATE_BINARY, dm.GATE_BINARY | dm.GATE_RENORM):
+            for _, d in reps:
+                d.gating = g
+            r = run_T(cfg, dl, reps, T, nsteps, args.warmup, profile=False)
+            nxt["gate_options_ms_per_step"][str(g)] = round(r["ms_per_step"], 4)
+        for _, d in reps:
+            d.gating = cfg.gating
+        r = run_T(cfg, dl, reps, T, nsteps, args.warmup, profile=True, backward=True)
+        sec = r["ms_per_step"] / 1e3
+        nxt["mask_backward"] = {
+            "what": "beam_moe_mask_backward: L_reg and straight-through dL/dWm, dL/db_m; "
+                    "every top-K candidate runs its expert",
+            "tokens_per_s": round(T / sec, 1), "ms_per_step": round(r["ms_per_step"], 4),
+            "candidate_experts": round(r["candidate_experts"], 2),
+            "hbm_gbs": round(r["bytes_per_step"] / sec / 1e9, 1),
+            "kernels_mean_us": {k: round(v["mean_us"], 2) for k, v in r["kernels"].items()}}
+
     # the same decode layer with FP8 (E4M3) expert weights, same batch size
     fp8 = None
-    if (args.config == "dsv2lite_decode" and not args.no_fp8 and not args.segment
-            and args.gating is None and not args.zero_mask):
+    if args.config == "dsv2lite_decode" and not args.no_fp8 and plain:
         del reps
         dl = None
         torch.cuda.empty_cache()
@@ -256,8 +308,7 @@ def main():
 
     # prefill: the same layer shapes at T=4096 (high sparsity, router-bias skew)
     prefill = None
-    if (args.config == "dsv2lite_decode" and not args.no_prefill and not args.segment
-            and args.gating is None and not args.zero_mask):
+    if args.config == "dsv2lite_decode" and not args.no_prefill and plain:
         reps = dl = None
         torch.cuda.empty_cache()
         cp = synth.CONFIGS["dsv2lite_prefill"]
@@ -298,7 +349,8 @@ def main():
                                + (" expert weights E4M3" if cfg.expert_format == synth.FP8 else "")
                                + (f" segment={cfg.segment}" if cfg.segment > 1 else "")
                                + (f" gating={cfg.gating}" if cfg.gating else "")
-                               + (" mask router zero" if args.zero_mask else ""),
+                               + (" mask router zero" if args.zero_mask else "")
+                               + (" mask-router backward step" if args.mask_backward else ""),
                    "tokens": T, "weight_copies": copies, "input_pool": args.pool},
         "layer": {"avg_k": round(main_res["avg_k"], 3),
                   "active_experts": round(main_res["active_experts"], 2),
@@ -310,6 +362,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "sweep": sweep,
+        "next_rows": nxt,
         "fp8_weights": fp8,
         "prefill": prefill,
     }
@@ -332,14 +385,18 @@ def cpu_baseline(cfg, host, T, args):
     batches = 0
     while time.perf_counter() - t0 < args.cpu_seconds:
         x = synth.make_x(cfg, T, f"bench{batches % args.pool}")
-        oracle.forward(host, x)
+        if args.mask_backward:
+            dy = oracle.widen(synth.make_x(cfg, T, f"dy{batches % args.pool}"), cfg.dtype)
+            oracle.mask_router_backward(host, x, dy, 0.1)
+        else:
+            oracle.forward(host, x)
         done += T
         batches += 1
     el = time.perf_counter() - t0
     return {"value": round(done / el, 2), "unit": "tokens/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{batches} whole batches of T={T} ({done} tokens) of the same workload, "
-                      f"float64 numpy, {el:.1f}s"}
+                      f"{'mask-router backward, ' if args.mask_backward else ''}float64 numpy, {el:.1f}s"}
 
 
 if __name__ == "__main__":
