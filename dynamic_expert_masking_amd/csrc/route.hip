@@ -616,8 +616,12 @@ __global__ __launch_bounds__(1024) void k_select(SelectArgs a) {
   __shared__ int32_t s_idx[kSelBlock * 32];
   __shared__ uint32_t s_mask[kSelBlock];
   __shared__ PlanSmem s_plan[1];   // used by the PLAN form only
-  constexpr int TPW = kSelTokPerWave;
-  constexpr int KB = NPER >= 4 ? 1 : 4 / NPER;   // partial slices loaded per round
+  // PLAN batches have at most kSelWaves tokens: one per wave, so no wave
+  // carries empty token slots through the top-K rounds, and the (at most 4)
+  // partial-sum slices of its token are loaded in one round.
+  constexpr int TPW = PLAN ? 1 : kSelTokPerWave;
+  constexpr int KB = NPER >= 16 ? 1 : PLAN ? 4 : (NPER >= 4 ? 1 : 4 / NPER);
+  static_assert(!PLAN || kSelMergedMax <= kSelWaves, "PLAN: one token per wave");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int blk = blockIdx.x;
   const int t0 = blk * kSelBlock;
