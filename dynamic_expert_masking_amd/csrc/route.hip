@@ -862,28 +862,69 @@ hipError_t launch_select(const beam_moe_layer& L, int32_t T, int tile_rows, cons
 // exclusive offsets, then the plan.
 // ---------------------------------------------------------------------------
 
+constexpr int kScanVals = 32;   // block counts per thread held in registers by k_scan
+
 __global__ __launch_bounds__(1024) void k_scan(int T, int E, int nblk, int tile_rows,
                                                int has_shared, int32_t* __restrict__ block_counts,
                                                int32_t* __restrict__ counts,
                                                int32_t* __restrict__ expert_off,
                                                Plan* __restrict__ plan, Tile* __restrict__ tiles) {
   __shared__ PlanSmem psm;
+  __shared__ int32_t s_part[1024];
   const int tid = threadIdx.x;
-  for (int e = tid; e < E; e += 1024) {
-    // exclusive running sum over blocks, 8 independent loads at a time
-    int32_t run = 0;
-    for (int b0 = 0; b0 < nblk; b0 += 8) {
-      int32_t c[8];
+  // G threads per expert (the largest power of two with G * E <= 1024, at
+  // most 64), each holding up to kScanVals consecutive block counts of its
+  // expert in registers: thread (part, e) = (tid / E, tid % E) owns blocks
+  // [part * per, part * per + per).  Its sum goes to LDS, and the sums of the
+  // earlier parts give its running offset.  A thread's loads are independent,
+  // so it waits for memory about once.
+  int G = 1;
+  while (2 * G * E <= 1024 && G < 64) G *= 2;
+  const int per = (nblk + G - 1) / G;
+  if (per <= kScanVals) {
+    const int part = tid / E, e = tid - part * E;
+    const bool act = part < G;
+    const int b0 = part * per;
+    int32_t c[kScanVals];
+    int32_t sum = 0;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) c[u] = b0 + u < nblk ? block_counts[size_t(b0 + u) * E + e] : 0;
+    for (int u = 0; u < kScanVals; ++u) {
+      const int b = b0 + u;
+      c[u] = (act && u < per && b < nblk) ? block_counts[size_t(b) * E + e] : 0;
+      sum += c[u];
+    }
+    if (act) s_part[part * E + e] = sum;
+    __syncthreads();
+    if (act) {
+      int32_t run = 0;
+      for (int q = 0; q < part; ++q) run += s_part[q * E + e];
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (b0 + u < nblk) {
-          block_counts[size_t(b0 + u) * E + e] = run;
+      for (int u = 0; u < kScanVals; ++u) {
+        const int b = b0 + u;
+        if (u < per && b < nblk) {
+          block_counts[size_t(b) * E + e] = run;
           run += c[u];
         }
+      }
+      if (part == G - 1) psm.cnt[e] = run;
     }
-    psm.cnt[e] = run;
+  } else {
+    for (int e = tid; e < E; e += 1024) {
+      // exclusive running sum over blocks, 8 independent loads at a time
+      int32_t run = 0;
+      for (int bb = 0; bb < nblk; bb += 8) {
+        int32_t c[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) c[u] = bb + u < nblk ? block_counts[size_t(bb + u) * E + e] : 0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (bb + u < nblk) {
+            block_counts[size_t(bb + u) * E + e] = run;
+            run += c[u];
+          }
+      }
+      psm.cnt[e] = run;
+    }
   }
   __syncthreads();
   build_plan<1024>(psm, T, E, tile_rows, has_shared, counts, expert_off, plan, tiles);
