@@ -441,13 +441,106 @@ __device__ __forceinline__ float token_gate(int gating, bool slot, bool keep, fl
   return gh;
 }
 
+// Order-preserving 32-bit key of a float: a larger float has a larger key
+// (callers canonicalise -0 to +0; logits are never NaN).
+__device__ __forceinline__ uint32_t order_key(float v) {
+  const uint32_t u = __float_as_uint(v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+constexpr int kTopKBufWords = 96;   // per-wave LDS scratch of select_topk
+
+// Top-K of one token by one wave.  Expert e = 64 i + lane has logit vals[i];
+// experts e >= E are absent.  On return lane k < K holds the k-th selected
+// expert and its logit, in descending logit order, equal logits by ascending
+// expert index (1 <= K <= min(E, 32)).  buf: kTopKBufWords words of LDS
+// owned by this wave.
+//
+// The K-th largest order key is found bit by bit from the top: a candidate
+// prefix is kept when at least K keys are at or above it, counted with one
+// compare per register slot and scalar popcounts of the ballots; the search
+// ends early once exactly K keys are at or above the prefix.  The selection
+// is every key above the threshold plus, among the keys equal to it, those
+// of the lowest expert indices.  The winners are compacted in expert order,
+// each one's rank is counted against the others, and they are placed by rank.
+template <int NPER>
+__device__ __forceinline__ void select_topk(const float (&vals)[NPER], int E, int K, int lane,
+                                            uint32_t* buf, int& my_e, float& my_r) {
+  uint32_t key[NPER];
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) key[i] = (lane + kWave * i < E) ? order_key(vals[i]) : 0u;
+  // Present keys are at least order_key(-inf) > 0, and K <= E of them exist,
+  // so the threshold p ends above 0 and absent experts are never selected.
+  uint32_t p = 0;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t c = p | (1u << b);
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) cnt += __popcll(__ballot(key[i] >= c));
+    if (cnt >= K) {
+      p = c;
+      if (cnt == K) break;
+    }
+  }
+  unsigned long long sel[NPER];
+  int need = K;
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    sel[i] = __ballot(key[i] > p);
+    need -= __popcll(sel[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    unsigned long long eq = __ballot(key[i] == p);
+    while (need > 0 && eq) {   // equal keys: lowest expert index first
+      const unsigned long long lo = eq & (~eq + 1ull);
+      sel[i] |= lo;
+      eq ^= lo;
+      --need;
+    }
+  }
+  // compaction in expert order: positions 0..K-1
+  uint32_t* ck = buf;
+  uint32_t* ce = buf + 32;
+  uint32_t* sk = buf + 64;
+  int base = 0;
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    if ((sel[i] >> lane) & 1ull) {
+      const int pos = base + __popcll(sel[i] & ((1ull << lane) - 1ull));
+      ck[pos] = key[i];
+      ce[pos] = uint32_t(kWave * i + lane);
+    }
+    base += __popcll(sel[i]);
+  }
+  __builtin_amdgcn_wave_barrier();
+  const bool slot = lane < K;
+  const uint32_t mk = slot ? ck[lane] : 0u;
+  const uint32_t me = slot ? ce[lane] : 0u;
+  // rank among the K: larger keys, and equal keys earlier in expert order
+  int r = 0;
+  for (int j = 0; j < K; ++j) {
+    const uint32_t kj = uint32_t(__builtin_amdgcn_readlane(int(mk), j));
+    r += (kj > mk || (kj == mk && j < lane)) ? 1 : 0;
+  }
+  __builtin_amdgcn_wave_barrier();
+  if (slot) {
+    sk[r] = mk;
+    ck[r] = me;   // expert of rank r (ck is free once every lane read its entry)
+  }
+  __builtin_amdgcn_wave_barrier();
+  my_e = slot ? int(ck[lane]) : 0;
+  my_r = slot ? key_value(sk[lane]) : 0.f;
+}
+
 // Token t's selection by one wave.  Expert e's logits are held by lane
 // e % 64 in register e / 64; the KS partial sums are added in ks order, then
-// the biases.  Round k of the top-K takes the wave-wide maximum M of the
-// remaining logits and the lowest expert index holding M (ballot and
-// find-first-set), then removes that entry.
+// the biases; select_topk picks the K.  buf: the wave's select_topk scratch.
 template <int NPER>
-__device__ __forceinline__ void select_token(const SelectArgs& a, int t, int lane) {
+__device__ __forceinline__ void select_token(const SelectArgs& a, int t, int lane, uint32_t* buf) {
   const int E = a.E, K = a.K;
   float pr[4][NPER], pz[4][NPER];
 #pragma unroll
@@ -480,27 +573,9 @@ __device__ __forceinline__ void select_token(const SelectArgs& a, int t, int lan
   float r_all[NPER];
 #pragma unroll
   for (int i = 0; i < NPER; ++i) r_all[i] = vals[i];
-  int my_e = 0;
-  float my_r = 0.f;
-  for (int k = 0; k < K; ++k) {
-    float m[1] = {vals[0]};
-#pragma unroll
-    for (int i = 1; i < NPER; ++i) m[0] = fmaxf(m[0], vals[i]);
-    wave_max_f32_n<1>(m);
-    int win = 0;
-#pragma unroll
-    for (int i = NPER - 1; i >= 0; --i) {
-      const unsigned long long b = __ballot(vals[i] == m[0] && lane + kWave * i < E);
-      if (b) win = kWave * i + __builtin_ctzll(b);
-    }
-#pragma unroll
-    for (int i = 0; i < NPER; ++i)
-      if (win == kWave * i + lane) vals[i] = -__builtin_inff();
-    if (lane == k) {
-      my_e = win;
-      my_r = m[0];
-    }
-  }
+  int my_e;
+  float my_r;
+  select_topk<NPER>(vals, E, K, lane, buf, my_e, my_r);
   const bool slot = lane < K;
   const int e_k = slot ? my_e : 0;
   const float r_k = slot ? my_r : 0.f;
@@ -552,9 +627,10 @@ __device__ __forceinline__ void stage_to_lds(D* dst, const S* __restrict__ src, 
 // One wave per token, NT / 64 tokens per workgroup.
 template <int NPER, int NT>
 __global__ __launch_bounds__(NT) void k_select_tokens(SelectArgs a) {
+  __shared__ uint32_t sbuf[NT / kWave][kTopKBufWords];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t = blockIdx.x * (NT / kWave) + wave;
-  if (t < a.T) select_token<NPER>(a, t, lane);
+  if (t < a.T) select_token<NPER>(a, t, lane, sbuf[wave]);
 }
 
 // The plan from all tokens' selections, in one workgroup: every token's mask
@@ -616,6 +692,7 @@ __global__ __launch_bounds__(1024) void k_select(SelectArgs a) {
   __shared__ int32_t s_idx[kSelBlock * 32];
   __shared__ uint32_t s_mask[kSelBlock];
   __shared__ PlanSmem s_plan[1];   // used by the PLAN form only
+  __shared__ uint32_t sbuf[kSelWaves][kTopKBufWords];
   // PLAN batches have at most kSelWaves tokens: one per wave, so no wave
   // carries empty token slots through the top-K rounds, and the (at most 4)
   // partial-sum slices of its token are loaded in one round.
@@ -675,67 +752,28 @@ __global__ __launch_bounds__(1024) void k_select(SelectArgs a) {
   }
   __syncthreads();   // bits[] cleared
 
-  // Top-K of the wave's tokens, IL tokens at a time with their reductions
-  // interleaved.  Round k: the wave-wide maximum M of the remaining logits,
-  // then the lowest expert index holding M (ballot + find-first-set, so equal
-  // logits go to the lower index); that entry is then removed.
-  constexpr int IL = NPER <= 4 ? TPW : 1;
+  // Top-K of the wave's tokens, one after another (select_topk).
 #pragma unroll
-  for (int j0 = 0; j0 < TPW; j0 += IL) {
-    if (t0 + j0 * kSelWaves + wave >= T) break;   // no valid token left in this wave
-    float vals[IL][NPER];
-#pragma unroll
-    for (int jj = 0; jj < IL; ++jj)
+  for (int j = 0; j < TPW; ++j) {
+    const int tl = j * kSelWaves + wave;
+    const int t = t0 + tl;
+    if (t >= T) break;   // no valid token left in this wave
+    {
+      float vals[NPER];
 #pragma unroll
       for (int i = 0; i < NPER; ++i)
-        vals[jj][i] = (lane + kWave * i < E) ? rv[j0 + jj][i] + 0.0f : -__builtin_inff();
-    int mine_e[IL];
-    float mine_r[IL];
-#pragma unroll
-    for (int jj = 0; jj < IL; ++jj) {
-      mine_e[jj] = 0;
-      mine_r[jj] = 0.f;
-    }
-    for (int k = 0; k < K; ++k) {
-      float m[IL];
-#pragma unroll
-      for (int jj = 0; jj < IL; ++jj) {
-        m[jj] = vals[jj][0];
-#pragma unroll
-        for (int i = 1; i < NPER; ++i) m[jj] = fmaxf(m[jj], vals[jj][i]);
-      }
-      wave_max_f32_n<IL>(m);
-#pragma unroll
-      for (int jj = 0; jj < IL; ++jj) {
-        int win = 0;
-#pragma unroll
-        for (int i = NPER - 1; i >= 0; --i) {
-          const unsigned long long b = __ballot(vals[jj][i] == m[jj] && lane + kWave * i < E);
-          if (b) win = kWave * i + __builtin_ctzll(b);
-        }
-        // win is wave-uniform: remove it from its owner lane
-#pragma unroll
-        for (int i = 0; i < NPER; ++i)
-          if (win == kWave * i + lane) vals[jj][i] = -__builtin_inff();
-        if (lane == k) {
-          mine_e[jj] = win;
-          mine_r[jj] = m[jj];
-        }
-      }
-    }
-#pragma unroll
-    for (int jj = 0; jj < IL; ++jj) {
-      const int tl = (j0 + jj) * kSelWaves + wave;
-      const int t = t0 + tl;
-      if (t >= T) break;
+        vals[i] = (lane + kWave * i < E) ? rv[j][i] + 0.0f : -__builtin_inff();   // + 0: -0 == +0
+      int my_e;
+      float my_r;
+      select_topk<NPER>(vals, E, K, lane, sbuf[wave], my_e, my_r);
       const bool slot = lane < K;
-      const int e_k = slot ? mine_e[jj] : 0;
-      const float r_k = slot ? mine_r[jj] : 0.f;
+      const int e_k = slot ? my_e : 0;
+      const float r_k = slot ? my_r : 0.f;
       // mask logit of expert e_k lives in lane e_k % 64, register e_k / 64
       float z_k = 0.f;
 #pragma unroll
       for (int i = 0; i < NPER; ++i) {
-        const float c = __shfl(zv[j0 + jj][i], e_k & 63, kWave);
+        const float c = __shfl(zv[j][i], e_k & 63, kWave);
         if (i == (e_k >> 6)) z_k = c;
       }
       const bool keep = slot && (a.all_pairs || z_k >= 0.f);
@@ -743,7 +781,7 @@ __global__ __launch_bounds__(1024) void k_select(SelectArgs a) {
       float r_all[NPER];
 #pragma unroll
       for (int i = 0; i < NPER; ++i)
-        r_all[i] = (lane + kWave * i < E) ? rv[j0 + jj][i] : -__builtin_inff();
+        r_all[i] = (lane + kWave * i < E) ? rv[j][i] : -__builtin_inff();
       const float gh = token_gate<NPER>(a.gating, slot, keep, r_k, r_all);
       if (slot) {
         a.idx[size_t(t) * K + lane] = e_k;

@@ -198,6 +198,43 @@ def test_k_extremes(E, K):
     check_output(y, y_ref, "bf16")
 
 
+def _tied_layer(E, K):
+    """Router logits from a handful of exact values, so that most tokens have
+    equal logits inside their top-K and across the K-th / (K+1)-th boundary:
+    r_e = x[t, e % 16] * w_e + b_e with x in {-1, 0, 1, 2}, w_e in {0, 0.25, 0.5}
+    and b_e in {-0.5, -0.0, 0, 0.5} (every product and sum exact in fp32, -0
+    and +0 both present).  Mask logits are b_m = +-1 (fixed keep pattern)."""
+    from dataclasses import replace
+    layer = small_layer(f"gpu_tie{E}_{K}", D=128, E=E, K=K, I=64, keep=0.5)
+    rng = np.random.default_rng(1000 + E + K)
+    wr = np.zeros((E, 128), np.float32)
+    wr[np.arange(E), np.arange(E) % 16] = rng.choice([0.0, 0.25, 0.5], size=E)
+    b_r = rng.choice(np.array([-0.5, -0.0, 0.0, 0.5], np.float32), size=E).astype(np.float32)
+    b_m = rng.choice(np.array([-1.0, 1.0], np.float32), size=E).astype(np.float32)
+    return replace(layer, w_router=synth.f32_to_bf16_bits(wr),
+                   w_mask=synth.f32_to_bf16_bits(np.zeros((E, 128), np.float32)),
+                   b_router=b_r, b_mask=b_m)
+
+
+@pytest.mark.parametrize("E,K", [(40, 7), (100, 32), (212, 16), (700, 5)])
+@pytest.mark.parametrize("T", [9, 70, 1200])
+def test_topk_ties(E, K, T):
+    """Top-K with many exactly equal logits (equal logits go to the lower
+    expert index, also at the boundary of the K kept), for every register
+    width of the selection (E <= 64, 128, 256, 1024) and each selection form:
+    9 tokens (one workgroup selects and plans), 70 (one wave per token, then
+    the bitmap plan) and 1200 (64-token blocks, scan, scatter)."""
+    layer = _tied_layer(E, K)
+    rng = np.random.default_rng(7 + T)
+    x = synth.f32_to_bf16_bits(rng.choice(np.array([-1.0, 0.0, 1.0, 2.0], np.float32),
+                                          size=(T, 128)).astype(np.float32))
+    note(f"[top-K ties] E={E} K={K} T={T}")
+    y, rt, _ = run_forward(device_layer(layer), x)
+    rt_ref, y_ref = oracle.forward(layer, x)
+    check_routing(rt, rt_ref, E)
+    check_output(y, y_ref, "bf16")
+
+
 @pytest.mark.parametrize("flags", [1, 2, 3])
 @pytest.mark.parametrize("T", [37, 4200])
 def test_gate_options(flags, T):
