@@ -704,65 +704,70 @@ __global__ __launch_bounds__(1024) void k_select(SelectArgs a) {
   const int t0 = blk * kSelBlock;
   const int T = a.T, E = a.E, K = a.K;
   for (int e = tid; e < E; e += blockDim.x) bits[e] = 0ull;
-  // r and z of this wave's tokens: partial sums added in ks order, then the
-  // biases.  All loads of a round are issued before any is used.
-  float rv[TPW][NPER], zv[TPW][NPER];
-#pragma unroll
-  for (int j = 0; j < TPW; ++j)
-#pragma unroll
-    for (int i = 0; i < NPER; ++i) rv[j][i] = zv[j][i] = 0.f;
-  for (int ks0 = 0; ks0 < a.KS; ks0 += KB) {
-    float pr[KB][TPW][NPER], pz[KB][TPW][NPER];
-#pragma unroll
-    for (int u = 0; u < KB; ++u)
-#pragma unroll
-      for (int j = 0; j < TPW; ++j) {
-        const int t = t0 + j * kSelWaves + wave;
-#pragma unroll
-        for (int i = 0; i < NPER; ++i) {
-          const int e = lane + kWave * i;
-          pr[u][j][i] = pz[u][j][i] = 0.f;
-          if (ks0 + u < a.KS && t < T && e < E) {
-            const float* row = a.part + (size_t(ks0 + u) * T + route_row(a, t)) * 2 * E;
-            pr[u][j][i] = row[e];
-            pz[u][j][i] = row[E + e];
-          }
-        }
-      }
-#pragma unroll
-    for (int u = 0; u < KB; ++u)
-#pragma unroll
-      for (int j = 0; j < TPW; ++j)
-#pragma unroll
-        for (int i = 0; i < NPER; ++i) {
-          rv[j][i] += pr[u][j][i];
-          zv[j][i] += pz[u][j][i];
-        }
-  }
-#pragma unroll
-  for (int i = 0; i < NPER; ++i) {
-    const int e = lane + kWave * i;
-    const float b_r = (a.br && e < E) ? a.br[e] : 0.f;
-    const float b_m = (a.bm && e < E) ? a.bm[e] : 0.f;
-#pragma unroll
-    for (int j = 0; j < TPW; ++j) {
-      rv[j][i] += b_r;
-      zv[j][i] += b_m;
-    }
-  }
   __syncthreads();   // bits[] cleared
 
-  // Top-K of the wave's tokens, one after another (select_topk).
+  // The wave's tokens, TL at a time: r and z of TL tokens (partial sums added
+  // in ks order, then the biases; all loads of a round issued before any is
+  // used), then their top-K one after another (select_topk).  TL is all of
+  // the wave's tokens, except at 16 logits per lane, where holding four
+  // tokens' r and z would not fit in registers.
+  constexpr int TL = NPER >= 16 ? 1 : TPW;
 #pragma unroll
-  for (int j = 0; j < TPW; ++j) {
-    const int tl = j * kSelWaves + wave;
-    const int t = t0 + tl;
-    if (t >= T) break;   // no valid token left in this wave
-    {
+  for (int jg = 0; jg < TPW; jg += TL) {
+    if (t0 + jg * kSelWaves + wave >= T) break;   // no valid token left in this wave
+    float rv[TL][NPER], zv[TL][NPER];
+#pragma unroll
+    for (int j = 0; j < TL; ++j)
+#pragma unroll
+      for (int i = 0; i < NPER; ++i) rv[j][i] = zv[j][i] = 0.f;
+    for (int ks0 = 0; ks0 < a.KS; ks0 += KB) {
+      float pr[KB][TL][NPER], pz[KB][TL][NPER];
+#pragma unroll
+      for (int u = 0; u < KB; ++u)
+#pragma unroll
+        for (int j = 0; j < TL; ++j) {
+          const int t = t0 + (jg + j) * kSelWaves + wave;
+#pragma unroll
+          for (int i = 0; i < NPER; ++i) {
+            const int e = lane + kWave * i;
+            pr[u][j][i] = pz[u][j][i] = 0.f;
+            if (ks0 + u < a.KS && t < T && e < E) {
+              const float* row = a.part + (size_t(ks0 + u) * T + route_row(a, t)) * 2 * E;
+              pr[u][j][i] = row[e];
+              pz[u][j][i] = row[E + e];
+            }
+          }
+        }
+#pragma unroll
+      for (int u = 0; u < KB; ++u)
+#pragma unroll
+        for (int j = 0; j < TL; ++j)
+#pragma unroll
+          for (int i = 0; i < NPER; ++i) {
+            rv[j][i] += pr[u][j][i];
+            zv[j][i] += pz[u][j][i];
+          }
+    }
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) {
+      const int e = lane + kWave * i;
+      const float b_r = (a.br && e < E) ? a.br[e] : 0.f;
+      const float b_m = (a.bm && e < E) ? a.bm[e] : 0.f;
+#pragma unroll
+      for (int j = 0; j < TL; ++j) {
+        rv[j][i] += b_r;
+        zv[j][i] += b_m;
+      }
+    }
+#pragma unroll
+    for (int jj = 0; jj < TL; ++jj) {
+      const int tl = (jg + jj) * kSelWaves + wave;
+      const int t = t0 + tl;
+      if (t >= T) break;
       float vals[NPER];
 #pragma unroll
       for (int i = 0; i < NPER; ++i)
-        vals[i] = (lane + kWave * i < E) ? rv[j][i] + 0.0f : -__builtin_inff();   // + 0: -0 == +0
+        vals[i] = (lane + kWave * i < E) ? rv[jj][i] + 0.0f : -__builtin_inff();   // + 0: -0 == +0
       int my_e;
       float my_r;
       select_topk<NPER>(vals, E, K, lane, sbuf[wave], my_e, my_r);
@@ -773,7 +778,7 @@ __global__ __launch_bounds__(1024) void k_select(SelectArgs a) {
       float z_k = 0.f;
 #pragma unroll
       for (int i = 0; i < NPER; ++i) {
-        const float c = __shfl(zv[j][i], e_k & 63, kWave);
+        const float c = __shfl(zv[jj][i], e_k & 63, kWave);
         if (i == (e_k >> 6)) z_k = c;
       }
       const bool keep = slot && (a.all_pairs || z_k >= 0.f);
@@ -781,7 +786,7 @@ __global__ __launch_bounds__(1024) void k_select(SelectArgs a) {
       float r_all[NPER];
 #pragma unroll
       for (int i = 0; i < NPER; ++i)
-        r_all[i] = (lane + kWave * i < E) ? rv[j][i] : -__builtin_inff();
+        r_all[i] = (lane + kWave * i < E) ? rv[jj][i] : -__builtin_inff();
       const float gh = token_gate<NPER>(a.gating, slot, keep, r_k, r_all);
       if (slot) {
         a.idx[size_t(t) * K + lane] = e_k;
