@@ -97,8 +97,15 @@ __device__ __forceinline__ void router_skinny_block(const RouterArgs& a, int blk
         if (g * MT + b == q) v = acc[g][b];
     const int t = t0 + 16 * (q % MT) + (lane & 15);
     const int j = j0 + 16 * (q / MT) + 4 * (lane >> 4);
+    // v holds router rows j .. j + 3 of token t: one 16-byte store when E is
+    // even (rows of 2E floats, j a multiple of 4: the four exist or none does)
+    if ((a.E & 1) == 0) {
+      if (t < a.T && j < 2 * a.E)
+        *reinterpret_cast<f32x4*>(a.part + (size_t(ks) * a.T + t) * 2 * a.E + j) = v;
+    } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) router_store(a, ks, t, j + i, v[i]);
+      for (int i = 0; i < 4; ++i) router_store(a, ks, t, j + i, v[i]);
+    }
   }
 }
 
@@ -108,7 +115,11 @@ __global__ __launch_bounds__(256) void k_router_skinny(RouterArgs a) {
   router_skinny_block<NM, MT>(a, blockIdx.x, red);
 }
 
-constexpr int kRouterBN = 64, kRouterBM = 256;
+// Tiled router (large batches with many experts): tiles of 64 rows of one
+// router matrix x 128 tokens.  At T = 8192 and 212 experts that is 512 items,
+// two workgroups per CU, which hide each other's load latency (256-token
+// tiles, one workgroup per CU: 39.3 -> 35.7 us on MI355X).
+constexpr int kRouterBN = 64, kRouterBM = 128;
 
 // A tile covers rows [jb, jb + 64) of one of the two weight matrices
 // (which = 0: Wr, 1: Wm), so that its rows share one base address.
@@ -148,10 +159,23 @@ __global__ __launch_bounds__(256, 2) void k_router_tiled(RouterArgs a) {
 #pragma unroll
       for (int jm = 0; jm < JM; ++jm) {
         const int t = t0 + wm * (kRouterBM / 2) + jm * 32 + (lane & 31);
+        // Entries 4q .. 4q + 3 of a lane are four consecutive router rows of
+        // one token: one 16-byte store when E is a multiple of 4 (then the
+        // four exist or none does).  Scalar stores of single logits, 32
+        // tokens' rows per instruction, took 49 us instead of 39 at T = 8192.
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int jr = pv.jb + wn * (kRouterBN / 2) + jn * 32 + 8 * (i / 4) + 4 * (lane >> 5) + (i % 4);
-          if (jr < a.E) router_store(a, 0, t, pv.which * a.E + jr, acc[jn][jm][i]);
+        for (int q = 0; q < 4; ++q) {
+          const int jr = pv.jb + wn * (kRouterBN / 2) + jn * 32 + 8 * q + 4 * (lane >> 5);
+          const f32x16& v = acc[jn][jm];
+          if ((a.E & 3) == 0) {
+            if (t < a.T && jr < a.E)
+              *reinterpret_cast<float4*>(a.part + size_t(t) * 2 * a.E + pv.which * a.E + jr) =
+                  make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (jr + i < a.E) router_store(a, 0, t, pv.which * a.E + jr + i, v[4 * q + i]);
+          }
         }
       }
   }
