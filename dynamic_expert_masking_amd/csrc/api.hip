@@ -53,8 +53,8 @@ WsLayout workspace_layout(const beam_moe_layer& L, int32_t T) {
   w.slot_pos = take(TK * 4);
   w.h = take(TK * L.I * elt);
   w.h_shared = take(size_t(T) * IS * elt);
-  w.o = take(TK * L.D * 4);
-  w.o_shared = take(IS ? size_t(T) * L.D * 4 : 0);
+  w.o = take(TK * L.D * elt);
+  w.o_shared = take(IS ? size_t(T) * L.D * elt : 0);
   w.zsel = take(TK * 4);
   w.dz = take(TK * 4);
   w.lreg_tok = take(size_t(T) * 4);
@@ -207,8 +207,8 @@ static Ptrs carve(const WsLayout& w, void* ws, const beam_route_out* out) {
   p.slot_pos = reinterpret_cast<int32_t*>(b + w.slot_pos);
   p.h = b + w.h;
   p.h_shared = b + w.h_shared;
-  p.o = reinterpret_cast<float*>(b + w.o);
-  p.o_shared = reinterpret_cast<float*>(b + w.o_shared);
+  p.o = b + w.o;
+  p.o_shared = b + w.o_shared;
   p.zsel = reinterpret_cast<float*>(b + w.zsel);
   p.dz = reinterpret_cast<float*>(b + w.dz);
   p.lreg_tok = reinterpret_cast<float*>(b + w.lreg_tok);

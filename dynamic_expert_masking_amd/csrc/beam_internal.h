@@ -63,8 +63,8 @@ struct Ptrs {
   // experts
   void* h;
   void* h_shared;
-  float* o;
-  float* o_shared;
+  void* o;          // [P][D] expert outputs: fp32 for fp32 layers, bf16 otherwise
+  void* o_shared;   // [T][D] shared-expert outputs, same type
   // mask-router backward
   float* zsel;       // [T][K] mask logit of each candidate
   float* dz;         // [P] dL/dz of each pair (pair order)

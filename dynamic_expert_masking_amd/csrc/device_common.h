@@ -34,6 +34,26 @@ __device__ __forceinline__ u16 f32_to_bf16(float f) {
   return u16(u >> 16);
 }
 
+// Four consecutive elements at base[elem], as floats: bf16 (BF16) or fp32.
+template <bool BF16>
+__device__ __forceinline__ float4 ld4_f32(const void* base, size_t elem) {
+  if (BF16) {
+    const ushort4 v = *reinterpret_cast<const ushort4*>(static_cast<const u16*>(base) + elem);
+    return make_float4(bf16_to_f32(v.x), bf16_to_f32(v.y), bf16_to_f32(v.z), bf16_to_f32(v.w));
+  }
+  return *reinterpret_cast<const float4*>(static_cast<const float*>(base) + elem);
+}
+
+// Four floats rounded to bf16 and stored at base[elem] (8 bytes).
+__device__ __forceinline__ void st4_bf16(u16* base, size_t elem, float a, float b, float c, float d) {
+  ushort4 v;
+  v.x = f32_to_bf16(a);
+  v.y = f32_to_bf16(b);
+  v.z = f32_to_bf16(c);
+  v.w = f32_to_bf16(d);
+  *reinterpret_cast<ushort4*>(base + elem) = v;
+}
+
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
 // Streaming load for weights that are read once per call.

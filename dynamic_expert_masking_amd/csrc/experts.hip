@@ -44,8 +44,8 @@ struct ExpertArgs {
   const int32_t* perm_token;
   void* h;         // [P][I]
   void* h_sh;      // [T][S*Is]
-  float* o;        // [P][D]
-  float* o_sh;     // [T][D]
+  void* o;         // [P][D] expert outputs: fp32 (fp32 layers) or bf16
+  void* o_sh;      // [T][D] shared-expert outputs, same type
 };
 
 // Order of the shared items.  Every shared tile reads the same weights, so
@@ -379,7 +379,7 @@ struct DownStream {
   }
   __device__ void store_o(const Tile tl, int nb, bool shared, const f32x4 (&acc)[NB][MT],
                           int lane) const {
-    float* ob = shared ? a->o_sh : a->o;
+    u16* ob = static_cast<u16*>(shared ? a->o_sh : a->o);
 #pragma unroll
     for (int b = 0; b < MT; ++b) {
       const int r = 16 * b + (lane & 15);
@@ -388,7 +388,7 @@ struct DownStream {
         for (int g = 0; g < NB; ++g) {
           const int d = (nb * NB + g) * 16 + 4 * (lane >> 4);
           const f32x4 v = acc[g][b];
-          *reinterpret_cast<float4*>(ob + size_t(tl.row0 + r) * a->D + d) = make_float4(v[0], v[1], v[2], v[3]);
+          st4_bf16(ob, size_t(tl.row0 + r) * a->D + d, v[0], v[1], v[2], v[3]);
         }
       }
     }
@@ -552,7 +552,7 @@ __global__ __launch_bounds__(256, 2) void k_down_tiled(ExpertArgs a) {
     pv.d0 = nb * BN;
     f32x16 acc[JN][JM];
     tiled_accumulate<BN, BM>(pv, sm, acc, tl.rows);
-    float* ob = shared ? a.o_sh : a.o;
+    u16* ob = static_cast<u16*>(shared ? a.o_sh : a.o);
 #pragma unroll
     for (int jn = 0; jn < JN; ++jn)
 #pragma unroll
@@ -564,8 +564,8 @@ __global__ __launch_bounds__(256, 2) void k_down_tiled(ExpertArgs a) {
             const int d = nb * BN + wn * (BN / 2) + jn * 32 + 8 * q + 4 * (lane >> 5);
             if (d < a.D) {
               const f32x16& v = acc[jn][jm];
-              *reinterpret_cast<float4*>(ob + size_t(tl.row0 + r) * a.D + d) =
-                  make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+              st4_bf16(ob, size_t(tl.row0 + r) * a.D + d, v[4 * q], v[4 * q + 1], v[4 * q + 2],
+                       v[4 * q + 3]);
             }
           }
         }
@@ -626,27 +626,29 @@ __global__ __launch_bounds__(256) void k_down_f32(ExpertArgs a) {
         const float* wrow = (const float*)a.sd + size_t(sx) * a.D * a.Is + size_t(d) * a.Is;
         for (int i = 0; i < a.Is; ++i) s = fmaf(hr[sx * a.Is + i], wrow[i], s);
       }
-      a.o_sh[size_t(tl.row0 + r) * a.D + d] = s;
+      static_cast<float*>(a.o_sh)[size_t(tl.row0 + r) * a.D + d] = s;
     } else {
       const float* hr = (const float*)a.h + size_t(tl.row0 + r) * a.I;
       const float* wrow = (const float*)a.wd + size_t(tl.expert) * a.D * a.I + size_t(d) * a.I;
       for (int i = 0; i < a.I; ++i) s = fmaf(hr[i], wrow[i], s);
-      a.o[size_t(tl.row0 + r) * a.D + d] = s;
+      static_cast<float*>(a.o)[size_t(tl.row0 + r) * a.D + d] = s;
     }
   }
 }
 
 // ---------------------------------------------------------------------------
 // Combine: y[t] = sum_{k=0}^{K-1} g_hat[t][k] O[slot_pos[t][k]] + O_shared[t],
-// accumulated in fp32 in slot order, rounded once.  A token with no surviving
+// accumulated in fp32 in slot order, rounded once.  O is stored in the
+// layer's dtype (bf16 layers: each expert output rounded to bf16 once, which
+// halves its write and read traffic).  A token with no surviving
 // pair and no shared expert gets exactly 0.
 // ---------------------------------------------------------------------------
 
-template <bool BF16_OUT>
+template <bool BF16>
 __global__ __launch_bounds__(256) void k_combine(int T, int D, int K, const float* __restrict__ gates,
                                                  const int32_t* __restrict__ slot_pos,
-                                                 const float* __restrict__ o,
-                                                 const float* __restrict__ o_sh, void* __restrict__ y) {
+                                                 const void* __restrict__ o,
+                                                 const void* __restrict__ o_sh, void* __restrict__ y) {
   __shared__ float s_g[32];
   __shared__ int32_t s_p[32];
   const int t = blockIdx.x;
@@ -661,26 +663,21 @@ __global__ __launch_bounds__(256) void k_combine(int T, int D, int K, const floa
       const int p = s_p[k];
       if (p < 0) continue;
       const float g = s_g[k];
-      const float4 v = *reinterpret_cast<const float4*>(o + size_t(p) * D + d);
+      const float4 v = ld4_f32<BF16>(o, size_t(p) * D + d);
       acc.x += g * v.x;
       acc.y += g * v.y;
       acc.z += g * v.z;
       acc.w += g * v.w;
     }
     if (o_sh) {
-      const float4 v = *reinterpret_cast<const float4*>(o_sh + size_t(t) * D + d);
+      const float4 v = ld4_f32<BF16>(o_sh, size_t(t) * D + d);
       acc.x += v.x;
       acc.y += v.y;
       acc.z += v.z;
       acc.w += v.w;
     }
-    if (BF16_OUT) {
-      ushort4 out;
-      out.x = f32_to_bf16(acc.x);
-      out.y = f32_to_bf16(acc.y);
-      out.z = f32_to_bf16(acc.z);
-      out.w = f32_to_bf16(acc.w);
-      *reinterpret_cast<ushort4*>((u16*)y + size_t(t) * D + d) = out;
+    if (BF16) {
+      st4_bf16(static_cast<u16*>(y), size_t(t) * D + d, acc.x, acc.y, acc.z, acc.w);
     } else {
       *reinterpret_cast<float4*>((float*)y + size_t(t) * D + d) = acc;
     }
@@ -916,7 +913,7 @@ hipError_t launch_down(const beam_moe_layer& L, int32_t T, int tile_rows, const 
 
 hipError_t launch_combine(const beam_moe_layer& L, int32_t T, const Ptrs& p, void* y,
                           hipStream_t s) {
-  const float* osh = L.n_shared > 0 ? p.o_shared : nullptr;
+  const void* osh = L.n_shared > 0 ? p.o_shared : nullptr;
   prof_before("combine", s);
   if (L.dtype == BEAM_F32)
     hipLaunchKernelGGL(k_combine<false>, dim3(unsigned(T)), dim3(256), 0, s, T, L.D, L.K, p.gates,

@@ -15,21 +15,12 @@
 //   dL/db_m[e]  = sum over the same candidates of dL/dz_k
 //
 // The caller's routing ran in all-pairs mode: every top-K candidate has an
-// expert output row O[slot_pos[t][k]] (fp32), gates[t][k] holds the unmasked
+// expert output row O[slot_pos[t][k]] (the layer's dtype), gates[t][k] holds the unmasked
 // g, zsel[t][k] the mask logit, and the pairs are in expert-major order.
 #include "beam_internal.h"
 #include "device_common.h"
 
 namespace beam {
-
-template <bool BF16>
-__device__ __forceinline__ float4 ld4(const void* base, size_t elem) {
-  if (BF16) {
-    const ushort4 v = *reinterpret_cast<const ushort4*>(static_cast<const u16*>(base) + elem);
-    return make_float4(bf16_to_f32(v.x), bf16_to_f32(v.y), bf16_to_f32(v.z), bf16_to_f32(v.w));
-  }
-  return *reinterpret_cast<const float4*>(static_cast<const float*>(base) + elem);
-}
 
 // Sum over the workgroup's 256 threads in a fixed order (deterministic).
 __device__ __forceinline__ float block_sum256(float v, float* red) {
@@ -51,7 +42,7 @@ __global__ __launch_bounds__(256) void k_mask_grad_pairs(const void* __restrict_
                                                          const float* __restrict__ gates,
                                                          const float* __restrict__ zsel,
                                                          const int32_t* __restrict__ slot_pos,
-                                                         const float* __restrict__ o,
+                                                         const void* __restrict__ o,
                                                          float* __restrict__ dz,
                                                          float* __restrict__ lreg_tok) {
   __shared__ float red[4];
@@ -61,8 +52,8 @@ __global__ __launch_bounds__(256) void k_mask_grad_pairs(const void* __restrict_
     const int pos = slot_pos[size_t(t) * K + k];
     float part = 0.f;
     for (int d = 4 * threadIdx.x; d < D; d += 4 * 256) {
-      const float4 g4 = ld4<BF16>(dy, size_t(t) * D + d);
-      const float4 o4 = *reinterpret_cast<const float4*>(o + size_t(pos) * D + d);
+      const float4 g4 = ld4_f32<BF16>(dy, size_t(t) * D + d);
+      const float4 o4 = ld4_f32<BF16>(o, size_t(pos) * D + d);
       part += (g4.x * o4.x + g4.y * o4.y) + (g4.z * o4.z + g4.w * o4.w);
     }
     const float dot = block_sum256(part, red);
@@ -103,7 +94,7 @@ __global__ __launch_bounds__(256) void k_mask_grad_wm(const void* __restrict__ x
       for (int u = 0; u < 8; ++u) {
         const int q = min(q0 + u, p1 - 1);
         w[u] = q0 + u < p1 ? dz[q] : 0.f;
-        xv[u] = ld4<BF16>(x, size_t(perm_token[q]) * D + d);
+        xv[u] = ld4_f32<BF16>(x, size_t(perm_token[q]) * D + d);
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
