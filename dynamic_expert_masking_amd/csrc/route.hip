@@ -380,16 +380,16 @@ __device__ void build_plan(PlanSmem& sm, int T, int E, int tile_rows, int has_sh
 // index first), softmax over the K kept logits, mask bit m_k = [z >= 0] on
 // the candidates, g_hat = g * m.
 //
-// Two forms.  When the batch's per-expert token bitmaps (E x ceil(T/64)
-// words) and its selections fit in one workgroup's LDS, one wave selects each
-// token (k_select_tokens) and a one-workgroup kernel builds the plan and
-// places every pair (k_plan_bitmap).  Otherwise one 1024-thread workgroup
-// handles each 64-token block and records block-local ranks and counts, and
-// the scan and scatter kernels follow (k_select).
+// Three forms.  Up to 16 tokens, one workgroup selects and plans
+// (k_select_plan).  Otherwise one wave selects each token (k_select_tokens);
+// then, when the batch's per-expert token bitmaps (E x ceil(T/64) words) and
+// its selections fit in one workgroup's LDS, a one-workgroup kernel builds the
+// plan and places every pair (k_plan_bitmap), and else one workgroup per
+// 64-token block records block-local ranks and counts (k_block_ranks) and the
+// scan and scatter kernels follow.
 // ---------------------------------------------------------------------------
 
-constexpr int kSelWaves = 16;
-constexpr int kSelTokPerWave = kSelBlock / kSelWaves;   // 4
+constexpr int kSelWaves = 16;   // waves of the one-workgroup selection
 constexpr int kSelMergedMax = 16;   // largest batch whose selection builds the plan itself
 // Limits of the bitmap plan (LDS of its one workgroup).
 constexpr int kPlanWords = 4096;    // E * ceil(T / 64) bitmap words
@@ -700,163 +700,139 @@ __global__ __launch_bounds__(NT) void k_plan_bitmap(SelectArgs a) {
   }
 }
 
-// Multi-block form: one 1024-thread workgroup per 64-token block; each of its
-// 16 waves handles 4 tokens (wave w: tokens w, w + 16, w + 32, w + 48 of the
-// block, so that short batches use every wave), with all four tokens' logits
-// loaded before any is processed.  Then, per block, the block-local rank of every surviving
-// pair among the block's pairs of the same expert (token order) and the
-// block's per-expert pair counts.
-//
-// PLAN (batches of at most 64 tokens, one workgroup): the block's token
-// bitmaps are the whole batch's, so the same workgroup then builds the plan
-// from them, as k_plan_bitmap does, instead of recording block ranks.
-template <int NPER, bool PLAN>
-__global__ __launch_bounds__(1024) void k_select(SelectArgs a) {
+// Batches of at most kSelWaves tokens, one workgroup: wave w selects token w
+// (its partial logit slices loaded in one round), then the same workgroup
+// builds the plan from the batch's per-expert token bitmaps in LDS, as
+// k_plan_bitmap does: one launch instead of two.
+template <int NPER>
+__global__ __launch_bounds__(1024) void k_select_plan(SelectArgs a) {
   __shared__ unsigned long long bits[kMaxExperts];
-  __shared__ int32_t s_idx[kSelBlock * 32];
-  __shared__ uint32_t s_mask[kSelBlock];
-  __shared__ PlanSmem s_plan[1];   // used by the PLAN form only
+  __shared__ int32_t s_idx[kSelWaves * 32];
+  __shared__ uint32_t s_mask[kSelWaves];
+  __shared__ PlanSmem s_plan;
   __shared__ uint32_t sbuf[kSelWaves][kTopKBufWords];
-  // PLAN batches have at most kSelWaves tokens: one per wave, so no wave
-  // carries empty token slots through the top-K rounds, and the (at most 4)
-  // partial-sum slices of its token are loaded in one round.
-  constexpr int TPW = PLAN ? 1 : kSelTokPerWave;
-  constexpr int KB = NPER >= 16 ? 1 : PLAN ? 4 : (NPER >= 4 ? 1 : 4 / NPER);
-  static_assert(!PLAN || kSelMergedMax <= kSelWaves, "PLAN: one token per wave");
+  constexpr int KB = NPER >= 16 ? 1 : 4;   // partial slices loaded per round
+  static_assert(kSelMergedMax <= kSelWaves, "one token per wave");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int blk = blockIdx.x;
-  const int t0 = blk * kSelBlock;
   const int T = a.T, E = a.E, K = a.K;
   for (int e = tid; e < E; e += blockDim.x) bits[e] = 0ull;
   __syncthreads();   // bits[] cleared
 
-  // The wave's tokens, TL at a time: r and z of TL tokens (partial sums added
-  // in ks order, then the biases; all loads of a round issued before any is
-  // used), then their top-K one after another (select_topk).  TL is all of
-  // the wave's tokens, except at 16 logits per lane, where holding four
-  // tokens' r and z would not fit in registers.
-  constexpr int TL = NPER >= 16 ? 1 : TPW;
+  const int t = wave;
+  if (t < T) {
+    // r and z of token t: partial sums added in ks order, then the biases
+    float rv[NPER], zv[NPER];
 #pragma unroll
-  for (int jg = 0; jg < TPW; jg += TL) {
-    if (t0 + jg * kSelWaves + wave >= T) break;   // no valid token left in this wave
-    float rv[TL][NPER], zv[TL][NPER];
-#pragma unroll
-    for (int j = 0; j < TL; ++j)
-#pragma unroll
-      for (int i = 0; i < NPER; ++i) rv[j][i] = zv[j][i] = 0.f;
+    for (int i = 0; i < NPER; ++i) rv[i] = zv[i] = 0.f;
     for (int ks0 = 0; ks0 < a.KS; ks0 += KB) {
-      float pr[KB][TL][NPER], pz[KB][TL][NPER];
+      float pr[KB][NPER], pz[KB][NPER];
 #pragma unroll
       for (int u = 0; u < KB; ++u)
 #pragma unroll
-        for (int j = 0; j < TL; ++j) {
-          const int t = t0 + (jg + j) * kSelWaves + wave;
-#pragma unroll
-          for (int i = 0; i < NPER; ++i) {
-            const int e = lane + kWave * i;
-            pr[u][j][i] = pz[u][j][i] = 0.f;
-            if (ks0 + u < a.KS && t < T && e < E) {
-              const float* row = a.part + (size_t(ks0 + u) * T + route_row(a, t)) * 2 * E;
-              pr[u][j][i] = row[e];
-              pz[u][j][i] = row[E + e];
-            }
+        for (int i = 0; i < NPER; ++i) {
+          const int e = lane + kWave * i;
+          pr[u][i] = pz[u][i] = 0.f;
+          if (ks0 + u < a.KS && e < E) {
+            const float* row = a.part + (size_t(ks0 + u) * T + route_row(a, t)) * 2 * E;
+            pr[u][i] = row[e];
+            pz[u][i] = row[E + e];
           }
         }
 #pragma unroll
       for (int u = 0; u < KB; ++u)
 #pragma unroll
-        for (int j = 0; j < TL; ++j)
-#pragma unroll
-          for (int i = 0; i < NPER; ++i) {
-            rv[j][i] += pr[u][j][i];
-            zv[j][i] += pz[u][j][i];
-          }
+        for (int i = 0; i < NPER; ++i) {
+          rv[i] += pr[u][i];
+          zv[i] += pz[u][i];
+        }
     }
+    float vals[NPER], r_all[NPER];
 #pragma unroll
     for (int i = 0; i < NPER; ++i) {
       const int e = lane + kWave * i;
-      const float b_r = (a.br && e < E) ? a.br[e] : 0.f;
-      const float b_m = (a.bm && e < E) ? a.bm[e] : 0.f;
-#pragma unroll
-      for (int j = 0; j < TL; ++j) {
-        rv[j][i] += b_r;
-        zv[j][i] += b_m;
-      }
+      rv[i] += (a.br && e < E) ? a.br[e] : 0.f;
+      zv[i] += (a.bm && e < E) ? a.bm[e] : 0.f;
+      vals[i] = e < E ? rv[i] + 0.0f : -__builtin_inff();   // + 0: -0 == +0
+      r_all[i] = e < E ? rv[i] : -__builtin_inff();
     }
+    int my_e;
+    float my_r;
+    select_topk<NPER>(vals, E, K, lane, sbuf[wave], my_e, my_r);
+    const bool slot = lane < K;
+    const int e_k = slot ? my_e : 0;
+    const float r_k = slot ? my_r : 0.f;
+    // mask logit of expert e_k lives in lane e_k % 64, register e_k / 64
+    float z_k = 0.f;
 #pragma unroll
-    for (int jj = 0; jj < TL; ++jj) {
-      const int tl = (jg + jj) * kSelWaves + wave;
-      const int t = t0 + tl;
-      if (t >= T) break;
-      float vals[NPER];
-#pragma unroll
-      for (int i = 0; i < NPER; ++i)
-        vals[i] = (lane + kWave * i < E) ? rv[jj][i] + 0.0f : -__builtin_inff();   // + 0: -0 == +0
-      int my_e;
-      float my_r;
-      select_topk<NPER>(vals, E, K, lane, sbuf[wave], my_e, my_r);
-      const bool slot = lane < K;
-      const int e_k = slot ? my_e : 0;
-      const float r_k = slot ? my_r : 0.f;
-      // mask logit of expert e_k lives in lane e_k % 64, register e_k / 64
-      float z_k = 0.f;
-#pragma unroll
-      for (int i = 0; i < NPER; ++i) {
-        const float c = __shfl(zv[jj][i], e_k & 63, kWave);
-        if (i == (e_k >> 6)) z_k = c;
-      }
-      const bool keep = slot && (a.all_pairs || z_k >= 0.f);
-      const unsigned long long bal = __ballot(keep);
-      float r_all[NPER];
-#pragma unroll
-      for (int i = 0; i < NPER; ++i)
-        r_all[i] = (lane + kWave * i < E) ? rv[jj][i] : -__builtin_inff();
-      const float gh = token_gate<NPER>(a.gating, slot, keep, r_k, r_all);
-      if (slot) {
-        a.idx[size_t(t) * K + lane] = e_k;
-        a.gates[size_t(t) * K + lane] = gh;
-        s_idx[tl * 32 + lane] = e_k;
-        if (a.all_pairs) a.zsel[size_t(t) * K + lane] = z_k;
-      }
-      if (lane == 0) {
-        a.mask[t] = uint32_t(bal);
-        s_mask[tl] = uint32_t(bal);
-      }
-      if (keep) atomicOr(&bits[e_k], 1ull << tl);
+    for (int i = 0; i < NPER; ++i) {
+      const float c = __shfl(zv[i], e_k & 63, kWave);
+      if (i == (e_k >> 6)) z_k = c;
     }
+    const bool keep = slot && (a.all_pairs || z_k >= 0.f);
+    const unsigned long long bal = __ballot(keep);
+    const float gh = token_gate<NPER>(a.gating, slot, keep, r_k, r_all);
+    if (slot) {
+      a.idx[size_t(t) * K + lane] = e_k;
+      a.gates[size_t(t) * K + lane] = gh;
+      s_idx[t * 32 + lane] = e_k;
+      if (a.all_pairs) a.zsel[size_t(t) * K + lane] = z_k;
+    }
+    if (lane == 0) {
+      a.mask[t] = uint32_t(bal);
+      s_mask[t] = uint32_t(bal);
+    }
+    if (keep) atomicOr(&bits[e_k], 1ull << t);
   }
   __syncthreads();
 
-  if constexpr (PLAN) {
-    PlanSmem& pl = s_plan[0];
-    for (int e = tid; e < E; e += blockDim.x) pl.cnt[e] = __popcll(bits[e]);
-    __syncthreads();
-    build_plan<1024>(pl, T, E, a.tile_rows, a.has_shared, a.counts, a.expert_off, a.plan, a.tiles);
-    for (int q = tid; q < T * K; q += blockDim.x) {
-      const int tl = q / K, k = q - tl * K;
-      int pos = -1;
-      if ((s_mask[tl] >> k) & 1u) {
-        const int e = s_idx[tl * 32 + k];
-        pos = pl.off[e] + __popcll(bits[e] & ((1ull << tl) - 1ull));
-        a.perm_token[pos] = tl;
-      }
-      a.slot_pos[q] = pos;
+  PlanSmem& pl = s_plan;
+  for (int e = tid; e < E; e += blockDim.x) pl.cnt[e] = __popcll(bits[e]);
+  __syncthreads();
+  build_plan<1024>(pl, T, E, a.tile_rows, a.has_shared, a.counts, a.expert_off, a.plan, a.tiles);
+  for (int q = tid; q < T * K; q += blockDim.x) {
+    const int tl = q / K, k = q - tl * K;
+    int pos = -1;
+    if ((s_mask[tl] >> k) & 1u) {
+      const int e = s_idx[tl * 32 + k];
+      pos = pl.off[e] + __popcll(bits[e] & ((1ull << tl) - 1ull));
+      a.perm_token[pos] = tl;
     }
-  } else {
-    for (int q = tid; q < kSelBlock * K; q += blockDim.x) {
-      const int tl = q / K, k = q % K;
-      const int t = t0 + tl;
-      if (t >= T) continue;
-      int rk = -1;
-      if ((s_mask[tl] >> k) & 1u) {
-        const int e = s_idx[tl * 32 + k];
-        rk = __popcll(bits[e] & ((1ull << tl) - 1ull));
-      }
-      a.rank[size_t(t) * K + k] = rk;
-    }
-    for (int e = tid; e < E; e += blockDim.x)
-      a.block_counts[size_t(blk) * E + e] = __popcll(bits[e]);
+    a.slot_pos[q] = pos;
   }
+}
+
+// Block ranks from the selections already written (idx, mask): one
+// workgroup per 64-token block builds the block's per-expert token bitmaps
+// and records each surviving pair's rank among the block's pairs of its
+// expert (token order) and the block's per-expert counts.  The selection
+// itself ran before with one wave per token across the whole GPU; selecting
+// inside these workgroups (four tokens per wave, one 64-token block per
+// workgroup) kept half the CUs idle at T = 8192 (fine-grained layer: 23.2 us
+// for selection and ranks together, now 14.1 + 7.2 us).
+__global__ __launch_bounds__(256) void k_block_ranks(SelectArgs a) {
+  __shared__ unsigned long long bits[kMaxExperts];
+  __shared__ uint32_t s_mask[kSelBlock];
+  const int tid = threadIdx.x, blk = blockIdx.x;
+  const int t0 = blk * kSelBlock;
+  const int T = a.T, E = a.E, K = a.K;
+  const int nt = min(kSelBlock, T - t0);
+  for (int e = tid; e < E; e += blockDim.x) bits[e] = 0ull;
+  if (tid < nt) s_mask[tid] = a.mask[t0 + tid];
+  __syncthreads();
+  for (int q = tid; q < nt * K; q += blockDim.x) {
+    const int tl = q / K, k = q - tl * K;
+    if ((s_mask[tl] >> k) & 1u) atomicOr(&bits[a.idx[size_t(t0) * K + q]], 1ull << tl);
+  }
+  __syncthreads();
+  for (int q = tid; q < nt * K; q += blockDim.x) {
+    const int tl = q / K, k = q - tl * K;
+    int rk = -1;
+    if ((s_mask[tl] >> k) & 1u)
+      rk = __popcll(bits[a.idx[size_t(t0) * K + q]] & ((1ull << tl) - 1ull));
+    a.rank[size_t(t0) * K + q] = rk;
+  }
+  for (int e = tid; e < E; e += blockDim.x)
+    a.block_counts[size_t(blk) * E + e] = __popcll(bits[e]);
 }
 
 hipError_t launch_select(const beam_moe_layer& L, int32_t T, int tile_rows, const Ptrs& p,
@@ -891,10 +867,10 @@ hipError_t launch_select(const beam_moe_layer& L, int32_t T, int tile_rows, cons
   // in one workgroup costs more than the second launch saves.
   if (T <= kSelMergedMax) {
     prof_before("select_plan", s);
-    if (L.E <= 64) hipLaunchKernelGGL((k_select<1, true>), dim3(1), dim3(1024), 0, s, a);
-    else if (L.E <= 128) hipLaunchKernelGGL((k_select<2, true>), dim3(1), dim3(1024), 0, s, a);
-    else if (L.E <= 256) hipLaunchKernelGGL((k_select<4, true>), dim3(1), dim3(1024), 0, s, a);
-    else hipLaunchKernelGGL((k_select<16, true>), dim3(1), dim3(1024), 0, s, a);
+    if (L.E <= 64) hipLaunchKernelGGL((k_select_plan<1>), dim3(1), dim3(1024), 0, s, a);
+    else if (L.E <= 128) hipLaunchKernelGGL((k_select_plan<2>), dim3(1), dim3(1024), 0, s, a);
+    else if (L.E <= 256) hipLaunchKernelGGL((k_select_plan<4>), dim3(1), dim3(1024), 0, s, a);
+    else hipLaunchKernelGGL((k_select_plan<16>), dim3(1), dim3(1024), 0, s, a);
     prof_after(s);
     return hipGetLastError();
   }
@@ -913,13 +889,21 @@ hipError_t launch_select(const beam_moe_layer& L, int32_t T, int tile_rows, cons
     prof_after(s);
     return hipGetLastError();
   }
+  // Larger batches: one wave per token across the GPU, then the block ranks.
+  {
+    constexpr int nt = kSelThreads;
+    const dim3 g{unsigned((T + nt / kWave - 1) / (nt / kWave)), 1, 1}, b{unsigned(nt), 1, 1};
+    prof_before("select_topk_mask", s);
+    if (L.E <= 64) hipLaunchKernelGGL((k_select_tokens<1, nt>), g, b, 0, s, a);
+    else if (L.E <= 128) hipLaunchKernelGGL((k_select_tokens<2, nt>), g, b, 0, s, a);
+    else if (L.E <= 256) hipLaunchKernelGGL((k_select_tokens<4, nt>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((k_select_tokens<16, nt>), g, b, 0, s, a);
+    prof_after(s);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  }
   const int nblk = (T + kSelBlock - 1) / kSelBlock;
-  const dim3 g{unsigned(nblk), 1, 1}, b{1024, 1, 1};
-  prof_before("select_topk_mask", s);
-  if (L.E <= 64) hipLaunchKernelGGL((k_select<1, false>), g, b, 0, s, a);
-  else if (L.E <= 128) hipLaunchKernelGGL((k_select<2, false>), g, b, 0, s, a);
-  else if (L.E <= 256) hipLaunchKernelGGL((k_select<4, false>), g, b, 0, s, a);
-  else hipLaunchKernelGGL((k_select<16, false>), g, b, 0, s, a);
+  prof_before("block_ranks", s);
+  hipLaunchKernelGGL(k_block_ranks, dim3(unsigned(nblk)), dim3(256), 0, s, a);
   prof_after(s);
   return hipGetLastError();
 }
