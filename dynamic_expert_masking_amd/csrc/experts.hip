@@ -763,30 +763,38 @@ static unsigned persistent_grid(long items, long cap) {
 }
 
 // Launches the streaming gate/up variant <MT token blocks, NB row groups,
-// U-chunk stages, FP8 weights?> with k split ks.
+// U-chunk stages, k split KS, FP8 weights?>.
+template <int MT, int NB, int U, int KS, bool F8>
+static void gate_up_stream_k(const ExpertArgs& a, long ntr, long nts, int I, int Is_all,
+                             hipStream_t s) {
+  const long items = ntr * (I / (16 * NB)) + nts * (Is_all / (16 * NB));
+  hipLaunchKernelGGL((k_gate_up_stream<MT, NB, U, KS, F8>),
+                     dim3(stream_grid((const void*)&k_gate_up_stream<MT, NB, U, KS, F8>, items, KS)),
+                     dim3(kStreamWaves * 64), 0, s, a);
+}
+
+// The same with the k split ks (1, 2 or 4) chosen at run time.
 template <int MT, int NB, int U, bool F8>
 static void gate_up_stream(const ExpertArgs& a, long ntr, long nts, int I, int Is_all, int ks,
                            hipStream_t s) {
-  const long items = ntr * (I / (16 * NB)) + nts * (Is_all / (16 * NB));
-  const dim3 blk(kStreamWaves * 64);
-#define BEAM_GU(KS_)                                                                       \
-  hipLaunchKernelGGL((k_gate_up_stream<MT, NB, U, KS_, F8>),                               \
-                     dim3(stream_grid((const void*)&k_gate_up_stream<MT, NB, U, KS_, F8>, items, KS_)), \
-                     blk, 0, s, a)
-  if (ks == 1) BEAM_GU(1); else if (ks == 2) BEAM_GU(2); else BEAM_GU(4);
-#undef BEAM_GU
+  if (ks == 1) gate_up_stream_k<MT, NB, U, 1, F8>(a, ntr, nts, I, Is_all, s);
+  else if (ks == 2) gate_up_stream_k<MT, NB, U, 2, F8>(a, ntr, nts, I, Is_all, s);
+  else gate_up_stream_k<MT, NB, U, 4, F8>(a, ntr, nts, I, Is_all, s);
+}
+
+template <int MT, int NB, int U, int KS, bool F8>
+static void down_stream_k(const ExpertArgs& a, long tiles, int D, hipStream_t s) {
+  const long items = tiles * (D / (16 * NB));
+  hipLaunchKernelGGL((k_down_stream<MT, NB, U, KS, F8>),
+                     dim3(stream_grid((const void*)&k_down_stream<MT, NB, U, KS, F8>, items, KS)),
+                     dim3(kStreamWaves * 64), 0, s, a);
 }
 
 template <int MT, int NB, int U, bool F8>
 static void down_stream(const ExpertArgs& a, long tiles, int D, int ks, hipStream_t s) {
-  const long items = tiles * (D / (16 * NB));
-  const dim3 blk(kStreamWaves * 64);
-#define BEAM_DN(KS_)                                                                       \
-  hipLaunchKernelGGL((k_down_stream<MT, NB, U, KS_, F8>),                                  \
-                     dim3(stream_grid((const void*)&k_down_stream<MT, NB, U, KS_, F8>, items, KS_)), \
-                     blk, 0, s, a)
-  if (ks == 1) BEAM_DN(1); else if (ks == 2) BEAM_DN(2); else BEAM_DN(4);
-#undef BEAM_DN
+  if (ks == 1) down_stream_k<MT, NB, U, 1, F8>(a, tiles, D, s);
+  else if (ks == 2) down_stream_k<MT, NB, U, 2, F8>(a, tiles, D, s);
+  else down_stream_k<MT, NB, U, 4, F8>(a, tiles, D, s);
 }
 
 // Streaming launches for tiles of 16, 32 or 64 rows.  Weight chunks are 128
@@ -821,6 +829,18 @@ static void gate_up_streaming(const beam_moe_layer& L, const ExpertArgs& a, long
   } else if (tile_rows == 32) {
     gate_up_stream<2, 2, 1, F8>(a, ntr, nts, L.I, Is_all, chunks >= 64 ? 4 : 2, s);
   } else {
+    if constexpr (!F8) {
+      // 64-row tiles, rows of fewer than 64 chunks (no k split): four row
+      // groups per item, so the tile's token rows are re-read once per 64
+      // weight rows instead of once per 32 (DeepSeek-V2-Lite shapes, T = 512:
+      // 168 -> 147 us on MI355X).  With the 4-way split of longer rows that
+      // variant would spill; with short intermediate rows (fine-grained,
+      // I = 256: 4 items per tile) it leaves too few items (60 -> 64 us).
+      if (chunks < 64 && L.I >= 1024) {
+        gate_up_stream_k<4, 4, 1, 1, F8>(a, ntr, nts, L.I, Is_all, s);
+        return;
+      }
+    }
     gate_up_stream<4, 2, 1, F8>(a, ntr, nts, L.I, Is_all, chunks >= 64 ? 4 : 1, s);
   }
 }
@@ -833,8 +853,14 @@ static void down_streaming(const beam_moe_layer& L, const ExpertArgs& a, long ti
     const int ks = stream_ksplit_chunks(chunks);
     if (tiles * (L.D / 32) * ks >= kWideShares) down_stream<1, 2, 1, F8>(a, tiles, L.D, ks, s);
     else down_stream<1, 1, 2, F8>(a, tiles, L.D, ks, s);
+  } else if constexpr (!F8) {
+    // 32- and 64-row tiles: four row groups per item (fewer re-reads of the
+    // tile's h rows per weight byte; T = 256: 84 -> 76 us, T = 512:
+    // 113 -> 92 us on MI355X, DeepSeek-V2-Lite shapes)
+    if (tile_rows == 32) down_stream_k<2, 4, 1, 2, F8>(a, tiles, L.D, s);
+    else down_stream<4, 4, 1, F8>(a, tiles, L.D, chunks >= 16 ? 2 : 1, s);
   } else if (tile_rows == 32) {
-    down_stream<2, 2, 1, F8>(a, tiles, L.D, 2, s);
+    down_stream_k<2, 2, 1, 2, F8>(a, tiles, L.D, s);
   } else {
     down_stream<4, 2, 1, F8>(a, tiles, L.D, chunks >= 16 ? 2 : 1, s);
   }
