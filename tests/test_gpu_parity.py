@@ -457,3 +457,56 @@ def test_stats_on_device_counts():
     ref = oracle.layer_stats(cfg, oracle.expert_counts(oracle.route(layer, x), cfg.E), T)
     for k, v in ref.items():
         assert st[k] == pytest.approx(v, rel=1e-12), k
+
+
+@pytest.mark.parametrize("T", [1, 64, 1400])
+def test_graph_capture_replays(T):
+    """beam_moe_forward captured once in a HIP graph and replayed on three
+    different batches copied into the captured input buffer (eager copies and
+    synchronisations between the replays): every replay's y and routing
+    outputs equal an eager call's bit for bit.  The forward path enqueues
+    kernels only (no memsets, allocations or host synchronisation), so it can
+    be captured; 1, 64 and 1400 tokens take the one-workgroup, bitmap-plan and
+    block-rank routing forms."""
+    import dynamic_expert_masking_amd as dm
+    from dynamic_expert_masking_amd.device import to_device, to_host_bits
+    name = "dsv2lite_decode"
+    cfg = synth.CONFIGS[name]
+    layer = cached_layer(name)
+    dl = device_layer(layer, key=name)
+    xs = [to_device(inputs(cfg, T, layer, f"graph{i}")) for i in range(3)]
+    ws = dl.workspace(T)
+    y_ref = []
+    route_ref = []
+    for i in range(3):
+        yi = torch.empty(T, cfg.D, dtype=dl.torch_dtype, device="cuda")
+        bufs, out = dl.route_buffers(T)
+        dm.beam_moe_forward(dl.desc, xs[i], T, yi, out, ws, ws.numel(), torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        y_ref.append(to_host_bits(yi).copy())
+        route_ref.append({k: v.cpu().numpy().copy() for k, v in bufs.items()})
+    x_static = xs[0].clone()
+    y_static = torch.empty(T, cfg.D, dtype=dl.torch_dtype, device="cuda")
+    bufs, out = dl.route_buffers(T)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # warm-up on a side stream before capture
+        dm.beam_moe_forward(dl.desc, x_static, T, y_static, out, ws, ws.numel(), side.cuda_stream)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    note(f"[graph] capture T={T}")
+    with torch.cuda.graph(graph):
+        dm.beam_moe_forward(dl.desc, x_static, T, y_static, out, ws, ws.numel(),
+                            torch.cuda.current_stream().cuda_stream)
+    for rep in range(2):
+        for i in (2, 0, 1):
+            x_static.copy_(xs[i])
+            y_static.fill_(0)
+            torch.cuda.synchronize()
+            note(f"[graph] replay {rep} batch {i} T={T}")
+            graph.replay()
+            torch.cuda.synchronize()
+            assert np.array_equal(to_host_bits(y_static), y_ref[i]), f"replay {rep} batch {i}: y differs"
+            for k, v in bufs.items():
+                assert np.array_equal(v.cpu().numpy(), route_ref[i][k]), f"replay {rep} batch {i}: {k} differs"
