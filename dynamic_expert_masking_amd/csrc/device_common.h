@@ -96,15 +96,20 @@ __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
 
 __device__ __forceinline__ float silu_f32(float a) { return a / (1.0f + expf(-a)); }
 
-// Order-preserving map from float to uint32 (-0 and +0 map together).
+// Order-preserving map from float to uint32: a larger float has a larger
+// key, and -0 and +0 map together (logits are never NaN).
 __device__ __forceinline__ uint32_t float_key(float f) {
   uint32_t u = __float_as_uint(f + 0.0f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
+// Inverse of float_key (-0 comes back as +0).
+__device__ __forceinline__ float key_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
 
-// ---- wave-wide reductions without LDS round trips -------------------------
+// ---- wave-wide sums without LDS round trips --------------------------------
 // Within each 16-lane row, rotations by 8, 4, 2, 1 (DPP row_ror) leave every
-// lane holding the row's reduction; the four row results are then read with
+// lane holding the row's sum; the four row results are then read with
 // v_readlane and combined in row order 0..3, so every lane receives the same,
 // order-fixed result.
 
@@ -113,47 +118,6 @@ __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
   return uint32_t(__builtin_amdgcn_update_dpp(0, int(v), CTRL, 0xF, 0xF, false));
 }
 constexpr int kRowRor1 = 0x121, kRowRor2 = 0x122, kRowRor4 = 0x124, kRowRor8 = 0x128;
-
-template <int CTRL>
-__device__ __forceinline__ unsigned long long dpp_u64(unsigned long long v) {
-  const uint32_t lo = dpp_u32<CTRL>(uint32_t(v));
-  const uint32_t hi = dpp_u32<CTRL>(uint32_t(v >> 32));
-  return (static_cast<unsigned long long>(hi) << 32) | lo;
-}
-
-__device__ __forceinline__ unsigned long long umax64(unsigned long long a, unsigned long long b) {
-  return a > b ? a : b;
-}
-
-__device__ __forceinline__ unsigned long long readlane_u64(unsigned long long v, int lane) {
-  const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(v)), lane));
-  const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(v >> 32)), lane));
-  return (static_cast<unsigned long long>(hi) << 32) | lo;
-}
-
-// Maximum over the wave of N independent 64-bit values at once (their DPP
-// steps are interleaved, so the N dependency chains overlap).
-template <int N>
-__device__ __forceinline__ void wave_max_u64_n(unsigned long long (&v)[N]) {
-#pragma unroll
-  for (int j = 0; j < N; ++j) v[j] = umax64(v[j], dpp_u64<kRowRor8>(v[j]));
-#pragma unroll
-  for (int j = 0; j < N; ++j) v[j] = umax64(v[j], dpp_u64<kRowRor4>(v[j]));
-#pragma unroll
-  for (int j = 0; j < N; ++j) v[j] = umax64(v[j], dpp_u64<kRowRor2>(v[j]));
-#pragma unroll
-  for (int j = 0; j < N; ++j) v[j] = umax64(v[j], dpp_u64<kRowRor1>(v[j]));
-#pragma unroll
-  for (int j = 0; j < N; ++j)
-    v[j] = umax64(umax64(readlane_u64(v[j], 0), readlane_u64(v[j], 16)),
-                  umax64(readlane_u64(v[j], 32), readlane_u64(v[j], 48)));
-}
-
-__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
-  unsigned long long a[1] = {v};
-  wave_max_u64_n<1>(a);
-  return a[0];
-}
 
 __device__ __forceinline__ float dpp_f32_ror(float v, int step) {
   const uint32_t u = __float_as_uint(v);
@@ -165,33 +129,6 @@ __device__ __forceinline__ float dpp_f32_ror(float v, int step) {
     default: r = dpp_u32<kRowRor1>(u); break;
   }
   return __uint_as_float(r);
-}
-
-constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
-
-// Maximum over the wave of N independent floats at once; the result is
-// wave-uniform.  Row maxima by rotations, then row_bcast15 / row_bcast31
-// carry them up so that lane 63 holds the wave maximum.
-template <int N>
-__device__ __forceinline__ void wave_max_f32_n(float (&v)[N]) {
-#pragma unroll
-  for (int j = 0; j < N; ++j) v[j] = fmaxf(v[j], __uint_as_float(dpp_u32<kRowRor8>(__float_as_uint(v[j]))));
-#pragma unroll
-  for (int j = 0; j < N; ++j) v[j] = fmaxf(v[j], __uint_as_float(dpp_u32<kRowRor4>(__float_as_uint(v[j]))));
-#pragma unroll
-  for (int j = 0; j < N; ++j) v[j] = fmaxf(v[j], __uint_as_float(dpp_u32<kRowRor2>(__float_as_uint(v[j]))));
-#pragma unroll
-  for (int j = 0; j < N; ++j) v[j] = fmaxf(v[j], __uint_as_float(dpp_u32<kRowRor1>(__float_as_uint(v[j]))));
-#pragma unroll
-  for (int j = 0; j < N; ++j)
-    v[j] = fmaxf(v[j], __uint_as_float(uint32_t(__builtin_amdgcn_update_dpp(
-                           int(__float_as_uint(v[j])), int(__float_as_uint(v[j])), kRowBcast15, 0xA, 0xF, false))));
-#pragma unroll
-  for (int j = 0; j < N; ++j)
-    v[j] = fmaxf(v[j], __uint_as_float(uint32_t(__builtin_amdgcn_update_dpp(
-                           int(__float_as_uint(v[j])), int(__float_as_uint(v[j])), kRowBcast31, 0xC, 0xF, false))));
-#pragma unroll
-  for (int j = 0; j < N; ++j) v[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[j]), 63));
 }
 
 // Sum over the wave; identical in every lane.

@@ -465,16 +465,6 @@ __device__ __forceinline__ float token_gate(int gating, bool slot, bool keep, fl
   return gh;
 }
 
-// Order-preserving 32-bit key of a float: a larger float has a larger key
-// (callers canonicalise -0 to +0; logits are never NaN).
-__device__ __forceinline__ uint32_t order_key(float v) {
-  const uint32_t u = __float_as_uint(v);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float key_value(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
-}
-
 constexpr int kTopKBufWords = 96;   // per-wave LDS scratch of select_topk
 
 // Top-K of one token by one wave.  Expert e = 64 i + lane has logit vals[i];
@@ -495,8 +485,8 @@ __device__ __forceinline__ void select_topk(const float (&vals)[NPER], int E, in
                                             uint32_t* buf, int& my_e, float& my_r) {
   uint32_t key[NPER];
 #pragma unroll
-  for (int i = 0; i < NPER; ++i) key[i] = (lane + kWave * i < E) ? order_key(vals[i]) : 0u;
-  // Present keys are at least order_key(-inf) > 0, and K <= E of them exist,
+  for (int i = 0; i < NPER; ++i) key[i] = (lane + kWave * i < E) ? float_key(vals[i]) : 0u;
+  // Present keys are at least float_key(-inf) > 0, and K <= E of them exist,
   // so the threshold p ends above 0 and absent experts are never selected.
   uint32_t p = 0;
   for (int b = 31; b >= 0; --b) {
@@ -557,7 +547,7 @@ __device__ __forceinline__ void select_topk(const float (&vals)[NPER], int E, in
   }
   __builtin_amdgcn_wave_barrier();
   my_e = slot ? int(ck[lane]) : 0;
-  my_r = slot ? key_value(sk[lane]) : 0.f;
+  my_r = slot ? key_float(sk[lane]) : 0.f;
 }
 
 // Token t's selection by one wave.  Expert e's logits are held by lane
