@@ -45,8 +45,8 @@ KERNEL_SOURCES = ("dynamic_expert_masking_amd/csrc/experts.hip",
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--config", default="dsv2lite_decode")
     p.add_argument("--tokens", type=int, default=None, help="batch size (default: 64 for decode)")
     p.add_argument("--copies", type=int, default=0, help="weight copies rotated (0 = auto)")
@@ -314,7 +314,10 @@ def main():
         cp = synth.CONFIGS["dsv2lite_prefill"]
         Tp = cp.tokens[-1]
         _, dlp, repsp, _ = setup(cp)
-        r = run_T(cp, dlp, repsp, Tp, max(5, args.steps // 5), 2, profile=False)
+        # warm-up touches every weight copy before the timed steps, as for the
+        # decode layer; 30 timed steps, since the first steps after an idle
+        # moment run slower (10 steps: 537 us per step, 30 steps: 479 us)
+        r = run_T(cp, dlp, repsp, Tp, max(30, args.steps // 2), len(repsp) + 3, profile=False)
         sec = r["ms_per_step"] / 1e3
         prefill = {"workload": f"{cp.name}: D={cp.D} E={cp.E} K={cp.K} I={cp.I} shared={cp.S}x{cp.I_s} "
                                f"T={Tp}, router bias N(0,1)",
