@@ -510,3 +510,43 @@ def test_graph_capture_replays(T):
             assert np.array_equal(to_host_bits(y_static), y_ref[i]), f"replay {rep} batch {i}: y differs"
             for k, v in bufs.items():
                 assert np.array_equal(v.cpu().numpy(), route_ref[i][k]), f"replay {rep} batch {i}: {k} differs"
+
+
+def _random_case(i: int):
+    """Seeded random small layer configuration number i."""
+    rng = np.random.default_rng(4242 + i)
+    E = int(rng.choice([3, 7, 16, 40, 64, 65, 100, 128, 129, 212, 256, 257, 300]))
+    K = int(rng.integers(1, min(E, 32) + 1))
+    D = int(rng.choice([64, 128, 192, 256, 512]))
+    I = int(rng.choice([64, 128, 192, 320]))
+    S = int(rng.choice([0, 0, 1, 2]))
+    I_s = int(rng.choice([64, 128])) if S else 0
+    keep = float(rng.uniform(0.1, 0.9))
+    router_bias = bool(rng.random() < 0.5)
+    T = int(rng.choice([1, 2, 5, 16, 17, 33, 64, 65, 200, 513, 700]))
+    gating = int(rng.choice([0, 0, 1, 2, 3, 4, 6]))
+    segment = int(rng.choice([0, 0, 0, 2, 5]))
+    dtype = "f32" if rng.random() < 0.15 else "bf16"
+    return dict(E=E, K=K, D=D, I=I, S=S, I_s=I_s, keep=keep, router_bias=router_bias, T=T,
+                gating=gating, segment=segment, dtype=dtype)
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_random_configs(case):
+    """Seeded random small configurations across the parameter space: 3 to 300
+    experts (every register width of the selection), K up to min(E, 32),
+    hidden and intermediate sizes from 64 to 512, no, one or two shared
+    experts, every gate option, segment routing, 1 to 700 tokens (every tile
+    height and routing form), bf16 and fp32.  Routing bit-exact against the
+    oracle, y within the dtype's tolerance."""
+    from oracle_pins import with_segment
+    c = _random_case(case)
+    note(f"[random config {case}] {c}")
+    base = small_layer(f"rand{case}", dtype=c["dtype"], D=c["D"], E=c["E"], K=c["K"], I=c["I"],
+                       S=c["S"], I_s=c["I_s"], keep=c["keep"], router_bias=c["router_bias"])
+    layer = with_segment(base, c["segment"], c["gating"])
+    x = small_x(base, c["T"], f"rand{case}")
+    y, rt, _ = run_forward(device_layer(layer), x)
+    rt_ref, y_ref = oracle.forward(layer, x)
+    check_routing(rt, rt_ref, c["E"])
+    check_output(y, y_ref, c["dtype"])
