@@ -550,3 +550,49 @@ def test_random_configs(case):
     rt_ref, y_ref = oracle.forward(layer, x)
     check_routing(rt, rt_ref, c["E"])
     check_output(y, y_ref, c["dtype"])
+
+
+def _random_fp8_case(i: int):
+    """Seeded random small FP8 layer configuration number i (hidden and
+    intermediate sizes multiples of 128, as the format requires)."""
+    rng = np.random.default_rng(5151 + i)
+    E = int(rng.choice([4, 12, 40, 64, 130]))
+    K = int(rng.integers(1, min(E, 8) + 1))
+    D = int(rng.choice([128, 256, 384, 512]))
+    I = int(rng.choice([128, 256, 384]))
+    S = int(rng.choice([0, 1, 2]))
+    I_s = int(rng.choice([128, 256])) if S else 0
+    T = int(rng.choice([1, 3, 16, 40, 129, 300, 600]))
+    return dict(E=E, K=K, D=D, I=I, S=S, I_s=I_s, keep=float(rng.uniform(0.2, 0.9)),
+                router_bias=bool(rng.random() < 0.5), T=T)
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_random_fp8_configs(case):
+    """Seeded random small FP8 (E4M3) layers with widely varying row scales,
+    1 to 600 tokens (16-, 32- and 64-row tiles): routing bit-exact, y within
+    the bf16 tolerance."""
+    from oracle_pins import fp8_layer
+    c = _random_fp8_case(case)
+    note(f"[random fp8 config {case}] {c}")
+    layer = _fp8_scaled(fp8_layer(f"rfp8_{case}", D=c["D"], E=c["E"], K=c["K"], I=c["I"], S=c["S"],
+                                  I_s=c["I_s"], keep=c["keep"], router_bias=c["router_bias"]),
+                        900 + case)
+    x = small_x(layer, c["T"], f"rfp8_{case}")
+    y, rt, _ = run_forward(device_layer(layer), x)
+    rt_ref, y_ref = oracle.forward(layer, x)
+    check_routing(rt, rt_ref, c["E"])
+    check_output(y, y_ref, "bf16")
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_random_mask_backward(case):
+    """The mask-router loss and straight-through gradient on seeded random
+    small layers (the random forward configurations' shapes, method's gate,
+    no segment routing)."""
+    c = _random_case(100 + case)
+    note(f"[random mask backward {case}] {c}")
+    layer = small_layer(f"rbwd{case}", dtype=c["dtype"], D=c["D"], E=c["E"], K=c["K"], I=c["I"],
+                        S=c["S"], I_s=c["I_s"], keep=c["keep"], router_bias=c["router_bias"])
+    x = small_x(layer, c["T"], f"rbwd{case}")
+    _mask_backward_case(layer, x, 0.2, 40 + case)
