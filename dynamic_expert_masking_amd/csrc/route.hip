@@ -276,8 +276,9 @@ hipError_t launch_router_logits(const beam_moe_layer& L, const void* x, int32_t 
 // passes of NT entries: wave-level scans, then the wave totals.
 template <int NT>
 __device__ void block_exclusive_scan2(int32_t* v1, int32_t* v2, int n,
-                                      int32_t* tmp /* >= 2 * NT / 64 entries */) {
+                                      int32_t* tmp /* >= 4 * NT / 64 + 2 entries */) {
   constexpr int NW = NT / kWave;
+  static_assert(NW <= kWave, "one wave scans the wave totals");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int32_t c1 = 0, c2 = 0;   // totals of the earlier passes
   for (int base = 0; base < n; base += NT) {
@@ -291,20 +292,29 @@ __device__ void block_exclusive_scan2(int32_t* v1, int32_t* v2, int n,
       tmp[NW + wave] = ib;
     }
     __syncthreads();
-    int32_t pa = c1, pb = c2;
-    for (int w = 0; w < NW; ++w) {
-      const int32_t ta = tmp[w], tb = tmp[NW + w];
-      if (w < wave) {
-        pa += ta;
-        pb += tb;
+    // wave 0 turns the wave totals into exclusive wave offsets and the pass
+    // totals, so that every wave then reads one entry per array
+    if (wave == 0) {
+      const int32_t ta = lane < NW ? tmp[lane] : 0;
+      const int32_t tb = lane < NW ? tmp[NW + lane] : 0;
+      const int32_t sa = wave_inclusive_scan_i32(ta, lane);
+      const int32_t sb = wave_inclusive_scan_i32(tb, lane);
+      if (lane < NW) {
+        tmp[2 * NW + lane] = sa - ta;
+        tmp[3 * NW + lane] = sb - tb;
       }
-      c1 += ta;
-      c2 += tb;
+      if (lane == NW - 1) {
+        tmp[4 * NW] = sa;
+        tmp[4 * NW + 1] = sb;
+      }
     }
+    __syncthreads();
     if (i < n) {
-      v1[i] = pa + ia - a;
-      v2[i] = pb + ib - b;
+      v1[i] = c1 + tmp[2 * NW + wave] + ia - a;
+      v2[i] = c2 + tmp[3 * NW + wave] + ib - b;
     }
+    c1 += tmp[4 * NW];
+    c2 += tmp[4 * NW + 1];
     __syncthreads();
   }
 }
@@ -313,7 +323,7 @@ struct PlanSmem {
   int32_t cnt[kMaxExperts];
   int32_t off[kMaxExperts];
   int32_t toff[kMaxExperts];
-  int32_t tmp[32];
+  int32_t tmp[4 * 1024 / kWave + 2];   // block_exclusive_scan2 scratch for 1024 threads
   int32_t act;
 };
 
@@ -325,7 +335,6 @@ __device__ void build_plan(PlanSmem& sm, int T, int E, int tile_rows, int has_sh
   if (tid == 0) sm.act = 0;
   for (int e = tid; e < E; e += NT) {
     const int32_t c = sm.cnt[e];
-    counts[e] = c;
     sm.off[e] = c;
     sm.toff[e] = (c + tile_rows - 1) / tile_rows;
   }
@@ -333,25 +342,28 @@ __device__ void build_plan(PlanSmem& sm, int T, int E, int tile_rows, int has_sh
   const int32_t last_cnt = sm.cnt[E - 1];
   const int32_t last_tiles = sm.toff[E - 1];
   block_exclusive_scan2<NT>(sm.off, sm.toff, E, sm.tmp);
+  for (int e0 = 0; e0 < E; e0 += NT) {   // whole waves, for the ballot
+    const int e = e0 + tid;
+    const unsigned long long act = __ballot(e < E && sm.cnt[e] > 0);
+    if (lane == 0 && act) atomicAdd(&sm.act, int32_t(__popcll(act)));
+  }
+  __syncthreads();
+  // The global outputs are stored after the last barrier.
   const int32_t P = sm.off[E - 1] + last_cnt;
   const int32_t ntr = sm.toff[E - 1] + last_tiles;
   const int32_t nts = has_shared ? (T + tile_rows - 1) / tile_rows : 0;
-  for (int e0 = 0; e0 < E; e0 += NT) {   // whole waves, for the ballot
-    const int e = e0 + tid;
-    const int32_t c = e < E ? sm.cnt[e] : 0;
-    const unsigned long long act = __ballot(c > 0);
-    if (lane == 0 && act) atomicAdd(&sm.act, int32_t(__popcll(act)));
-    if (e < E) {
-      expert_off[e] = sm.off[e];
-      const int nt = (c + tile_rows - 1) / tile_rows;
-      for (int j = 0; j < nt; ++j) {
-        Tile tl;
-        tl.expert = e;
-        tl.row0 = sm.off[e] + j * tile_rows;
-        tl.rows = min(tile_rows, c - j * tile_rows);
-        tl.pad = 0;
-        tiles[sm.toff[e] + j] = tl;
-      }
+  for (int e = tid; e < E; e += NT) {
+    const int32_t c = sm.cnt[e];
+    counts[e] = c;
+    expert_off[e] = sm.off[e];
+    const int nt = (c + tile_rows - 1) / tile_rows;
+    for (int j = 0; j < nt; ++j) {
+      Tile tl;
+      tl.expert = e;
+      tl.row0 = sm.off[e] + j * tile_rows;
+      tl.rows = min(tile_rows, c - j * tile_rows);
+      tl.pad = 0;
+      tiles[sm.toff[e] + j] = tl;
     }
   }
   for (int j = tid; j < nts; j += NT) {
@@ -362,7 +374,6 @@ __device__ void build_plan(PlanSmem& sm, int T, int E, int tile_rows, int has_sh
     tl.pad = 0;
     tiles[ntr + j] = tl;
   }
-  __syncthreads();
   if (tid == 0) {
     expert_off[E] = P;
     Plan pl;
@@ -372,7 +383,6 @@ __device__ void build_plan(PlanSmem& sm, int T, int E, int tile_rows, int has_sh
     pl.active_experts = sm.act;
     *plan = pl;
   }
-  __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
@@ -709,6 +719,10 @@ __global__ __launch_bounds__(1024) void k_select_plan(SelectArgs a) {
   __syncthreads();   // bits[] cleared
 
   const int t = wave;
+  // this wave's token outputs, stored at the end
+  int out_e = 0;
+  float out_g = 0.f, out_z = 0.f;
+  uint32_t out_mask = 0;
   if (t < T) {
     // r and z of token t: partial sums added in ks order, then the biases
     float rv[NPER], zv[NPER];
@@ -761,17 +775,13 @@ __global__ __launch_bounds__(1024) void k_select_plan(SelectArgs a) {
     const bool keep = slot && (a.all_pairs || z_k >= 0.f);
     const unsigned long long bal = __ballot(keep);
     const float gh = token_gate<NPER>(a.gating, slot, keep, r_k, r_all);
-    if (slot) {
-      a.idx[size_t(t) * K + lane] = e_k;
-      a.gates[size_t(t) * K + lane] = gh;
-      s_idx[t * 32 + lane] = e_k;
-      if (a.all_pairs) a.zsel[size_t(t) * K + lane] = z_k;
-    }
-    if (lane == 0) {
-      a.mask[t] = uint32_t(bal);
-      s_mask[t] = uint32_t(bal);
-    }
+    if (slot) s_idx[t * 32 + lane] = e_k;
+    if (lane == 0) s_mask[t] = uint32_t(bal);
     if (keep) atomicOr(&bits[e_k], 1ull << t);
+    out_e = e_k;
+    out_g = gh;
+    out_z = z_k;
+    out_mask = uint32_t(bal);
   }
   __syncthreads();
 
@@ -788,6 +798,14 @@ __global__ __launch_bounds__(1024) void k_select_plan(SelectArgs a) {
       a.perm_token[pos] = tl;
     }
     a.slot_pos[q] = pos;
+  }
+  if (t < T) {
+    if (lane < K) {
+      a.idx[size_t(t) * K + lane] = out_e;
+      a.gates[size_t(t) * K + lane] = out_g;
+      if (a.all_pairs) a.zsel[size_t(t) * K + lane] = out_z;
+    }
+    if (lane == 0) a.mask[t] = out_mask;
   }
 }
 
