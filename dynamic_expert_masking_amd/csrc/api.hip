@@ -119,6 +119,10 @@ using namespace beam;
 // Validation
 // ---------------------------------------------------------------------------
 
+// Largest element count that 32-bit row offsets reach (x [T][D], one expert's
+// weight matrix, the shared experts' stacked matrices).
+constexpr long kMaxOffsetElems = 0x7FFFFFFFL;
+
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 static int check_layer(const beam_moe_layer* L) {
@@ -148,6 +152,10 @@ static int check_layer(const beam_moe_layer* L) {
   if (L->D % 64 || L->I % 64 || L->D > 16384 || L->I > (1 << 20)) return BEAM_ERR_UNSUPPORTED;
   if (L->n_shared > 0 && (L->I_shared % 64 || long(L->n_shared) * L->I_shared > (1 << 20)))
     return BEAM_ERR_UNSUPPORTED;
+  // The tiled kernels address weight rows with 32-bit element offsets.
+  if (long(L->I) * L->D > kMaxOffsetElems ||
+      long(L->n_shared) * L->I_shared * L->D > kMaxOffsetElems)
+    return BEAM_ERR_UNSUPPORTED;
   if (L->expert_format != BEAM_WEIGHTS_DTYPE && L->expert_format != BEAM_WEIGHTS_FP8_E4M3)
     return BEAM_ERR_INVALID_ARG;
   if (L->expert_format == BEAM_WEIGHTS_FP8_E4M3) {
@@ -172,7 +180,7 @@ static int check_call(const beam_moe_layer* L, const void* x, int32_t T, void* w
   int st = check_layer(L);
   if (st != BEAM_OK) return st;
   if (T < 0) return BEAM_ERR_INVALID_ARG;
-  if (long(T) * L->K > (1L << 30)) return BEAM_ERR_UNSUPPORTED;
+  if (long(T) * L->K > (1L << 30) || long(T) * L->D > kMaxOffsetElems) return BEAM_ERR_UNSUPPORTED;
   if (T == 0) return BEAM_OK;
   if (!x || !aligned16(x)) return BEAM_ERR_INVALID_ARG;
   *lay = workspace_layout(*L, T);
@@ -232,7 +240,7 @@ extern "C" {
 
 size_t beam_moe_workspace_size(const beam_moe_layer* layer, int32_t T_max) {
   if (check_layer(layer) != BEAM_OK || T_max < 0) return 0;
-  if (long(T_max) * layer->K > (1L << 30)) return 0;
+  if (long(T_max) * layer->K > (1L << 30) || long(T_max) * layer->D > kMaxOffsetElems) return 0;
   return workspace_layout(*layer, T_max).total;
 }
 

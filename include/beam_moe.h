@@ -98,7 +98,11 @@ typedef enum { BEAM_WEIGHTS_DTYPE = 0, BEAM_WEIGHTS_FP8_E4M3 = 1 } beam_weight_f
 /* Layer description.  Shapes: D hidden, E routed experts, K top-K, I routed
  * expert intermediate size, n_shared shared experts of intermediate size
  * I_shared.  Supported: 1 <= K <= min(E, 32), E <= 1024, D, I and I_shared
- * multiples of 64, D <= 16384.  Every weight tensor has the layer's dtype,
+ * multiples of 64, D <= 16384, I <= 2^20, n_shared * I_shared <= 2^20, and
+ * I * D and n_shared * I_shared * D below 2^31 (the kernels address rows with
+ * 32-bit element offsets); per call T * K <= 2^30 and T * D < 2^31.  Shapes
+ * outside these give BEAM_ERR_UNSUPPORTED (workspace size 0).  Every weight
+ * tensor has the layer's dtype,
  * except the expert weights when expert_format is BEAM_WEIGHTS_FP8_E4M3.
  * Fields past `gating` may be left zero (= BEAM_WEIGHTS_DTYPE, no scales). */
 typedef struct {

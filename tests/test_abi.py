@@ -84,6 +84,9 @@ def test_workspace_size_monotone_and_invalid():
     (dict(n_shared=2, I_shared=0), dm.BEAM_ERR_INVALID_ARG),
     (dict(n_shared=1, I_shared=64), dm.BEAM_ERR_INVALID_ARG),       # shared pointers missing
     (dict(n_shared=1, I_shared=96, ws_gate=FAKE, ws_up=FAKE, ws_down=FAKE), dm.BEAM_ERR_UNSUPPORTED),
+    (dict(D=16384, I=131072), dm.BEAM_ERR_UNSUPPORTED),               # I * D = 2^31 elements
+    (dict(D=8192, n_shared=2, I_shared=131072, ws_gate=FAKE, ws_up=FAKE, ws_down=FAKE),
+     dm.BEAM_ERR_UNSUPPORTED),                                          # shared rows * D = 2^31
     # FP8 (E4M3) expert weights
     (dict(expert_format=2), dm.BEAM_ERR_INVALID_ARG),
     (dict(expert_format=1), dm.BEAM_ERR_INVALID_ARG),                  # scales missing
@@ -121,6 +124,12 @@ def test_forward_rejects_bad_calls():
     bad_out = dm.beam_route_out(FAKE, None, FAKE, FAKE)
     assert f(ctypes.byref(L), FAKE, 4, FAKE * 2, ctypes.byref(bad_out), FAKE * 3, big, None) \
         == dm.BEAM_ERR_INVALID_ARG
+    # x [T][D] of 2^31 elements or more is outside the kernels' 32-bit offsets
+    L2 = fake_layer(D=16384)
+    assert f(ctypes.byref(L2), FAKE, 131072, FAKE * 2, None, FAKE * 3, big, None) == dm.BEAM_ERR_UNSUPPORTED
+    assert dm.beam_moe_workspace_size(L2, 131072) == 0
+    assert dm.beam_moe_workspace_size(L2, 131071) > 0
+    assert dm.beam_moe_workspace_size(fake_layer(D=16384, I=131008), 1) > 0   # I * D just below 2^31
     # T = 0 is a no-op, even with no workspace
     assert f(ctypes.byref(L), FAKE, 0, FAKE * 2, None, None, 0, None) == dm.BEAM_OK
 
