@@ -89,10 +89,16 @@ def check_routing(rt_gpu: dict, rt_ref, E: int, tokens=None) -> None:
         assert np.array_equal(rt_gpu["expert_count"].astype(np.int64), ref_counts), "expert counts differ"
 
 
+# Every compared output's max|err| / max|y_ref|, by dtype (reported at the end
+# of the session by conftest.py).
+REL_ERRORS = {"bf16": [], "f32": []}
+
+
 def check_output(y_gpu: np.ndarray, y_ref: np.ndarray, dtype: str) -> float:
     scale = np.abs(y_ref).max()
     err = np.abs(y_gpu - y_ref).max()
     rel = err / scale if scale > 0 else err
+    REL_ERRORS[dtype].append(float(rel))
     assert err <= TOL[dtype] * max(scale, 1e-30) or (scale == 0 and err == 0), \
         f"max|err| {err:.3e} > {TOL[dtype]} * max|y_ref| {scale:.3e}"
     return rel
