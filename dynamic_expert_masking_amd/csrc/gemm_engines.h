@@ -23,6 +23,8 @@
 // both staged through LDS in 64-wide k slices with double buffering; 4 waves
 // in a 2 x 2 layout each own a 64 x BM/2 sub-tile of 16 x 16 MFMA blocks.
 #pragma once
+#include <type_traits>
+
 #include "device_common.h"
 
 namespace beam {
@@ -146,8 +148,11 @@ __device__ __forceinline__ void skinny_reduce(f32x4 (&acc)[NMAT][MT], f32x4* red
 // multiplied out of a padded LDS tile (row stride 144 bytes, so the 16 rows
 // read by 16 consecutive lanes hit distinct banks).  Loads are branch-free:
 // absent rows read row 0 of their operand and the slice past the end reads
-// one fixed address, so the compiler's load counters stay exact; absent rows
-// only feed accumulator rows or columns that the epilogues never store.
+// the first element of its bases, so the compiler's load counters stay exact;
+// absent rows only feed accumulator rows or columns that the epilogues never
+// store.  The MFMA loop is branch-free too: the number of a wave's 32-token
+// blocks that hold valid rows is decided once per tile (a wave-uniform
+// value), and the slice loop is instantiated for each count.
 // ---------------------------------------------------------------------------
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -183,6 +188,17 @@ struct TiledSmem {
 // acc[jn][jm][i] = C[n = (BN/2)*(wave&1) + 32*jn + 8*(i/4) + 4*(lane/32) + i%4]
 //                   [m = (BM/2)*(wave>>1) + 32*jm + lane%32]
 // MFMAs of 32-row token blocks at or past rows_valid are skipped.
+// Calls f(std::integral_constant<int, n>) for the runtime n in 0..J.
+template <int J, class F>
+__device__ __forceinline__ void tiled_dispatch(int n, F&& f) {
+  if constexpr (J == 0) {
+    f(std::integral_constant<int, 0>{});
+  } else {
+    if (n >= J) f(std::integral_constant<int, J>{});
+    else tiled_dispatch<J - 1>(n, f);
+  }
+}
+
 template <int BN, int BM, class Prov>
 __device__ __forceinline__ void tiled_accumulate(const Prov& pv, TiledSmem<BN, BM>& sm,
                                                  f32x16 (&acc)[BN / 64][BM / 64], int rows_valid) {
@@ -190,7 +206,10 @@ __device__ __forceinline__ void tiled_accumulate(const Prov& pv, TiledSmem<BN, B
   constexpr int WL = BN / 32;   // weight chunks per thread per slice
   constexpr int XL = BM / 32;   // token chunks per thread per slice
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  // The wave index is uniform across the wave; readfirstlane lets the compiler
+  // know it, so per-wave decisions below are scalar branches.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave & 1, wm = wave >> 1;
 #pragma unroll
   for (int a = 0; a < JN; ++a)
@@ -209,27 +228,27 @@ __device__ __forceinline__ void tiled_accumulate(const Prov& pv, TiledSmem<BN, B
   for (int i = 0; i < WL; ++i) wo[i] = pv.woff(lrow + 32 * i) + lcol;
 #pragma unroll
   for (int i = 0; i < XL; ++i) xo[i] = pv.xoff(lrow + 32 * i) + lcol;
-  const u16* const w_dummy = pv.wbase(0, 0);
-  const u16* const x_dummy = pv.xbase(0);
 
   struct Stage {
     u32x4 w[WL];
     u32x4 x[XL];
   };
-  // The slice past the end is loaded from one fixed address (all lanes the
-  // same, one cache line) so that every call issues the same loads.
+  // The slice past the end reads the first element of the last segment's
+  // bases (all lanes the same line), so that every call issues the same
+  // loads.  Its offsets are masked to zero with integer arithmetic: a select
+  // between two base pointers can become a branch around each load, and the
+  // join of such branches makes the compiler wait for every load in flight.
   auto load = [&](Stage& st, int c) {
-    const bool live = c < C;
+    const uint32_t msk = c < C ? ~0u : 0u;
     const int cc = min(c, C - 1);
     const int seg = cc / cps;
-    const uint32_t k = uint32_t(cc - seg * cps) * kTBK;
-    const u16* xb = live ? pv.xbase(seg) : x_dummy;
-    const uint32_t km = live ? k : 0u;
+    const uint32_t km = uint32_t(cc - seg * cps) * kTBK;
+    const u16* xb = pv.xbase(seg);
 #pragma unroll
     for (int i = 0; i < WL; ++i)   // this thread's row lrow + 32 i lies in row group i
-      st.w[i] = ld16_at_stream(live ? pv.wbase(i, seg) : w_dummy, live ? wo[i] + km : 0u);
+      st.w[i] = ld16_at_stream(pv.wbase(i, seg), (wo[i] + km) & msk);
 #pragma unroll
-    for (int i = 0; i < XL; ++i) st.x[i] = ld16_at(xb, live ? xo[i] + km : 0u);
+    for (int i = 0; i < XL; ++i) st.x[i] = ld16_at(xb, (xo[i] + km) & msk);
   };
   auto store = [&](const Stage& st) {
 #pragma unroll
@@ -241,36 +260,41 @@ __device__ __forceinline__ void tiled_accumulate(const Prov& pv, TiledSmem<BN, B
   };
   const int fr = lane & 31;
   const int fk = (lane >> 5) * 8;
-  auto compute = [&]() {
+  // The first NJ of this wave's 32-token blocks, straight-line code.
+  auto compute = [&](auto nj_const) {
+    constexpr int NJ = decltype(nj_const)::value;
 #pragma unroll
     for (int ks = 0; ks < kTBK / 16; ++ks) {
-      u32x4 wf[JN], xf[JM];
+      u32x4 wf[JN], xf[NJ > 0 ? NJ : 1];
 #pragma unroll
       for (int jn = 0; jn < JN; ++jn)
         wf[jn] = *reinterpret_cast<const u32x4*>(
             &sm.w[(wn * (BN / 2) + jn * 32 + fr) * kTLD + ks * 16 + fk]);
 #pragma unroll
-      for (int jm = 0; jm < JM; ++jm)
+      for (int jm = 0; jm < NJ; ++jm)
         xf[jm] = *reinterpret_cast<const u32x4*>(
             &sm.x[(wm * (BM / 2) + jm * 32 + fr) * kTLD + ks * 16 + fk]);
 #pragma unroll
-      for (int jm = 0; jm < JM; ++jm)
-        if (wm * (BM / 2) + jm * 32 < rows_valid) {
+      for (int jm = 0; jm < NJ; ++jm)
 #pragma unroll
-          for (int jn = 0; jn < JN; ++jn) acc[jn][jm] = mfma32_bf16(wf[jn], xf[jm], acc[jn][jm]);
-        }
+        for (int jn = 0; jn < JN; ++jn) acc[jn][jm] = mfma32_bf16(wf[jn], xf[jm], acc[jn][jm]);
     }
   };
-
-  Stage st;
-  load(st, 0);
-  for (int c = 0; c < C; ++c) {
-    store(st);          // slice c
-    __syncthreads();
-    load(st, c + 1);    // in flight while slice c is multiplied
-    compute();
-    __syncthreads();
-  }
+  auto run = [&](auto nj_const) {
+    Stage st;
+    load(st, 0);
+    for (int c = 0; c < C; ++c) {
+      store(st);          // slice c
+      __syncthreads();
+      load(st, c + 1);    // in flight while slice c is multiplied
+      if constexpr (decltype(nj_const)::value > 0) compute(nj_const);
+      __syncthreads();
+    }
+  };
+  // Token blocks of this wave that hold valid rows (a wave-uniform count),
+  // chosen once per tile so the slice loop has no branches around its MFMAs.
+  const int nj = min(JM, max(0, (rows_valid - wm * (BM / 2) + 31) / 32));
+  tiled_dispatch<JM>(nj, run);
 }
 
 // Persistent, XCD-aware work split: workgroups are dispatched round-robin over
