@@ -287,6 +287,9 @@ __device__ __forceinline__ void tiled_accumulate(const Prov& pv, TiledSmem<BN, B
       store(st);          // slice c
       __syncthreads();
       load(st, c + 1);    // in flight while slice c is multiplied
+      // Issue all of the next slice's loads before the MFMAs (the scheduler
+      // otherwise sinks some of them below the first MFMAs).
+      __builtin_amdgcn_sched_barrier(0);
       if constexpr (decltype(nj_const)::value > 0) compute(nj_const);
       __syncthreads();
     }
