@@ -644,37 +644,73 @@ __global__ __launch_bounds__(256) void k_down_f32(ExpertArgs a) {
 // pair and no shared expert gets exactly 0.
 // ---------------------------------------------------------------------------
 
-template <bool BF16>
+// The slots of a token are walked in chunks of KC: the O rows of a chunk are
+// loaded together (absent entries read row 0, a valid address), then added in
+// slot order; a select, not a product with 0, drops the absent ones, so the
+// sums are those of the plain slot loop.  With COMPACT the kept slots
+// (slot_pos >= 0) are first gathered, in slot order, at the front of the LDS
+// list and only those are walked; without it all K slots are.  Small batches
+// take KC > 1 (one load per slot in turn would wait out a memory latency per
+// kept slot): all K slots in one chunk when K <= 8, else the kept ones four at
+// a time.  Large batches take the kept slots one at a time (many resident
+// workgroups hide the latency, and padded loads would cost bandwidth).
+template <bool BF16, int KC, bool COMPACT>
 __global__ __launch_bounds__(256) void k_combine(int T, int D, int K, const float* __restrict__ gates,
                                                  const int32_t* __restrict__ slot_pos,
                                                  const void* __restrict__ o,
                                                  const void* __restrict__ o_sh, void* __restrict__ y) {
   __shared__ float s_g[32];
   __shared__ int32_t s_p[32];
+  __shared__ int s_n;
   const int t = blockIdx.x;
-  if (threadIdx.x < K) {
-    s_g[threadIdx.x] = gates[size_t(t) * K + threadIdx.x];
-    s_p[threadIdx.x] = slot_pos[size_t(t) * K + threadIdx.x];
+  if (threadIdx.x < 32) {   // wave 0
+    const int l = threadIdx.x;
+    const bool in = l < K;
+    const int32_t pl = in ? slot_pos[size_t(t) * K + l] : -1;
+    const float gl = in ? gates[size_t(t) * K + l] : 0.f;
+    if (COMPACT) {
+      const uint64_t kept = __ballot(pl >= 0);
+      s_p[l] = -1;
+      if (pl >= 0) {
+        const int r = __popcll(kept & ((1ull << l) - 1ull));
+        s_p[r] = pl;
+        s_g[r] = gl;
+      }
+      if (l == 0) s_n = __popcll(kept);
+    } else {
+      s_p[l] = pl;
+      s_g[l] = gl;
+    }
   }
   __syncthreads();
+  const int nk = COMPACT ? s_n : K;
   for (int d = threadIdx.x * 4; d < D; d += blockDim.x * 4) {
+    float4 sh = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (o_sh) sh = ld4_f32<BF16>(o_sh, size_t(t) * D + d);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int k = 0; k < K; ++k) {
-      const int p = s_p[k];
-      if (p < 0) continue;
-      const float g = s_g[k];
-      const float4 v = ld4_f32<BF16>(o, size_t(p) * D + d);
-      acc.x += g * v.x;
-      acc.y += g * v.y;
-      acc.z += g * v.z;
-      acc.w += g * v.w;
+    for (int k0 = 0; k0 < nk; k0 += KC) {
+      float4 v[KC];
+      int pk[KC];
+#pragma unroll
+      for (int j = 0; j < KC; ++j) {
+        pk[j] = s_p[k0 + j];
+        v[j] = ld4_f32<BF16>(o, size_t(pk[j] < 0 ? 0 : pk[j]) * D + d);
+      }
+#pragma unroll
+      for (int j = 0; j < KC; ++j) {
+        const float g = s_g[k0 + j];
+        const bool on = pk[j] >= 0;
+        acc.x = on ? acc.x + g * v[j].x : acc.x;
+        acc.y = on ? acc.y + g * v[j].y : acc.y;
+        acc.z = on ? acc.z + g * v[j].z : acc.z;
+        acc.w = on ? acc.w + g * v[j].w : acc.w;
+      }
     }
     if (o_sh) {
-      const float4 v = ld4_f32<BF16>(o_sh, size_t(t) * D + d);
-      acc.x += v.x;
-      acc.y += v.y;
-      acc.z += v.z;
-      acc.w += v.w;
+      acc.x += sh.x;
+      acc.y += sh.y;
+      acc.z += sh.z;
+      acc.w += sh.w;
     }
     if (BF16) {
       st4_bf16(static_cast<u16*>(y), size_t(t) * D + d, acc.x, acc.y, acc.z, acc.w);
@@ -941,12 +977,18 @@ hipError_t launch_combine(const beam_moe_layer& L, int32_t T, const Ptrs& p, voi
                           hipStream_t s) {
   const void* osh = L.n_shared > 0 ? p.o_shared : nullptr;
   prof_before("combine", s);
-  if (L.dtype == BEAM_F32)
-    hipLaunchKernelGGL(k_combine<false>, dim3(unsigned(T)), dim3(256), 0, s, T, L.D, L.K, p.gates,
-                       p.slot_pos, p.o, osh, y);
-  else
-    hipLaunchKernelGGL(k_combine<true>, dim3(unsigned(T)), dim3(256), 0, s, T, L.D, L.K, p.gates,
-                       p.slot_pos, p.o, osh, y);
+  // Below 1024 tokens: all K slots in one chunk when K <= 8, else the kept
+  // slots four at a time; from 1024 tokens: the kept slots one at a time.
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(unsigned(T)), dim3(256), 0, s, T, L.D, L.K, p.gates, p.slot_pos,
+                       p.o, osh, y);
+  };
+  const bool bf = L.dtype != BEAM_F32;
+  if (T >= 1024) bf ? go(k_combine<true, 1, true>) : go(k_combine<false, 1, true>);
+  else if (L.K <= 2) bf ? go(k_combine<true, 2, false>) : go(k_combine<false, 2, false>);
+  else if (L.K <= 4) bf ? go(k_combine<true, 4, false>) : go(k_combine<false, 4, false>);
+  else if (L.K <= 8) bf ? go(k_combine<true, 8, false>) : go(k_combine<false, 8, false>);
+  else bf ? go(k_combine<true, 4, true>) : go(k_combine<false, 4, true>);
   prof_after(s);
   return hipGetLastError();
 }
