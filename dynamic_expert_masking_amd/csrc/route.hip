@@ -628,26 +628,6 @@ struct BitmapPlanSmem {
   PlanSmem plan;
 };
 
-// Copies n entries of src (global) into dst (LDS), four independent loads in
-// flight per thread.
-template <int NT, class S, class D>
-__device__ __forceinline__ void stage_to_lds(D* dst, const S* __restrict__ src, int n) {
-  const int tid = threadIdx.x;
-  for (int i0 = 0; i0 < n; i0 += 4 * NT) {
-    S v[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = i0 + u * NT + tid;
-      v[u] = src[i < n ? i : 0];
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = i0 + u * NT + tid;
-      if (i < n) dst[i] = D(v[u]);
-    }
-  }
-}
-
 // One wave per token, NT / 64 tokens per workgroup.
 template <int NPER, int NT>
 __global__ __launch_bounds__(NT) void k_select_tokens(SelectArgs a) {
@@ -668,8 +648,23 @@ __global__ __launch_bounds__(NT) void k_plan_bitmap(SelectArgs a) {
   const int T = a.T, E = a.E, K = a.K;
   const int W = (T + kSelBlock - 1) / kSelBlock;
   const int TK = T * K;
-  stage_to_lds<NT>(sm.mask, a.mask, T);
-  stage_to_lds<NT>(sm.idx, a.idx, TK);
+  // masks and indices copied together: both arrays' loads in flight at once
+  for (int i0 = 0; i0 < max(T, TK); i0 += 4 * NT) {
+    uint32_t vm[4];
+    int32_t vi[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * NT + tid;
+      vm[u] = a.mask[i < T ? i : 0];
+      vi[u] = a.idx[i < TK ? i : 0];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * NT + tid;
+      if (i < T) sm.mask[i] = vm[u];
+      if (i < TK) sm.idx[i] = uint16_t(vi[u]);
+    }
+  }
   for (int i = tid; i < E * W; i += NT) sm.bits[i] = 0ull;
   __syncthreads();
   for (int q = tid; q < TK; q += NT) {
