@@ -560,39 +560,92 @@ __device__ __forceinline__ void select_topk(const float (&vals)[NPER], int E, in
   my_r = slot ? key_float(sk[lane]) : 0.f;
 }
 
+// r and z of token t for this lane's experts (e = lane + 64 i): the KS
+// partial sums added in ks order, then the biases; experts past E give 0.
+// Every load is issued unconditionally (absent experts read expert 0 and are
+// dropped by a select) so that they are in flight together: a branch around
+// each load compiles to a wait for it.  With NPER >= 16 the partial sums are
+// read one ks slice per round, to bound the registers.
+template <int NPER, int KS>
+__device__ __forceinline__ void token_logits_k(const SelectArgs& a, int t, int lane,
+                                               float (&rv)[NPER], float (&zv)[NPER]) {
+  const int E = a.E;
+  const float* row = a.part + size_t(route_row(a, t)) * 2 * E;
+  const size_t kstride = size_t(a.T) * 2 * E;
+  const float* brp = a.br ? a.br : a.part;   // a valid address either way
+  const float* bmp = a.bm ? a.bm : a.part;
+  // with NPER >= 16 the biases are read after the partial sums (registers)
+  constexpr bool kBiasFirst = NPER < 16;
+  auto ee = [&](int i) {   // expert of register slot i, or 0 past E
+    const int e = lane + kWave * i;
+    return e < E ? e : 0;
+  };
+  float bb[NPER], bz[NPER];
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    if (kBiasFirst) {
+      bb[i] = brp[ee(i)];
+      bz[i] = bmp[ee(i)];
+    }
+    rv[i] = zv[i] = 0.f;
+  }
+  constexpr int KB = NPER >= 16 ? 1 : KS;   // ks slices per round
+#pragma unroll
+  for (int k0 = 0; k0 < KS; k0 += KB) {
+    float pr[KB][NPER], pz[KB][NPER];
+#pragma unroll
+    for (int u = 0; u < KB; ++u)
+#pragma unroll
+      for (int i = 0; i < NPER; ++i) {
+        pr[u][i] = row[size_t(k0 + u) * kstride + ee(i)];
+        pz[u][i] = row[size_t(k0 + u) * kstride + E + ee(i)];
+      }
+#pragma unroll
+    for (int u = 0; u < KB; ++u)
+#pragma unroll
+      for (int i = 0; i < NPER; ++i) {
+        rv[i] += pr[u][i];
+        zv[i] += pz[u][i];
+      }
+  }
+  if (!kBiasFirst) {
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) {
+      bb[i] = brp[ee(i)];
+      bz[i] = bmp[ee(i)];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    const bool ok = lane + kWave * i < E;
+    rv[i] = ok ? rv[i] + (a.br ? bb[i] : 0.f) : 0.f;
+    zv[i] = ok ? zv[i] + (a.bm ? bz[i] : 0.f) : 0.f;
+  }
+}
+
+template <int NPER>
+__device__ __forceinline__ void token_logits(const SelectArgs& a, int t, int lane,
+                                             float (&rv)[NPER], float (&zv)[NPER]) {
+  switch (a.KS) {   // uniform
+    case 1: token_logits_k<NPER, 1>(a, t, lane, rv, zv); break;
+    case 2: token_logits_k<NPER, 2>(a, t, lane, rv, zv); break;
+    case 3: token_logits_k<NPER, 3>(a, t, lane, rv, zv); break;
+    default: token_logits_k<NPER, 4>(a, t, lane, rv, zv); break;
+  }
+}
+
 // Token t's selection by one wave.  Expert e's logits are held by lane
 // e % 64 in register e / 64; the KS partial sums are added in ks order, then
 // the biases; select_topk picks the K.  buf: the wave's select_topk scratch.
 template <int NPER>
 __device__ __forceinline__ void select_token(const SelectArgs& a, int t, int lane, uint32_t* buf) {
   const int E = a.E, K = a.K;
-  float pr[4][NPER], pz[4][NPER];
-#pragma unroll
-  for (int u = 0; u < 4; ++u)
-#pragma unroll
-    for (int i = 0; i < NPER; ++i) {
-      const int e = lane + kWave * i;
-      pr[u][i] = pz[u][i] = 0.f;
-      if (u < a.KS && e < E) {
-        const float* row = a.part + (size_t(u) * a.T + route_row(a, t)) * 2 * E;
-        pr[u][i] = row[e];
-        pz[u][i] = row[E + e];
-      }
-    }
-  float vals[NPER], zv[NPER];
+  float rv[NPER], vals[NPER], zv[NPER];
+  token_logits<NPER>(a, t, lane, rv, zv);
 #pragma unroll
   for (int i = 0; i < NPER; ++i) {
     const int e = lane + kWave * i;
-    float r = 0.f, z = 0.f;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      r += pr[u][i];
-      z += pz[u][i];
-    }
-    r += (a.br && e < E) ? a.br[e] : 0.f;
-    z += (a.bm && e < E) ? a.bm[e] : 0.f;
-    vals[i] = e < E ? r + 0.0f : -__builtin_inff();   // + 0: -0 and +0 compare alike
-    zv[i] = z;
+    vals[i] = e < E ? rv[i] + 0.0f : -__builtin_inff();   // + 0: -0 and +0 compare alike
   }
   float r_all[NPER];
 #pragma unroll
@@ -706,7 +759,6 @@ __global__ __launch_bounds__(1024) void k_select_plan(SelectArgs a) {
   __shared__ uint32_t s_mask[kSelWaves];
   __shared__ PlanSmem s_plan;
   __shared__ uint32_t sbuf[kSelWaves][kTopKBufWords];
-  constexpr int KB = NPER >= 16 ? 1 : 4;   // partial slices loaded per round
   static_assert(kSelMergedMax <= kSelWaves, "one token per wave");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int T = a.T, E = a.E, K = a.K;
@@ -721,36 +773,11 @@ __global__ __launch_bounds__(1024) void k_select_plan(SelectArgs a) {
   if (t < T) {
     // r and z of token t: partial sums added in ks order, then the biases
     float rv[NPER], zv[NPER];
-#pragma unroll
-    for (int i = 0; i < NPER; ++i) rv[i] = zv[i] = 0.f;
-    for (int ks0 = 0; ks0 < a.KS; ks0 += KB) {
-      float pr[KB][NPER], pz[KB][NPER];
-#pragma unroll
-      for (int u = 0; u < KB; ++u)
-#pragma unroll
-        for (int i = 0; i < NPER; ++i) {
-          const int e = lane + kWave * i;
-          pr[u][i] = pz[u][i] = 0.f;
-          if (ks0 + u < a.KS && e < E) {
-            const float* row = a.part + (size_t(ks0 + u) * T + route_row(a, t)) * 2 * E;
-            pr[u][i] = row[e];
-            pz[u][i] = row[E + e];
-          }
-        }
-#pragma unroll
-      for (int u = 0; u < KB; ++u)
-#pragma unroll
-        for (int i = 0; i < NPER; ++i) {
-          rv[i] += pr[u][i];
-          zv[i] += pz[u][i];
-        }
-    }
+    token_logits<NPER>(a, t, lane, rv, zv);
     float vals[NPER], r_all[NPER];
 #pragma unroll
     for (int i = 0; i < NPER; ++i) {
       const int e = lane + kWave * i;
-      rv[i] += (a.br && e < E) ? a.br[e] : 0.f;
-      zv[i] += (a.bm && e < E) ? a.bm[e] : 0.f;
       vals[i] = e < E ? rv[i] + 0.0f : -__builtin_inff();   // + 0: -0 == +0
       r_all[i] = e < E ? rv[i] : -__builtin_inff();
     }
