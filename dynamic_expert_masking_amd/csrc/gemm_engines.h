@@ -179,15 +179,6 @@ struct TiledSmem {
   u16 x[BM * kTLD];
 };
 
-// Provider interface (per tile):
-//   int nseg(), seg_chunks()
-//   const u16* wbase(g, seg)    uniform base of weight rows [32g, 32g+32) in segment seg
-//   uint32_t   woff(r)          element offset of weight row r (0..BN-1) from its base
-//   const u16* xbase(seg)       uniform base of the token rows in segment seg
-//   uint32_t   xoff(r)          element offset of token row r (0..BM-1) from xbase
-// acc[jn][jm][i] = C[n = (BN/2)*(wave&1) + 32*jn + 8*(i/4) + 4*(lane/32) + i%4]
-//                   [m = (BM/2)*(wave>>1) + 32*jm + lane%32]
-// MFMAs of 32-row token blocks at or past rows_valid are skipped.
 // Calls f(std::integral_constant<int, n>) for the runtime n in 0..J.
 template <int J, class F>
 __device__ __forceinline__ void tiled_dispatch(int n, F&& f) {
@@ -199,6 +190,15 @@ __device__ __forceinline__ void tiled_dispatch(int n, F&& f) {
   }
 }
 
+// Provider interface (per tile):
+//   int nseg(), seg_chunks()
+//   const u16* wbase(g, seg)    uniform base of weight rows [32g, 32g+32) in segment seg
+//   uint32_t   woff(r)          element offset of weight row r (0..BN-1) from its base
+//   const u16* xbase(seg)       uniform base of the token rows in segment seg
+//   uint32_t   xoff(r)          element offset of token row r (0..BM-1) from xbase
+// acc[jn][jm][i] = C[n = (BN/2)*(wave&1) + 32*jn + 8*(i/4) + 4*(lane/32) + i%4]
+//                   [m = (BM/2)*(wave>>1) + 32*jm + lane%32]
+// MFMAs of 32-row token blocks at or past rows_valid are skipped.
 template <int BN, int BM, class Prov>
 __device__ __forceinline__ void tiled_accumulate(const Prov& pv, TiledSmem<BN, BM>& sm,
                                                  f32x16 (&acc)[BN / 64][BM / 64], int rows_valid) {
