@@ -915,7 +915,11 @@ hipError_t launch_select(const beam_moe_layer& L, int32_t T, int tile_rows, cons
     prof_after(s);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     prof_before("plan_bitmap", s);
-    hipLaunchKernelGGL((k_plan_bitmap<kPlanThreads>), dim3(1), dim3(kPlanThreads), 0, s, a);
+    // small batches: 4 waves reach each barrier sooner than 16 (T=64: 7.45 -> 7.2 us)
+    if (long(T) * L.K <= 2048)
+      hipLaunchKernelGGL((k_plan_bitmap<256>), dim3(1), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_plan_bitmap<kPlanThreads>), dim3(1), dim3(kPlanThreads), 0, s, a);
     prof_after(s);
     return hipGetLastError();
   }
