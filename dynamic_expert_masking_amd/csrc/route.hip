@@ -752,8 +752,8 @@ __global__ __launch_bounds__(NT) void k_plan_bitmap(SelectArgs a) {
 // (its partial logit slices loaded in one round), then the same workgroup
 // builds the plan from the batch's per-expert token bitmaps in LDS, as
 // k_plan_bitmap does: one launch instead of two.
-template <int NPER>
-__global__ __launch_bounds__(1024) void k_select_plan(SelectArgs a) {
+template <int NPER, int NT>
+__global__ __launch_bounds__(NT) void k_select_plan(SelectArgs a) {
   __shared__ unsigned long long bits[kMaxExperts];
   __shared__ int32_t s_idx[kSelWaves * 32];
   __shared__ uint32_t s_mask[kSelWaves];
@@ -810,7 +810,7 @@ __global__ __launch_bounds__(1024) void k_select_plan(SelectArgs a) {
   PlanSmem& pl = s_plan;
   for (int e = tid; e < E; e += blockDim.x) pl.cnt[e] = __popcll(bits[e]);
   __syncthreads();
-  build_plan<1024>(pl, T, E, a.tile_rows, a.has_shared, a.counts, a.expert_off, a.plan, a.tiles);
+  build_plan<NT>(pl, T, E, a.tile_rows, a.has_shared, a.counts, a.expert_off, a.plan, a.tiles);
   for (int q = tid; q < T * K; q += blockDim.x) {
     const int tl = q / K, k = q - tl * K;
     int pos = -1;
@@ -897,10 +897,16 @@ hipError_t launch_select(const beam_moe_layer& L, int32_t T, int tile_rows, cons
   // in one workgroup costs more than the second launch saves.
   if (T <= kSelMergedMax) {
     prof_before("select_plan", s);
-    if (L.E <= 64) hipLaunchKernelGGL((k_select_plan<1>), dim3(1), dim3(1024), 0, s, a);
-    else if (L.E <= 128) hipLaunchKernelGGL((k_select_plan<2>), dim3(1), dim3(1024), 0, s, a);
-    else if (L.E <= 256) hipLaunchKernelGGL((k_select_plan<4>), dim3(1), dim3(1024), 0, s, a);
-    else hipLaunchKernelGGL((k_select_plan<16>), dim3(1), dim3(1024), 0, s, a);
+    // one wave per token: 4 waves for up to 4 tokens (fewer waves at each
+    // barrier), else 16
+    auto go = [&](auto k4, auto k16) {
+      if (T <= 4) hipLaunchKernelGGL(k4, dim3(1), dim3(256), 0, s, a);
+      else hipLaunchKernelGGL(k16, dim3(1), dim3(1024), 0, s, a);
+    };
+    if (L.E <= 64) go(k_select_plan<1, 256>, k_select_plan<1, 1024>);
+    else if (L.E <= 128) go(k_select_plan<2, 256>, k_select_plan<2, 1024>);
+    else if (L.E <= 256) go(k_select_plan<4, 256>, k_select_plan<4, 1024>);
+    else go(k_select_plan<16, 256>, k_select_plan<16, 1024>);
     prof_after(s);
     return hipGetLastError();
   }
