@@ -25,6 +25,21 @@ int expert_tile_rows(const beam_moe_layer& L, int32_t T) {
   return 256;
 }
 
+// Rows of router partial logits ([KS][T] of them) that the workspace holds
+// for a batch of T tokens: an upper bound on KS(T') * T' over every T' <= T,
+// so that a workspace sized for T_max serves every smaller batch (KS rises as
+// T falls).  The router splits k at most 4 ways and only while its grid has
+// fewer than 256 / (KS - 1) workgroups; with at least ceil(T / 64) token
+// blocks that needs T < 16384 for a 2-way split, T <= 8128 for 3 and
+// T <= 5440 for 4.  A maximum of non-decreasing terms, so the bound (and the
+// whole workspace size) is non-decreasing in T.
+long router_logit_rows(const beam_moe_layer& L, int32_t T) {
+  if (L.dtype == BEAM_F32) return T;
+  const long t = T;
+  return std::max({t, 2 * std::min<long>(t, 16383), 3 * std::min<long>(t, 8128),
+                   4 * std::min<long>(t, 5440)});
+}
+
 WsLayout workspace_layout(const beam_moe_layer& L, int32_t T) {
   WsLayout w;
   const size_t TK = size_t(T) * L.K;
@@ -40,7 +55,7 @@ WsLayout workspace_layout(const beam_moe_layer& L, int32_t T) {
     return o;
   };
   w.plan = take(sizeof(Plan));
-  w.logits = take(size_t(router_ksplit(L, T)) * T * 2 * L.E * 4);
+  w.logits = take(size_t(router_logit_rows(L, T)) * 2 * L.E * 4);
   w.idx = take(TK * 4);
   w.gates = take(TK * 4);
   w.mask = take(size_t(T) * 4);

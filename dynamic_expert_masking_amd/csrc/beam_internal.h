@@ -42,6 +42,9 @@ struct WsLayout {
 
 // Number of k slices of the router logits (partial sums added by selection).
 int router_ksplit(const beam_moe_layer& L, int32_t T);
+// Rows of partial logits the workspace reserves (>= router_ksplit(L, T') * T'
+// for every T' <= T; non-decreasing in T).
+long router_logit_rows(const beam_moe_layer& L, int32_t T);
 // Row-tile height of the expert kernels (multiple of 16).
 int expert_tile_rows(const beam_moe_layer& L, int32_t T);
 WsLayout workspace_layout(const beam_moe_layer& L, int32_t T);

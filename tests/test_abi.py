@@ -71,6 +71,45 @@ def test_workspace_size_monotone_and_invalid():
     assert dm.beam_moe_workspace_size(fake_layer(**f8), 64) == sizes[2]
 
 
+def config_layer(cfg):
+    """A descriptor with a workload's shapes and fake (never dereferenced) pointers."""
+    kw = dict(D=cfg.D, E=cfg.E, K=cfg.K, I=cfg.I,
+              dtype=dm.BEAM_F32 if cfg.dtype == "f32" else dm.BEAM_BF16)
+    if cfg.S:
+        kw.update(n_shared=cfg.S, I_shared=cfg.I_s, ws_gate=FAKE, ws_up=FAKE, ws_down=FAKE)
+    if cfg.expert_format == synth.FP8:
+        kw.update(expert_format=dm.WEIGHTS_FP8_E4M3, scale_gate=FAKE, scale_up=FAKE, scale_down=FAKE,
+                  scale_shared_gate=FAKE, scale_shared_up=FAKE, scale_shared_down=FAKE)
+    return fake_layer(**kw)
+
+
+@pytest.mark.parametrize("name", synth.CONFIG_ORDER)
+def test_workspace_serves_every_smaller_batch(name):
+    """A workspace sized for T_max serves every batch T <= T_max: the size is
+    non-decreasing in T (the router's k split, and so its partial-logit rows,
+    rises as T falls; the workspace reserves a bound that does not), so
+    ws(T) <= ws(T_max) for every T <= T_max; and a workspace one byte short
+    of ws(T) is rejected before any launch.  (No call here is given enough
+    workspace to pass validation: it would launch kernels on fake pointers.)"""
+    L = config_layer(synth.CONFIGS[name])
+    Ts = list(range(0, 1100)) + list(range(1100, 17000, 7)) + [4080, 5440, 5441, 8128, 8129,
+                                                               16383, 16384, 16385]
+    Ts = sorted(set(Ts))
+    sizes = [dm.beam_moe_workspace_size(L, T) for T in Ts]
+    for (t0, a), (t1, b) in zip(zip(Ts, sizes), zip(Ts[1:], sizes[1:])):
+        assert a <= b, f"workspace size drops from T={t0} ({a}) to T={t1} ({b})"
+    f = dm.lib().beam_moe_forward
+    for T_max in (161, 497, 1360, 4080):
+        need = dm.beam_moe_workspace_size(L, T_max)
+        for T in sorted({1, 2, 48, 64, 144, 160, 496, T_max - 1, T_max}):
+            if T > T_max:
+                continue
+            # a workspace one byte short of ws(T) is rejected; ws(T_max) is not
+            assert f(ctypes.byref(L), FAKE, T, FAKE * 2, None, FAKE * 3,
+                     dm.beam_moe_workspace_size(L, T) - 1, None) == dm.BEAM_ERR_WORKSPACE
+            assert dm.beam_moe_workspace_size(L, T) <= need
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(K=0), dm.BEAM_ERR_INVALID_ARG),
     (dict(K=9), dm.BEAM_ERR_INVALID_ARG),

@@ -217,13 +217,14 @@ def _tied_layer(E, K):
 
 
 @pytest.mark.parametrize("E,K", [(40, 7), (100, 32), (212, 16), (700, 5)])
-@pytest.mark.parametrize("T", [9, 70, 1200])
+@pytest.mark.parametrize("T", [2, 9, 70, 1200])
 def test_topk_ties(E, K, T):
     """Top-K with many exactly equal logits (equal logits go to the lower
     expert index, also at the boundary of the K kept), for every register
     width of the selection (E <= 64, 128, 256, 1024) and each selection form:
-    9 tokens (one workgroup selects and plans), 70 (one wave per token, then
-    the bitmap plan) and 1200 (64-token blocks, scan, scatter)."""
+    2 tokens (one 4-wave workgroup selects and plans), 9 (the same with 16
+    waves), 70 (one wave per token, then the bitmap plan) and 1200 (64-token
+    blocks, scan, scatter)."""
     layer = _tied_layer(E, K)
     rng = np.random.default_rng(7 + T)
     x = synth.f32_to_bf16_bits(rng.choice(np.array([-1.0, 0.0, 1.0, 2.0], np.float32),
