@@ -104,6 +104,8 @@ def lib() -> ctypes.CDLL:
         L.beam_profile_begin.restype = ctypes.c_int
         L.beam_profile_end.argtypes = [P(ctypes.c_char_p), P(I32), P(ctypes.c_double), I32]
         L.beam_profile_end.restype = ctypes.c_int
+        L.beam_mfma_loop.argtypes = [VP, I32, I32, VP]
+        L.beam_mfma_loop.restype = ctypes.c_int
         L.beam_copy_kernel.argtypes = [VP, VP, SZ, VP]
         L.beam_copy_kernel.restype = ctypes.c_int
         _lib = L
@@ -205,3 +207,8 @@ def beam_profile_end(max_out: int = 64) -> dict:
 
 def beam_copy_kernel(dst, src, nbytes: int, stream: int = 0) -> None:
     _check(lib().beam_copy_kernel(_ptr(dst), _ptr(src), int(nbytes), stream), "beam_copy_kernel")
+
+
+def beam_mfma_loop(out, blocks: int, iters: int, stream: int = 0) -> None:
+    """MFMA throughput probe (see the header); out holds blocks * 256 floats."""
+    _check(lib().beam_mfma_loop(_ptr(out), int(blocks), int(iters), stream), "beam_mfma_loop")

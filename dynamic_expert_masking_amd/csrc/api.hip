@@ -432,6 +432,15 @@ int beam_profile_end(const char** names, int32_t* launches, double* total_ms, in
   return n;
 }
 
+int beam_mfma_loop(float* out, int32_t blocks, int32_t iters, void* stream) {
+  if (!out || (reinterpret_cast<uintptr_t>(out) & 3u) || blocks <= 0 || iters <= 0 ||
+      blocks > (1 << 20))
+    return BEAM_ERR_INVALID_ARG;
+  return launch_mfma_loop(out, blocks, iters, static_cast<hipStream_t>(stream)) == hipSuccess
+             ? BEAM_OK
+             : BEAM_ERR_HIP;
+}
+
 int beam_copy_kernel(void* dst, const void* src, size_t bytes, void* stream) {
   if (!dst || !src || bytes % 16 || !aligned16(dst) || !aligned16(src)) return BEAM_ERR_INVALID_ARG;
   if (bytes == 0) return BEAM_OK;

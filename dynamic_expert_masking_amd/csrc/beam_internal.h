@@ -96,6 +96,7 @@ hipError_t launch_down(const beam_moe_layer& L, int32_t T, int tile_rows, const 
 hipError_t launch_combine(const beam_moe_layer& L, int32_t T, const Ptrs& p, void* y,
                           hipStream_t s);
 hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t s);
+hipError_t launch_mfma_loop(float* out, int blocks, int iters, hipStream_t s);
 // Mask-router backward from the all-pairs expert outputs O: per-pair dL/dz and
 // per-token sums of m_hat, then dL/dWm, dL/db_m and L_reg.
 hipError_t launch_mask_grad(const beam_moe_layer& L, const void* x, const void* dy, int32_t T,

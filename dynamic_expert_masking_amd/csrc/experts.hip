@@ -1003,6 +1003,40 @@ __global__ __launch_bounds__(256) void k_copy16(uint4* __restrict__ dst,
     dst[i] = src[i];
 }
 
+// MFMA throughput probe: every wave runs `iters` rounds of four independent
+// v_mfma_f32_32x32x16_bf16 accumulation chains on register operands (the
+// chains keep the matrix unit busy across their latency), then stores the
+// sum of its accumulators so the work is kept.  FLOPs per launch:
+// blocks * 4 waves * iters * 4 * (2 * 32 * 32 * 16).
+__global__ __launch_bounds__(256) void k_mfma_loop(float* __restrict__ out, int iters) {
+  const int lane = threadIdx.x & 63;
+  // bf16 values 2^-8 .. (lane-dependent), so that sums stay small and finite
+  const uint32_t va = 0x3B803B80u + (uint32_t(lane & 7) << 16);
+  const u32x4 a = u32x4{va, va, va, va}, b = u32x4{0x3B803B80u, 0x3B803B80u, 0x3B803B80u, 0x3B803B80u};
+  f32x16 acc[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[c][i] = 0.f;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[c] = mfma32_bf16(a, b, acc[c]);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s += acc[c][i];
+  out[size_t(blockIdx.x) * blockDim.x + threadIdx.x] = s;
+}
+
+hipError_t launch_mfma_loop(float* out, int blocks, int iters, hipStream_t s) {
+  prof_before("mfma_loop", s);
+  hipLaunchKernelGGL(k_mfma_loop, dim3(unsigned(blocks)), dim3(256), 0, s, out, iters);
+  prof_after(s);
+  return hipGetLastError();
+}
+
 hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t s) {
   const long n = long(bytes / 16);
   const long blocks = std::min<long>((n + 255) / 256, 4096);

@@ -234,6 +234,13 @@ int beam_profile_end(const char **names, int32_t *launches, double *total_ms,
  * (multiple of 16) from src to dst; used to calibrate memory counters. */
 int beam_copy_kernel(void *dst, const void *src, size_t bytes, void *stream);
 
+/* MFMA throughput probe: `blocks` workgroups of 4 waves, each wave running
+ * `iters` rounds of four independent bf16 32x32x16 MFMA accumulation chains
+ * on registers (blocks * iters * 4 * 4 * 32768 FLOPs per launch); one float
+ * per thread is written to out [blocks * 256] so the work is kept.  Used to
+ * measure the dense bf16 MFMA rate the chip sustains. */
+int beam_mfma_loop(float *out, int32_t blocks, int32_t iters, void *stream);
+
 #ifdef __cplusplus
 }
 #endif
