@@ -91,6 +91,8 @@ def lib() -> ctypes.CDLL:
         L.beam_moe_route.restype = ctypes.c_int
         L.beam_moe_forward.argtypes = [P(beam_moe_layer), VP, I32, VP, P(beam_route_out), VP, SZ, VP]
         L.beam_moe_forward.restype = ctypes.c_int
+        L.beam_moe_forward_static.argtypes = [P(beam_moe_layer), VP, I32, VP, P(beam_route_out), VP]
+        L.beam_moe_forward_static.restype = ctypes.c_int
         L.beam_moe_mask_backward.argtypes = [P(beam_moe_layer), VP, VP, I32, ctypes.c_float, VP, VP,
                                              VP, VP, SZ, VP]
         L.beam_moe_mask_backward.restype = ctypes.c_int
@@ -168,6 +170,19 @@ def beam_moe_forward(layer: beam_moe_layer, x, T: int, y, out: Optional[beam_rou
     outp = ctypes.byref(out) if out is not None else None
     _check(lib().beam_moe_forward(ctypes.byref(layer), _ptr(x), int(T), _ptr(y), outp, _ptr(ws),
                                   int(ws_bytes), stream), "beam_moe_forward")
+
+
+# Size of the static device workspace of beam_moe_forward_static (bytes).
+STATIC_WORKSPACE_BYTES = 64 << 20
+
+
+def beam_moe_forward_static(layer: beam_moe_layer, x, T: int, y, out: Optional[beam_route_out],
+                            stream: int = 0) -> None:
+    """beam_moe_forward without a caller workspace (the library's static
+    device array; allocates nothing)."""
+    outp = ctypes.byref(out) if out is not None else None
+    _check(lib().beam_moe_forward_static(ctypes.byref(layer), _ptr(x), int(T), _ptr(y), outp, stream),
+           "beam_moe_forward_static")
 
 
 def beam_moe_stats(layer: beam_moe_layer, expert_count, T: int, stream: int = 0) -> dict:

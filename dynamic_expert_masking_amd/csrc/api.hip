@@ -290,6 +290,55 @@ int beam_moe_forward(const beam_moe_layer* layer, const void* x, int32_t T, void
   return BEAM_OK;
 }
 
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Allocation-free forward: the workspace is a static device array.
+// ---------------------------------------------------------------------------
+
+// Every GPU the library runs on holds its own copy of this array from the
+// first call of beam_moe_forward_static on it until the process ends.  In
+// host code `scratch` names a host-side stand-in, not device memory: its
+// device address on each GPU comes from hipGetSymbolAddress, once per device,
+// and only that address is ever handed to kernels.
+static __device__ __align__(256) unsigned char scratch[BEAM_STATIC_WORKSPACE_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (nullptr on failure).
+void* device_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" {
+
+int beam_moe_forward_static(const beam_moe_layer* layer, const void* x, int32_t T, void* y,
+                            const beam_route_out* out, void* stream) {
+  // Sizes are checked before any HIP call: a batch whose workspace exceeds
+  // the array is rejected with nothing launched.
+  int st = check_layer(layer);
+  if (st != BEAM_OK) return st;
+  if (T < 0) return BEAM_ERR_INVALID_ARG;
+  if (long(T) * layer->K > (1L << 30) || long(T) * layer->D > kMaxOffsetElems) return BEAM_ERR_UNSUPPORTED;
+  if (T == 0) return BEAM_OK;
+  if (workspace_layout(*layer, T).total > size_t(BEAM_STATIC_WORKSPACE_BYTES)) return BEAM_ERR_WORKSPACE;
+  void* ws = device_scratch();
+  if (!ws) return BEAM_ERR_HIP;
+  return beam_moe_forward(layer, x, T, y, out, ws, size_t(BEAM_STATIC_WORKSPACE_BYTES), stream);
+}
+
 int beam_moe_mask_backward(const beam_moe_layer* layer, const void* x, const void* dy, int32_t T,
                            float beta, float* dwm, float* dbm, float* lreg, void* ws,
                            size_t ws_bytes, void* stream) {

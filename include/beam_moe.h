@@ -21,7 +21,8 @@
  * Conventions for every call below:
  *   - All tensor pointers are DEVICE pointers, owned by the caller, 16-byte
  *     aligned, row-major and densely packed.  The library allocates nothing
- *     and keeps no state between calls except the optional profiler.
+ *     and keeps no state between calls except the optional profiler and the
+ *     static workspace of beam_moe_forward_static.
  *   - `stream` is a hipStream_t (NULL = the default stream).  route and
  *     forward only enqueue work: they never synchronise the host.
  *   - Arguments are validated before anything is launched; on any error
@@ -179,6 +180,31 @@ int beam_moe_route(const beam_moe_layer *layer, const void *x, int32_t T,
 int beam_moe_forward(const beam_moe_layer *layer, const void *x, int32_t T,
                      void *y, const beam_route_out *out, void *ws,
                      size_t ws_bytes, void *stream);
+
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc: the same
+ * forward pass as beam_moe_forward, with its workspace taken from a static
+ * device array of BEAM_STATIC_WORKSPACE_BYTES (64 MiB) inside the library
+ * instead of a caller buffer.  Arguments and results are those of
+ * beam_moe_forward; the current device (hipGetDevice) must be the one that
+ * holds the tensors and the stream.
+ *   - Batches whose workspace (beam_moe_workspace_size(layer, T)) exceeds
+ *     BEAM_STATIC_WORKSPACE_BYTES are rejected with BEAM_ERR_WORKSPACE before
+ *     anything is launched (every decode batch of up to 512 tokens of the
+ *     DeepSeek-V2-Lite-, Mixtral- and fine-grained-shaped layers fits).
+ *   - Calls no hipMalloc, hipFree or other allocating routine.  Each GPU the
+ *     library runs on holds its own copy of the array from the first call on
+ *     that GPU until the process ends (the first call per GPU also looks up
+ *     the array's device address, a host-side runtime call).
+ *   - Every call on one GPU shares that GPU's array: two calls that overlap
+ *     in time on one GPU (different streams or threads) race and corrupt each
+ *     other's results.  Serialise them on one stream.
+ *   - The array keeps the last call's contents; nothing in it needs to start
+ *     at zero (every call writes what it later reads). */
+#define BEAM_STATIC_WORKSPACE_BYTES (64u << 20)
+int beam_moe_forward_static(const beam_moe_layer *layer, const void *x,
+                            int32_t T, void *y, const beam_route_out *out,
+                            void *stream);
 
 /* Mask-router training step: the loss value and straight-through gradient.
  * (BEAM page on aitrends.kr, method paragraph, training strategy: L = L_lm +

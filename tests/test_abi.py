@@ -173,6 +173,24 @@ def test_forward_rejects_bad_calls():
     assert f(ctypes.byref(L), FAKE, 0, FAKE * 2, None, None, 0, None) == dm.BEAM_OK
 
 
+def test_forward_static_argument_checks():
+    """The allocation-free forward validates (layer, T, and the batch's
+    workspace against the static array's size) before any HIP call."""
+    L = fake_layer()
+    f = dm.lib().beam_moe_forward_static
+    assert f(ctypes.byref(fake_layer(K=9)), FAKE, 4, FAKE * 2, None, None) == dm.BEAM_ERR_INVALID_ARG
+    assert f(ctypes.byref(L), FAKE, -1, FAKE * 2, None, None) == dm.BEAM_ERR_INVALID_ARG
+    assert f(ctypes.byref(L), FAKE, 0, FAKE * 2, None, None) == dm.BEAM_OK
+    big = 1
+    while dm.beam_moe_workspace_size(L, big) <= dm.STATIC_WORKSPACE_BYTES:
+        big *= 2
+    assert f(ctypes.byref(L), FAKE, big, FAKE * 2, None, None) == dm.BEAM_ERR_WORKSPACE
+    # every decode batch of the DeepSeek-V2-Lite-, Mixtral- and fine-grained-shaped layers fits
+    for name in ("dsv2lite_decode", "mixtral", "finegrained", "dsv2lite_decode_fp8"):
+        assert dm.beam_moe_workspace_size(config_layer(synth.CONFIGS[name]), 512) \
+            <= dm.STATIC_WORKSPACE_BYTES, name
+
+
 def test_mask_backward_argument_checks():
     L = fake_layer()
     ws = 0x20000
