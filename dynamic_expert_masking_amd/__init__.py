@@ -173,7 +173,7 @@ def beam_moe_forward(layer: beam_moe_layer, x, T: int, y, out: Optional[beam_rou
 
 
 # Size of the static device workspace of beam_moe_forward_static (bytes).
-STATIC_WORKSPACE_BYTES = 64 << 20
+STATIC_WORKSPACE_BYTES = 128 << 20
 
 
 def beam_moe_forward_static(layer: beam_moe_layer, x, T: int, y, out: Optional[beam_route_out],

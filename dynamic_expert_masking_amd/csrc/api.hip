@@ -70,6 +70,13 @@ WsLayout workspace_layout(const beam_moe_layer& L, int32_t T) {
   w.h_shared = take(size_t(T) * IS * elt);
   w.o = take(TK * L.D * elt);
   w.o_shared = take(IS ? size_t(T) * L.D * elt : 0);
+  // fp32 partials of a k-split prefill down product (tiles over 64 rows,
+  // bf16 weights): kMaxDownSplit x ([T K][D] + [T][D]).  The tile height, and
+  // so this size, is non-decreasing in T.
+  const bool split_down = L.dtype != BEAM_F32 && L.expert_format != BEAM_WEIGHTS_FP8_E4M3 &&
+                          expert_tile_rows(L, T) > 64;
+  w.o_part_bytes = split_down ? size_t(kMaxDownSplit) * (TK + (IS ? T : 0)) * L.D * 4 : 0;
+  w.o_part = take(w.o_part_bytes);
   w.zsel = take(TK * 4);
   w.dz = take(TK * 4);
   w.lreg_tok = take(size_t(T) * 4);
@@ -232,6 +239,7 @@ static Ptrs carve(const WsLayout& w, void* ws, const beam_route_out* out) {
   p.h_shared = b + w.h_shared;
   p.o = b + w.o;
   p.o_shared = b + w.o_shared;
+  p.o_part = w.o_part_bytes ? reinterpret_cast<float*>(b + w.o_part) : nullptr;
   p.zsel = reinterpret_cast<float*>(b + w.zsel);
   p.dz = reinterpret_cast<float*>(b + w.dz);
   p.lreg_tok = reinterpret_cast<float*>(b + w.lreg_tok);
@@ -285,8 +293,8 @@ int beam_moe_forward(const beam_moe_layer* layer, const void* x, int32_t T, void
   if ((st = run_routing(*layer, x, T, tile_rows, p, s)) != BEAM_OK) return st;
   if (!select_builds_plan(*layer, T)) BEAM_TRY(launch_scatter(*layer, T, p, s));
   BEAM_TRY(launch_gate_up(*layer, x, T, tile_rows, lay, p, s));
-  BEAM_TRY(launch_down(*layer, T, tile_rows, lay, p, s));
-  BEAM_TRY(launch_combine(*layer, T, p, y, s));
+  BEAM_TRY(launch_down(*layer, T, tile_rows, lay, p, s, /*allow_split=*/true));
+  BEAM_TRY(launch_combine(*layer, T, tile_rows, p, y, s));
   return BEAM_OK;
 }
 

@@ -36,7 +36,8 @@ struct Tile {
 
 struct WsLayout {
   size_t plan, logits, idx, gates, mask, counts, rank, block_counts, expert_off, tiles, perm_token,
-      slot_pos, h, h_shared, o, o_shared, zsel, dz, lreg_tok, total;
+      slot_pos, h, h_shared, o, o_shared, o_part, zsel, dz, lreg_tok, total;
+  size_t o_part_bytes;   // 0 when the layer's down product never splits
   int32_t max_tiles;
 };
 
@@ -68,11 +69,37 @@ struct Ptrs {
   void* h_shared;
   void* o;          // [P][D] expert outputs: fp32 for fp32 layers, bf16 otherwise
   void* o_shared;   // [T][D] shared-expert outputs, same type
+  // k-split down products (prefill tiles): fp32 partial outputs
+  // [kMaxDownSplit][T K][D], then the shared ones [kMaxDownSplit][T][D]
+  float* o_part;
   // mask-router backward
   float* zsel;       // [T][K] mask logit of each candidate
   float* dz;         // [P] dL/dz of each pair (pair order)
   float* lreg_tok;   // [T] sum of m_hat over the token's candidates
 };
+
+// k split of the prefill down product: chosen on the device, identically by
+// the down and combine kernels, from the plan's tile count.  A launch with
+// fewer items (tiles x output blocks) than resident workgroups leaves CUs
+// idle for its whole duration; splitting the k range s ways multiplies the
+// items by s and divides their length by s.  s (1 to kMaxDownSplit)
+// minimises ceil(items s / slots) / s, the time in units of one unsplit
+// item; split only when there is less than one full round of items (more
+// already fill the GPU, and the fp32 partials cost traffic).
+constexpr int kMaxDownSplit = 4;
+__host__ __device__ inline int down_split(long items, long slots) {
+  if (slots <= 0 || items <= 0 || items >= slots) return 1;
+  int best = 1;
+  long best_cost = 12;   // rounds x 12 / s, with 12 = lcm(1, 2, 3, 4)
+  for (int s = 2; s <= kMaxDownSplit; ++s) {
+    const long cost = (items * s + slots - 1) / slots * (12 / s);
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = s;
+    }
+  }
+  return best;
+}
 
 // ---- launchers (return hipSuccess or the launch error) ----
 hipError_t launch_router_logits(const beam_moe_layer& L, const void* x, int32_t T, const Ptrs& p,
@@ -91,10 +118,13 @@ hipError_t launch_scan(const beam_moe_layer& L, int32_t T, int tile_rows, const 
 hipError_t launch_scatter(const beam_moe_layer& L, int32_t T, const Ptrs& p, hipStream_t s);
 hipError_t launch_gate_up(const beam_moe_layer& L, const void* x, int32_t T, int tile_rows,
                           const WsLayout& w, const Ptrs& p, hipStream_t s);
+// allow_split: the prefill down product may split k (fp32 partials in
+// p.o_part, added by the combine); the mask-router backward reads O itself
+// and passes false.
 hipError_t launch_down(const beam_moe_layer& L, int32_t T, int tile_rows, const WsLayout& w,
-                       const Ptrs& p, hipStream_t s);
-hipError_t launch_combine(const beam_moe_layer& L, int32_t T, const Ptrs& p, void* y,
-                          hipStream_t s);
+                       const Ptrs& p, hipStream_t s, bool allow_split = false);
+hipError_t launch_combine(const beam_moe_layer& L, int32_t T, int tile_rows, const Ptrs& p,
+                          void* y, hipStream_t s);
 hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t s);
 hipError_t launch_mfma_loop(float* out, int blocks, int iters, hipStream_t s);
 // Mask-router backward from the all-pairs expert outputs O: per-pair dL/dz and

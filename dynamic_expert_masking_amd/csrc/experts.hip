@@ -46,6 +46,11 @@ struct ExpertArgs {
   void* h_sh;      // [T][S*Is]
   void* o;         // [P][D] expert outputs: fp32 (fp32 layers) or bf16
   void* o_sh;      // [T][D] shared-expert outputs, same type
+  // k-split prefill down: fp32 partials [split][T K][D] and [split][T][D]
+  float* op;
+  float* op_sh;
+  long op_stride, op_sh_stride;   // elements per split
+  int down_slots;                 // resident workgroups of the down kernel (0: never split)
 };
 
 // Order of the shared items.  Every shared tile reads the same weights, so
@@ -533,6 +538,11 @@ __device__ __forceinline__ void down_setup(const ExpertArgs& a, const Tile& tl, 
   }
 }
 
+// With a k split (down_split: too few items to fill the GPU), item w is
+// split w % ks of (tile, d-block) w / ks: the adjacent items of one output
+// block read disjoint k ranges of the same weight rows, and each writes its
+// fp32 partial sums to its own slice of the partial buffer; the combine adds
+// the slices in split order.
 template <int BN, int BM>
 __global__ __launch_bounds__(256, 2) void k_down_tiled(ExpertArgs a) {
   __shared__ TiledSmem<BN, BM> sm;
@@ -541,18 +551,23 @@ __global__ __launch_bounds__(256, 2) void k_down_tiled(ExpertArgs a) {
   const int wn = wave & 1, wm = wave >> 1;
   const int ntr = a.plan->n_tiles_routed, nts = a.plan->n_tiles_shared;
   const int nb_all = (a.D + BN - 1) / BN;
-  const long total = long(ntr + nts) * nb_all;
-  for (XcdRange it = xcd_range(total); it.next < it.end; it.next += it.step) {
+  const long items = long(ntr + nts) * nb_all;
+  const int ks = down_split(items, a.down_slots);
+  for (XcdRange it = xcd_range(items * ks); it.next < it.end; it.next += it.step) {
     int ti, nb;
-    down_item(it.next, ntr, nts, nb_all, ti, nb);
+    const long wi = it.next / ks;
+    const int split = int(it.next - wi * ks);
+    down_item(wi, ntr, nts, nb_all, ti, nb);
     const bool shared = ti >= ntr;
     const Tile tl = a.tiles[ti];
     DownProvBase pv;
     down_setup(a, tl, shared, pv);
     pv.d0 = nb * BN;
+    const int C = pv.nseg() * pv.seg_chunks();
     f32x16 acc[JN][JM];
-    tiled_accumulate<BN, BM>(pv, sm, acc, tl.rows);
+    tiled_accumulate<BN, BM>(pv, sm, acc, tl.rows, C * split / ks, C * (split + 1) / ks);
     u16* ob = static_cast<u16*>(shared ? a.o_sh : a.o);
+    float* pb = shared ? a.op_sh + split * a.op_sh_stride : a.op + split * a.op_stride;
 #pragma unroll
     for (int jn = 0; jn < JN; ++jn)
 #pragma unroll
@@ -564,8 +579,12 @@ __global__ __launch_bounds__(256, 2) void k_down_tiled(ExpertArgs a) {
             const int d = nb * BN + wn * (BN / 2) + jn * 32 + 8 * q + 4 * (lane >> 5);
             if (d < a.D) {
               const f32x16& v = acc[jn][jm];
-              st4_bf16(ob, size_t(tl.row0 + r) * a.D + d, v[4 * q], v[4 * q + 1], v[4 * q + 2],
-                       v[4 * q + 3]);
+              const size_t e = size_t(tl.row0 + r) * a.D + d;
+              if (ks == 1)
+                st4_bf16(ob, e, v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+              else
+                *reinterpret_cast<float4*>(pb + e) =
+                    make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
             }
           }
         }
@@ -654,15 +673,43 @@ __global__ __launch_bounds__(256) void k_down_f32(ExpertArgs a) {
 // kept slot): all K slots in one chunk when K <= 8, else the kept ones four at
 // a time.  Large batches take the kept slots one at a time (many resident
 // workgroups hide the latency, and padded loads would cost bandwidth).
+// Split down products (plan-dependent, see down_split): each O row is the
+// sum of the fp32 partials of the splits, added in split order.
+struct CombineSplit {
+  const Plan* plan;        // null: the down product is never split
+  int slots, nb_all;       // as passed to the down kernel
+  const float* op;
+  const float* op_sh;
+  long op_stride, op_sh_stride;
+};
+
+__device__ __forceinline__ float4 split_row4(const float* base, long stride, int ks, size_t e) {
+  float4 v = *reinterpret_cast<const float4*>(base + e);
+  for (int q = 1; q < ks; ++q) {
+    const float4 w = *reinterpret_cast<const float4*>(base + q * stride + e);
+    v.x += w.x;
+    v.y += w.y;
+    v.z += w.z;
+    v.w += w.w;
+  }
+  return v;
+}
+
 template <bool BF16, int KC, bool COMPACT>
 __global__ __launch_bounds__(256) void k_combine(int T, int D, int K, const float* __restrict__ gates,
                                                  const int32_t* __restrict__ slot_pos,
                                                  const void* __restrict__ o,
-                                                 const void* __restrict__ o_sh, void* __restrict__ y) {
+                                                 const void* __restrict__ o_sh, void* __restrict__ y,
+                                                 CombineSplit cs) {
   __shared__ float s_g[32];
   __shared__ int32_t s_p[32];
   __shared__ int s_n;
   const int t = blockIdx.x;
+  int ks = 1;
+  if (cs.plan) {
+    const int ntr = ld_const(&cs.plan->n_tiles_routed), nts = ld_const(&cs.plan->n_tiles_shared);
+    ks = down_split(long(ntr + nts) * cs.nb_all, cs.slots);
+  }
   if (threadIdx.x < 32) {   // wave 0
     const int l = threadIdx.x;
     const bool in = l < K;
@@ -684,6 +731,31 @@ __global__ __launch_bounds__(256) void k_combine(int T, int D, int K, const floa
   }
   __syncthreads();
   const int nk = COMPACT ? s_n : K;
+  if (ks > 1) {   // fp32 partial sums of a split down product, slot by slot
+    for (int d = threadIdx.x * 4; d < D; d += blockDim.x * 4) {
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int k = 0; k < nk; ++k) {
+        const int pk = s_p[k];
+        if (pk < 0) continue;
+        const float g = s_g[k];
+        const float4 v = split_row4(cs.op, cs.op_stride, ks, size_t(pk) * D + d);
+        acc.x += g * v.x;
+        acc.y += g * v.y;
+        acc.z += g * v.z;
+        acc.w += g * v.w;
+      }
+      if (o_sh) {
+        const float4 sh = split_row4(cs.op_sh, cs.op_sh_stride, ks, size_t(t) * D + d);
+        acc.x += sh.x;
+        acc.y += sh.y;
+        acc.z += sh.z;
+        acc.w += sh.w;
+      }
+      if (BF16) st4_bf16(static_cast<u16*>(y), size_t(t) * D + d, acc.x, acc.y, acc.z, acc.w);
+      else *reinterpret_cast<float4*>((float*)y + size_t(t) * D + d) = acc;
+    }
+    return;
+  }
   for (int d = threadIdx.x * 4; d < D; d += blockDim.x * 4) {
     float4 sh = make_float4(0.f, 0.f, 0.f, 0.f);
     if (o_sh) sh = ld4_f32<BF16>(o_sh, size_t(t) * D + d);
@@ -752,6 +824,11 @@ static ExpertArgs expert_args(const beam_moe_layer& L, const void* x, int32_t T,
   a.h_sh = p.h_shared;
   a.o = p.o;
   a.o_sh = p.o_shared;
+  a.op = p.o_part;
+  a.op_stride = long(T) * L.K * L.D;
+  a.op_sh = p.o_part ? p.o_part + kMaxDownSplit * a.op_stride : nullptr;
+  a.op_sh_stride = long(T) * L.D;
+  a.down_slots = 0;
   return a;
 }
 
@@ -938,9 +1015,25 @@ hipError_t launch_gate_up(const beam_moe_layer& L, const void* x, int32_t T, int
   return hipGetLastError();
 }
 
+// Resident workgroups of the tiled down kernel for a tile height (0: the
+// launch streams, no split).
+static int down_tiled_slots(int tile_rows) {
+  if (tile_rows == 256) return resident_blocks((const void*)&k_down_tiled<128, 256>, 256);
+  if (tile_rows == 128) return resident_blocks((const void*)&k_down_tiled<256, 128>, 256);
+  return 0;
+}
+static int down_tiled_nb(const beam_moe_layer& L, int tile_rows) {
+  const int bn = tile_rows == 256 ? 128 : 256;
+  return (L.D + bn - 1) / bn;
+}
+static bool down_may_split(const beam_moe_layer& L, int tile_rows) {
+  return L.dtype != BEAM_F32 && L.expert_format != BEAM_WEIGHTS_FP8_E4M3 && tile_rows > 64;
+}
+
 hipError_t launch_down(const beam_moe_layer& L, int32_t T, int tile_rows, const WsLayout&,
-                       const Ptrs& p, hipStream_t s) {
-  const ExpertArgs a = expert_args(L, nullptr, T, p);
+                       const Ptrs& p, hipStream_t s, bool allow_split) {
+  ExpertArgs a = expert_args(L, nullptr, T, p);
+  if (allow_split && p.o_part && down_may_split(L, tile_rows)) a.down_slots = down_tiled_slots(tile_rows);
   long nts;
   const long ntr = tile_bound(L, T, tile_rows, &nts);
   if (L.dtype == BEAM_F32) {
@@ -961,27 +1054,35 @@ hipError_t launch_down(const beam_moe_layer& L, int32_t T, int tile_rows, const 
   } else {
     const int bn = tile_rows == 256 ? 128 : 256;
     const long items = (ntr + nts) * ((L.D + bn - 1) / bn);
+    // room for the items of a k split (the device decides from the plan)
+    const long gi = a.down_slots > 0 ? items * kMaxDownSplit : items;
     prof_before("down_tiled", s);
     if (tile_rows == 256)
       hipLaunchKernelGGL((k_down_tiled<128, 256>),
-                         dim3(tiled_grid((const void*)&k_down_tiled<128, 256>, items)), dim3(256), 0, s, a);
+                         dim3(tiled_grid((const void*)&k_down_tiled<128, 256>, gi)), dim3(256), 0, s, a);
     else
       hipLaunchKernelGGL((k_down_tiled<256, 128>),
-                         dim3(tiled_grid((const void*)&k_down_tiled<256, 128>, items)), dim3(256), 0, s, a);
+                         dim3(tiled_grid((const void*)&k_down_tiled<256, 128>, gi)), dim3(256), 0, s, a);
     prof_after(s);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const beam_moe_layer& L, int32_t T, const Ptrs& p, void* y,
-                          hipStream_t s) {
+hipError_t launch_combine(const beam_moe_layer& L, int32_t T, int tile_rows, const Ptrs& p,
+                          void* y, hipStream_t s) {
   const void* osh = L.n_shared > 0 ? p.o_shared : nullptr;
+  CombineSplit cs{nullptr, 0, 0, nullptr, nullptr, 0, 0};
+  if (p.o_part && down_may_split(L, tile_rows)) {
+    const ExpertArgs a = expert_args(L, nullptr, T, p);
+    cs = CombineSplit{p.plan, down_tiled_slots(tile_rows), down_tiled_nb(L, tile_rows), a.op, a.op_sh,
+                      a.op_stride, a.op_sh_stride};
+  }
   prof_before("combine", s);
   // Below 1024 tokens: all K slots in one chunk when K <= 8, else the kept
   // slots four at a time; from 1024 tokens: the kept slots one at a time.
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3(unsigned(T)), dim3(256), 0, s, T, L.D, L.K, p.gates, p.slot_pos,
-                       p.o, osh, y);
+                       p.o, osh, y, cs);
   };
   const bool bf = L.dtype != BEAM_F32;
   if (T >= 1024) bf ? go(k_combine<true, 1, true>) : go(k_combine<false, 1, true>);

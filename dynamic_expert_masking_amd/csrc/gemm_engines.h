@@ -199,9 +199,12 @@ __device__ __forceinline__ void tiled_dispatch(int n, F&& f) {
 // acc[jn][jm][i] = C[n = (BN/2)*(wave&1) + 32*jn + 8*(i/4) + 4*(lane/32) + i%4]
 //                   [m = (BM/2)*(wave>>1) + 32*jm + lane%32]
 // MFMAs of 32-row token blocks at or past rows_valid are skipped.
+// k chunks [c_lo, c_hi) of the provider's nseg * seg_chunks (c_hi < 0: to
+// the end), for a k split of the product.
 template <int BN, int BM, class Prov>
 __device__ __forceinline__ void tiled_accumulate(const Prov& pv, TiledSmem<BN, BM>& sm,
-                                                 f32x16 (&acc)[BN / 64][BM / 64], int rows_valid) {
+                                                 f32x16 (&acc)[BN / 64][BM / 64], int rows_valid,
+                                                 int c_lo = 0, int c_hi = -1) {
   constexpr int JN = BN / 64, JM = BM / 64;
   constexpr int WL = BN / 32;   // weight chunks per thread per slice
   constexpr int XL = BM / 32;   // token chunks per thread per slice
@@ -220,7 +223,7 @@ __device__ __forceinline__ void tiled_accumulate(const Prov& pv, TiledSmem<BN, B
 
   const int nseg = pv.nseg();
   const int cps = pv.seg_chunks();
-  const int C = nseg * cps;
+  const int C = c_hi < 0 ? nseg * cps : c_hi;
   const int lrow = tid >> 3;          // 0..31
   const int lcol = (tid & 7) * 8;     // element offset of this thread's 16 bytes
   uint32_t wo[WL], xo[XL];
@@ -240,7 +243,7 @@ __device__ __forceinline__ void tiled_accumulate(const Prov& pv, TiledSmem<BN, B
   // join of such branches makes the compiler wait for every load in flight.
   auto load = [&](Stage& st, int c) {
     const uint32_t msk = c < C ? ~0u : 0u;
-    const int cc = min(c, C - 1);
+    const int cc = max(min(c, C - 1), 0);   // an empty range reads chunk 0
     const int seg = cc / cps;
     const uint32_t km = uint32_t(cc - seg * cps) * kTBK;
     const u16* xb = pv.xbase(seg);
@@ -282,8 +285,8 @@ __device__ __forceinline__ void tiled_accumulate(const Prov& pv, TiledSmem<BN, B
   };
   auto run = [&](auto nj_const) {
     Stage st;
-    load(st, 0);
-    for (int c = 0; c < C; ++c) {
+    load(st, c_lo);
+    for (int c = c_lo; c < C; ++c) {
       store(st);          // slice c
       __syncthreads();
       load(st, c + 1);    // in flight while slice c is multiplied

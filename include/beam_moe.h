@@ -184,7 +184,7 @@ int beam_moe_forward(const beam_moe_layer *layer, const void *x, int32_t T,
 /* For callers that cannot allocate device memory -- code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc: the same
  * forward pass as beam_moe_forward, with its workspace taken from a static
- * device array of BEAM_STATIC_WORKSPACE_BYTES (64 MiB) inside the library
+ * device array of BEAM_STATIC_WORKSPACE_BYTES (128 MiB) inside the library
  * instead of a caller buffer.  Arguments and results are those of
  * beam_moe_forward; the current device (hipGetDevice) must be the one that
  * holds the tensors and the stream.
@@ -201,7 +201,7 @@ int beam_moe_forward(const beam_moe_layer *layer, const void *x, int32_t T,
  *     other's results.  Serialise them on one stream.
  *   - The array keeps the last call's contents; nothing in it needs to start
  *     at zero (every call writes what it later reads). */
-#define BEAM_STATIC_WORKSPACE_BYTES (64u << 20)
+#define BEAM_STATIC_WORKSPACE_BYTES (128u << 20)
 int beam_moe_forward_static(const beam_moe_layer *layer, const void *x,
                             int32_t T, void *y, const beam_route_out *out,
                             void *stream);

@@ -152,6 +152,23 @@ def test_wide_tiles(D):
     check_output(y, y_ref, "bf16")
 
 
+@pytest.mark.parametrize("T,S", [(1200, 2), (700, 0), (3000, 1)])
+def test_split_down(T, S):
+    """The prefill down product split over k (fp32 partials added by the
+    combine): few tiles against the resident workgroups make every split
+    count from 2 to 4 occur; two shared experts put a segment boundary inside
+    a split's k range, and splits of fewer chunks than the split count get
+    empty ranges (zero partials)."""
+    layer = small_layer(f"split{S}", D=256, E=8, K=2, I=256, S=S, I_s=128 if S else 0, keep=0.7,
+                        router_bias=True)
+    x = small_x(layer, T, "split")
+    note(f"[split down] T={T} S={S}")
+    y, rt, _ = run_forward(device_layer(layer), x)
+    rt_ref, y_ref = oracle.forward(layer, x)
+    check_routing(rt, rt_ref, layer.cfg.E)
+    check_output(y, y_ref, "bf16")
+
+
 @pytest.mark.parametrize("fp8", [False, True])
 def test_max_hidden_size(fp8):
     """The largest supported hidden size, D = 16384 (router k split, 256-chunk
