@@ -87,6 +87,9 @@ def parse():
                    help="zero mask router (every top-K candidate kept: plain top-K routing)")
     p.add_argument("--mask-backward", action="store_true",
                    help="time the mask-router training step (beam_moe_mask_backward) instead")
+    p.add_argument("--pack", choices=("prefill", "all", "none"), default="prefill",
+                   help="give the layer packed copies of its expert weights (beam_moe_pack_weights, "
+                        "done once at load): for the prefill rows (default), every row, or none")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--calibrate-copy", type=int, default=0,
                    help="only run the plain copy kernel on this many MiB (counter calibration)")
@@ -168,9 +171,10 @@ def main():
     # ------------------------------------------------------------------
     cache = {}
 
-    def layer_for(name):
-        if name in cache:
-            return cache[name]
+    def layer_for(name, pack=False):
+        key = (name, pack)
+        if key in cache:
+            return cache[key]
         for k in list(cache):   # one workload resident at a time
             del cache[k]
         torch.cuda.empty_cache()
@@ -181,13 +185,14 @@ def main():
         host = synth.make_layer(c)
         if args.zero_mask:
             host = replace(host, w_mask=np.zeros_like(host.w_mask), b_mask=None)
-        dl = DeviceLayer(host, dev)
+        dl = DeviceLayer(host, dev, pack=pack)
         per_copy = sum(v.numel() * v.element_size() for v in dl.t.values() if v is not None)
         copies = args.copies or max(2, min(16, int(np.ceil(1.5e9 / max(1, per_copy))) + 1))
         reps = [(dl.t, dl.desc)] + dl.replicas(copies - 1)
-        log(f"{c.name}: layer {per_copy / 1e9:.2f} GB x {copies} copies (setup {time.time() - t0:.1f}s)")
-        cache[name] = (c, host, dl, reps, copies)
-        return cache[name]
+        log(f"{c.name}: layer {per_copy / 1e9:.2f} GB x {copies} copies"
+            f"{' (with packed expert weights)' if dl.packed else ''} (setup {time.time() - t0:.1f}s)")
+        cache[key] = (c, host, dl, reps, copies)
+        return cache[key]
 
     def gate_up_work(c, active, T):
         """Algorithmic bytes and FLOPs of one gate/up launch: the gate and up
@@ -202,7 +207,8 @@ def main():
         return float(b)
 
     def run_row(name, T, shape, backward=False, gating=None, profile=True):
-        c, host, dl, reps, copies = layer_for(name)
+        pack = args.pack == "all" or (args.pack == "prefill" and shape == "prefill")
+        c, host, dl, reps, copies = layer_for(name, pack)
         descs = [d for _, d in reps]
         if gating is not None:
             for d in descs:
@@ -248,6 +254,7 @@ def main():
         used = [stats[i % args.pool] for i in range(args.pool)]
         elt = 4 if c.dtype == "f32" else 2
         r = {"workload": name, "config": CONFIG_LABEL.get(name, name), "T": T, "shape": shape,
+             "expert_weights": "row-major + packed copy" if dl.packed else "row-major",
              "ms_per_step": round(ms, 5), "window_ms": [round(w, 5) for w in win_ms],
              "tokens_per_s": round(T / (ms / 1e3), 1)}
         bytes_step = float(np.mean([s["bytes_total_min"] for s in used]))

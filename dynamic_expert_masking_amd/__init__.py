@@ -43,7 +43,9 @@ class beam_moe_layer(ctypes.Structure):
                 ("scale_gate", ctypes.c_void_p), ("scale_up", ctypes.c_void_p),
                 ("scale_down", ctypes.c_void_p), ("scale_shared_gate", ctypes.c_void_p),
                 ("scale_shared_up", ctypes.c_void_p), ("scale_shared_down", ctypes.c_void_p),
-                ("segment_len", ctypes.c_int32)]
+                ("segment_len", ctypes.c_int32),
+                ("wp_gate", ctypes.c_void_p), ("wp_up", ctypes.c_void_p), ("wp_down", ctypes.c_void_p),
+                ("wsp_gate", ctypes.c_void_p), ("wsp_up", ctypes.c_void_p), ("wsp_down", ctypes.c_void_p)]
 
 
 # beam_gate_flag bits of beam_moe_layer.gating
@@ -106,6 +108,8 @@ def lib() -> ctypes.CDLL:
         L.beam_profile_begin.restype = ctypes.c_int
         L.beam_profile_end.argtypes = [P(ctypes.c_char_p), P(I32), P(ctypes.c_double), I32]
         L.beam_profile_end.restype = ctypes.c_int
+        L.beam_moe_pack_weights.argtypes = [VP, I32, I32, I32, VP, VP]
+        L.beam_moe_pack_weights.restype = ctypes.c_int
         L.beam_mfma_loop.argtypes = [VP, I32, I32, VP]
         L.beam_mfma_loop.restype = ctypes.c_int
         L.beam_copy_kernel.argtypes = [VP, VP, SZ, VP]
@@ -132,7 +136,8 @@ def make_layer(D, E, K, I, dtype, w_router, w_mask, w_gate, w_up, w_down, b_rout
                b_mask=None, n_shared=0, I_shared=0, ws_gate=None, ws_up=None,
                ws_down=None, gating=0, expert_format=WEIGHTS_DTYPE, scale_gate=None,
                scale_up=None, scale_down=None, scale_shared_gate=None, scale_shared_up=None,
-               scale_shared_down=None, segment_len=0) -> beam_moe_layer:
+               scale_shared_down=None, segment_len=0, wp_gate=None, wp_up=None, wp_down=None,
+               wsp_gate=None, wsp_up=None, wsp_down=None) -> beam_moe_layer:
     """Fill a beam_moe_layer descriptor from tensors (or raw addresses).  The
     caller keeps the tensors alive while the descriptor is in use."""
     return beam_moe_layer(D, E, K, I, n_shared, I_shared, dtype, _ptr(w_router), _ptr(w_mask),
@@ -140,7 +145,8 @@ def make_layer(D, E, K, I, dtype, w_router, w_mask, w_gate, w_up, w_down, b_rout
                           _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down), int(gating),
                           int(expert_format), _ptr(scale_gate), _ptr(scale_up), _ptr(scale_down),
                           _ptr(scale_shared_gate), _ptr(scale_shared_up), _ptr(scale_shared_down),
-                          int(segment_len))
+                          int(segment_len), _ptr(wp_gate), _ptr(wp_up), _ptr(wp_down),
+                          _ptr(wsp_gate), _ptr(wsp_up), _ptr(wsp_down))
 
 
 def make_route_out(topk_idx, gates, mask, expert_count) -> beam_route_out:
@@ -227,3 +233,9 @@ def beam_copy_kernel(dst, src, nbytes: int, stream: int = 0) -> None:
 def beam_mfma_loop(out, blocks: int, iters: int, stream: int = 0) -> None:
     """MFMA throughput probe (see the header); out holds blocks * 256 floats."""
     _check(lib().beam_mfma_loop(_ptr(out), int(blocks), int(iters), stream), "beam_mfma_loop")
+
+
+def beam_moe_pack_weights(w, mats: int, rows: int, cols: int, packed, stream: int = 0) -> None:
+    """Packed operand layout of `mats` bf16 matrices [rows][cols] (see the header)."""
+    _check(lib().beam_moe_pack_weights(_ptr(w), int(mats), int(rows), int(cols), _ptr(packed), stream),
+           "beam_moe_pack_weights")

@@ -21,7 +21,8 @@ int expert_tile_rows(const beam_moe_layer& L, int32_t T) {
   if (per_expert <= 32) return 32;
   // FP8 weights only have the streaming kernels (tiles of up to 64 rows)
   if (per_expert <= 96 || L.expert_format == BEAM_WEIGHTS_FP8_E4M3) return 64;
-  if (per_expert < 512) return 128;
+  // packed weights: the prefill kernels take tiles of 128 token rows
+  if (per_expert < 512 || L.wp_gate) return 128;
   return 256;
 }
 
@@ -180,6 +181,27 @@ static int check_layer(const beam_moe_layer* L) {
     return BEAM_ERR_UNSUPPORTED;
   if (L->expert_format != BEAM_WEIGHTS_DTYPE && L->expert_format != BEAM_WEIGHTS_FP8_E4M3)
     return BEAM_ERR_INVALID_ARG;
+  // packed copies: all that the layer uses, or none (bf16 weights only)
+  {
+    const void* pk[] = {L->wp_gate, L->wp_up, L->wp_down};
+    const void* pks[] = {L->wsp_gate, L->wsp_up, L->wsp_down};
+    int given = 0, bad = 0;
+    for (const void* q : pk) {
+      given += q != nullptr;
+      bad += q && !aligned16(q);
+    }
+    for (const void* q : pks) {
+      given += q != nullptr;
+      bad += q && !aligned16(q);
+    }
+    const int need = L->n_shared > 0 ? 6 : 3;
+    if (given > 0) {
+      if (bad || L->dtype != BEAM_BF16 || L->expert_format != BEAM_WEIGHTS_DTYPE) return BEAM_ERR_INVALID_ARG;
+      if (!L->wp_gate || !L->wp_up || !L->wp_down) return BEAM_ERR_INVALID_ARG;
+      if (L->n_shared > 0 && (!L->wsp_gate || !L->wsp_up || !L->wsp_down)) return BEAM_ERR_INVALID_ARG;
+      if (given != need) return BEAM_ERR_INVALID_ARG;   // shared copies without shared experts
+    }
+  }
   if (L->expert_format == BEAM_WEIGHTS_FP8_E4M3) {
     const float* sc[] = {L->scale_gate, L->scale_up, L->scale_down};
     for (const float* p : sc)
@@ -487,6 +509,21 @@ int beam_profile_end(const char** names, int32_t* launches, double* total_ms, in
     ++n;
   }
   return n;
+}
+
+int beam_moe_pack_weights(const void* w, int32_t mats, int32_t rows, int32_t cols, void* packed,
+                          void* stream) {
+  if (!w || !packed || !aligned16(w) || !aligned16(packed) || mats < 0 || rows <= 0 || cols <= 0 ||
+      rows % 32 || cols % 64 || long(rows) * cols > kMaxOffsetElems)
+    return BEAM_ERR_INVALID_ARG;
+  const size_t bytes = size_t(mats) * rows * cols * 2;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(w), b = reinterpret_cast<uintptr_t>(packed);
+  if (mats > 0 && a < b + bytes && b < a + bytes) return BEAM_ERR_INVALID_ARG;   // overlap
+  if (mats == 0) return BEAM_OK;
+  return launch_pack_weights(w, mats, rows, cols, packed, static_cast<hipStream_t>(stream)) ==
+                 hipSuccess
+             ? BEAM_OK
+             : BEAM_ERR_HIP;
 }
 
 int beam_mfma_loop(float* out, int32_t blocks, int32_t iters, void* stream) {

@@ -79,18 +79,21 @@ struct Ptrs {
 };
 
 // k split of the prefill down product: chosen on the device, identically by
-// the down and combine kernels, from the plan's tile count.  A launch with
-// fewer items (tiles x output blocks) than resident workgroups leaves CUs
-// idle for its whole duration; splitting the k range s ways multiplies the
-// items by s and divides their length by s.  s (1 to kMaxDownSplit)
-// minimises ceil(items s / slots) / s, the time in units of one unsplit
-// item; split only when there is less than one full round of items (more
-// already fill the GPU, and the fp32 partials cost traffic).
+// the down and combine kernels, from the plan's tile count.  A launch whose
+// items (tiles x output blocks) leave the resident workgroups badly used --
+// fewer items than workgroups, or a last round mostly empty -- idles CUs;
+// splitting the k range s ways multiplies the items by s and divides their
+// length by s.  s (1 to kMaxDownSplit) minimises ceil(items s / slots) / s,
+// the time in units of one unsplit item, and is taken only when it saves at
+// least a third of that time: the fp32 partials cost HBM traffic (written
+// here, read by the combine), and the estimate takes every item to be as
+// long as a full tile's.
 constexpr int kMaxDownSplit = 4;
 __host__ __device__ inline int down_split(long items, long slots) {
-  if (slots <= 0 || items <= 0 || items >= slots) return 1;
+  if (slots <= 0 || items <= 0) return 1;
+  const long cost1 = (items + slots - 1) / slots * 12;   // rounds x 12 / s, 12 = lcm(1..4)
   int best = 1;
-  long best_cost = 12;   // rounds x 12 / s, with 12 = lcm(1, 2, 3, 4)
+  long best_cost = cost1;
   for (int s = 2; s <= kMaxDownSplit; ++s) {
     const long cost = (items * s + slots - 1) / slots * (12 / s);
     if (cost < best_cost) {
@@ -98,7 +101,7 @@ __host__ __device__ inline int down_split(long items, long slots) {
       best = s;
     }
   }
-  return best;
+  return 3 * best_cost <= 2 * cost1 ? best : 1;
 }
 
 // ---- launchers (return hipSuccess or the launch error) ----
@@ -127,6 +130,9 @@ hipError_t launch_combine(const beam_moe_layer& L, int32_t T, int tile_rows, con
                           void* y, hipStream_t s);
 hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t s);
 hipError_t launch_mfma_loop(float* out, int blocks, int iters, hipStream_t s);
+// Packed operand layout of `mats` bf16 matrices [rows][cols] (see the header).
+hipError_t launch_pack_weights(const void* w, int mats, int rows, int cols, void* packed,
+                               hipStream_t s);
 // Mask-router backward from the all-pairs expert outputs O: per-pair dL/dz and
 // per-token sums of m_hat, then dL/dWm, dL/db_m and L_reg.
 hipError_t launch_mask_grad(const beam_moe_layer& L, const void* x, const void* dy, int32_t T,

@@ -19,6 +19,7 @@
 
 #include "beam_internal.h"
 #include "gemm_engines.h"
+#include "prefill_engine.h"
 #include "stream_engine.h"
 
 namespace beam {
@@ -38,10 +39,19 @@ struct ExpertArgs {
   const float* qsg;   // [S*Is] (the fused shared expert's intermediate rows)
   const float* qsu;   // [S*Is]
   const float* qsd;   // [S][D]
+  // the same weights in the packed operand layout (prefill kernels), or null
+  const u16* pg;    // [E] x packed [I][D]
+  const u16* pu;
+  const u16* pd;    // [E] x packed [D][I]
+  const u16* psg;   // packed [S*Is][D]
+  const u16* psu;
+  const u16* psd;   // [S] x packed [D][Is]
   int T, D, E, I, S, Is;
   const Plan* plan;
   const Tile* tiles;
   const int32_t* perm_token;
+  const int32_t* expert_off;   // [E + 1] first pair of each expert (prefill item order)
+  int tile_rows;               // rows per routed tile (the last of an expert may be shorter)
   void* h;         // [P][I]
   void* h_sh;      // [T][S*Is]
   void* o;         // [P][D] expert outputs: fp32 (fp32 layers) or bf16
@@ -593,6 +603,229 @@ __global__ __launch_bounds__(256, 2) void k_down_tiled(ExpertArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Prefill kernels on packed weights (tiles of 128 token rows; prefill_engine.h)
+// ---------------------------------------------------------------------------
+
+// Routed items of the packed kernels, expert by expert and n-block-major
+// within an expert: the tiles of one expert that read the same weight block
+// are adjacent items, so they run at about the same time on one XCD (the
+// item space is cut into one contiguous part per XCD) and the block comes
+// from HBM once; these kernels stream their weights at close to the HBM rate,
+// and with tile-major items an expert's two or three 128-row tiles each
+// fetched its weights from HBM again.  Item w lies in the range of the
+// expert of tile w / nb_per_tile (the tile-major order covers each expert's
+// tiles contiguously too), whose first tile and tile count follow from its
+// pair offsets.
+__device__ __forceinline__ void packed_routed_item(const ExpertArgs& a, long w, int nb_per_tile,
+                                                   int& ti, int& nb) {
+  const int ti0 = int(w / nb_per_tile);
+  const Tile t0 = ld_tile(a.tiles + ti0);
+  const int off = ld_const(a.expert_off + t0.expert);
+  const int cnt = ld_const(a.expert_off + t0.expert + 1) - off;
+  const int base = ti0 - (t0.row0 - off) / a.tile_rows;
+  const int nt = (cnt + a.tile_rows - 1) / a.tile_rows;
+  const long q = w - long(base) * nb_per_tile;
+  nb = int(q / nt);
+  ti = base + int(q - long(nb) * nt);
+}
+
+// Gate/up: a workgroup's 256 weight rows are 128 intermediate rows of Wg and
+// Wu; wave w takes intermediate rows 32 w .. 32 w + 31 as its gate block
+// (j = 0) and up block (j = 1), so a lane holds gate and up of the same
+// elements and SwiGLU is applied in registers.
+struct GateUpPackedProv {
+  const u16* wg;     // packed [Iv][D] of the (virtual) expert
+  const u16* wu;
+  const u16* xb;
+  int D, Iv, i0, wave;
+  const int32_t* perm;
+  int row0, rows;
+  __device__ int nseg() const { return 1; }
+  __device__ int seg_chunks() const { return D / kPK; }
+  __device__ const u16* wbase(int j, int) const { return j ? wu : wg; }
+  __device__ uint32_t wblk(int) const {
+    int rb = (i0 >> 5) + wave;
+    if (rb >= (Iv >> 5)) rb = 0;   // absent rows: results never stored
+    return uint32_t(rb) * uint32_t(D / kPK) * kPackBlock;
+  }
+  __device__ const u16* xbase(int) const { return xb; }
+  __device__ uint32_t xoff(int R) const {
+    const int rr = R < rows ? R : 0;   // absent rows read the tile's first token
+    const int t = perm ? perm[row0 + rr] : row0 + rr;
+    return uint32_t(t) * uint32_t(D);
+  }
+};
+
+__global__ __launch_bounds__(256, 1) void k_gate_up_packed(ExpertArgs a) {
+  __shared__ PrefillSmem<128> sm;
+  constexpr int BM = 128, JM = BM / 32, IB = 128;   // IB: intermediate rows per item
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ntr = ld_const(&a.plan->n_tiles_routed), nts = ld_const(&a.plan->n_tiles_shared);
+  const int nbr = (a.I + IB - 1) / IB, nbs = a.S > 0 ? (a.S * a.Is + IB - 1) / IB : 1;
+  const long total = long(ntr) * nbr + long(nts) * nbs;
+  for (XcdRange it = xcd_range(total); it.next < it.end; it.next += it.step) {
+    int ti, nb;
+    bool shared;
+    work_item(it.next, ntr, nts, nbr, nbs, ti, nb, shared);
+    if (!shared) packed_routed_item(a, it.next, nbr, ti, nb);
+    const Tile tl = ld_tile(a.tiles + ti);
+    const int Iv = shared ? a.S * a.Is : a.I;
+    GateUpPackedProv pv;
+    pv.wg = shared ? a.psg : a.pg + size_t(tl.expert) * a.I * a.D;
+    pv.wu = shared ? a.psu : a.pu + size_t(tl.expert) * a.I * a.D;
+    pv.perm = shared ? nullptr : a.perm_token;
+    pv.xb = (const u16*)a.x;
+    pv.D = a.D;
+    pv.Iv = Iv;
+    pv.i0 = nb * IB;
+    pv.wave = wave;
+    pv.row0 = tl.row0;
+    pv.rows = tl.rows;
+    f32x16 acc[2][JM];
+    prefill_accumulate<BM>(pv, sm, acc, tl.rows);
+    u16* hb = shared ? (u16*)a.h_sh : (u16*)a.h;
+#pragma unroll
+    for (int b = 0; b < JM; ++b) {
+      const int r = b * 32 + (lane & 31);
+      if (r < tl.rows) {
+        const f32x16 g = acc[0][b], u = acc[1][b];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = nb * IB + 32 * wave + 8 * q + 4 * (lane >> 5);
+          if (n < Iv) {
+            ushort4 hv;
+            hv.x = f32_to_bf16(silu_f32(g[4 * q + 0]) * u[4 * q + 0]);
+            hv.y = f32_to_bf16(silu_f32(g[4 * q + 1]) * u[4 * q + 1]);
+            hv.z = f32_to_bf16(silu_f32(g[4 * q + 2]) * u[4 * q + 2]);
+            hv.w = f32_to_bf16(silu_f32(g[4 * q + 3]) * u[4 * q + 3]);
+            *reinterpret_cast<ushort4*>(hb + size_t(tl.row0 + r) * Iv + n) = hv;
+          }
+        }
+      }
+    }
+  }
+}
+
+// Down: a workgroup's 256 weight rows are output features d0 .. d0 + 255;
+// wave w takes d0 + 64 w .. + 63 as two 32-row blocks.  The fused shared
+// expert has one k segment (one packed matrix) per shared expert.  With a k
+// split (down_split) the items are split as in k_down_tiled, and each split
+// writes fp32 partials.
+struct DownPackedProv {
+  const u16* wd;     // packed [D][I] of the expert, or the shared experts' first [D][Is]
+  const u16* h;      // rows of h for this tile, row stride hs
+  int D, Iv, Is, S, hs, d0, wave, rows;
+  bool shared;
+  __device__ int nseg() const { return shared ? S : 1; }
+  __device__ int seg_chunks() const { return (shared ? Is : Iv) / kPK; }
+  __device__ const u16* wbase(int, int seg) const { return shared ? wd + size_t(seg) * D * Is : wd; }
+  __device__ uint32_t wblk(int j) const {
+    int rb = (d0 >> 5) + 2 * wave + j;
+    if (rb >= (D >> 5)) rb = 0;
+    return uint32_t(rb) * uint32_t(seg_chunks()) * kPackBlock;
+  }
+  __device__ const u16* xbase(int seg) const { return h + (shared ? seg * Is : 0); }
+  __device__ uint32_t xoff(int R) const { return uint32_t(R < rows ? R : 0) * uint32_t(hs); }
+};
+
+__global__ __launch_bounds__(256, 1) void k_down_packed(ExpertArgs a) {
+  __shared__ PrefillSmem<128> sm;
+  constexpr int BM = 128, JM = BM / 32, DB = 256;   // output features per item
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ntr = ld_const(&a.plan->n_tiles_routed), nts = ld_const(&a.plan->n_tiles_shared);
+  const int nb_all = (a.D + DB - 1) / DB;
+  const long items = long(ntr + nts) * nb_all;
+  const int ks = down_split(items, a.down_slots);
+  for (XcdRange it = xcd_range(items * ks); it.next < it.end; it.next += it.step) {
+    int ti, nb;
+    const long wi = it.next / ks;
+    const int split = int(it.next - wi * ks);
+    down_item(wi, ntr, nts, nb_all, ti, nb);
+    const bool shared = ti >= ntr;
+    if (!shared) packed_routed_item(a, wi, nb_all, ti, nb);
+    const Tile tl = ld_tile(a.tiles + ti);
+    DownPackedProv pv;
+    pv.D = a.D;
+    pv.S = a.S;
+    pv.Is = a.Is;
+    pv.shared = shared;
+    pv.rows = tl.rows;
+    pv.wave = wave;
+    pv.d0 = nb * DB;
+    if (shared) {
+      pv.wd = a.psd;
+      pv.Iv = a.S * a.Is;
+      pv.hs = a.S * a.Is;
+      pv.h = (const u16*)a.h_sh + size_t(tl.row0) * pv.hs;
+    } else {
+      pv.wd = a.pd + size_t(tl.expert) * a.D * a.I;
+      pv.Iv = a.I;
+      pv.hs = a.I;
+      pv.h = (const u16*)a.h + size_t(tl.row0) * pv.hs;
+    }
+    const int C = pv.nseg() * pv.seg_chunks();
+    f32x16 acc[2][JM];
+    prefill_accumulate<BM>(pv, sm, acc, tl.rows, C * split / ks, C * (split + 1) / ks);
+    u16* ob = static_cast<u16*>(shared ? a.o_sh : a.o);
+    float* pb = shared ? a.op_sh + split * a.op_sh_stride : a.op + split * a.op_stride;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int b = 0; b < JM; ++b) {
+        const int r = b * 32 + (lane & 31);
+        if (r < tl.rows) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int d = pv.d0 + 64 * wave + 32 * j + 8 * q + 4 * (lane >> 5);
+            if (d < a.D) {
+              const f32x16& v = acc[j][b];
+              const size_t e = size_t(tl.row0 + r) * a.D + d;
+              if (ks == 1)
+                st4_bf16(ob, e, v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+              else
+                *reinterpret_cast<float4*>(pb + e) =
+                    make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+            }
+          }
+        }
+      }
+  }
+}
+
+// Packed operand layout (see beam_moe_pack_weights): one thread per 16-byte
+// chunk of the output, i.e. per (matrix, row block, k block, k-step, lane).
+__global__ __launch_bounds__(256) void k_pack_weights(const u16* __restrict__ w, long chunks,
+                                                      int rows, int cols, u16* __restrict__ out) {
+  const long per_mat = long(rows) * cols / 8;
+  for (long q = long(blockIdx.x) * blockDim.x + threadIdx.x; q < chunks; q += long(gridDim.x) * blockDim.x) {
+    const long m = q / per_mat;
+    const long r = q - m * per_mat;        // chunk within the matrix
+    const long blk = r >> 8;               // 256 chunks per 32 x 64 block
+    const int within = int(r & 255);
+    const int s = within >> 6, l = within & 63;
+    const long kbs = cols / 64;
+    const long rb = blk / kbs, kb = blk - rb * kbs;
+    const long row = 32 * rb + (l & 31);
+    const long col = 64 * kb + 16 * s + 8 * (l >> 5);
+    const u16* src = w + m * long(rows) * cols + row * cols + col;
+    *reinterpret_cast<u32x4*>(out + q * 8) = *reinterpret_cast<const u32x4*>(src);
+  }
+}
+
+hipError_t launch_pack_weights(const void* w, int mats, int rows, int cols, void* packed,
+                               hipStream_t s) {
+  const long chunks = long(mats) * rows * cols / 8;
+  const long blocks = std::min<long>((chunks + 255) / 256, 8192);
+  prof_before("pack_weights", s);
+  hipLaunchKernelGGL(k_pack_weights, dim3(unsigned(std::max<long>(blocks, 1))), dim3(256), 0, s,
+                     (const u16*)w, chunks, rows, cols, (u16*)packed);
+  prof_after(s);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // fp32 layers: plain SIMT products over the same tiles (16 rows per tile).
 // ---------------------------------------------------------------------------
 
@@ -811,6 +1044,12 @@ static ExpertArgs expert_args(const beam_moe_layer& L, const void* x, int32_t T,
   a.qsg = L.scale_shared_gate;
   a.qsu = L.scale_shared_up;
   a.qsd = L.scale_shared_down;
+  a.pg = (const u16*)L.wp_gate;
+  a.pu = (const u16*)L.wp_up;
+  a.pd = (const u16*)L.wp_down;
+  a.psg = (const u16*)L.wsp_gate;
+  a.psu = (const u16*)L.wsp_up;
+  a.psd = (const u16*)L.wsp_down;
   a.T = T;
   a.D = L.D;
   a.E = L.E;
@@ -820,6 +1059,8 @@ static ExpertArgs expert_args(const beam_moe_layer& L, const void* x, int32_t T,
   a.plan = p.plan;
   a.tiles = p.tiles;
   a.perm_token = p.perm_token;
+  a.expert_off = p.expert_off;
+  a.tile_rows = 0;
   a.h = p.h;
   a.h_sh = p.h_shared;
   a.o = p.o;
@@ -981,7 +1222,7 @@ static void down_streaming(const beam_moe_layer& L, const ExpertArgs& a, long ti
 
 hipError_t launch_gate_up(const beam_moe_layer& L, const void* x, int32_t T, int tile_rows,
                           const WsLayout&, const Ptrs& p, hipStream_t s) {
-  const ExpertArgs a = expert_args(L, x, T, p);
+  ExpertArgs a = expert_args(L, x, T, p);
   long nts;
   const long ntr = tile_bound(L, T, tile_rows, &nts);
   if (L.dtype == BEAM_F32) {
@@ -998,6 +1239,14 @@ hipError_t launch_gate_up(const beam_moe_layer& L, const void* x, int32_t T, int
   } else if (tile_rows <= 64) {
     prof_before("gate_up_swiglu_stream", s);
     gate_up_streaming<false>(L, a, ntr, nts, tile_rows, s);
+    prof_after(s);
+  } else if (L.wp_gate) {   // packed weights: tiles of 128 token rows
+    a.tile_rows = tile_rows;
+    const long items = ntr * ((L.I + 127) / 128) +
+                       nts * (L.n_shared ? (L.n_shared * L.I_shared + 127) / 128 : 0);
+    prof_before("gate_up_swiglu_packed", s);
+    hipLaunchKernelGGL(k_gate_up_packed, dim3(tiled_grid((const void*)&k_gate_up_packed, items)),
+                       dim3(256), 0, s, a);
     prof_after(s);
   } else {
     const int ib = tile_rows == 256 ? 64 : 128;   // intermediate rows per tile
@@ -1017,13 +1266,14 @@ hipError_t launch_gate_up(const beam_moe_layer& L, const void* x, int32_t T, int
 
 // Resident workgroups of the tiled down kernel for a tile height (0: the
 // launch streams, no split).
-static int down_tiled_slots(int tile_rows) {
+static int down_tiled_slots(const beam_moe_layer& L, int tile_rows) {
+  if (L.wp_gate) return resident_blocks((const void*)&k_down_packed, 256);
   if (tile_rows == 256) return resident_blocks((const void*)&k_down_tiled<128, 256>, 256);
   if (tile_rows == 128) return resident_blocks((const void*)&k_down_tiled<256, 128>, 256);
   return 0;
 }
 static int down_tiled_nb(const beam_moe_layer& L, int tile_rows) {
-  const int bn = tile_rows == 256 ? 128 : 256;
+  const int bn = L.wp_gate ? 256 : tile_rows == 256 ? 128 : 256;
   return (L.D + bn - 1) / bn;
 }
 static bool down_may_split(const beam_moe_layer& L, int tile_rows) {
@@ -1033,7 +1283,7 @@ static bool down_may_split(const beam_moe_layer& L, int tile_rows) {
 hipError_t launch_down(const beam_moe_layer& L, int32_t T, int tile_rows, const WsLayout&,
                        const Ptrs& p, hipStream_t s, bool allow_split) {
   ExpertArgs a = expert_args(L, nullptr, T, p);
-  if (allow_split && p.o_part && down_may_split(L, tile_rows)) a.down_slots = down_tiled_slots(tile_rows);
+  if (allow_split && p.o_part && down_may_split(L, tile_rows)) a.down_slots = down_tiled_slots(L, tile_rows);
   long nts;
   const long ntr = tile_bound(L, T, tile_rows, &nts);
   if (L.dtype == BEAM_F32) {
@@ -1050,6 +1300,14 @@ hipError_t launch_down(const beam_moe_layer& L, int32_t T, int tile_rows, const 
   } else if (tile_rows <= 64) {
     prof_before("down_stream", s);
     down_streaming<false>(L, a, ntr + nts, tile_rows, s);
+    prof_after(s);
+  } else if (L.wp_gate) {   // packed weights: tiles of 128 token rows
+    a.tile_rows = tile_rows;
+    const long items = (ntr + nts) * ((L.D + 255) / 256);
+    const long gi = a.down_slots > 0 ? items * kMaxDownSplit : items;
+    prof_before("down_packed", s);
+    hipLaunchKernelGGL(k_down_packed, dim3(tiled_grid((const void*)&k_down_packed, gi)), dim3(256),
+                       0, s, a);
     prof_after(s);
   } else {
     const int bn = tile_rows == 256 ? 128 : 256;
@@ -1074,7 +1332,7 @@ hipError_t launch_combine(const beam_moe_layer& L, int32_t T, int tile_rows, con
   CombineSplit cs{nullptr, 0, 0, nullptr, nullptr, 0, 0};
   if (p.o_part && down_may_split(L, tile_rows)) {
     const ExpertArgs a = expert_args(L, nullptr, T, p);
-    cs = CombineSplit{p.plan, down_tiled_slots(tile_rows), down_tiled_nb(L, tile_rows), a.op, a.op_sh,
+    cs = CombineSplit{p.plan, down_tiled_slots(L, tile_rows), down_tiled_nb(L, tile_rows), a.op, a.op_sh,
                       a.op_stride, a.op_sh_stride};
   }
   prof_before("combine", s);

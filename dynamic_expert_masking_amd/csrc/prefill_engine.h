@@ -1,0 +1,235 @@
+// Prefill matrix-product engine for expert weights in the packed operand
+// layout (gfx950).
+//
+// Packed layout of a weight matrix W [R][K] (R and K multiples of 32 and 64):
+// blocks of 32 rows x 64 k, block (rb, kb) at element (rb * K/64 + kb) * 2048;
+// inside a block, k-step s (16 k values) then lane l, 8 elements each:
+//   packed[(rb * K/64 + kb) * 2048 + s * 512 + l * 8 + j]
+//     = W[32 rb + l % 32][64 kb + 16 s + 8 (l / 32) + j],
+// which is the A operand of v_mfma_f32_32x32x16_bf16 for lane l.  One wave's
+// 16-byte loads of a k-step then read 1 KB of contiguous memory -- eight
+// whole 128-byte lines -- straight into operand registers.  (Loads in the
+// operand layout from row-major weights touch 32 lines per instruction and
+// run at about a third of the rate, even from L2.)
+//
+// One workgroup of 4 waves computes an output tile of 256 weight rows x BM
+// token rows (BM = 128) with fp32 accumulators.  Wave w owns weight rows
+// [64 w, 64 w + 64) (two 32-row blocks) against all BM token rows, so every
+// weight element is loaded by exactly one wave, kStages - 1 k slices ahead of
+// its use.  Token rows are shared by the 4 waves through a ring of three LDS
+// slice buffers: each 64-wide slice is loaded with coalesced 16-byte loads
+// (8 lanes per 128-byte row segment) one slice ahead, and stored with the
+// 16-byte chunks of each 128-byte row XOR-swizzled by (row / 2) % 8, so that
+// the 16 lanes of an LDS phase hit distinct bank groups both when storing and
+// when reading MFMA fragments.  One barrier per slice.  Loads are branch-free
+// (absent rows read a valid row whose results are never stored; the slices
+// past the end read offset 0 of their bases), and the MFMA loop is
+// instantiated per count of valid 32-token blocks.
+#pragma once
+#include "device_common.h"
+#include "gemm_engines.h"
+
+namespace beam {
+
+constexpr int kPK = 64;        // k slice (elements)
+constexpr int kPStages = 3;   // weight slices held in registers per wave
+
+template <int BM>
+struct PrefillSmem {
+  u16 x[3][BM * kPK];   // a ring of three token slices
+};
+
+constexpr int kPackBlock = 32 * kPK;   // elements of one packed 32 x 64 block
+
+// Element offset, in a slice buffer, of the 16-byte chunk c (k = 8c .. 8c+7)
+// of token row R.
+__device__ __forceinline__ int prefill_x_off(int R, int c) {
+  return R * kPK + 8 * (c ^ ((R >> 1) & 7));
+}
+
+// Provider interface (per tile):
+//   int nseg(), seg_chunks()        k segments and 64-wide slices per segment
+//   const u16* wbase(j, seg)        packed matrix of this wave's weight block j
+//                                   (0 or 1) in segment seg
+//   uint32_t wblk(j)                element offset of that block's row of
+//                                   packed blocks (32 rb * seg_chunks * 64)
+//   const u16* xbase(seg)           uniform base of the token rows
+//   uint32_t xoff(R)                element offset of token row R (0..BM-1)
+// On return acc[j][b][i] = C[n = 64 wave + 32 j + 8 (i / 4) + 4 (lane / 32) + i % 4]
+//                          [m = 32 b + lane % 32]
+// for the first NJ = ceil(rows_valid / 32) token blocks (the others are
+// left at zero).
+// k chunks [c_lo, c_hi) of the provider's nseg * seg_chunks (c_hi < 0: to the
+// end), for a k split of the product.
+template <int BM, class Prov>
+__device__ __forceinline__ void prefill_accumulate(const Prov& pv, PrefillSmem<BM>& sm,
+                                                   f32x16 (&acc)[2][BM / 32], int rows_valid,
+                                                   int c_lo = 0, int c_hi = -1) {
+  constexpr int JM = BM / 32;      // token blocks
+  constexpr int XL = BM / 32;      // token chunks per thread per slice
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int b = 0; b < JM; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[j][b][i] = 0.f;
+
+  const int nseg = pv.nseg();
+  const int cps = pv.seg_chunks();
+  const int C = c_hi < 0 ? nseg * cps : c_hi;
+  // weight operand offsets: this lane's 16 bytes of each packed k-step
+  uint32_t wo[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) wo[j] = pv.wblk(j) + 8 * lane;
+  // token slice loads: rows tid / 8 + 32 i, chunk tid % 8
+  const int trow = tid >> 3, tch = tid & 7;
+  uint32_t xo[XL];
+  int xl[XL];
+#pragma unroll
+  for (int i = 0; i < XL; ++i) {
+    xo[i] = pv.xoff(trow + 32 * i) + 8 * tch;
+    xl[i] = prefill_x_off(trow + 32 * i, tch);
+  }
+  // fragment reads: row lane % 32 of each 32-token block, chunk 2 s + lane / 32
+  int fo[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) fo[s] = prefill_x_off(lane & 31, 2 * s + (lane >> 5));
+
+  struct WStage {
+    u32x4 v[2][4];
+  };
+  struct XStage {
+    u32x4 v[XL];
+  };
+  // Slice c of this wave's weights; past the end, offset 0 of the last
+  // segment's bases (masked with integer arithmetic, so no branch).
+  auto load_w = [&](WStage& st, int c) {
+    const uint32_t msk = c < C ? ~0u : 0u;
+    const int cc = max(min(c, C - 1), 0);   // an empty range reads chunk 0
+    const int seg = cc / cps;
+    const uint32_t kb = uint32_t(cc - seg * cps) * kPackBlock;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const u16* b = pv.wbase(j, seg);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) st.v[j][s] = ld16_at(b, (wo[j] + kb + 512 * s) & msk);
+    }
+  };
+  auto load_x = [&](XStage& st, int c) {
+    const uint32_t msk = c < C ? ~0u : 0u;
+    const int cc = max(min(c, C - 1), 0);   // an empty range reads chunk 0
+    const int seg = cc / cps;
+    const uint32_t km = uint32_t(cc - seg * cps) * kPK;
+    const u16* xb = pv.xbase(seg);
+#pragma unroll
+    for (int i = 0; i < XL; ++i) st.v[i] = ld16_at(xb, (xo[i] + km) & msk);
+  };
+  // store a token slice at LDS element offset buf (0, BM*64 or 2*BM*64)
+  auto store_x_at = [&](const XStage& st, int buf) {
+#pragma unroll
+    for (int i = 0; i < XL; ++i) *reinterpret_cast<u32x4*>(&sm.x[0][buf + xl[i]]) = st.v[i];
+  };
+  auto store_x = [&](const XStage& st, int) { store_x_at(st, 0); };
+
+  auto run = [&](auto nj_const) {
+    constexpr int NJ = decltype(nj_const)::value;
+    typedef u32x4 Frag[NJ];
+    // fragments of k-step s of the slice at LDS element offset buf
+    auto frag = [&](Frag& xf, int buf, int s) {
+#pragma unroll
+      for (int b = 0; b < NJ; ++b)
+        xf[b] = *reinterpret_cast<const u32x4*>(&sm.x[0][buf + b * 32 * kPK + fo[s]]);
+    };
+    auto mma = [&](const WStage& w, const Frag& xf, int s) {
+#pragma unroll
+      for (int b = 0; b < NJ; ++b)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[j][b] = mfma32_bf16(w.v[j][s], xf[b], acc[j][b]);
+    };
+    // One k-step's MFMAs with the next k-step's fragment reads threaded
+    // between them (one LDS read per two MFMAs), so that the reads are in
+    // flight while the matrix unit is busy.
+    auto overlap = [&](const WStage& w, const Frag& cur, int s, Frag& nxt, int nbuf, int ns) {
+      frag(nxt, nbuf, ns);
+      mma(w, cur, s);
+#pragma unroll
+      for (int b = 0; b < NJ; ++b) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // two MFMAs
+      }
+    };
+    constexpr int SL = BM * kPK;   // elements per slice buffer
+    WStage ws[kPStages];
+    XStage xs;
+    Frag fa, fb;
+    // The prologue issues loads in the loop's pattern (token slice, then
+    // weight slice), so that the compiler's wait counts agree at the loop
+    // header with those inside the loop.
+    load_x(xs, c_lo);
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(ws[0], c_lo);
+    __builtin_amdgcn_sched_barrier(0);
+    store_x(xs, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_x(xs, c_lo + 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 1; q < kPStages - 1; ++q) load_w(ws[q], c_lo + q);
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    frag(fa, 0, 0);
+    int bcur = 0, bnxt = SL;   // LDS buffers of slices c and c + 1 (a ring of three)
+    // Iteration c: store token slice c + 1 (loaded during iteration c - 1)
+    // into the next buffer, issue the loads of token slice c + 2 and weight
+    // slice c + kStages - 1, then multiply slice c.  The one barrier sits
+    // after k-step 1: past it, slice c + 1 is in LDS (every wave stored its
+    // part before the barrier), so k-step 0 of slice c + 1 is read during
+    // k-step 3 of slice c; and the buffer written at iteration c + 1 (that
+    // of slice c - 1) was last read before this barrier.
+    // The three groups are kept in this order (scheduling barriers): loads
+    // complete in issue order, so waiting for the token slice before storing
+    // it must not also wait for weight loads issued after it.
+    auto step = [&](int c, const WStage& cur, WStage& nxt) {
+      store_x_at(xs, bnxt);
+      __builtin_amdgcn_sched_barrier(0);
+      load_x(xs, c + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      load_w(nxt, c + kPStages - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      overlap(cur, fa, 0, fb, bcur, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      overlap(cur, fb, 1, fa, bcur, 2);
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+      overlap(cur, fa, 2, fb, bcur, 3);
+      __builtin_amdgcn_sched_barrier(0);
+      overlap(cur, fb, 3, fa, bnxt, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      const int bn = bnxt + SL;
+      bcur = bnxt;
+      bnxt = bn == 3 * SL ? 0 : bn;
+    };
+    // whole rounds of kStages slices (static stage indices), then the rest
+    int c = c_lo;
+    static_assert(kPStages == 3, "the loop is unrolled for three stages");
+    for (; c + 3 <= C; c += 3) {
+      step(c, ws[0], ws[2]);
+      step(c + 1, ws[1], ws[0]);
+      step(c + 2, ws[2], ws[1]);
+    }
+    if (c < C) step(c, ws[0], ws[2]);
+    if (c + 1 < C) step(c + 1, ws[1], ws[0]);
+    // the last fragment reads (of the slice past the end) are discarded;
+    // the next tile's stores wait at its first barrier
+    __syncthreads();
+  };
+  static_assert(BM == 128, "tiles of 128 token rows");
+  const int nj = min(JM, max(1, (rows_valid + 31) / 32));
+  tiled_dispatch<JM>(nj, [&](auto nj_const) {
+    if constexpr (decltype(nj_const)::value > 0) run(nj_const);
+  });
+}
+
+}  // namespace beam

@@ -9,10 +9,11 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (BEAM_BF16, BEAM_F32, WEIGHTS_DTYPE, WEIGHTS_FP8_E4M3, beam_moe_workspace_size,
-               make_layer, make_route_out)
+from . import (BEAM_BF16, BEAM_F32, WEIGHTS_DTYPE, WEIGHTS_FP8_E4M3, beam_moe_pack_weights,
+               beam_moe_workspace_size, make_layer, make_route_out)
 
 SCALES = ("s_gate", "s_up", "s_down", "ss_gate", "ss_up", "ss_down")
+PACKED = ("wp_gate", "wp_up", "wp_down", "wsp_gate", "wsp_up", "wsp_down")
 
 
 def to_device(a: np.ndarray, device="cuda") -> torch.Tensor:
@@ -46,7 +47,7 @@ class DeviceLayer:
     ss_up, ss_down.
     """
 
-    def __init__(self, host, device="cuda"):
+    def __init__(self, host, device="cuda", pack=False):
         c = host.cfg
         self.cfg = c
         self.device = device
@@ -60,7 +61,28 @@ class DeviceLayer:
             self.t[name] = up(getattr(host, name, None)) if self.fp8 else None
         self.dtype_code = BEAM_F32 if c.dtype == "f32" else BEAM_BF16
         self.torch_dtype = torch.float32 if c.dtype == "f32" else torch.bfloat16
+        # optional second copies of the expert weights in the packed operand layout
+        self.packed = bool(pack) and c.dtype == "bf16" and not self.fp8
+        for name in PACKED:
+            self.t[name] = None
+        if self.packed:
+            self._pack()
         self.desc = self._desc(self.t)
+
+    def _pack(self):
+        """Packed copies of the bf16 expert weights (beam_moe_pack_weights)."""
+        c = self.cfg
+        plan = [("wp_gate", "w_gate", c.E, c.I, c.D), ("wp_up", "w_up", c.E, c.I, c.D),
+                ("wp_down", "w_down", c.E, c.D, c.I)]
+        if c.S:
+            plan += [("wsp_gate", "ws_gate", 1, c.S * c.I_s, c.D), ("wsp_up", "ws_up", 1, c.S * c.I_s, c.D),
+                     ("wsp_down", "ws_down", c.S, c.D, c.I_s)]
+        stream = torch.cuda.current_stream().cuda_stream
+        for dst, src, mats, rows, cols in plan:
+            w = self.t[src]
+            out = torch.empty_like(w)
+            beam_moe_pack_weights(w, mats, rows, cols, out, stream)
+            self.t[dst] = out
 
     def _desc(self, t):
         c = self.cfg
@@ -72,7 +94,8 @@ class DeviceLayer:
                           expert_format=WEIGHTS_FP8_E4M3 if self.fp8 else WEIGHTS_DTYPE,
                           scale_gate=t["s_gate"], scale_up=t["s_up"], scale_down=t["s_down"],
                           scale_shared_gate=t["ss_gate"], scale_shared_up=t["ss_up"],
-                          scale_shared_down=t["ss_down"], segment_len=getattr(c, "segment", 0))
+                          scale_shared_down=t["ss_down"], segment_len=getattr(c, "segment", 0),
+                          **{k: t[k] for k in PACKED})
 
     def replicas(self, n: int):
         """n extra copies of the expert weights at distinct addresses (same

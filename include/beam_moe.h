@@ -137,6 +137,20 @@ typedef struct {
                                   S-token segment of the batch, and runs those
                                   experts on its own x.  Negative values are
                                   BEAM_ERR_INVALID_ARG.                       */
+  /* Optional second copies of the bf16 expert weights in the packed operand
+   * layout written by beam_moe_pack_weights (same values, another
+   * arrangement; NULL = absent).  Either all that the layer uses are given
+   * (wp_gate, wp_up, wp_down, and the three shared ones when n_shared > 0,
+   * 16-byte aligned) or none; only with dtype BEAM_BF16 and expert_format
+   * BEAM_WEIGHTS_DTYPE.  Batches large enough for the prefill-shaped
+   * kernels (128-token tiles) then read these, whose operand-layout loads
+   * are whole cache lines; smaller batches read w_gate .. ws_down as always. */
+  const void *wp_gate;         /* packed w_gate: E matrices [I][D]            */
+  const void *wp_up;           /* packed w_up: E matrices [I][D]              */
+  const void *wp_down;         /* packed w_down: E matrices [D][I]            */
+  const void *wsp_gate;        /* packed ws_gate: one matrix [n_shared I_shared][D] */
+  const void *wsp_up;          /* packed ws_up: one matrix [n_shared I_shared][D]   */
+  const void *wsp_down;        /* packed ws_down: n_shared matrices [D][I_shared]   */
 } beam_moe_layer;
 
 /* Routing results (device pointers, caller-owned). */
@@ -211,6 +225,25 @@ int beam_moe_forward(const beam_moe_layer *layer, const void *x, int32_t T,
 int beam_moe_forward_static(const beam_moe_layer *layer, const void *x,
                             int32_t T, void *y, const beam_route_out *out,
                             void *stream);
+
+/* Packed operand layout of bf16 expert weights (for the wp_* / wsp_*
+ * fields above).  Rearranges `mats` row-major matrices W [rows][cols], stored
+ * one after another at w, into `packed` (same size, caller-owned, not
+ * overlapping w), matrix by matrix:
+ *   packed[m][(rb * cols/64 + kb) * 2048 + s * 512 + l * 8 + j]
+ *     = W_m[32 rb + l % 32][64 kb + 16 s + 8 (l / 32) + j]
+ * for rb < rows/32, kb < cols/64, s < 4, l < 64, j < 8: blocks of 32 rows x
+ * 64 columns, and within a block the A operand of the gfx950
+ * v_mfma_f32_32x32x16_bf16 instruction for lane l at k-step s.  A
+ * 64-lane load of one k-step then reads 1 KB of contiguous memory.  rows must
+ * be a multiple of 32, cols of 64, and rows * cols below 2^31.  Device
+ * pointers, 16-byte aligned; enqueued on `stream`.  Meant to run once, when
+ * the weights are loaded (for expert weights this is a layout of the layer's
+ * parameters, like a transposition).  The routed gate and up weights are E
+ * matrices [I][D], down E matrices [D][I]; the shared gate and up one matrix
+ * [n_shared I_shared][D], the shared down n_shared matrices [D][I_shared]. */
+int beam_moe_pack_weights(const void *w, int32_t mats, int32_t rows,
+                          int32_t cols, void *packed, void *stream);
 
 /* Mask-router training step: the loss value and straight-through gradient.
  * (BEAM page on aitrends.kr, method paragraph, training strategy: L = L_lm +

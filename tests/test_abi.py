@@ -191,6 +191,38 @@ def test_forward_static_argument_checks():
             <= dm.STATIC_WORKSPACE_BYTES, name
 
 
+def test_pack_weights_argument_checks():
+    """beam_moe_pack_weights validates before launching: rows a multiple of 32,
+    columns of 64, aligned non-null pointers, no overlap."""
+    f = dm.lib().beam_moe_pack_weights
+    assert f(FAKE, 2, 48, 64, FAKE * 64, None) == dm.BEAM_ERR_INVALID_ARG      # rows % 32
+    assert f(FAKE, 2, 64, 96, FAKE * 64, None) == dm.BEAM_ERR_INVALID_ARG      # cols % 64
+    assert f(None, 2, 64, 64, FAKE * 64, None) == dm.BEAM_ERR_INVALID_ARG
+    assert f(FAKE, 2, 64, 64, FAKE + 8, None) == dm.BEAM_ERR_INVALID_ARG        # misaligned
+    assert f(FAKE, 2, 64, 64, FAKE + 4096, None) == dm.BEAM_ERR_INVALID_ARG     # overlaps the input
+    assert f(FAKE, 0, 64, 64, FAKE * 64, None) == dm.BEAM_OK                    # nothing to do
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(wp_gate=FAKE), dm.BEAM_ERR_INVALID_ARG),                               # partial set
+    (dict(wp_gate=FAKE, wp_up=FAKE, wp_down=FAKE + 8), dm.BEAM_ERR_INVALID_ARG),  # misaligned
+    (dict(wp_gate=FAKE, wp_up=FAKE, wp_down=FAKE, dtype=dm.BEAM_F32), dm.BEAM_ERR_INVALID_ARG),
+    (dict(wp_gate=FAKE, wp_up=FAKE, wp_down=FAKE, wsp_gate=FAKE, wsp_up=FAKE, wsp_down=FAKE),
+     dm.BEAM_ERR_INVALID_ARG),                                                   # shared copies, no shared experts
+    (dict(wp_gate=FAKE, wp_up=FAKE, wp_down=FAKE, n_shared=1, I_shared=64, ws_gate=FAKE, ws_up=FAKE,
+          ws_down=FAKE), dm.BEAM_ERR_INVALID_ARG),                               # shared copies missing
+    (dict(wp_gate=FAKE, wp_up=FAKE, wp_down=FAKE, expert_format=1, scale_gate=FAKE, scale_up=FAKE,
+          scale_down=FAKE), dm.BEAM_ERR_INVALID_ARG),                            # FP8 weights
+])
+def test_packed_weight_fields(kw, status):
+    L = fake_layer(**kw)
+    assert dm.beam_moe_workspace_size(L, 16) == 0
+    rc = dm.lib().beam_moe_forward(ctypes.byref(L), FAKE, 4, FAKE * 2, None, FAKE * 3, 1 << 40, None)
+    assert rc == status
+    ok = fake_layer(wp_gate=FAKE, wp_up=FAKE, wp_down=FAKE)
+    assert dm.beam_moe_workspace_size(ok, 16) > 0
+
+
 def test_mask_backward_argument_checks():
     L = fake_layer()
     ws = 0x20000

@@ -19,6 +19,15 @@ import synth
 from common import (GOLDEN, cached_layer, inputs, layer_from_json, small_config, with_mask)
 from gpu_helpers import (check_output, check_routing, device_layer, note, padded_layer,
                          run_forward, run_route, sample_tokens)
+from gpu_helpers import _dev_cache as _gpu_dev_cache
+from dynamic_expert_masking_amd.device import to_device, to_host_bits
+import dynamic_expert_masking_amd as dm
+
+
+def _dev_cache_clear():
+    """Frees the cached device layer (the packed tests hold a second copy)."""
+    _gpu_dev_cache.clear()
+    torch.cuda.empty_cache()
 from oracle_pins import small_layer, small_x
 
 pytestmark = pytest.mark.gpu
@@ -164,6 +173,85 @@ def test_split_down(T, S):
     x = small_x(layer, T, "split")
     note(f"[split down] T={T} S={S}")
     y, rt, _ = run_forward(device_layer(layer), x)
+    rt_ref, y_ref = oracle.forward(layer, x)
+    check_routing(rt, rt_ref, layer.cfg.E)
+    check_output(y, y_ref, "bf16")
+
+
+def _packed_reference(w: np.ndarray) -> np.ndarray:
+    """The packed operand layout of matrices w [mats][rows][cols] (bf16 bits),
+    written out from its definition in the header: block (rb, kb) of 32 rows
+    x 64 columns, then k-step s, lane l, element j."""
+    mats, rows, cols = w.shape
+    out = np.empty(w.size, dtype=w.dtype)
+    kbs = cols // 64
+    q = 0
+    for m in range(mats):
+        for rb in range(rows // 32):
+            for kb in range(kbs):
+                for s in range(4):
+                    for l in range(64):
+                        r = 32 * rb + l % 32
+                        c = 64 * kb + 16 * s + 8 * (l // 32)
+                        out[q:q + 8] = w[m, r, c:c + 8]
+                        q += 8
+    return out
+
+
+def test_pack_weights_layout():
+    """beam_moe_pack_weights against the layout's definition, element by element."""
+    rng = np.random.default_rng(3)
+    w = rng.integers(0, 1 << 16, size=(3, 64, 192), dtype=np.uint16)
+    wd = to_device(w)
+    out = torch.empty_like(wd)
+    dm.beam_moe_pack_weights(wd, 3, 64, 192, out, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    got = to_host_bits(out).reshape(-1)
+    assert np.array_equal(got, _packed_reference(w))
+
+
+PACKED_CASES = [("mixtral", 2048), ("dsv2lite_prefill", 4096), ("finegrained", 8192), ("mixtral", 32),
+                ("dsv2lite_decode", 256)]
+
+
+@pytest.mark.parametrize("name,T", PACKED_CASES, ids=[f"{n}-T{T}" for n, T in PACKED_CASES])
+def test_packed_weights_workloads(name, T):
+    """The layer with packed copies of its expert weights: prefill-sized
+    batches run the packed kernels (tiles of 128 rows; the Mixtral down
+    product splits its k range), decode batches the streaming kernels on the
+    row-major weights.  Routing exact; y on every token up to 8192 (Mixtral
+    T=2048: a sample covering every 32-row block of every expert)."""
+    from dynamic_expert_masking_amd.device import DeviceLayer
+    cfg = synth.CONFIGS[name]
+    layer = cached_layer(name)
+    x = inputs(cfg, T, layer)
+    _dev_cache_clear()
+    dl = DeviceLayer(layer, pack=True)
+    note(f"[packed weights] {name} T={T}")
+    y, rt, ys = run_forward(dl, x, reps=2)
+    rt_ref = oracle.route(layer, x)
+    check_routing(rt, rt_ref, cfg.E)
+    assert np.array_equal(ys[0], ys[1]), "two identical calls gave different y"
+    toks = np.arange(T) if T <= FULL_Y_MAX[name] or name != "mixtral" else tile_cover_tokens(rt_ref, cfg.E, T)
+    _, y_ref = oracle.forward(layer, x, tokens=toks)
+    rel = check_output(y[toks], y_ref, cfg.dtype)
+    note(f"[packed weights] {name} T={T}: rel_err={rel:.2e} tokens_compared={len(toks)}")
+    del dl
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("T,S", [(1200, 2), (700, 0), (3000, 1), (130, 1)])
+def test_packed_small_layers(T, S):
+    """Packed weights on small layers: two shared experts (one packed down
+    matrix per shared expert, a segment boundary inside a split k range), no
+    shared expert, ragged tiles, and a batch small enough for the streaming
+    kernels."""
+    from dynamic_expert_masking_amd.device import DeviceLayer
+    layer = small_layer(f"packed{S}", D=256, E=8, K=2, I=256, S=S, I_s=128 if S else 0, keep=0.7,
+                        router_bias=True)
+    x = small_x(layer, T, "packed")
+    note(f"[packed weights] small layer T={T} S={S}")
+    y, rt, _ = run_forward(DeviceLayer(layer, pack=True), x)
     rt_ref, y_ref = oracle.forward(layer, x)
     check_routing(rt, rt_ref, layer.cfg.E)
     check_output(y, y_ref, "bf16")
