@@ -327,10 +327,12 @@ struct PlanSmem {
   int32_t act;
 };
 
+// write_out = false: only sm.off / sm.toff (every workgroup of a multi-
+// workgroup kernel computes them; one stores the plan).
 template <int NT>
 __device__ void build_plan(PlanSmem& sm, int T, int E, int tile_rows, int has_shared,
                            int32_t* __restrict__ counts, int32_t* __restrict__ expert_off,
-                           Plan* __restrict__ plan, Tile* __restrict__ tiles) {
+                           Plan* __restrict__ plan, Tile* __restrict__ tiles, bool write_out = true) {
   const int tid = threadIdx.x, lane = tid & 63;
   if (tid == 0) sm.act = 0;
   for (int e = tid; e < E; e += NT) {
@@ -349,6 +351,7 @@ __device__ void build_plan(PlanSmem& sm, int T, int E, int tile_rows, int has_sh
   }
   __syncthreads();
   // The global outputs are stored after the last barrier.
+  if (!write_out) return;
   const int32_t P = sm.off[E - 1] + last_cnt;
   const int32_t ntr = sm.toff[E - 1] + last_tiles;
   const int32_t nts = has_shared ? (T + tile_rows - 1) / tile_rows : 0;
@@ -1021,9 +1024,94 @@ __global__ __launch_bounds__(1024) void k_scan(int T, int E, int nblk, int tile_
   build_plan<1024>(psm, T, E, tile_rows, has_shared, counts, expert_off, plan, tiles);
 }
 
+// Scan and scatter in one launch, for batches of at most G * kScanVals
+// blocks (G as in k_scan): one workgroup per 64-token block.  Each recomputes,
+// from the block counts (L2-resident), every expert's total and its own
+// block's offset within the expert (the sum over earlier blocks), scans the
+// totals into the expert offsets (workgroup 0 stores the plan and tiles), and
+// places its block's pairs.  One launch instead of a one-workgroup scan
+// followed by the scatter.
+__global__ __launch_bounds__(1024) void k_scan_scatter(int T, int E, int K, int nblk, int tile_rows,
+                                                       int has_shared,
+                                                       const int32_t* __restrict__ block_counts,
+                                                       const int32_t* __restrict__ idx,
+                                                       const int32_t* __restrict__ rank,
+                                                       int32_t* __restrict__ counts,
+                                                       int32_t* __restrict__ expert_off,
+                                                       Plan* __restrict__ plan, Tile* __restrict__ tiles,
+                                                       int32_t* __restrict__ perm_token,
+                                                       int32_t* __restrict__ slot_pos) {
+  __shared__ PlanSmem psm;
+  __shared__ int32_t s_all[1024], s_below[1024];
+  __shared__ int32_t s_pre[kMaxExperts];
+  const int tid = threadIdx.x, blk = blockIdx.x;
+  int G = 1;
+  while (2 * G * E <= 1024 && G < 64) G *= 2;
+  const int per = (nblk + G - 1) / G;   // <= kScanVals (host check)
+  const int part = tid / E, e0 = tid - part * E;
+  const bool act = part < G;
+  const int b0 = part * per;
+  int32_t all = 0, below = 0;
+#pragma unroll
+  for (int u = 0; u < kScanVals; ++u) {
+    const int b = b0 + u;
+    const int32_t c = (act && u < per && b < nblk) ? block_counts[size_t(b) * E + e0] : 0;
+    all += c;
+    below += b < blk ? c : 0;
+  }
+  if (act) {
+    s_all[part * E + e0] = all;
+    s_below[part * E + e0] = below;
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += 1024) {
+    int32_t a = 0, bl = 0;
+    for (int q = 0; q < G; ++q) {
+      a += s_all[q * E + e];
+      bl += s_below[q * E + e];
+    }
+    psm.cnt[e] = a;
+    s_pre[e] = bl;
+  }
+  __syncthreads();
+  build_plan<1024>(psm, T, E, tile_rows, has_shared, counts, expert_off, plan, tiles, blk == 0);
+  const int t0 = blk * kSelBlock;
+  for (int q = tid; q < kSelBlock * K; q += 1024) {
+    const int tl = q / K, k = q - tl * K;
+    const int t = t0 + tl;
+    if (t >= T) continue;
+    const size_t sk = size_t(t) * K + k;
+    const int rk = rank[sk];
+    int pos = -1;
+    if (rk >= 0) {
+      const int e = idx[sk];
+      pos = psm.off[e] + s_pre[e] + rk;
+      perm_token[pos] = t;
+    }
+    slot_pos[sk] = pos;
+  }
+}
+
+// Whether the scan kernel also scatters (k_scan_scatter); the scatter launch
+// is then empty.
+static bool scan_scatters(const beam_moe_layer& L, int32_t T) {
+  const int nblk = (T + kSelBlock - 1) / kSelBlock;
+  int G = 1;
+  while (2 * G * L.E <= 1024 && G < 64) G *= 2;
+  return nblk <= long(G) * kScanVals;
+}
+
 hipError_t launch_scan(const beam_moe_layer& L, int32_t T, int tile_rows, const Ptrs& p,
                        hipStream_t s, bool all_pairs) {
   const int nblk = (T + kSelBlock - 1) / kSelBlock;
+  if (scan_scatters(L, T)) {
+    prof_before("scan_scatter", s);
+    hipLaunchKernelGGL(k_scan_scatter, dim3(unsigned(nblk)), dim3(1024), 0, s, T, L.E, L.K, nblk,
+                       tile_rows, (L.n_shared > 0 && !all_pairs) ? 1 : 0, p.block_counts, p.idx,
+                       p.rank, p.counts, p.expert_off, p.plan, p.tiles, p.perm_token, p.slot_pos);
+    prof_after(s);
+    return hipGetLastError();
+  }
   prof_before("scan_tiles", s);
   hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, T, L.E, nblk, tile_rows,
                      (L.n_shared > 0 && !all_pairs) ? 1 : 0, p.block_counts, p.counts,
@@ -1063,6 +1151,7 @@ __global__ __launch_bounds__(256) void k_scatter(int T, int E, int K, const int3
 }
 
 hipError_t launch_scatter(const beam_moe_layer& L, int32_t T, const Ptrs& p, hipStream_t s) {
+  if (scan_scatters(L, T)) return hipSuccess;   // placed by the scan kernel
   const int nblk = (T + kSelBlock - 1) / kSelBlock;
   prof_before("scatter_pairs", s);
   hipLaunchKernelGGL(k_scatter, dim3(unsigned(nblk)), dim3(256), 0, s, T, L.E, L.K, p.idx, p.rank,
