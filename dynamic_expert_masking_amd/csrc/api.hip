@@ -21,7 +21,10 @@ int expert_tile_rows(const beam_moe_layer& L, int32_t T) {
   if (per_expert <= 32) return 32;
   // FP8 weights only have the streaming kernels (tiles of up to 64 rows)
   if (per_expert <= 96 || L.expert_format == BEAM_WEIGHTS_FP8_E4M3) return 64;
-  // packed weights: the prefill kernels take tiles of 128 token rows
+  // packed weights: the expert-stationary kernels (no shared experts, at
+  // least kEsMinPerExpert candidates per expert), else tiles of 128 rows
+  if (L.wp_gate && L.n_shared == 0 && L.D % 128 == 0 && per_expert >= kEsMinPerExpert)
+    return kEsTileRows;
   if (per_expert < 512 || L.wp_gate) return 128;
   return 256;
 }
@@ -78,6 +81,11 @@ WsLayout workspace_layout(const beam_moe_layer& L, int32_t T) {
                           expert_tile_rows(L, T) > 64;
   w.o_part_bytes = split_down ? size_t(kMaxDownSplit) * (TK + (IS ? T : 0)) * L.D * 4 : 0;
   w.o_part = take(w.o_part_bytes);
+  // expert-stationary prefill: packed tokens and h of every tile
+  const bool es = expert_tile_rows(L, T) == kEsTileRows;
+  const size_t es_tiles = es ? size_t((TK + kEsTileRows - 1) / kEsTileRows + std::min<size_t>(L.E, TK)) : 0;
+  w.es_x = take(es_tiles * kEsTileRows * L.D * 2);
+  w.es_h = take(es_tiles * kEsTileRows * L.I * 2);
   w.zsel = take(TK * 4);
   w.dz = take(TK * 4);
   w.lreg_tok = take(size_t(T) * 4);
@@ -262,6 +270,8 @@ static Ptrs carve(const WsLayout& w, void* ws, const beam_route_out* out) {
   p.o = b + w.o;
   p.o_shared = b + w.o_shared;
   p.o_part = w.o_part_bytes ? reinterpret_cast<float*>(b + w.o_part) : nullptr;
+  p.es_x = b + w.es_x;
+  p.es_h = b + w.es_h;
   p.zsel = reinterpret_cast<float*>(b + w.zsel);
   p.dz = reinterpret_cast<float*>(b + w.dz);
   p.lreg_tok = reinterpret_cast<float*>(b + w.lreg_tok);

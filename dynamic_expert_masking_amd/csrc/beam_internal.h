@@ -34,9 +34,15 @@ struct Tile {
   int32_t pad;
 };
 
+// Expert-stationary prefill: tiles of this many token rows (12 blocks of 32)
+// for layers with packed weights and no shared experts whose batches give an
+// expert at least kEsMinPerExpert top-K candidates on average.
+constexpr int kEsTileRows = 384;
+constexpr int kEsMinPerExpert = 256;
+
 struct WsLayout {
   size_t plan, logits, idx, gates, mask, counts, rank, block_counts, expert_off, tiles, perm_token,
-      slot_pos, h, h_shared, o, o_shared, o_part, zsel, dz, lreg_tok, total;
+      slot_pos, h, h_shared, o, o_shared, o_part, zsel, dz, lreg_tok, es_x, es_h, total;
   size_t o_part_bytes;   // 0 when the layer's down product never splits
   int32_t max_tiles;
 };
@@ -72,6 +78,9 @@ struct Ptrs {
   // k-split down products (prefill tiles): fp32 partial outputs
   // [kMaxDownSplit][T K][D], then the shared ones [kMaxDownSplit][T][D]
   float* o_part;
+  // expert-stationary prefill: packed tokens and packed h of every tile
+  void* es_x;   // [tiles][12 x D/64 blocks of 32 x 64] bf16
+  void* es_h;   // [tiles][12 x I/64 blocks]
   // mask-router backward
   float* zsel;       // [T][K] mask logit of each candidate
   float* dz;         // [P] dL/dz of each pair (pair order)

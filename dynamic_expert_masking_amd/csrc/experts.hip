@@ -52,6 +52,10 @@ struct ExpertArgs {
   const int32_t* perm_token;
   const int32_t* expert_off;   // [E + 1] first pair of each expert (prefill item order)
   int tile_rows;               // rows per routed tile (the last of an expert may be shorter)
+  // expert-stationary prefill (tiles of kEsTileRows rows): packed tokens of
+  // each tile ([tile][12 x D/64 blocks of 32 x 64]) and packed h ([tile][12 x I/64])
+  u16* xpk;
+  u16* hpk;
   void* h;         // [P][I]
   void* h_sh;      // [T][S*Is]
   void* o;         // [P][D] expert outputs: fp32 (fp32 layers) or bf16
@@ -826,6 +830,149 @@ hipError_t launch_pack_weights(const void* w, int mats, int rows, int cols, void
 }
 
 // ---------------------------------------------------------------------------
+// Expert-stationary prefill (layers with packed weights and no shared
+// experts, tiles of kEsTileRows rows): the tokens of each tile are packed
+// into the MFMA operand layout once (k_pack_tokens_es), gate/up writes h in
+// the same packed layout, and both products run the expert-stationary
+// engine, so that an expert's weight blocks stream from HBM once per tile.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ size_t es_tile_elems(int K) { return size_t(kEsTokBlocks) * K * 32; }
+
+// Packed tokens of every routed tile: 16-byte chunk (tile t, token block tb,
+// k block kb, k-step s, lane l) = x[token of row 32 tb + l % 32][64 kb + 16 s
+// + 8 (l / 32) .. + 7]; rows past the tile's end take its first token (their
+// results are never stored).  Blocks with no token of the tile are skipped.
+__global__ __launch_bounds__(256) void k_pack_tokens_es(ExpertArgs a) {
+  const int ntr = ld_const(&a.plan->n_tiles_routed);
+  const int C = a.D / kPK;
+  const long per_tile = long(kEsTokBlocks) * C * 256;
+  const long total = long(ntr) * per_tile;
+  for (long q = long(blockIdx.x) * blockDim.x + threadIdx.x; q < total; q += long(gridDim.x) * blockDim.x) {
+    const int t = int(q / per_tile);
+    const long rem = q - long(t) * per_tile;
+    const int tb = int(rem / (long(C) * 256));
+    const int kb = int((rem >> 8) % C);
+    const int w = int(rem & 255), s = w >> 6, l = w & 63;
+    const Tile tl = ld_tile(a.tiles + t);
+    if (32 * tb >= tl.rows) continue;
+    const int r = 32 * tb + (l & 31);
+    const int tok = a.perm_token[tl.row0 + (r < tl.rows ? r : 0)];
+    const u16* src = static_cast<const u16*>(a.x) + size_t(tok) * a.D + 64 * kb + 16 * s + 8 * (l >> 5);
+    u16* dst = a.xpk + size_t(t) * es_tile_elems(a.D) + (size_t(tb) * C + kb) * kPackBlock + 512 * s + 8 * l;
+    *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+  }
+}
+
+struct EsGateUpProv {
+  const u16* wg;   // packed gate matrix of the expert, at row block 2 nb
+  const u16* wu;
+  const u16* xt;   // packed tokens of the tile
+  int C;
+  __device__ int chunks() const { return C; }
+  __device__ const u16* wbase(int bb) const {
+    return (bb < 2 ? wg : wu) + size_t(bb & 1) * C * kPackBlock;
+  }
+  __device__ const u16* xbase() const { return xt; }
+};
+
+// Items: (tile, block of 64 intermediate rows), tile-major, so that the
+// items of one tile (its tokens) share an XCD's L2.  Weight blocks 0, 1 are
+// gate rows 64 nb .. 64 nb + 63, blocks 2, 3 the same up rows: a lane holds
+// gate and up of the same element, and SwiGLU is applied in registers.  h is
+// written in the packed layout of the down product's token operand.
+__global__ __launch_bounds__(256, 1) void k_gate_up_es(ExpertArgs a) {
+  __shared__ EsSmem sm;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ntr = ld_const(&a.plan->n_tiles_routed);
+  const int nbk = a.I / 64;
+  const int C = a.D / kPK, CI = a.I / kPK;
+  const long total = long(ntr) * nbk;
+  for (XcdRange it = xcd_range(total); it.next < it.end; it.next += it.step) {
+    const int t = int(it.next / nbk), nb = int(it.next - long(t) * nbk);
+    const Tile tl = ld_tile(a.tiles + t);
+    EsGateUpProv pv;
+    pv.C = C;
+    const size_t ebase = size_t(tl.expert) * a.I * a.D;
+    pv.wg = a.pg + ebase + size_t(2 * nb) * C * kPackBlock;
+    pv.wu = a.pu + ebase + size_t(2 * nb) * C * kPackBlock;
+    pv.xt = a.xpk + size_t(t) * es_tile_elems(a.D);
+    const int nbt = (tl.rows + 31) / 32;
+    f32x16 acc[kEsWBlocks][kEsWaveBlocks];
+    es_accumulate(pv, sm, acc, nbt);
+    u16* ht = a.hpk + size_t(t) * es_tile_elems(a.I);
+#pragma unroll
+    for (int j = 0; j < kEsWaveBlocks; ++j) {
+      const int tb = wave + 4 * j;
+      if (tb >= nbt) continue;   // wave-uniform
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x16& g = acc[b][j];
+          const f32x16& u = acc[b + 2][j];
+          ushort4 hv;
+          hv.x = f32_to_bf16(silu_f32(g[4 * q + 0]) * u[4 * q + 0]);
+          hv.y = f32_to_bf16(silu_f32(g[4 * q + 1]) * u[4 * q + 1]);
+          hv.z = f32_to_bf16(silu_f32(g[4 * q + 2]) * u[4 * q + 2]);
+          hv.w = f32_to_bf16(silu_f32(g[4 * q + 3]) * u[4 * q + 3]);
+          // element (token 32 tb + lane % 32, k = 64 nb + 32 b + 8 q + 4 (lane / 32) .. + 3)
+          const int s2 = 2 * b + (q >> 1), l2 = (lane & 31) + 32 * (q & 1);
+          *reinterpret_cast<ushort4*>(ht + (size_t(tb) * CI + nb) * kPackBlock + 512 * s2 + 8 * l2 +
+                                      4 * (lane >> 5)) = hv;
+        }
+    }
+  }
+}
+
+struct EsDownProv {
+  const u16* wd;   // packed down matrix of the expert, at row block 4 db (D % 128 == 0)
+  const u16* ht;
+  int CI;          // k slices
+  __device__ int chunks() const { return CI; }
+  __device__ const u16* wbase(int bb) const { return wd + size_t(bb) * CI * kPackBlock; }
+  __device__ const u16* xbase() const { return ht; }
+};
+
+// Items: (tile, block of 128 output rows), tile-major.  O rows are written
+// in pair order for the combine.
+__global__ __launch_bounds__(256, 1) void k_down_es(ExpertArgs a) {
+  __shared__ EsSmem sm;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ntr = ld_const(&a.plan->n_tiles_routed);
+  const int ndb = a.D / 128;
+  const int CI = a.I / kPK;
+  const long total = long(ntr) * ndb;
+  for (XcdRange it = xcd_range(total); it.next < it.end; it.next += it.step) {
+    const int t = int(it.next / ndb), db = int(it.next - long(t) * ndb);
+    const Tile tl = ld_tile(a.tiles + t);
+    EsDownProv pv;
+    pv.CI = CI;
+    pv.wd = a.pd + size_t(tl.expert) * a.D * a.I + size_t(4 * db) * CI * kPackBlock;
+    pv.ht = a.hpk + size_t(t) * es_tile_elems(a.I);
+    const int nbt = (tl.rows + 31) / 32;
+    f32x16 acc[kEsWBlocks][kEsWaveBlocks];
+    es_accumulate(pv, sm, acc, nbt);
+    u16* ob = static_cast<u16*>(a.o);
+#pragma unroll
+    for (int j = 0; j < kEsWaveBlocks; ++j) {
+      const int m = 32 * (wave + 4 * j) + (lane & 31);
+      if (m >= tl.rows) continue;
+#pragma unroll
+      for (int b = 0; b < kEsWBlocks; ++b)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int d = 128 * db + 32 * b + 8 * q + 4 * (lane >> 5);
+          const f32x16& v = acc[b][j];
+          st4_bf16(ob, size_t(tl.row0 + m) * a.D + d, v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+        }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 layers: plain SIMT products over the same tiles (16 rows per tile).
 // ---------------------------------------------------------------------------
 
@@ -1061,6 +1208,8 @@ static ExpertArgs expert_args(const beam_moe_layer& L, const void* x, int32_t T,
   a.perm_token = p.perm_token;
   a.expert_off = p.expert_off;
   a.tile_rows = 0;
+  a.xpk = reinterpret_cast<u16*>(p.es_x);
+  a.hpk = reinterpret_cast<u16*>(p.es_h);
   a.h = p.h;
   a.h_sh = p.h_shared;
   a.o = p.o;
@@ -1240,6 +1389,17 @@ hipError_t launch_gate_up(const beam_moe_layer& L, const void* x, int32_t T, int
     prof_before("gate_up_swiglu_stream", s);
     gate_up_streaming<false>(L, a, ntr, nts, tile_rows, s);
     prof_after(s);
+  } else if (tile_rows == kEsTileRows) {   // expert-stationary (packed weights)
+    prof_before("pack_tokens_es", s);
+    const long chunks = ntr * kEsTokBlocks * long(L.D / kPK) * 256;
+    hipLaunchKernelGGL(k_pack_tokens_es, dim3(unsigned(std::min<long>((chunks + 255) / 256, 4096))),
+                       dim3(256), 0, s, a);
+    prof_after(s);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    prof_before("gate_up_swiglu_es", s);
+    hipLaunchKernelGGL(k_gate_up_es, dim3(tiled_grid((const void*)&k_gate_up_es, ntr * (L.I / 64))),
+                       dim3(256), 0, s, a);
+    prof_after(s);
   } else if (L.wp_gate) {   // packed weights: tiles of 128 token rows
     a.tile_rows = tile_rows;
     const long items = ntr * ((L.I + 127) / 128) +
@@ -1277,7 +1437,8 @@ static int down_tiled_nb(const beam_moe_layer& L, int tile_rows) {
   return (L.D + bn - 1) / bn;
 }
 static bool down_may_split(const beam_moe_layer& L, int tile_rows) {
-  return L.dtype != BEAM_F32 && L.expert_format != BEAM_WEIGHTS_FP8_E4M3 && tile_rows > 64;
+  return L.dtype != BEAM_F32 && L.expert_format != BEAM_WEIGHTS_FP8_E4M3 && tile_rows > 64 &&
+         tile_rows != kEsTileRows;
 }
 
 hipError_t launch_down(const beam_moe_layer& L, int32_t T, int tile_rows, const WsLayout&,
@@ -1300,6 +1461,11 @@ hipError_t launch_down(const beam_moe_layer& L, int32_t T, int tile_rows, const 
   } else if (tile_rows <= 64) {
     prof_before("down_stream", s);
     down_streaming<false>(L, a, ntr + nts, tile_rows, s);
+    prof_after(s);
+  } else if (tile_rows == kEsTileRows) {   // expert-stationary (packed weights)
+    prof_before("down_es", s);
+    hipLaunchKernelGGL(k_down_es, dim3(tiled_grid((const void*)&k_down_es, ntr * (L.D / 128))),
+                       dim3(256), 0, s, a);
     prof_after(s);
   } else if (L.wp_gate) {   // packed weights: tiles of 128 token rows
     a.tile_rows = tile_rows;

@@ -26,6 +26,7 @@
 // past the end read offset 0 of their bases), and the MFMA loop is
 // instantiated per count of valid 32-token blocks.
 #pragma once
+#include "beam_internal.h"
 #include "device_common.h"
 #include "gemm_engines.h"
 
@@ -230,6 +231,148 @@ __device__ __forceinline__ void prefill_accumulate(const Prov& pv, PrefillSmem<B
   tiled_dispatch<JM>(nj, [&](auto nj_const) {
     if constexpr (decltype(nj_const)::value > 0) run(nj_const);
   });
+}
+
+// ---------------------------------------------------------------------------
+// Expert-stationary engine: one workgroup multiplies a 128-row block of
+// weights (four packed 32-row blocks) with every token of one tile of up to
+// kEsTileRows rows, so each weight block of an expert is read from HBM once
+// per tile instead of once per 128-token tile.  The roles of the packed
+// engine above are swapped: the weight slice (16 KB per 64-wide k slice)
+// goes through two LDS buffers and is shared by the 4 waves; each wave takes
+// the tile's 32-token blocks w, w + 4, w + 8 and loads them straight into
+// MFMA operand registers from a packed copy of the tokens (the same block
+// layout as the packed weights: block (tb, kb) of a tile at element
+// (tb * C + kb) * 2048, lane l's 16 bytes of k-step s at s * 512 + l * 8).
+// Weight and token slices are both held in three rotating register stages;
+// one barrier per slice.
+// ---------------------------------------------------------------------------
+
+constexpr int kEsTokBlocks = kEsTileRows / 32;   // tokens of one tile: 12 blocks of 32
+constexpr int kEsWaveBlocks = kEsTokBlocks / 4;   // token blocks per wave
+constexpr int kEsWBlocks = 4;               // 32-row weight blocks per workgroup
+
+struct EsSmem {
+  u16 w[2][kEsWBlocks * kPackBlock];   // two weight slice buffers
+};
+
+// Provider interface (per item):
+//   int chunks()                   64-wide k slices of the product
+//   const u16* wbase(bb)           packed matrix of weight block bb (0..3), at
+//                                  its row of packed blocks
+//   const u16* xbase()             packed tokens of the tile (block row 0)
+// On return acc[bb][j][i] = C[n = 32 bb + 8 (i / 4) + 4 (lane / 32) + i % 4]
+//                            [m = 32 (wave + 4 j) + lane % 32]
+// for the token blocks wave + 4 j < nbt (the others are left at zero).
+template <class Prov>
+__device__ __forceinline__ void es_accumulate(const Prov& pv, EsSmem& sm,
+                                              f32x16 (&acc)[kEsWBlocks][kEsWaveBlocks], int nbt) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+#pragma unroll
+  for (int b = 0; b < kEsWBlocks; ++b)
+#pragma unroll
+    for (int j = 0; j < kEsWaveBlocks; ++j)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[b][j][i] = 0.f;
+  const int C = pv.chunks();
+  // weight slice loads: thread tid takes block tid / 64, its lane's 16 bytes
+  // of the four k-steps
+  const int wbb = tid >> 6;
+  const u16* wb = pv.wbase(wbb) + 8 * lane;
+  const u16* xb = pv.xbase() + 8 * lane;
+  // this wave's token blocks (wave-uniform count)
+  const int nj = min(kEsWaveBlocks, max(0, (nbt - wave + 3) / 4));
+
+  struct WStage {
+    u32x4 v[4];
+  };
+  struct XStage {
+    u32x4 v[kEsWaveBlocks][4];
+  };
+  auto load_w = [&](WStage& st, int c) {
+    const uint32_t off = uint32_t(min(c, C - 1)) * kPackBlock;   // past the end: the last slice
+#pragma unroll
+    for (int s = 0; s < 4; ++s) st.v[s] = ld16_at_stream(wb, off + 512 * s);
+  };
+  auto store_w = [&](const WStage& st, int buf) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      *reinterpret_cast<u32x4*>(&sm.w[buf][wbb * kPackBlock + 512 * s + 8 * lane]) = st.v[s];
+  };
+
+  auto run = [&](auto nj_const) {
+    constexpr int NJ = decltype(nj_const)::value;
+    auto load_x = [&](XStage& st, int c) {
+      const int cc = min(c, C - 1);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const uint32_t off = uint32_t((wave + 4 * j) * C + cc) * kPackBlock;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) st.v[j][s] = ld16_at(xb, off + 512 * s);
+      }
+    };
+    // the four k-steps of the slice in LDS buffer buf
+    auto mma = [&](const XStage& xs, int buf) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        u32x4 wf[kEsWBlocks];
+#pragma unroll
+        for (int b = 0; b < kEsWBlocks; ++b)
+          wf[b] = *reinterpret_cast<const u32x4*>(&sm.w[buf][b * kPackBlock + 512 * s + 8 * lane]);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int b = 0; b < kEsWBlocks; ++b) acc[b][j] = mfma32_bf16(wf[b], xs.v[j][s], acc[b][j]);
+      }
+    };
+    WStage ws[3];
+    XStage xs[3];
+    // Stage k % 3 holds slice k.  Loads complete in issue order, so each
+    // iteration issues its token slice before its weight slice: waiting for
+    // a token slice then never waits for a weight slice issued later.  The
+    // prologue issues x0, w0, w1, x1, w2, as the loop would have.
+    load_x(xs[0], 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(ws[0], 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(ws[1], 1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_x(xs[1], 1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(ws[2], 2);
+    __builtin_amdgcn_sched_barrier(0);
+    store_w(ws[0], 0);
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    // Iteration c: store weight slice c + 1 into the other buffer (it held
+    // slice c - 1, read before the last barrier), issue token slice c + 2
+    // and weight slice c + 3, multiply slice c, barrier.  A weight slice has
+    // two iterations to arrive, a token slice two.
+    int buf = 0;
+    auto step = [&](int c, WStage& wstore, XStage& xcur, XStage& xnext, WStage& wnext) {
+      store_w(wstore, buf ^ 1);
+      __builtin_amdgcn_sched_barrier(0);
+      load_x(xnext, c + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      load_w(wnext, c + 3);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(xcur, buf);
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+      buf ^= 1;
+    };
+    int c = 0;
+    for (; c + 3 <= C; c += 3) {
+      step(c, ws[1], xs[0], xs[2], ws[0]);
+      step(c + 1, ws[2], xs[1], xs[0], ws[1]);
+      step(c + 2, ws[0], xs[2], xs[1], ws[2]);
+    }
+    if (c < C) step(c, ws[1], xs[0], xs[2], ws[0]);
+    if (c + 1 < C) step(c + 1, ws[2], xs[1], xs[0], ws[1]);
+  };
+  tiled_dispatch<kEsWaveBlocks>(nj, [&](auto nj_const) { run(nj_const); });
 }
 
 }  // namespace beam

@@ -240,12 +240,14 @@ def test_packed_weights_workloads(name, T):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("T,S", [(1200, 2), (700, 0), (3000, 1), (130, 1)])
+@pytest.mark.parametrize("T,S", [(1200, 2), (700, 0), (3000, 1), (1100, 0), (3000, 0), (130, 1)])
 def test_packed_small_layers(T, S):
     """Packed weights on small layers: two shared experts (one packed down
     matrix per shared expert, a segment boundary inside a split k range), no
     shared expert, ragged tiles, and a batch small enough for the streaming
-    kernels."""
+    kernels.  Without shared experts and with at least 256 candidates per
+    expert (T = 1100, 3000) the expert-stationary kernels run, on tiles of up
+    to 384 rows (T = 3000: two tiles for most experts)."""
     from dynamic_expert_masking_amd.device import DeviceLayer
     layer = small_layer(f"packed{S}", D=256, E=8, K=2, I=256, S=S, I_s=128 if S else 0, keep=0.7,
                         router_bias=True)
