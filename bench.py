@@ -50,6 +50,7 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 KERNEL_SOURCES = ("dynamic_expert_masking_amd/csrc/experts.hip",
                   "dynamic_expert_masking_amd/csrc/stream_engine.h",
                   "dynamic_expert_masking_amd/csrc/gemm_engines.h",
+                  "dynamic_expert_masking_amd/csrc/prefill_engine.h",
                   "dynamic_expert_masking_amd/csrc/device_common.h")
 
 # (workload, T, shape, target): every batch size of every workload.
@@ -185,7 +186,8 @@ def main():
         host = synth.make_layer(c)
         if args.zero_mask:
             host = replace(host, w_mask=np.zeros_like(host.w_mask), b_mask=None)
-        dl = DeviceLayer(host, dev, pack=pack)
+        # the workload's Avg-K (K times its keep probability) as the kernel-choice hint
+        dl = DeviceLayer(host, dev, pack=pack, avg_k_hint=c.avg_k_target)
         per_copy = sum(v.numel() * v.element_size() for v in dl.t.values() if v is not None)
         copies = args.copies or max(2, min(16, int(np.ceil(1.5e9 / max(1, per_copy))) + 1))
         reps = [(dl.t, dl.desc)] + dl.replicas(copies - 1)

@@ -45,7 +45,8 @@ class beam_moe_layer(ctypes.Structure):
                 ("scale_shared_up", ctypes.c_void_p), ("scale_shared_down", ctypes.c_void_p),
                 ("segment_len", ctypes.c_int32),
                 ("wp_gate", ctypes.c_void_p), ("wp_up", ctypes.c_void_p), ("wp_down", ctypes.c_void_p),
-                ("wsp_gate", ctypes.c_void_p), ("wsp_up", ctypes.c_void_p), ("wsp_down", ctypes.c_void_p)]
+                ("wsp_gate", ctypes.c_void_p), ("wsp_up", ctypes.c_void_p), ("wsp_down", ctypes.c_void_p),
+                ("expected_avg_k", ctypes.c_float)]
 
 
 # beam_gate_flag bits of beam_moe_layer.gating
@@ -137,7 +138,7 @@ def make_layer(D, E, K, I, dtype, w_router, w_mask, w_gate, w_up, w_down, b_rout
                ws_down=None, gating=0, expert_format=WEIGHTS_DTYPE, scale_gate=None,
                scale_up=None, scale_down=None, scale_shared_gate=None, scale_shared_up=None,
                scale_shared_down=None, segment_len=0, wp_gate=None, wp_up=None, wp_down=None,
-               wsp_gate=None, wsp_up=None, wsp_down=None) -> beam_moe_layer:
+               wsp_gate=None, wsp_up=None, wsp_down=None, expected_avg_k=0.0) -> beam_moe_layer:
     """Fill a beam_moe_layer descriptor from tensors (or raw addresses).  The
     caller keeps the tensors alive while the descriptor is in use."""
     return beam_moe_layer(D, E, K, I, n_shared, I_shared, dtype, _ptr(w_router), _ptr(w_mask),
@@ -146,7 +147,7 @@ def make_layer(D, E, K, I, dtype, w_router, w_mask, w_gate, w_up, w_down, b_rout
                           int(expert_format), _ptr(scale_gate), _ptr(scale_up), _ptr(scale_down),
                           _ptr(scale_shared_gate), _ptr(scale_shared_up), _ptr(scale_shared_down),
                           int(segment_len), _ptr(wp_gate), _ptr(wp_up), _ptr(wp_down),
-                          _ptr(wsp_gate), _ptr(wsp_up), _ptr(wsp_down))
+                          _ptr(wsp_gate), _ptr(wsp_up), _ptr(wsp_down), float(expected_avg_k))
 
 
 def make_route_out(topk_idx, gates, mask, expert_count) -> beam_route_out:

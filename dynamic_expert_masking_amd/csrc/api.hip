@@ -23,8 +23,11 @@ int expert_tile_rows(const beam_moe_layer& L, int32_t T) {
   if (per_expert <= 96 || L.expert_format == BEAM_WEIGHTS_FP8_E4M3) return 64;
   // packed weights: the expert-stationary kernels (no shared experts, at
   // least kEsMinPerExpert candidates per expert), else tiles of 128 rows
-  if (L.wp_gate && L.n_shared == 0 && L.D % 128 == 0 && per_expert >= kEsMinPerExpert)
-    return kEsTileRows;
+  if (L.wp_gate && L.n_shared == 0 && L.D % 128 == 0) {
+    // surviving pairs per expert expected from the layer's Avg-K (K if unknown)
+    const float avg_k = L.expected_avg_k > 0.f ? L.expected_avg_k : float(L.K);
+    if (double(T) * avg_k >= double(kEsMinPerExpert) * L.E) return kEsTileRows;
+  }
   if (per_expert < 512 || L.wp_gate) return 128;
   return 256;
 }
@@ -167,6 +170,7 @@ static int check_layer(const beam_moe_layer* L) {
   if ((L->gating & BEAM_GATE_BINARY) && (L->gating & BEAM_GATE_SOFTMAX_ALL))
     return BEAM_ERR_INVALID_ARG;
   if (L->segment_len < 0) return BEAM_ERR_INVALID_ARG;
+  if (!(L->expected_avg_k >= 0.f && L->expected_avg_k <= float(L->K))) return BEAM_ERR_INVALID_ARG;
   if (L->n_shared > 0 && L->I_shared <= 0) return BEAM_ERR_INVALID_ARG;
   const void* req[] = {L->w_router, L->w_mask, L->w_gate, L->w_up, L->w_down};
   for (const void* p : req)

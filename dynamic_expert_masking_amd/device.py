@@ -44,13 +44,16 @@ class DeviceLayer:
     D, E, K, I, S, I_s, dtype and optionally gating, expert_format, segment), w_router,
     w_mask, b_router, b_mask, w_gate, w_up, w_down, ws_gate, ws_up, ws_down,
     and for FP8 expert weights the row scales s_gate, s_up, s_down, ss_gate,
-    ss_up, ss_down.
+    ss_up, ss_down.  pack=True adds packed copies of bf16 expert weights
+    (beam_moe_pack_weights); avg_k_hint fills the descriptor's
+    expected_avg_k (0: unknown).
     """
 
-    def __init__(self, host, device="cuda", pack=False):
+    def __init__(self, host, device="cuda", pack=False, avg_k_hint=0.0):
         c = host.cfg
         self.cfg = c
         self.device = device
+        self.avg_k_hint = float(avg_k_hint)   # expected_avg_k of the descriptor (0: unknown)
         up = lambda a: None if a is None else to_device(a, device)  # noqa: E731
         self.t = {name: up(getattr(host, name)) for name in
                   ("w_router", "w_mask", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")}
@@ -95,7 +98,7 @@ class DeviceLayer:
                           scale_gate=t["s_gate"], scale_up=t["s_up"], scale_down=t["s_down"],
                           scale_shared_gate=t["ss_gate"], scale_shared_up=t["ss_up"],
                           scale_shared_down=t["ss_down"], segment_len=getattr(c, "segment", 0),
-                          **{k: t[k] for k in PACKED})
+                          expected_avg_k=self.avg_k_hint, **{k: t[k] for k in PACKED})
 
     def replicas(self, n: int):
         """n extra copies of the expert weights at distinct addresses (same

@@ -151,6 +151,14 @@ typedef struct {
   const void *wsp_gate;        /* packed ws_gate: one matrix [n_shared I_shared][D] */
   const void *wsp_up;          /* packed ws_up: one matrix [n_shared I_shared][D]   */
   const void *wsp_down;        /* packed ws_down: n_shared matrices [D][I_shared]   */
+  /* Expected Avg-K of the layer (mean number of kept experts per token, the
+   * figure the BEAM pages report; aitrends.kr results paragraph), or 0 when
+   * unknown (then K is assumed).  A hint for choosing kernels only: with
+   * packed weights and no shared experts, batches expected to give each
+   * expert at least 256 surviving pairs (T x expected_avg_k / E) run the
+   * expert-stationary prefill kernels.  Results never depend on it.  Must
+   * be finite and in [0, K] (else BEAM_ERR_INVALID_ARG). */
+  float expected_avg_k;
 } beam_moe_layer;
 
 /* Routing results (device pointers, caller-owned). */

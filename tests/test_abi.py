@@ -281,3 +281,24 @@ def test_stats_host_rejects_negative_counts():
     L = fake_layer()
     with pytest.raises(dm.BeamError):
         dm.beam_moe_stats_host(L, [1, -1, 0, 0, 0, 0, 0, 0], 4)
+
+
+def test_expected_avg_k_hint():
+    """expected_avg_k must lie in [0, K]; it only steers the kernel choice:
+    for a packed layer without shared experts, the expert-stationary
+    kernels (and their workspace) are chosen from T x Avg-K / E >= 256."""
+    for bad in (-0.5, 2.5, float("nan"), float("inf")):
+        assert dm.beam_moe_workspace_size(fake_layer(expected_avg_k=bad), 16) == 0
+    packed = dict(wp_gate=FAKE, wp_up=FAKE, wp_down=FAKE)
+    T = 1024   # T x K / E = 256: expert-stationary without a hint
+    full = dm.beam_moe_workspace_size(fake_layer(**packed), T)
+    thin = dm.beam_moe_workspace_size(fake_layer(expected_avg_k=0.5, **packed), T)
+    same = dm.beam_moe_workspace_size(fake_layer(expected_avg_k=2.0, **packed), T)
+    assert full == same > thin > 0
+    # without packed copies the hint changes nothing
+    assert (dm.beam_moe_workspace_size(fake_layer(), T) ==
+            dm.beam_moe_workspace_size(fake_layer(expected_avg_k=0.5), T))
+    # sizes stay non-decreasing in T with the hint as well
+    L = fake_layer(expected_avg_k=1.0, **packed)
+    sizes = [dm.beam_moe_workspace_size(L, t) for t in (1, 512, 1024, 2047, 2048, 4096)]
+    assert all(a <= b for a, b in zip(sizes, sizes[1:]))
