@@ -161,6 +161,22 @@ __device__ __forceinline__ void prefill_accumulate(const Prov& pv, PrefillSmem<B
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // two MFMAs
       }
     };
+    // The same with the step's global loads threaded in as well, ceil(loads /
+    // 2 NJ) after each pair of MFMAs of the first two k-steps, so that the
+    // wave issues them while the matrix unit works through queued MFMAs
+    // (DeepSeek-V2-Lite prefill T = 4096 on MI355X: gate/up 216 -> 208 us,
+    // down 163 -> 159 us).
+    auto overlap_v = [&](const WStage& w, const Frag& cur, int s, Frag& nxt, int nbuf, int ns) {
+      frag(nxt, nbuf, ns);
+      mma(w, cur, s);
+      constexpr int VM = (XL + 8 + 2 * NJ - 1) / (2 * NJ);
+#pragma unroll
+      for (int b = 0; b < NJ; ++b) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // two MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x020, VM, 0);  // global loads
+      }
+    };
     constexpr int SL = BM * kPK;   // elements per slice buffer
     WStage ws[kPStages];
     XStage xs;
@@ -189,19 +205,18 @@ __device__ __forceinline__ void prefill_accumulate(const Prov& pv, PrefillSmem<B
     // part before the barrier), so k-step 0 of slice c + 1 is read during
     // k-step 3 of slice c; and the buffer written at iteration c + 1 (that
     // of slice c - 1) was last read before this barrier.
-    // The three groups are kept in this order (scheduling barriers): loads
-    // complete in issue order, so waiting for the token slice before storing
-    // it must not also wait for weight loads issued after it.
+    // The token stores come first (a scheduling barrier), then the token
+    // loads ahead of the weight loads, threaded among the MFMAs of the first
+    // two k-steps: loads complete in issue order, so waiting for the token
+    // slice before storing it must not also wait for weight loads issued
+    // after it.
     auto step = [&](int c, const WStage& cur, WStage& nxt) {
       store_x_at(xs, bnxt);
       __builtin_amdgcn_sched_barrier(0);
       load_x(xs, c + 2);
-      __builtin_amdgcn_sched_barrier(0);
       load_w(nxt, c + kPStages - 1);
-      __builtin_amdgcn_sched_barrier(0);
-      overlap(cur, fa, 0, fb, bcur, 1);
-      __builtin_amdgcn_sched_barrier(0);
-      overlap(cur, fb, 1, fa, bcur, 2);
+      overlap_v(cur, fa, 0, fb, bcur, 1);
+      overlap_v(cur, fb, 1, fa, bcur, 2);
       __builtin_amdgcn_sched_barrier(0);
       __syncthreads();
       overlap(cur, fa, 2, fb, bcur, 3);
@@ -313,18 +328,38 @@ __device__ __forceinline__ void es_accumulate(const Prov& pv, EsSmem& sm,
         for (int s = 0; s < 4; ++s) st.v[j][s] = ld16_at(xb, off + 512 * s);
       }
     };
-    // the four k-steps of the slice in LDS buffer buf
+    // The four k-steps of the slice in LDS buffer buf, in groups of (weight
+    // block b, k-step s): the group's NJ MFMAs, then one global load of the
+    // step's token and weight slices (the first 4 NJ + 4 groups), one store
+    // of the next weight slice into LDS (the last four groups, after every
+    // fragment read), and the read of block b's fragment of k-step s + 1
+    // into the register the MFMAs just consumed.  A fragment read then has
+    // three groups of MFMAs to arrive, and the wave issues its loads and
+    // stores while the matrix unit works through queued MFMAs instead of
+    // ahead of them (Mixtral-shaped T = 2048 on MI355X: gate/up 583 -> 551
+    // us with the loads threaded, 572 with the stores too; down 283 -> 273).
+    // The grouping is pinned with scheduling-group barriers: left alone, the
+    // compiler sinks every read to just before its MFMAs.
     auto mma = [&](const XStage& xs, int buf) {
+      const u16* wl = &sm.w[buf][8 * lane];
+      u32x4 wf[kEsWBlocks];
+#pragma unroll
+      for (int b = 0; b < kEsWBlocks; ++b) wf[b] = *reinterpret_cast<const u32x4*>(wl + b * kPackBlock);
+      __builtin_amdgcn_sched_group_barrier(0x100, kEsWBlocks, 0);   // LDS reads
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        u32x4 wf[kEsWBlocks];
 #pragma unroll
-        for (int b = 0; b < kEsWBlocks; ++b)
-          wf[b] = *reinterpret_cast<const u32x4*>(&sm.w[buf][b * kPackBlock + 512 * s + 8 * lane]);
+        for (int b = 0; b < kEsWBlocks; ++b) {
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
-#pragma unroll
-          for (int b = 0; b < kEsWBlocks; ++b) acc[b][j] = mfma32_bf16(wf[b], xs.v[j][s], acc[b][j]);
+          for (int j = 0; j < NJ; ++j) acc[b][j] = mfma32_bf16(wf[b], xs.v[j][s], acc[b][j]);
+          if (NJ > 0) __builtin_amdgcn_sched_group_barrier(0x008, NJ, 0);   // MFMAs
+          if (4 * s + b < 4 * NJ + 4) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // global load
+          if (s == 3) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // LDS store
+          if (s < 3) {
+            wf[b] = *reinterpret_cast<const u32x4*>(wl + b * kPackBlock + 512 * (s + 1));
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+          }
+        }
       }
     };
     WStage ws[3];
@@ -346,19 +381,17 @@ __device__ __forceinline__ void es_accumulate(const Prov& pv, EsSmem& sm,
     store_w(ws[0], 0);
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
-    // Iteration c: store weight slice c + 1 into the other buffer (it held
-    // slice c - 1, read before the last barrier), issue token slice c + 2
-    // and weight slice c + 3, multiply slice c, barrier.  A weight slice has
-    // two iterations to arrive, a token slice two.
+    // Iteration c: issue token slice c + 2 and weight slice c + 3, multiply
+    // slice c, store weight slice c + 1 into the other buffer (it held slice
+    // c - 1, read before the last barrier; the stores follow every fragment
+    // read of this iteration), barrier.  A weight slice has about three
+    // iterations to arrive, a token slice two.
     int buf = 0;
     auto step = [&](int c, WStage& wstore, XStage& xcur, XStage& xnext, WStage& wnext) {
-      store_w(wstore, buf ^ 1);
-      __builtin_amdgcn_sched_barrier(0);
       load_x(xnext, c + 2);
-      __builtin_amdgcn_sched_barrier(0);
       load_w(wnext, c + 3);
-      __builtin_amdgcn_sched_barrier(0);
       mma(xcur, buf);
+      store_w(wstore, buf ^ 1);
       __builtin_amdgcn_sched_barrier(0);
       __syncthreads();
       buf ^= 1;
