@@ -23,6 +23,10 @@ struct Plan {
   int32_t n_tiles_routed;   // tiles of routed experts
   int32_t n_tiles_shared;   // tiles of the fused shared expert
   int32_t active_experts;
+  // work counters of the dynamically scheduled prefill gate/up and down
+  // kernels (zeroed with the plan, taken with atomics by the kernels)
+  int32_t gate_up_next;
+  int32_t down_next;
 };
 
 // One tile of rows of a (virtual) expert: rows [row0, row0 + rows) of the

@@ -715,7 +715,14 @@ __global__ __launch_bounds__(256, 1) void k_gate_up_packed(ExpertArgs a) {
 // wave w takes d0 + 64 w .. + 63 as two 32-row blocks.  The fused shared
 // expert has one k segment (one packed matrix) per shared expert.  With a k
 // split (down_split) the items are split as in k_down_tiled, and each split
-// writes fp32 partials.
+// writes fp32 partials.  With shared experts the items are handed out in
+// order by a work counter (ItemQueue): the shared tiles (full, 128 rows)
+// come after the routed ones (often a few rows), so a static split left the
+// XCDs with routed parts idle early (DeepSeek-V2-Lite prefill T = 4096 on
+// MI355X: 158 -> 135 us).  Routed-only layers keep the static split (the
+// fine-grained T = 8192 layer: 66.5 us static, 69.5 with the counter), and
+// so does the gate/up kernel, where the counter cost more in L2 reuse than
+// it gained (206 -> 215 us on the DeepSeek-V2-Lite layer).
 struct DownPackedProv {
   const u16* wd;     // packed [D][I] of the expert, or the shared experts' first [D][Is]
   const u16* h;      // rows of h for this tile, row stride hs
@@ -742,10 +749,17 @@ __global__ __launch_bounds__(256, 1) void k_down_packed(ExpertArgs a) {
   const int nb_all = (a.D + DB - 1) / DB;
   const long items = long(ntr + nts) * nb_all;
   const int ks = down_split(items, a.down_slots);
-  for (XcdRange it = xcd_range(items * ks); it.next < it.end; it.next += it.step) {
+  // shared tiles present: the work counter; otherwise the static split
+  const bool dyn = nts > 0;
+  const XcdRange xr = xcd_range(items * ks);
+  __shared__ int qslot[2];
+  ItemQueue q(const_cast<int32_t*>(&a.plan->down_next), qslot);
+  for (long item = dyn ? long(blockIdx.x) : xr.next; item < (dyn ? items * ks : xr.end);
+       item = dyn ? q.next() : item + xr.step) {
+    if (dyn) q.claim();
     int ti, nb;
-    const long wi = it.next / ks;
-    const int split = int(it.next - wi * ks);
+    const long wi = item / ks;
+    const int split = int(item - wi * ks);
     down_item(wi, ntr, nts, nb_all, ti, nb);
     const bool shared = ti >= ntr;
     if (!shared) packed_routed_item(a, wi, nb_all, ti, nb);
@@ -876,8 +890,13 @@ struct EsGateUpProv {
   __device__ const u16* xbase() const { return xt; }
 };
 
-// Items: (tile, block of 64 intermediate rows), tile-major, so that the
-// items of one tile (its tokens) share an XCD's L2.  Weight blocks 0, 1 are
+// Items: (tile, block of 64 intermediate rows), tile-major, handed out in
+// order by a work counter (ItemQueue).  A static split gives each XCD one
+// expert's tile, and tiles differ in height (a 290-row tile puts three
+// 32-token blocks on some waves, a 256-row one two), so the XCDs with the
+// tallest tiles finished last (Mixtral-shaped T = 2048 on MI355X: 551 -> 515
+// us with the counter, 550 with per-XCD counters that steal once their
+// part is done).  Weight blocks 0, 1 are
 // gate rows 64 nb .. 64 nb + 63, blocks 2, 3 the same up rows: a lane holds
 // gate and up of the same element, and SwiGLU is applied in registers.  h is
 // written in the packed layout of the down product's token operand.
@@ -889,8 +908,11 @@ __global__ __launch_bounds__(256, 1) void k_gate_up_es(ExpertArgs a) {
   const int nbk = a.I / 64;
   const int C = a.D / kPK, CI = a.I / kPK;
   const long total = long(ntr) * nbk;
-  for (XcdRange it = xcd_range(total); it.next < it.end; it.next += it.step) {
-    const int t = int(it.next / nbk), nb = int(it.next - long(t) * nbk);
+  __shared__ int qslot[2];
+  ItemQueue q(const_cast<int32_t*>(&a.plan->gate_up_next), qslot);
+  for (long item = blockIdx.x; item < total; item = q.next()) {
+    q.claim();
+    const int t = int(item / nbk), nb = int(item - long(t) * nbk);
     const Tile tl = ld_tile(a.tiles + t);
     EsGateUpProv pv;
     pv.C = C;

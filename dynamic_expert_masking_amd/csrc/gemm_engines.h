@@ -327,4 +327,32 @@ __device__ __forceinline__ XcdRange xcd_range(long total) {
   return r;
 }
 
+// Dynamic item order for persistent kernels whose items differ in length
+// (tiles of different heights, shared and routed items): a workgroup starts
+// with item blockIdx.x, then takes the next value of a device counter (zeroed
+// before the launch by the kernel that writes the plan) plus the grid size.
+// Items are handed out in order over the whole chip, so the items that run
+// at once are neighbours in the item order, as xcd_range's parts are, but on
+// every XCD.  Thread 0 claims the following item when an item starts, so the
+// atomic's latency overlaps the item's first loads, and hands it to the other
+// threads through LDS when the item ends.  slot is a __shared__ int[2]: the
+// two alternate, so one barrier per item suffices.
+struct ItemQueue {
+  int* counter;
+  int* slot;
+  int par = 0;
+  int nxt = 0;
+  __device__ ItemQueue(int* c, int* s) : counter(c), slot(s) {}
+  __device__ void claim() {
+    if (threadIdx.x == 0) nxt = atomicAdd(counter, 1) + int(gridDim.x);
+  }
+  __device__ long next() {
+    if (threadIdx.x == 0) slot[par] = nxt;
+    __syncthreads();
+    const long v = slot[par];
+    par ^= 1;
+    return v;
+  }
+};
+
 }  // namespace beam

@@ -254,13 +254,14 @@ __device__ __forceinline__ void prefill_accumulate(const Prov& pv, PrefillSmem<B
 // kEsTileRows rows, so each weight block of an expert is read from HBM once
 // per tile instead of once per 128-token tile.  The roles of the packed
 // engine above are swapped: the weight slice (16 KB per 64-wide k slice)
-// goes through two LDS buffers and is shared by the 4 waves; each wave takes
-// the tile's 32-token blocks w, w + 4, w + 8 and loads them straight into
-// MFMA operand registers from a packed copy of the tokens (the same block
-// layout as the packed weights: block (tb, kb) of a tile at element
-// (tb * C + kb) * 2048, lane l's 16 bytes of k-step s at s * 512 + l * 8).
-// Weight and token slices are both held in three rotating register stages;
-// one barrier per slice.
+// goes through a ring of three LDS buffers and is shared by the 4 waves;
+// each wave takes the tile's 32-token blocks w, w + 4, w + 8 and loads them
+// straight into MFMA operand registers from a packed copy of the tokens (the
+// same block layout as the packed weights: block (tb, kb) of a tile at
+// element (tb * C + kb) * 2048, lane l's 16 bytes of k-step s at s * 512 +
+// l * 8).  Weight and token slices are both held in three rotating register
+// stages; one barrier per slice, after its third k-step, so that the
+// fragments of the next slice's first k-step are read during its fourth.
 // ---------------------------------------------------------------------------
 
 constexpr int kEsTokBlocks = kEsTileRows / 32;   // tokens of one tile: 12 blocks of 32
@@ -268,7 +269,7 @@ constexpr int kEsWaveBlocks = kEsTokBlocks / 4;   // token blocks per wave
 constexpr int kEsWBlocks = 4;               // 32-row weight blocks per workgroup
 
 struct EsSmem {
-  u16 w[2][kEsWBlocks * kPackBlock];   // two weight slice buffers
+  u16 w[3][kEsWBlocks * kPackBlock];   // three weight slice buffers (a ring)
 };
 
 // Provider interface (per item):
@@ -328,46 +329,48 @@ __device__ __forceinline__ void es_accumulate(const Prov& pv, EsSmem& sm,
         for (int s = 0; s < 4; ++s) st.v[j][s] = ld16_at(xb, off + 512 * s);
       }
     };
-    // The four k-steps of the slice in LDS buffer buf, in groups of (weight
-    // block b, k-step s): the group's NJ MFMAs, then one global load of the
-    // step's token and weight slices (the first 4 NJ + 4 groups), one store
-    // of the next weight slice into LDS (the last four groups, after every
-    // fragment read), and the read of block b's fragment of k-step s + 1
-    // into the register the MFMAs just consumed.  A fragment read then has
-    // three groups of MFMAs to arrive, and the wave issues its loads and
-    // stores while the matrix unit works through queued MFMAs instead of
-    // ahead of them (Mixtral-shaped T = 2048 on MI355X: gate/up 583 -> 551
-    // us with the loads threaded, 572 with the stores too; down 283 -> 273).
-    // The grouping is pinned with scheduling-group barriers: left alone, the
-    // compiler sinks every read to just before its MFMAs.
-    auto mma = [&](const XStage& xs, int buf) {
-      const u16* wl = &sm.w[buf][8 * lane];
-      u32x4 wf[kEsWBlocks];
+    WStage ws[3];
+    XStage xs[3];
+    u32x4 wf[kEsWBlocks];   // block b's fragment of the next k-step to multiply
+    auto wl = [&](int buf) { return &sm.w[buf][8 * lane]; };
+    // K-steps S0 .. S1 - 1 of slice c (LDS buffer buf) in groups of (weight
+    // block b, k-step s): the group's NJ MFMAs, then VM of the step's global
+    // loads (while any remain, k-steps 0-2), one store of the next weight
+    // slice into LDS (the groups of k-step 2), and the read of block b's
+    // fragment of the following k-step -- k-step 0 of slice c + 1 (buffer
+    // nbuf) after k-step 3 -- into the register the MFMAs just consumed.
+    // A fragment read then has three groups of MFMAs to arrive, and the wave
+    // issues its loads and stores while the matrix unit works through queued
+    // MFMAs instead of ahead of them; the grouping is pinned with
+    // scheduling-group barriers (left alone, the compiler sinks every read
+    // to just before its MFMAs).  Mixtral-shaped T = 2048 on MI355X, gate/up
+    // / down: 583 / 283 us with loads, stores and reads in blocks, 551 / 265
+    // with the loads threaded, 572 / 273 with the stores too (two buffers,
+    // stores after the last read), 557 / 265 with this ring of three.
+    auto ksteps = [&](const XStage& xs, int buf, int nbuf, auto s0c, auto s1c) {
+      constexpr int S0 = decltype(s0c)::value, S1 = decltype(s1c)::value;
+      constexpr int NL = 4 * NJ + 4;
+      constexpr int VM = (NL + 11) / 12;
 #pragma unroll
-      for (int b = 0; b < kEsWBlocks; ++b) wf[b] = *reinterpret_cast<const u32x4*>(wl + b * kPackBlock);
-      __builtin_amdgcn_sched_group_barrier(0x100, kEsWBlocks, 0);   // LDS reads
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
+      for (int s = S0; s < S1; ++s) {
 #pragma unroll
         for (int b = 0; b < kEsWBlocks; ++b) {
 #pragma unroll
           for (int j = 0; j < NJ; ++j) acc[b][j] = mfma32_bf16(wf[b], xs.v[j][s], acc[b][j]);
           if (NJ > 0) __builtin_amdgcn_sched_group_barrier(0x008, NJ, 0);   // MFMAs
-          if (4 * s + b < 4 * NJ + 4) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // global load
-          if (s == 3) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // LDS store
-          if (s < 3) {
-            wf[b] = *reinterpret_cast<const u32x4*>(wl + b * kPackBlock + 512 * (s + 1));
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
-          }
+          if (s < 3 && VM * (4 * s + b) < NL) __builtin_amdgcn_sched_group_barrier(0x020, VM, 0);
+          if (s == 2) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // LDS store
+          wf[b] = *reinterpret_cast<const u32x4*>(s < 3 ? wl(buf) + b * kPackBlock + 512 * (s + 1)
+                                                        : wl(nbuf) + b * kPackBlock);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
         }
       }
     };
-    WStage ws[3];
-    XStage xs[3];
-    // Stage k % 3 holds slice k.  Loads complete in issue order, so each
-    // iteration issues its token slice before its weight slice: waiting for
-    // a token slice then never waits for a weight slice issued later.  The
-    // prologue issues x0, w0, w1, x1, w2, as the loop would have.
+    // Stage k % 3 holds slice k, LDS buffer k % 3 too.  Loads complete in
+    // issue order, so each iteration issues its token slice before its
+    // weight slice: waiting for a token slice then never waits for a weight
+    // slice issued later.  The prologue issues x0, w0, w1, x1, w2, as the
+    // loop would have.
     load_x(xs[0], 0);
     __builtin_amdgcn_sched_barrier(0);
     load_w(ws[0], 0);
@@ -381,29 +384,35 @@ __device__ __forceinline__ void es_accumulate(const Prov& pv, EsSmem& sm,
     store_w(ws[0], 0);
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
+#pragma unroll
+    for (int b = 0; b < kEsWBlocks; ++b) wf[b] = *reinterpret_cast<const u32x4*>(wl(0) + b * kPackBlock);
     // Iteration c: issue token slice c + 2 and weight slice c + 3, multiply
-    // slice c, store weight slice c + 1 into the other buffer (it held slice
-    // c - 1, read before the last barrier; the stores follow every fragment
-    // read of this iteration), barrier.  A weight slice has about three
-    // iterations to arrive, a token slice two.
-    int buf = 0;
-    auto step = [&](int c, WStage& wstore, XStage& xcur, XStage& xnext, WStage& wnext) {
+    // k-steps 0-2 of slice c while storing weight slice c + 1 into its
+    // buffer (that of slice c - 2, last read before the previous barrier),
+    // barrier, then k-step 3 while reading k-step 0 of slice c + 1.  A weight
+    // slice has two iterations to arrive, a token slice two.
+    auto step = [&](int c, WStage& wstore, XStage& xcur, XStage& xnext, WStage& wnext, int buf,
+                    int nbuf) {
       load_x(xnext, c + 2);
       load_w(wnext, c + 3);
-      mma(xcur, buf);
-      store_w(wstore, buf ^ 1);
+      ksteps(xcur, buf, nbuf, std::integral_constant<int, 0>{}, std::integral_constant<int, 3>{});
+      store_w(wstore, nbuf);
       __builtin_amdgcn_sched_barrier(0);
       __syncthreads();
-      buf ^= 1;
+      ksteps(xcur, buf, nbuf, std::integral_constant<int, 3>{}, std::integral_constant<int, 4>{});
+      __builtin_amdgcn_sched_barrier(0);
     };
     int c = 0;
     for (; c + 3 <= C; c += 3) {
-      step(c, ws[1], xs[0], xs[2], ws[0]);
-      step(c + 1, ws[2], xs[1], xs[0], ws[1]);
-      step(c + 2, ws[0], xs[2], xs[1], ws[2]);
+      step(c, ws[1], xs[0], xs[2], ws[0], 0, 1);
+      step(c + 1, ws[2], xs[1], xs[0], ws[1], 1, 2);
+      step(c + 2, ws[0], xs[2], xs[1], ws[2], 2, 0);
     }
-    if (c < C) step(c, ws[1], xs[0], xs[2], ws[0]);
-    if (c + 1 < C) step(c + 1, ws[2], xs[1], xs[0], ws[1]);
+    if (c < C) step(c, ws[1], xs[0], xs[2], ws[0], 0, 1);
+    if (c + 1 < C) step(c + 1, ws[2], xs[1], xs[0], ws[1], 1, 2);
+    // the last fragment reads (of the slice past the end) are discarded;
+    // the next item's stores wait at its first barrier
+    __syncthreads();
   };
   tiled_dispatch<kEsWaveBlocks>(nj, [&](auto nj_const) { run(nj_const); });
 }

@@ -384,6 +384,8 @@ __device__ void build_plan(PlanSmem& sm, int T, int E, int tile_rows, int has_sh
     pl.n_tiles_routed = ntr;
     pl.n_tiles_shared = nts;
     pl.active_experts = sm.act;
+    pl.gate_up_next = 0;
+    pl.down_next = 0;
     *plan = pl;
   }
 }
