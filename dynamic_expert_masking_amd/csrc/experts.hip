@@ -926,10 +926,11 @@ __global__ __launch_bounds__(256, 1) void k_gate_up_es(ExpertArgs a) {
     u16* ht = a.hpk + size_t(t) * es_tile_elems(a.I);
 #pragma unroll
     for (int j = 0; j < kEsWaveBlocks; ++j) {
-      const int tb = wave + 4 * j;
+      const int tb = es_token_block(wave, j, nbt);
       if (tb >= nbt) continue;   // wave-uniform
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+      for (int b = 0; b < 2; ++b) {
+        if (j == 2 && !es_block_valid(wave, b, nbt)) continue;   // (up block b + 2: same parity)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const f32x16& g = acc[b][j];
@@ -944,6 +945,7 @@ __global__ __launch_bounds__(256, 1) void k_gate_up_es(ExpertArgs a) {
           *reinterpret_cast<ushort4*>(ht + (size_t(tb) * CI + nb) * kPackBlock + 512 * s2 + 8 * l2 +
                                       4 * (lane >> 5)) = hv;
         }
+      }
     }
   }
 }
@@ -980,16 +982,18 @@ __global__ __launch_bounds__(256, 1) void k_down_es(ExpertArgs a) {
     u16* ob = static_cast<u16*>(a.o);
 #pragma unroll
     for (int j = 0; j < kEsWaveBlocks; ++j) {
-      const int m = 32 * (wave + 4 * j) + (lane & 31);
+      const int m = 32 * es_token_block(wave, j, nbt) + (lane & 31);
       if (m >= tl.rows) continue;
 #pragma unroll
-      for (int b = 0; b < kEsWBlocks; ++b)
+      for (int b = 0; b < kEsWBlocks; ++b) {
+        if (j == 2 && !es_block_valid(wave, b, nbt)) continue;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int d = 128 * db + 32 * b + 8 * q + 4 * (lane >> 5);
           const f32x16& v = acc[b][j];
           st4_bf16(ob, size_t(tl.row0 + m) * a.D + d, v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
         }
+      }
     }
   }
 }

@@ -278,8 +278,27 @@ struct EsSmem {
 //                                  its row of packed blocks
 //   const u16* xbase()             packed tokens of the tile (block row 0)
 // On return acc[bb][j][i] = C[n = 32 bb + 8 (i / 4) + 4 (lane / 32) + i % 4]
-//                            [m = 32 (wave + 4 j) + lane % 32]
-// for the token blocks wave + 4 j < nbt (the others are left at zero).
+//                            [m = 32 tb_j + lane % 32]
+// for the token blocks tb_j = es_token_block(wave, j, nbt) < nbt (the others
+// are left at zero); for j = 2 only the weight blocks bb that
+// es_block_valid(wave, bb, nbt) accepts.
+//
+// Token blocks of a wave: w, w + 4, w + 8, except in tiles of 9 or 10
+// blocks.  There the third block would fall to one or two waves, which
+// would then take half as long again as the others at every barrier;
+// instead blocks 8 and 9 are split by weight-block parity: waves 0 and 1
+// take block 8, waves 2 and 3 block 9, each with the weight blocks of its
+// own parity (w % 2 and w % 2 + 2 -- a gate block and the up block of the
+// same rows).  The busiest wave then issues 40 MFMAs per slice instead of
+// 48.
+__device__ __forceinline__ bool es_split_tile(int nbt) { return nbt == 9 || nbt == 10; }
+__device__ __forceinline__ int es_token_block(int wave, int j, int nbt) {
+  if (j < 2 || !es_split_tile(nbt)) return wave + 4 * j;
+  return 8 + wave / 2;
+}
+__device__ __forceinline__ bool es_block_valid(int wave, int bb, int nbt) {
+  return !es_split_tile(nbt) || ((bb ^ wave) & 1) == 0;
+}
 template <class Prov>
 __device__ __forceinline__ void es_accumulate(const Prov& pv, EsSmem& sm,
                                               f32x16 (&acc)[kEsWBlocks][kEsWaveBlocks], int nbt) {
@@ -298,8 +317,11 @@ __device__ __forceinline__ void es_accumulate(const Prov& pv, EsSmem& sm,
   const int wbb = tid >> 6;
   const u16* wb = pv.wbase(wbb) + 8 * lane;
   const u16* xb = pv.xbase() + 8 * lane;
-  // this wave's token blocks (wave-uniform count)
-  const int nj = min(kEsWaveBlocks, max(0, (nbt - wave + 3) / 4));
+  // this wave's token blocks w + 4 j (wave-uniform count), and the block
+  // it shares in a tile of 9 or 10 blocks (-1: none)
+  const bool split = es_split_tile(nbt);
+  const int nj = split ? 2 : min(kEsWaveBlocks, max(0, (nbt - wave + 3) / 4));
+  const int xblk = split && es_token_block(wave, 2, nbt) < nbt ? es_token_block(wave, 2, nbt) : -1;
 
   struct WStage {
     u32x4 v[4];
@@ -318,13 +340,18 @@ __device__ __forceinline__ void es_accumulate(const Prov& pv, EsSmem& sm,
       *reinterpret_cast<u32x4*>(&sm.w[buf][wbb * kPackBlock + 512 * s + 8 * lane]) = st.v[s];
   };
 
-  auto run = [&](auto nj_const) {
+  // NJ own token blocks; XP = 0, or 1 + p: block xblk too, with the weight
+  // blocks of parity p
+  auto run = [&](auto nj_const, auto xp_const) {
     constexpr int NJ = decltype(nj_const)::value;
+    constexpr int XP = decltype(xp_const)::value;
+    constexpr int NT = NJ + (XP ? 1 : 0);   // token blocks loaded
     auto load_x = [&](XStage& st, int c) {
       const int cc = min(c, C - 1);
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const uint32_t off = uint32_t((wave + 4 * j) * C + cc) * kPackBlock;
+      for (int j = 0; j < NT; ++j) {
+        const int tb = j < NJ ? wave + 4 * j : xblk;
+        const uint32_t off = uint32_t(tb * C + cc) * kPackBlock;
 #pragma unroll
         for (int s = 0; s < 4; ++s) st.v[j][s] = ld16_at(xb, off + 512 * s);
       }
@@ -349,7 +376,7 @@ __device__ __forceinline__ void es_accumulate(const Prov& pv, EsSmem& sm,
     // stores after the last read), 557 / 265 with this ring of three.
     auto ksteps = [&](const XStage& xs, int buf, int nbuf, auto s0c, auto s1c) {
       constexpr int S0 = decltype(s0c)::value, S1 = decltype(s1c)::value;
-      constexpr int NL = 4 * NJ + 4;
+      constexpr int NL = 4 * NT + 4;
       constexpr int VM = (NL + 11) / 12;
 #pragma unroll
       for (int s = S0; s < S1; ++s) {
@@ -357,7 +384,10 @@ __device__ __forceinline__ void es_accumulate(const Prov& pv, EsSmem& sm,
         for (int b = 0; b < kEsWBlocks; ++b) {
 #pragma unroll
           for (int j = 0; j < NJ; ++j) acc[b][j] = mfma32_bf16(wf[b], xs.v[j][s], acc[b][j]);
+          const bool X = XP != 0 && (b & 1) == XP - 1;   // a constant after unrolling
+          if (X) acc[b][NJ] = mfma32_bf16(wf[b], xs.v[NJ][s], acc[b][NJ]);
           if (NJ > 0) __builtin_amdgcn_sched_group_barrier(0x008, NJ, 0);   // MFMAs
+          if (X) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           if (s < 3 && VM * (4 * s + b) < NL) __builtin_amdgcn_sched_group_barrier(0x020, VM, 0);
           if (s == 2) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // LDS store
           wf[b] = *reinterpret_cast<const u32x4*>(s < 3 ? wl(buf) + b * kPackBlock + 512 * (s + 1)
@@ -414,7 +444,13 @@ __device__ __forceinline__ void es_accumulate(const Prov& pv, EsSmem& sm,
     // the next item's stores wait at its first barrier
     __syncthreads();
   };
-  tiled_dispatch<kEsWaveBlocks>(nj, [&](auto nj_const) { run(nj_const); });
+  using I0 = std::integral_constant<int, 0>;
+  if (xblk >= 0) {
+    if (wave & 1) run(std::integral_constant<int, 2>{}, std::integral_constant<int, 2>{});
+    else run(std::integral_constant<int, 2>{}, std::integral_constant<int, 1>{});
+  } else {
+    tiled_dispatch<kEsWaveBlocks>(nj, [&](auto nj_const) { run(nj_const, I0{}); });
+  }
 }
 
 }  // namespace beam
