@@ -303,6 +303,124 @@ __device__ __forceinline__ void tiled_accumulate(const Prov& pv, TiledSmem<BN, B
   tiled_dispatch<JM>(nj, run);
 }
 
+// The tiled engine with both operands double-buffered in LDS, for tiles
+// whose MFMAs per slice are few (the router's 64 x 128 tiles: 8 per wave):
+// tiled_accumulate's slice loop (store, barrier, load, multiply, barrier)
+// leaves each slice's load latency and LDS round trip exposed, and took
+// 27 us for the fine-grained T = 8192 router even with every load an L2 hit.
+// Here iteration c issues the loads of slice c + 2, multiplies slice c out
+// of buffer c % 2 (all of its fragment reads issued first), stores slice
+// c + 1 (loaded during iteration c - 1) into the other buffer, whose slice
+// c - 1 was read before the last barrier, and ends with the one barrier
+// (that router on MI355X: 34.2 -> 30.0 us).  Full k range only; same
+// provider and accumulator layout.
+template <int BN, int BM>
+struct TiledSmem2 {
+  u16 w[2][BN * kTLD];
+  u16 x[2][BM * kTLD];
+};
+
+template <int BN, int BM, class Prov>
+__device__ __forceinline__ void tiled_accumulate_db(const Prov& pv, TiledSmem2<BN, BM>& sm,
+                                                    f32x16 (&acc)[BN / 64][BM / 64], int rows_valid) {
+  constexpr int JN = BN / 64, JM = BM / 64;
+  constexpr int WL = BN / 32;
+  constexpr int XL = BM / 32;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave & 1, wm = wave >> 1;
+#pragma unroll
+  for (int a = 0; a < JN; ++a)
+#pragma unroll
+    for (int b = 0; b < JM; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
+  const int cps = pv.seg_chunks();
+  const int C = pv.nseg() * cps;
+  const int lrow = tid >> 3;
+  const int lcol = (tid & 7) * 8;
+  uint32_t wo[WL], xo[XL];
+#pragma unroll
+  for (int i = 0; i < WL; ++i) wo[i] = pv.woff(lrow + 32 * i) + lcol;
+#pragma unroll
+  for (int i = 0; i < XL; ++i) xo[i] = pv.xoff(lrow + 32 * i) + lcol;
+  struct Stage {
+    u32x4 w[WL];
+    u32x4 x[XL];
+  };
+  // past the end: offset 0 of the last segment's bases (masked, no branch)
+  auto load = [&](Stage& st, int c) {
+    const uint32_t msk = c < C ? ~0u : 0u;
+    const int cc = max(min(c, C - 1), 0);
+    const int seg = cc / cps;
+    const uint32_t km = uint32_t(cc - seg * cps) * kTBK;
+    const u16* xb = pv.xbase(seg);
+#pragma unroll
+    for (int i = 0; i < WL; ++i) st.w[i] = ld16_at(pv.wbase(i, seg), (wo[i] + km) & msk);
+#pragma unroll
+    for (int i = 0; i < XL; ++i) st.x[i] = ld16_at(xb, (xo[i] + km) & msk);
+  };
+  auto store = [&](const Stage& st, int buf) {
+#pragma unroll
+    for (int i = 0; i < WL; ++i)
+      *reinterpret_cast<u32x4*>(&sm.w[buf][(lrow + 32 * i) * kTLD + lcol]) = st.w[i];
+#pragma unroll
+    for (int i = 0; i < XL; ++i)
+      *reinterpret_cast<u32x4*>(&sm.x[buf][(lrow + 32 * i) * kTLD + lcol]) = st.x[i];
+  };
+  const int fr = lane & 31;
+  const int fk = (lane >> 5) * 8;
+  auto run = [&](auto nj_const) {
+    constexpr int NJ = decltype(nj_const)::value;
+    auto compute = [&](int buf) {
+      u32x4 wf[4][JN], xf[4][NJ > 0 ? NJ : 1];
+#pragma unroll
+      for (int ks = 0; ks < kTBK / 16; ++ks) {
+#pragma unroll
+        for (int jn = 0; jn < JN; ++jn)
+          wf[ks][jn] = *reinterpret_cast<const u32x4*>(
+              &sm.w[buf][(wn * (BN / 2) + jn * 32 + fr) * kTLD + ks * 16 + fk]);
+#pragma unroll
+        for (int jm = 0; jm < NJ; ++jm)
+          xf[ks][jm] = *reinterpret_cast<const u32x4*>(
+              &sm.x[buf][(wm * (BM / 2) + jm * 32 + fr) * kTLD + ks * 16 + fk]);
+      }
+#pragma unroll
+      for (int ks = 0; ks < kTBK / 16; ++ks)
+#pragma unroll
+        for (int jm = 0; jm < NJ; ++jm)
+#pragma unroll
+          for (int jn = 0; jn < JN; ++jn) acc[jn][jm] = mfma32_bf16(wf[ks][jn], xf[ks][jm], acc[jn][jm]);
+    };
+    Stage st[2];
+    load(st[0], 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load(st[1], 1);
+    __builtin_amdgcn_sched_barrier(0);
+    store(st[0], 0);
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    auto step = [&](int c, Stage& nxt_load, const Stage& to_store, int buf) {
+      load(nxt_load, c + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (NJ > 0) compute(buf);
+      __builtin_amdgcn_sched_barrier(0);
+      store(to_store, buf ^ 1);
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+    };
+    int c = 0;
+    for (; c + 2 <= C; c += 2) {
+      step(c, st[0], st[1], 0);
+      step(c + 1, st[1], st[0], 1);
+    }
+    if (c < C) step(c, st[0], st[1], 0);
+  };
+  const int nj = min(JM, max(0, (rows_valid - wm * (BM / 2) + 31) / 32));
+  tiled_dispatch<JM>(nj, run);
+}
+
 // Persistent, XCD-aware work split: workgroups are dispatched round-robin over
 // the 8 XCDs (b % 8), so the item space is cut into 8 contiguous parts and the
 // workgroups of one XCD stride through its part.  Items that share operands

@@ -116,9 +116,12 @@ __global__ __launch_bounds__(256) void k_router_skinny(RouterArgs a) {
 }
 
 // Tiled router (large batches with many experts): tiles of 64 rows of one
-// router matrix x 128 tokens.  At T = 8192 and 212 experts that is 512 items,
+// router matrix x 128 tokens, both operands double-buffered in LDS
+// (tiled_accumulate_db).  At T = 8192 and 212 experts that is 512 items,
 // two workgroups per CU, which hide each other's load latency (256-token
-// tiles, one workgroup per CU: 39.3 -> 35.7 us on MI355X).
+// tiles, one workgroup per CU: 39.3 -> 35.7 us on MI355X).  Tiles of 64 x
+// 64 (four workgroups per CU) or 128 x 128 and 256 x 64 (fewer operand
+// re-reads) were slower: 41.6, 36.2 and 40.6 us against 34.1.
 constexpr int kRouterBN = 64, kRouterBM = 128;
 
 // A tile covers rows [jb, jb + 64) of one of the two weight matrices
@@ -142,7 +145,7 @@ struct RouterTiledProv {
 
 // Persistent: items are (token tile, matrix, 64-row block).
 __global__ __launch_bounds__(256, 2) void k_router_tiled(RouterArgs a) {
-  __shared__ TiledSmem<kRouterBN, kRouterBM> sm;
+  __shared__ TiledSmem2<kRouterBN, kRouterBM> sm;
   constexpr int JN = kRouterBN / 64, JM = kRouterBM / 64;
   const int nrb = (a.E + kRouterBN - 1) / kRouterBN;   // blocks per matrix
   const long total = long((a.T + kRouterBM - 1) / kRouterBM) * 2 * nrb;
@@ -153,7 +156,7 @@ __global__ __launch_bounds__(256, 2) void k_router_tiled(RouterArgs a) {
     const int t0 = int(it.next / (2 * nrb)) * kRouterBM;
     RouterTiledProv pv{&a, rb / nrb, (rb % nrb) * kRouterBN, t0};
     f32x16 acc[JN][JM];
-    tiled_accumulate<kRouterBN, kRouterBM>(pv, sm, acc, a.T - t0);
+    tiled_accumulate_db<kRouterBN, kRouterBM>(pv, sm, acc, a.T - t0);
 #pragma unroll
     for (int jn = 0; jn < JN; ++jn)
 #pragma unroll
