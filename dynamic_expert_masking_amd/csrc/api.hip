@@ -32,6 +32,12 @@ int expert_tile_rows(const beam_moe_layer& L, int32_t T) {
   return 256;
 }
 
+bool es_shared_experts(const beam_moe_layer& L, int32_t T) {
+  return L.wsp_gate && L.n_shared > 0 && L.dtype == BEAM_BF16 && L.expert_format == BEAM_WEIGHTS_DTYPE &&
+         T >= kEsSharedMinT && L.D % 128 == 0 && L.I_shared % 64 == 0 &&
+         expert_tile_rows(L, T) == 128;
+}
+
 // Rows of router partial logits ([KS][T] of them) that the workspace holds
 // for a batch of T tokens: an upper bound on KS(T') * T' over every T' <= T,
 // so that a workspace sized for T_max serves every smaller batch (KS rises as
@@ -84,11 +90,13 @@ WsLayout workspace_layout(const beam_moe_layer& L, int32_t T) {
                           expert_tile_rows(L, T) > 64;
   w.o_part_bytes = split_down ? size_t(kMaxDownSplit) * (TK + (IS ? T : 0)) * L.D * 4 : 0;
   w.o_part = take(w.o_part_bytes);
-  // expert-stationary prefill: packed tokens and h of every tile
+  // expert-stationary prefill: packed tokens and h of every tile (routed
+  // tiles without shared experts; the shared experts' tiles with them)
   const bool es = expert_tile_rows(L, T) == kEsTileRows;
   const size_t es_tiles = es ? size_t((TK + kEsTileRows - 1) / kEsTileRows + std::min<size_t>(L.E, TK)) : 0;
-  w.es_x = take(es_tiles * kEsTileRows * L.D * 2);
-  w.es_h = take(es_tiles * kEsTileRows * L.I * 2);
+  const size_t ess_tiles = es_shared_experts(L, T) ? (size_t(T) + kEsTileRows - 1) / kEsTileRows : 0;
+  w.es_x = take(std::max(es_tiles, ess_tiles) * kEsTileRows * L.D * 2);
+  w.es_h = take(std::max(es_tiles * L.I, ess_tiles * IS) * kEsTileRows * 2);
   w.zsel = take(TK * 4);
   w.dz = take(TK * 4);
   w.lreg_tok = take(size_t(T) * 4);

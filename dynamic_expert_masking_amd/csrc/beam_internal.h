@@ -43,6 +43,10 @@ struct Tile {
 // expert at least kEsMinPerExpert top-K candidates on average.
 constexpr int kEsTileRows = 384;
 constexpr int kEsMinPerExpert = 256;
+// Packed layers with shared experts: from this many tokens the fused shared
+// expert (every token) runs on the expert-stationary kernels, on tiles of
+// kEsTileRows consecutive tokens, and the routed tiles on the 128-row ones.
+constexpr int kEsSharedMinT = 1024;
 
 struct WsLayout {
   size_t plan, logits, idx, gates, mask, counts, rank, block_counts, expert_off, tiles, perm_token,
@@ -58,6 +62,9 @@ int router_ksplit(const beam_moe_layer& L, int32_t T);
 long router_logit_rows(const beam_moe_layer& L, int32_t T);
 // Row-tile height of the expert kernels (multiple of 16).
 int expert_tile_rows(const beam_moe_layer& L, int32_t T);
+// True when the shared experts of a batch run on the expert-stationary
+// kernels (see kEsSharedMinT); the routed down product then never splits k.
+bool es_shared_experts(const beam_moe_layer& L, int32_t T);
 WsLayout workspace_layout(const beam_moe_layer& L, int32_t T);
 
 struct Ptrs {
@@ -83,8 +90,9 @@ struct Ptrs {
   // [kMaxDownSplit][T K][D], then the shared ones [kMaxDownSplit][T][D]
   float* o_part;
   // expert-stationary prefill: packed tokens and packed h of every tile
+  // (routed tiles, or the shared experts' tiles of consecutive tokens)
   void* es_x;   // [tiles][12 x D/64 blocks of 32 x 64] bf16
-  void* es_h;   // [tiles][12 x I/64 blocks]
+  void* es_h;   // [tiles][12 x I/64 blocks] (shared: S Is / 64 blocks)
   // mask-router backward
   float* zsel;       // [T][K] mask logit of each candidate
   float* dz;         // [P] dL/dz of each pair (pair order)

@@ -65,6 +65,8 @@ struct ExpertArgs {
   float* op_sh;
   long op_stride, op_sh_stride;   // elements per split
   int down_slots;                 // resident workgroups of the down kernel (0: never split)
+  int es_ntiles;                  // > 0: the expert-stationary kernels take the shared
+                                  // experts, tiles of kEsTileRows consecutive tokens
 };
 
 // Order of the shared items.  Every shared tile reads the same weights, so
@@ -660,19 +662,19 @@ struct GateUpPackedProv {
   }
 };
 
-__global__ __launch_bounds__(256, 1) void k_gate_up_packed(ExpertArgs a) {
-  __shared__ PrefillSmem<128> sm;
-  constexpr int BM = 128, JM = BM / 32, IB = 128;   // IB: intermediate rows per item
+constexpr int kPackedIB = 128;   // intermediate rows per packed gate/up item
+
+// One item of the packed gate/up kernel (item < ntr nbr + nts nbs).
+__device__ __forceinline__ void packed_gate_up_item(const ExpertArgs& a, PrefillSmem<128>& sm, long item,
+                                                    int ntr, int nts, int nbr, int nbs) {
+  constexpr int BM = 128, JM = BM / 32, IB = kPackedIB;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int ntr = ld_const(&a.plan->n_tiles_routed), nts = ld_const(&a.plan->n_tiles_shared);
-  const int nbr = (a.I + IB - 1) / IB, nbs = a.S > 0 ? (a.S * a.Is + IB - 1) / IB : 1;
-  const long total = long(ntr) * nbr + long(nts) * nbs;
-  for (XcdRange it = xcd_range(total); it.next < it.end; it.next += it.step) {
+  {
     int ti, nb;
     bool shared;
-    work_item(it.next, ntr, nts, nbr, nbs, ti, nb, shared);
-    if (!shared) packed_routed_item(a, it.next, nbr, ti, nb);
+    work_item(item, ntr, nts, nbr, nbs, ti, nb, shared);
+    if (!shared) packed_routed_item(a, item, nbr, ti, nb);
     const Tile tl = ld_tile(a.tiles + ti);
     const int Iv = shared ? a.S * a.Is : a.I;
     GateUpPackedProv pv;
@@ -711,6 +713,16 @@ __global__ __launch_bounds__(256, 1) void k_gate_up_packed(ExpertArgs a) {
   }
 }
 
+__global__ __launch_bounds__(256, 1) void k_gate_up_packed(ExpertArgs a) {
+  __shared__ PrefillSmem<128> sm;
+  const int ntr = ld_const(&a.plan->n_tiles_routed), nts = ld_const(&a.plan->n_tiles_shared);
+  const int nbr = (a.I + kPackedIB - 1) / kPackedIB;
+  const int nbs = a.S > 0 ? (a.S * a.Is + kPackedIB - 1) / kPackedIB : 1;
+  const long total = long(ntr) * nbr + long(nts) * nbs;
+  for (XcdRange it = xcd_range(total); it.next < it.end; it.next += it.step)
+    packed_gate_up_item(a, sm, it.next, ntr, nts, nbr, nbs);
+}
+
 // Down: a workgroup's 256 weight rows are output features d0 .. d0 + 255;
 // wave w takes d0 + 64 w .. + 63 as two 32-row blocks.  The fused shared
 // expert has one k segment (one packed matrix) per shared expert.  With a k
@@ -740,23 +752,15 @@ struct DownPackedProv {
   __device__ uint32_t xoff(int R) const { return uint32_t(R < rows ? R : 0) * uint32_t(hs); }
 };
 
-__global__ __launch_bounds__(256, 1) void k_down_packed(ExpertArgs a) {
-  __shared__ PrefillSmem<128> sm;
-  constexpr int BM = 128, JM = BM / 32, DB = 256;   // output features per item
+constexpr int kPackedDB = 256;   // output features per packed down item
+
+// One item of the packed down kernel (item < (ntr + nts) nb_all ks).
+__device__ __forceinline__ void packed_down_item(const ExpertArgs& a, PrefillSmem<128>& sm, long item,
+                                                 int ntr, int nts, int nb_all, int ks) {
+  constexpr int BM = 128, JM = BM / 32, DB = kPackedDB;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int ntr = ld_const(&a.plan->n_tiles_routed), nts = ld_const(&a.plan->n_tiles_shared);
-  const int nb_all = (a.D + DB - 1) / DB;
-  const long items = long(ntr + nts) * nb_all;
-  const int ks = down_split(items, a.down_slots);
-  // shared tiles present: the work counter; otherwise the static split
-  const bool dyn = nts > 0;
-  const XcdRange xr = xcd_range(items * ks);
-  __shared__ int qslot[2];
-  ItemQueue q(const_cast<int32_t*>(&a.plan->down_next), qslot);
-  for (long item = dyn ? long(blockIdx.x) : xr.next; item < (dyn ? items * ks : xr.end);
-       item = dyn ? q.next() : item + xr.step) {
-    if (dyn) q.claim();
+  {
     int ti, nb;
     const long wi = item / ks;
     const int split = int(item - wi * ks);
@@ -812,6 +816,24 @@ __global__ __launch_bounds__(256, 1) void k_down_packed(ExpertArgs a) {
   }
 }
 
+__global__ __launch_bounds__(256, 1) void k_down_packed(ExpertArgs a) {
+  __shared__ PrefillSmem<128> sm;
+  const int ntr = ld_const(&a.plan->n_tiles_routed), nts = ld_const(&a.plan->n_tiles_shared);
+  const int nb_all = (a.D + kPackedDB - 1) / kPackedDB;
+  const long items = long(ntr + nts) * nb_all;
+  const int ks = down_split(items, a.down_slots);
+  // shared tiles present: the work counter; otherwise the static split
+  const bool dyn = nts > 0;
+  const XcdRange xr = xcd_range(items * ks);
+  __shared__ int qslot[2];
+  ItemQueue q(const_cast<int32_t*>(&a.plan->down_next), qslot);
+  for (long item = dyn ? long(blockIdx.x) : xr.next; item < (dyn ? items * ks : xr.end);
+       item = dyn ? q.next() : item + xr.step) {
+    if (dyn) q.claim();
+    packed_down_item(a, sm, item, ntr, nts, nb_all, ks);
+  }
+}
+
 // Packed operand layout (see beam_moe_pack_weights): one thread per 16-byte
 // chunk of the output, i.e. per (matrix, row block, k block, k-step, lane).
 __global__ __launch_bounds__(256) void k_pack_weights(const u16* __restrict__ w, long chunks,
@@ -844,21 +866,41 @@ hipError_t launch_pack_weights(const void* w, int mats, int rows, int cols, void
 }
 
 // ---------------------------------------------------------------------------
-// Expert-stationary prefill (layers with packed weights and no shared
-// experts, tiles of kEsTileRows rows): the tokens of each tile are packed
-// into the MFMA operand layout once (k_pack_tokens_es), gate/up writes h in
-// the same packed layout, and both products run the expert-stationary
-// engine, so that an expert's weight blocks stream from HBM once per tile.
+// Expert-stationary prefill (tiles of kEsTileRows rows): the tokens of each
+// tile are packed into the MFMA operand layout once (k_pack_tokens_es),
+// gate/up writes h in the same packed layout, and both products run the
+// expert-stationary engine, so that an expert's weight blocks stream from
+// HBM once per tile.  The tiles are the routed tiles of the plan (layers
+// without shared experts), or, with es_ntiles > 0, the fused shared expert's
+// tiles of consecutive tokens (the routed tiles then run on the 128-row
+// kernels).
 // ---------------------------------------------------------------------------
 
 __device__ __forceinline__ size_t es_tile_elems(int K) { return size_t(kEsTokBlocks) * K * 32; }
+
+// Tiles of the expert-stationary kernels: their count, and tile t.
+__device__ __forceinline__ int es_tile_count(const ExpertArgs& a) {
+  return a.es_ntiles > 0 ? a.es_ntiles : ld_const(&a.plan->n_tiles_routed);
+}
+__device__ __forceinline__ Tile es_tile(const ExpertArgs& a, int t) {
+  if (a.es_ntiles > 0) {
+    Tile tl;
+    tl.expert = a.E;
+    tl.row0 = t * kEsTileRows;
+    tl.rows = min(kEsTileRows, a.T - tl.row0);
+    tl.pad = 0;
+    return tl;
+  }
+  return ld_tile(a.tiles + t);
+}
 
 // Packed tokens of every routed tile: 16-byte chunk (tile t, token block tb,
 // k block kb, k-step s, lane l) = x[token of row 32 tb + l % 32][64 kb + 16 s
 // + 8 (l / 32) .. + 7]; rows past the tile's end take its first token (their
 // results are never stored).  Blocks with no token of the tile are skipped.
 __global__ __launch_bounds__(256) void k_pack_tokens_es(ExpertArgs a) {
-  const int ntr = ld_const(&a.plan->n_tiles_routed);
+  const int ntr = es_tile_count(a);
+  const bool sh = a.es_ntiles > 0;
   const int C = a.D / kPK;
   const long per_tile = long(kEsTokBlocks) * C * 256;
   const long total = long(ntr) * per_tile;
@@ -868,10 +910,11 @@ __global__ __launch_bounds__(256) void k_pack_tokens_es(ExpertArgs a) {
     const int tb = int(rem / (long(C) * 256));
     const int kb = int((rem >> 8) % C);
     const int w = int(rem & 255), s = w >> 6, l = w & 63;
-    const Tile tl = ld_tile(a.tiles + t);
+    const Tile tl = es_tile(a, t);
     if (32 * tb >= tl.rows) continue;
     const int r = 32 * tb + (l & 31);
-    const int tok = a.perm_token[tl.row0 + (r < tl.rows ? r : 0)];
+    const int row = tl.row0 + (r < tl.rows ? r : 0);
+    const int tok = sh ? row : a.perm_token[row];
     const u16* src = static_cast<const u16*>(a.x) + size_t(tok) * a.D + 64 * kb + 16 * s + 8 * (l >> 5);
     u16* dst = a.xpk + size_t(t) * es_tile_elems(a.D) + (size_t(tb) * C + kb) * kPackBlock + 512 * s + 8 * l;
     *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
@@ -887,6 +930,7 @@ struct EsGateUpProv {
   __device__ const u16* wbase(int bb) const {
     return (bb < 2 ? wg : wu) + size_t(bb & 1) * C * kPackBlock;
   }
+  __device__ uint32_t wslice(int c) const { return uint32_t(c) * kPackBlock; }
   __device__ const u16* xbase() const { return xt; }
 };
 
@@ -900,30 +944,31 @@ struct EsGateUpProv {
 // gate rows 64 nb .. 64 nb + 63, blocks 2, 3 the same up rows: a lane holds
 // gate and up of the same element, and SwiGLU is applied in registers.  h is
 // written in the packed layout of the down product's token operand.
-__global__ __launch_bounds__(256, 1) void k_gate_up_es(ExpertArgs a) {
-  __shared__ EsSmem sm;
+// Rows of the expert-stationary products: the routed experts' I, or the
+// fused shared experts' S Is.
+__device__ __forceinline__ int es_rows(const ExpertArgs& a) { return a.es_ntiles > 0 ? a.S * a.Is : a.I; }
+
+// One item of the expert-stationary gate/up (item < tiles x es_rows / 64).
+__device__ __forceinline__ void es_gate_up_item(const ExpertArgs& a, EsSmem& sm, long item) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int ntr = ld_const(&a.plan->n_tiles_routed);
-  const int nbk = a.I / 64;
-  const int C = a.D / kPK, CI = a.I / kPK;
-  const long total = long(ntr) * nbk;
-  __shared__ int qslot[2];
-  ItemQueue q(const_cast<int32_t*>(&a.plan->gate_up_next), qslot);
-  for (long item = blockIdx.x; item < total; item = q.next()) {
-    q.claim();
+  const bool sh = a.es_ntiles > 0;
+  const int Iv = es_rows(a);
+  const int nbk = Iv / 64;
+  const int C = a.D / kPK, CI = Iv / kPK;
+  {
     const int t = int(item / nbk), nb = int(item - long(t) * nbk);
-    const Tile tl = ld_tile(a.tiles + t);
+    const Tile tl = es_tile(a, t);
     EsGateUpProv pv;
     pv.C = C;
-    const size_t ebase = size_t(tl.expert) * a.I * a.D;
-    pv.wg = a.pg + ebase + size_t(2 * nb) * C * kPackBlock;
-    pv.wu = a.pu + ebase + size_t(2 * nb) * C * kPackBlock;
+    const size_t ebase = sh ? 0 : size_t(tl.expert) * a.I * a.D;
+    pv.wg = (sh ? a.psg : a.pg) + ebase + size_t(2 * nb) * C * kPackBlock;
+    pv.wu = (sh ? a.psu : a.pu) + ebase + size_t(2 * nb) * C * kPackBlock;
     pv.xt = a.xpk + size_t(t) * es_tile_elems(a.D);
     const int nbt = (tl.rows + 31) / 32;
     f32x16 acc[kEsWBlocks][kEsWaveBlocks];
     es_accumulate(pv, sm, acc, nbt);
-    u16* ht = a.hpk + size_t(t) * es_tile_elems(a.I);
+    u16* ht = a.hpk + size_t(t) * es_tile_elems(Iv);
 #pragma unroll
     for (int j = 0; j < kEsWaveBlocks; ++j) {
       const int tb = es_token_block(wave, j, nbt);
@@ -950,36 +995,59 @@ __global__ __launch_bounds__(256, 1) void k_gate_up_es(ExpertArgs a) {
   }
 }
 
+__global__ __launch_bounds__(256, 1) void k_gate_up_es(ExpertArgs a) {
+  __shared__ EsSmem sm;
+  const long total = long(es_tile_count(a)) * (es_rows(a) / 64);
+  __shared__ int qslot[2];
+  ItemQueue q(const_cast<int32_t*>(&a.plan->gate_up_next), qslot);
+  for (long item = blockIdx.x; item < total; item = q.next()) {
+    q.claim();
+    es_gate_up_item(a, sm, item);
+  }
+}
+
 struct EsDownProv {
-  const u16* wd;   // packed down matrix of the expert, at row block 4 db (D % 128 == 0)
+  const u16* wd;   // packed down matrix of the expert (of the first shared expert), at row
+                   // block 4 db (D % 128 == 0)
   const u16* ht;
   int CI;          // k slices
+  int cps;         // k slices per packed matrix: CI, or Is / 64 for the shared experts,
+                   // whose k range runs through one packed [D][Is] matrix per expert
+  size_t seg;      // elements per packed matrix
   __device__ int chunks() const { return CI; }
-  __device__ const u16* wbase(int bb) const { return wd + size_t(bb) * CI * kPackBlock; }
+  __device__ const u16* wbase(int bb) const { return wd + size_t(bb) * cps * kPackBlock; }
+  __device__ uint32_t wslice(int c) const {
+    const int sg = c / cps;
+    return uint32_t(size_t(sg) * seg + size_t(c - sg * cps) * kPackBlock);
+  }
   __device__ const u16* xbase() const { return ht; }
 };
 
 // Items: (tile, block of 128 output rows), tile-major.  O rows are written
-// in pair order for the combine.
-__global__ __launch_bounds__(256, 1) void k_down_es(ExpertArgs a) {
-  __shared__ EsSmem sm;
+// in pair order for the combine (shared experts: O_shared rows in token
+// order).
+// One item of the expert-stationary down product (item < tiles x D / 128).
+__device__ __forceinline__ void es_down_item(const ExpertArgs& a, EsSmem& sm, long item) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int ntr = ld_const(&a.plan->n_tiles_routed);
+  const bool sh = a.es_ntiles > 0;
+  const int Iv = es_rows(a);
   const int ndb = a.D / 128;
-  const int CI = a.I / kPK;
-  const long total = long(ntr) * ndb;
-  for (XcdRange it = xcd_range(total); it.next < it.end; it.next += it.step) {
-    const int t = int(it.next / ndb), db = int(it.next - long(t) * ndb);
-    const Tile tl = ld_tile(a.tiles + t);
+  const int CI = Iv / kPK;
+  {
+    const int t = int(item / ndb), db = int(item - long(t) * ndb);
+    const Tile tl = es_tile(a, t);
     EsDownProv pv;
     pv.CI = CI;
-    pv.wd = a.pd + size_t(tl.expert) * a.D * a.I + size_t(4 * db) * CI * kPackBlock;
-    pv.ht = a.hpk + size_t(t) * es_tile_elems(a.I);
+    pv.cps = sh ? a.Is / kPK : CI;
+    pv.seg = size_t(a.D) * (sh ? a.Is : a.I);
+    pv.wd = sh ? a.psd + size_t(4 * db) * pv.cps * kPackBlock
+               : a.pd + size_t(tl.expert) * a.D * a.I + size_t(4 * db) * CI * kPackBlock;
+    pv.ht = a.hpk + size_t(t) * es_tile_elems(Iv);
     const int nbt = (tl.rows + 31) / 32;
     f32x16 acc[kEsWBlocks][kEsWaveBlocks];
     es_accumulate(pv, sm, acc, nbt);
-    u16* ob = static_cast<u16*>(a.o);
+    u16* ob = static_cast<u16*>(sh ? a.o_sh : a.o);
 #pragma unroll
     for (int j = 0; j < kEsWaveBlocks; ++j) {
       const int m = 32 * es_token_block(wave, j, nbt) + (lane & 31);
@@ -995,6 +1063,79 @@ __global__ __launch_bounds__(256, 1) void k_down_es(ExpertArgs a) {
         }
       }
     }
+  }
+}
+
+__global__ __launch_bounds__(256, 1) void k_down_es(ExpertArgs a) {
+  __shared__ EsSmem sm;
+  const long total = long(es_tile_count(a)) * (a.D / 128);
+  for (XcdRange it = xcd_range(total); it.next < it.end; it.next += it.step) es_down_item(a, sm, it.next);
+}
+
+// Layers whose shared experts run expert-stationary (es_ntiles > 0): one
+// launch per product takes the fused shared expert's items (expert-stationary
+// engine: MFMA- and L2-heavy) and the routed tiles' items (128-row packed
+// engine: a few tokens per expert, weight streaming) from one work counter,
+// so that the two kinds run side by side.  Run as two launches, the routed
+// gate/up alone took 136 us and the shared one 102 us on the
+// DeepSeek-V2-Lite prefill layer at T = 4096, against 208 us for the launch
+// that took both on the packed engine.  Item order, measured on that layer
+// (gate/up / down us): the kinds alternating 206 / 132, shared first 224 /
+// 109, routed first 220 / 159; the gate/up kernel alternates, the down
+// kernel (176 long shared items for 256 CUs) takes the shared ones first.
+union MixedSmem {
+  EsSmem es;
+  PrefillSmem<128> pk;
+};
+
+// Item i: *shared = is a shared item; returns its index among its kind (ns
+// shared items, nr routed ones), the kinds alternating while both last, or
+// the shared ones first.
+__device__ __forceinline__ long mixed_item(long i, long ns, long nr, bool alternate, bool* shared) {
+  if (!alternate) {
+    *shared = i < ns;
+    return i < ns ? i : i - ns;
+  }
+  const long m = min(ns, nr);
+  if (i < 2 * m) {
+    *shared = (i & 1) == 0;
+    return i >> 1;
+  }
+  *shared = ns > nr;
+  return m + (i - 2 * m);
+}
+
+__global__ __launch_bounds__(256, 1) void k_gate_up_mixed(ExpertArgs a) {
+  __shared__ MixedSmem sm;
+  const long ns = long(a.es_ntiles) * (a.S * a.Is / 64);
+  const int ntr = ld_const(&a.plan->n_tiles_routed);
+  const int nbr = (a.I + kPackedIB - 1) / kPackedIB;
+  const long nr = long(ntr) * nbr;
+  __shared__ int qslot[2];
+  ItemQueue q(const_cast<int32_t*>(&a.plan->gate_up_next), qslot);
+  for (long item = blockIdx.x; item < ns + nr; item = q.next()) {
+    q.claim();
+    bool shared;
+    const long j = mixed_item(item, ns, nr, true, &shared);
+    if (shared) es_gate_up_item(a, sm.es, j);   // workgroup-uniform
+    else packed_gate_up_item(a, sm.pk, j, ntr, 0, nbr, 1);
+  }
+}
+
+__global__ __launch_bounds__(256, 1) void k_down_mixed(ExpertArgs a) {
+  __shared__ MixedSmem sm;
+  const long ns = long(a.es_ntiles) * (a.D / 128);
+  const int ntr = ld_const(&a.plan->n_tiles_routed);
+  const int nb_all = (a.D + kPackedDB - 1) / kPackedDB;
+  const long nr = long(ntr) * nb_all;
+  __shared__ int qslot[2];
+  ItemQueue q(const_cast<int32_t*>(&a.plan->down_next), qslot);
+  for (long item = blockIdx.x; item < ns + nr; item = q.next()) {
+    q.claim();
+    bool shared;
+    const long j = mixed_item(item, ns, nr, false, &shared);
+    if (shared) es_down_item(a, sm.es, j);
+    else packed_down_item(a, sm.pk, j, ntr, 0, nb_all, 1);
   }
 }
 
@@ -1234,6 +1375,7 @@ static ExpertArgs expert_args(const beam_moe_layer& L, const void* x, int32_t T,
   a.perm_token = p.perm_token;
   a.expert_off = p.expert_off;
   a.tile_rows = 0;
+  a.es_ntiles = 0;
   a.xpk = reinterpret_cast<u16*>(p.es_x);
   a.hpk = reinterpret_cast<u16*>(p.es_h);
   a.h = p.h;
@@ -1426,6 +1568,22 @@ hipError_t launch_gate_up(const beam_moe_layer& L, const void* x, int32_t T, int
     hipLaunchKernelGGL(k_gate_up_es, dim3(tiled_grid((const void*)&k_gate_up_es, ntr * (L.I / 64))),
                        dim3(256), 0, s, a);
     prof_after(s);
+  } else if (L.wp_gate && es_shared_experts(L, T)) {
+    // routed tiles on the 128-row kernel, the shared experts' tiles of
+    // consecutive tokens on the expert-stationary ones
+    a.tile_rows = tile_rows;
+    a.es_ntiles = (T + kEsTileRows - 1) / kEsTileRows;
+    prof_before("shared_pack_tokens_es", s);
+    const long chunks = long(a.es_ntiles) * kEsTokBlocks * long(L.D / kPK) * 256;
+    hipLaunchKernelGGL(k_pack_tokens_es, dim3(unsigned(std::min<long>((chunks + 255) / 256, 4096))),
+                       dim3(256), 0, s, a);
+    prof_after(s);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    prof_before("gate_up_swiglu_mixed", s);
+    const long items = long(a.es_ntiles) * (L.n_shared * L.I_shared / 64) + ntr * ((L.I + 127) / 128);
+    hipLaunchKernelGGL(k_gate_up_mixed, dim3(tiled_grid((const void*)&k_gate_up_mixed, items)), dim3(256), 0,
+                       s, a);
+    prof_after(s);
   } else if (L.wp_gate) {   // packed weights: tiles of 128 token rows
     a.tile_rows = tile_rows;
     const long items = ntr * ((L.I + 127) / 128) +
@@ -1470,7 +1628,9 @@ static bool down_may_split(const beam_moe_layer& L, int tile_rows) {
 hipError_t launch_down(const beam_moe_layer& L, int32_t T, int tile_rows, const WsLayout&,
                        const Ptrs& p, hipStream_t s, bool allow_split) {
   ExpertArgs a = expert_args(L, nullptr, T, p);
-  if (allow_split && p.o_part && down_may_split(L, tile_rows)) a.down_slots = down_tiled_slots(L, tile_rows);
+  const bool ess = L.wp_gate && es_shared_experts(L, T);
+  if (allow_split && p.o_part && down_may_split(L, tile_rows) && !ess)
+    a.down_slots = down_tiled_slots(L, tile_rows);
   long nts;
   const long ntr = tile_bound(L, T, tile_rows, &nts);
   if (L.dtype == BEAM_F32) {
@@ -1492,6 +1652,15 @@ hipError_t launch_down(const beam_moe_layer& L, int32_t T, int tile_rows, const 
     prof_before("down_es", s);
     hipLaunchKernelGGL(k_down_es, dim3(tiled_grid((const void*)&k_down_es, ntr * (L.D / 128))),
                        dim3(256), 0, s, a);
+    prof_after(s);
+  } else if (ess) {
+    // routed tiles on the 128-row kernel (no k split), the shared experts'
+    // tiles on the expert-stationary one (output O_shared)
+    a.tile_rows = tile_rows;
+    a.es_ntiles = (T + kEsTileRows - 1) / kEsTileRows;
+    prof_before("down_mixed", s);
+    const long items = long(a.es_ntiles) * (L.D / 128) + ntr * ((L.D + 255) / 256);
+    hipLaunchKernelGGL(k_down_mixed, dim3(tiled_grid((const void*)&k_down_mixed, items)), dim3(256), 0, s, a);
     prof_after(s);
   } else if (L.wp_gate) {   // packed weights: tiles of 128 token rows
     a.tile_rows = tile_rows;
@@ -1522,7 +1691,7 @@ hipError_t launch_combine(const beam_moe_layer& L, int32_t T, int tile_rows, con
                           void* y, hipStream_t s) {
   const void* osh = L.n_shared > 0 ? p.o_shared : nullptr;
   CombineSplit cs{nullptr, 0, 0, nullptr, nullptr, 0, 0};
-  if (p.o_part && down_may_split(L, tile_rows)) {
+  if (p.o_part && down_may_split(L, tile_rows) && !(L.wp_gate && es_shared_experts(L, T))) {
     const ExpertArgs a = expert_args(L, nullptr, T, p);
     cs = CombineSplit{p.plan, down_tiled_slots(L, tile_rows), down_tiled_nb(L, tile_rows), a.op, a.op_sh,
                       a.op_stride, a.op_sh_stride};

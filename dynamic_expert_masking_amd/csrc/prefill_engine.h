@@ -276,6 +276,8 @@ struct EsSmem {
 //   int chunks()                   64-wide k slices of the product
 //   const u16* wbase(bb)           packed matrix of weight block bb (0..3), at
 //                                  its row of packed blocks
+//   uint32_t wslice(c)             element offset of k slice c from wbase (c *
+//                                  kPackBlock within one packed matrix)
 //   const u16* xbase()             packed tokens of the tile (block row 0)
 // On return acc[bb][j][i] = C[n = 32 bb + 8 (i / 4) + 4 (lane / 32) + i % 4]
 //                            [m = 32 tb_j + lane % 32]
@@ -330,7 +332,7 @@ __device__ __forceinline__ void es_accumulate(const Prov& pv, EsSmem& sm,
     u32x4 v[kEsWaveBlocks][4];
   };
   auto load_w = [&](WStage& st, int c) {
-    const uint32_t off = uint32_t(min(c, C - 1)) * kPackBlock;   // past the end: the last slice
+    const uint32_t off = pv.wslice(min(c, C - 1));   // past the end: the last slice
 #pragma unroll
     for (int s = 0; s < 4; ++s) st.v[s] = ld16_at_stream(wb, off + 512 * s);
   };
