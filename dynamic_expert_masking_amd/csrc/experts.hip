@@ -1339,6 +1339,128 @@ __global__ __launch_bounds__(256) void k_combine(int T, int D, int K, const floa
   }
 }
 
+// Large bf16 batches: one wave per token
+// (each workgroup's four waves take tokens 4 b + w, then a grid stride),
+// lane l holding outputs 8 l .. 8 l + 7 of each 512-wide pass, so that every
+// kept slot's row is read with one 16-byte load per pass, all P passes in
+// flight at once (SPLIT: the down product may have split k; then the fp32
+// partials of the splits, added in split order).  The sum is the same as
+// k_combine's: fp32, kept slots in slot order, the shared output last, one
+// rounding.  Against k_combine (one workgroup per token) on MI355X: 14.5 ->
+// 12.0 us on the DeepSeek-V2-Lite prefill batch (T = 4096), 24.7 -> 22.0 on
+// the fine-grained T = 8192 one, 10.3 -> 9.9 on the Mixtral-shaped T = 2048
+// one.
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+
+template <int P, bool SPLIT>
+__global__ __launch_bounds__(256) void k_combine_tok(int T, int D, int K, const float* __restrict__ gates,
+                                                     const int32_t* __restrict__ slot_pos,
+                                                     const u16* __restrict__ o, const u16* __restrict__ o_sh,
+                                                     u16* __restrict__ y, CombineSplit cs) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int ks = 1;
+  if constexpr (SPLIT) {   // the down product may have split k
+    const int ntr = ld_const(&cs.plan->n_tiles_routed), nts = ld_const(&cs.plan->n_tiles_shared);
+    ks = down_split(long(ntr + nts) * cs.nb_all, cs.slots);
+  }
+  for (int t = blockIdx.x * 4 + wave; t < T; t += gridDim.x * 4) {
+    int32_t pl = -1;
+    float gl = 0.f;
+    if (lane < K) {
+      pl = slot_pos[size_t(t) * K + lane];
+      gl = gates[size_t(t) * K + lane];
+    }
+    uint64_t kept = __ballot(pl >= 0);
+    float acc[P][8];
+#pragma unroll
+    for (int q = 0; q < P; ++q)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[q][i] = 0.f;
+    while (kept) {   // wave-uniform
+      const int k = __ffsll(static_cast<unsigned long long>(kept)) - 1;
+      kept &= kept - 1;
+      const int p = __shfl(pl, k);
+      const float g = __shfl(gl, k);
+      if (SPLIT && ks > 1) {   // wave-uniform
+#pragma unroll
+        for (int q = 0; q < P; ++q) {
+          const int d = 512 * q + 8 * lane;
+          if (d < D) {
+            const float4 a = split_row4(cs.op, cs.op_stride, ks, size_t(p) * D + d);
+            const float4 b = split_row4(cs.op, cs.op_stride, ks, size_t(p) * D + d + 4);
+            acc[q][0] += g * a.x;
+            acc[q][1] += g * a.y;
+            acc[q][2] += g * a.z;
+            acc[q][3] += g * a.w;
+            acc[q][4] += g * b.x;
+            acc[q][5] += g * b.y;
+            acc[q][6] += g * b.z;
+            acc[q][7] += g * b.w;
+          }
+        }
+        continue;
+      }
+      u32x4 v[P];
+#pragma unroll
+      for (int q = 0; q < P; ++q) {
+        const int d = 512 * q + 8 * lane;
+        v[q] = d < D ? ld16(o + size_t(p) * D + d) : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int q = 0; q < P; ++q)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[q][2 * i] += g * bf16_lo(v[q][i]);
+          acc[q][2 * i + 1] += g * bf16_hi(v[q][i]);
+        }
+    }
+    if (SPLIT && o_sh && ks > 1) {
+#pragma unroll
+      for (int q = 0; q < P; ++q) {
+        const int d = 512 * q + 8 * lane;
+        if (d < D) {
+          const float4 a = split_row4(cs.op_sh, cs.op_sh_stride, ks, size_t(t) * D + d);
+          const float4 b = split_row4(cs.op_sh, cs.op_sh_stride, ks, size_t(t) * D + d + 4);
+          acc[q][0] += a.x;
+          acc[q][1] += a.y;
+          acc[q][2] += a.z;
+          acc[q][3] += a.w;
+          acc[q][4] += b.x;
+          acc[q][5] += b.y;
+          acc[q][6] += b.z;
+          acc[q][7] += b.w;
+        }
+      }
+    } else if (o_sh) {
+#pragma unroll
+      for (int q = 0; q < P; ++q) {
+        const int d = 512 * q + 8 * lane;
+        if (d < D) {
+          const u32x4 v = ld16(o_sh + size_t(t) * D + d);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[q][2 * i] += bf16_lo(v[i]);
+            acc[q][2 * i + 1] += bf16_hi(v[i]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < P; ++q) {
+      const int d = 512 * q + 8 * lane;
+      if (d < D) {
+        u32x4 r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          r[i] = uint32_t(f32_to_bf16(acc[q][2 * i])) | (uint32_t(f32_to_bf16(acc[q][2 * i + 1])) << 16);
+        *reinterpret_cast<u32x4*>(y + size_t(t) * D + d) = r;
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
@@ -1697,13 +1819,36 @@ hipError_t launch_combine(const beam_moe_layer& L, int32_t T, int tile_rows, con
                       a.op_stride, a.op_sh_stride};
   }
   prof_before("combine", s);
+  const bool bf = L.dtype != BEAM_F32;
+  if (bf && T >= 1024 && L.D <= 4096 && L.D % 8 == 0) {
+    const unsigned grid = unsigned(std::min<long>((T + 3) / 4, 2048));
+    auto tok = [&](auto kern) {
+      hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, s, T, L.D, L.K, p.gates, p.slot_pos,
+                         (const u16*)p.o, (const u16*)osh, (u16*)y, cs);
+    };
+    const int P = (L.D + 511) / 512;
+    if (cs.plan) {
+      if (P <= 1) tok(k_combine_tok<1, true>);
+      else if (P <= 2) tok(k_combine_tok<2, true>);
+      else if (P <= 3) tok(k_combine_tok<3, true>);
+      else if (P <= 4) tok(k_combine_tok<4, true>);
+      else tok(k_combine_tok<8, true>);
+    } else {
+      if (P <= 1) tok(k_combine_tok<1, false>);
+      else if (P <= 2) tok(k_combine_tok<2, false>);
+      else if (P <= 3) tok(k_combine_tok<3, false>);
+      else if (P <= 4) tok(k_combine_tok<4, false>);
+      else tok(k_combine_tok<8, false>);
+    }
+    prof_after(s);
+    return hipGetLastError();
+  }
   // Below 1024 tokens: all K slots in one chunk when K <= 8, else the kept
   // slots four at a time; from 1024 tokens: the kept slots one at a time.
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3(unsigned(T)), dim3(256), 0, s, T, L.D, L.K, p.gates, p.slot_pos,
                        p.o, osh, y, cs);
   };
-  const bool bf = L.dtype != BEAM_F32;
   if (T >= 1024) bf ? go(k_combine<true, 1, true>) : go(k_combine<false, 1, true>);
   else if (L.K <= 2) bf ? go(k_combine<true, 2, false>) : go(k_combine<false, 2, false>);
   else if (L.K <= 4) bf ? go(k_combine<true, 4, false>) : go(k_combine<false, 4, false>);
