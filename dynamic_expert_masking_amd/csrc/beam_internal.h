@@ -45,8 +45,10 @@ constexpr int kEsTileRows = 384;
 constexpr int kEsMinPerExpert = 256;
 // Packed layers with shared experts: from this many tokens the fused shared
 // expert (every token) runs on the expert-stationary kernels, on tiles of
-// kEsTileRows consecutive tokens, and the routed tiles on the 128-row ones.
-constexpr int kEsSharedMinT = 1024;
+// kEsTileRows consecutive tokens, and the routed tiles on the 128-row ones
+// (DeepSeek-V2-Lite prefill shapes on MI355X, us per step with / without:
+// T = 1536 289 / 285, T = 2048 309 / 324, T = 4096 388 / 410).
+constexpr int kEsSharedMinT = 2048;
 
 struct WsLayout {
   size_t plan, logits, idx, gates, mask, counts, rank, block_counts, expert_off, tiles, perm_token,

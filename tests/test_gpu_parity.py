@@ -240,14 +240,17 @@ def test_packed_weights_workloads(name, T):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("T,S", [(1200, 2), (700, 0), (3000, 1), (1100, 0), (3000, 0), (130, 1)])
+@pytest.mark.parametrize("T,S", [(1200, 2), (700, 0), (3000, 1), (2100, 2), (1100, 0), (3000, 0), (130, 1)])
 def test_packed_small_layers(T, S):
     """Packed weights on small layers: two shared experts (one packed down
     matrix per shared expert, a segment boundary inside a split k range), no
     shared expert, ragged tiles, and a batch small enough for the streaming
     kernels.  Without shared experts and with at least 256 candidates per
     expert (T = 1100, 3000) the expert-stationary kernels run, on tiles of up
-    to 384 rows (T = 3000: two tiles for most experts)."""
+    to 384 rows (T = 3000: two tiles for most experts); with shared experts
+    and at least 2048 tokens (T = 2100, 3000) the shared experts run on them
+    beside the routed 128-row tiles (one packed down matrix per shared
+    expert, the last tile partly filled)."""
     from dynamic_expert_masking_amd.device import DeviceLayer
     layer = small_layer(f"packed{S}", D=256, E=8, K=2, I=256, S=S, I_s=128 if S else 0, keep=0.7,
                         router_bias=True)
