@@ -71,6 +71,26 @@ def test_workspace_size_monotone_and_invalid():
     assert dm.beam_moe_workspace_size(fake_layer(**f8), 64) == sizes[2]
 
 
+def test_shared_expert_stationary_workspace():
+    """Packed layers with shared experts run the shared experts on the
+    expert-stationary kernels from 2048 tokens: the workspace then also holds
+    their packed tokens and h (ceil(T / 384) tiles of 384 x (D + S Is) bf16),
+    and it stays non-decreasing in T across the switch.  Below it, the packed
+    and the unpacked layer need the same workspace."""
+    cfg = synth.CONFIGS["dsv2lite_prefill"]
+    kw = dict(D=cfg.D, E=cfg.E, K=cfg.K, I=cfg.I, n_shared=cfg.S, I_shared=cfg.I_s, ws_gate=FAKE,
+              ws_up=FAKE, ws_down=FAKE)
+    packed = dict(wp_gate=FAKE, wp_up=FAKE, wp_down=FAKE, wsp_gate=FAKE, wsp_up=FAKE, wsp_down=FAKE)
+    Lp, Lu = fake_layer(**kw, **packed), fake_layer(**kw)
+    Ts = [1, 64, 1024, 2000, 2047, 2048, 2049, 3000, 4096]
+    sizes = [dm.beam_moe_workspace_size(Lp, T) for T in Ts]
+    assert all(a <= b for a, b in zip(sizes, sizes[1:]))
+    for T in (64, 1024, 2047):
+        assert dm.beam_moe_workspace_size(Lp, T) == dm.beam_moe_workspace_size(Lu, T)
+    es_bytes = -(-2048 // 384) * 384 * (cfg.D + cfg.S * cfg.I_s) * 2
+    assert (dm.beam_moe_workspace_size(Lp, 2048) - dm.beam_moe_workspace_size(Lu, 2048)) >= es_bytes
+
+
 def config_layer(cfg):
     """A descriptor with a workload's shapes and fake (never dereferenced) pointers."""
     kw = dict(D=cfg.D, E=cfg.E, K=cfg.K, I=cfg.I,
