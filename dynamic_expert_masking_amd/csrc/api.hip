@@ -2,6 +2,7 @@
 // carving, launch sequence, work accounting and the launch profiler.
 #include <string.h>
 
+#include <cmath>
 #include <map>
 #include <mutex>
 #include <string>
@@ -17,10 +18,22 @@ int expert_tile_rows(const beam_moe_layer& L, int32_t T) {
   if (L.dtype == BEAM_F32) return 16;
   // Expected tokens per routed expert if every top-K candidate were kept.
   const long per_expert = (long(T) * L.K + L.E - 1) / L.E;
-  if (per_expert <= 16) return 16;
-  if (per_expert <= 32) return 32;
   // FP8 weights only have the streaming kernels (tiles of up to 64 rows)
-  if (per_expert <= 96 || L.expert_format == BEAM_WEIGHTS_FP8_E4M3) return 64;
+  if (per_expert <= 96 || L.expert_format == BEAM_WEIGHTS_FP8_E4M3) {
+    // Layers without shared experts size these tiles by the surviving pairs
+    // expected from the layer's Avg-K (fine-grained layer, T = 512: 16-row
+    // tiles for about 6 pairs per expert instead of 64-row ones, 126 -> 122
+    // us per step on MI355X).  With shared experts, whose tiles span the
+    // whole batch at the same height, smaller tiles re-read the shared
+    // weights more often than they save (DeepSeek-V2-Lite T = 256: 236 ->
+    // 254 us), so those keep the top-K estimate.
+    long pe = per_expert;
+    if (L.n_shared == 0 && L.expected_avg_k > 0.f)
+      pe = long(std::ceil(double(T) * L.expected_avg_k / L.E));
+    if (pe <= 16) return 16;
+    if (pe <= 32) return 32;
+    return 64;
+  }
   // packed weights: the expert-stationary kernels (no shared experts, at
   // least kEsMinPerExpert candidates per expert), else tiles of 128 rows
   if (L.wp_gate && L.n_shared == 0 && L.D % 128 == 0) {

@@ -61,10 +61,12 @@ struct RouterSkinnyProv {
 // stream through many CUs; from 2048 tokens on, four row groups share each
 // token-row load (the token rows, not the weights, are then the traffic:
 // T = 4096, E = 64: 26.8 -> 21.8 us on MI355X; at 256 tokens the smaller grid
-// costs more than the re-reads).
+// costs more than the re-reads).  Layers of at least 128 experts have enough
+// row groups to keep the grid full with four per workgroup from 256 tokens
+// on (E = 212, T = 512: 15.9 -> 14.8 us).
 constexpr int kRouterSkinnyMaxT = 1024;
 __host__ __device__ inline bool router_use_skinny(int T, int E) { return T <= kRouterSkinnyMaxT || E <= 64; }
-__host__ __device__ inline int router_nm(int T, int E) { return T >= 2048 && 2 * E >= 64 ? 4 : 1; }
+__host__ __device__ inline int router_nm(int T, int E) { return (T >= 2048 && 2 * E >= 64) || (T >= 256 && E >= 128) ? 4 : 1; }
 __host__ __device__ inline int router_mt(int T, int E) {
   const int nrb = (2 * E + 16 * router_nm(T, E) - 1) / (16 * router_nm(T, E));
   if (T <= 16) return 1;
