@@ -156,8 +156,12 @@ typedef struct {
    * unknown (then K is assumed).  A hint for choosing kernels only: with
    * packed weights and no shared experts, batches expected to give each
    * expert at least 256 surviving pairs (T x expected_avg_k / E) run the
-   * expert-stationary prefill kernels.  Results never depend on it.  Must
-   * be finite and in [0, K] (else BEAM_ERR_INVALID_ARG). */
+   * expert-stationary prefill kernels, and on layers without shared
+   * experts the decode-sized row tiles (16, 32 or 64 rows) are sized by
+   * the same expected count.  The kernels it picks between compute the
+   * same sums, possibly in another order: routing is unchanged, y agrees
+   * within rounding.  Must be finite and in [0, K] (else
+   * BEAM_ERR_INVALID_ARG). */
   float expected_avg_k;
 } beam_moe_layer;
 
