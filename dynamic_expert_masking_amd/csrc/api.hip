@@ -54,16 +54,17 @@ bool es_shared_experts(const beam_moe_layer& L, int32_t T) {
 // Rows of router partial logits ([KS][T] of them) that the workspace holds
 // for a batch of T tokens: an upper bound on KS(T') * T' over every T' <= T,
 // so that a workspace sized for T_max serves every smaller batch (KS rises as
-// T falls).  The router splits k at most 4 ways and only while its grid has
-// fewer than 256 / (KS - 1) workgroups; with at least ceil(T / 64) token
-// blocks that needs T < 16384 for a 2-way split, T <= 8128 for 3 and
-// T <= 5440 for 4.  A maximum of non-decreasing terms, so the bound (and the
-// whole workspace size) is non-decreasing in T.
+// T falls).  The router splits k at most 4 ways, and only while its grid of
+// blocks x KS workgroups stays within 512 (from 256 tokens; below, while
+// blocks x (KS - 1) < 256, which is the weaker bound).  With at least
+// ceil(T / 64) token blocks that needs T <= 16384 for a 2-way split,
+// T <= 10880 for 3 and T <= 8192 for 4.  A maximum of non-decreasing terms,
+// so the bound (and the whole workspace size) is non-decreasing in T.
 long router_logit_rows(const beam_moe_layer& L, int32_t T) {
   if (L.dtype == BEAM_F32) return T;
   const long t = T;
-  return std::max({t, 2 * std::min<long>(t, 16383), 3 * std::min<long>(t, 8128),
-                   4 * std::min<long>(t, 5440)});
+  return std::max({t, 2 * std::min<long>(t, 16384), 3 * std::min<long>(t, 10880),
+                   4 * std::min<long>(t, 8192)});
 }
 
 WsLayout workspace_layout(const beam_moe_layer& L, int32_t T) {

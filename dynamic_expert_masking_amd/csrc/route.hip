@@ -67,8 +67,17 @@ struct RouterSkinnyProv {
 constexpr int kRouterSkinnyMaxT = 1024;
 __host__ __device__ inline bool router_use_skinny(int T, int E) { return T <= kRouterSkinnyMaxT || E <= 64; }
 __host__ __device__ inline int router_nm(int T, int E) { return (T >= 2048 && 2 * E >= 64) || (T >= 256 && E >= 128) ? 4 : 1; }
+// From kRouterWideT tokens the token blocks are tall (32 tokens, 64 with
+// four row groups from 2048 tokens) and the k split fills the grid instead
+// (router_ksplit): each weight row is then loaded for more tokens.  MI355X,
+// us for (row groups, token blocks of 16, k split), against the earlier
+// choice: DeepSeek-V2-Lite shapes T = 4096 (4, 4, 4) 18.1 against (4, 2, 1)
+// 20.0; fine-grained T = 512 (4, 2, 4) 11.6 against (4, 1, 2) 14.6;
+// Mixtral-shaped T = 2048 (1, 2, 4) 9.0 against (1, 1, 2) 10.1.
+constexpr int kRouterWideT = 256;
 __host__ __device__ inline int router_mt(int T, int E) {
   const int nrb = (2 * E + 16 * router_nm(T, E) - 1) / (16 * router_nm(T, E));
+  if (T >= kRouterWideT) return router_nm(T, E) == 4 && T >= 2048 ? 4 : 2;
   if (T <= 16) return 1;
   if (T <= 32) return 2;
   if (long(nrb) * ((T + 63) / 64) >= 256) return 4;
@@ -222,8 +231,10 @@ int router_ksplit(const beam_moe_layer& L, int32_t T) {
   const int nm = router_nm(T, L.E), mt = router_mt(T, L.E);
   const long blocks = long((2 * L.E + 16 * nm - 1) / (16 * nm)) * ((T + 16 * mt - 1) / (16 * mt));
   int best = 1;
-  for (int ks = 2; ks <= 4; ++ks)
-    if (chunks % ks == 0 && chunks / ks >= 4 && blocks * (ks - 1) < 256) best = ks;
+  for (int ks = 2; ks <= 4; ++ks) {
+    const bool fills = T >= kRouterWideT ? blocks * ks <= 512 : blocks * (ks - 1) < 256;
+    if (chunks % ks == 0 && chunks / ks >= 4 && fills) best = ks;
+  }
   return best;
 }
 
@@ -240,6 +251,7 @@ hipError_t launch_router_logits(const beam_moe_layer& L, const void* x, int32_t 
     return hipGetLastError();
   }
   const int KS = router_ksplit(L, T);
+  if (long(KS) * T > router_logit_rows(L, T)) return hipErrorInvalidValue;   // workspace bound
   RouterArgs a{(const u16*)x, (const u16*)L.w_router, (const u16*)L.w_mask, part, T, L.D, L.E, KS};
   if (router_use_skinny(T, L.E)) {
     const int nm = router_nm(T, L.E), mt = router_mt(T, L.E);
