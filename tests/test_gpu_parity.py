@@ -240,6 +240,40 @@ def test_packed_weights_workloads(name, T):
     torch.cuda.empty_cache()
 
 
+# The benchmark's launch configuration for the layers without shared
+# experts, where the descriptor's Avg-K hint can change the kernels: it gives
+# every layer its workload's Avg-K as expected_avg_k and the prefill-sized
+# batches packed weight copies (fine-grained T = 512: 16-row streaming tiles
+# instead of 64-row ones; T = 8192: the 128-row packed kernels instead of the
+# expert-stationary ones).  Layers with shared experts choose the same kernels
+# with or without the hint and are covered by the workload tests above.
+HINT_CASES = [("finegrained", 16, False), ("finegrained", 512, False), ("finegrained", 8192, True),
+              ("mixtral", 1, False), ("mixtral", 32, False), ("mixtral", 2048, True)]
+
+
+@pytest.mark.parametrize("name,T,pack", HINT_CASES, ids=[f"{n}-T{T}" for n, T, _ in HINT_CASES])
+def test_bench_configuration(name, T, pack):
+    """Routing exact on every token, y on every token (Mixtral T = 2048: every
+    32-row block of every expert), with the benchmark's Avg-K hint and packing."""
+    from dynamic_expert_masking_amd.device import DeviceLayer
+    cfg = synth.CONFIGS[name]
+    layer = cached_layer(name)
+    x = inputs(cfg, T, layer)
+    _dev_cache_clear()
+    dl = DeviceLayer(layer, pack=pack, avg_k_hint=cfg.avg_k_target)
+    note(f"[bench configuration] {name} T={T} pack={pack} expected_avg_k={cfg.avg_k_target:.3f}")
+    y, rt, ys = run_forward(dl, x, reps=2)
+    rt_ref = oracle.route(layer, x)
+    check_routing(rt, rt_ref, cfg.E)
+    assert np.array_equal(ys[0], ys[1]), "two identical calls gave different y"
+    toks = np.arange(T) if T <= FULL_Y_MAX[name] or name != "mixtral" else tile_cover_tokens(rt_ref, cfg.E, T)
+    _, y_ref = oracle.forward(layer, x, tokens=toks)
+    rel = check_output(y[toks], y_ref, cfg.dtype)
+    note(f"[bench configuration] {name} T={T}: rel_err={rel:.2e} tokens_compared={len(toks)}")
+    del dl
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("T,S", [(1200, 2), (700, 0), (3000, 1), (2100, 2), (1100, 0), (3000, 0), (130, 1)])
 def test_packed_small_layers(T, S):
     """Packed weights on small layers: two shared experts (one packed down
