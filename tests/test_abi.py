@@ -113,6 +113,7 @@ def test_workspace_serves_every_smaller_batch(name):
     workspace to pass validation: it would launch kernels on fake pointers.)"""
     L = config_layer(synth.CONFIGS[name])
     Ts = list(range(0, 1100)) + list(range(1100, 17000, 7)) + [4080, 5440, 5441, 8128, 8129,
+                                                               8192, 8193, 10880, 10881,
                                                                16383, 16384, 16385]
     Ts = sorted(set(Ts))
     sizes = [dm.beam_moe_workspace_size(L, T) for T in Ts]
