@@ -589,13 +589,41 @@ def pin_stats_formulas(O):
     assert st["bytes_active_expert_weights"] == 3 * 10 * 3 * 2 * 2 + 3 * 10 * 5 * 2
 
 
+def pin_stats_bytes_from_arrays(O):
+    """The byte counts against the parameter arrays themselves: every expert
+    with at least one surviving pair contributes the nbytes of its three
+    matrices (FP8: codes and row scales), the shared experts theirs, and the
+    total adds both router matrices, x and y -- for bf16, fp32 and FP8
+    layers, with the counts taken from the oracle's own routing."""
+    cases = [small_layer("bytes_bf16", "bf16", D=64, E=12, K=3, I=40, S=1, I_s=24, keep=0.3),
+             small_layer("bytes_f32", "f32", D=32, E=6, K=2, I=16, keep=0.6),
+             fp8_layer("bytes_fp8", D=64, E=9, K=3, I=32, S=2, I_s=32, keep=0.4)]
+    for layer in cases:
+        x = small_x(layer, 7)
+        rt = O.route(layer, x)
+        counts = O.expert_counts(rt, layer.cfg.E)
+        st = O.layer_stats(layer.cfg, counts, x.shape[0])
+        scales = [layer.s_gate, layer.s_up, layer.s_down]
+        routed = 0
+        for e in np.nonzero(counts > 0)[0]:
+            routed += layer.w_gate[e].nbytes + layer.w_up[e].nbytes + layer.w_down[e].nbytes
+            routed += sum(a[e].nbytes for a in scales if a is not None)
+        shared = sum(a.nbytes for a in (layer.ws_gate, layer.ws_up, layer.ws_down,
+                                        layer.ss_gate, layer.ss_up, layer.ss_down)
+                     if a is not None and a.size)
+        assert st["bytes_active_expert_weights"] == routed + shared, layer.cfg.name
+        total = routed + shared + layer.w_router.nbytes + layer.w_mask.nbytes + 2 * x.nbytes
+        assert st["bytes_total_min"] == total, layer.cfg.name
+        assert 0 < (counts > 0).sum() < layer.cfg.E or layer.cfg.E <= 6, "some experts idle"
+
+
 ALL_PINS = [
     pin_golden_routed, pin_golden_shared, pin_golden_gating, pin_gate_options_vs_torch,
     pin_gate_options_identity, pin_mask_backward_autograd, pin_mask_backward_zero_router,
     pin_zero_mask_router_is_topk, pin_dense_bruteforce,
     pin_avgk_popcount, pin_mask_bias_extremes, pin_k1, pin_k_equals_e, pin_gate_properties,
     pin_threshold_is_sigmoid_half, pin_batch_invariance, pin_expert_permutation,
-    pin_silu_closed_forms, pin_widen_bf16, pin_stats_formulas,
+    pin_silu_closed_forms, pin_widen_bf16, pin_stats_formulas, pin_stats_bytes_from_arrays,
     pin_e4m3_known_values, pin_e4m3_vs_torch, pin_fp8_layer_vs_torch,
     pin_golden_segment, pin_segment_vs_torch, pin_segment_properties,
 ]

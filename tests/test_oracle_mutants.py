@@ -106,6 +106,15 @@ MUTANTS = {
     "binary_over_k": ("            g[t] = 1.0\n", "            g[t] = 1.0 / K\n"),
     # Avg-K counts all top-K slots
     "avgk_topk": ('"avg_k": (P / T) if T > 0 else 0.0', '"avg_k": (cfg.K if T > 0 else 0.0)'),
+    # bytes: every routed expert counted, active or not
+    "bytes_all_experts": ('"bytes_active_expert_weights": float(per_routed * active + per_shared * cfg.S)',
+                          '"bytes_active_expert_weights": float(per_routed * cfg.E + per_shared * cfg.S)'),
+    # bytes: one router matrix instead of two
+    "bytes_one_router": ("+ 2.0 * cfg.E * D * elt          # router + mask-router weights",
+                         "+ 1.0 * cfg.E * D * elt          # router + mask-router weights"),
+    # bytes: FP8 row scales left out
+    "bytes_fp8_no_scales": ("per_routed = 3 * D * I + 4 * (2 * I + D) if fp8 else 3 * D * I * elt",
+                            "per_routed = 3 * D * I if fp8 else 3 * D * I * elt"),
 }
 
 
