@@ -1620,6 +1620,16 @@ static void gate_up_streaming(const beam_moe_layer& L, const ExpertArgs& a, long
     if (items2 * ks >= kWideShares) gate_up_stream<1, 2, 1, F8>(a, ntr, nts, L.I, Is_all, ks, s);
     else gate_up_stream<1, 1, 1, F8>(a, ntr, nts, L.I, Is_all, ks, s);
   } else if (tile_rows == 32) {
+    // rows of fewer than 64 chunks: four row groups per item and no k split,
+    // as for the 64-row tiles below (DeepSeek-V2-Lite shapes, T = 256: gate/up
+    // 144.7 -> 137.6 us on MI355X against two row groups and a 2-way split;
+    // two row groups with no split 152.0, four with a 2-way split 142.7)
+    if constexpr (!F8) {
+      if (chunks < 64) {
+        gate_up_stream_k<2, 4, 1, 1, F8>(a, ntr, nts, L.I, Is_all, s);
+        return;
+      }
+    }
     gate_up_stream<2, 2, 1, F8>(a, ntr, nts, L.I, Is_all, chunks >= 64 ? 4 : 2, s);
   } else {
     if constexpr (!F8) {
