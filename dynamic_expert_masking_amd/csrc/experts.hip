@@ -14,6 +14,7 @@
 // rows back to back.  Grids are persistent: workgroup b takes items b,
 // b + gridDim.x, ... up to the device-side item count, so no host readback of
 // the counts is needed.
+#include <cmath>
 #include <map>
 #include <mutex>
 
@@ -1616,8 +1617,21 @@ static void gate_up_streaming(const beam_moe_layer& L, const ExpertArgs& a, long
   }
   if (tile_rows == 16) {
     const int ks = stream_ksplit_chunks(chunks);
-    const long items2 = ntr * (L.I / 32) + nts * (Is_all / 32);
-    if (items2 * ks >= kWideShares) gate_up_stream<1, 2, 1, F8>(a, ntr, nts, L.I, Is_all, ks, s);
+    // The choice counts the routed tiles expected from the layer's Avg-K hint
+    // (K when unknown): the distinct experts that T x Avg-K pairs hit, plus
+    // one tile per 16 pairs, at most the bound the grid is sized for.  The
+    // bound alone (one tile per expert up to T x K) overstates small batches
+    // of many experts: fine-grained layer, T = 16, 37 active experts against
+    // a bound of 228 tiles; one row group per item there takes 40.4 us per
+    // step on MI355X against 42.3 with two.  Shares of at least 16 chunks
+    // per wave keep two row groups whatever the count (Mixtral-shaped, T = 1:
+    // 84.7 us against 85.3 with one).
+    const double pairs = double(a.T) * (L.expected_avg_k > 0.f ? L.expected_avg_k : float(L.K));
+    const double expect = double(L.E) * (1.0 - std::exp(-pairs / L.E)) + std::floor(pairs / 16.0);
+    const long ntr_exp = std::min<long>(ntr, long(std::ceil(expect)));
+    const long items2 = ntr_exp * (L.I / 32) + nts * (Is_all / 32);
+    if (items2 * ks >= kWideShares || chunks / ks >= 16)
+      gate_up_stream<1, 2, 1, F8>(a, ntr, nts, L.I, Is_all, ks, s);
     else gate_up_stream<1, 1, 1, F8>(a, ntr, nts, L.I, Is_all, ks, s);
   } else if (tile_rows == 32) {
     // rows of fewer than 64 chunks: four row groups per item and no k split,
