@@ -1591,6 +1591,19 @@ static void down_stream(const ExpertArgs& a, long tiles, int D, int ks, hipStrea
   else down_stream_k<MT, NB, U, 4, F8>(a, tiles, D, s);
 }
 
+// Routed 16-row tiles a batch of T tokens is expected to give, for choosing
+// the streaming variant: the distinct experts that T x Avg-K pairs hit
+// (E (1 - e^(-T Avg-K / E)), Avg-K from the descriptor's hint, K when
+// unknown) plus one tile per 16 pairs, at most the bound ntr the grid is
+// sized for.  The bound (one tile per expert up to T x K) overstates small
+// batches of many experts: the fine-grained layer at T = 16 has about 37
+// active experts against a bound of 228 tiles.
+static long expected_routed_tiles(const beam_moe_layer& L, int T, long ntr) {
+  const double pairs = double(T) * (L.expected_avg_k > 0.f ? L.expected_avg_k : float(L.K));
+  const double expect = double(L.E) * (1.0 - std::exp(-pairs / L.E)) + std::floor(pairs / 16.0);
+  return std::min<long>(ntr, long(std::ceil(expect)));
+}
+
 // Streaming launches for tiles of 16, 32 or 64 rows.  Weight chunks are 128
 // bytes of a row in both formats, so the k split follows the chunk count.
 template <bool F8>
@@ -1604,7 +1617,9 @@ static void gate_up_streaming(const beam_moe_layer& L, const ExpertArgs& a, long
     // per wave of a full grid; 32-row tiles four row groups on short rows,
     // else two with a 2-way split; 64-row tiles as bf16.
     if (tile_rows == 16) {
-      const long items1 = ntr * (L.I / 16) + nts * (Is_all / 16);
+      // (expected tiles: T = 1, 12.6 -> 12.0 us with the 4-way split the
+      // bound's 2-way choice missed)
+      const long items1 = expected_routed_tiles(L, a.T, ntr) * (L.I / 16) + nts * (Is_all / 16);
       const long want = kStreamGrid * kStreamWaves * 3 / 4;
       const int ks = items1 >= want ? 1 : 2 * items1 >= want ? 2 : 4;
       gate_up_stream<1, 1, 1, F8>(a, ntr, nts, L.I, Is_all, ks, s);
@@ -1620,19 +1635,12 @@ static void gate_up_streaming(const beam_moe_layer& L, const ExpertArgs& a, long
   }
   if (tile_rows == 16) {
     const int ks = stream_ksplit_chunks(chunks);
-    // The choice counts the routed tiles expected from the layer's Avg-K hint
-    // (K when unknown): the distinct experts that T x Avg-K pairs hit, plus
-    // one tile per 16 pairs, at most the bound the grid is sized for.  The
-    // bound alone (one tile per expert up to T x K) overstates small batches
-    // of many experts: fine-grained layer, T = 16, 37 active experts against
-    // a bound of 228 tiles; one row group per item there takes 40.4 us per
-    // step on MI355X against 42.3 with two.  Shares of at least 16 chunks
-    // per wave keep two row groups whatever the count (Mixtral-shaped, T = 1:
+    // Two row groups per item when the expected tiles give enough shares
+    // (fine-grained layer, T = 16: one group 40.4 us per step on MI355X
+    // against 42.3 with two, which the bound alone would pick), or when the
+    // shares are long, at least 16 chunks per wave (Mixtral-shaped, T = 1:
     // 84.7 us against 85.3 with one).
-    const double pairs = double(a.T) * (L.expected_avg_k > 0.f ? L.expected_avg_k : float(L.K));
-    const double expect = double(L.E) * (1.0 - std::exp(-pairs / L.E)) + std::floor(pairs / 16.0);
-    const long ntr_exp = std::min<long>(ntr, long(std::ceil(expect)));
-    const long items2 = ntr_exp * (L.I / 32) + nts * (Is_all / 32);
+    const long items2 = expected_routed_tiles(L, a.T, ntr) * (L.I / 32) + nts * (Is_all / 32);
     if (items2 * ks >= kWideShares || chunks / ks >= 16)
       gate_up_stream<1, 2, 1, F8>(a, ntr, nts, L.I, Is_all, ks, s);
     else gate_up_stream<1, 1, 1, F8>(a, ntr, nts, L.I, Is_all, ks, s);
