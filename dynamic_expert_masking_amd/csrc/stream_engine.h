@@ -13,8 +13,10 @@
 // line of a row, so every load instruction touches 8 whole lines (2
 // instructions per chunk).  A wave-private LDS tile then turns each chunk
 // into the MFMA operand layout (lane l: row l % 16 and 8 consecutive k
-// values).  FP8 codes are widened to bf16 in registers first, exactly, and
-// go through the tile in two halves.  Token rows are small and cache-resident
+// values).  FP8 codes go through the tile as they are and are widened to
+// bf16, exactly, in registers after the fragment reads (one round trip per
+// chunk; widening first and sending the two halves through the tile took
+// two: DeepSeek-V2-Lite FP8 shapes on MI355X, see stream_consume).  Token rows are small and cache-resident
 // and are loaded straight in operand layout.  Stages of U chunks are
 // double-buffered in registers, so the next stage's loads are in flight while
 // the current one is multiplied; the next item's first stage is issued before
@@ -68,8 +70,8 @@ struct StreamStage {
 // k order inside a chunk (applied to weights and tokens alike, which leaves
 // the products unchanged): bf16 k-step q of lane group s = lane/16 covers
 // k = 32q + 8s .. +7; FP8 steps 0..3 cover k = 16s, 64 + 16s, 16s + 8 and
-// 64 + 16s + 8 (.. +7), the order in which the widened halves come out of
-// the LDS tile.
+// 64 + 16s + 8 (.. +7): the low and then the high 8 codes of the two 16-code
+// fragments a lane reads from the LDS tile.
 template <int NMAT, int MT, int U, bool F8>
 __device__ __forceinline__ void stream_issue(StreamStage<NMAT, MT, U, F8>& st,
                                              const StreamItem<NMAT, MT>& it, int c_begin,
@@ -133,20 +135,46 @@ __device__ __forceinline__ void stream_consume(const StreamStage<NMAT, MT, U, F8
   for (int u = 0; u < U; ++u) {
     if (!valid || c_begin + u >= c_end) continue;
     u16* buf = lds + (U > 1 ? (u & 1) : 0) * NMAT * 16 * kLdsRow;
-    constexpr int NH = F8 ? 2 : 1;   // FP8: the low then the high 8 codes of each load
+    if constexpr (F8) {
+      // The raw codes go through the tile (each lane's 16 bytes at the place
+      // its 8 widened bf16 values would take) and are widened after the
+      // fragment reads: one LDS round trip per chunk instead of one per half.
+      // Lane l reads codes k = 16 (l/16) .. +15 and 64 + 16 (l/16) .. +15 of
+      // row l % 16; their low 8 codes are k-steps 0 and 1, their high 8
+      // steps 2 and 3 (the order of the token operands), and the MFMAs run
+      // in the same order as when each half went through the tile.
+      u32x4 r[NMAT][2];
 #pragma unroll
-    for (int hf = 0; hf < NH; ++hf) {
+      for (int m = 0; m < NMAT; ++m) {
+        u16* t = buf + m * 16 * kLdsRow;
+        *reinterpret_cast<u32x4*>(t + wr * kLdsRow + wc) = st.w[u][m][0];
+        *reinterpret_cast<u32x4*>(t + (wr + 8) * kLdsRow + wc) = st.w[u][m][1];
+      }
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m) {
+        const u16* t = buf + m * 16 * kLdsRow;
+        r[m][0] = *reinterpret_cast<const u32x4*>(t + fr * kLdsRow + fk);
+        r[m][1] = *reinterpret_cast<const u32x4*>(t + fr * kLdsRow + 32 + fk);
+      }
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) {
+          const u32x4 f0 = e4m3x8_to_bf16(r[m][0][2 * hf], r[m][0][2 * hf + 1]);
+          const u32x4 f1 = e4m3x8_to_bf16(r[m][1][2 * hf], r[m][1][2 * hf + 1]);
+#pragma unroll
+          for (int b = 0; b < MT; ++b) {
+            acc[m][b] = mfma_bf16(f0, st.x[u][b][2 * hf], acc[m][b]);
+            acc[m][b] = mfma_bf16(f1, st.x[u][b][2 * hf + 1], acc[m][b]);
+          }
+        }
+    } else {
       u32x4 f[NMAT][2];
 #pragma unroll
       for (int m = 0; m < NMAT; ++m) {
         u16* t = buf + m * 16 * kLdsRow;
-        u32x4 v0 = st.w[u][m][0], v1 = st.w[u][m][1];
-        if constexpr (F8) {
-          v0 = hf == 0 ? e4m3x8_to_bf16(v0[0], v0[1]) : e4m3x8_to_bf16(v0[2], v0[3]);
-          v1 = hf == 0 ? e4m3x8_to_bf16(v1[0], v1[1]) : e4m3x8_to_bf16(v1[2], v1[3]);
-        }
-        *reinterpret_cast<u32x4*>(t + wr * kLdsRow + wc) = v0;
-        *reinterpret_cast<u32x4*>(t + (wr + 8) * kLdsRow + wc) = v1;
+        *reinterpret_cast<u32x4*>(t + wr * kLdsRow + wc) = st.w[u][m][0];
+        *reinterpret_cast<u32x4*>(t + (wr + 8) * kLdsRow + wc) = st.w[u][m][1];
       }
 #pragma unroll
       for (int m = 0; m < NMAT; ++m) {
@@ -154,13 +182,13 @@ __device__ __forceinline__ void stream_consume(const StreamStage<NMAT, MT, U, F8
         f[m][0] = *reinterpret_cast<const u32x4*>(t + fr * kLdsRow + fk);
         f[m][1] = *reinterpret_cast<const u32x4*>(t + fr * kLdsRow + 32 + fk);
       }
-      // bf16: x steps 0, 1; FP8 half 0: steps 0, 1 (k 16s, 64 + 16s), half 1: 2, 3
+      // x steps 0, 1
 #pragma unroll
       for (int m = 0; m < NMAT; ++m)
 #pragma unroll
         for (int b = 0; b < MT; ++b) {
-          acc[m][b] = mfma_bf16(f[m][0], st.x[u][b][2 * hf], acc[m][b]);
-          acc[m][b] = mfma_bf16(f[m][1], st.x[u][b][2 * hf + 1], acc[m][b]);
+          acc[m][b] = mfma_bf16(f[m][0], st.x[u][b][0], acc[m][b]);
+          acc[m][b] = mfma_bf16(f[m][1], st.x[u][b][1], acc[m][b]);
         }
     }
     chunk_end(c_begin + u);
