@@ -351,6 +351,10 @@ int beam_moe_forward(const beam_moe_layer* layer, const void* x, int32_t T, void
   if ((st = run_routing(*layer, x, T, tile_rows, p, s)) != BEAM_OK) return st;
   if (!select_builds_plan(*layer, T)) BEAM_TRY(launch_scatter(*layer, T, p, s));
   BEAM_TRY(launch_gate_up(*layer, x, T, tile_rows, lay, p, s));
+  if (down_combine_fused(*layer, T)) {
+    BEAM_TRY(launch_down_combine_t1(*layer, p, y, s));
+    return BEAM_OK;
+  }
   BEAM_TRY(launch_down(*layer, T, tile_rows, lay, p, s, /*allow_split=*/true));
   BEAM_TRY(launch_combine(*layer, T, tile_rows, p, y, s));
   return BEAM_OK;

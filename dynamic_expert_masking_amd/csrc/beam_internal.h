@@ -149,6 +149,10 @@ hipError_t launch_gate_up(const beam_moe_layer& L, const void* x, int32_t T, int
 // and passes false.
 hipError_t launch_down(const beam_moe_layer& L, int32_t T, int tile_rows, const WsLayout& w,
                        const Ptrs& p, hipStream_t s, bool allow_split = false);
+// Single-token batches of bf16 layers with intermediate sizes up to 2048:
+// the down product and the combine in one launch (y written directly).
+bool down_combine_fused(const beam_moe_layer& L, int32_t T);
+hipError_t launch_down_combine_t1(const beam_moe_layer& L, const Ptrs& p, void* y, hipStream_t s);
 hipError_t launch_combine(const beam_moe_layer& L, int32_t T, int tile_rows, const Ptrs& p,
                           void* y, hipStream_t s);
 hipError_t launch_copy(void* dst, const void* src, size_t bytes, hipStream_t s);

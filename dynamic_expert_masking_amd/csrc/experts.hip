@@ -1463,6 +1463,149 @@ __global__ __launch_bounds__(256) void k_combine_tok(int T, int D, int K, const 
 }
 
 // ---------------------------------------------------------------------------
+// Single-token batches: the down product and the combine in one launch.
+//
+// With one token every expert's down product is a matrix-vector product, so
+// a workgroup takes kDcRows output rows and every segment of the token --
+// its kept slots in slot order, then the shared experts -- one segment per
+// wave: the wave streams the segment's kDcRows weight rows and its h row
+// with all loads in flight at once, and takes the kDcRows dot products with
+// fp32 sums and fixed-order wave reductions.  The dots meet in LDS, and one
+// wave adds them per row in segment order, each kept slot times its gate
+// (y = sum_k g_k (W_k h_k) + sum_s Ws_s h_s), rounding y once.  Against the
+// streaming down kernel and the combine (O stored in bf16 between them) the
+// result differs only by that rounding.  Segments of at most kDcMaxChunks
+// 16-byte chunks per lane (intermediate sizes up to 2048).
+// ---------------------------------------------------------------------------
+
+constexpr int kDcRows = 8;         // output rows per workgroup
+constexpr int kDcWaves = 8;        // waves per workgroup: segments taken per round
+constexpr int kDcMaxChunks = 4;    // 16-byte chunks of a segment row per lane
+constexpr int kDcMaxShared = 8;
+constexpr int kDcMaxSeg = 32 + kDcMaxShared;
+
+struct DownCombineArgs {
+  const u16* wd;       // [E][D][I]
+  const u16* sd;       // [S][D][Is]
+  const u16* h;        // [P][I], pair order
+  const u16* h_sh;     // [1][S Is]
+  const int32_t* slot_pos;
+  const float* gates;
+  const int32_t* idx;
+  u16* y;
+  int D, I, Is, S, K;
+};
+
+bool down_combine_fused(const beam_moe_layer& L, int32_t T) {
+  return T == 1 && L.dtype == BEAM_BF16 && L.expert_format == BEAM_WEIGHTS_DTYPE &&
+         L.I <= kWave * kDcMaxChunks * 8 && L.n_shared <= kDcMaxShared &&
+         (L.n_shared == 0 || L.I_shared <= kWave * kDcMaxChunks * 8) && L.K <= 32 &&
+         L.D % kDcRows == 0;
+}
+
+__global__ __launch_bounds__(kDcWaves * 64) void k_down_combine_t1(DownCombineArgs a) {
+  __shared__ float s_dot[kDcMaxSeg][kDcRows];
+  __shared__ float s_gate[kDcMaxSeg];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int d0 = blockIdx.x * kDcRows;
+  // the token's slots, lane k < K: pair position (-1: masked), gate, expert
+  int pos = -1, ex = 0;
+  float gt = 0.f;
+  if (lane < a.K) {
+    pos = a.slot_pos[lane];
+    gt = a.gates[lane];
+    ex = a.idx[lane];
+  }
+  const unsigned long long kept = __ballot(pos >= 0);
+  const int nk = __popcll(kept);
+  const int nseg = nk + a.S;
+  const int rank = __popcll(kept & ((1ull << lane) - 1ull));
+  for (int q = wave; q < nseg; q += kDcWaves) {   // wave-uniform
+    const u16* w;
+    const u16* hr;
+    int len;
+    float gq = 1.f;
+    if (q < nk) {   // the q-th kept slot
+      const unsigned long long sel = __ballot(((kept >> lane) & 1ull) && rank == q);
+      const int k = __ffsll(static_cast<unsigned long long>(sel)) - 1;
+      const int ek = __builtin_amdgcn_readlane(ex, k);
+      const int pk = __builtin_amdgcn_readlane(pos, k);
+      gq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gt), k));
+      w = a.wd + (size_t(ek) * a.D + d0) * a.I;
+      hr = a.h + size_t(pk) * a.I;
+      len = a.I;
+    } else {        // shared expert q - nk
+      const int sx = q - nk;
+      w = a.sd + (size_t(sx) * a.D + d0) * a.Is;
+      hr = a.h_sh + size_t(sx) * a.Is;
+      len = a.Is;
+    }
+    const int nch = len / 8;
+    u32x4 hv[kDcMaxChunks], wv[kDcRows][kDcMaxChunks];
+#pragma unroll
+    for (int j = 0; j < kDcMaxChunks; ++j) {   // every load issued before any use
+      const int c = lane + kWave * j;
+      const int cc = c < nch ? c : 0;
+      hv[j] = ld16(hr + size_t(cc) * 8);
+#pragma unroll
+      for (int r = 0; r < kDcRows; ++r) wv[r][j] = ld16_stream(w + size_t(r) * len + size_t(cc) * 8);
+    }
+    float dot[kDcRows];
+#pragma unroll
+    for (int r = 0; r < kDcRows; ++r) dot[r] = 0.f;
+#pragma unroll
+    for (int j = 0; j < kDcMaxChunks; ++j) {
+      if (lane + kWave * j >= nch) continue;   // chunk past the row: no contribution
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float h0 = __uint_as_float(hv[j][i] << 16), h1 = __uint_as_float(hv[j][i] & 0xffff0000u);
+#pragma unroll
+        for (int r = 0; r < kDcRows; ++r) {
+          dot[r] = fmaf(__uint_as_float(wv[r][j][i] << 16), h0, dot[r]);
+          dot[r] = fmaf(__uint_as_float(wv[r][j][i] & 0xffff0000u), h1, dot[r]);
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kDcRows; ++r) {
+      const float v = wave_sum_f32(dot[r]);
+      if (lane == 0) s_dot[q][r] = v;
+    }
+    if (lane == 0) s_gate[q] = gq;
+  }
+  __syncthreads();
+  if (wave == 0 && lane < kDcRows) {
+    float acc = 0.f;
+    for (int q = 0; q < nk; ++q) acc += s_gate[q] * s_dot[q][lane];   // slot order
+    float sh = 0.f;
+    for (int q = nk; q < nseg; ++q) sh += s_dot[q][lane];
+    a.y[d0 + lane] = f32_to_bf16(acc + sh);
+  }
+}
+
+hipError_t launch_down_combine_t1(const beam_moe_layer& L, const Ptrs& p, void* y, hipStream_t s) {
+  DownCombineArgs a;
+  a.wd = static_cast<const u16*>(L.w_down);
+  a.sd = static_cast<const u16*>(L.ws_down);
+  a.h = static_cast<const u16*>(p.h);
+  a.h_sh = static_cast<const u16*>(p.h_shared);
+  a.slot_pos = p.slot_pos;
+  a.gates = p.gates;
+  a.idx = p.idx;
+  a.y = static_cast<u16*>(y);
+  a.D = L.D;
+  a.I = L.I;
+  a.Is = L.I_shared;
+  a.S = L.n_shared;
+  a.K = L.K;
+  prof_before("down_combine", s);
+  hipLaunchKernelGGL(k_down_combine_t1, dim3(unsigned(L.D / kDcRows)), dim3(kDcWaves * 64), 0, s, a);
+  prof_after(s);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 
