@@ -1478,7 +1478,8 @@ __global__ __launch_bounds__(256) void k_combine_tok(int T, int D, int K, const 
 // 16-byte chunks per lane (intermediate sizes up to 2048).
 // ---------------------------------------------------------------------------
 
-constexpr int kDcRows = 8;         // output rows per workgroup
+constexpr int kDcRows = 4;         // output rows per workgroup (DeepSeek-V2-Lite shapes, step
+                                   // us on MI355X: 2 rows 31.9, 4 rows 30.6, 8 rows 31.5, 16 rows 37.3)
 constexpr int kDcWaves = 8;        // waves per workgroup: segments taken per round
 constexpr int kDcMaxChunks = 4;    // 16-byte chunks of a segment row per lane
 constexpr int kDcMaxShared = 8;
