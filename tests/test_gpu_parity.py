@@ -352,6 +352,38 @@ def test_all_masked(shared):
         assert np.all(y == 0.0)
 
 
+# Single-token batches of bf16 layers with intermediate sizes up to 2048 take
+# the fused down+combine kernel: row counts of 64 (one chunk in a quarter of
+# the lanes) to 2048 (four chunks in every lane), 0-8 shared experts, K up to
+# 32, and tokens with every slot masked.
+T1_CASES = [dict(D=256, E=16, K=4, I=64, S=0, I_s=0), dict(D=512, E=12, K=3, I=2048, S=1, I_s=2048),
+            dict(D=128, E=40, K=32, I=192, S=2, I_s=64), dict(D=1024, E=64, K=6, I=1408, S=8, I_s=128),
+            dict(D=64, E=5, K=5, I=320, S=3, I_s=1984)]
+
+
+@pytest.mark.parametrize("case", range(len(T1_CASES)))
+@pytest.mark.parametrize("masked", [False, True])
+def test_single_token_fused_down(case, masked):
+    """T = 1: routing exact, y against the oracle on many single tokens
+    (each its own batch), including batches where nothing survives."""
+    kw = T1_CASES[case]
+    base = small_layer(f"t1fused{case}", **kw, keep=0.5, router_bias=True)
+    layer = with_mask(base, b_mask=-1e4) if masked else base
+    dl = device_layer(layer)
+    note(f"[single token] case={case} masked={masked} {kw}")
+    for i in range(6):
+        x = small_x(base, 1, f"t1_{i}")
+        y, rt, ys = run_forward(dl, x, reps=2)
+        assert np.array_equal(ys[0], ys[1]), "two identical calls gave different y"
+        rt_ref = oracle.route(layer, x)
+        check_routing(rt, rt_ref, kw["E"])
+        if masked and kw["S"] == 0:
+            assert np.all(y == 0.0)
+            continue
+        _, y_ref = oracle.forward(layer, x)
+        check_output(y, y_ref, "bf16")
+
+
 @pytest.mark.parametrize("E,K", [(7, 1), (8, 8), (64, 32), (300, 12), (1024, 3)])
 def test_k_extremes(E, K):
     layer = small_layer(f"gpu_k{E}_{K}", D=128, E=E, K=K, I=64, keep=0.5)
