@@ -149,8 +149,9 @@ hipError_t launch_gate_up(const beam_moe_layer& L, const void* x, int32_t T, int
 // and passes false.
 hipError_t launch_down(const beam_moe_layer& L, int32_t T, int tile_rows, const WsLayout& w,
                        const Ptrs& p, hipStream_t s, bool allow_split = false);
-// Single-token batches of bf16 layers with intermediate sizes up to 2048:
-// the down product and the combine in one launch (y written directly).
+// Single-token batches of bf16 layers with intermediate sizes up to 2048
+// (4096 with FP8 expert weights): the down product and the combine in one
+// launch (y written directly).
 bool down_combine_fused(const beam_moe_layer& L, int32_t T);
 hipError_t launch_down_combine_t1(const beam_moe_layer& L, const Ptrs& p, void* y, hipStream_t s);
 hipError_t launch_combine(const beam_moe_layer& L, int32_t T, int tile_rows, const Ptrs& p,

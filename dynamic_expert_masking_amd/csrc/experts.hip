@@ -1475,7 +1475,8 @@ __global__ __launch_bounds__(256) void k_combine_tok(int T, int D, int K, const 
 // (y = sum_k g_k (W_k h_k) + sum_s Ws_s h_s), rounding y once.  Against the
 // streaming down kernel and the combine (O stored in bf16 between them) the
 // result differs only by that rounding.  Segments of at most kDcMaxChunks
-// 16-byte chunks per lane (intermediate sizes up to 2048).
+// 16-byte chunks per lane (intermediate sizes up to 2048 for bf16 weights,
+// 4096 for FP8 ones).
 // ---------------------------------------------------------------------------
 
 constexpr int kDcRows = 4;         // output rows per workgroup (DeepSeek-V2-Lite shapes, step
@@ -1486,8 +1487,10 @@ constexpr int kDcMaxShared = 8;
 constexpr int kDcMaxSeg = 32 + kDcMaxShared;
 
 struct DownCombineArgs {
-  const u16* wd;       // [E][D][I]
-  const u16* sd;       // [S][D][Is]
+  const void* wd;      // [E][D][I]: bf16, or E4M3 codes
+  const void* sd;      // [S][D][Is]
+  const float* qd;     // FP8: scale of each output row [E][D] (else null)
+  const float* qsd;    // FP8: [S][D]
   const u16* h;        // [P][I], pair order
   const u16* h_sh;     // [1][S Is]
   const int32_t* slot_pos;
@@ -1497,14 +1500,23 @@ struct DownCombineArgs {
   int D, I, Is, S, K;
 };
 
+// Weight elements per 16-byte chunk.
+template <bool F8>
+constexpr int dc_chunk() { return F8 ? 16 : 8; }
+
 bool down_combine_fused(const beam_moe_layer& L, int32_t T) {
-  return T == 1 && L.dtype == BEAM_BF16 && L.expert_format == BEAM_WEIGHTS_DTYPE &&
-         L.I <= kWave * kDcMaxChunks * 8 && L.n_shared <= kDcMaxShared &&
-         (L.n_shared == 0 || L.I_shared <= kWave * kDcMaxChunks * 8) && L.K <= 32 &&
-         L.D % kDcRows == 0;
+  const bool f8 = L.expert_format == BEAM_WEIGHTS_FP8_E4M3;
+  const long rows_max = long(kWave) * kDcMaxChunks * (f8 ? 16 : 8);
+  return T == 1 && L.dtype == BEAM_BF16 && L.I <= rows_max && L.n_shared <= kDcMaxShared &&
+         (L.n_shared == 0 || L.I_shared <= rows_max) && L.K <= 32 && L.D % kDcRows == 0;
 }
 
+// FP8: a chunk holds 16 codes, widened exactly to bf16 in registers; each
+// weight row's dot is multiplied by the row's scale before it leaves the wave.
+template <bool F8>
 __global__ __launch_bounds__(kDcWaves * 64) void k_down_combine_t1(DownCombineArgs a) {
+  constexpr int CK = dc_chunk<F8>();
+  constexpr int HL = F8 ? 2 : 1;   // 16-byte loads of h per chunk
   __shared__ float s_dot[kDcMaxSeg][kDcRows];
   __shared__ float s_gate[kDcMaxSeg];
   const int lane = threadIdx.x & 63;
@@ -1523,8 +1535,9 @@ __global__ __launch_bounds__(kDcWaves * 64) void k_down_combine_t1(DownCombineAr
   const int nseg = nk + a.S;
   const int rank = __popcll(kept & ((1ull << lane) - 1ull));
   for (int q = wave; q < nseg; q += kDcWaves) {   // wave-uniform
-    const u16* w;
+    const unsigned char* w;
     const u16* hr;
+    const float* sc = nullptr;   // FP8: scales of this segment's rows d0 ..
     int len;
     float gq = 1.f;
     if (q < nk) {   // the q-th kept slot
@@ -1533,24 +1546,28 @@ __global__ __launch_bounds__(kDcWaves * 64) void k_down_combine_t1(DownCombineAr
       const int ek = __builtin_amdgcn_readlane(ex, k);
       const int pk = __builtin_amdgcn_readlane(pos, k);
       gq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gt), k));
-      w = a.wd + (size_t(ek) * a.D + d0) * a.I;
+      w = static_cast<const unsigned char*>(a.wd) + (size_t(ek) * a.D + d0) * a.I * (F8 ? 1 : 2);
       hr = a.h + size_t(pk) * a.I;
+      if (F8) sc = a.qd + size_t(ek) * a.D + d0;
       len = a.I;
     } else {        // shared expert q - nk
       const int sx = q - nk;
-      w = a.sd + (size_t(sx) * a.D + d0) * a.Is;
+      w = static_cast<const unsigned char*>(a.sd) + (size_t(sx) * a.D + d0) * a.Is * (F8 ? 1 : 2);
       hr = a.h_sh + size_t(sx) * a.Is;
+      if (F8) sc = a.qsd + size_t(sx) * a.D + d0;
       len = a.Is;
     }
-    const int nch = len / 8;
-    u32x4 hv[kDcMaxChunks], wv[kDcRows][kDcMaxChunks];
+    const size_t row_bytes = size_t(len) * (F8 ? 1 : 2);
+    const int nch = len / CK;
+    u32x4 hv[kDcMaxChunks][HL], wv[kDcRows][kDcMaxChunks];
 #pragma unroll
     for (int j = 0; j < kDcMaxChunks; ++j) {   // every load issued before any use
       const int c = lane + kWave * j;
       const int cc = c < nch ? c : 0;
-      hv[j] = ld16(hr + size_t(cc) * 8);
 #pragma unroll
-      for (int r = 0; r < kDcRows; ++r) wv[r][j] = ld16_stream(w + size_t(r) * len + size_t(cc) * 8);
+      for (int u = 0; u < HL; ++u) hv[j][u] = ld16(hr + size_t(cc) * CK + 8 * u);
+#pragma unroll
+      for (int r = 0; r < kDcRows; ++r) wv[r][j] = ld16_stream(w + r * row_bytes + size_t(cc) * 16);
     }
     float dot[kDcRows];
 #pragma unroll
@@ -1559,18 +1576,24 @@ __global__ __launch_bounds__(kDcWaves * 64) void k_down_combine_t1(DownCombineAr
     for (int j = 0; j < kDcMaxChunks; ++j) {
       if (lane + kWave * j >= nch) continue;   // chunk past the row: no contribution
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float h0 = __uint_as_float(hv[j][i] << 16), h1 = __uint_as_float(hv[j][i] & 0xffff0000u);
+      for (int u = 0; u < HL; ++u)
 #pragma unroll
         for (int r = 0; r < kDcRows; ++r) {
-          dot[r] = fmaf(__uint_as_float(wv[r][j][i] << 16), h0, dot[r]);
-          dot[r] = fmaf(__uint_as_float(wv[r][j][i] & 0xffff0000u), h1, dot[r]);
+          // this chunk's 8 weights that meet h values 8u .. 8u + 7, as bf16
+          const u32x4 wb = F8 ? e4m3x8_to_bf16(wv[r][j][2 * u], wv[r][j][2 * u + 1]) : wv[r][j];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float h0 = __uint_as_float(hv[j][u][i] << 16);
+            const float h1 = __uint_as_float(hv[j][u][i] & 0xffff0000u);
+            dot[r] = fmaf(__uint_as_float(wb[i] << 16), h0, dot[r]);
+            dot[r] = fmaf(__uint_as_float(wb[i] & 0xffff0000u), h1, dot[r]);
+          }
         }
-      }
     }
 #pragma unroll
     for (int r = 0; r < kDcRows; ++r) {
-      const float v = wave_sum_f32(dot[r]);
+      float v = wave_sum_f32(dot[r]);
+      if (F8) v *= sc[r];
       if (lane == 0) s_dot[q][r] = v;
     }
     if (lane == 0) s_gate[q] = gq;
@@ -1587,8 +1610,10 @@ __global__ __launch_bounds__(kDcWaves * 64) void k_down_combine_t1(DownCombineAr
 
 hipError_t launch_down_combine_t1(const beam_moe_layer& L, const Ptrs& p, void* y, hipStream_t s) {
   DownCombineArgs a;
-  a.wd = static_cast<const u16*>(L.w_down);
-  a.sd = static_cast<const u16*>(L.ws_down);
+  a.wd = L.w_down;
+  a.sd = L.ws_down;
+  a.qd = L.scale_down;
+  a.qsd = L.scale_shared_down;
   a.h = static_cast<const u16*>(p.h);
   a.h_sh = static_cast<const u16*>(p.h_shared);
   a.slot_pos = p.slot_pos;
@@ -1600,8 +1625,14 @@ hipError_t launch_down_combine_t1(const beam_moe_layer& L, const Ptrs& p, void* 
   a.Is = L.I_shared;
   a.S = L.n_shared;
   a.K = L.K;
-  prof_before("down_combine", s);
-  hipLaunchKernelGGL(k_down_combine_t1, dim3(unsigned(L.D / kDcRows)), dim3(kDcWaves * 64), 0, s, a);
+  const dim3 grid(unsigned(L.D / kDcRows)), block(kDcWaves * 64);
+  if (L.expert_format == BEAM_WEIGHTS_FP8_E4M3) {
+    prof_before("down_combine_fp8", s);
+    hipLaunchKernelGGL(k_down_combine_t1<true>, grid, block, 0, s, a);
+  } else {
+    prof_before("down_combine", s);
+    hipLaunchKernelGGL(k_down_combine_t1<false>, grid, block, 0, s, a);
+  }
   prof_after(s);
   return hipGetLastError();
 }

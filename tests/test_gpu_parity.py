@@ -361,6 +361,27 @@ T1_CASES = [dict(D=256, E=16, K=4, I=64, S=0, I_s=0), dict(D=512, E=12, K=3, I=2
             dict(D=64, E=5, K=5, I=320, S=3, I_s=1984)]
 
 
+T1_FP8_CASES = [dict(D=256, E=16, K=4, I=128, S=0, I_s=0), dict(D=512, E=12, K=3, I=4096, S=1, I_s=4096),
+                dict(D=128, E=40, K=8, I=384, S=2, I_s=128)]
+
+
+@pytest.mark.parametrize("case", range(len(T1_FP8_CASES)))
+def test_single_token_fused_down_fp8(case):
+    """T = 1 with E4M3 expert weights and row scales perturbed by 2^+-6: the
+    fused kernel widens the codes and applies each row's scale."""
+    from oracle_pins import fp8_layer
+    kw = T1_FP8_CASES[case]
+    layer = _fp8_scaled(fp8_layer(f"t1fp8{case}", **kw, keep=0.5, router_bias=True), 11 + case)
+    dl = device_layer(layer)
+    note(f"[single token fp8] case={case} {kw}")
+    for i in range(6):
+        x = small_x(layer, 1, f"t1f_{i}")
+        y, rt, _ = run_forward(dl, x)
+        check_routing(rt, oracle.route(layer, x), kw["E"])
+        _, y_ref = oracle.forward(layer, x)
+        check_output(y, y_ref, "bf16")
+
+
 @pytest.mark.parametrize("case", range(len(T1_CASES)))
 @pytest.mark.parametrize("masked", [False, True])
 def test_single_token_fused_down(case, masked):
