@@ -920,18 +920,24 @@ hipError_t launch_select(const beam_moe_layer& L, int32_t T, int tile_rows, cons
   if (T <= kSelMergedMax) {
     prof_before("select_plan", s);
     // one wave per token: a single wave for one token, 4 waves for up to 4
-    // tokens (fewer waves at each barrier), else 16 (T = 1, DeepSeek-V2-Lite
-    // shapes: select+plan 7.35 -> 6.74 us, step 35.8 -> 35.3 us on MI355X
-    // with one wave instead of four)
-    auto go = [&](auto k1, auto k4, auto k16) {
+    // tokens, 8 for up to 8 (fewer waves at each barrier), else 16 (T = 1,
+    // DeepSeek-V2-Lite shapes: select+plan 7.35 -> 6.74 us, step 35.8 -> 35.3
+    // us on MI355X with one wave instead of four; T = 8: 8.2 -> 7.9 us with
+    // 8 waves instead of 16)
+    auto go = [&](auto k1, auto k4, auto k8, auto k16) {
       if (T == 1) hipLaunchKernelGGL(k1, dim3(1), dim3(64), 0, s, a);
       else if (T <= 4) hipLaunchKernelGGL(k4, dim3(1), dim3(256), 0, s, a);
+      else if (T <= 8) hipLaunchKernelGGL(k8, dim3(1), dim3(512), 0, s, a);
       else hipLaunchKernelGGL(k16, dim3(1), dim3(1024), 0, s, a);
     };
-    if (L.E <= 64) go(k_select_plan<1, 64>, k_select_plan<1, 256>, k_select_plan<1, 1024>);
-    else if (L.E <= 128) go(k_select_plan<2, 64>, k_select_plan<2, 256>, k_select_plan<2, 1024>);
-    else if (L.E <= 256) go(k_select_plan<4, 64>, k_select_plan<4, 256>, k_select_plan<4, 1024>);
-    else go(k_select_plan<16, 64>, k_select_plan<16, 256>, k_select_plan<16, 1024>);
+    if (L.E <= 64)
+      go(k_select_plan<1, 64>, k_select_plan<1, 256>, k_select_plan<1, 512>, k_select_plan<1, 1024>);
+    else if (L.E <= 128)
+      go(k_select_plan<2, 64>, k_select_plan<2, 256>, k_select_plan<2, 512>, k_select_plan<2, 1024>);
+    else if (L.E <= 256)
+      go(k_select_plan<4, 64>, k_select_plan<4, 256>, k_select_plan<4, 512>, k_select_plan<4, 1024>);
+    else
+      go(k_select_plan<16, 64>, k_select_plan<16, 256>, k_select_plan<16, 512>, k_select_plan<16, 1024>);
     prof_after(s);
     return hipGetLastError();
   }
