@@ -350,7 +350,8 @@ int beam_moe_forward(const beam_moe_layer* layer, const void* x, int32_t T, void
   const int tile_rows = expert_tile_rows(*layer, T);
   if ((st = run_routing(*layer, x, T, tile_rows, p, s)) != BEAM_OK) return st;
   if (!select_builds_plan(*layer, T)) BEAM_TRY(launch_scatter(*layer, T, p, s));
-  BEAM_TRY(launch_gate_up(*layer, x, T, tile_rows, lay, p, s));
+  if (gate_up_t1(*layer, T)) BEAM_TRY(launch_gate_up_t1(*layer, x, p, s));
+  else BEAM_TRY(launch_gate_up(*layer, x, T, tile_rows, lay, p, s));
   if (down_combine_fused(*layer, T)) {
     BEAM_TRY(launch_down_combine_t1(*layer, p, y, s));
     return BEAM_OK;

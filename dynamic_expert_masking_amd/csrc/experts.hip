@@ -1608,6 +1608,137 @@ __global__ __launch_bounds__(kDcWaves * 64) void k_down_combine_t1(DownCombineAr
   }
 }
 
+// Single-token batches, gate/up and SwiGLU (bf16 weights, d_model up to
+// 2048): each expert's gate and up products are matrix-vector products too.
+// A workgroup takes kGuRows intermediate rows of every segment -- the kept
+// slots, then each shared expert -- one segment per wave: the wave issues
+// every load of the segment's kGuRows gate and up rows and of the token's x
+// row at once, forms the dots in fp32 with fixed-order wave reductions, and
+// writes h = silu(g) * u (rounded to bf16 once) for those rows, where the
+// down product reads it (pair order; the shared experts' [S Is] row).
+// One row per wave measured fastest: at four rows a workgroup's registers
+// left one workgroup resident per compute unit and the grid ran in two
+// uneven waves.
+constexpr int kGuRows = 1;
+
+struct GateUpT1Args {
+  const u16* x;
+  const u16* wg;   // [E][I][D]
+  const u16* wu;
+  const u16* sg;   // [S Is][D]
+  const u16* su;
+  const int32_t* slot_pos;
+  const int32_t* idx;
+  u16* h;          // [P][I]
+  u16* h_sh;       // [1][S Is]
+  int D, I, Is, S, K;
+};
+
+bool gate_up_t1(const beam_moe_layer& L, int32_t T) {
+  return down_combine_fused(L, T) && L.expert_format == BEAM_WEIGHTS_DTYPE && L.D % 8 == 0 &&
+         L.D <= kWave * kDcMaxChunks * 8 && L.I % kGuRows == 0 &&
+         (L.n_shared == 0 || L.I_shared % kGuRows == 0);
+}
+
+__global__ __launch_bounds__(kDcWaves * 64) void k_gate_up_t1(GateUpT1Args a) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r0 = blockIdx.x * kGuRows;
+  int pos = -1, ex = 0;
+  if (lane < a.K) {
+    pos = a.slot_pos[lane];
+    ex = a.idx[lane];
+  }
+  const unsigned long long kept = __ballot(pos >= 0);
+  const int nk = __popcll(kept);
+  const int nseg = nk + a.S;
+  const int rank = __popcll(kept & ((1ull << lane) - 1ull));
+  const int nch = a.D / 8;
+  for (int q = wave; q < nseg; q += kDcWaves) {   // wave-uniform
+    const u16* g;
+    const u16* u;
+    u16* hr;
+    if (q < nk) {   // the q-th kept slot
+      if (r0 >= a.I) continue;
+      const unsigned long long sel = __ballot(((kept >> lane) & 1ull) && rank == q);
+      const int k = __ffsll(static_cast<unsigned long long>(sel)) - 1;
+      const int ek = __builtin_amdgcn_readlane(ex, k);
+      const int pk = __builtin_amdgcn_readlane(pos, k);
+      g = a.wg + (size_t(ek) * a.I + r0) * a.D;
+      u = a.wu + (size_t(ek) * a.I + r0) * a.D;
+      hr = a.h + size_t(pk) * a.I + r0;
+    } else {        // shared expert q - nk: rows sx Is + r0 .. of the fused matrices
+      if (r0 >= a.Is) continue;
+      const int sx = q - nk;
+      g = a.sg + (size_t(sx) * a.Is + r0) * a.D;
+      u = a.su + (size_t(sx) * a.Is + r0) * a.D;
+      hr = a.h_sh + size_t(sx) * a.Is + r0;
+    }
+    u32x4 xv[kDcMaxChunks], gv[kGuRows][kDcMaxChunks], uv[kGuRows][kDcMaxChunks];
+#pragma unroll
+    for (int j = 0; j < kDcMaxChunks; ++j) {   // every load issued before any use
+      const int c = lane + kWave * j;
+      const size_t cc = size_t(c < nch ? c : 0) * 8;
+      xv[j] = ld16(a.x + cc);
+#pragma unroll
+      for (int r = 0; r < kGuRows; ++r) {
+        gv[r][j] = ld16_stream(g + size_t(r) * a.D + cc);
+        uv[r][j] = ld16_stream(u + size_t(r) * a.D + cc);
+      }
+    }
+    float dg[kGuRows], du[kGuRows];
+#pragma unroll
+    for (int r = 0; r < kGuRows; ++r) dg[r] = du[r] = 0.f;
+#pragma unroll
+    for (int j = 0; j < kDcMaxChunks; ++j) {
+      if (lane + kWave * j >= nch) continue;   // chunk past the row: no contribution
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float x0 = __uint_as_float(xv[j][i] << 16), x1 = __uint_as_float(xv[j][i] & 0xffff0000u);
+#pragma unroll
+        for (int r = 0; r < kGuRows; ++r) {
+          dg[r] = fmaf(__uint_as_float(gv[r][j][i] << 16), x0, dg[r]);
+          dg[r] = fmaf(__uint_as_float(gv[r][j][i] & 0xffff0000u), x1, dg[r]);
+          du[r] = fmaf(__uint_as_float(uv[r][j][i] << 16), x0, du[r]);
+          du[r] = fmaf(__uint_as_float(uv[r][j][i] & 0xffff0000u), x1, du[r]);
+        }
+      }
+    }
+    u16 hv[kGuRows];
+#pragma unroll
+    for (int r = 0; r < kGuRows; ++r) hv[r] = f32_to_bf16(silu_f32(wave_sum_f32(dg[r])) * wave_sum_f32(du[r]));
+    if (lane < kGuRows) {
+      u16 v = hv[0];
+#pragma unroll
+      for (int r = 1; r < kGuRows; ++r) v = lane == r ? hv[r] : v;
+      hr[lane] = v;
+    }
+  }
+}
+
+hipError_t launch_gate_up_t1(const beam_moe_layer& L, const void* x, const Ptrs& p, hipStream_t s) {
+  GateUpT1Args a;
+  a.x = static_cast<const u16*>(x);
+  a.wg = static_cast<const u16*>(L.w_gate);
+  a.wu = static_cast<const u16*>(L.w_up);
+  a.sg = static_cast<const u16*>(L.ws_gate);
+  a.su = static_cast<const u16*>(L.ws_up);
+  a.slot_pos = p.slot_pos;
+  a.idx = p.idx;
+  a.h = static_cast<u16*>(p.h);
+  a.h_sh = static_cast<u16*>(p.h_shared);
+  a.D = L.D;
+  a.I = L.I;
+  a.Is = L.I_shared;
+  a.S = L.n_shared;
+  a.K = L.K;
+  const int rows = std::max(L.I, L.n_shared > 0 ? L.I_shared : 0);
+  prof_before("gate_up_swiglu_t1", s);
+  hipLaunchKernelGGL(k_gate_up_t1, dim3(unsigned(rows / kGuRows)), dim3(kDcWaves * 64), 0, s, a);
+  prof_after(s);
+  return hipGetLastError();
+}
+
 hipError_t launch_down_combine_t1(const beam_moe_layer& L, const Ptrs& p, void* y, hipStream_t s) {
   DownCombineArgs a;
   a.wd = L.w_down;
