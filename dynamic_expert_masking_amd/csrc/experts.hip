@@ -1610,17 +1610,16 @@ __global__ __launch_bounds__(kDcWaves * 64) void k_down_combine_t1(DownCombineAr
 
 // Single-token batches, gate/up and SwiGLU (bf16 weights, d_model up to
 // 2048): each expert's gate and up products are matrix-vector products too.
-// A workgroup takes kGuRows intermediate rows of every segment -- the kept
-// slots, then each shared expert -- one segment per wave: the wave issues
-// every load of the segment's kGuRows gate and up rows and of the token's x
-// row at once, forms the dots in fp32 with fixed-order wave reductions, and
-// writes h = silu(g) * u (rounded to bf16 once) for those rows, where the
-// down product reads it (pair order; the shared experts' [S Is] row).
-// One row per wave measured fastest: at four rows a workgroup's registers
-// left one workgroup resident per compute unit and the grid ran in two
-// uneven waves.
-constexpr int kGuRows = 1;
-
+// A workgroup takes one intermediate row of every segment -- the kept slots,
+// then each shared expert -- one segment per wave: the wave issues the
+// segment's gate and up rows and the token's x row at once, forms both dots
+// in fp32 with fixed-order wave reductions, and writes h = silu(g) * u
+// (rounded to bf16 once) where the down product reads it (pair order; the
+// shared experts' [S Is] row). One row per workgroup measured fastest: at
+// four rows a workgroup's registers left one workgroup resident per compute
+// unit and the grid ran in two uneven waves. Staging x in LDS once per
+// workgroup did not help; with FP8 weights (half the bytes per row) this form
+// lost to the streaming kernel, so FP8 layers keep that one.
 struct GateUpT1Args {
   const u16* x;
   const u16* wg;   // [E][I][D]
@@ -1636,14 +1635,13 @@ struct GateUpT1Args {
 
 bool gate_up_t1(const beam_moe_layer& L, int32_t T) {
   return down_combine_fused(L, T) && L.expert_format == BEAM_WEIGHTS_DTYPE && L.D % 8 == 0 &&
-         L.D <= kWave * kDcMaxChunks * 8 && L.I % kGuRows == 0 &&
-         (L.n_shared == 0 || L.I_shared % kGuRows == 0);
+         L.D <= kWave * kDcMaxChunks * 8;
 }
 
 __global__ __launch_bounds__(kDcWaves * 64) void k_gate_up_t1(GateUpT1Args a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r0 = blockIdx.x * kGuRows;
+  const int row = blockIdx.x;
   int pos = -1, ex = 0;
   if (lane < a.K) {
     pos = a.slot_pos[lane];
@@ -1659,60 +1657,45 @@ __global__ __launch_bounds__(kDcWaves * 64) void k_gate_up_t1(GateUpT1Args a) {
     const u16* u;
     u16* hr;
     if (q < nk) {   // the q-th kept slot
-      if (r0 >= a.I) continue;
+      if (row >= a.I) continue;
       const unsigned long long sel = __ballot(((kept >> lane) & 1ull) && rank == q);
       const int k = __ffsll(static_cast<unsigned long long>(sel)) - 1;
       const int ek = __builtin_amdgcn_readlane(ex, k);
       const int pk = __builtin_amdgcn_readlane(pos, k);
-      g = a.wg + (size_t(ek) * a.I + r0) * a.D;
-      u = a.wu + (size_t(ek) * a.I + r0) * a.D;
-      hr = a.h + size_t(pk) * a.I + r0;
-    } else {        // shared expert q - nk: rows sx Is + r0 .. of the fused matrices
-      if (r0 >= a.Is) continue;
-      const int sx = q - nk;
-      g = a.sg + (size_t(sx) * a.Is + r0) * a.D;
-      u = a.su + (size_t(sx) * a.Is + r0) * a.D;
-      hr = a.h_sh + size_t(sx) * a.Is + r0;
+      g = a.wg + (size_t(ek) * a.I + row) * a.D;
+      u = a.wu + (size_t(ek) * a.I + row) * a.D;
+      hr = a.h + size_t(pk) * a.I + row;
+    } else {        // shared expert q - nk: row sx Is + row of the fused matrices
+      if (row >= a.Is) continue;
+      const size_t wrow = size_t(q - nk) * a.Is + row;
+      g = a.sg + wrow * a.D;
+      u = a.su + wrow * a.D;
+      hr = a.h_sh + wrow;
     }
-    u32x4 xv[kDcMaxChunks], gv[kGuRows][kDcMaxChunks], uv[kGuRows][kDcMaxChunks];
+    u32x4 xv[kDcMaxChunks], gv[kDcMaxChunks], uv[kDcMaxChunks];
 #pragma unroll
     for (int j = 0; j < kDcMaxChunks; ++j) {   // every load issued before any use
       const int c = lane + kWave * j;
       const size_t cc = size_t(c < nch ? c : 0) * 8;
       xv[j] = ld16(a.x + cc);
-#pragma unroll
-      for (int r = 0; r < kGuRows; ++r) {
-        gv[r][j] = ld16_stream(g + size_t(r) * a.D + cc);
-        uv[r][j] = ld16_stream(u + size_t(r) * a.D + cc);
-      }
+      gv[j] = ld16_stream(g + cc);
+      uv[j] = ld16_stream(u + cc);
     }
-    float dg[kGuRows], du[kGuRows];
-#pragma unroll
-    for (int r = 0; r < kGuRows; ++r) dg[r] = du[r] = 0.f;
+    float dg = 0.f, du = 0.f;
 #pragma unroll
     for (int j = 0; j < kDcMaxChunks; ++j) {
       if (lane + kWave * j >= nch) continue;   // chunk past the row: no contribution
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float x0 = __uint_as_float(xv[j][i] << 16), x1 = __uint_as_float(xv[j][i] & 0xffff0000u);
-#pragma unroll
-        for (int r = 0; r < kGuRows; ++r) {
-          dg[r] = fmaf(__uint_as_float(gv[r][j][i] << 16), x0, dg[r]);
-          dg[r] = fmaf(__uint_as_float(gv[r][j][i] & 0xffff0000u), x1, dg[r]);
-          du[r] = fmaf(__uint_as_float(uv[r][j][i] << 16), x0, du[r]);
-          du[r] = fmaf(__uint_as_float(uv[r][j][i] & 0xffff0000u), x1, du[r]);
-        }
+        dg = fmaf(__uint_as_float(gv[j][i] << 16), x0, dg);
+        dg = fmaf(__uint_as_float(gv[j][i] & 0xffff0000u), x1, dg);
+        du = fmaf(__uint_as_float(uv[j][i] << 16), x0, du);
+        du = fmaf(__uint_as_float(uv[j][i] & 0xffff0000u), x1, du);
       }
     }
-    u16 hv[kGuRows];
-#pragma unroll
-    for (int r = 0; r < kGuRows; ++r) hv[r] = f32_to_bf16(silu_f32(wave_sum_f32(dg[r])) * wave_sum_f32(du[r]));
-    if (lane < kGuRows) {
-      u16 v = hv[0];
-#pragma unroll
-      for (int r = 1; r < kGuRows; ++r) v = lane == r ? hv[r] : v;
-      hr[lane] = v;
-    }
+    const float gs = wave_sum_f32(dg), us = wave_sum_f32(du);
+    if (lane == 0) *hr = f32_to_bf16(silu_f32(gs) * us);
   }
 }
 
@@ -1732,9 +1715,9 @@ hipError_t launch_gate_up_t1(const beam_moe_layer& L, const void* x, const Ptrs&
   a.Is = L.I_shared;
   a.S = L.n_shared;
   a.K = L.K;
-  const int rows = std::max(L.I, L.n_shared > 0 ? L.I_shared : 0);
+  const unsigned rows = unsigned(std::max(L.I, L.n_shared > 0 ? L.I_shared : 0));
   prof_before("gate_up_swiglu_t1", s);
-  hipLaunchKernelGGL(k_gate_up_t1, dim3(unsigned(rows / kGuRows)), dim3(kDcWaves * 64), 0, s, a);
+  hipLaunchKernelGGL(k_gate_up_t1, dim3(rows), dim3(kDcWaves * 64), 0, s, a);
   prof_after(s);
   return hipGetLastError();
 }
