@@ -223,8 +223,45 @@ __global__ __launch_bounds__(256) void k_router_f32(RouterArgsF32 a) {
   a.part[size_t(t) * R + j] = s;
 }
 
+// One token, bf16, d_model up to 4096 (a multiple of 8): the 2E logits are
+// matrix-vector products. One wave per router row: it issues every 16-byte
+// chunk of its row and of x at once, sums in fp32 and reduces over the wave
+// in a fixed order; the logits land unsplit (KS = 1).
+bool router_t1(const beam_moe_layer& L, int32_t T) {
+  return T == 1 && L.dtype == BEAM_BF16 && L.D % 8 == 0 && L.D <= kWave * 8 * 8;
+}
+
+template <int NJ>   // 16-byte chunks per lane: D <= 512 NJ
+__global__ __launch_bounds__(256) void k_router_t1(RouterArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (j >= 2 * a.E) return;   // wave-uniform
+  const u16* w = router_row(a, j);
+  const int nch = a.D / 8;
+  u32x4 xv[NJ], wv[NJ];
+#pragma unroll
+  for (int q = 0; q < NJ; ++q) {
+    const int c = lane + kWave * q;
+    const size_t cc = size_t(c < nch ? c : 0) * 8;
+    xv[q] = ld16(a.x + cc);
+    wv[q] = ld16_stream(w + cc);
+  }
+  float d = 0.f;
+#pragma unroll
+  for (int q = 0; q < NJ; ++q) {
+    if (lane + kWave * q >= nch) continue;   // chunk past the row: no contribution
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      d = fmaf(__uint_as_float(wv[q][i] << 16), __uint_as_float(xv[q][i] << 16), d);
+      d = fmaf(__uint_as_float(wv[q][i] & 0xffff0000u), __uint_as_float(xv[q][i] & 0xffff0000u), d);
+    }
+  }
+  d = wave_sum_f32(d);
+  if (lane == 0) a.part[j] = d;
+}
+
 int router_ksplit(const beam_moe_layer& L, int32_t T) {
-  if (L.dtype == BEAM_F32 || !router_use_skinny(T, L.E)) return 1;
+  if (L.dtype == BEAM_F32 || router_t1(L, T) || !router_use_skinny(T, L.E)) return 1;
   // Split k (at most 4 ways, so that selection reads at most 4 partial sums
   // per logit) when the (row block x token block) grid is small.
   const int chunks = L.D / 64;
@@ -253,7 +290,13 @@ hipError_t launch_router_logits(const beam_moe_layer& L, const void* x, int32_t 
   const int KS = router_ksplit(L, T);
   if (long(KS) * T > router_logit_rows(L, T)) return hipErrorInvalidValue;   // workspace bound
   RouterArgs a{(const u16*)x, (const u16*)L.w_router, (const u16*)L.w_mask, part, T, L.D, L.E, KS};
-  if (router_use_skinny(T, L.E)) {
+  if (router_t1(L, T)) {
+    const dim3 grid(unsigned((2 * L.E + 3) / 4));
+    prof_before("router_logits_t1", s);
+    if (L.D <= kWave * 8 * 4) hipLaunchKernelGGL(k_router_t1<4>, grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(k_router_t1<8>, grid, dim3(256), 0, s, a);
+    prof_after(s);
+  } else if (router_use_skinny(T, L.E)) {
     const int nm = router_nm(T, L.E), mt = router_mt(T, L.E);
     const int nrb = (2 * L.E + 16 * nm - 1) / (16 * nm);
     const int ntb = (T + 16 * mt - 1) / (16 * mt);
