@@ -454,11 +454,30 @@ def test_topk_ties(E, K, T):
     check_output(y, y_ref, "bf16")
 
 
+@pytest.mark.parametrize("E,K", [(7, 1), (40, 7), (212, 16), (700, 5), (1024, 3)])
+def test_single_token_ties(E, K):
+    """One token per batch on the tied-logit layer: the single-token router's
+    fixed-order sums keep the exact ties, and the single-token gate/up and
+    down kernels consume what the selection kept."""
+    layer = _tied_layer(E, K)
+    dl = device_layer(layer)
+    rng = np.random.default_rng(50 + E + K)
+    note(f"[single token ties] E={E} K={K}")
+    for i in range(4):
+        x = synth.f32_to_bf16_bits(rng.choice(np.array([-1.0, 0.0, 1.0, 2.0], np.float32),
+                                              size=(1, 128)).astype(np.float32))
+        y, rt, _ = run_forward(dl, x)
+        rt_ref, y_ref = oracle.forward(layer, x)
+        check_routing(rt, rt_ref, E)
+        check_output(y, y_ref, "bf16")
+
+
 @pytest.mark.parametrize("flags", [1, 2, 3])
-@pytest.mark.parametrize("T", [37, 4200])
+@pytest.mark.parametrize("T", [1, 37, 4200])
 def test_gate_options(flags, T):
-    """Gate options (softmax over all E; renormalised masked gates), in the
-    one-wave-per-token selection (37 tokens) and the 64-token-block one (4200)."""
+    """Gate options (softmax over all E; renormalised masked gates), for one
+    token (the single-token kernels), in the one-wave-per-token selection (37
+    tokens) and the 64-token-block one (4200)."""
     from oracle_pins import with_gating
     base = small_layer("gates", D=128, E=40, K=6, I=64, S=1, I_s=64, keep=0.4, router_bias=True)
     layer = with_gating(base, flags)
