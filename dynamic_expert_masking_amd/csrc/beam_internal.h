@@ -155,7 +155,8 @@ hipError_t launch_down(const beam_moe_layer& L, int32_t T, int tile_rows, const 
 bool down_combine_fused(const beam_moe_layer& L, int32_t T);
 hipError_t launch_down_combine_t1(const beam_moe_layer& L, const Ptrs& p, void* y, hipStream_t s);
 // Single-token batches whose down product takes that launch and whose d_model
-// is at most 2048 (bf16 weights): gate/up and SwiGLU as matrix-vector products.
+// is at most 2048 (4096 with FP8 expert weights): gate/up and SwiGLU as
+// matrix-vector products.
 bool gate_up_t1(const beam_moe_layer& L, int32_t T);
 hipError_t launch_gate_up_t1(const beam_moe_layer& L, const void* x, const Ptrs& p, hipStream_t s);
 hipError_t launch_combine(const beam_moe_layer& L, int32_t T, int tile_rows, const Ptrs& p,

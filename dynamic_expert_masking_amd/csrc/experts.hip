@@ -1513,7 +1513,7 @@ bool down_combine_fused(const beam_moe_layer& L, int32_t T) {
 
 // FP8: a chunk holds 16 codes, widened exactly to bf16 in registers; each
 // weight row's dot is multiplied by the row's scale before it leaves the wave.
-template <bool F8>
+template <bool F8, int NJ>   // NJ: 16-byte chunks per lane of the longest segment row
 __global__ __launch_bounds__(kDcWaves * 64) void k_down_combine_t1(DownCombineArgs a) {
   constexpr int CK = dc_chunk<F8>();
   constexpr int HL = F8 ? 2 : 1;   // 16-byte loads of h per chunk
@@ -1559,9 +1559,9 @@ __global__ __launch_bounds__(kDcWaves * 64) void k_down_combine_t1(DownCombineAr
     }
     const size_t row_bytes = size_t(len) * (F8 ? 1 : 2);
     const int nch = len / CK;
-    u32x4 hv[kDcMaxChunks][HL], wv[kDcRows][kDcMaxChunks];
+    u32x4 hv[NJ][HL], wv[kDcRows][NJ];
 #pragma unroll
-    for (int j = 0; j < kDcMaxChunks; ++j) {   // every load issued before any use
+    for (int j = 0; j < NJ; ++j) {   // every load issued before any use
       const int c = lane + kWave * j;
       const int cc = c < nch ? c : 0;
 #pragma unroll
@@ -1573,7 +1573,7 @@ __global__ __launch_bounds__(kDcWaves * 64) void k_down_combine_t1(DownCombineAr
 #pragma unroll
     for (int r = 0; r < kDcRows; ++r) dot[r] = 0.f;
 #pragma unroll
-    for (int j = 0; j < kDcMaxChunks; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       if (lane + kWave * j >= nch) continue;   // chunk past the row: no contribution
 #pragma unroll
       for (int u = 0; u < HL; ++u)
@@ -1608,37 +1608,46 @@ __global__ __launch_bounds__(kDcWaves * 64) void k_down_combine_t1(DownCombineAr
   }
 }
 
-// Single-token batches, gate/up and SwiGLU (bf16 weights, d_model up to
-// 2048): each expert's gate and up products are matrix-vector products too.
-// A workgroup takes one intermediate row of every segment -- the kept slots,
-// then each shared expert -- one segment per wave: the wave issues the
-// segment's gate and up rows and the token's x row at once, forms both dots
-// in fp32 with fixed-order wave reductions, and writes h = silu(g) * u
+// Single-token batches, gate/up and SwiGLU (d_model up to 2048 with bf16
+// weights, 4096 with FP8): each expert's gate and up products are
+// matrix-vector products too. A workgroup takes one intermediate row of
+// every segment -- the kept slots, then each shared expert -- one segment per
+// wave: the wave issues the segment's gate and up rows and the token's x row
+// at once (NJ 16-byte chunks per lane, no more than the row has), forms both
+// dots in fp32 with fixed-order wave reductions, and writes h = silu(g) * u
 // (rounded to bf16 once) where the down product reads it (pair order; the
 // shared experts' [S Is] row). One row per workgroup measured fastest: at
 // four rows a workgroup's registers left one workgroup resident per compute
-// unit and the grid ran in two uneven waves. Staging x in LDS once per
-// workgroup did not help; with FP8 weights (half the bytes per row) this form
-// lost to the streaming kernel, so FP8 layers keep that one.
+// unit and the grid ran in two uneven waves; staging x in LDS once per
+// workgroup did not help. FP8: a chunk holds 16 codes, widened exactly to
+// bf16 in registers, and each dot is multiplied by its row's scale before
+// SwiGLU.
 struct GateUpT1Args {
+  const void* wg;       // [E][I][D]: bf16, or E4M3 codes
+  const void* wu;
+  const void* sg;       // [S Is][D]
+  const void* su;
+  const float* qg;      // FP8: row scales [E][I] (else null)
+  const float* qu;
+  const float* qsg;     // FP8: [S Is]
+  const float* qsu;
   const u16* x;
-  const u16* wg;   // [E][I][D]
-  const u16* wu;
-  const u16* sg;   // [S Is][D]
-  const u16* su;
   const int32_t* slot_pos;
   const int32_t* idx;
-  u16* h;          // [P][I]
-  u16* h_sh;       // [1][S Is]
+  u16* h;               // [P][I]
+  u16* h_sh;            // [1][S Is]
   int D, I, Is, S, K;
 };
 
 bool gate_up_t1(const beam_moe_layer& L, int32_t T) {
-  return down_combine_fused(L, T) && L.expert_format == BEAM_WEIGHTS_DTYPE && L.D % 8 == 0 &&
-         L.D <= kWave * kDcMaxChunks * 8;
+  const int ck = L.expert_format == BEAM_WEIGHTS_FP8_E4M3 ? 16 : 8;   // elements per chunk
+  return down_combine_fused(L, T) && L.D % ck == 0 && L.D <= kWave * kDcMaxChunks * ck;
 }
 
+template <bool F8, int NJ>   // NJ: 16-byte chunks per lane of a row
 __global__ __launch_bounds__(kDcWaves * 64) void k_gate_up_t1(GateUpT1Args a) {
+  constexpr int CK = dc_chunk<F8>();
+  constexpr int HL = F8 ? 2 : 1;   // 16-byte loads of x per chunk
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row = blockIdx.x;
@@ -1651,10 +1660,14 @@ __global__ __launch_bounds__(kDcWaves * 64) void k_gate_up_t1(GateUpT1Args a) {
   const int nk = __popcll(kept);
   const int nseg = nk + a.S;
   const int rank = __popcll(kept & ((1ull << lane) - 1ull));
-  const int nch = a.D / 8;
+  const int nch = a.D / CK;
+  const size_t row_bytes = size_t(a.D) * (F8 ? 1 : 2);
   for (int q = wave; q < nseg; q += kDcWaves) {   // wave-uniform
-    const u16* g;
-    const u16* u;
+    size_t wrow;   // row of the segment's matrices
+    const void* gm;
+    const void* um;
+    const float* qg;
+    const float* qu;
     u16* hr;
     if (q < nk) {   // the q-th kept slot
       if (row >= a.I) continue;
@@ -1662,50 +1675,72 @@ __global__ __launch_bounds__(kDcWaves * 64) void k_gate_up_t1(GateUpT1Args a) {
       const int k = __ffsll(static_cast<unsigned long long>(sel)) - 1;
       const int ek = __builtin_amdgcn_readlane(ex, k);
       const int pk = __builtin_amdgcn_readlane(pos, k);
-      g = a.wg + (size_t(ek) * a.I + row) * a.D;
-      u = a.wu + (size_t(ek) * a.I + row) * a.D;
+      wrow = size_t(ek) * a.I + row;
+      gm = a.wg;
+      um = a.wu;
+      qg = a.qg;
+      qu = a.qu;
       hr = a.h + size_t(pk) * a.I + row;
     } else {        // shared expert q - nk: row sx Is + row of the fused matrices
       if (row >= a.Is) continue;
-      const size_t wrow = size_t(q - nk) * a.Is + row;
-      g = a.sg + wrow * a.D;
-      u = a.su + wrow * a.D;
+      wrow = size_t(q - nk) * a.Is + row;
+      gm = a.sg;
+      um = a.su;
+      qg = a.qsg;
+      qu = a.qsu;
       hr = a.h_sh + wrow;
     }
-    u32x4 xv[kDcMaxChunks], gv[kDcMaxChunks], uv[kDcMaxChunks];
+    const unsigned char* g = static_cast<const unsigned char*>(gm) + wrow * row_bytes;
+    const unsigned char* u = static_cast<const unsigned char*>(um) + wrow * row_bytes;
+    u32x4 xv[NJ][HL], gv[NJ], uv[NJ];
 #pragma unroll
-    for (int j = 0; j < kDcMaxChunks; ++j) {   // every load issued before any use
+    for (int j = 0; j < NJ; ++j) {   // every load issued before any use
       const int c = lane + kWave * j;
-      const size_t cc = size_t(c < nch ? c : 0) * 8;
-      xv[j] = ld16(a.x + cc);
-      gv[j] = ld16_stream(g + cc);
-      uv[j] = ld16_stream(u + cc);
+      const size_t cc = size_t(c < nch ? c : 0);
+#pragma unroll
+      for (int v = 0; v < HL; ++v) xv[j][v] = ld16(a.x + cc * CK + 8 * v);
+      gv[j] = ld16_stream(g + cc * 16);
+      uv[j] = ld16_stream(u + cc * 16);
     }
     float dg = 0.f, du = 0.f;
 #pragma unroll
-    for (int j = 0; j < kDcMaxChunks; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       if (lane + kWave * j >= nch) continue;   // chunk past the row: no contribution
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float x0 = __uint_as_float(xv[j][i] << 16), x1 = __uint_as_float(xv[j][i] & 0xffff0000u);
-        dg = fmaf(__uint_as_float(gv[j][i] << 16), x0, dg);
-        dg = fmaf(__uint_as_float(gv[j][i] & 0xffff0000u), x1, dg);
-        du = fmaf(__uint_as_float(uv[j][i] << 16), x0, du);
-        du = fmaf(__uint_as_float(uv[j][i] & 0xffff0000u), x1, du);
+      for (int v = 0; v < HL; ++v) {
+        // this chunk's 8 weights that meet x values 8v .. 8v + 7, as bf16
+        const u32x4 gb = F8 ? e4m3x8_to_bf16(gv[j][2 * v], gv[j][2 * v + 1]) : gv[j];
+        const u32x4 ub = F8 ? e4m3x8_to_bf16(uv[j][2 * v], uv[j][2 * v + 1]) : uv[j];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x0 = __uint_as_float(xv[j][v][i] << 16), x1 = __uint_as_float(xv[j][v][i] & 0xffff0000u);
+          dg = fmaf(__uint_as_float(gb[i] << 16), x0, dg);
+          dg = fmaf(__uint_as_float(gb[i] & 0xffff0000u), x1, dg);
+          du = fmaf(__uint_as_float(ub[i] << 16), x0, du);
+          du = fmaf(__uint_as_float(ub[i] & 0xffff0000u), x1, du);
+        }
       }
     }
-    const float gs = wave_sum_f32(dg), us = wave_sum_f32(du);
+    float gs = wave_sum_f32(dg), us = wave_sum_f32(du);
+    if (F8) {
+      gs *= qg[wrow];
+      us *= qu[wrow];
+    }
     if (lane == 0) *hr = f32_to_bf16(silu_f32(gs) * us);
   }
 }
 
 hipError_t launch_gate_up_t1(const beam_moe_layer& L, const void* x, const Ptrs& p, hipStream_t s) {
   GateUpT1Args a;
+  a.wg = L.w_gate;
+  a.wu = L.w_up;
+  a.sg = L.ws_gate;
+  a.su = L.ws_up;
+  a.qg = L.scale_gate;
+  a.qu = L.scale_up;
+  a.qsg = L.scale_shared_gate;
+  a.qsu = L.scale_shared_up;
   a.x = static_cast<const u16*>(x);
-  a.wg = static_cast<const u16*>(L.w_gate);
-  a.wu = static_cast<const u16*>(L.w_up);
-  a.sg = static_cast<const u16*>(L.ws_gate);
-  a.su = static_cast<const u16*>(L.ws_up);
   a.slot_pos = p.slot_pos;
   a.idx = p.idx;
   a.h = static_cast<u16*>(p.h);
@@ -1715,9 +1750,22 @@ hipError_t launch_gate_up_t1(const beam_moe_layer& L, const void* x, const Ptrs&
   a.Is = L.I_shared;
   a.S = L.n_shared;
   a.K = L.K;
-  const unsigned rows = unsigned(std::max(L.I, L.n_shared > 0 ? L.I_shared : 0));
-  prof_before("gate_up_swiglu_t1", s);
-  hipLaunchKernelGGL(k_gate_up_t1, dim3(rows), dim3(kDcWaves * 64), 0, s, a);
+  const bool f8 = L.expert_format == BEAM_WEIGHTS_FP8_E4M3;
+  const int nj = (L.D / (f8 ? 16 : 8) + kWave - 1) / kWave;   // 1 .. kDcMaxChunks
+  const dim3 grid(unsigned(std::max(L.I, L.n_shared > 0 ? L.I_shared : 0))), block(kDcWaves * 64);
+  auto go = [&](auto k1, auto k2, auto k3, auto k4) {
+    if (nj <= 1) hipLaunchKernelGGL(k1, grid, block, 0, s, a);
+    else if (nj == 2) hipLaunchKernelGGL(k2, grid, block, 0, s, a);
+    else if (nj == 3) hipLaunchKernelGGL(k3, grid, block, 0, s, a);
+    else hipLaunchKernelGGL(k4, grid, block, 0, s, a);
+  };
+  if (f8) {
+    prof_before("gate_up_swiglu_t1_fp8", s);
+    go(k_gate_up_t1<true, 1>, k_gate_up_t1<true, 2>, k_gate_up_t1<true, 3>, k_gate_up_t1<true, 4>);
+  } else {
+    prof_before("gate_up_swiglu_t1", s);
+    go(k_gate_up_t1<false, 1>, k_gate_up_t1<false, 2>, k_gate_up_t1<false, 3>, k_gate_up_t1<false, 4>);
+  }
   prof_after(s);
   return hipGetLastError();
 }
@@ -1740,12 +1788,23 @@ hipError_t launch_down_combine_t1(const beam_moe_layer& L, const Ptrs& p, void* 
   a.S = L.n_shared;
   a.K = L.K;
   const dim3 grid(unsigned(L.D / kDcRows)), block(kDcWaves * 64);
-  if (L.expert_format == BEAM_WEIGHTS_FP8_E4M3) {
+  const bool f8 = L.expert_format == BEAM_WEIGHTS_FP8_E4M3;
+  const int len = std::max(L.I, L.n_shared > 0 ? L.I_shared : 0);
+  const int nj = (len / (f8 ? 16 : 8) + kWave - 1) / kWave;   // 1 .. kDcMaxChunks
+  auto go = [&](auto k1, auto k2, auto k3, auto k4) {
+    if (nj <= 1) hipLaunchKernelGGL(k1, grid, block, 0, s, a);
+    else if (nj == 2) hipLaunchKernelGGL(k2, grid, block, 0, s, a);
+    else if (nj == 3) hipLaunchKernelGGL(k3, grid, block, 0, s, a);
+    else hipLaunchKernelGGL(k4, grid, block, 0, s, a);
+  };
+  if (f8) {
     prof_before("down_combine_fp8", s);
-    hipLaunchKernelGGL(k_down_combine_t1<true>, grid, block, 0, s, a);
+    go(k_down_combine_t1<true, 1>, k_down_combine_t1<true, 2>, k_down_combine_t1<true, 3>,
+       k_down_combine_t1<true, 4>);
   } else {
     prof_before("down_combine", s);
-    hipLaunchKernelGGL(k_down_combine_t1<false>, grid, block, 0, s, a);
+    go(k_down_combine_t1<false, 1>, k_down_combine_t1<false, 2>, k_down_combine_t1<false, 3>,
+       k_down_combine_t1<false, 4>);
   }
   prof_after(s);
   return hipGetLastError();
