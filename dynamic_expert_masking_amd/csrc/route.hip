@@ -292,9 +292,20 @@ hipError_t launch_router_logits(const beam_moe_layer& L, const void* x, int32_t 
   RouterArgs a{(const u16*)x, (const u16*)L.w_router, (const u16*)L.w_mask, part, T, L.D, L.E, KS};
   if (router_t1(L, T)) {
     const dim3 grid(unsigned((2 * L.E + 3) / 4));
+    // chunks per lane sized to the row, so no lane re-reads a chunk for nothing
+    const int nj = (L.D / 8 + kWave - 1) / kWave;
+    const dim3 block(256);
     prof_before("router_logits_t1", s);
-    if (L.D <= kWave * 8 * 4) hipLaunchKernelGGL(k_router_t1<4>, grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(k_router_t1<8>, grid, dim3(256), 0, s, a);
+    switch (nj) {
+      case 1: hipLaunchKernelGGL(k_router_t1<1>, grid, block, 0, s, a); break;
+      case 2: hipLaunchKernelGGL(k_router_t1<2>, grid, block, 0, s, a); break;
+      case 3: hipLaunchKernelGGL(k_router_t1<3>, grid, block, 0, s, a); break;
+      case 4: hipLaunchKernelGGL(k_router_t1<4>, grid, block, 0, s, a); break;
+      case 5: hipLaunchKernelGGL(k_router_t1<5>, grid, block, 0, s, a); break;
+      case 6: hipLaunchKernelGGL(k_router_t1<6>, grid, block, 0, s, a); break;
+      case 7: hipLaunchKernelGGL(k_router_t1<7>, grid, block, 0, s, a); break;
+      default: hipLaunchKernelGGL(k_router_t1<8>, grid, block, 0, s, a); break;
+    }
     prof_after(s);
   } else if (router_use_skinny(T, L.E)) {
     const int nm = router_nm(T, L.E), mt = router_mt(T, L.E);
